@@ -1,0 +1,556 @@
+"""Plain fp64 CPU oracle for the RoPE -> randomized-Hadamard -> Lloyd-Max (+ QJL) KV codec.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this module: only
+`tests/`, `__graft_entry__.smoke()` and the `cpu_baseline` leg of `bench.py` may
+import or call it.  It shares no code with the HIP library (no kernels, headers,
+tables or constant generators); the two meet only in the seeded input generators,
+which hold none of the method's arithmetic.
+
+Every step is written in the slowest obvious form: a dense d x d rotation matrix
+applied as a matvec, brute-force nearest codeword over all 2^b centroids, an
+explicit m x d Gaussian matrix S, fp64 softmax.  Library primitives (numpy matmul,
+scipy's regularized incomplete beta) serve as single steps.
+
+Sources (titles of the pages; sections as they appear there):
+  [TurboESM]  "TurboESM: Ultra-Efficient 3-Bit KV Cache Quantization for Protein
+              Language Models ..." -- technical summary section 2.A (RoPE applied
+              before the orthogonal rotation, invariance of the attention score
+              under an orthogonal Pi), 2.C (Lloyd-Max look-up tables), 2.D (1-bit
+              residual correction), 2.E (fused decode: dequantize, correct,
+              inverse rotation, online softmax in one pass).
+  [TurboQuant] news summary of the TurboQuant blog post -- "Etape 1" (random
+              rotation then a standard scalar quantizer per coordinate), "Etape 2"
+              and "QJL" (Johnson-Lindenstrauss projection reduced to sign bits,
+              asymmetric estimator with a full-precision query), reader comment on
+              Lloyd-Max boundaries/reconstruction values and per-dimension coding,
+              "Performances en recherche vectorielle" (recall 1@k, top-k search).
+  [NSNQuant]  "NSNQuant ..." technical summary section 2 (randomized Hadamard
+              transform) -- cited for the choice of a seeded-sign Hadamard rotation.
+
+Readings where the pages are silent (each is also listed in the design doc):
+  * PRNG: SplitMix64 (Steele, Lea & Flood 2014) used as a counter-based generator;
+    Gaussians by Box-Muller (cos branch) in fp64, rounded to fp32.
+  * Rotation: Pi = blockdiag(H_B, ..., H_B) diag(D) / sqrt(B), H_B Sylvester, B the
+    largest power of two dividing d (B = d for d = 64, 128; B = 512 for d = 1536).
+  * RoPE: half-split pairs (j, j + d/2), theta_j = base^(-2j/d), angles in fp64.
+  * Codebook: Lloyd-Max for the exact marginal of one coordinate of a uniform unit
+    vector in R^d; the stored codebook is each centroid rounded to fp16, and codes
+    are nearest stored centroid (ties to the larger index).
+  * Residual r = y - fp16(n) * c[code]; QJL bits = [ (S r)_i >= 0 ]; estimator
+    scale sqrt(pi/2)/m.
+
+Parity pinned by tests/test_oracle_*.py (closed forms, textbook tables, invariants,
+brute force).  Parity unpinned: the pages' model-level accuracy claims (cosine
+similarity on protein families, lossless 3-bit LLM quality) -- no models or data.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from scipy.special import betainc, gammaln
+
+__all__ = [
+    "splitmix64", "uniform01", "rotation_signs", "gaussian_projection",
+    "sphere_marginal_cdf", "sphere_marginal_pdf", "sphere_partial_mean", "lloyd_max",
+    "Codebook", "make_codebook", "hadamard", "rotation_matrix", "rope",
+    "fp16_sat", "Codec", "make_codec", "encode", "pack_cache", "unpack_cache",
+    "cache_layout", "attend", "search_scores", "topk", "exact_topk",
+]
+
+_GOLDEN_GAMMA = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+
+# PRNG stream ids (disjoint 2^32-long segments of one SplitMix64 sequence)
+STREAM_SIGNS = 1
+STREAM_GAUSS = 2
+
+
+# ----------------------------------------------------------------------------------
+# Counter-based SplitMix64 (Steele, Lea & Flood, "Fast splittable pseudorandom
+# number generators", OOPSLA 2014): output k of a generator seeded with s is
+# mix(s + (k+1) * golden_gamma).  Stream t, index i uses k = t * 2^32 + i.
+# ----------------------------------------------------------------------------------
+def splitmix64(seed: int, stream: int, idx) -> np.ndarray:
+    """uint64 SplitMix64 outputs for counter positions `idx` of `stream`."""
+    idx = np.asarray(idx, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        k = np.uint64(stream) * np.uint64(1 << 32) + idx + np.uint64(1)
+        z = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) + k * _GOLDEN_GAMMA
+        z = (z ^ (z >> np.uint64(30))) * _M1
+        z = (z ^ (z >> np.uint64(27))) * _M2
+        z = z ^ (z >> np.uint64(31))
+    return z
+
+
+def uniform01(seed: int, stream: int, idx) -> np.ndarray:
+    """Open-interval uniforms in (0, 1): ((x >> 11) + 0.5) * 2^-53, fp64."""
+    x = splitmix64(seed, stream, idx)
+    return ((x >> np.uint64(11)).astype(np.float64) + 0.5) * (2.0 ** -53)
+
+
+def rotation_signs(d: int, seed: int) -> np.ndarray:
+    """D_j = +1 if the top bit of SplitMix64(seed, signs stream, j) is 0, else -1."""
+    x = splitmix64(seed, STREAM_SIGNS, np.arange(d, dtype=np.uint64))
+    return np.where((x >> np.uint64(63)) == 0, 1.0, -1.0)
+
+
+def gaussian_projection(m: int, d: int, seed: int) -> np.ndarray:
+    """S (m x d): Box-Muller cos branch, u1 = U(2(i d + j)), u2 = U(2(i d + j) + 1),
+    z = sqrt(-2 ln u1) * cos((2 pi) * u2) in fp64, rounded to fp32 (returned as fp32)."""
+    n = np.arange(m * d, dtype=np.uint64)
+    u1 = uniform01(seed, STREAM_GAUSS, 2 * n)
+    u2 = uniform01(seed, STREAM_GAUSS, 2 * n + 1)
+    z = np.sqrt(-2.0 * np.log(u1)) * np.cos((2.0 * math.pi) * u2)
+    return z.astype(np.float32).reshape(m, d)
+
+
+# ----------------------------------------------------------------------------------
+# Lloyd-Max codebook for one coordinate of a uniform random unit vector in R^d
+# ([TurboQuant] "Etape 1": after a random rotation each coordinate gets its own
+# standard scalar quantizer; reader comment: Lloyd-Max boundaries and reconstruction
+# values).  Density f_d(x) = C_d (1 - x^2)^((d-3)/2) on [-1, 1]; X^2 ~ Beta(1/2, (d-1)/2).
+# ----------------------------------------------------------------------------------
+def _log_cd(d: int) -> float:
+    return gammaln(d / 2.0) - 0.5 * math.log(math.pi) - gammaln((d - 1) / 2.0)
+
+
+def sphere_marginal_pdf(x, d: int):
+    x = np.asarray(x, dtype=np.float64)
+    inside = np.abs(x) < 1.0
+    out = np.zeros_like(x)
+    xi = x[inside]
+    out[inside] = np.exp(_log_cd(d) + 0.5 * (d - 3) * np.log1p(-xi * xi))
+    return out
+
+
+def sphere_marginal_cdf(x, d: int):
+    """F(x) = 1/2 + sign(x)/2 * I_{x^2}(1/2, (d-1)/2)."""
+    x = np.clip(np.asarray(x, dtype=np.float64), -1.0, 1.0)
+    return 0.5 + 0.5 * np.sign(x) * betainc(0.5, (d - 1) / 2.0, x * x)
+
+
+def sphere_partial_mean(x, d: int):
+    """M(x) = int_{-1}^{x} t f_d(t) dt = -C_d (1 - x^2)^((d-1)/2) / (d - 1)."""
+    x = np.clip(np.asarray(x, dtype=np.float64), -1.0, 1.0)
+    one_m = np.maximum(1.0 - x * x, 0.0)
+    with np.errstate(divide="ignore"):
+        val = np.where(one_m > 0.0,
+                       np.exp(_log_cd(d) + 0.5 * (d - 1) * np.log(np.where(one_m > 0, one_m, 1.0))),
+                       0.0)
+    return -val / (d - 1)
+
+
+def lloyd_max(d: int, bits: int, tol: float = 1e-13, max_iter: int = 100000):
+    """Lloyd iteration (Lloyd 1982; Max 1960) in fp64.
+
+    t_k = (c_k + c_{k+1}) / 2;  c_k = E[X | t_{k-1} < X <= t_k], with t_{-1} = -1,
+    t_{K-1} = +1.  Stops when max |sqrt(d) * delta c| < tol.
+    Returns (centroids, boundaries, iterations), ascending."""
+    K = 1 << bits
+    # start from equal-mass cells of the N(0, 1/d) limit
+    c = np.array([(k + 0.5) / K for k in range(K)], dtype=np.float64)
+    c = (np.sqrt(2.0) * _erfinv(2.0 * c - 1.0)) / math.sqrt(d)
+    c = np.clip(c, -0.999, 0.999)
+    it = 0
+    for it in range(1, max_iter + 1):
+        t = 0.5 * (c[:-1] + c[1:])
+        edges = np.concatenate(([-1.0], t, [1.0]))
+        F = sphere_marginal_cdf(edges, d)
+        M = sphere_partial_mean(edges, d)
+        c_new = (M[1:] - M[:-1]) / (F[1:] - F[:-1])
+        delta = np.max(np.abs(c_new - c)) * math.sqrt(d)
+        c = c_new
+        if delta < tol:
+            break
+    t = 0.5 * (c[:-1] + c[1:])
+    return c, t, it
+
+
+def _erfinv(y):
+    from scipy.special import erfinv
+    return erfinv(y)
+
+
+class Codebook:
+    """Lloyd-Max codebook and the stored (fp16-rounded) form the codec uses."""
+
+    def __init__(self, d: int, bits: int):
+        self.d, self.bits = d, bits
+        self.c64, self.t64, self.iterations = lloyd_max(d, bits)
+        # stored codebook: each centroid rounded to the nearest fp16 (RNE)
+        self.c = self.c64.astype(np.float16).astype(np.float64)
+        # decision boundaries of the stored codebook: exact midpoints
+        self.t = 0.5 * (self.c[:-1] + self.c[1:])
+
+    def mse(self) -> float:
+        """Per-coordinate MSE E[(X - Q(X))^2] of the fp64 codebook (closed form)."""
+        d = self.d
+        edges = np.concatenate(([-1.0], self.t64, [1.0]))
+        F = sphere_marginal_cdf(edges, d)
+        # with c_k the cell means: E[(X - Q(X))^2] = E[X^2] - sum_k c_k^2 P_k, E[X^2] = 1/d
+        P = F[1:] - F[:-1]
+        return 1.0 / d - float(np.sum(self.c64 ** 2 * P))
+
+
+_CODEBOOK_CACHE: dict = {}
+
+
+def make_codebook(d: int, bits: int) -> Codebook:
+    key = (d, bits)
+    if key not in _CODEBOOK_CACHE:
+        _CODEBOOK_CACHE[key] = Codebook(d, bits)
+    return _CODEBOOK_CACHE[key]
+
+
+# ----------------------------------------------------------------------------------
+# Rotation ([TurboESM] 2.A: orthogonal Pi with Pi^T Pi = I applied after RoPE;
+# [TurboQuant] "Etape 1": random rotation; [NSNQuant] 2: randomized Hadamard).
+# ----------------------------------------------------------------------------------
+def hadamard(n: int) -> np.ndarray:
+    """Sylvester Hadamard matrix: H[i][j] = (-1)^popcount(i & j)."""
+    assert n > 0 and (n & (n - 1)) == 0
+    i = np.arange(n)
+    pc = np.zeros((n, n), dtype=np.int64)
+    x = i[:, None] & i[None, :]
+    while np.any(x):
+        pc += x & 1
+        x = x >> 1
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def hadamard_block(d: int) -> int:
+    """Largest power of two dividing d."""
+    return d & (-d)
+
+
+def rotation_matrix(d: int, seed: int) -> np.ndarray:
+    """Dense Pi = blockdiag(H_B) diag(D) / sqrt(B)."""
+    B = hadamard_block(d)
+    H = hadamard(B)
+    P = np.zeros((d, d))
+    for b in range(d // B):
+        P[b * B:(b + 1) * B, b * B:(b + 1) * B] = H
+    D = rotation_signs(d, seed)
+    return P * D[None, :] / math.sqrt(B)
+
+
+def rope(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """Half-split rotary embedding applied to rows of x at positions `pos` (fp64).
+
+    For j < d/2: phi = pos * base^(-2j/d);
+    (x_j, x_{j+d/2}) <- (x_j cos phi - x_{j+d/2} sin phi, x_j sin phi + x_{j+d/2} cos phi).
+    base == 0 means no rotary embedding."""
+    x = np.asarray(x, dtype=np.float64)
+    if base == 0:
+        return x.copy()
+    d = x.shape[-1]
+    h = d // 2
+    j = np.arange(h, dtype=np.float64)
+    theta = np.power(float(base), -2.0 * j / d)
+    pos = np.asarray(pos, dtype=np.float64)
+    phi = pos[..., None] * theta
+    c, s = np.cos(phi), np.sin(phi)
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+FP16_MAX = 65504.0
+
+
+def fp16_sat(x):
+    """fp16 round-to-nearest-even; values that would round to inf become 65504.
+    Returns (fp16-valued fp64 array, overflow mask)."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        h = x.astype(np.float16)
+    over = ~np.isfinite(h)
+    h = np.where(over, np.float16(FP16_MAX), h)
+    return h.astype(np.float64), over
+
+
+# ----------------------------------------------------------------------------------
+# Codec: rotation, codebooks, S
+# ----------------------------------------------------------------------------------
+class Codec:
+    def __init__(self, d: int, bits_k: int, bits_v: int, m: int, seed: int):
+        self.d, self.bits_k, self.bits_v, self.m, self.seed = d, bits_k, bits_v, m, seed
+        self.Pi = rotation_matrix(d, seed)
+        self.D = rotation_signs(d, seed)
+        self.cb_k = make_codebook(d, bits_k)
+        self.cb_v = make_codebook(d, bits_v) if bits_v > 0 else None
+        self.S = gaussian_projection(m, d, seed).astype(np.float64) if m > 0 else None
+
+    @property
+    def qjl_scale(self) -> float:
+        return math.sqrt(math.pi / 2.0) / self.m
+
+
+def make_codec(d, bits_k, bits_v, m, seed) -> Codec:
+    return Codec(d, bits_k, bits_v, m, seed)
+
+
+def _nearest(u: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """Brute force over all centroids: argmin_k |u - c_k|, exact ties to larger k."""
+    best = np.zeros(u.shape, dtype=np.int64)
+    bestd = np.abs(u - c[0])
+    for k in range(1, len(c)):
+        dk = np.abs(u - c[k])
+        take = dk <= bestd
+        best = np.where(take, k, best)
+        bestd = np.where(take, dk, bestd)
+    return best
+
+
+def encode(x, codec: Codec, *, kind: str, positions=None, rope_base: float = 0.0):
+    """Encode rows of x ([N, d], any float dtype; converted exactly to fp64).
+
+    kind = 'key' (RoPE if rope_base != 0, scalar codes with bits_k, QJL residual sketch),
+           'value' (scalar codes with bits_v), 'db' (like 'key' without RoPE).
+    Returns a dict with y (rotated, fp64), u, codes, n16, and for keys rn16, bits, z,
+    plus overflow flags."""
+    x = np.asarray(x, dtype=np.float64)
+    if kind == "key" and rope_base != 0:
+        x = rope(x, positions, rope_base)
+    y = x @ codec.Pi.T
+    n = np.sqrt(np.sum(y * y, axis=-1))
+    safe = np.where(n > 0, n, 1.0)
+    u = np.where(n[..., None] > 0, y / safe[..., None], 0.0)
+    cb = codec.cb_v if kind == "value" else codec.cb_k
+    codes = _nearest(u, cb.c)
+    n16, over_n = fp16_sat(n)
+    out = {"y": y, "u": u, "codes": codes, "n": n, "n16": n16, "overflow": over_n.copy()}
+    if kind in ("key", "db"):
+        r = y - n16[..., None] * cb.c[codes]
+        rn = np.sqrt(np.sum(r * r, axis=-1))
+        rn16, over_r = fp16_sat(rn)
+        z = r @ codec.S.T
+        out.update(r=r, rn=rn, rn16=rn16, z=z, bits=(z >= 0).astype(np.int64))
+        out["overflow"] = out["overflow"] | over_r
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# Packed cache format, version 1 (written from the format description, independently
+# of the library):
+#   header: 256 bytes; u32 magic 0x564B5154 ("TQKV"), u32 version 1, u32 flags
+#           (bit 0: a norm saturated to fp16 max), u32 0, then i32 batch, kv_heads, d,
+#           capacity, bits_k, bits_v, m; zero padding.
+#   Kbits:  [batch][kv_heads][capacity][kbytes], kbytes = (bits_k*d + m)/8: plane p of the
+#           scalar code (bit p of code_j at plane bit j), p = 0..bits_k-1, then the m
+#           QJL sign bits.  Plane bit j lives in byte j/8, bit j%8 (little-endian).
+#   Knorm:  [batch][kv_heads][capacity] x {fp16 n, fp16 ||r||}.
+#   Vcodes: [batch][kv_heads][ceil(capacity/32)][d][4*bits_v bytes]: for a tile of 32
+#           tokens and coordinate j, a (32*bits_v)-bit little-endian integer whose bits
+#           [bits_v*i, bits_v*(i+1)) hold the value code of token 32*tile + i.
+#   Vnorm:  [batch][kv_heads][capacity] fp16 n.
+#   Each region starts at a multiple of 256 bytes.
+# ----------------------------------------------------------------------------------
+CACHE_MAGIC = 0x564B5154
+CACHE_VERSION = 1
+HEADER_BYTES = 256
+
+
+def _align(x, a=256):
+    return (x + a - 1) // a * a
+
+
+def cache_layout(batch, kv_heads, d, capacity, bits_k, bits_v, m):
+    kbytes = (bits_k * d + m) // 8
+    units = batch * kv_heads
+    tiles = (capacity + 31) // 32
+    off = {}
+    cur = HEADER_BYTES
+    off["kbits"] = cur
+    cur = _align(cur + units * capacity * kbytes)
+    off["knorm"] = cur
+    cur = _align(cur + units * capacity * 4)
+    if bits_v > 0:
+        off["vcodes"] = cur
+        cur = _align(cur + units * tiles * d * 4 * bits_v)
+        off["vnorm"] = cur
+        cur = _align(cur + units * capacity * 2)
+    off["total"] = cur
+    off["kbytes"] = kbytes
+    off["tiles"] = tiles
+    return off
+
+
+def _bits_to_bytes(bitmat: np.ndarray) -> np.ndarray:
+    """[..., nbits] of 0/1 -> [..., nbits/8] uint8, bit j in byte j/8 bit j%8."""
+    sh = bitmat.shape
+    b = bitmat.reshape(sh[:-1] + (sh[-1] // 8, 8)).astype(np.uint8)
+    w = (1 << np.arange(8)).astype(np.uint8)
+    return np.sum(b * w, axis=-1, dtype=np.uint64).astype(np.uint8)
+
+
+def pack_cache(desc: dict, fields: dict, start_pos: int = 0, image: np.ndarray | None = None,
+               flags: int = 0) -> np.ndarray:
+    """Write tokens [start_pos, start_pos + n) of every (batch, kv-head) unit.
+
+    fields: kcodes [B, H, n, d], n16 [B, H, n], rn16 [B, H, n], bits [B, H, n, m],
+            and if bits_v > 0: vcodes [B, H, n, d], vn16 [B, H, n]."""
+    B, H, d, cap = desc["batch"], desc["kv_heads"], desc["d"], desc["capacity"]
+    bk, bv, m = desc["bits_k"], desc["bits_v"], desc["m"]
+    lay = cache_layout(B, H, d, cap, bk, bv, m)
+    if image is None:
+        image = np.zeros(lay["total"], dtype=np.uint8)
+    hdr = np.zeros(HEADER_BYTES // 4, dtype=np.uint32)
+    hdr[0], hdr[1], hdr[2] = CACHE_MAGIC, CACHE_VERSION, flags
+    hdr[4:11] = np.array([B, H, d, cap, bk, bv, m], dtype=np.int64).astype(np.uint32)
+    hdr[2] |= np.uint32(image[8:12].view(np.uint32)[0])
+    image[:HEADER_BYTES] = hdr.view(np.uint8)
+
+    kcodes = np.asarray(fields["kcodes"])
+    n = kcodes.shape[2]
+    if n == 0:
+        return image
+    assert start_pos + n <= cap
+    kb = lay["kbytes"]
+    planes = [((kcodes >> p) & 1) for p in range(bk)]
+    kbitsm = np.concatenate(planes + [np.asarray(fields["bits"])], axis=-1)  # [B,H,n,bk*d+m]
+    rec = _bits_to_bytes(kbitsm)  # [B,H,n,kb]
+    kreg = image[lay["kbits"]:lay["kbits"] + B * H * cap * kb].reshape(B, H, cap, kb)
+    kreg[:, :, start_pos:start_pos + n, :] = rec
+    norms = np.stack([np.asarray(fields["n16"]), np.asarray(fields["rn16"])], axis=-1)
+    nreg = image[lay["knorm"]:lay["knorm"] + B * H * cap * 4].view(np.float16).reshape(B, H, cap, 2)
+    nreg[:, :, start_pos:start_pos + n, :] = norms.astype(np.float16)
+    if bv > 0:
+        vcodes = np.asarray(fields["vcodes"]).astype(np.int64)
+        tiles = lay["tiles"]
+        wbytes = 4 * bv
+        vreg = image[lay["vcodes"]:lay["vcodes"] + B * H * tiles * d * wbytes].reshape(B, H, tiles, d, wbytes)
+        for i in range(n):
+            t = start_pos + i
+            tile, slot = divmod(t, 32)
+            for p in range(bv):
+                bit = (vcodes[:, :, i, :] >> p) & 1          # [B, H, d]
+                pos = bv * slot + p
+                byte, sh = divmod(pos, 8)
+                cur = vreg[:, :, tile, :, byte].astype(np.int64)
+                cur = (cur & ~(1 << sh)) | (bit << sh)
+                vreg[:, :, tile, :, byte] = cur.astype(np.uint8)
+        vnreg = image[lay["vnorm"]:lay["vnorm"] + B * H * cap * 2].view(np.float16).reshape(B, H, cap)
+        vnreg[:, :, start_pos:start_pos + n] = np.asarray(fields["vn16"]).astype(np.float16)
+    return image
+
+
+def unpack_cache(image: np.ndarray, desc: dict, length: int) -> dict:
+    """Inverse of pack_cache for tokens [0, length)."""
+    B, H, d, cap = desc["batch"], desc["kv_heads"], desc["d"], desc["capacity"]
+    bk, bv, m = desc["bits_k"], desc["bits_v"], desc["m"]
+    lay = cache_layout(B, H, d, cap, bk, bv, m)
+    image = np.asarray(image, dtype=np.uint8)
+    hdr = image[:HEADER_BYTES].view(np.uint32)
+    kb = lay["kbytes"]
+    kreg = image[lay["kbits"]:lay["kbits"] + B * H * cap * kb].reshape(B, H, cap, kb)[:, :, :length]
+    bitsall = np.unpackbits(kreg, axis=-1, bitorder="little").astype(np.int64)
+    kcodes = np.zeros((B, H, length, d), dtype=np.int64)
+    for p in range(bk):
+        kcodes |= bitsall[..., p * d:(p + 1) * d] << p
+    out = {
+        "magic": int(hdr[0]), "version": int(hdr[1]), "flags": int(hdr[2]),
+        "kcodes": kcodes, "bits": bitsall[..., bk * d:bk * d + m],
+    }
+    nreg = image[lay["knorm"]:lay["knorm"] + B * H * cap * 4].view(np.float16).reshape(B, H, cap, 2)
+    out["n16"] = nreg[:, :, :length, 0].astype(np.float64)
+    out["rn16"] = nreg[:, :, :length, 1].astype(np.float64)
+    if bv > 0:
+        tiles = lay["tiles"]
+        wbytes = 4 * bv
+        vreg = image[lay["vcodes"]:lay["vcodes"] + B * H * tiles * d * wbytes].reshape(B, H, tiles, d, wbytes)
+        vbits = np.unpackbits(vreg, axis=-1, bitorder="little").astype(np.int64)  # [B,H,tiles,d,32*bv]
+        vcodes = np.zeros((B, H, length, d), dtype=np.int64)
+        for t in range(length):
+            tile, slot = divmod(t, 32)
+            for p in range(bv):
+                vcodes[:, :, t, :] |= vbits[:, :, tile, :, bv * slot + p] << p
+        out["vcodes"] = vcodes
+        vnreg = image[lay["vnorm"]:lay["vnorm"] + B * H * cap * 2].view(np.float16).reshape(B, H, cap)
+        out["vn16"] = vnreg[:, :, :length].astype(np.float64)
+    return out
+
+
+# ----------------------------------------------------------------------------------
+# Decode attention ([TurboESM] 2.E: dequantize, residual correction, online softmax,
+# inverse rotation; [TurboQuant] QJL: full-precision query against sign bits).
+# Written as plain full softmax (no online rescaling): mathematically identical.
+# ----------------------------------------------------------------------------------
+def estimate_scores(qr: np.ndarray, sq: np.ndarray, kcodes, n16, rn16, bits, codec: Codec):
+    """score_t = n16_t <qr, c_k[code_t]> + rn16_t sqrt(pi/2)/m <sq, 2 bits_t - 1>."""
+    khat = codec.cb_k.c[kcodes]                               # [T, d]
+    mse = n16 * (khat @ qr)
+    if codec.m > 0:
+        qjl = rn16 * codec.qjl_scale * ((2.0 * bits - 1.0) @ sq)
+    else:
+        qjl = 0.0
+    return mse + qjl
+
+
+def attend(fields: dict, q, codec: Codec, *, q_pos: int, rope_base: float, scale: float,
+           kv_heads: int, length: int):
+    """fp64 decode attention of q [B, Hq, d] over tokens [0, length) of `fields`
+    (as returned by unpack_cache or built from encode outputs).
+
+    GQA: q-head h reads kv-head floor(h * Hkv / Hq).  Returns (out [B, Hq, d],
+    scores [B, Hq, length]); scores are the unscaled estimates, the softmax uses
+    scale * score.  length == 0 gives out = 0."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    out = np.zeros((B, Hq, d))
+    scores = np.zeros((B, Hq, length))
+    if scale == 0:
+        scale = 1.0 / math.sqrt(d)
+    for b in range(B):
+        for h in range(Hq):
+            g = (h * kv_heads) // Hq
+            qp = rope(q[b, h][None, :], [q_pos], rope_base)[0] if rope_base != 0 else q[b, h]
+            qr = codec.Pi @ qp
+            sq = codec.S @ qr if codec.m > 0 else None
+            if length == 0:
+                continue
+            s = estimate_scores(qr, sq, fields["kcodes"][b, g, :length], fields["n16"][b, g, :length],
+                                fields["rn16"][b, g, :length], fields["bits"][b, g, :length], codec)
+            scores[b, h] = s
+            lam = scale * s
+            p = np.exp(lam - np.max(lam))
+            p = p / np.sum(p)
+            vhat = fields["vn16"][b, g, :length, None] * codec.cb_v.c[fields["vcodes"][b, g, :length]]
+            o_rot = p @ vhat
+            out[b, h] = codec.Pi.T @ o_rot
+    return out, scores
+
+
+# ----------------------------------------------------------------------------------
+# Inner-product search over packed vectors ([TurboQuant] vector search: top-k by the
+# estimated inner product, recall 1@k).
+# ----------------------------------------------------------------------------------
+def search_scores(fields: dict, queries, codec: Codec):
+    """Estimated <q, x> for every (query, database vector): [nq, n_db] fp64."""
+    Q = np.asarray(queries, dtype=np.float64)
+    qr = Q @ codec.Pi.T
+    sq = qr @ codec.S.T
+    khat = codec.cb_k.c[fields["kcodes"]]                         # [n, d]
+    mse = (qr @ khat.T) * fields["n16"][None, :]
+    qjl = (sq @ (2.0 * fields["bits"] - 1.0).T) * (fields["rn16"][None, :] * codec.qjl_scale)
+    return mse + qjl
+
+
+def topk(scores: np.ndarray, k: int):
+    """Per row: the k largest scores in descending order, equal scores to the lower index."""
+    nq, n = scores.shape
+    k_eff = min(k, n)
+    idx = np.zeros((nq, k), dtype=np.int64) - 1
+    val = np.full((nq, k), -np.inf)
+    for i in range(nq):
+        order = np.lexsort((np.arange(n), -scores[i]))[:k_eff]
+        idx[i, :k_eff] = order
+        val[i, :k_eff] = scores[i, order]
+    return idx, val
+
+
+def exact_topk(db, queries, k: int):
+    """Ground truth for recall: fp64 brute-force inner products on unquantized vectors."""
+    s = np.asarray(queries, dtype=np.float64) @ np.asarray(db, dtype=np.float64).T
+    return topk(s, k)

@@ -1,0 +1,418 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix (no GPU).
+
+Each test names what it pins.  The oracle is checked against closed forms, textbook
+tables, invariants and brute force -- never against a retyping of its own formulas.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate, stats
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ------------------------------------------------------------------ PRNG
+def test_splitmix64_published_vector(O):
+    want = [int(x, 16) for x in _golden_lines("splitmix64_seed0.txt")]
+    got = [int(v) for v in O.splitmix64(0, 0, np.arange(len(want)))]
+    assert got == want
+
+
+def test_uniform_open_interval_and_moments(O):
+    u = O.uniform01(123, 2, np.arange(200000))
+    assert u.min() > 0.0 and u.max() < 1.0
+    assert abs(u.mean() - 0.5) < 4 * math.sqrt(1 / 12 / len(u))
+    # KS against U(0,1)
+    assert stats.kstest(u, "uniform").pvalue > 1e-4
+
+
+def test_gaussian_projection_is_standard_normal(O):
+    S = O.gaussian_projection(256, 512, seed=7).astype(np.float64).ravel()
+    n = S.size
+    assert abs(S.mean()) < 4 / math.sqrt(n)
+    assert abs(S.var() - 1.0) < 4 * math.sqrt(2.0 / n)
+    assert stats.kstest(S, "norm").pvalue > 1e-4
+    # deterministic per seed, different across seeds
+    assert np.array_equal(O.gaussian_projection(8, 8, 7), O.gaussian_projection(8, 8, 7))
+    assert not np.array_equal(O.gaussian_projection(8, 8, 7), O.gaussian_projection(8, 8, 8))
+
+
+def test_rotation_signs_balanced(O):
+    D = O.rotation_signs(100000, seed=3)
+    assert set(np.unique(D)) == {-1.0, 1.0}
+    assert abs(D.mean()) < 4 / math.sqrt(D.size)
+
+
+# ------------------------------------------------------------------ codebook
+@pytest.mark.parametrize("d", [8, 64, 128, 1536])
+def test_marginal_density_normalised_and_unit_second_moment(O, d):
+    # independent numerical quadrature of the density: mass 1, E[X^2] = 1/d
+    f = lambda x: O.sphere_marginal_pdf(np.array([x]), d)[0]
+    lim = min(1.0, 12.0 / math.sqrt(d))
+    mass = integrate.quad(f, -lim, lim, limit=200, epsabs=1e-14)[0]
+    m2 = integrate.quad(lambda x: x * x * f(x), -lim, lim, limit=200, epsabs=1e-16)[0]
+    assert abs(mass - 1.0) < 1e-10
+    assert abs(m2 * d - 1.0) < 1e-8
+
+
+@pytest.mark.parametrize("d,bits", [(8, 2), (64, 2), (64, 3), (128, 2), (128, 3), (1536, 3)])
+def test_lloyd_conditions_by_independent_quadrature(O, d, bits):
+    cb = O.make_codebook(d, bits)
+    c, t = cb.c64, cb.t64
+    np.testing.assert_allclose(t, 0.5 * (c[:-1] + c[1:]), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(c, -c[::-1], rtol=0, atol=1e-14)      # symmetry
+    edges = np.concatenate(([-1.0], t, [1.0]))
+    f = lambda x: O.sphere_marginal_pdf(np.array([x]), d)[0]
+    for k in range(len(c)):
+        a, b = edges[k], edges[k + 1]
+        lo, hi = max(a, -14 / math.sqrt(d)), min(b, 14 / math.sqrt(d))
+        mass = integrate.quad(f, lo, hi, limit=400, epsabs=1e-15, epsrel=1e-13)[0]
+        mom = integrate.quad(lambda x: x * f(x), lo, hi, limit=400, epsabs=1e-17, epsrel=1e-13)[0]
+        assert abs(mom / mass - c[k]) * math.sqrt(d) < 1e-10
+
+
+@pytest.mark.parametrize("d", [8, 64, 128, 1536])
+def test_one_bit_closed_form(O, d):
+    # b = 1: c = +-E|X| = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2))
+    want = math.exp(math.lgamma(d / 2) - 0.5 * math.log(math.pi) - math.lgamma((d + 1) / 2))
+    cb = O.make_codebook(d, 1)
+    np.testing.assert_allclose(cb.c64, [-want, want], rtol=1e-11)  # lgamma cancellation at large d
+
+
+def test_large_d_limit_is_max_gaussian_table(O):
+    rows = _golden_lines("max1960_gaussian.txt")
+    d = 1 << 22
+    for row in rows:
+        lv, mse = row.split("|")
+        parts = lv.split()
+        bits, levels = int(parts[0]), [float(x) for x in parts[1:]]
+        cb = O.make_codebook(d, bits)
+        pos = cb.c64[len(cb.c64) // 2:] * math.sqrt(d)
+        np.testing.assert_allclose(pos, levels, atol=6e-4)
+        assert abs(cb.mse() * d - float(mse)) < 2e-4
+
+
+def test_codebook_matches_monte_carlo_conditional_means(O):
+    # uniform unit vectors in R^64: empirical cell means of one coordinate ~ centroids
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((200000, 64))
+    u = (x / np.linalg.norm(x, axis=1, keepdims=True))[:, 0]
+    cb = O.make_codebook(64, 2)
+    cell = np.searchsorted(cb.t64, u)
+    for k in range(4):
+        sel = u[cell == k]
+        assert abs(sel.mean() - cb.c64[k]) < 5 * sel.std() / math.sqrt(len(sel))
+
+
+def test_stored_codebook_is_fp16_rounding_with_midpoint_boundaries(O):
+    cb = O.make_codebook(128, 3)
+    np.testing.assert_array_equal(cb.c, cb.c64.astype(np.float16).astype(np.float64))
+    np.testing.assert_array_equal(cb.t, 0.5 * (cb.c[:-1] + cb.c[1:]))
+    # the midpoints are exact in fp32
+    np.testing.assert_array_equal(cb.t.astype(np.float32).astype(np.float64), cb.t)
+
+
+# ------------------------------------------------------------------ rotation / RoPE
+def test_hadamard_small_cases(O):
+    np.testing.assert_array_equal(O.hadamard(2), [[1, 1], [1, -1]])
+    np.testing.assert_array_equal(O.hadamard(4), [[1, 1, 1, 1], [1, -1, 1, -1],
+                                                  [1, 1, -1, -1], [1, -1, -1, 1]])
+    H = O.hadamard(64)
+    np.testing.assert_array_equal(H @ H.T, 64 * np.eye(64))
+
+
+@pytest.mark.parametrize("d", [64, 128, 1536])
+def test_rotation_orthogonal_and_norm_preserving(O, d):
+    P = O.rotation_matrix(d, seed=0)
+    np.testing.assert_allclose(P.T @ P, np.eye(d), atol=1e-13)
+    x = np.random.default_rng(0).standard_normal((50, d)) * 3
+    y = x @ P.T
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+    if d == 1536:   # block-diagonal of three 512 blocks
+        assert np.all(P[:512, 512:] == 0) and np.all(P[512:1024, 1024:] == 0)
+
+
+def test_rope_two_dim_is_plane_rotation(O):
+    # d = 2: theta_0 = 1, so position p rotates by p radians
+    x = np.array([[0.3, -1.7]])
+    for p in [0, 1, 5, 131071]:
+        c, s = math.cos(p), math.sin(p)
+        want = np.array([0.3 * c + 1.7 * s, 0.3 * s - 1.7 * c])
+        np.testing.assert_allclose(O.rope(x, [p], 10000.0)[0], want, atol=1e-12)
+
+
+def test_rope_half_split_pairs(O):
+    # d = 4, base 100: pair (0, 2) at angle p, pair (1, 3) at angle p / 10
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    p = 3.0
+    a0, a1 = p, p / 10.0
+    want = [1 * math.cos(a0) - 3 * math.sin(a0), 2 * math.cos(a1) - 4 * math.sin(a1),
+            1 * math.sin(a0) + 3 * math.cos(a0), 2 * math.sin(a1) + 4 * math.cos(a1)]
+    np.testing.assert_allclose(O.rope(x, [p], 100.0)[0], want, atol=1e-14)
+
+
+def test_rope_relative_position_and_rotation_invariance(O):
+    # <R_i q, R_j k> = <q, R_{j-i} k>   and   <Pi R_i q, Pi R_j k> = <R_i q, R_j k>
+    rng = np.random.default_rng(5)
+    d = 128
+    P = O.rotation_matrix(d, seed=11)
+    for (i, j) in [(0, 7), (1000, 1000), (12345, 131071), (131071, 3)]:
+        q, k = rng.standard_normal(d), rng.standard_normal(d) * 5
+        a = O.rope(q[None], [i], 500000.0)[0] @ O.rope(k[None], [j], 500000.0)[0]
+        b = q @ O.rope(k[None], [j - i], 500000.0)[0]
+        c = (P @ O.rope(q[None], [i], 500000.0)[0]) @ (P @ O.rope(k[None], [j], 500000.0)[0])
+        assert abs(a - b) <= 1e-9 * (1 + abs(a))
+        assert abs(c - a) <= 1e-12 * (1 + np.linalg.norm(q) * np.linalg.norm(k))
+    np.testing.assert_array_equal(O.rope(np.ones((2, 8)), [0, 0], 10000.0), np.ones((2, 8)))
+
+
+# ------------------------------------------------------------------ encoder
+@pytest.mark.parametrize("bits", [1, 2, 3])
+def test_d8_exhaustive_codeword_search_equals_per_coordinate(O, bits):
+    # nearest point of the product codebook C^8, searched over all 2^(8b) code vectors
+    # (bits = 3 sampled over 4096 random code vectors plus the optimum), equals the
+    # per-coordinate brute-force codes the encoder produces.
+    codec = O.make_codec(8, bits, 0, 8, seed=2)
+    rng = np.random.default_rng(bits)
+    x = rng.standard_normal((6, 8))
+    enc = O.encode(x, codec, kind="db")
+    c = codec.cb_k.c
+    K = len(c)
+    if bits <= 2:
+        allcodes = np.array(list(itertools.product(range(K), repeat=8)))
+    else:
+        allcodes = np.concatenate([rng.integers(0, K, (4096, 8)), enc["codes"]])
+    for r in range(x.shape[0]):
+        dist = np.sum((enc["u"][r][None, :] - c[allcodes]) ** 2, axis=1)
+        best = allcodes[np.argmin(dist)]
+        assert np.array_equal(best, enc["codes"][r])
+        assert np.min(dist) == pytest.approx(np.sum((enc["u"][r] - c[enc["codes"][r]]) ** 2))
+
+
+def test_encode_mse_matches_codebook_mse(O):
+    codec = O.make_codec(128, 2, 3, 128, seed=0)
+    x = np.random.default_rng(9).standard_normal((4000, 128))
+    for kind, cb in (("db", codec.cb_k), ("value", codec.cb_v)):
+        enc = O.encode(x, codec, kind=kind)
+        err = np.sum((enc["u"] - cb.c[enc["codes"]]) ** 2, axis=1)
+        want = cb.mse() * 128
+        assert abs(err.mean() - want) < 5 * err.std() / math.sqrt(len(err)) + 2e-4
+
+
+def test_nearest_ties_go_to_larger_index(O):
+    c = np.array([-1.0, 0.0, 1.0])
+    got = O._nearest(np.array([-0.5, 0.5, -2.0, 0.25]), c)
+    np.testing.assert_array_equal(got, [1, 2, 0, 1])
+
+
+def test_zero_vector_and_fp16_saturation(O):
+    codec = O.make_codec(64, 2, 3, 64, seed=1)
+    x = np.zeros((1, 64))
+    enc = O.encode(x, codec, kind="key", positions=[5], rope_base=10000.0)
+    assert enc["n16"][0] == 0 and enc["rn16"][0] == 0
+    assert np.all(enc["bits"] == 1)                      # sign(0) -> bit 1
+    # code of u = 0: nearest stored centroid with ties up -> index 2 (first positive)
+    assert np.all(enc["codes"] == 2)
+    big = np.full((1, 64), 1e4)
+    enc = O.encode(big, codec, kind="value")
+    assert enc["n16"][0] == 65504.0 and enc["overflow"][0]
+
+
+def test_residual_is_against_fp16_norm(O):
+    codec = O.make_codec(64, 2, 0, 64, seed=4)
+    x = np.random.default_rng(2).standard_normal((10, 64)) * 7
+    enc = O.encode(x, codec, kind="db")
+    recon = enc["n16"][:, None] * codec.cb_k.c[enc["codes"]]
+    np.testing.assert_allclose(enc["r"], enc["y"] - recon, atol=1e-13)
+    np.testing.assert_allclose(enc["z"], enc["r"] @ codec.S.T, atol=1e-12)
+
+
+# ------------------------------------------------------------------ QJL estimator
+def test_qjl_estimator_unbiased_over_seeds(O):
+    # E_S[ ||r|| sqrt(pi/2)/m <S q, sign(S r)> ] = <q, r>, checked over 10^4 seeds
+    d = m = 64
+    rng = np.random.default_rng(0)
+    q, r = rng.standard_normal(d), rng.standard_normal(d)
+    est = np.empty(10000)
+    for s in range(est.size):
+        S = O.gaussian_projection(m, d, seed=1000 + s).astype(np.float64)
+        sgn = np.where(S @ r >= 0, 1.0, -1.0)
+        est[s] = np.linalg.norm(r) * math.sqrt(math.pi / 2) / m * ((S @ q) @ sgn)
+    err = est - q @ r
+    sigma = err.std()
+    assert abs(err.mean()) < 3 * sigma / math.sqrt(est.size)
+    # variance: ||r||^2/m ((pi/2)||q||^2 - (q . r_hat)^2)
+    rh = r / np.linalg.norm(r)
+    var = (r @ r) / m * (math.pi / 2 * (q @ q) - (q @ rh) ** 2)
+    assert abs(est.var() / var - 1.0) < 0.06
+
+
+def test_qjl_zero_residual_gives_exact_score(O):
+    codec = O.make_codec(64, 2, 3, 64, seed=0)
+    qr = np.random.default_rng(1).standard_normal(64)
+    kc = np.random.default_rng(2).integers(0, 4, (3, 64))
+    n16 = np.array([1.5, 2.0, 0.0])
+    s = O.estimate_scores(qr, codec.S @ qr, kc, n16, np.zeros(3), np.ones((3, 64)), codec)
+    np.testing.assert_allclose(s, n16 * (codec.cb_k.c[kc] @ qr), rtol=1e-14)
+
+
+# ------------------------------------------------------------------ attention
+def _fields_from_khat(O, codec, kcodes, n16, vcodes, vn16, bits=None):
+    B, H, T, d = kcodes.shape
+    return {"kcodes": kcodes, "n16": n16, "rn16": np.zeros((B, H, T)),
+            "bits": np.ones((B, H, T, codec.m)) if bits is None else bits,
+            "vcodes": vcodes, "vn16": vn16}
+
+
+def test_attend_reduces_to_textbook_softmax_attention(O):
+    # keys/values chosen on the codebook lattice with zero residual: the estimator is
+    # then exact and the oracle's attention must equal softmax(q K^T scale) V computed
+    # in the original (unrotated) coordinates, including RoPE on q and GQA mapping.
+    d, B, Hkv, Hq, T = 64, 2, 2, 4, 37
+    codec = O.make_codec(d, 2, 3, d, seed=3)
+    rng = np.random.default_rng(4)
+    kc = rng.integers(0, 4, (B, Hkv, T, d))
+    vc = rng.integers(0, 8, (B, Hkv, T, d))
+    n16 = rng.uniform(1, 20, (B, Hkv, T)).astype(np.float16).astype(np.float64)
+    vn16 = rng.uniform(1, 20, (B, Hkv, T)).astype(np.float16).astype(np.float64)
+    fields = _fields_from_khat(O, codec, kc, n16, vc, vn16)
+    q = rng.standard_normal((B, Hq, d))
+    q_pos, base = 900, 10000.0
+    out, scores = O.attend(fields, q, codec, q_pos=q_pos, rope_base=base, scale=0.0,
+                           kv_heads=Hkv, length=T)
+    P = codec.Pi
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            K = (n16[b, g][:, None] * codec.cb_k.c[kc[b, g]]) @ P        # back to original coords
+            V = (vn16[b, g][:, None] * codec.cb_v.c[vc[b, g]]) @ P
+            qq = O.rope(q[b, h][None], [q_pos], base)[0]
+            s = K @ qq
+            w = np.exp(s / math.sqrt(d) - np.max(s / math.sqrt(d)))
+            w /= w.sum()
+            np.testing.assert_allclose(scores[b, h], s, rtol=1e-11, atol=1e-11)
+            np.testing.assert_allclose(out[b, h], w @ V, rtol=1e-11, atol=1e-11)
+
+
+def test_attend_single_token_and_empty(O):
+    d = 64
+    codec = O.make_codec(d, 2, 3, d, seed=3)
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((1, d))
+    kenc = O.encode(x, codec, kind="key", positions=[0], rope_base=0.0)
+    venc = O.encode(x * 2, codec, kind="value")
+    fields = {"kcodes": kenc["codes"][None, None], "n16": kenc["n16"][None, None],
+              "rn16": kenc["rn16"][None, None], "bits": kenc["bits"][None, None],
+              "vcodes": venc["codes"][None, None], "vn16": venc["n16"][None, None]}
+    q = rng.standard_normal((1, 1, d))
+    out, _ = O.attend(fields, q, codec, q_pos=1, rope_base=0.0, scale=0.0, kv_heads=1, length=1)
+    vhat = codec.Pi.T @ (venc["n16"][0] * codec.cb_v.c[venc["codes"][0]])
+    np.testing.assert_allclose(out[0, 0], vhat, atol=1e-12)
+    out0, s0 = O.attend(fields, q, codec, q_pos=1, rope_base=0.0, scale=0.0, kv_heads=1, length=0)
+    assert np.all(out0 == 0) and s0.shape == (1, 1, 0)
+
+
+# ------------------------------------------------------------------ packed format
+def test_pack_handcrafted_bytes(O):
+    # d = 8, bits_k = 2, m = 8, bits_v = 3, one unit, capacity 33 (two value tiles)
+    desc = dict(batch=1, kv_heads=1, d=8, capacity=33, bits_k=2, bits_v=3, m=8)
+    kc = np.array([[[[0, 1, 2, 3, 3, 2, 1, 0]]]])
+    bits = np.array([[[[1, 0, 0, 0, 0, 0, 0, 1]]]])
+    vc = np.array([[[[7, 0, 1, 2, 3, 4, 5, 6]]]])
+    f = dict(kcodes=kc, bits=bits, n16=np.array([[[1.5]]]), rn16=np.array([[[0.25]]]),
+             vcodes=vc, vn16=np.array([[[2.0]]]))
+    img = O.pack_cache(desc, f, start_pos=32)
+    lay = O.cache_layout(1, 1, 8, 33, 2, 3, 8)
+    hdr = img[:16].view(np.uint32)
+    assert list(hdr) == [0x564B5154, 1, 0, 0]
+    assert list(img[16:44].view(np.int32)) == [1, 1, 8, 33, 2, 3, 8]
+    rec = img[lay["kbits"] + 32 * 3: lay["kbits"] + 33 * 3]
+    # plane 0 bits (code & 1): 0,1,0,1,1,0,1,0 -> 0b01011010 = 0x5A
+    # plane 1 bits (code >> 1): 0,0,1,1,1,1,0,0 -> 0b00111100 = 0x3C;  signs -> 0x81
+    assert list(rec) == [0x5A, 0x3C, 0x81]
+    norms = img[lay["knorm"] + 32 * 4: lay["knorm"] + 33 * 4].view(np.float16)
+    assert list(norms) == [1.5, 0.25]
+    # token 32 is slot 0 of tile 1: coordinate j word = its 3-bit code in bits 0..2
+    vt = img[lay["vcodes"] + 1 * 8 * 12: lay["vcodes"] + 2 * 8 * 12].reshape(8, 12)
+    assert list(vt[:, 0]) == [7, 0, 1, 2, 3, 4, 5, 6] and np.all(vt[:, 1:] == 0)
+    assert img[lay["vnorm"] + 64: lay["vnorm"] + 66].view(np.float16)[0] == 2.0
+    # tokens in slots 2 and 10 of tile 0: bits 6..8 and 30..32 (straddling bytes 0/1, 3/4)
+    desc0 = dict(desc)
+    f2 = dict(f, vcodes=np.array([[[[5] * 8]]]))
+    img0 = O.pack_cache(desc0, f2, start_pos=2)
+    img0 = O.pack_cache(desc0, f2, start_pos=10, image=img0)
+    w = img0[lay["vcodes"]: lay["vcodes"] + 12]
+    # code 5 = 0b101 at bit 6 -> byte0 bit6 set, byte1 bit0 set; at bit 30 -> byte3 bit6, byte4 bit0
+    assert list(w) == [0x40, 0x01, 0x00, 0x40, 0x01, 0, 0, 0, 0, 0, 0, 0]
+
+
+def test_pack_unpack_roundtrip(O):
+    rng = np.random.default_rng(3)
+    desc = dict(batch=2, kv_heads=3, d=64, capacity=100, bits_k=2, bits_v=3, m=64)
+    n = 70
+    f = dict(kcodes=rng.integers(0, 4, (2, 3, n, 64)), bits=rng.integers(0, 2, (2, 3, n, 64)),
+             n16=rng.uniform(0, 9, (2, 3, n)).astype(np.float16).astype(np.float64),
+             rn16=rng.uniform(0, 9, (2, 3, n)).astype(np.float16).astype(np.float64),
+             vcodes=rng.integers(0, 8, (2, 3, n, 64)),
+             vn16=rng.uniform(0, 9, (2, 3, n)).astype(np.float16).astype(np.float64))
+    img = O.pack_cache(desc, f, start_pos=5)
+    u = O.unpack_cache(img, desc, length=75)
+    for key in ("kcodes", "bits", "n16", "rn16", "vcodes", "vn16"):
+        np.testing.assert_array_equal(u[key][:, :, 5:], f[key])
+    assert u["magic"] == 0x564B5154 and u["version"] == 1
+
+
+def test_memory_arithmetic(O):
+    # record bytes: key = b_k d/8 + m/8 + 2 + 2, value = b_v d/8 + 2
+    lay = O.cache_layout(1, 1, 128, 1024, 2, 3, 128)
+    assert lay["kbytes"] + 4 == 52
+    lay = O.cache_layout(1, 1, 64, 1024, 2, 3, 64)
+    assert lay["kbytes"] + 4 == 28
+    # ESM-2 650M fp32 K+V at 1024 tokens (33 layers, 20 heads, head dim 64): 330 MiB
+    assert 2 * 33 * 1024 * 1280 * 4 == 346030080 == 330 * 2 ** 20
+
+
+# ------------------------------------------------------------------ search
+def test_topk_is_full_sort_with_lower_index_ties(O):
+    s = np.array([[0.5, 0.9, 0.5, 0.1, 0.9, 0.2]])
+    idx, val = O.topk(s, 4)
+    assert list(idx[0]) == [1, 4, 0, 2]
+    assert list(val[0]) == [0.9, 0.9, 0.5, 0.5]
+    rng = np.random.default_rng(0)
+    s = rng.standard_normal((5, 300))
+    idx, val = O.topk(s, 10)
+    for i in range(5):
+        np.testing.assert_array_equal(val[i], np.sort(s[i])[::-1][:10])
+
+
+def test_search_scores_match_attention_estimator_and_recall(O):
+    d = 128
+    codec = O.make_codec(d, 3, 0, d, seed=5)
+    rng = np.random.default_rng(6)
+    db = rng.standard_normal((3000, d))
+    db /= np.linalg.norm(db, axis=1, keepdims=True)
+    qs = rng.standard_normal((20, d))
+    qs /= np.linalg.norm(qs, axis=1, keepdims=True)
+    enc = O.encode(db, codec, kind="db")
+    fields = {"kcodes": enc["codes"], "n16": enc["n16"], "rn16": enc["rn16"], "bits": enc["bits"]}
+    s = O.search_scores(fields, qs, codec)
+    for i in (0, 7):
+        qr = codec.Pi @ qs[i]
+        want = O.estimate_scores(qr, codec.S @ qr, enc["codes"], enc["n16"], enc["rn16"],
+                                 enc["bits"], codec)
+        np.testing.assert_allclose(s[i], want, rtol=1e-12, atol=1e-13)
+    # the estimate tracks the exact inner product closely at 4 bits/coordinate
+    exact = qs @ db.T
+    assert np.sqrt(np.mean((s - exact) ** 2)) < 0.35 / math.sqrt(d)
+    idx, _ = O.topk(s, 10)
+    gt, _ = O.exact_topk(db, qs, 10)
+    recall1 = np.mean([gt[i, 0] in idx[i] for i in range(20)])
+    assert recall1 >= 0.8
