@@ -1,0 +1,187 @@
+/*
+ * tq.h -- C ABI of libtq: a packed KV-cache codec (RoPE, randomized Hadamard rotation,
+ * Lloyd-Max scalar codes, 1-bit QJL residual sketch), decode attention over the packed
+ * cache and inner-product top-k search over packed vectors, for AMD MI355X (gfx950).
+ *
+ * Sources (page titles; the section or passage on each page):
+ *   [TurboESM]   "TurboESM: Ultra-Efficient 3-Bit KV Cache Quantization for Protein
+ *                Language Models with Orthogonal Rotation and QJL Correction", technical
+ *                summary: 2.A RoPE before the orthogonal rotation Pi and the invariance of
+ *                (Pi R_i q)^T (Pi R_j k); 2.C Lloyd-Max look-up tables; 2.D 1-bit residual
+ *                correction; 2.E one fused decode pass (dequantize, correct, inverse
+ *                rotation, online softmax).
+ *   [TurboQuant] news summary of the TurboQuant post: "Etape 1" random rotation then a
+ *                per-coordinate scalar quantizer; "Etape 2"/"QJL" sign bits of a
+ *                Johnson-Lindenstrauss projection of the residual with an estimator that
+ *                pairs a full-precision query with the 1-bit data; vector search section
+ *                (top-k by estimated inner product, recall 1@k).
+ *   [NSNQuant]   technical summary, section 2: randomized Hadamard transform.
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller allocates and frees every buffer (host and device).  The
+ *     library never allocates, keeps no global state and is reentrant.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Device work is
+ *     enqueued asynchronously on it; buffers must stay valid until it completes.
+ *   - Errors: every argument, shape and capacity check runs on the host before anything
+ *     is enqueued; a failing check returns its status and enqueues nothing.  A failed
+ *     kernel launch returns TQ_EDEVICE.  No C++ exception crosses this interface.
+ *   - A norm too large for fp16 is stored as 65504 and sets bit 0 of the cache header's
+ *     flags word (byte offset 8), which stays set until tq_cache_init.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = 1,        /* NULL pointer, negative size, inconsistent shapes */
+  TQ_EUNSUPPORTED = 2,  /* valid but not implemented: d, bits or m outside the supported set */
+  TQ_ECAPACITY = 3,     /* start_pos + n_new or length beyond the cache capacity */
+  TQ_ENOSPACE = 4,      /* output or workspace buffer smaller than required */
+  TQ_EDEVICE = 5        /* a HIP launch or runtime call failed */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
+
+/* Codec parameters.  d: vector dimension; bits_k: scalar bits of keys / database
+ * vectors (1..4); bits_v: scalar bits of values (0 = keys only, else 1..4); m: QJL rows
+ * (0 = no residual sketch, else a multiple of 32, at most 2048); seed: draws the rotation
+ * signs D and the Gaussian projection S. */
+typedef struct {
+  int32_t d, bits_k, bits_v, m;
+  uint64_t seed;
+} tq_codec_desc;
+
+/* Packed cache shape: `batch` x `kv_heads` units of `capacity` token slots each. */
+typedef struct {
+  int32_t batch, kv_heads, d, capacity, bits_k, bits_v, m;
+} tq_cache_desc;
+
+typedef void *tq_stream_t; /* hipStream_t */
+
+/* Version string of the library and of the packed format ("libtq <x.y> format 1"). */
+const char *tq_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char *tq_status_str(tq_status s);
+
+/* Lloyd-Max codebook ([TurboQuant] "Etape 1" and the reader comment on Lloyd-Max
+ * boundaries; [TurboESM] 2.C) for one coordinate of a uniformly random unit vector in
+ * R^d, density proportional to (1 - x^2)^((d-3)/2) on [-1, 1], computed in fp64 on the
+ * host.  The codec stores each centroid rounded to fp16; `centroids` (2^bits values,
+ * ascending) receives those stored values and `bounds` (2^bits - 1 values) the exact
+ * midpoints between consecutive stored centroids, which are the encoder's decision
+ * boundaries.  Supported: 8 <= d <= 4096, 1 <= bits <= 4.  Host only, synchronous. */
+tq_status tq_make_codebook(int32_t d, int32_t bits, float *centroids, float *bounds);
+
+/* Same computation, returning the fp64 Lloyd-Max centroids and boundaries before the
+ * fp16 rounding (for checking the iteration itself). */
+tq_status tq_make_codebook_f64(int32_t d, int32_t bits, double *centroids, double *bounds);
+
+/* Size in bytes of the codec table built by tq_codec_build (0 if the desc is invalid). */
+size_t tq_codec_bytes(const tq_codec_desc *desc);
+
+/* Build the codec table on the host into `host_out` (tq_codec_bytes(desc) bytes): key
+ * and value codebooks, the rotation signs D_j and the m x d Gaussian projection S, all
+ * drawn from desc->seed.  The caller copies the table to device memory once and passes
+ * that copy as `codec_dev` to the device entry points; it must have been built with the
+ * same d, bits_k, bits_v and m as the cache it is used with.
+ * Draws: SplitMix64 (Steele, Lea & Flood 2014) as a counter generator, output k of the
+ * generator seeded with `seed` being mix(seed + (k + 1) * 0x9E3779B97F4A7C15); D_j uses
+ * k = 2^32 + j and is -1 when the top bit is set; S_ij is the Box-Muller cosine branch
+ * with uniforms from k = 2^33 + 2(i d + j) and the next k, in fp64, rounded to fp32. */
+tq_status tq_codec_build(const tq_codec_desc *desc, void *host_out, size_t bytes);
+
+/* Size in bytes of a packed cache (header + key bits + key norms [+ value codes + value
+ * norms]), format version 1:
+ *   header  256 B: u32 magic 0x564B5154, u32 version 1, u32 flags, u32 0, then the desc.
+ *   Kbits   [batch][kv_heads][capacity][(bits_k d + m)/8]: bit p of each key code as
+ *           plane p (coordinate j at byte j/8, bit j%8), planes p = 0..bits_k-1, then the
+ *           m QJL sign bits.
+ *   Knorm   [batch][kv_heads][capacity] x {fp16 ||y||, fp16 ||r||}.
+ *   Vcodes  [batch][kv_heads][ceil(capacity/32)][d][4 bits_v bytes]: per 32-token tile and
+ *           coordinate, token i's value code in bits [bits_v i, bits_v (i+1)) of a
+ *           little-endian integer.
+ *   Vnorm   [batch][kv_heads][capacity] fp16 ||y||.
+ * Regions start at multiples of 256 bytes.  Returns 0 if the desc is invalid. */
+size_t tq_cache_bytes(const tq_cache_desc *desc);
+
+/* Write the cache header (magic, version, desc) and clear the flags word.  Token slots
+ * are not touched.  Enqueued on `stream`. */
+tq_status tq_cache_init(const tq_cache_desc *desc, void *cache_dev, tq_stream_t stream);
+
+/* Append tokens [start_pos, start_pos + n_new) of every (batch, kv-head) unit to the
+ * packed cache ([TurboESM] 2.A-2.D; [TurboQuant] "Etape 1", "Etape 2"):
+ *   keys:   y = Pi RoPE(k, pos) with Pi = blockdiag(H_B) diag(D) / sqrt(B) (H_B Sylvester,
+ *           B the largest power of two dividing d), RoPE half-split with
+ *           theta_j = rope_base^(-2j/d) (rope_base == 0: none); n = ||y||; code_j = number
+ *           of boundaries t with y_j/n >= t; r = y - fp16(n) c[code]; QJL bit i =
+ *           [(S r)_i >= 0]; stored: planes, sign bits, fp16 n, fp16 ||r||.
+ *   values: y = Pi v (no RoPE), codes with the value codebook, fp16 n.
+ * k, v: device arrays [batch][kv_heads][n_new][d] of `dtype`, contiguous; v must be NULL
+ * iff desc->bits_v == 0.  n_new == 0 is a no-op.  Writes never touch other slots. */
+tq_status tq_quantize_kv(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
+                         const void *k, const void *v, tq_dtype dtype, int32_t start_pos,
+                         int32_t n_new, float rope_base, tq_stream_t stream);
+
+/* Workspace bytes tq_decode_attend needs for this shape (splits chosen by the library). */
+size_t tq_decode_workspace_bytes(const tq_cache_desc *desc, int32_t q_heads, int32_t length);
+
+/* Split count tq_decode_attend uses for this shape (for inspection). */
+int32_t tq_decode_splits(const tq_cache_desc *desc, int32_t q_heads, int32_t length);
+
+/* GQA decode attention of one query per (batch, q-head) over cached tokens [0, length)
+ * ([TurboESM] 2.A and 2.E; [TurboQuant] QJL estimator):
+ *   q_rot = Pi RoPE(q, q_pos); sq = S q_rot;
+ *   score_t = n_t <q_rot, c_k[code_t]> + ||r_t|| sqrt(pi/2)/m <sq, 2 bits_t - 1>;
+ *   p = softmax(scale * score) (scale == 0: 1/sqrt(d)), computed as an online softmax
+ *   over token splits; o_rot = sum_t p_t n_v,t c_v[vcode_t]; out = Pi^T o_rot.
+ * q-head h reads kv-head floor(h * kv_heads / q_heads); q_heads must be a multiple of
+ * kv_heads.  q: device [batch][q_heads][d] of `dtype`.  out: device fp32
+ * [batch][q_heads][d].  scores: NULL or device fp32 [batch][q_heads][length], receiving
+ * the unscaled score_t.  length == 0 writes out = 0.  ws: device workspace of at least
+ * tq_decode_workspace_bytes bytes, overwritten. */
+tq_status tq_decode_attend(const tq_cache_desc *desc, const void *codec_dev,
+                           const void *cache_dev, int32_t length, const void *q,
+                           tq_dtype dtype, int32_t q_heads, int32_t q_pos, float rope_base,
+                           float scale, float *out, float *scores, void *ws, size_t ws_bytes,
+                           tq_stream_t stream);
+
+/* As tq_decode_attend with an explicit token split count (0 = the library's choice);
+ * the workspace must then be tq_decode_workspace_bytes_splits(desc, q_heads, splits). */
+size_t tq_decode_workspace_bytes_splits(const tq_cache_desc *desc, int32_t q_heads,
+                                        int32_t splits);
+tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_dev,
+                                  const void *cache_dev, int32_t length, const void *q,
+                                  tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                                  float rope_base, float scale, float *out, float *scores,
+                                  int32_t splits, void *ws, size_t ws_bytes,
+                                  tq_stream_t stream);
+
+/* Workspace bytes tq_search_topk needs. */
+size_t tq_search_workspace_bytes(const tq_cache_desc *db, int32_t n_db, int32_t nq, int32_t k);
+
+/* Inner-product top-k search over packed database vectors ([TurboQuant] vector search:
+ * top-k by the estimated inner product).  The database is a cache with batch =
+ * kv_heads = 1 and bits_v = 0 filled by tq_quantize_kv (rope_base = 0, v = NULL), slots
+ * [0, n_db).  For each query (device fp32 [nq][d]) the score of vector x is the same
+ * estimator as in tq_decode_attend (with q_rot = Pi q, no RoPE).  idx_out (device int32
+ * [nq][k]) and score_out (device fp32 [nq][k]) receive the k best in descending score,
+ * equal scores ordered by lower index; if k > n_db the tail is idx -1, score -inf.
+ * 1 <= k <= 64. */
+tq_status tq_search_topk(const tq_cache_desc *db, const void *codec_dev, const void *db_cache,
+                         int32_t n_db, const float *queries, int32_t nq, int32_t k,
+                         int32_t *idx_out, float *score_out, void *ws, size_t ws_bytes,
+                         tq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

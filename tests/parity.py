@@ -1,0 +1,124 @@
+"""Parity helpers shared by the GPU tests: run the library and the oracle on the same
+seeded inputs and compare under the codec's parity rule.
+
+Codes and bits must equal the oracle's.  The only mismatches excused are
+  * a scalar code whose oracle coordinate u_j lies within 1e-6 of a decision boundary,
+  * a QJL bit whose oracle |z_i| / ||r|| <= 1e-6,
+  * an fp16 norm whose fp64 value lies within 1e-6 (relative) of an fp16 rounding midpoint,
+and these must number at most 1e-6 of all codes.  A token with an excused scalar-code or
+norm mismatch has a different residual on the two sides, so its residual norm and QJL
+bits are compared only when its codes and norm agree.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from oracle import tq_oracle as O
+from vector_quantization_rope_amd import tq
+
+MARGIN = 1e-6
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def oracle_encode_unitwise(K, V, codec, positions, rope_base):
+    """K, V: fp64 [B, H, T, d] -> dict of oracle fields for all units."""
+    B, H, T, d = K.shape
+    ke = O.encode(K.reshape(-1, d), codec, kind="key",
+                  positions=np.tile(positions, B * H), rope_base=rope_base)
+    out = {
+        "kcodes": ke["codes"].reshape(B, H, T, d), "n16": ke["n16"].reshape(B, H, T),
+        "rn16": ke["rn16"].reshape(B, H, T), "bits": ke["bits"].reshape(B, H, T, -1),
+        "ku": ke["u"].reshape(B, H, T, d), "kn": ke["n"].reshape(B, H, T),
+        "krn": ke["rn"].reshape(B, H, T), "kz": ke["z"].reshape(B, H, T, -1),
+        "overflow": ke["overflow"].reshape(B, H, T),
+    }
+    if V is not None:
+        ve = O.encode(V.reshape(-1, d), codec, kind="value")
+        out.update(vcodes=ve["codes"].reshape(B, H, T, d), vn16=ve["n16"].reshape(B, H, T),
+                   vu=ve["u"].reshape(B, H, T, d), vn=ve["n"].reshape(B, H, T))
+        out["overflow"] = out["overflow"] | ve["overflow"].reshape(B, H, T)
+    return out
+
+
+def _near_boundary(u, t):
+    return np.min(np.abs(u[..., None] - t), axis=-1) <= MARGIN
+
+
+def _near_fp16_midpoint(x):
+    """fp64 norm within 1e-6 relative of a midpoint between adjacent fp16 values."""
+    x = np.asarray(x, dtype=np.float64)
+    h = x.astype(np.float16).astype(np.float64)
+    up = np.nextafter(h.astype(np.float16), np.float16(np.inf)).astype(np.float64)
+    dn = np.nextafter(h.astype(np.float16), np.float16(-np.inf)).astype(np.float64)
+    mids = np.stack([(h + up) / 2, (h + dn) / 2], -1)
+    return np.min(np.abs(mids - x[..., None]), -1) <= MARGIN * np.maximum(np.abs(x), 1e-30)
+
+
+def compare_codes(gpu: dict, orc: dict, codec, report=None):
+    """gpu: unpacked GPU cache fields for the same tokens; orc: oracle_encode_unitwise.
+    Returns a dict of counts; raises AssertionError on any non-excused mismatch."""
+    cbk = codec.cb_k
+    res = {"codes": 0, "excused": 0, "dependent": 0}
+    kc_bad = gpu["kcodes"] != orc["kcodes"]
+    res["codes"] += orc["kcodes"].size
+    if np.any(kc_bad):
+        ok = _near_boundary(orc["ku"], cbk.t)
+        assert np.all(ok[kc_bad]), f"{int(np.sum(kc_bad & ~ok))} key codes differ away from a boundary"
+        res["excused"] += int(np.sum(kc_bad))
+    n_bad = gpu["n16"] != orc["n16"]
+    if np.any(n_bad):
+        ok = _near_fp16_midpoint(orc["kn"])
+        assert np.all(ok[n_bad]), f"{int(np.sum(n_bad & ~ok))} key norms differ away from an fp16 midpoint"
+        res["excused"] += int(np.sum(n_bad))
+    # tokens whose residual is defined the same way on both sides
+    same_tok = ~(np.any(kc_bad, axis=-1) | n_bad)
+    if codec.m > 0:
+        b_bad = (gpu["bits"] != orc["bits"]) & same_tok[..., None]
+        res["codes"] += orc["bits"].size
+        if np.any(b_bad):
+            scale = np.where(orc["krn"] > 0, orc["krn"], 1.0)[..., None]
+            ok = np.abs(orc["kz"]) / scale <= MARGIN
+            assert np.all(ok[b_bad]), f"{int(np.sum(b_bad & ~ok))} QJL bits differ away from zero"
+            res["excused"] += int(np.sum(b_bad))
+        rn_bad = (gpu["rn16"] != orc["rn16"]) & same_tok
+        if np.any(rn_bad):
+            ok = _near_fp16_midpoint(orc["krn"])
+            assert np.all(ok[rn_bad]), f"{int(np.sum(rn_bad & ~ok))} residual norms differ"
+            res["excused"] += int(np.sum(rn_bad))
+        res["dependent"] += int(np.sum((gpu["bits"] != orc["bits"]) & ~same_tok[..., None]))
+    if "vcodes" in orc:
+        cbv = codec.cb_v
+        vc_bad = gpu["vcodes"] != orc["vcodes"]
+        res["codes"] += orc["vcodes"].size
+        if np.any(vc_bad):
+            ok = _near_boundary(orc["vu"], cbv.t)
+            assert np.all(ok[vc_bad]), f"{int(np.sum(vc_bad & ~ok))} value codes differ away from a boundary"
+            res["excused"] += int(np.sum(vc_bad))
+        vn_bad = gpu["vn16"] != orc["vn16"]
+        if np.any(vn_bad):
+            ok = _near_fp16_midpoint(orc["vn"])
+            assert np.all(ok[vn_bad]), f"{int(np.sum(vn_bad & ~ok))} value norms differ"
+            res["excused"] += int(np.sum(vn_bad))
+    assert res["excused"] <= MARGIN * res["codes"], f"excused mismatches over budget: {res}"
+    if report is not None:
+        report.update(res)
+    return res
+
+
+def gpu_fields(cache: "tq.PackedCache", length: int) -> dict:
+    img = cache.buf.to("cpu").numpy()
+    return O.unpack_cache(img, cache.desc.as_dict(), length)
+
+
+def oracle_image(desc: dict, fields: dict, start=0) -> np.ndarray:
+    return O.pack_cache(desc, fields, start_pos=start)
+
+
+def max_abs(a, b) -> float:
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the same seeded
+inputs.
+
+  * codes, bit planes, QJL bits and fp16 norms: bit-exact except coordinates within 1e-6
+    of a decision boundary (see tests/parity.py), at most 1e-6 of all codes;
+  * decode attention: max-abs 2e-3 against the oracle attending over the same packed cache
+    (the oracle's own packing, uploaded), and end-to-end against oracle encode + attend;
+  * search: top-10 identical up to swaps of near-equal scores (|diff| <= 1e-6).
+Small cases span several tiles and ragged tails; the full-size cases use the launch
+configuration bench.py times and compare sampled (batch, kv-head) units.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import tq_oracle as O
+from vector_quantization_rope_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from vector_quantization_rope_amd import tq as _tq
+    return _tq
+
+
+@pytest.fixture(scope="module")
+def P():
+    import parity
+    return parity
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def build(tq, w, K, V, chunks=None, capacity=None):
+    B, H, T, d = K.shape
+    codec = tq.Codec(d, w.bits_k, w.bits_v, w.m, seed=0)
+    cache = tq.PackedCache(B, H, d, capacity or T, w.bits_k, w.bits_v, w.m)
+    chunks = chunks or [(0, T)]
+    for s, e in chunks:
+        tq.quantize_kv(cache.desc, codec.dev, cache.buf, K[:, :, s:e].contiguous(),
+                       V[:, :, s:e].contiguous() if V is not None else None, s, w.rope_base)
+    return codec, cache
+
+
+def decode(tq, codec, cache, q, length, q_pos, rope_base, splits=0, want_scores=True):
+    B, Hq, d = q.shape
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    scores = torch.empty((B, Hq, max(1, length)), dtype=torch.float32, device="cuda") if want_scores else None
+    nws = tq.decode_workspace_bytes(cache.desc, Hq, length, splits=splits)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    tq.decode_attend(cache.desc, codec.dev, cache.buf, length, q, q_pos, rope_base, out,
+                     scores=scores, ws=ws, splits=splits)
+    torch.cuda.synchronize()
+    return out, scores
+
+
+def oracle_side(P, w, K, V, q, length, codec_o):
+    Kd, Vd = P.to_f64(K), P.to_f64(V)
+    T = Kd.shape[2]
+    fields = P.oracle_encode_unitwise(Kd, Vd, codec_o, np.arange(T), w.rope_base)
+    out, scores = O.attend(fields, P.to_f64(q), codec_o, q_pos=w.q_pos, rope_base=w.rope_base,
+                           scale=0.0, kv_heads=K.shape[1], length=length)
+    return fields, out, scores
+
+
+def check_case(tq, P, w, K, V, q, chunks=None, splits=0, label=""):
+    """Full check of one small case: codes, decode over the oracle's cache, end to end."""
+    B, H, T, d = K.shape
+    say(f"[case] {label} B={B} Hkv={H} Hq={q.shape[1]} T={T} d={d} chunks={chunks} splits={splits}")
+    codec, cache = build(tq, w, K.cuda(), V.cuda(), chunks)
+    codec_o = O.make_codec(d, w.bits_k, w.bits_v, w.m, 0)
+    fields, out_o, sc_o = oracle_side(P, w, K, V, q, T, codec_o)
+    rep = {}
+    P.compare_codes(P.gpu_fields(cache, T), fields, codec_o, rep)
+    # decode over the oracle's packed cache
+    img = P.oracle_image(cache.desc.as_dict(), fields)
+    ocache = tq.PackedCache(B, H, d, T, w.bits_k, w.bits_v, w.m)
+    ocache.buf.copy_(torch.from_numpy(img))
+    out, sc = decode(tq, codec, ocache, q.cuda(), T, w.q_pos, w.rope_base, splits=splits)
+    e_out = P.max_abs(out.cpu().numpy(), out_o)
+    e_sc = P.max_abs(sc.cpu().numpy()[:, :, :T], sc_o)
+    # end to end: the GPU's own cache
+    out2, _ = decode(tq, codec, cache, q.cuda(), T, w.q_pos, w.rope_base, splits=splits, want_scores=False)
+    e_e2e = P.max_abs(out2.cpu().numpy(), out_o)
+    say(f"    codes {rep} | out {e_out:.2e} scores {e_sc:.2e} e2e {e_e2e:.2e}")
+    assert e_out <= TOL and e_sc <= TOL
+    if rep["excused"] == 0:
+        assert e_e2e <= TOL
+    return rep
+
+
+# ------------------------------------------------------------------ small cases
+def test_single_head_workload_full(tq, P):
+    """Single head, d 128, 1024 fp32 N(0,1) keys/values with 4 channels x20, no RoPE."""
+    w = W.SINGLE_HEAD
+    K, V = W.gen_kv(w)
+    q = W.gen_q(w)
+    check_case(tq, P, w, K, V, q, label="single_head")
+
+
+@pytest.mark.parametrize("d,G,T,chunks", [
+    (128, 4, 1000, [(0, 100), (100, 237), (237, 1000)]),
+    (128, 8, 777, None),
+    (64, 1, 333, [(0, 31), (31, 64), (64, 333)]),
+    (64, 4, 2100, None),
+])
+def test_gqa_ragged_and_appends(tq, P, d, G, T, chunks):
+    w = W.LONG_CONTEXT.scaled(batch=2, kv_heads=2, q_heads=2 * G, d=d, m=d, context=T)
+    K, V = W.gen_kv(w)
+    q = W.gen_q(w)
+    check_case(tq, P, w, K, V, q, chunks=chunks, label=f"gqa d{d} G{G}")
+
+
+@pytest.mark.parametrize("bk,bv,m", [(1, 2, 64), (3, 4, 128), (4, 1, 32), (2, 3, 0)])
+def test_other_bit_widths(tq, P, bk, bv, m):
+    w = W.LLAMA3_8B.scaled(batch=1, kv_heads=2, q_heads=4, context=300, bits_k=bk, bits_v=bv, m=m)
+    K, V = W.gen_kv(w)
+    q = W.gen_q(w)
+    check_case(tq, P, w, K, V, q, label=f"bits k{bk} v{bv} m{m}")
+
+
+def test_split_counts_and_determinism(tq, P):
+    w = W.LLAMA3_8B.scaled(batch=1, kv_heads=2, q_heads=8, context=1500)
+    K, V = W.gen_kv(w)
+    q = W.gen_q(w)
+    codec, cache = build(tq, w, K.cuda(), V.cuda())
+    codec_o = O.make_codec(w.d, w.bits_k, w.bits_v, w.m, 0)
+    fields, out_o, _ = oracle_side(P, w, K, V, q, 1500, codec_o)
+    outs = []
+    for s in (1, 3, 7, 0):
+        out, _ = decode(tq, codec, cache, q.cuda(), 1500, w.q_pos, w.rope_base, splits=s)
+        outs.append(out.cpu().numpy())
+        assert P.max_abs(outs[-1], out_o) <= TOL
+    out_again, _ = decode(tq, codec, cache, q.cuda(), 1500, w.q_pos, w.rope_base, splits=0)
+    assert np.array_equal(out_again.cpu().numpy(), outs[-1])
+    # quantize is deterministic too
+    _, cache2 = build(tq, w, K.cuda(), V.cuda())
+    assert torch.equal(cache.buf, cache2.buf)
+
+
+def test_edge_cases_zero_overflow_empty(tq, P):
+    w = W.LLAMA3_8B.scaled(batch=1, kv_heads=1, q_heads=2, context=64)
+    K, V = W.gen_kv(w)
+    K = K.float()
+    V = V.float()
+    K[0, 0, 5] = 0.0
+    V[0, 0, 6] = 0.0
+    K[0, 0, 9] = 3.0e4          # norm far beyond fp16 range
+    w32 = w.scaled(dtype="f32")
+    q = W.gen_q(w32)
+    codec, cache = build(tq, w32, K.cuda(), V.cuda())
+    codec_o = O.make_codec(w.d, w.bits_k, w.bits_v, w.m, 0)
+    fields = P.oracle_encode_unitwise(P.to_f64(K), P.to_f64(V), codec_o, np.arange(64), w.rope_base)
+    g = P.gpu_fields(cache, 64)
+    P.compare_codes(g, fields, codec_o)
+    assert g["flags"] & 1, "fp16 norm saturation must set the header flag"
+    assert g["n16"][0, 0, 9] == 65504.0
+    assert np.all(g["bits"][0, 0, 5] == 1) and g["n16"][0, 0, 5] == 0 and g["rn16"][0, 0, 5] == 0
+    # n_new = 0 is a no-op; length = 0 gives zeros
+    before = cache.buf.clone()
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, K[:, :, :0].cuda(), V[:, :, :0].cuda(), 3, w.rope_base)
+    torch.cuda.synchronize()
+    assert torch.equal(before, cache.buf)
+    out, _ = decode(tq, codec, cache, q.cuda(), 0, 0, w.rope_base, want_scores=False)
+    assert torch.all(out == 0)
+    # a single cached token: out = Pi^T (n_v c_v[code]) of that token (oracle)
+    out1, _ = decode(tq, codec, cache, q.cuda(), 1, 1, w.rope_base)
+    o1, _ = O.attend(fields, P.to_f64(q), codec_o, q_pos=1, rope_base=w.rope_base, scale=0.0,
+                     kv_heads=1, length=1)
+    assert P.max_abs(out1.cpu().numpy(), o1) <= TOL
+    # cache_init clears the flag
+    tq.cache_init(cache.desc, cache.buf)
+    torch.cuda.synchronize()
+    assert P.gpu_fields(cache, 0)["flags"] == 0
+
+
+def test_esm2_all_layers(tq, P):
+    """ESM-2-650M-shaped: 33 layers x 20 heads x d 64, 1024 tokens, bf16 Student-t, RoPE."""
+    w = W.ESM2_650M
+    codec_o = O.make_codec(w.d, w.bits_k, w.bits_v, w.m, 0)
+    tot = {"codes": 0, "excused": 0, "dependent": 0}
+    worst = 0.0
+    for layer in range(w.layers):
+        K, V = W.gen_kv(w, layer)
+        q = W.gen_q(w, layer)
+        codec, cache = build(tq, w, K.cuda(), V.cuda())
+        fields, out_o, _ = oracle_side(P, w, K, V, q, w.context, codec_o)
+        rep = P.compare_codes(P.gpu_fields(cache, w.context), fields, codec_o)
+        for kk in tot:
+            tot[kk] += rep[kk]
+        out, _ = decode(tq, codec, cache, q.cuda(), w.context, w.q_pos, w.rope_base, want_scores=False)
+        worst = max(worst, P.max_abs(out.cpu().numpy(), out_o))
+    say(f"[esm2] codes {tot} worst e2e out {worst:.2e}")
+    assert tot["excused"] <= 1e-6 * tot["codes"]
+    assert worst <= TOL
+
+
+# ------------------------------------------------------------------ search
+def test_search_small(tq, P):
+    w = W.VECTOR_SEARCH.scaled(n_db=3000, nq=16)
+    db, qs = W.gen_search(w)
+    codec = tq.Codec(w.d, w.bits, 0, w.m, seed=0)
+    cache = tq.PackedCache(1, 1, w.d, w.n_db, w.bits, 0, w.m)
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, db.cuda()[None, None], None, 0, 0.0)
+    codec_o = O.make_codec(w.d, w.bits, 0, w.m, 0)
+    enc = O.encode(db.double().numpy(), codec_o, kind="db")
+    g = O.unpack_cache(cache.buf.cpu().numpy(), cache.desc.as_dict(), w.n_db)
+    orc = {"kcodes": enc["codes"][None, None], "n16": enc["n16"][None, None], "rn16": enc["rn16"][None, None],
+           "bits": enc["bits"][None, None], "ku": enc["u"][None, None], "kn": enc["n"][None, None],
+           "krn": enc["rn"][None, None], "kz": enc["z"][None, None]}
+    rep = P.compare_codes(g, orc, codec_o)
+    say(f"[search db] {rep}")
+    # search over the oracle's packed database
+    fields = {"kcodes": enc["codes"], "n16": enc["n16"], "rn16": enc["rn16"], "bits": enc["bits"]}
+    img = O.pack_cache(cache.desc.as_dict(), {k: v[None, None] for k, v in fields.items()})
+    ocache = tq.PackedCache(1, 1, w.d, w.n_db, w.bits, 0, w.m)
+    ocache.buf.copy_(torch.from_numpy(img))
+    s_o = O.search_scores(fields, qs.double().numpy(), codec_o)
+    idx_o, val_o = O.topk(s_o, w.k)
+    idx = torch.empty((w.nq, w.k), dtype=torch.int32, device="cuda")
+    val = torch.empty((w.nq, w.k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tq.search_workspace_bytes(ocache.desc, w.n_db, w.nq, w.k), dtype=torch.uint8, device="cuda")
+    tq.search_topk(ocache.desc, codec.dev, ocache.buf, w.n_db, qs.cuda(), w.k, idx, val, ws)
+    torch.cuda.synchronize()
+    check_topk(idx.cpu().numpy(), val.cpu().numpy(), s_o, idx_o, val_o)
+
+
+def check_topk(idx, val, s_o, idx_o, val_o, tie=1e-6, stol=1e-4):
+    """Top-k identical except swaps among entries whose oracle scores differ by <= tie."""
+    nq, k = idx.shape
+    for i in range(nq):
+        # returned scores agree with the oracle's score of the returned index
+        np.testing.assert_allclose(val[i], s_o[i, idx[i]], atol=stol)
+        if np.array_equal(idx[i], idx_o[i]):
+            continue
+        kth = val_o[i, -1]
+        for r in range(k):
+            if idx[i, r] != idx_o[i, r]:
+                # the two entries at this rank must be near-tied in the oracle's scores
+                assert abs(s_o[i, idx[i, r]] - val_o[i, r]) <= tie, (i, r)
+        # any index outside the oracle's list must tie with its k-th score
+        for j in set(idx[i]) - set(idx_o[i]):
+            assert abs(s_o[i, j] - kth) <= tie

@@ -1,0 +1,64 @@
+// Internal declarations shared by the host part (tq_host.cpp) and the device part
+// (tq_device.hip) of libtq.  Not installed; the public interface is include/tq.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr uint32_t kCacheMagic = 0x564B5154u;  // "TQKV"
+constexpr uint32_t kCodecMagic = 0x44435154u;  // "TQCD"
+constexpr uint32_t kFormatVersion = 1;
+constexpr size_t kHeaderBytes = 256;
+constexpr int kValueTile = 32;   // tokens per value-code tile
+constexpr int kMaxCodes = 16;    // 2^4 centroids at most
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Largest power of two dividing d: the Hadamard block size.
+inline int hadamard_block(int d) { return d & (-d); }
+
+struct CacheLayout {
+  size_t kbits = 0, knorm = 0, vcodes = 0, vnorm = 0, total = 0;
+  int kbytes = 0;   // bytes of one key record (planes + sign bits)
+  int tiles = 0;    // value tiles per unit
+  int vwords = 0;   // dwords per (tile, coordinate) = bits_v
+};
+
+struct CodecLayout {
+  // byte offsets inside the codec table
+  size_t ck = 0, tk = 0, cv = 0, tv = 0, D = 0, S = 0, ST = 0, Shi = 0, Slo = 0, total = 0;
+  int block = 0;
+};
+
+// Host-side header of the codec table (first 256 bytes).
+struct CodecHeader {
+  uint32_t magic, version;
+  int32_t d, bits_k, bits_v, m;
+  uint64_t seed;
+  int32_t block;
+  float qjl_scale;       // sqrt(pi/2) / m (0 if m == 0)
+  float inv_sqrt_block;  // 1 / sqrt(block)
+  uint32_t reserved[53];
+};
+static_assert(sizeof(CodecHeader) == 256, "codec header is 256 bytes");
+
+struct CacheHeader {
+  uint32_t magic, version, flags, zero;
+  int32_t batch, kv_heads, d, capacity, bits_k, bits_v, m;
+  uint32_t reserved[53];
+};
+static_assert(sizeof(CacheHeader) == 256, "cache header is 256 bytes");
+
+bool codec_desc_valid(const tq_codec_desc &c);
+bool cache_desc_valid(const tq_cache_desc &c);
+CacheLayout cache_layout(const tq_cache_desc &c);
+CodecLayout codec_layout(int d, int bits_k, int bits_v, int m);
+
+// fp64 -> fp16 (round to nearest even); returns the fp16 value as a double and its bits.
+double round_fp16(double x, uint16_t *bits_out = nullptr);
+
+}  // namespace tq
