@@ -164,6 +164,22 @@ tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_d
                                   int32_t splits, void *ws, size_t ws_bytes,
                                   tq_stream_t stream);
 
+/* Instrumented forms for measurement: identical to tq_quantize_kv and
+ * tq_decode_attend_splits, and in addition record the caller's hipEvent_t `ev_start`
+ * right before and `ev_stop` right after the kernel that streams the packed cache (the
+ * quantize kernel; the split-K decode kernel) on `stream`.  Either event may be NULL. */
+tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_dev,
+                                  void *cache_dev, const void *k, const void *v,
+                                  tq_dtype dtype, int32_t start_pos, int32_t n_new,
+                                  float rope_base, void *ev_start, void *ev_stop,
+                                  tq_stream_t stream);
+tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec_dev,
+                                    const void *cache_dev, int32_t length, const void *q,
+                                    tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                                    float rope_base, float scale, float *out, float *scores,
+                                    int32_t splits, void *ws, size_t ws_bytes,
+                                    void *ev_start, void *ev_stop, tq_stream_t stream);
+
 /* Workspace bytes tq_search_topk needs. */
 size_t tq_search_workspace_bytes(const tq_cache_desc *db, int32_t n_db, int32_t nq, int32_t k);
 

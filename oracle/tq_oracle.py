@@ -325,7 +325,7 @@ def encode(x, codec: Codec, *, kind: str, positions=None, rope_base: float = 0.0
         r = y - n16[..., None] * cb.c[codes]
         rn = np.sqrt(np.sum(r * r, axis=-1))
         rn16, over_r = fp16_sat(rn)
-        z = r @ codec.S.T
+        z = r @ codec.S.T if codec.m > 0 else np.zeros(r.shape[:-1] + (0,))
         out.update(r=r, rn=rn, rn16=rn16, z=z, bits=(z >= 0).astype(np.int64))
         out["overflow"] = out["overflow"] | over_r
     return out

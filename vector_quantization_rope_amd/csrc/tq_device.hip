@@ -2,9 +2,9 @@
 //
 // Kernels (the step of the method each one carries out is named at its definition):
 //   k_cache_init        header of a packed cache
-//   k_quantize_small    RoPE -> seeded-sign FWHT -> norm -> Lloyd-Max codes -> bit planes
-//                       -> residual -> QJL sign bits, one lane per token, d in {64, 128}
-//   k_quantize_large    the same for database vectors of large d (one wave per vector)
+//   k_quantize_kv       RoPE -> seeded-sign FWHT -> norm -> Lloyd-Max codes -> bit planes
+//                       -> residual -> QJL sign bits (MFMA), 4 lanes per token, d in {64, 128}
+//   k_quantize_db       the same for database vectors of large d (one wave per vector)
 //   k_qprep             query RoPE, rotation Pi q, S q_rot and their sums
 //   k_decode_split      split-K decode: scores from the packed keys, online softmax,
 //                       accumulation of dequantized values in the rotated basis
@@ -66,15 +66,15 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // Sylvester FWHT of N values held in registers of one lane (natural order):
 // y = H_N x with H[i][j] = (-1)^popcount(i & j).
-template <int N>
-__device__ __forceinline__ void fwht_regs(float *x) {
+template <int N, typename T>
+__device__ __forceinline__ void fwht_regs(T *x) {
 #pragma unroll
   for (int h = 1; h < N; h <<= 1) {
 #pragma unroll
     for (int i = 0; i < N; i += 2 * h) {
 #pragma unroll
       for (int j = i; j < i + h; ++j) {
-        const float a = x[j], b = x[j + h];
+        const T a = x[j], b = x[j + h];
         x[j] = a + b;
         x[j + h] = a - b;
       }
@@ -148,319 +148,431 @@ __global__ void k_cache_init(uint32_t *hdr, tq_cache_desc c) {
   hdr[i] = v;
 }
 
-// ------------------------------------------------------------------ quantize (d <= 128)
+// ------------------------------------------------------------------ quantize
 struct QuantArgs {
   CodecPtrs cp;
   CachePtrs ch;
   const void *k, *v;
-  int dtype, start, n_new, capacity, bits_k, bits_v, m, units;
+  int start, n_new, capacity, bits_k, bits_v, m, units;
   float rope_base;
 };
 
-// Scalar codes against ascending boundaries t[0..K-2]: code = #{k : u >= t_k}; the
-// matching stored centroid comes out of the same comparisons (no indexed load).
-__device__ __forceinline__ int bucketize(float u, const float *t, const float *c, int K,
-                                         float *chat) {
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ double load_d(const void *p, size_t i) {
+  if constexpr (DT == TQ_F32) {
+    return double(static_cast<const float *>(p)[i]);
+  } else if constexpr (DT == TQ_BF16) {
+    return double(__uint_as_float(uint32_t(static_cast<const uint16_t *>(p)[i]) << 16));
+  } else {
+    const uint16_t b = static_cast<const uint16_t *>(p)[i];
+    _Float16 h;
+    __builtin_memcpy(&h, &b, 2);
+    return double(float(h));
+  }
+}
+
+// fp64 -> fp16 bits, round to nearest even, for x >= 0: round toward zero to fp32 and
+// set the sticky bit if inexact (round-to-odd), then let the fp32 -> fp16 conversion
+// round to nearest even; 24 >= 11 + 2 bits makes the double rounding exact.  Values that
+// would round to infinity are stored as 65504 and reported through *over.
+__device__ __forceinline__ uint16_t f64_to_f16_sat(double x, bool *over) {
+  if (!(x < 65520.0)) {
+    *over = true;
+    return 0x7BFF;
+  }
+  const float f = __double2float_rz(x);
+  uint32_t b = __float_as_uint(f);
+  if (double(f) != x) b |= 1u;
+  _Float16 h = (_Float16)__uint_as_float(b);
+  uint16_t r;
+  __builtin_memcpy(&r, &h, 2);
+  return r;
+}
+
+// code = #{k : u >= t_k} over ascending boundaries t[0..K-2] (fp64 compares; the fp32
+// boundaries are exact in fp64); the stored centroid of that code comes from the same
+// comparisons.
+__device__ __forceinline__ int bucketize64(double u, const float *t, const float *c, int K,
+                                           double *chat) {
   int code = 0;
   float cv = c[0];
 #pragma unroll
   for (int k = 0; k < kMaxCodes - 1; ++k) {
-    if (k < K - 1 && u >= t[k]) {
+    if (k < K - 1 && u >= double(t[k])) {
       code = k + 1;
       cv = c[k + 1];
     }
   }
-  *chat = cv;
+  *chat = double(cv);
   return code;
 }
 
-// One wave: a 64-token window aligned to value tiles.  Each lane carries one token's
-// whole vector in registers.  The RoPE table of the window (64 positions x d/2
-// frequencies) is built once in LDS: angle (p0 + i) theta_j by rotating the fp64
-// (cos, sin) of p0 theta_j by theta_j i times.
+// Seeded-sign FWHT of one vector spread over the 4 lanes of a group: lane q holds chunk A
+// (coordinates q*HC + e) and chunk B (D/2 + q*HC + e), e < HC.  Coordinate bits below
+// HC are in-lane, the next two bits select the lane, the top bit selects the chunk.
 template <int D>
-__global__ __launch_bounds__(64) void k_quantize_small(QuantArgs a) {
-  constexpr int H = D / 2;
-  constexpr int W = D / 32;  // dwords per plane
-  __shared__ float2 rope_cs[64][H + 1];
-  __shared__ uint8_t vcode_s[64][D];
-  __shared__ float sc_k[kMaxCodes], st_k[kMaxCodes], sc_v[kMaxCodes], st_v[kMaxCodes];
+__device__ __forceinline__ void fwht_group4(double *x, int q) {
+  constexpr int HC = D / 8;
+  fwht_regs<HC>(x);
+  fwht_regs<HC>(x + HC);
+#pragma unroll
+  for (int e = 0; e < HC; ++e) {
+    const double a = x[e], b = x[HC + e];
+    x[e] = a + b;
+    x[HC + e] = a - b;
+  }
+#pragma unroll
+  for (int dist = 1; dist <= 2; dist <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 2 * HC; ++e) {
+      const double o = __shfl_xor(x[e], dist, 64);
+      x[e] = (q & dist) ? (o - x[e]) : (x[e] + o);
+    }
+  }
+}
 
-  const int lane = threadIdx.x;
+__device__ __forceinline__ double group4_sum(double v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t group4_or(uint32_t v) {
+  v |= __shfl_xor(v, 1, 64);
+  v |= __shfl_xor(v, 2, 64);
+  return v;
+}
+
+// One workgroup (4 waves) per 64-token window aligned to value tiles; 4 lanes per token.
+// Keys: RoPE (fp64 angles from an LDS table built by the fp64 rotation recurrence),
+// signs, FWHT, norm, codes and residual all in fp64; the QJL projection z = S r runs
+// on fp32 MFMA (v_mfma_f32_32x32x2f32) over the window's 64 residuals.  Values: signs,
+// FWHT, norm, codes in fp64, then the window's codes are packed into value tiles.
+template <int D, int DT>
+__global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
+  constexpr int H = D / 2;
+  constexpr int HC = D / 8;     // coordinates per chunk
+  constexpr int C = 2 * HC;     // coordinates per lane
+  constexpr int W = D / 32;     // dwords per plane
+  constexpr int RS = D + 1;     // padded residual row (floats)
+  constexpr int ROPE_BYTES = 64 * H * 16;
+  constexpr int R_BYTES = 64 * RS * 4;
+  constexpr int U_BYTES = ROPE_BYTES > R_BYTES ? ROPE_BYTES : R_BYTES;
+  __shared__ __align__(16) unsigned char u_s[U_BYTES];   // RoPE table, later residuals
+  __shared__ uint8_t vcode_s[64][D];
+  __shared__ float cb_s[4][kMaxCodes];
+  double2 *rope_s = reinterpret_cast<double2 *>(u_s);   // [64][H]
+  float *r_s = reinterpret_cast<float *>(u_s);           // [64][RS]
+
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int slot = wv * 16 + (lane >> 2), q = lane & 3;
   const int unit = blockIdx.y;
   const int first_tile = a.start / kValueTile;
   const int p0 = (first_tile + 2 * int(blockIdx.x)) * kValueTile;
-  const int p = p0 + lane;
+  const int p = p0 + slot;
   const int end = a.start + a.n_new;
   const bool valid = p >= a.start && p < end;
+  const size_t row = size_t(unit) * size_t(a.n_new) + size_t(valid ? p - a.start : 0);
+  bool over = false;
 
-  if (lane < kMaxCodes) {
-    sc_k[lane] = a.cp.ck[lane];
-    st_k[lane] = a.cp.tk[lane];
-    sc_v[lane] = a.cp.cv[lane];
-    st_v[lane] = a.cp.tv[lane];
+  if (tid < kMaxCodes) {
+    cb_s[0][tid] = a.cp.ck[tid];
+    cb_s[1][tid] = a.cp.tk[tid];
+    cb_s[2][tid] = a.cp.cv[tid];
+    cb_s[3][tid] = a.cp.tv[tid];
   }
   const bool use_rope = a.rope_base != 0.0f;
   if (use_rope) {
-    // lanes split over (frequency, half of the window) when H < 64
-    constexpr int per = (H >= 64) ? 64 : 64 / (64 / H);
-    const int j = lane % H;
-    const int i0 = (lane / H) * per;
-    const int cnt = (H >= 64) ? 64 : per;
-    if (lane < H * (64 / cnt)) {
-      const double theta = pow(double(a.rope_base), -2.0 * double(j) / double(D));
-      double c, s, cd, sd;
-      sincos(double(p0 + i0) * theta, &s, &c);
-      sincos(theta, &sd, &cd);
-      for (int i = 0; i < cnt; ++i) {
-        rope_cs[i0 + i][j] = make_float2(float(c), float(s));
-        const double cn = c * cd - s * sd;
-        s = s * cd + c * sd;
-        c = cn;
-      }
+    constexpr int nblk = 256 / H, per = 64 / nblk;
+    const int j = tid % H, i0 = (tid / H) * per;
+    const double theta = pow(double(a.rope_base), -2.0 * double(j) / double(D));
+    double s, c, sd, cd;
+    sincos(double(p0 + i0) * theta, &s, &c);
+    sincos(theta, &sd, &cd);
+    for (int i = 0; i < per; ++i) {
+      rope_s[(i0 + i) * H + j] = make_double2(c, s);
+      const double cn = c * cd - s * sd;
+      s = s * cd + c * sd;
+      c = cn;
     }
   }
   __syncthreads();
 
-  const int K_k = 1 << a.bits_k;
-  const size_t row = size_t(unit) * size_t(a.n_new) + size_t(p - a.start);
-  bool over = false;
+  const double inv_sqrt_b = 1.0 / sqrt(double(a.cp.block));
+  auto coord = [&](int e) { return e < HC ? q * HC + e : H + q * HC + (e - HC); };
 
-  // ---------------- keys
+  // ------------------------------------------------------------ keys
   {
-    float x[D];
+    double x[C];
 #pragma unroll
-    for (int j = 0; j < D; ++j) x[j] = valid ? load_elem(a.k, row * D + j, a.dtype) : 0.0f;
+    for (int e = 0; e < C; ++e) x[e] = valid ? load_d<DT>(a.k, row * D + coord(e)) : 0.0;
     if (use_rope) {
 #pragma unroll
-      for (int j = 0; j < H; ++j) {
-        const float2 cs = rope_cs[lane][j];
-        const float x0 = x[j], x1 = x[j + H];
-        x[j] = x0 * cs.x - x1 * cs.y;
-        x[j + H] = x0 * cs.y + x1 * cs.x;
+      for (int e = 0; e < HC; ++e) {
+        const double2 cs = rope_s[slot * H + q * HC + e];
+        const double x0 = x[e], x1 = x[HC + e];
+        x[e] = x0 * cs.x - x1 * cs.y;
+        x[HC + e] = x0 * cs.y + x1 * cs.x;
       }
     }
 #pragma unroll
-    for (int j = 0; j < D; ++j) x[j] *= a.cp.D[j];
-    fwht_regs<D>(x);
-    float ss = 0.0f;
+    for (int e = 0; e < C; ++e) x[e] *= double(a.cp.D[coord(e)]);
+    fwht_group4<D>(x, q);
+    double ss = 0.0;
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      x[j] *= a.cp.inv_sqrt_block;
-      ss += x[j] * x[j];
+    for (int e = 0; e < C; ++e) {
+      x[e] *= inv_sqrt_b;
+      ss += x[e] * x[e];
     }
-    const float n = sqrtf(ss);
-    const uint16_t n16b = f16_sat_bits(n, &over);
-    const float n16 = f16_bits_to_float(n16b);
-    const float inv = n > 0.0f ? 1.0f / n : 0.0f;
-    uint32_t plane[4][W];
+    const double n = sqrt(group4_sum(ss));
+    const uint16_t n16b = f64_to_f16_sat(n, &over);
+    const double n16 = double(f16_bits_to_float(n16b));
+    const double inv = n > 0.0 ? 1.0 / n : 0.0;
+    const int K = 1 << a.bits_k;
+    uint32_t pl[4][W];
 #pragma unroll
     for (int pp = 0; pp < 4; ++pp)
 #pragma unroll
-      for (int w = 0; w < W; ++w) plane[pp][w] = 0u;
-    float rr = 0.0f;
+      for (int w = 0; w < W; ++w) pl[pp][w] = 0u;
+    double rr = 0.0;
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      float chat;
-      const int code = bucketize(x[j] * inv, st_k, sc_k, K_k, &chat);
+    for (int e = 0; e < C; ++e) {
+      double chat;
+      const int code = bucketize64(x[e] * inv, cb_s[1], cb_s[0], K, &chat);
+      const int j = coord(e);
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) plane[pp][j / 32] |= uint32_t((code >> pp) & 1) << (j % 32);
-      x[j] = x[j] - n16 * chat;  // residual against the stored fp16 norm
-      rr += x[j] * x[j];
+      for (int pp = 0; pp < 4; ++pp) pl[pp][j >> 5] |= uint32_t((code >> pp) & 1) << (j & 31);
+      x[e] -= n16 * chat;   // residual against the stored fp16 norm
+      rr += x[e] * x[e];
     }
-    const uint16_t rn16b = f16_sat_bits(sqrtf(rr), &over);
-    if (valid) {
-      uint32_t *rec = reinterpret_cast<uint32_t *>(a.ch.kbits + (size_t(unit) * a.capacity + p) * a.ch.kbytes);
-      int o = 0;
-      for (int pp = 0; pp < a.bits_k; ++pp)
+    const uint16_t rn16b = f64_to_f16_sat(sqrt(group4_sum(rr)), &over);
+    uint32_t *rec = reinterpret_cast<uint32_t *>(a.ch.kbits + (size_t(unit) * a.capacity + (valid ? p : 0)) * a.ch.kbytes);
 #pragma unroll
-        for (int w = 0; w < W; ++w) rec[o++] = plane[pp][w];
-      // QJL: z = S r over the m rows, one sign dword per 32 rows
-      for (int i0 = 0; i0 < a.m; i0 += 32) {
-        uint32_t bits = 0u;
-        for (int ii = 0; ii < 32; ++ii) {
-          const float *srow = a.cp.S + size_t(i0 + ii) * D;
-          float z = 0.0f;
+    for (int pp = 0; pp < 4; ++pp) {
 #pragma unroll
-          for (int j = 0; j < D; ++j) z = fmaf(srow[j], x[j], z);
-          bits |= uint32_t(z >= 0.0f) << ii;
-        }
-        rec[o++] = bits;
+      for (int w = 0; w < W; ++w) {
+        const uint32_t v = group4_or(pl[pp][w]);
+        if (valid && pp < a.bits_k && (w & 3) == q) rec[pp * W + w] = v;
       }
+    }
+    if (valid && q == 0)
       a.ch.knorm[size_t(unit) * a.capacity + p] = uint32_t(n16b) | (uint32_t(rn16b) << 16);
+    __syncthreads();   // every wave is done with the RoPE table before residuals overwrite it
+#pragma unroll
+    for (int e = 0; e < C; ++e) r_s[slot * RS + coord(e)] = float(x[e]);
+    __syncthreads();
+    // z^T[m x 64 tokens] = S[m x D] . R^T[D x 64]: one 32 x 32 output tile per iteration
+    const int mt_n = a.m / 32;
+    for (int it = wv; it < 2 * mt_n; it += 4) {
+      const int mt = it >> 1, tt = it & 1;
+      v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const float *srow = a.cp.S + size_t(32 * mt + (lane & 31)) * D + (lane >> 5);
+      const float *rrow = r_s + (32 * tt + (lane & 31)) * RS + (lane >> 5);
+#pragma unroll 8
+      for (int j0 = 0; j0 < D; j0 += 2)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(srow[j0], rrow[j0], acc, 0, 0, 0);
+      uint32_t bits = 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        bits |= uint32_t(acc[r] >= 0.0f) << (8 * (r >> 2) + 4 * (lane >> 5) + (r & 3));
+      bits |= __shfl_xor(bits, 32, 64);
+      const int ts = 32 * tt + (lane & 31);
+      const int pt = p0 + ts;
+      if (lane < 32 && pt >= a.start && pt < end) {
+        uint32_t *rt = reinterpret_cast<uint32_t *>(a.ch.kbits + (size_t(unit) * a.capacity + pt) * a.ch.kbytes);
+        rt[a.bits_k * W + mt] = bits;
+      }
     }
   }
 
-  // ---------------- values
+  // ------------------------------------------------------------ values
   if (a.bits_v > 0) {
-    const int K_v = 1 << a.bits_v;
-    float x[D];
+    double x[C];
 #pragma unroll
-    for (int j = 0; j < D; ++j) x[j] = valid ? load_elem(a.v, row * D + j, a.dtype) : 0.0f;
+    for (int e = 0; e < C; ++e)
+      x[e] = valid ? load_d<DT>(a.v, row * D + coord(e)) * double(a.cp.D[coord(e)]) : 0.0;
+    fwht_group4<D>(x, q);
+    double ss = 0.0;
 #pragma unroll
-    for (int j = 0; j < D; ++j) x[j] *= a.cp.D[j];
-    fwht_regs<D>(x);
-    float ss = 0.0f;
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      x[j] *= a.cp.inv_sqrt_block;
-      ss += x[j] * x[j];
+    for (int e = 0; e < C; ++e) {
+      x[e] *= inv_sqrt_b;
+      ss += x[e] * x[e];
     }
-    const float n = sqrtf(ss);
-    const uint16_t n16b = f16_sat_bits(n, &over);
-    const float inv = n > 0.0f ? 1.0f / n : 0.0f;
+    const double n = sqrt(group4_sum(ss));
+    const uint16_t n16b = f64_to_f16_sat(n, &over);
+    const double inv = n > 0.0 ? 1.0 / n : 0.0;
+    const int K = 1 << a.bits_v;
 #pragma unroll
-    for (int j = 0; j < D; ++j) {
-      float chat;
-      vcode_s[lane][j] = uint8_t(bucketize(x[j] * inv, st_v, sc_v, K_v, &chat));
+    for (int e = 0; e < C; ++e) {
+      double chat;
+      vcode_s[slot][coord(e)] = uint8_t(bucketize64(x[e] * inv, cb_s[3], cb_s[2], K, &chat));
     }
-    if (valid) a.ch.vnorm[size_t(unit) * a.capacity + p] = n16b;
+    if (valid && q == 0) a.ch.vnorm[size_t(unit) * a.capacity + p] = n16b;
     __syncthreads();
-    // value tiles: one (tile, coordinate) word per iteration; tokens outside the written
+    // value tiles: one (tile, coordinate) word per thread; tokens outside the written
     // range keep their previous bits
     const int bv = a.bits_v;
-    for (int w = lane; w < 2 * D; w += 64) {
-      const int tloc = w / D, j = w % D;
+    const uint32_t mask = (1u << bv) - 1u;
+    for (int wi = tid; wi < 2 * D; wi += 256) {
+      const int tloc = wi / D, j = wi % D;
       const int tile = first_tile + 2 * int(blockIdx.x) + tloc;
       const int tstart = tile * kValueTile;
       if (tstart >= end || tile >= a.ch.tiles) continue;
-      uint32_t *wp = a.ch.vcodes + (size_t(unit) * a.ch.tiles + tile) * size_t(D) * bv + size_t(j) * bv;
-      uint32_t word[4] = {0u, 0u, 0u, 0u}, keep[4] = {0u, 0u, 0u, 0u};
+      uint32_t *wp = a.ch.vcodes + ((size_t(unit) * a.ch.tiles + tile) * D + j) * bv;
+      uint32_t word[4] = {0u, 0u, 0u, 0u};
       const bool full = tstart >= a.start && tstart + kValueTile <= end;
       if (!full)
-        for (int q = 0; q < bv; ++q) word[q] = wp[q];
+        for (int qq = 0; qq < bv; ++qq) word[qq] = wp[qq];
       for (int i = 0; i < kValueTile; ++i) {
         const int t = tstart + i;
         if (t < a.start || t >= end) continue;
         const uint32_t code = vcode_s[tloc * kValueTile + i][j];
         const int bit = bv * i;
-        const int q = bit >> 5, s = bit & 31;
-        const uint32_t mask = (1u << bv) - 1u;
-        word[q] = (word[q] & ~(mask << s)) | (code << s);
-        if (s + bv > 32) {
-          const int s2 = 32 - s;
-          word[q + 1] = (word[q + 1] & ~(mask >> s2)) | (code >> s2);
+        const int qq = bit >> 5, sh = bit & 31;
+        word[qq] = (word[qq] & ~(mask << sh)) | (code << sh);
+        if (sh + bv > 32) {
+          const int s2 = 32 - sh;
+          word[qq + 1] = (word[qq + 1] & ~(mask >> s2)) | (code >> s2);
         }
       }
-      (void)keep;
-      for (int q = 0; q < bv; ++q) wp[q] = word[q];
+      for (int qq = 0; qq < bv; ++qq) wp[qq] = word[qq];
     }
   }
   if (over) atomicOr(a.ch.flags, 1u);
 }
 
-// ------------------------------------------------------------------ quantize (large d)
-// One wave per vector.  Lane l holds, in each Hadamard block b, the E consecutive
-// coordinates b*B + E*l .. +E-1 (B = 64 E).  Keys/database vectors only.
-template <int C, int E>
-__global__ __launch_bounds__(256) void k_quantize_large(QuantArgs a) {
-  constexpr int NB = C / E;   // Hadamard blocks
+// Database vectors of large d (keys only, no RoPE): one wave per vector for the fp64
+// rotation, norm, codes and residual (lane l holds, in each Hadamard block b, the E
+// consecutive coordinates b*B + E*l + e); the workgroup's 16 residuals then go through
+// z = S r on fp32 MFMA (v_mfma_f32_16x16x4f32), S streamed from L2.
+constexpr int kLargeGroup = 16;
+
+template <int C, int E, int DT>
+__global__ __launch_bounds__(256) void k_quantize_db(QuantArgs a) {
+  constexpr int NB = C / E;
   constexpr int B = 64 * E;
   constexpr int Dm = C * 64;
-  __shared__ float r_s[4][Dm];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  constexpr int RS = Dm + 4;
+  extern __shared__ float r_s[];   // [16][RS]
+  __shared__ float cb_s[2][kMaxCodes];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int unit = blockIdx.y;
-  const int p = a.start + int(blockIdx.x) * 4 + wv;
-  const bool valid = p < a.start + a.n_new;   // every wave still reaches the barrier
-  const size_t row = size_t(unit) * size_t(a.n_new) + size_t(valid ? p - a.start : 0);
-  float x[C];
+  const int g0 = a.start + int(blockIdx.x) * kLargeGroup;
+  const int end = a.start + a.n_new;
+  if (tid < kMaxCodes) {
+    cb_s[0][tid] = a.cp.ck[tid];
+    cb_s[1][tid] = a.cp.tk[tid];
+  }
+  __syncthreads();
+  const double inv_sqrt_b = 1.0 / sqrt(double(B));
+  const int K = 1 << a.bits_k;
+  const int dbytes = Dm / 8;
+  for (int vi = wv; vi < kLargeGroup; vi += 4) {
+    const int p = g0 + vi;
+    const bool valid = p < end;
+    const size_t row = size_t(unit) * size_t(a.n_new) + size_t(valid ? p - a.start : 0);
+    double x[C];
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int j = b * B + E * lane + e;
-      x[b * E + e] = valid ? load_elem(a.k, row * Dm + j, a.dtype) * a.cp.D[j] : 0.0f;
-    }
-  // FWHT per block: in-lane stages, then cross-lane stages
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    fwht_regs<E>(x + b * E);
-#pragma unroll
-    for (int dist = 1; dist < 64; dist <<= 1) {
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const float o = __shfl_xor(x[b * E + e], dist, 64);
-        x[b * E + e] = (lane & dist) ? (o - x[b * E + e]) : (x[b * E + e] + o);
+        const int j = b * B + E * lane + e;
+        x[b * E + e] = valid ? load_d<DT>(a.k, row * Dm + j) * double(a.cp.D[j]) : 0.0;
       }
-    }
-  }
-  float ss = 0.0f;
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    x[c] *= a.cp.inv_sqrt_block;
-    ss += x[c] * x[c];
-  }
-  ss = wave_sum(ss);
-  const float n = sqrtf(ss);
-  bool over = false;
-  const uint16_t n16b = f16_sat_bits(n, &over);
-  const float n16 = f16_bits_to_float(n16b);
-  const float inv = n > 0.0f ? 1.0f / n : 0.0f;
-  const int K = 1 << a.bits_k;
-  float t[kMaxCodes], cc[kMaxCodes];
-#pragma unroll
-  for (int k = 0; k < kMaxCodes; ++k) {
-    t[k] = a.cp.tk[k];
-    cc[k] = a.cp.ck[k];
-  }
-  uint8_t *rec = a.ch.kbits + (size_t(unit) * a.capacity + (valid ? p : 0)) * a.ch.kbytes;
-  uint32_t planebits[4][NB];  // E bits per (plane, block), E <= 32
-#pragma unroll
-  for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-    for (int b = 0; b < NB; ++b) planebits[pp][b] = 0u;
-  float rr = 0.0f;
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    float chat;
-    const int code = bucketize(x[c] * inv, t, cc, K, &chat);
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp) planebits[pp][c / E] |= uint32_t((code >> pp) & 1) << (c % E);
-    x[c] -= n16 * chat;
-    rr += x[c] * x[c];
-  }
-  rr = wave_sum(rr);
-  const uint16_t rn16b = f16_sat_bits(sqrtf(rr), &over);
-  // planes: lane l's E bits of block b sit at plane bit b*B + E*l
-  const int dbytes = Dm / 8;
-  for (int pp = 0; valid && pp < a.bits_k; ++pp) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const uint32_t v = planebits[pp][b];
-      if (E >= 8) {
+      fwht_regs<E>(x + b * E);
 #pragma unroll
-        for (int by = 0; by < E / 8; ++by)
-          rec[pp * dbytes + (b * B + E * lane) / 8 + by] = uint8_t(v >> (8 * by));
-      } else {
-        // E < 8: gather 8/E lanes into one byte
-        uint32_t acc = v << ((E * lane) & 7);
+      for (int dist = 1; dist < 64; dist <<= 1) {
 #pragma unroll
-        for (int o = 1; o < 8 / E; o <<= 1) acc |= __shfl_xor(acc, o, 64);
-        if (((E * lane) & 7) == 0) rec[pp * dbytes + (b * B + E * lane) / 8] = uint8_t(acc);
+        for (int e = 0; e < E; ++e) {
+          const double o = __shfl_xor(x[b * E + e], dist, 64);
+          x[b * E + e] = (lane & dist) ? (o - x[b * E + e]) : (x[b * E + e] + o);
+        }
       }
     }
-  }
-  // QJL: z_i = sum_j S_ij r_j with r broadcast through LDS and S^T read coalesced
+    double ss = 0.0;
 #pragma unroll
-  for (int b = 0; b < NB; ++b)
+    for (int c = 0; c < C; ++c) {
+      x[c] *= inv_sqrt_b;
+      ss += x[c] * x[c];
+    }
 #pragma unroll
-    for (int e = 0; e < E; ++e) r_s[wv][b * B + E * lane + e] = x[b * E + e];
-  __syncthreads();
-  for (int i0 = 0; i0 < a.m; i0 += 64) {
-    const int i = i0 + lane;
-    float z = 0.0f;
-    if (i < a.m)
-      for (int j = 0; j < Dm; ++j) z = fmaf(a.cp.ST[size_t(j) * a.m + i], r_s[wv][j], z);
-    const unsigned long long bal = __ballot(z >= 0.0f);
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const double n = sqrt(ss);
+    bool over = false;
+    const uint16_t n16b = f64_to_f16_sat(n, &over);
+    const double n16 = double(f16_bits_to_float(n16b));
+    const double inv = n > 0.0 ? 1.0 / n : 0.0;
+    uint32_t planebits[4][NB];
+#pragma unroll
+    for (int pp = 0; pp < 4; ++pp)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) planebits[pp][b] = 0u;
+    double rr = 0.0;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      double chat;
+      const int code = bucketize64(x[c] * inv, cb_s[1], cb_s[0], K, &chat);
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) planebits[pp][c / E] |= uint32_t((code >> pp) & 1) << (c % E);
+      x[c] -= n16 * chat;
+      rr += x[c] * x[c];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) rr += __shfl_xor(rr, o, 64);
+    const uint16_t rn16b = f64_to_f16_sat(sqrt(rr), &over);
+    uint8_t *rec = a.ch.kbits + (size_t(unit) * a.capacity + (valid ? p : 0)) * a.ch.kbytes;
+    for (int pp = 0; pp < a.bits_k; ++pp) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const uint32_t v = planebits[pp][b];
+        if (E >= 8) {
+#pragma unroll
+          for (int by = 0; by < E / 8; ++by)
+            if (valid) rec[pp * dbytes + (b * B + E * lane) / 8 + by] = uint8_t(v >> (8 * by));
+        } else {
+          uint32_t acc = v << ((E * lane) & 7);
+#pragma unroll
+          for (int o = 1; o < 8 / E; o <<= 1) acc |= __shfl_xor(acc, o, 64);
+          if (valid && ((E * lane) & 7) == 0) rec[pp * dbytes + (b * B + E * lane) / 8] = uint8_t(acc);
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int e = 0; e < E; ++e) r_s[vi * RS + b * B + E * lane + e] = float(x[b * E + e]);
     if (valid && lane == 0) {
-      uint8_t *sb = rec + a.bits_k * dbytes + i0 / 8;
-      const int nb = (a.m - i0) >= 64 ? 8 : (a.m - i0) / 8;
-      for (int by = 0; by < nb; ++by) sb[by] = uint8_t(bal >> (8 * by));
+      a.ch.knorm[size_t(unit) * a.capacity + p] = uint32_t(n16b) | (uint32_t(rn16b) << 16);
+      if (over) atomicOr(a.ch.flags, 1u);
     }
   }
-  if (valid && lane == 0) {
-    a.ch.knorm[size_t(unit) * a.capacity + p] = uint32_t(n16b) | (uint32_t(rn16b) << 16);
-    if (over) atomicOr(a.ch.flags, 1u);
+  __syncthreads();
+  // z^T[m x 16] = S[m x Dm] . R^T[Dm x 16], 16-row output tiles spread over the waves
+  const int mt_n = a.m / 16;
+  for (int mt = wv; mt < mt_n; mt += 4) {
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    const float *srow = a.cp.S + size_t(16 * mt + (lane & 15)) * Dm + (lane >> 4);
+    const float *rrow = r_s + (lane & 15) * RS + (lane >> 4);
+#pragma unroll 8
+    for (int j0 = 0; j0 < Dm; j0 += 4)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(srow[j0], rrow[j0], acc, 0, 0, 0);
+    // lane holds outputs 16 mt + 4 (lane / 16) + r of vector lane % 16
+    uint32_t bits = 0u;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bits |= uint32_t(acc[r] >= 0.0f) << (4 * (lane >> 4) + r);
+    bits |= __shfl_xor(bits, 16, 64);
+    bits |= __shfl_xor(bits, 32, 64);
+    const int p = g0 + (lane & 15);
+    if (lane < 16 && p < end) {
+      uint8_t *rec = a.ch.kbits + (size_t(unit) * a.capacity + p) * a.ch.kbytes;
+      uint16_t *sb = reinterpret_cast<uint16_t *>(rec + a.bits_k * dbytes + 2 * mt);
+      *sb = uint16_t(bits);
+    }
   }
 }
 
@@ -989,16 +1101,17 @@ tq_status tq_cache_init(const tq_cache_desc *desc, void *cache_dev, tq_stream_t 
   return launch_status();
 }
 
-tq_status tq_quantize_kv(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
-                         const void *k, const void *v, tq_dtype dtype, int32_t start_pos,
-                         int32_t n_new, float rope_base, tq_stream_t stream) {
+tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_dev,
+                                  void *cache_dev, const void *k, const void *v,
+                                  tq_dtype dtype, int32_t start_pos, int32_t n_new,
+                                  float rope_base, void *ev_start, void *ev_stop,
+                                  tq_stream_t stream) {
   if (!desc || !codec_dev || !cache_dev) return TQ_EINVAL;
   if (!cache_desc_valid(*desc)) return TQ_EUNSUPPORTED;
   if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_EINVAL;
   if (start_pos < 0 || n_new < 0) return TQ_EINVAL;
   if (int64_t(start_pos) + int64_t(n_new) > int64_t(desc->capacity)) return TQ_ECAPACITY;
-  if ((desc->bits_v > 0) != (v != nullptr)) return TQ_EINVAL;
-  if (n_new > 0 && !k) return TQ_EINVAL;
+  if (n_new > 0 && (!k || (desc->bits_v > 0) != (v != nullptr))) return TQ_EINVAL;
   if (!std::isfinite(rope_base) || rope_base < 0.0f) return TQ_EINVAL;
   const int d = desc->d;
   const bool small = (d == 64 || d == 128);
@@ -1006,12 +1119,12 @@ tq_status tq_quantize_kv(const tq_cache_desc *desc, const void *codec_dev, void 
   if (!small && !(large && desc->bits_v == 0)) return TQ_EUNSUPPORTED;
   if (large && rope_base != 0.0f) return TQ_EUNSUPPORTED;
   if (n_new == 0) return TQ_OK;
+  if (desc->m > 0 && (desc->m % 32) != 0) return TQ_EUNSUPPORTED;
   QuantArgs a;
   a.cp = codec_ptrs(codec_dev, d, desc->bits_k, desc->bits_v, desc->m);
   a.ch = cache_ptrs(cache_dev, *desc);
   a.k = k;
   a.v = v;
-  a.dtype = int(dtype);
   a.start = start_pos;
   a.n_new = n_new;
   a.capacity = desc->capacity;
@@ -1021,26 +1134,51 @@ tq_status tq_quantize_kv(const tq_cache_desc *desc, const void *codec_dev, void 
   a.units = desc->batch * desc->kv_heads;
   a.rope_base = rope_base;
   hipStream_t s = hipStream_t(stream);
+  if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
   if (small) {
     const int first_tile = start_pos / kValueTile;
     const int end_tile = (start_pos + n_new + kValueTile - 1) / kValueTile;
     const int windows = (end_tile - first_tile + 1) / 2;
     dim3 grid(windows, a.units);
-    if (d == 64)
-      hipLaunchKernelGGL(k_quantize_small<64>, grid, dim3(64), 0, s, a);
-    else
-      hipLaunchKernelGGL(k_quantize_small<128>, grid, dim3(64), 0, s, a);
-  } else {
-    dim3 grid((n_new + 3) / 4, a.units);
-    switch (d) {
-      case 256: hipLaunchKernelGGL((k_quantize_large<4, 4>), grid, dim3(256), 0, s, a); break;
-      case 512: hipLaunchKernelGGL((k_quantize_large<8, 8>), grid, dim3(256), 0, s, a); break;
-      case 1024: hipLaunchKernelGGL((k_quantize_large<16, 16>), grid, dim3(256), 0, s, a); break;
-      case 1536: hipLaunchKernelGGL((k_quantize_large<24, 8>), grid, dim3(256), 0, s, a); break;
-      default: hipLaunchKernelGGL((k_quantize_large<32, 32>), grid, dim3(256), 0, s, a); break;
+#define TQ_QKV(DD, TT) hipLaunchKernelGGL((k_quantize_kv<DD, TT>), grid, dim3(256), 0, s, a)
+    if (d == 64) {
+      if (dtype == TQ_F32) TQ_QKV(64, TQ_F32); else if (dtype == TQ_BF16) TQ_QKV(64, TQ_BF16); else TQ_QKV(64, TQ_F16);
+    } else {
+      if (dtype == TQ_F32) TQ_QKV(128, TQ_F32); else if (dtype == TQ_BF16) TQ_QKV(128, TQ_BF16); else TQ_QKV(128, TQ_F16);
     }
+#undef TQ_QKV
+  } else {
+    dim3 grid((n_new + kLargeGroup - 1) / kLargeGroup, a.units);
+    const size_t shm = size_t(kLargeGroup) * (d + 4) * 4;
+#define TQ_QDB(CC, EE, TT)                                                                     \
+  do {                                                                                         \
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_quantize_db<CC, EE, TT>),         \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess) \
+      return TQ_EDEVICE;                                                                       \
+    hipLaunchKernelGGL((k_quantize_db<CC, EE, TT>), grid, dim3(256), shm, s, a);               \
+  } while (0)
+#define TQ_QDB_T(CC, EE) \
+  do { if (dtype == TQ_F32) TQ_QDB(CC, EE, TQ_F32); else if (dtype == TQ_BF16) TQ_QDB(CC, EE, TQ_BF16); else TQ_QDB(CC, EE, TQ_F16); } while (0)
+    switch (d) {
+      case 256: TQ_QDB_T(4, 4); break;
+      case 512: TQ_QDB_T(8, 8); break;
+      case 1024: TQ_QDB_T(16, 16); break;
+      case 1536: TQ_QDB_T(24, 8); break;
+      default: TQ_QDB_T(32, 32); break;
+    }
+#undef TQ_QDB_T
+#undef TQ_QDB
   }
-  return launch_status();
+  const tq_status st = launch_status();
+  if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
+  return st;
+}
+
+tq_status tq_quantize_kv(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
+                         const void *k, const void *v, tq_dtype dtype, int32_t start_pos,
+                         int32_t n_new, float rope_base, tq_stream_t stream) {
+  return tq_quantize_kv_profiled(desc, codec_dev, cache_dev, k, v, dtype, start_pos, n_new,
+                                 rope_base, nullptr, nullptr, stream);
 }
 
 size_t tq_decode_workspace_bytes_splits(const tq_cache_desc *desc, int32_t q_heads,
@@ -1059,12 +1197,12 @@ size_t tq_decode_workspace_bytes(const tq_cache_desc *desc, int32_t q_heads, int
   return decode_ws(*desc, q_heads, default_splits(*desc, length));
 }
 
-tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_dev,
-                                  const void *cache_dev, int32_t length, const void *q,
-                                  tq_dtype dtype, int32_t q_heads, int32_t q_pos,
-                                  float rope_base, float scale, float *out, float *scores,
-                                  int32_t splits, void *ws, size_t ws_bytes,
-                                  tq_stream_t stream) {
+tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec_dev,
+                                    const void *cache_dev, int32_t length, const void *q,
+                                    tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                                    float rope_base, float scale, float *out, float *scores,
+                                    int32_t splits, void *ws, size_t ws_bytes,
+                                    void *ev_start, void *ev_stop, tq_stream_t stream) {
   if (!desc || !codec_dev || !cache_dev || !q || !out || !ws) return TQ_EINVAL;
   if (!cache_desc_valid(*desc)) return TQ_EUNSUPPORTED;
   if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_EINVAL;
@@ -1119,12 +1257,25 @@ tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_d
   // the value-phase partial sums reuse the p region: (256 / d) * kMaxG * d floats
   const size_t shm_all = shm;
   dim3 grid(desc->batch * desc->kv_heads, S);
+  if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
   if (d == 64)
     hipLaunchKernelGGL(k_decode_split<64>, grid, dim3(kDecThreads), shm_all, s, a);
   else
     hipLaunchKernelGGL(k_decode_split<128>, grid, dim3(kDecThreads), shm_all, s, a);
+  if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
   hipLaunchKernelGGL(k_decode_combine, dim3(rows), dim3(128), d * 4, s, part, S, d, cp, out);
   return launch_status();
+}
+
+tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_dev,
+                                  const void *cache_dev, int32_t length, const void *q,
+                                  tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                                  float rope_base, float scale, float *out, float *scores,
+                                  int32_t splits, void *ws, size_t ws_bytes,
+                                  tq_stream_t stream) {
+  return tq_decode_attend_profiled(desc, codec_dev, cache_dev, length, q, dtype, q_heads, q_pos,
+                                   rope_base, scale, out, scores, splits, ws, ws_bytes, nullptr,
+                                   nullptr, stream);
 }
 
 tq_status tq_decode_attend(const tq_cache_desc *desc, const void *codec_dev, const void *cache_dev,

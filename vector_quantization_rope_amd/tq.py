@@ -29,7 +29,8 @@ EXPORTS = [
     "tq_codec_build", "tq_cache_bytes", "tq_cache_init", "tq_quantize_kv",
     "tq_decode_workspace_bytes", "tq_decode_splits", "tq_decode_attend",
     "tq_decode_workspace_bytes_splits", "tq_decode_attend_splits",
-    "tq_search_workspace_bytes", "tq_search_topk",
+    "tq_search_workspace_bytes", "tq_search_topk", "tq_quantize_kv_profiled",
+    "tq_decode_attend_profiled",
 ]
 
 
@@ -78,6 +79,10 @@ _decode_attend_splits = _sig("tq_decode_attend_splits", ctypes.c_int,
                              [_KD, _P, _P, _I, _P, ctypes.c_int, _I, _I, _F, _F, _P, _P, _I, _P, _S, _P])
 _decode_attend = _sig("tq_decode_attend", ctypes.c_int,
                       [_KD, _P, _P, _I, _P, ctypes.c_int, _I, _I, _F, _F, _P, _P, _P, _S, _P])
+_quantize_kv_prof = _sig("tq_quantize_kv_profiled", ctypes.c_int,
+                         [_KD, _P, _P, _P, _P, ctypes.c_int, _I, _I, _F, _P, _P, _P])
+_decode_attend_prof = _sig("tq_decode_attend_profiled", ctypes.c_int,
+                           [_KD, _P, _P, _I, _P, ctypes.c_int, _I, _I, _F, _F, _P, _P, _I, _P, _S, _P, _P, _P])
 _search_ws = _sig("tq_search_workspace_bytes", _S, [_KD, _I, _I, _I])
 _search_topk = _sig("tq_search_topk", ctypes.c_int,
                     [_KD, _P, _P, _I, _P, _I, _I, _P, _P, _P, _S, _P])
@@ -162,12 +167,14 @@ def cache_init(desc: CacheDesc, cache, stream=None):
 
 
 def quantize_kv(desc: CacheDesc, codec_dev, cache, k, v, start_pos: int, rope_base: float,
-                n_new: int | None = None, stream=None, dtype: int | None = None):
+                n_new: int | None = None, stream=None, dtype: int | None = None, events=None):
+    """events: optional (start, stop) hipEvent_t handles recorded around the kernel."""
     if n_new is None:
         n_new = 0 if k is None else int(k.shape[-2])
     code = dtype if dtype is not None else (_dtype_code(k) if k is not None else TQ_F32)
-    _check(_quantize_kv(ctypes.byref(desc), _ptr(codec_dev), _ptr(cache), _ptr(k), _ptr(v), code,
-                        int(start_pos), int(n_new), float(rope_base), _stream(stream)),
+    ev0, ev1 = events if events else (None, None)
+    _check(_quantize_kv_prof(ctypes.byref(desc), _ptr(codec_dev), _ptr(cache), _ptr(k), _ptr(v), code,
+                             int(start_pos), int(n_new), float(rope_base), ev0, ev1, _stream(stream)),
            "tq_quantize_kv")
 
 
@@ -183,14 +190,16 @@ def decode_splits(desc: CacheDesc, q_heads: int, length: int) -> int:
 
 def decode_attend(desc: CacheDesc, codec_dev, cache, length: int, q, q_pos: int, rope_base: float,
                   out, scores=None, ws=None, scale: float = 0.0, splits: int = 0, stream=None,
-                  ws_bytes: int | None = None):
+                  ws_bytes: int | None = None, events=None):
+    """events: optional (start, stop) hipEvent_t handles recorded around the split-K kernel."""
     q_heads = int(q.shape[1])
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
-    _check(_decode_attend_splits(ctypes.byref(desc), _ptr(codec_dev), _ptr(cache), int(length),
-                                 _ptr(q), _dtype_code(q), q_heads, int(q_pos), float(rope_base),
-                                 float(scale), _ptr(out), _ptr(scores), int(splits), _ptr(ws),
-                                 int(ws_bytes), _stream(stream)),
+    ev0, ev1 = events if events else (None, None)
+    _check(_decode_attend_prof(ctypes.byref(desc), _ptr(codec_dev), _ptr(cache), int(length),
+                               _ptr(q), _dtype_code(q), q_heads, int(q_pos), float(rope_base),
+                               float(scale), _ptr(out), _ptr(scores), int(splits), _ptr(ws),
+                               int(ws_bytes), ev0, ev1, _stream(stream)),
            "tq_decode_attend")
 
 
