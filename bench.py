@@ -1,0 +1,275 @@
+"""Benchmark: one step of the packed-KV hot path on the long-context GQA workload.
+
+Workload (one GPU's share of a long-context decode): 1 layer, 64 q-heads / 8 kv-heads,
+head dim 128, batch 4, context 131072, bf16 unit-variance Laplace keys/values with 4
+channels x20, RoPE base 500000, keys 2-bit + 1-bit QJL (m = 128), values 3-bit.
+The cache is prefilled with positions [0, 126976) before timing.  One step =
+  * append: tq_quantize_kv of the last 4096 positions [126976, 131072) of every
+    (batch, kv-head) unit (rewritten each step), and
+  * decode: tq_decode_attend of one query per (batch, q-head) over all 131072 tokens.
+Inputs (K, V, q) are resident in HBM before timing.  `value` is the decode attention
+throughput in GB/s of algorithmic packed-cache bytes (52 B key + 50 B value per token
+per kv-head) over the whole decode call.  Extra fields give the append throughput
+(Mtokens/s, a token being one position of one sequence with all its kv-heads, K and V),
+the roofline of the dominant kernel (split-K decode; its duration comes from HIP
+events the library records around that kernel), and the CPU oracle timed on a bounded
+sample on this host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KEY_RECORD = 52      # bytes per token per kv-head: 2-bit planes 32 + signs 16 + 2 fp16 norms
+VALUE_RECORD = 50    # 3-bit codes 48 + fp16 norm
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_split_long_context_counters.json")
+DEVICE_SRC = os.path.join(ROOT, "vector_quantization_rope_amd", "csrc", "tq_device.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEventCreate / hipEventElapsedTime through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = None
+        for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+            try:
+                self.hip = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if self.hip is None:
+            raise RuntimeError("libamdhip64.so not found")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return ev.value
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ev, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+
+def kernel_source_hash() -> str:
+    with open(DEVICE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_counters(launch_bytes: float):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, K, V, q, units_total: int):
+    """Time the CPU oracle on one (batch, kv-head) unit of the same workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import tq_oracle as O
+
+    Kd = K[0, 0].to("cpu").to(torch.float64).numpy()
+    Vd = V[0, 0].to("cpu").to(torch.float64).numpy()
+    qd = q[0:1, 0:w.q_heads // w.kv_heads].to("cpu").to(torch.float64).numpy()
+    T = Kd.shape[0]
+    codec = O.make_codec(w.d, w.bits_k, w.bits_v, w.m, 0)
+    t0 = time.perf_counter()
+    ke = O.encode(Kd, codec, kind="key", positions=np.arange(T), rope_base=w.rope_base)
+    ve = O.encode(Vd, codec, kind="value")
+    t_enc = time.perf_counter() - t0
+    fields = {"kcodes": ke["codes"][None, None], "n16": ke["n16"][None, None],
+              "rn16": ke["rn16"][None, None], "bits": ke["bits"][None, None],
+              "vcodes": ve["codes"][None, None], "vn16": ve["n16"][None, None]}
+    t0 = time.perf_counter()
+    O.attend(fields, qd, codec, q_pos=w.q_pos, rope_base=w.rope_base, scale=0.0, kv_heads=1, length=T)
+    t_att = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    gbs = T * (KEY_RECORD + VALUE_RECORD) / t_att / 1e9
+    # tokens: positions of one sequence with all kv-heads -> one unit covers 1/kv_heads of it
+    mtok = T / w.kv_heads / t_enc / 1e6
+    return {
+        "value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+        "sample": (f"one (batch, kv-head) unit of {units_total}: oracle decode attention of its "
+                   f"{w.q_heads // w.kv_heads} q-heads over {T} tokens ({t_att:.2f} s); oracle encode "
+                   f"of its {T} keys and values ({t_enc:.2f} s)"),
+        "quantize_mtokens_s": round(mtok, 6),
+        "seconds": round(t_enc + t_att, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (for counter scaling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the packed-KV path runs on a single device and this "
+              "build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from vector_quantization_rope_amd import tq
+    from vector_quantization_rope_amd import workloads as W
+
+    w = W.LONG_CONTEXT
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    T, A = w.context, w.append
+    pre = T - A
+    log(f"[bench] generating {w.name} inputs on the GPU ...")
+    K, V = W.gen_kv(w, device=dev)
+    q = W.gen_q(w, device=dev)
+    codec = tq.Codec(w.d, w.bits_k, w.bits_v, w.m, seed=0, device=dev)
+    cache = tq.PackedCache(w.batch, w.kv_heads, w.d, T, w.bits_k, w.bits_v, w.m, device=dev)
+    Kp, Vp = K[:, :, :pre].contiguous(), V[:, :, :pre].contiguous()
+    Ka, Va = K[:, :, pre:].contiguous(), V[:, :, pre:].contiguous()
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, Kp, Vp, 0, w.rope_base)
+    del Kp, Vp
+    out = torch.empty((w.batch, w.q_heads, w.d), dtype=torch.float32, device=dev)
+    splits = tq.decode_splits(cache.desc, w.q_heads, T)
+    ws = torch.empty(tq.decode_workspace_bytes(cache.desc, w.q_heads, T), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] prefill done; decode splits {splits}")
+
+    ev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    E = {k: [ev.create() for _ in range(args.steps)] for k in
+         ("a0", "a1", "k0", "k1", "d0", "d1")}
+
+    def step(i=None):
+        if i is None:
+            tq.quantize_kv(cache.desc, codec.dev, cache.buf, Ka, Va, pre, w.rope_base)
+            tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos, w.rope_base, out, ws=ws)
+            return
+        tq.quantize_kv(cache.desc, codec.dev, cache.buf, Ka, Va, pre, w.rope_base,
+                       events=(E["a0"][i], E["a1"][i]))
+        ev.record(E["d0"][i], stream)
+        tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos, w.rope_base, out, ws=ws,
+                         events=(E["k0"][i], E["k1"][i]))
+        ev.record(E["d1"][i], stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    append_ms = [ev.elapsed_ms(E["a0"][i], E["a1"][i]) for i in range(args.steps)]
+    kern_ms = [ev.elapsed_ms(E["k0"][i], E["k1"][i]) for i in range(args.steps)]
+    dec_ms = [ev.elapsed_ms(E["d0"][i], E["d1"][i]) for i in range(args.steps)]
+    mean = lambda v: sum(v) / len(v)
+    units = w.batch * w.kv_heads
+    dec_bytes = units * T * (KEY_RECORD + VALUE_RECORD)
+    dec_gbs = dec_bytes / (mean(dec_ms) * 1e-3) / 1e9
+    kern_gbs = dec_bytes / (mean(kern_ms) * 1e-3) / 1e9
+    append_tokens = w.batch * A
+    append_mtok = append_tokens / (mean(append_ms) * 1e-3) / 1e6
+    # append algorithmic bytes: bf16 K and V read + records written
+    append_bytes = units * A * (2 * w.d * 2 + KEY_RECORD + VALUE_RECORD)
+    log(f"[bench] decode call {mean(dec_ms)*1e3:.1f} us ({dec_gbs:.0f} GB/s), split kernel "
+        f"{mean(kern_ms)*1e3:.1f} us ({kern_gbs:.0f} GB/s), append {mean(append_ms)*1e3:.1f} us "
+        f"({append_mtok:.1f} Mtokens/s, {append_bytes/(mean(append_ms)*1e-3)/1e9:.0f} GB/s)")
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: {n} bytes copied 3 times")
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        base = cpu_baseline(w, K, V, q, units)
+        log(f"[bench] cpu baseline {base}")
+
+    rec = {
+        "metric": "packed-KV decode attention GB/s & % HBM peak; quantize Mtokens/s",
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": ("long_context: 1 layer, 64 q-heads / 8 kv-heads, head dim 128, batch 4, "
+                         "context 131072, append 4096, bf16 Laplace K/V + 4 channels x20, RoPE 500000, "
+                         "keys 2-bit + QJL m=128, values 3-bit"),
+            "batch": w.batch, "context": T, "append_tokens": A, "q_heads": w.q_heads,
+            "kv_heads": w.kv_heads, "head_dim": w.d, "decode_splits": splits,
+        },
+        "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+        "decode_us": round(mean(dec_ms) * 1e3, 2),
+        "append_us": round(mean(append_ms) * 1e3, 2),
+        "quantize_mtokens_s": round(append_mtok, 2),
+        "quantize_gbs": round(append_bytes / (mean(append_ms) * 1e-3) / 1e9, 2),
+        "roofline": {
+            "kernel": "k_decode_split (split-K decode over the packed cache)",
+            "bound": "hbm",
+            "achieved": round(kern_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_counters(dec_bytes),
+            "algorithmic_bytes_per_launch": dec_bytes,
+            "avg_launch_us": round(mean(kern_ms) * 1e3, 2),
+        },
+        "cpu_baseline": base,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
