@@ -5,10 +5,13 @@
 //   k_quantize_kv       RoPE -> seeded-sign FWHT -> norm -> Lloyd-Max codes -> bit planes
 //                       -> residual -> QJL sign bits (MFMA), 4 lanes per token, d in {64, 128}
 //   k_quantize_db       the same for database vectors of large d (one wave per vector)
-//   k_qprep             query RoPE, rotation Pi q, S q_rot and their sums
-//   k_decode_split      split-K decode: scores from the packed keys, online softmax,
-//                       accumulation of dequantized values in the rotated basis
-//   k_decode_combine    merge of the splits, normalisation, inverse rotation Pi^T
+//   k_qprep_pack        query RoPE, rotation Pi q, S q_rot and their sums; for the MFMA
+//                       decode also the int8 digit rows and score coefficients
+//   k_decode_lds        split-K decode on MFMA with LDS-staged tiles: key scores (int8),
+//                       online softmax, values (fp16 hi/lo against LUT-dequantized
+//                       centroids), accumulated in the rotated basis
+//   k_decode_split      the same on plain fp32 arithmetic for the other bit widths
+//   k_decode_merge      merge of the splits, normalisation, inverse rotation Pi^T
 //   k_search_tile       packed database scores for a query tile + per-tile top-k
 //   k_search_merge      per-query top-k over the tile candidates
 
@@ -576,78 +579,6 @@ __global__ __launch_bounds__(256) void k_quantize_db(QuantArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ query preparation
-// One block per query row: q_rot = Pi RoPE(q, q_pos) (LDS FWHT), sq = S q_rot,
-// sums sum_j q_rot_j and sum_i sq_i.  Output row layout: [q_rot d][sq m][sum_q, sum_sq].
-__global__ __launch_bounds__(256) void k_qprep(const void *q, int dtype, int d, int m,
-                                               int q_pos, float rope_base, CodecPtrs cp,
-                                               float *out, int out_stride) {
-  extern __shared__ float qs[];  // d floats
-  const int rowi = blockIdx.x;
-  const int tid = threadIdx.x;
-  const size_t base = size_t(rowi) * d;
-  const int h = d / 2;
-  if (rope_base != 0.0f) {
-    for (int j = tid; j < h; j += blockDim.x) {
-      const double theta = pow(double(rope_base), -2.0 * double(j) / double(d));
-      double s, c;
-      sincos(double(q_pos) * theta, &s, &c);
-      const float x0 = load_elem(q, base + j, dtype), x1 = load_elem(q, base + j + h, dtype);
-      qs[j] = (x0 * float(c) - x1 * float(s)) * cp.D[j];
-      qs[j + h] = (x0 * float(s) + x1 * float(c)) * cp.D[j + h];
-    }
-  } else {
-    for (int j = tid; j < d; j += blockDim.x) qs[j] = load_elem(q, base + j, dtype) * cp.D[j];
-  }
-  __syncthreads();
-  const int B = cp.block;
-  for (int hh = 1; hh < B; hh <<= 1) {
-    for (int k = tid; k < d / 2; k += blockDim.x) {
-      // butterfly k of this stage: pairs (i, i + hh) inside each block
-      const int blk = k / (B / 2), kk = k % (B / 2);
-      const int i = blk * B + (kk / hh) * 2 * hh + (kk % hh);
-      const float x0 = qs[i], x1 = qs[i + hh];
-      qs[i] = x0 + x1;
-      qs[i + hh] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  float *o = out + size_t(rowi) * out_stride;
-  float part = 0.0f;
-  for (int j = tid; j < d; j += blockDim.x) {
-    const float v = qs[j] * cp.inv_sqrt_block;
-    o[j] = v;
-    part += v;
-  }
-  __syncthreads();
-  for (int j = tid; j < d; j += blockDim.x) qs[j] *= cp.inv_sqrt_block;
-  __syncthreads();
-  float part2 = 0.0f;
-  for (int i = tid; i < m; i += blockDim.x) {
-    float z = 0.0f;
-    for (int j = 0; j < d; ++j) z = fmaf(cp.S[size_t(i) * d + j], qs[j], z);
-    o[d + i] = z;
-    part2 += z;
-  }
-  __shared__ float red[2][8];
-  part = wave_sum(part);
-  part2 = wave_sum(part2);
-  if ((tid & 63) == 0) {
-    red[0][tid >> 6] = part;
-    red[1][tid >> 6] = part2;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    float s0 = 0.0f, s1 = 0.0f;
-    for (int w = 0; w < int(blockDim.x) / 64; ++w) {
-      s0 += red[0][w];
-      s1 += red[1][w];
-    }
-    o[d + m] = s0;
-    o[d + m + 1] = s1;
-  }
-}
-
 // ------------------------------------------------------------------ decode (split-K)
 struct DecodeArgs {
   CodecPtrs cp;
@@ -849,32 +780,657 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_split(DecodeArgs a) {
   }
 }
 
-// Merge of the splits and inverse rotation: out = D .* (H o) / sqrt(B) = Pi^T o.
-__global__ __launch_bounds__(256) void k_decode_combine(const float *part, int splits, int d,
-                                                        CodecPtrs cp, float *out) {
-  extern __shared__ float os[];
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const float *pr = part + size_t(row) * splits * (d + 2);
-  float Mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) Mx = fmaxf(Mx, pr[size_t(s) * (d + 2) + d]);
-  float L = 0.0f;
-  for (int s = 0; s < splits; ++s) {
-    const float ms = pr[size_t(s) * (d + 2) + d];
-    if (ms != -INFINITY) L += pr[size_t(s) * (d + 2) + d + 1] * __expf(ms - Mx);
-  }
-  const float invL = L > 0.0f ? 1.0f / L : 0.0f;
-  for (int j = tid; j < d; j += blockDim.x) {
-    float v = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-      const float ms = pr[size_t(s) * (d + 2) + d];
-      if (ms != -INFINITY) v += pr[size_t(s) * (d + 2) + j] * __expf(ms - Mx);
+// ------------------------------------------------------------------ decode (MFMA path)
+// For bits_k = 2, m = d, bits_v = 3, d in {64, 128} and up to 8 q-heads per kv-head.
+//
+// Keys: the G query rows are written as 24-bit fixed point in three signed int8 digits
+// (rows digit * 8 + head of a 32-row A operand) and the packed 0/1 bit planes of 32 tokens
+// are the B operand of v_mfma_i32_32x32x32_i8: the products are exact integers, so
+// q . plane and S q . signs come out exact for the quantized query; the digits recombine
+// in-lane.  With c[code] = c0 + (c1 - c0) b0 + (c2 - c0) b1 (symmetric 2-bit codebook):
+//   score = n (c0 sum q + (c1-c0) q.b0 + (c2-c0) q.b1) + ||r|| sqrt(pi/2)/m (2 sq.s - sum sq).
+// Values: p n_v is split into fp16 hi + lo rows (16 rows for 8 heads) and multiplied on
+// v_mfma_f32_16x16x32_f16 with the fp16 centroids of 32 tokens, looked up 4 codes at a
+// time from a 4096-entry LDS table (the stored centroids are fp16 values, so this B is
+// exact).  Accumulation is fp32 in the rotated basis; the combine applies Pi^T.
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr int kMfmaMaxG = 8;
+constexpr int kQpackCoef = 8;   // floats per head: k0..k4, padding
+
+// Per unit: [2 (q, sq)][32 rows][2 halves][d/32 chunks][16 bytes] of int8 digits, then
+// [8 heads][kQpackCoef] floats.
+__host__ __device__ constexpr size_t qpack_unit_bytes(int d) { return size_t(2) * 32 * 2 * (d / 32) * 16 + kMfmaMaxG * kQpackCoef * 4; }
+
+struct MfmaArgs {
+  const uint8_t *kbits;
+  const uint32_t *knorm;
+  const uint32_t *vcodes;
+  const uint16_t *vnorm;
+  const float *cv;
+  const uint8_t *qpack;
+  float *part;
+  float *scores;
+  int kbytes, tiles, capacity, length, chunk, splits, kv_heads, q_heads, G;
+  float scale_log2;
+};
+
+__device__ __forceinline__ uint32_t f16bits(float x) {
+  _Float16 h = (_Float16)x;
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+
+__device__ __forceinline__ float max32(float v) {   // max over the 32 lanes of a half
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float sum32(float v) {
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Query preparation for the MFMA path, one block per (batch, q-head) row: q_rot =
+// Pi RoPE(q, q_pos) (LDS FWHT), sq = S q_rot, their sums (kept in the fp32 rows for the
+// plain path as well), then the head's three int8 digit rows of the key-score A operand
+// and its score coefficients.  The first head of each kv-head also clears the unused
+// rows (digit 3, heads >= G) of its unit.
+__global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, int d, int m,
+                                                    int q_pos, float rope_base, CodecPtrs cp,
+                                                    float *qrows, int qstride, int q_heads,
+                                                    int G, uint8_t *qpack) {
+  extern __shared__ float qs[];   // d floats (q_rot), then m floats (sq)
+  float *sqs = qs + d;
+  __shared__ float red[4][4];
+  __shared__ int sexp[2];
+  const int rowi = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = rowi / q_heads, hq = rowi % q_heads;
+  const int g = hq / G, h = hq % G;
+  const int kv_heads = q_heads / G;
+  const size_t base = size_t(rowi) * d;
+  const int hh = d / 2;
+  if (rope_base != 0.0f) {
+    for (int j = tid; j < hh; j += 256) {
+      const double theta = pow(double(rope_base), -2.0 * double(j) / double(d));
+      double s, c;
+      sincos(double(q_pos) * theta, &s, &c);
+      const float x0 = load_elem(q, base + j, dtype), x1 = load_elem(q, base + j + hh, dtype);
+      qs[j] = (x0 * float(c) - x1 * float(s)) * cp.D[j];
+      qs[j + hh] = (x0 * float(s) + x1 * float(c)) * cp.D[j + hh];
     }
-    os[j] = v * invL;
+  } else {
+    for (int j = tid; j < d; j += 256) qs[j] = load_elem(q, base + j, dtype) * cp.D[j];
+  }
+  __syncthreads();
+  const int B = cp.block;
+  for (int st = 1; st < B; st <<= 1) {
+    for (int k = tid; k < d / 2; k += 256) {
+      const int blk = k / (B / 2), kk = k % (B / 2);
+      const int i = blk * B + (kk / st) * 2 * st + (kk % st);
+      const float x0 = qs[i], x1 = qs[i + st];
+      qs[i] = x0 + x1;
+      qs[i + st] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  for (int j = tid; j < d; j += 256) qs[j] *= cp.inv_sqrt_block;
+  __syncthreads();
+  for (int i = tid; i < m; i += 256) {
+    float z = 0.0f;
+    for (int j = 0; j < d; ++j) z = fmaf(cp.ST[size_t(j) * m + i], qs[j], z);
+    sqs[i] = z;
+  }
+  __syncthreads();
+  // fp32 rows and sums; maxima for the fixed-point scaling
+  float *o = qrows + size_t(rowi) * qstride;
+  float s0 = 0.0f, s1 = 0.0f, m0 = 0.0f, m1 = 0.0f;
+  for (int j = tid; j < d; j += 256) {
+    o[j] = qs[j];
+    s0 += qs[j];
+    m0 = fmaxf(m0, fabsf(qs[j]));
+  }
+  for (int i = tid; i < m; i += 256) {
+    o[d + i] = sqs[i];
+    s1 += sqs[i];
+    m1 = fmaxf(m1, fabsf(sqs[i]));
+  }
+  s0 = wave_sum(s0);
+  s1 = wave_sum(s1);
+  m0 = wave_max(m0);
+  m1 = wave_max(m1);
+  if (lane == 0) {
+    red[0][wv] = s0;
+    red[1][wv] = s1;
+    red[2][wv] = m0;
+    red[3][wv] = m1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const float S0 = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    const float S1 = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+    o[d + m] = S0;
+    o[d + m + 1] = S1;
+    for (int v = 0; v < 2; ++v) {
+      const float mx = fmaxf(fmaxf(red[2 + v][0], red[2 + v][1]), fmaxf(red[2 + v][2], red[2 + v][3]));
+      int e = 0;
+      if (mx > 0.0f) {
+        int ex;
+        frexpf(mx, &ex);   // mx < 2^ex
+        e = 22 - ex;
+      }
+      sexp[v] = e;
+    }
+    if (qpack) {
+      float *coef = reinterpret_cast<float *>(qpack + size_t(b * kv_heads + g) * qpack_unit_bytes(d) +
+                                              size_t(2) * 32 * 2 * (d / 32) * 16);
+      const float iq = ldexpf(1.0f, -sexp[0]), is = ldexpf(1.0f, -sexp[1]);
+      const float c0 = cp.ck[0], dc1 = cp.ck[1] - cp.ck[0], dc2 = cp.ck[2] - cp.ck[0];
+      float *k = coef + h * kQpackCoef;
+      k[0] = c0 * S0;
+      k[1] = dc1 * iq;
+      k[2] = dc2 * iq;
+      k[3] = 2.0f * cp.qjl_scale * is;
+      k[4] = cp.qjl_scale * S1;
+      k[5] = k[6] = k[7] = 0.0f;
+      if (h == 0)
+        for (int hz = G; hz < kMfmaMaxG; ++hz)
+          for (int i = 0; i < kQpackCoef; ++i) coef[hz * kQpackCoef + i] = 0.0f;
+    }
+  }
+  __syncthreads();
+  if (!qpack) return;
+  const int nch = d / 32;
+  uint32_t *o32 = reinterpret_cast<uint32_t *>(qpack + size_t(b * kv_heads + g) * qpack_unit_bytes(d));
+  // this head's rows digit * 8 + h, both vectors: [v][digit][half][chunk][e]
+  const int ndw = 2 * 3 * 2 * nch * 4;
+  for (int i = tid; i < ndw; i += 256) {
+    const int e = i & 3, c = (i >> 2) % nch, half = (i / (4 * nch)) & 1;
+    const int digit = (i / (8 * nch)) % 3, v = i / (24 * nch);
+    const float *src = v == 0 ? qs : sqs;
+    uint32_t word = 0u;
+#pragma unroll
+    for (int beta = 0; beta < 4; ++beta) {
+      const int j = 32 * (half * (d / 64) + (c >> 1)) + 8 * beta + 4 * (c & 1) + e;
+      const int xi = int(rintf(ldexpf(src[j], sexp[v])));
+      const int d0 = ((xi + 128) & 255) - 128;
+      const int x1 = (xi - d0) >> 8;
+      const int d1 = ((x1 + 128) & 255) - 128;
+      const int d2 = (x1 - d1) >> 8;
+      const int dg = digit == 0 ? d0 : (digit == 1 ? d1 : d2);
+      word |= uint32_t(dg & 255) << (8 * beta);
+    }
+    const int row = digit * 8 + h;
+    o32[(((v * 32 + row) * 2 + half) * nch + c) * 4 + e] = word;
+  }
+  if (h == 0) {
+    // rows of absent heads and the padding digit row group
+    const int nrow = 32 - 3 * G;
+    for (int i = tid; i < 2 * nrow * 2 * nch * 4; i += 256) {
+      const int e = i & 3, c = (i >> 2) % nch, half = (i / (4 * nch)) & 1;
+      const int ri = (i / (8 * nch)) % nrow, v = i / (8 * nch * nrow);
+      int row;
+      if (ri < 8) {
+        row = 24 + ri;
+      } else {
+        const int k = ri - 8;               // (digit, absent head) pairs
+        row = (k / (8 - G)) * 8 + G + k % (8 - G);
+      }
+      o32[(((v * 32 + row) * 2 + half) * nch + c) * 4 + e] = 0u;
+    }
+  }
+}
+
+// LDS-staged split-K decode.  Each wave streams its tiles through a ring of kRing LDS
+// slots filled by direct global->LDS loads (global_load_lds_dwordx3), two tiles ahead of
+// the one it computes, so the packed bytes in flight do not cost registers; the token
+// norms come one tile ahead in registers.  Per tile: int8 MFMA key scores, online
+// softmax, fp16 MFMA value accumulation, as in the register-fed kernel above.
+constexpr int kRing = 3;
+
+// Reads of a ring slot written by direct global->LDS loads.  They are inline assembly,
+// each block waiting for its own results (lgkmcnt(0)), because the compiler would
+// otherwise wait for every direct-to-LDS load in flight (including the prefetches into
+// the other slots) before any LDS read; the ring's own vmcnt waits order them instead.
+// the two value-code dwords of 8 value tiles (d = 128) or 4 (d = 64), 192 bytes apart
+template <int NT>
+__device__ __forceinline__ void lds_read_vals(uint32_t addr, uint32_t (&w)[NT][2]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (NT == 8) {
+    asm volatile(
+        "ds_read_b32 %0, %16\n"
+        "ds_read_b32 %1, %16 offset:4\n"
+        "ds_read_b32 %2, %16 offset:192\n"
+        "ds_read_b32 %3, %16 offset:196\n"
+        "ds_read_b32 %4, %16 offset:384\n"
+        "ds_read_b32 %5, %16 offset:388\n"
+        "ds_read_b32 %6, %16 offset:576\n"
+        "ds_read_b32 %7, %16 offset:580\n"
+        "ds_read_b32 %8, %16 offset:768\n"
+        "ds_read_b32 %9, %16 offset:772\n"
+        "ds_read_b32 %10, %16 offset:960\n"
+        "ds_read_b32 %11, %16 offset:964\n"
+        "ds_read_b32 %12, %16 offset:1152\n"
+        "ds_read_b32 %13, %16 offset:1156\n"
+        "ds_read_b32 %14, %16 offset:1344\n"
+        "ds_read_b32 %15, %16 offset:1348\n"
+        "s_waitcnt lgkmcnt(0)\n"
+        : "=v"(w[0][0]), "=v"(w[0][1]), "=v"(w[1][0]), "=v"(w[1][1]), "=v"(w[2][0]), "=v"(w[2][1]),
+          "=v"(w[3][0]), "=v"(w[3][1]), "=v"(w[4][0]), "=v"(w[4][1]), "=v"(w[5][0]), "=v"(w[5][1]),
+          "=v"(w[6][0]), "=v"(w[6][1]), "=v"(w[7][0]), "=v"(w[7][1])
+        : "v"(addr)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b32 %0, %8\n"
+        "ds_read_b32 %1, %8 offset:4\n"
+        "ds_read_b32 %2, %8 offset:192\n"
+        "ds_read_b32 %3, %8 offset:196\n"
+        "ds_read_b32 %4, %8 offset:384\n"
+        "ds_read_b32 %5, %8 offset:388\n"
+        "ds_read_b32 %6, %8 offset:576\n"
+        "ds_read_b32 %7, %8 offset:580\n"
+        "s_waitcnt lgkmcnt(0)\n"
+        : "=v"(w[0][0]), "=v"(w[0][1]), "=v"(w[1][0]), "=v"(w[1][1]), "=v"(w[2][0]), "=v"(w[2][1]),
+          "=v"(w[3][0]), "=v"(w[3][1])
+        : "v"(addr)
+        : "memory");
+  }
+#else
+  (void)addr;
+  (void)w;
+#endif
+}
+
+template <int D>
+struct LdsGeom {
+  static constexpr int KB = 3 * D / 8;     // key record bytes (2 planes + m = d sign bits)
+  static constexpr int KT = 32 * KB;       // key bytes per 32-token tile
+  static constexpr int VT = 12 * D;        // value-code bytes per 32-token tile
+  // direct-to-LDS loads land lane-contiguously for 4- and 16-byte sizes: keys of d = 128
+  // and all value tiles go as 16-byte chunks (96 or 48 lanes), the 24-byte key records of
+  // d = 64 (not 16-byte aligned in general) as dwords
+  static constexpr int KCH = D >= 128 ? 16 : 4;   // key chunk bytes
+  static constexpr int NK = (KT / KCH + 63) / 64; // key DMA instructions
+  static constexpr int NV = (VT / 16 + 63) / 64;  // value DMA instructions
+  static constexpr int NDMA = NK + NV + 2;        // + key norms + value norms
+  static constexpr int KN = KT + VT;       // offset of the 32 key norms (128 B)
+  static constexpr int VN = KN + 128;      // offset of the value norms (68 B: 17 dwords)
+  static constexpr int SLOT = VN + 80;
+};
+
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  // s_waitcnt with vmcnt = n and expcnt / lgkmcnt left at their "no wait" maxima (gfx9
+  // encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14])
+  switch (n) {
+    case 8: __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8)); break;
+    case 12: __builtin_amdgcn_s_waitcnt(12 | (7 << 4) | (15 << 8)); break;
+    default: __builtin_amdgcn_s_waitcnt(0); break;
+  }
+}
+
+__device__ __forceinline__ void wait_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
+  // The body is device code only (its local lambdas call device builtins); the host pass
+  // needs nothing but the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  using Gm = LdsGeom<D>;
+  constexpr int NCH = D / 32, NT = D / 16;
+  // one LDS array per ring slot: the loads in flight into the other slots are distinct
+  // memory from the slot being read
+  __shared__ __align__(16) uint8_t ring0[4][Gm::SLOT];
+  __shared__ __align__(16) uint8_t ring1[4][Gm::SLOT];
+  __shared__ __align__(16) uint8_t ring2[4][Gm::SLOT];
+  __shared__ uint2 lut[4096];
+  __shared__ __align__(16) _Float16 pt_s[4][16][40];
+  __shared__ __align__(16) float coef_s[2][5][4];
+  __shared__ float red_s[4][2][kMfmaMaxG];
+
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int unit = blockIdx.x, split = blockIdx.y;
+  const int b = unit / a.kv_heads, g = unit % a.kv_heads;
+  const int hq0 = g * a.G;
+  for (int i = tid; i < 4096; i += 256) {
+    const uint32_t h0 = f16bits(a.cv[i & 7]), h1 = f16bits(a.cv[(i >> 3) & 7]);
+    const uint32_t h2 = f16bits(a.cv[(i >> 6) & 7]), h3 = f16bits(a.cv[(i >> 9) & 7]);
+    lut[i] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+  }
+  const uint8_t *qpk = a.qpack + size_t(unit) * qpack_unit_bytes(D);
+  const float *coef = reinterpret_cast<const float *>(qpk + size_t(2) * 32 * 2 * NCH * 16);
+  if (tid < 40) {
+    const int hf = tid / 20, k = (tid / 4) % 5, r = tid % 4;
+    coef_s[hf][k][r] = coef[(4 * hf + r) * kQpackCoef + k];
+  }
+  const int row = lane & 31, half = lane >> 5;
+  v4i Aq[NCH], As[NCH];
+  {
+    const v4i *src = reinterpret_cast<const v4i *>(qpk);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      Aq[c] = src[((0 * 32 + row) * 2 + half) * NCH + c];
+      As[c] = src[((1 * 32 + row) * 2 + half) * NCH + c];
+    }
+  }
+  __syncthreads();
+
+  const int t_begin = split * a.chunk;
+  const int t_end = min(a.length, t_begin + a.chunk);
+  const size_t ubase = size_t(unit) * a.capacity;
+  const int t_first = t_begin + 32 * wv;
+  const int nk = t_end > t_first ? (t_end - t_first + 127) / 128 : 0;
+  float M[kMfmaMaxG], lsum[4];
+#pragma unroll
+  for (int h = 0; h < kMfmaMaxG; ++h) M[h] = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lsum[r] = 0.0f;
+  v4f acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int vq = lane >> 4, vn = lane & 15;
+  const int vidx = (24 * vq) >> 5, vsh = (24 * vq) & 31;
+  const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.vcodes) + size_t(unit) * a.tiles * Gm::VT;
+  const uint8_t *vnbase = reinterpret_cast<const uint8_t *>(a.vnorm);
+
+  // Tile k of this wave starts at t_first + 128 k.  Every chunk a lane loads stays inside
+  // the tokens [t0, t_end); tiles past the end reload the last one into a slot that is
+  // never read, so every step issues the same Gm::NDMA loads.
+  auto issue_dma = [&](int k, uint8_t *slot) {
+    const int kk = k < nk ? k : nk - 1;
+    const int t0 = t_first + 128 * kk;
+    const int nv = t_end - t0;   // valid tokens in the tile (1..32)
+    const uint8_t *ksrc = a.kbits + (ubase + t0) * Gm::KB;
+    const int last = nv * Gm::KB / Gm::KCH - 1;
+    constexpr int kchunks = Gm::KT / Gm::KCH;
+#pragma unroll
+    for (int i = 0; i < Gm::NK; ++i) {
+      if (64 * i + 64 <= kchunks || lane < kchunks - 64 * i) {
+        const int c = min(64 * i + lane, last);
+        __builtin_amdgcn_global_load_lds(ksrc + Gm::KCH * c, slot + 64 * Gm::KCH * i, Gm::KCH, 0, 0);
+      }
+    }
+    const uint8_t *vsrc = vbase + size_t(t0 / kValueTile) * Gm::VT;
+    constexpr int vchunks = Gm::VT / 16;
+#pragma unroll
+    for (int i = 0; i < Gm::NV; ++i) {
+      if (64 * i + 64 <= vchunks || lane < vchunks - 64 * i)
+        __builtin_amdgcn_global_load_lds(vsrc + 1024 * i + 16 * lane, slot + Gm::KT + 1024 * i, 16, 0, 0);
+    }
+    if (lane < 32) {
+      const uint32_t *kn = a.knorm + ubase + t0 + min(lane, nv - 1);
+      __builtin_amdgcn_global_load_lds(kn, slot + Gm::KN, 4, 0, 0);
+    }
+    if (lane < 17) {
+      // value norms: 17 dwords from the 4-byte boundary at or below token t0's norm
+      const size_t byte0 = (ubase + t0) * 2;
+      const size_t lastb = (ubase + t0 + nv - 1) * 2;
+      const size_t dw = min((byte0 & ~size_t(3)) + 4 * size_t(lane), lastb & ~size_t(3));
+      __builtin_amdgcn_global_load_lds(vnbase + dw, slot + Gm::VN, 4, 0, 0);
+    }
+  };
+
+  auto step = [&](int k, const uint8_t *slot, uint8_t *nxt2) {
+    wait_lgkm0();                 // reads of the slot refilled below are complete
+    issue_dma(k + 2, nxt2);
+    if (a.scores)
+      __builtin_amdgcn_s_waitcnt(0);
+    else
+      wait_vmcnt_le(2 * Gm::NDMA);   // this tile's loads are the oldest still counted
+    const int t0 = t_first + 128 * k;
+    const int t = t0 + row;
+    const bool valid = t < t_end;
+    const uint32_t sbase = uint32_t(reinterpret_cast<uintptr_t>(slot));
+    // ---- this lane's key words and its token's norms
+    uint2 kw[3];
+    uint32_t nr, vnb;
+    {
+      const uint32_t kaddr = sbase + row * Gm::KB + half * (D / 16);
+      const uint32_t naddr = sbase + Gm::KN + 4 * row;
+      const uint32_t vaddr = sbase + Gm::VN + uint32_t(((ubase + t0) * 2) & 3) + 2 * row;
+#if defined(__HIP_DEVICE_COMPILE__)
+      if constexpr (D >= 128) {
+        asm volatile(
+            "ds_read_b64 %0, %5\n"
+            "ds_read_b64 %1, %5 offset:16\n"
+            "ds_read_b64 %2, %5 offset:32\n"
+            "ds_read_b32 %3, %6\n"
+            "ds_read_u16 %4, %7\n"
+            "s_waitcnt lgkmcnt(0)\n"
+            : "=v"(kw[0]), "=v"(kw[1]), "=v"(kw[2]), "=v"(nr), "=v"(vnb)
+            : "v"(kaddr), "v"(naddr), "v"(vaddr)
+            : "memory");
+      } else {
+        uint32_t x0, x1, x2;
+        asm volatile(
+            "ds_read_b32 %0, %5\n"
+            "ds_read_b32 %1, %5 offset:8\n"
+            "ds_read_b32 %2, %5 offset:16\n"
+            "ds_read_b32 %3, %6\n"
+            "ds_read_u16 %4, %7\n"
+            "s_waitcnt lgkmcnt(0)\n"
+            : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(nr), "=v"(vnb)
+            : "v"(kaddr), "v"(naddr), "v"(vaddr)
+            : "memory");
+        kw[0] = make_uint2(x0, 0u);
+        kw[1] = make_uint2(x1, 0u);
+        kw[2] = make_uint2(x2, 0u);
+      }
+#else
+      (void)kaddr;
+      (void)naddr;
+      (void)vaddr;
+      nr = vnb = 0u;
+      kw[0] = kw[1] = kw[2] = make_uint2(0u, 0u);
+#endif
+    }
+    // ---- key scores on int8 MFMA
+    v16i s0 = {}, s1 = {}, s2 = {};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint32_t w0 = (c >> 1) ? kw[0].y : kw[0].x;
+      const uint32_t w1 = (c >> 1) ? kw[1].y : kw[1].x;
+      const uint32_t w2 = (c >> 1) ? kw[2].y : kw[2].x;
+      v4i b0, b1, b2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int sh = 4 * (c & 1) + e;
+        b0[e] = int((w0 >> sh) & 0x01010101u);
+        b1[e] = int((w1 >> sh) & 0x01010101u);
+        b2[e] = int((w2 >> sh) & 0x01010101u);
+      }
+      s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq[c], b0, s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq[c], b1, s1, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(As[c], b2, s2, 0, 0, 0);
+    }
+    const float n16 = f16_bits_to_float(nr & 0xFFFFu), rn16 = f16_bits_to_float(nr >> 16);
+    const float vnorm = f16_bits_to_float(vnb & 0xFFFFu);
+    const float4 k0 = *reinterpret_cast<const float4 *>(coef_s[half][0]);
+    const float4 k1 = *reinterpret_cast<const float4 *>(coef_s[half][1]);
+    const float4 k2 = *reinterpret_cast<const float4 *>(coef_s[half][2]);
+    const float4 k3 = *reinterpret_cast<const float4 *>(coef_s[half][3]);
+    const float4 k4 = *reinterpret_cast<const float4 *>(coef_s[half][4]);
+    const float K0[4] = {k0.x, k0.y, k0.z, k0.w}, K1[4] = {k1.x, k1.y, k1.z, k1.w};
+    const float K2[4] = {k2.x, k2.y, k2.z, k2.w}, K3[4] = {k3.x, k3.y, k3.z, k3.w};
+    const float K4[4] = {k4.x, k4.y, k4.z, k4.w};
+    float lam[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int S0 = s0[r] + 256 * s0[4 + r] + 65536 * s0[8 + r];
+      const int S1 = s1[r] + 256 * s1[4 + r] + 65536 * s1[8 + r];
+      const int S2 = s2[r] + 256 * s2[4 + r] + 65536 * s2[8 + r];
+      const float score = n16 * (K0[r] + K1[r] * float(S0) + K2[r] * float(S1)) +
+                          rn16 * (K3[r] * float(S2) - K4[r]);
+      const int h = 4 * half + r;
+      const bool live = valid && h < a.G;
+      if (live && a.scores) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.length + t] = score;
+      lam[r] = live ? score * a.scale_log2 : -INFINITY;
+    }
+    // ---- online softmax (log2 domain); the running maxima are wave-uniform
+    float tm[kMfmaMaxG];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mine = max32(lam[r]);
+      const float other = __shfl_xor(mine, 32, 64);
+      tm[r] = half ? other : mine;
+      tm[4 + r] = half ? mine : other;
+    }
+    bool grow = false;
+    float alpha[kMfmaMaxG];
+#pragma unroll
+    for (int h = 0; h < kMfmaMaxG; ++h) {
+      const float nm = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(fmaxf(M[h], tm[h]))));
+      alpha[h] = (nm == -INFINITY || nm == M[h]) ? 1.0f : exp2f(M[h] - nm);
+      grow |= (nm != M[h]);
+      M[h] = nm;
+    }
+    if (grow) {
+      // accumulator row 4 vq + r holds head 4 (vq & 1) + r
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float al = (vq & 1) ? alpha[4 + r] : alpha[r];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= al;
+        lsum[r] *= half ? alpha[4 + r] : alpha[r];
+      }
+    }
+    float mh[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mh[r] = half ? M[4 + r] : M[r];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * half + r;
+      const float p = lam[r] == -INFINITY ? 0.0f : exp2f(lam[r] - mh[r]);
+      lsum[r] += p;
+      const float pv = p * vnorm;
+      const _Float16 hi = (_Float16)pv;
+      const _Float16 lo = (_Float16)(pv - float(hi));
+      pt_s[wv][h][row] = hi;
+      pt_s[wv][8 + h][row] = lo;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const v8h A = *reinterpret_cast<const v8h *>(&pt_s[wv][vn][8 * vq]);
+    uint32_t vwr[NT][2];
+    lds_read_vals<NT>(sbase + Gm::KT + vn * 12 + 4 * vidx, vwr);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t lo = vwr[nt][0];
+      const uint32_t hi = vidx < 2 ? vwr[nt][1] : 0u;
+      const uint32_t x = uint32_t(((uint64_t(hi) << 32) | lo) >> vsh);
+      const uint2 e0 = lut[x & 0xFFFu], e1 = lut[(x >> 12) & 0xFFFu];
+      v4i bw = {int(e0.x), int(e0.y), int(e1.x), int(e1.y)};
+      v8h Bv;
+      __builtin_memcpy(&Bv, &bw, 16);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bv, acc[nt], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  };
+
+  if (nk > 0) {
+    uint8_t *r0 = &ring0[wv][0], *r1 = &ring1[wv][0], *r2 = &ring2[wv][0];
+    issue_dma(0, r0);
+    issue_dma(1, r1);
+    for (int k = 0; k < nk; k += kRing) {
+      step(k, r0, r2);
+      if (k + 1 < nk) step(k + 1, r1, r0);
+      if (k + 2 < nk) step(k + 2, r2, r1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);   // drain the tail loads before the slots are reused
+  }
+  // ---- merge the block's waves
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lsum[r] = sum32(lsum[r]);
+  __syncthreads();
+  float *acc_s = reinterpret_cast<float *>(lut);   // [4 waves][16 rows][D]
+  if (lane == 0 || lane == 32) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red_s[wv][1][4 * half + r] = lsum[r];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < kMfmaMaxG; ++h) red_s[wv][0][h] = M[h];
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc_s[(wv * 16 + 4 * vq + r) * D + 16 * nt + vn] = acc[nt][r];
+  __syncthreads();
+  for (int i = tid; i < a.G * D; i += 256) {
+    const int h = i / D, j = i % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red_s[w][0][h]);
+    float v = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = red_s[w][0][h];
+      if (mw == -INFINITY) continue;
+      const float f = exp2f(mw - mx);
+      v += (acc_s[(w * 16 + h) * D + j] + acc_s[(w * 16 + 8 + h) * D + j]) * f;
+      L += red_s[w][1][h] * f;
+    }
+    float *o = a.part + ((size_t(b * a.q_heads + hq0 + h) * a.splits) + split) * (D + 2);
+    o[j] = v;
+    if (j == 0) {
+      o[D] = mx == -INFINITY ? -INFINITY : mx * 0.69314718055994531f;
+      o[D + 1] = L;
+    }
+  }
+#else
+  (void)a;
+#endif
+}
+
+// Merge of the splits and inverse rotation: out = D .* (H o) / sqrt(B) = Pi^T o.
+// One block per (batch, q-head) row; split maxima and sums go through LDS first.
+__global__ __launch_bounds__(256) void k_decode_merge(const float *part, int splits, int d,
+                                                      CodecPtrs cp, float *out) {
+  extern __shared__ float ms[];   // [splits] weights, then d outputs
+  float *os = ms + splits;
+  __shared__ float red[2][4];
+  const int rowi = blockIdx.x, tid = threadIdx.x;
+  const float *pr = part + size_t(rowi) * splits * (d + 2);
+  float mx = -INFINITY;
+  for (int s = tid; s < splits; s += 256) mx = fmaxf(mx, pr[size_t(s) * (d + 2) + d]);
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) red[0][tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  float L = 0.0f;
+  for (int s = tid; s < splits; s += 256) {
+    const float m_s = pr[size_t(s) * (d + 2) + d];
+    const float w = m_s == -INFINITY ? 0.0f : __expf(m_s - mx);
+    ms[s] = w;
+    L += w * pr[size_t(s) * (d + 2) + d + 1];
+  }
+  L = wave_sum(L);
+  if ((tid & 63) == 0) red[1][tid >> 6] = L;
+  __syncthreads();
+  L = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const float invL = L > 0.0f ? 1.0f / L : 0.0f;
+  for (int j = tid; j < d; j += 256) {
+    float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
+    int s = 0;
+    for (; s + 4 <= splits; s += 4) {
+      v0 += pr[size_t(s) * (d + 2) + j] * ms[s];
+      v1 += pr[size_t(s + 1) * (d + 2) + j] * ms[s + 1];
+      v2 += pr[size_t(s + 2) * (d + 2) + j] * ms[s + 2];
+      v3 += pr[size_t(s + 3) * (d + 2) + j] * ms[s + 3];
+    }
+    for (; s < splits; ++s) v0 += pr[size_t(s) * (d + 2) + j] * ms[s];
+    os[j] = ((v0 + v1) + (v2 + v3)) * invL;
   }
   __syncthreads();
   const int B = cp.block;
   for (int hh = 1; hh < B; hh <<= 1) {
-    for (int k = tid; k < d / 2; k += blockDim.x) {
+    for (int k = tid; k < d / 2; k += 256) {
       const int blk = k / (B / 2), kk = k % (B / 2);
       const int i = blk * B + (kk / hh) * 2 * hh + (kk % hh);
       const float x0 = os[i], x1 = os[i + hh];
@@ -883,7 +1439,7 @@ __global__ __launch_bounds__(256) void k_decode_combine(const float *part, int s
     }
     __syncthreads();
   }
-  for (int j = tid; j < d; j += blockDim.x) out[size_t(row) * d + j] = os[j] * cp.inv_sqrt_block * cp.D[j];
+  for (int j = tid; j < d; j += 256) out[size_t(rowi) * d + j] = os[j] * cp.inv_sqrt_block * cp.D[j];
 }
 
 // ------------------------------------------------------------------ search
@@ -1067,21 +1623,37 @@ bool decode_supported(const tq_cache_desc &c) {
   return (c.d == 64 || c.d == 128) && c.bits_v > 0;
 }
 
+// The MFMA path covers the 2-bit + QJL (m = d) keys, 3-bit values configuration.
+bool decode_mfma_path(const tq_cache_desc &c, int q_heads) {
+  return (c.d == 64 || c.d == 128) && c.bits_k == 2 && c.bits_v == 3 && c.m == c.d &&
+         q_heads / c.kv_heads <= kMfmaMaxG;
+}
+
+constexpr int kMfmaChunk = 128;   // tokens per block iteration (4 waves x 32)
+
 int default_splits(const tq_cache_desc &c, int length) {
   if (length <= 0) return 1;
   const int units = c.batch * c.kv_heads;
-  const int by_len = (length + 255) / 256;
-  const int want = (4096 + units - 1) / units;
+  const int by_len = (length + kMfmaChunk - 1) / kMfmaChunk;
+  const int want = (2048 + units - 1) / units;
   int s = by_len < want ? by_len : want;
   if (s < 1) s = 1;
   if (s > 4096) s = 4096;
   return s;
 }
 
+// Tokens per split: a multiple of 128 so that every block works on whole 32-token tiles.
+int split_chunk(int length, int splits) {
+  const int per = (length + splits - 1) / splits;
+  return (per + kMfmaChunk - 1) / kMfmaChunk * kMfmaChunk;
+}
+
 size_t decode_ws(const tq_cache_desc &c, int q_heads, int splits) {
   const size_t rows = size_t(c.batch) * q_heads;
   const size_t qstride = size_t(c.d) + c.m + 2;
-  return align256(rows * qstride * 4) + align256(rows * size_t(splits) * (c.d + 2) * 4);
+  const size_t units = size_t(c.batch) * c.kv_heads;
+  return align256(rows * qstride * 4) + align256(units * qpack_unit_bytes(c.d)) +
+         align256(rows * size_t(splits) * (c.d + 2) * 4);
 }
 
 int search_tiles(int n_db) { return (n_db + kSearchTile - 1) / kSearchTile; }
@@ -1225,45 +1797,82 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
   const CodecPtrs cp = codec_ptrs(codec_dev, d, desc->bits_k, desc->bits_v, m);
   float *qp = static_cast<float *>(ws);
   const int qstride = d + m + 2;
-  float *part = reinterpret_cast<float *>(static_cast<uint8_t *>(ws) + align256(size_t(rows) * qstride * 4));
-  hipLaunchKernelGGL(k_qprep, dim3(rows), dim3(256), d * 4, s, q, int(dtype), d, m, q_pos,
-                     rope_base, cp, qp, qstride);
-  DecodeArgs a;
+  const int units = desc->batch * desc->kv_heads;
+  uint8_t *qpack = static_cast<uint8_t *>(ws) + align256(size_t(rows) * qstride * 4);
+  float *part = reinterpret_cast<float *>(qpack + align256(size_t(units) * qpack_unit_bytes(d)));
+  const int G = q_heads / desc->kv_heads;
+  const float sc = scale == 0.0f ? float(1.0 / std::sqrt(double(d))) : scale;
+  const bool mfma = decode_mfma_path(*desc, q_heads);
+  // symmetric 2-bit codebook on the MFMA path: c[code] = c0 + (c1 - c0) b0 + (c2 - c0) b1
+  hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m) * 4, s, q, int(dtype), d,
+                     m, q_pos, rope_base, cp, qp, qstride, q_heads, G, mfma ? qpack : nullptr);
   const CachePtrs ch = cache_ptrs(const_cast<void *>(cache_dev), *desc);
-  a.cp = cp;
-  a.kbits = ch.kbits;
-  a.knorm = ch.knorm;
-  a.vcodes = ch.vcodes;
-  a.vnorm = ch.vnorm;
-  a.kbytes = ch.kbytes;
-  a.tiles = ch.tiles;
-  a.capacity = desc->capacity;
-  a.bits_k = desc->bits_k;
-  a.bits_v = desc->bits_v;
-  a.m = m;
-  a.kv_heads = desc->kv_heads;
-  a.q_heads = q_heads;
-  a.G = q_heads / desc->kv_heads;
-  a.length = length;
-  a.splits = S;
-  a.chunk = (length + S - 1) / S;
-  a.scale = scale == 0.0f ? float(1.0 / std::sqrt(double(d))) : scale;
-  a.qp = qp;
-  a.qstride = qstride;
-  a.part = part;
-  a.scores = scores;
-  const size_t shm = (size_t(kMaxG) * d + size_t(kMaxG) * m + size_t(kMaxG) * kDecThreads +
-                      4 * kMaxG) * 4;
-  // the value-phase partial sums reuse the p region: (256 / d) * kMaxG * d floats
-  const size_t shm_all = shm;
-  dim3 grid(desc->batch * desc->kv_heads, S);
-  if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
-  if (d == 64)
-    hipLaunchKernelGGL(k_decode_split<64>, grid, dim3(kDecThreads), shm_all, s, a);
-  else
-    hipLaunchKernelGGL(k_decode_split<128>, grid, dim3(kDecThreads), shm_all, s, a);
-  if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
-  hipLaunchKernelGGL(k_decode_combine, dim3(rows), dim3(128), d * 4, s, part, S, d, cp, out);
+  int used_splits = S;
+  if (mfma) {
+    const int chunk = split_chunk(length, S);
+    used_splits = (length + chunk - 1) / chunk;
+    MfmaArgs ma;
+    ma.kbits = ch.kbits;
+    ma.knorm = ch.knorm;
+    ma.vcodes = ch.vcodes;
+    ma.vnorm = ch.vnorm;
+    ma.cv = cp.cv;
+    ma.qpack = qpack;
+    ma.part = part;
+    ma.scores = scores;
+    ma.kbytes = ch.kbytes;
+    ma.tiles = ch.tiles;
+    ma.capacity = desc->capacity;
+    ma.length = length;
+    ma.chunk = chunk;
+    ma.splits = used_splits;
+    ma.kv_heads = desc->kv_heads;
+    ma.q_heads = q_heads;
+    ma.G = G;
+    ma.scale_log2 = sc * 1.4426950408889634f;
+    dim3 grid(units, used_splits);
+    if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
+    if (d == 64)
+      hipLaunchKernelGGL(k_decode_lds<64>, grid, dim3(256), 0, s, ma);
+    else
+      hipLaunchKernelGGL(k_decode_lds<128>, grid, dim3(256), 0, s, ma);
+    if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
+  } else {
+    DecodeArgs a;
+    a.cp = cp;
+    a.kbits = ch.kbits;
+    a.knorm = ch.knorm;
+    a.vcodes = ch.vcodes;
+    a.vnorm = ch.vnorm;
+    a.kbytes = ch.kbytes;
+    a.tiles = ch.tiles;
+    a.capacity = desc->capacity;
+    a.bits_k = desc->bits_k;
+    a.bits_v = desc->bits_v;
+    a.m = m;
+    a.kv_heads = desc->kv_heads;
+    a.q_heads = q_heads;
+    a.G = G;
+    a.length = length;
+    a.splits = S;
+    a.chunk = (length + S - 1) / S;
+    a.scale = sc;
+    a.qp = qp;
+    a.qstride = qstride;
+    a.part = part;
+    a.scores = scores;
+    const size_t shm = (size_t(kMaxG) * d + size_t(kMaxG) * m + size_t(kMaxG) * kDecThreads +
+                        4 * kMaxG) * 4;
+    dim3 grid(units, S);
+    if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
+    if (d == 64)
+      hipLaunchKernelGGL(k_decode_split<64>, grid, dim3(kDecThreads), shm, s, a);
+    else
+      hipLaunchKernelGGL(k_decode_split<128>, grid, dim3(kDecThreads), shm, s, a);
+    if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
+  }
+  hipLaunchKernelGGL(k_decode_merge, dim3(rows), dim3(256), size_t(used_splits + d) * 4, s, part,
+                     used_splits, d, cp, out);
   return launch_status();
 }
 
@@ -1317,8 +1926,9 @@ tq_status tq_search_topk(const tq_cache_desc *db, const void *codec_dev, const v
   uint8_t *wb = static_cast<uint8_t *>(ws);
   float *cand_s = reinterpret_cast<float *>(wb + align256(size_t(nq) * qstride * 4));
   int *cand_i = reinterpret_cast<int *>(wb + align256(size_t(nq) * qstride * 4) + align256(cand * 4));
-  hipLaunchKernelGGL(k_qprep, dim3(nq), dim3(256), d * 4, s, static_cast<const void *>(queries),
-                     int(TQ_F32), d, m, 0, 0.0f, cp, qp, qstride);
+  hipLaunchKernelGGL(k_qprep_pack, dim3(nq), dim3(256), size_t(d + m) * 4, s,
+                     static_cast<const void *>(queries), int(TQ_F32), d, m, 0, 0.0f, cp, qp, qstride,
+                     nq, 1, static_cast<uint8_t *>(nullptr));
   if (n_db > 0) {
     SearchArgs a;
     const CachePtrs ch = cache_ptrs(const_cast<void *>(db_cache), *db);
