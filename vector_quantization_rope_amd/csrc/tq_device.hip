@@ -830,6 +830,26 @@ __device__ __forceinline__ float max32(float v) {   // max over the 32 lanes of 
   return v;
 }
 
+// Max over each group of 32 lanes with DPP row operations: within rows of 16 (quad
+// swaps, half-row mirror, row mirror), then row_bcast15 folds row 0 into row 1 and row 2
+// into row 3; the group maxima end up in lanes 31 and 63.  The floats are compared as
+// integers under the order-preserving map x -> x ^ ((x >> 31) & 0x7fffffff), which keeps
+// the reduction free of NaN canonicalization and lets the moves fold into v_max_i32_dpp.
+__device__ __forceinline__ int f2ord(float v) {
+  const int x = __float_as_int(v);
+  return x ^ ((x >> 31) & 0x7fffffff);
+}
+__device__ __forceinline__ float ord2f(int x) { return __int_as_float(x ^ ((x >> 31) & 0x7fffffff)); }
+
+__device__ __forceinline__ int dpp_max32_tail(int x) {
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x142, 0xA, 0xF, false));
+  return x;
+}
+
 __device__ __forceinline__ float sum32(float v) {
 #pragma unroll
   for (int o = 1; o < 32; o <<= 1) v += __shfl_xor(v, o, 64);
@@ -845,7 +865,7 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
                                                     int q_pos, float rope_base, CodecPtrs cp,
                                                     float *qrows, int qstride, int q_heads,
                                                     int G, uint8_t *qpack) {
-  extern __shared__ float qs[];   // d floats (q_rot), then m floats (sq)
+  extern __shared__ float qs[];   // d floats (q_rot), m floats (sq), max(1024, m) partial sums
   float *sqs = qs + d;
   __shared__ float red[4][4];
   __shared__ int sexp[2];
@@ -881,10 +901,40 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
   }
   for (int j = tid; j < d; j += 256) qs[j] *= cp.inv_sqrt_block;
   __syncthreads();
-  for (int i = tid; i < m; i += 256) {
-    float z = 0.0f;
-    for (int j = 0; j < d; ++j) z = fmaf(cp.ST[size_t(j) * m + i], qs[j], z);
-    sqs[i] = z;
+  // sq = S q_rot: each thread takes 4 consecutive outputs (a float4 of a row of S^T) over
+  // one of `slices` slices of the inner dimension; the slices are summed through LDS
+  if (m > 0) {
+    const int g4 = m / 4;
+    int slices = 1;                                 // largest power of two <= 256 / g4
+    while (2 * slices * g4 <= 256) slices *= 2;
+    const int jl = d / slices;
+    float *part = sqs + m;                          // [slices][m] (shared with the final sq)
+    for (int og = tid % g4 + (tid / g4 >= slices ? g4 : 0), sl = tid / g4; og < g4; og += 256) {
+      const int j0 = (slices > 1 ? sl : 0) * jl, j1 = slices > 1 ? j0 + jl : d;
+      float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 *st = reinterpret_cast<const float4 *>(cp.ST) + og;
+#pragma unroll 8
+      for (int j = j0; j < j1; ++j) {
+        const float4 sv = st[size_t(j) * g4];
+        const float x = qs[j];
+        z.x = fmaf(sv.x, x, z.x);
+        z.y = fmaf(sv.y, x, z.y);
+        z.z = fmaf(sv.z, x, z.z);
+        z.w = fmaf(sv.w, x, z.w);
+      }
+      float *o4 = part + (slices > 1 ? sl : 0) * m + 4 * og;
+      o4[0] = z.x;
+      o4[1] = z.y;
+      o4[2] = z.z;
+      o4[3] = z.w;
+      if (slices > 1) break;
+    }
+    __syncthreads();
+    for (int i = tid; i < m; i += 256) {
+      float z = 0.0f;
+      for (int sl = 0; sl < slices; ++sl) z += part[sl * m + i];
+      sqs[i] = z;
+    }
   }
   __syncthreads();
   // fp32 rows and sums; maxima for the fixed-point scaling
@@ -1260,38 +1310,42 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
     const float K0[4] = {k0.x, k0.y, k0.z, k0.w}, K1[4] = {k1.x, k1.y, k1.z, k1.w};
     const float K2[4] = {k2.x, k2.y, k2.z, k2.w}, K3[4] = {k3.x, k3.y, k3.z, k3.w};
     const float K4[4] = {k4.x, k4.y, k4.z, k4.w};
-    float lam[4];
+    float lam[4], sc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int S0 = s0[r] + 256 * s0[4 + r] + 65536 * s0[8 + r];
       const int S1 = s1[r] + 256 * s1[4 + r] + 65536 * s1[8 + r];
       const int S2 = s2[r] + 256 * s2[4 + r] + 65536 * s2[8 + r];
-      const float score = n16 * (K0[r] + K1[r] * float(S0) + K2[r] * float(S1)) +
-                          rn16 * (K3[r] * float(S2) - K4[r]);
-      const int h = 4 * half + r;
-      const bool live = valid && h < a.G;
-      if (live && a.scores) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.length + t] = score;
-      lam[r] = live ? score * a.scale_log2 : -INFINITY;
+      sc[r] = n16 * (K0[r] + K1[r] * float(S0) + K2[r] * float(S1)) + rn16 * (K3[r] * float(S2) - K4[r]);
+      lam[r] = (valid && 4 * half + r < a.G) ? sc[r] * a.scale_log2 : -INFINITY;
     }
-    // ---- online softmax (log2 domain); the running maxima are wave-uniform
-    float tm[kMfmaMaxG];
+    if (a.scores) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mine = max32(lam[r]);
-      const float other = __shfl_xor(mine, 32, 64);
-      tm[r] = half ? other : mine;
-      tm[4 + r] = half ? mine : other;
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * half + r;
+        if (valid && h < a.G) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.length + t] = sc[r];
+      }
     }
-    bool grow = false;
-    float alpha[kMfmaMaxG];
+    // ---- online softmax (log2 domain); tile maxima and running maxima are wave-uniform.
+    // The tile maxima are reduced only when some score exceeds its head's running max.
+    bool above = false;
 #pragma unroll
-    for (int h = 0; h < kMfmaMaxG; ++h) {
-      const float nm = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(fmaxf(M[h], tm[h]))));
-      alpha[h] = (nm == -INFINITY || nm == M[h]) ? 1.0f : exp2f(M[h] - nm);
-      grow |= (nm != M[h]);
-      M[h] = nm;
-    }
-    if (grow) {
+    for (int r = 0; r < 4; ++r) above |= lam[r] > (half ? M[4 + r] : M[r]);
+    if (__builtin_amdgcn_ballot_w64(above) != 0) {
+      float tm[kMfmaMaxG];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int v = dpp_max32_tail(f2ord(lam[r]));
+        tm[r] = ord2f(__builtin_amdgcn_readlane(v, 31));
+        tm[4 + r] = ord2f(__builtin_amdgcn_readlane(v, 63));
+      }
+      float alpha[kMfmaMaxG];
+#pragma unroll
+      for (int h = 0; h < kMfmaMaxG; ++h) {
+        const float nm = fmaxf(M[h], tm[h]);
+        alpha[h] = (nm == M[h]) ? 1.0f : __builtin_amdgcn_exp2f(M[h] - nm);
+        M[h] = nm;
+      }
       // accumulator row 4 vq + r holds head 4 (vq & 1) + r
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1301,13 +1355,11 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
         lsum[r] *= half ? alpha[4 + r] : alpha[r];
       }
     }
-    float mh[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mh[r] = half ? M[4 + r] : M[r];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * half + r;
-      const float p = lam[r] == -INFINITY ? 0.0f : exp2f(lam[r] - mh[r]);
+      const float mh = half ? M[4 + r] : M[r];
+      const float p = lam[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lam[r] - mh);
       lsum[r] += p;
       const float pv = p * vnorm;
       const _Float16 hi = (_Float16)pv;
@@ -1392,7 +1444,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
 // One block per (batch, q-head) row; split maxima and sums go through LDS first.
 __global__ __launch_bounds__(256) void k_decode_merge(const float *part, int splits, int d,
                                                       CodecPtrs cp, float *out) {
-  extern __shared__ float ms[];   // [splits] weights, then d outputs
+  extern __shared__ float ms[];   // [splits] weights, d outputs, then [256 / d][d] partial sums
   float *os = ms + splits;
   __shared__ float red[2][4];
   const int rowi = blockIdx.x, tid = threadIdx.x;
@@ -1415,17 +1467,25 @@ __global__ __launch_bounds__(256) void k_decode_merge(const float *part, int spl
   __syncthreads();
   L = red[1][0] + red[1][1] + red[1][2] + red[1][3];
   const float invL = L > 0.0f ? 1.0f / L : 0.0f;
-  for (int j = tid; j < d; j += 256) {
-    float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f, v3 = 0.0f;
-    int s = 0;
-    for (; s + 4 <= splits; s += 4) {
-      v0 += pr[size_t(s) * (d + 2) + j] * ms[s];
-      v1 += pr[size_t(s + 1) * (d + 2) + j] * ms[s + 1];
-      v2 += pr[size_t(s + 2) * (d + 2) + j] * ms[s + 2];
-      v3 += pr[size_t(s + 3) * (d + 2) + j] * ms[s + 3];
+  // coordinate j over the splits of one parity class per thread group, 8 loads in flight
+  const int groups = 256 / d > 0 ? 256 / d : 1;
+  float *acc2 = os + d;   // [groups][d]
+  for (int jt = tid; jt < d * groups; jt += 256) {
+    const int j = jt % d, g0 = jt / d;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int s = g0;
+    for (; s + 7 * groups < splits; s += 8 * groups) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] += pr[size_t(s + u * groups) * (d + 2) + j] * ms[s + u * groups];
     }
-    for (; s < splits; ++s) v0 += pr[size_t(s) * (d + 2) + j] * ms[s];
-    os[j] = ((v0 + v1) + (v2 + v3)) * invL;
+    for (; s < splits; s += groups) v[0] += pr[size_t(s) * (d + 2) + j] * ms[s];
+    acc2[g0 * d + j] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+  }
+  __syncthreads();
+  for (int j = tid; j < d; j += 256) {
+    float v = 0.0f;
+    for (int g0 = 0; g0 < groups; ++g0) v += acc2[g0 * d + j];
+    os[j] = v * invL;
   }
   __syncthreads();
   const int B = cp.block;
@@ -1635,7 +1695,7 @@ int default_splits(const tq_cache_desc &c, int length) {
   if (length <= 0) return 1;
   const int units = c.batch * c.kv_heads;
   const int by_len = (length + kMfmaChunk - 1) / kMfmaChunk;
-  const int want = (2048 + units - 1) / units;
+  const int want = (1024 + units - 1) / units;
   int s = by_len < want ? by_len : want;
   if (s < 1) s = 1;
   if (s > 4096) s = 4096;
@@ -1804,7 +1864,7 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
   const float sc = scale == 0.0f ? float(1.0 / std::sqrt(double(d))) : scale;
   const bool mfma = decode_mfma_path(*desc, q_heads);
   // symmetric 2-bit codebook on the MFMA path: c[code] = c0 + (c1 - c0) b0 + (c2 - c0) b1
-  hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m) * 4, s, q, int(dtype), d,
+  hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s, q, int(dtype), d,
                      m, q_pos, rope_base, cp, qp, qstride, q_heads, G, mfma ? qpack : nullptr);
   const CachePtrs ch = cache_ptrs(const_cast<void *>(cache_dev), *desc);
   int used_splits = S;
@@ -1871,7 +1931,7 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
       hipLaunchKernelGGL(k_decode_split<128>, grid, dim3(kDecThreads), shm, s, a);
     if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
   }
-  hipLaunchKernelGGL(k_decode_merge, dim3(rows), dim3(256), size_t(used_splits + d) * 4, s, part,
+  hipLaunchKernelGGL(k_decode_merge, dim3(rows), dim3(256), size_t(used_splits + d + 256 + d) * 4, s, part,
                      used_splits, d, cp, out);
   return launch_status();
 }
@@ -1926,7 +1986,7 @@ tq_status tq_search_topk(const tq_cache_desc *db, const void *codec_dev, const v
   uint8_t *wb = static_cast<uint8_t *>(ws);
   float *cand_s = reinterpret_cast<float *>(wb + align256(size_t(nq) * qstride * 4));
   int *cand_i = reinterpret_cast<int *>(wb + align256(size_t(nq) * qstride * 4) + align256(cand * 4));
-  hipLaunchKernelGGL(k_qprep_pack, dim3(nq), dim3(256), size_t(d + m) * 4, s,
+  hipLaunchKernelGGL(k_qprep_pack, dim3(nq), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s,
                      static_cast<const void *>(queries), int(TQ_F32), d, m, 0, 0.0f, cp, qp, qstride,
                      nq, 1, static_cast<uint8_t *>(nullptr));
   if (n_db > 0) {
