@@ -35,7 +35,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 KEY_RECORD = 52      # bytes per token per kv-head: 2-bit planes 32 + signs 16 + 2 fp16 norms
 VALUE_RECORD = 50    # 3-bit codes 48 + fp16 norm
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_split_long_context_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_lds_long_context_counters.txt")
 DEVICE_SRC = os.path.join(ROOT, "vector_quantization_rope_amd", "csrc", "tq_device.hip")
 
 
@@ -97,38 +97,45 @@ def traffic_from_counters(launch_bytes: float):
     return c.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(w, K, V, q, units_total: int):
-    """Time the CPU oracle on one (batch, kv-head) unit of the same workload."""
+def cpu_baseline(w, K, V, q, units_total: int, n_units: int = 8):
+    """Time the CPU oracle on a bounded sample of the same workload: the first `n_units`
+    (batch, kv-head) units, each encoded (all its keys and values) and attended by its
+    G q-heads over all its tokens."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
 
     from oracle import tq_oracle as O
 
-    Kd = K[0, 0].to("cpu").to(torch.float64).numpy()
-    Vd = V[0, 0].to("cpu").to(torch.float64).numpy()
-    qd = q[0:1, 0:w.q_heads // w.kv_heads].to("cpu").to(torch.float64).numpy()
-    T = Kd.shape[0]
+    G = w.q_heads // w.kv_heads
     codec = O.make_codec(w.d, w.bits_k, w.bits_v, w.m, 0)
-    t0 = time.perf_counter()
-    ke = O.encode(Kd, codec, kind="key", positions=np.arange(T), rope_base=w.rope_base)
-    ve = O.encode(Vd, codec, kind="value")
-    t_enc = time.perf_counter() - t0
-    fields = {"kcodes": ke["codes"][None, None], "n16": ke["n16"][None, None],
-              "rn16": ke["rn16"][None, None], "bits": ke["bits"][None, None],
-              "vcodes": ve["codes"][None, None], "vn16": ve["n16"][None, None]}
-    t0 = time.perf_counter()
-    O.attend(fields, qd, codec, q_pos=w.q_pos, rope_base=w.rope_base, scale=0.0, kv_heads=1, length=T)
-    t_att = time.perf_counter() - t0
+    t_enc = t_att = 0.0
+    T = K.shape[2]
+    for u in range(n_units):
+        b, g = divmod(u, w.kv_heads)
+        Kd = K[b, g].to("cpu").to(torch.float64).numpy()
+        Vd = V[b, g].to("cpu").to(torch.float64).numpy()
+        qd = q[b:b + 1, g * G:(g + 1) * G].to("cpu").to(torch.float64).numpy()
+        t0 = time.perf_counter()
+        ke = O.encode(Kd, codec, kind="key", positions=np.arange(T), rope_base=w.rope_base)
+        ve = O.encode(Vd, codec, kind="value")
+        t_enc += time.perf_counter() - t0
+        fields = {"kcodes": ke["codes"][None, None], "n16": ke["n16"][None, None],
+                  "rn16": ke["rn16"][None, None], "bits": ke["bits"][None, None],
+                  "vcodes": ve["codes"][None, None], "vn16": ve["n16"][None, None]}
+        del ke, ve
+        t0 = time.perf_counter()
+        O.attend(fields, qd, codec, q_pos=w.q_pos, rope_base=w.rope_base, scale=0.0, kv_heads=1, length=T)
+        t_att += time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    gbs = T * (KEY_RECORD + VALUE_RECORD) / t_att / 1e9
-    # tokens: positions of one sequence with all kv-heads -> one unit covers 1/kv_heads of it
-    mtok = T / w.kv_heads / t_enc / 1e6
+    gbs = n_units * T * (KEY_RECORD + VALUE_RECORD) / t_att / 1e9
+    # a token is one position of one sequence with all its kv-heads
+    mtok = n_units * T / w.kv_heads / t_enc / 1e6
     return {
         "value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-        "sample": (f"one (batch, kv-head) unit of {units_total}: oracle decode attention of its "
-                   f"{w.q_heads // w.kv_heads} q-heads over {T} tokens ({t_att:.2f} s); oracle encode "
-                   f"of its {T} keys and values ({t_enc:.2f} s)"),
+        "sample": (f"{n_units} of the {units_total} (batch, kv-head) units: oracle decode attention of "
+                   f"their {G} q-heads each over all {T} tokens ({t_att:.1f} s), and oracle encode of "
+                   f"their {T} keys and values each ({t_enc:.1f} s)"),
         "quantize_mtokens_s": round(mtok, 6),
         "seconds": round(t_enc + t_att, 2),
     }
@@ -216,13 +223,15 @@ def main():
         f"({append_mtok:.1f} Mtokens/s, {append_bytes/(mean(append_ms)*1e-3)/1e9:.0f} GB/s)")
 
     if args.copy_calibration:
+        # a plain streaming kernel of known traffic (reads n bytes, writes n bytes), whose
+        # FETCH_SIZE / WRITE_SIZE readings scale the counters of the decode kernel
         n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
-        log(f"[bench] copy calibration: {n} bytes copied 3 times")
+        log(f"[bench] copy calibration: elementwise neg over {n} bytes, 3 launches")
 
     base = None
     if not args.no_cpu_baseline:
@@ -241,7 +250,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "i8+f16 mfma, f32 accumulate",
         "data": "synthetic",
         "config": {
             "workload": ("long_context: 1 layer, 64 q-heads / 8 kv-heads, head dim 128, batch 4, "
@@ -256,7 +265,7 @@ def main():
         "quantize_mtokens_s": round(append_mtok, 2),
         "quantize_gbs": round(append_bytes / (mean(append_ms) * 1e-3) / 1e9, 2),
         "roofline": {
-            "kernel": "k_decode_split (split-K decode over the packed cache)",
+            "kernel": "k_decode_lds<128> (split-K decode over the packed cache)",
             "bound": "hbm",
             "achieved": round(kern_gbs, 2),
             "peak": HBM_PEAK_GBS,

@@ -437,7 +437,7 @@ def pack_cache(desc: dict, fields: dict, start_pos: int = 0, image: np.ndarray |
 
 
 def unpack_cache(image: np.ndarray, desc: dict, length: int) -> dict:
-    """Inverse of pack_cache for tokens [0, length)."""
+    """Inverse of pack_cache for tokens [0, length).  Codes and bits come back as uint8."""
     B, H, d, cap = desc["batch"], desc["kv_heads"], desc["d"], desc["capacity"]
     bk, bv, m = desc["bits_k"], desc["bits_v"], desc["m"]
     lay = cache_layout(B, H, d, cap, bk, bv, m)
@@ -445,10 +445,10 @@ def unpack_cache(image: np.ndarray, desc: dict, length: int) -> dict:
     hdr = image[:HEADER_BYTES].view(np.uint32)
     kb = lay["kbytes"]
     kreg = image[lay["kbits"]:lay["kbits"] + B * H * cap * kb].reshape(B, H, cap, kb)[:, :, :length]
-    bitsall = np.unpackbits(kreg, axis=-1, bitorder="little").astype(np.int64)
-    kcodes = np.zeros((B, H, length, d), dtype=np.int64)
+    bitsall = np.unpackbits(kreg, axis=-1, bitorder="little")
+    kcodes = np.zeros((B, H, length, d), dtype=np.uint8)
     for p in range(bk):
-        kcodes |= bitsall[..., p * d:(p + 1) * d] << p
+        kcodes |= bitsall[..., p * d:(p + 1) * d] << np.uint8(p)
     out = {
         "magic": int(hdr[0]), "version": int(hdr[1]), "flags": int(hdr[2]),
         "kcodes": kcodes, "bits": bitsall[..., bk * d:bk * d + m],
@@ -460,13 +460,14 @@ def unpack_cache(image: np.ndarray, desc: dict, length: int) -> dict:
         tiles = lay["tiles"]
         wbytes = 4 * bv
         vreg = image[lay["vcodes"]:lay["vcodes"] + B * H * tiles * d * wbytes].reshape(B, H, tiles, d, wbytes)
-        vbits = np.unpackbits(vreg, axis=-1, bitorder="little").astype(np.int64)  # [B,H,tiles,d,32*bv]
-        vcodes = np.zeros((B, H, length, d), dtype=np.int64)
-        for t in range(length):
-            tile, slot = divmod(t, 32)
-            for p in range(bv):
-                vcodes[:, :, t, :] |= vbits[:, :, tile, :, bv * slot + p] << p
-        out["vcodes"] = vcodes
+        used = (length + 31) // 32
+        # token 32*tile + i, bit p of its code: bit bv*i + p of the tile's integer
+        vbits = np.unpackbits(vreg[:, :, :used], axis=-1, bitorder="little")  # [B,H,used,d,32*bv]
+        vbits = vbits.reshape(B, H, used, d, 32, bv)
+        codes = np.zeros((B, H, used, d, 32), dtype=np.uint8)
+        for p in range(bv):
+            codes |= vbits[..., p] << np.uint8(p)
+        out["vcodes"] = codes.transpose(0, 1, 2, 4, 3).reshape(B, H, used * 32, d)[:, :, :length]
         vnreg = image[lay["vnorm"]:lay["vnorm"] + B * H * cap * 2].view(np.float16).reshape(B, H, cap)
         out["vn16"] = vnreg[:, :, :length].astype(np.float64)
     return out

@@ -122,3 +122,33 @@ def oracle_image(desc: dict, fields: dict, start=0) -> np.ndarray:
 
 def max_abs(a, b) -> float:
     return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
+
+
+def unit_fields(cache: "tq.PackedCache", unit: int, length: int) -> dict:
+    """Unpacked fields of one (batch, kv-head) unit of a device cache, tokens [0, length).
+
+    Copies only that unit's slices of each region (the layout of the format description,
+    as the oracle computes it) into a one-unit image and unpacks it with the oracle."""
+    desc = cache.desc.as_dict()
+    lay = O.cache_layout(desc["batch"], desc["kv_heads"], desc["d"], desc["capacity"],
+                         desc["bits_k"], desc["bits_v"], desc["m"])
+    sub = dict(desc, batch=1, kv_heads=1)
+    sl = O.cache_layout(1, 1, sub["d"], sub["capacity"], sub["bits_k"], sub["bits_v"], sub["m"])
+    img = np.zeros(sl["total"], dtype=np.uint8)
+    img[:256] = cache.buf[:256].cpu().numpy()
+    cap = desc["capacity"]
+    sizes = {"kbits": cap * lay["kbytes"], "knorm": cap * 4}
+    if desc["bits_v"] > 0:
+        sizes.update(vcodes=lay["tiles"] * desc["d"] * 4 * desc["bits_v"], vnorm=cap * 2)
+    for name, n in sizes.items():
+        src = cache.buf[lay[name] + unit * n: lay[name] + (unit + 1) * n]
+        img[sl[name]: sl[name] + n] = src.cpu().numpy()
+    return O.unpack_cache(img, sub, length)
+
+
+def fields_slice(f: dict, t0: int, t1: int) -> dict:
+    """Tokens [t0, t1) of unpacked / oracle fields ([1, 1, T, ...] arrays)."""
+    out = {}
+    for k, v in f.items():
+        out[k] = v[:, :, t0:t1] if isinstance(v, np.ndarray) and v.ndim >= 3 else v
+    return out

@@ -344,6 +344,9 @@ def test_pack_handcrafted_bytes(O):
     vt = img[lay["vcodes"] + 1 * 8 * 12: lay["vcodes"] + 2 * 8 * 12].reshape(8, 12)
     assert list(vt[:, 0]) == [7, 0, 1, 2, 3, 4, 5, 6] and np.all(vt[:, 1:] == 0)
     assert img[lay["vnorm"] + 64: lay["vnorm"] + 66].view(np.float16)[0] == 2.0
+    u = O.unpack_cache(img, desc, length=33)
+    assert list(u["vcodes"][0, 0, 32]) == [7, 0, 1, 2, 3, 4, 5, 6] and np.all(u["vcodes"][0, 0, :32] == 0)
+    assert list(u["kcodes"][0, 0, 32]) == [0, 1, 2, 3, 3, 2, 1, 0] and list(u["bits"][0, 0, 32]) == [1, 0, 0, 0, 0, 0, 0, 1]
     # tokens in slots 2 and 10 of tile 0: bits 6..8 and 30..32 (straddling bytes 0/1, 3/4)
     desc0 = dict(desc)
     f2 = dict(f, vcodes=np.array([[[[5] * 8]]]))
