@@ -213,9 +213,35 @@ __device__ __forceinline__ int bucketize64(double u, const float *t, const float
   return code;
 }
 
-// Seeded-sign FWHT of one vector spread over the 4 lanes of a group: lane q holds chunk A
-// (coordinates q*HC + e) and chunk B (D/2 + q*HC + e), e < HC.  Coordinate bits below
-// HC are in-lane, the next two bits select the lane, the top bit selects the chunk.
+// Exchange of a double with lane ^ 1 (kDppXor1) or lane ^ 2 (kDppXor2) inside each group
+// of 4 lanes (DPP quad permutation of both halves).
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double x) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_mov_dpp(int(uint32_t(b)), CTRL, 0xF, 0xF, true));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_mov_dpp(int(uint32_t(b >> 32)), CTRL, 0xF, 0xF, true));
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return uint32_t(__builtin_amdgcn_mov_dpp(int(x), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ double group4_sum(double v) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  return v;
+}
+
+// Unnormalised Sylvester FWHT (H_D x) of one vector spread over the 4 lanes of a group:
+// lane q holds chunk A (coordinates q*HC + e) and chunk B (D/2 + q*HC + e), e < HC.
+// Coordinate bits below HC are in-lane, the next two select the lane, the top bit the
+// chunk.  Cross-lane butterflies use DPP; x_new = partner + s * x with s = +1 on the lower
+// lane of a pair and -1 on the upper one (exact sign, one rounding, as a + b / a - b).
 template <int D>
 __device__ __forceinline__ void fwht_group4(double *x, int q) {
   constexpr int HC = D / 8;
@@ -227,45 +253,91 @@ __device__ __forceinline__ void fwht_group4(double *x, int q) {
     x[e] = a + b;
     x[HC + e] = a - b;
   }
+  const double s1 = (q & 1) ? -1.0 : 1.0, s2 = (q & 2) ? -1.0 : 1.0;
 #pragma unroll
-  for (int dist = 1; dist <= 2; dist <<= 1) {
+  for (int e = 0; e < 2 * HC; ++e) x[e] = fma(s1, x[e], dpp_f64<kDppXor1>(x[e]));
 #pragma unroll
-    for (int e = 0; e < 2 * HC; ++e) {
-      const double o = __shfl_xor(x[e], dist, 64);
-      x[e] = (q & dist) ? (o - x[e]) : (x[e] + o);
+  for (int e = 0; e < 2 * HC; ++e) x[e] = fma(s2, x[e], dpp_f64<kDppXor2>(x[e]));
+}
+
+// N consecutive input elements starting at element `off`, converted exactly to fp64
+// (16-byte vector loads; off * sizeof(element) is a multiple of 16).
+template <int DT, int N>
+__device__ __forceinline__ void load_chunk(const void *base, size_t off, double *x) {
+  if constexpr (DT == TQ_F32) {
+    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off);
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      const float4 v = p[i];
+      x[4 * i] = v.x;
+      x[4 * i + 1] = v.y;
+      x[4 * i + 2] = v.z;
+      x[4 * i + 3] = v.w;
+    }
+  } else {
+    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off);
+#pragma unroll
+    for (int i = 0; i < N / 8; ++i) {
+      const uint4 v = p[i];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if constexpr (DT == TQ_BF16) {
+          x[8 * i + 2 * k] = double(__uint_as_float(w[k] << 16));
+          x[8 * i + 2 * k + 1] = double(__uint_as_float(w[k] & 0xFFFF0000u));
+        } else {
+          x[8 * i + 2 * k] = double(f16_bits_to_float(w[k] & 0xFFFFu));
+          x[8 * i + 2 * k + 1] = double(f16_bits_to_float(w[k] >> 16));
+        }
+      }
     }
   }
 }
 
-__device__ __forceinline__ double group4_sum(double v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  return v;
-}
-
-__device__ __forceinline__ uint32_t group4_or(uint32_t v) {
-  v |= __shfl_xor(v, 1, 64);
-  v |= __shfl_xor(v, 2, 64);
-  return v;
+// Bit planes of one lane's coordinates (16-bit chunk A / B halves, bit e = coordinate
+// e of the chunk) joined into the plane's dwords and stored: lane q writes the word(s)
+// the 4 lanes of its group are assigned.  D = 128: word (q >> 1) of chunk A is
+// A(2w) | A(2w + 1) << 16; D = 64: word 0 is A(0) | A(1) << 8 | A(2) << 16 | A(3) << 24.
+template <int D>
+__device__ __forceinline__ void store_plane(uint32_t hA, uint32_t hB, int q, uint32_t *dst, bool valid) {
+  constexpr int HC = D / 8;
+  if constexpr (D == 128) {
+    const uint32_t ca = hA << (HC * (q & 1)), cb = hB << (HC * (q & 1));
+    const uint32_t wa = ca | dpp_u32<kDppXor1>(ca);
+    const uint32_t wb = cb | dpp_u32<kDppXor1>(cb);
+    // q = 0: word 0, q = 1: word 2, q = 2: word 1, q = 3: word 3
+    if (valid) dst[(q & 1) ? 2 + (q >> 1) : (q >> 1)] = (q & 1) ? wb : wa;
+  } else {
+    uint32_t ca = hA << (HC * q), cb = hB << (HC * q);
+    ca |= dpp_u32<kDppXor1>(ca);
+    ca |= dpp_u32<kDppXor2>(ca);
+    cb |= dpp_u32<kDppXor1>(cb);
+    cb |= dpp_u32<kDppXor2>(cb);
+    if (valid && q < 2) dst[q] = q ? cb : ca;
+  }
 }
 
 // One workgroup (4 waves) per 64-token window aligned to value tiles; 4 lanes per token.
-// Keys: RoPE (fp64 angles from an LDS table built by the fp64 rotation recurrence),
-// signs, FWHT, norm, codes and residual all in fp64; the QJL projection z = S r runs
-// on fp32 MFMA (v_mfma_f32_32x32x2f32) over the window's 64 residuals.  Values: signs,
-// FWHT, norm, codes in fp64, then the window's codes are packed into value tiles.
-template <int D, int DT>
+// Keys: RoPE (fp64 angles from an LDS table built by the fp64 rotation recurrence), the
+// seeded signs D, the unnormalised FWHT H_B, norm, codes and residual in fp64, with the
+// 1/sqrt(B) of Pi folded into the norms; the QJL projection z = S r runs on fp32 MFMA
+// (v_mfma_f32_32x32x2f32) over the window's 64 residuals.  Values: signs, FWHT, norm and
+// codes in fp64, then the window's codes are packed into value tiles.
+// KK / KV: number of key / value codes when known at compile time (0: from the
+// descriptor, a slower loop).  Codes compare the unnormalised coordinate y_j with
+// ||y|| * t_k, which is u_j >= t_k up to one rounding.
+template <int D, int DT, int KK, int KV>
 __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   constexpr int H = D / 2;
   constexpr int HC = D / 8;     // coordinates per chunk
   constexpr int C = 2 * HC;     // coordinates per lane
   constexpr int W = D / 32;     // dwords per plane
-  constexpr int RS = D + 1;     // padded residual row (floats)
+  constexpr int RS = D + 4;     // padded residual row (floats)
   constexpr int ROPE_BYTES = 64 * H * 16;
   constexpr int R_BYTES = 64 * RS * 4;
   constexpr int U_BYTES = ROPE_BYTES > R_BYTES ? ROPE_BYTES : R_BYTES;
   __shared__ __align__(16) unsigned char u_s[U_BYTES];   // RoPE table, later residuals
-  __shared__ uint8_t vcode_s[64][D];
+  __shared__ __align__(16) uint8_t vcode_s[64][D];
   __shared__ float cb_s[4][kMaxCodes];
   double2 *rope_s = reinterpret_cast<double2 *>(u_s);   // [64][H]
   float *r_s = reinterpret_cast<float *>(u_s);           // [64][RS]
@@ -302,121 +374,211 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
       c = cn;
     }
   }
+  // seeded signs of this lane's coordinates: bit e set when D_j = -1
+  uint32_t dmask = 0u;
+#pragma unroll
+  for (int e = 0; e < HC; ++e) {
+    dmask |= uint32_t(a.cp.D[HC * q + e] < 0.0f) << e;
+    dmask |= uint32_t(a.cp.D[H + HC * q + e] < 0.0f) << (HC + e);
+  }
   __syncthreads();
 
-  const double inv_sqrt_b = 1.0 / sqrt(double(a.cp.block));
-  auto coord = [&](int e) { return e < HC ? q * HC + e : H + q * HC + (e - HC); };
+  const double sqrt_b = sqrt(double(a.cp.block));
+  const double inv_sqrt_b = 1.0 / sqrt_b;
+  uint32_t *rec = reinterpret_cast<uint32_t *>(a.ch.kbits + (size_t(unit) * a.capacity + (valid ? p : 0)) * a.ch.kbytes);
 
   // ------------------------------------------------------------ keys
-  {
-    double x[C];
+  double x[C];
+  if (valid) {
+    load_chunk<DT, HC>(a.k, row * D + HC * q, x);
+    load_chunk<DT, HC>(a.k, row * D + H + HC * q, x + HC);
+  } else {
 #pragma unroll
-    for (int e = 0; e < C; ++e) x[e] = valid ? load_d<DT>(a.k, row * D + coord(e)) : 0.0;
-    if (use_rope) {
+    for (int e = 0; e < C; ++e) x[e] = 0.0;
+  }
+  if (use_rope) {
 #pragma unroll
-      for (int e = 0; e < HC; ++e) {
-        const double2 cs = rope_s[slot * H + q * HC + e];
-        const double x0 = x[e], x1 = x[HC + e];
-        x[e] = x0 * cs.x - x1 * cs.y;
-        x[HC + e] = x0 * cs.y + x1 * cs.x;
-      }
+    for (int e = 0; e < HC; ++e) {
+      const double2 cs = rope_s[slot * H + HC * q + e];
+      const double x0 = x[e], x1 = x[HC + e];
+      x[e] = x0 * cs.x - x1 * cs.y;
+      x[HC + e] = x0 * cs.y + x1 * cs.x;
     }
+  }
 #pragma unroll
-    for (int e = 0; e < C; ++e) x[e] *= double(a.cp.D[coord(e)]);
-    fwht_group4<D>(x, q);
+  for (int e = 0; e < C; ++e) x[e] = ((dmask >> e) & 1u) ? -x[e] : x[e];
+  fwht_group4<D>(x, q);
+  {
     double ss = 0.0;
 #pragma unroll
-    for (int e = 0; e < C; ++e) {
-      x[e] *= inv_sqrt_b;
-      ss += x[e] * x[e];
-    }
-    const double n = sqrt(group4_sum(ss));
-    const uint16_t n16b = f64_to_f16_sat(n, &over);
-    const double n16 = double(f16_bits_to_float(n16b));
-    const double inv = n > 0.0 ? 1.0 / n : 0.0;
-    const int K = 1 << a.bits_k;
-    uint32_t pl[4][W];
-#pragma unroll
-    for (int pp = 0; pp < 4; ++pp)
-#pragma unroll
-      for (int w = 0; w < W; ++w) pl[pp][w] = 0u;
+    for (int e = 0; e < C; ++e) ss = fma(x[e], x[e], ss);
+    const double nu = sqrt(group4_sum(ss));           // ||H D x'|| = sqrt(B) ||y||
+    const uint16_t n16b = f64_to_f16_sat(nu * inv_sqrt_b, &over);
+    const double nb16 = double(f16_bits_to_float(n16b)) * sqrt_b;   // fp16(n) in H-units
+    const double sc = nu > 0.0 ? nu : 1.0;
+    // planes that can be non-zero: log2(KK) when the code count is fixed, else up to 4
+    constexpr int NP = KK == 2 ? 1 : KK == 4 ? 2 : KK == 8 ? 3 : 4;
+    uint32_t hA[4] = {0u, 0u, 0u, 0u}, hB[4] = {0u, 0u, 0u, 0u};
     double rr = 0.0;
+    if constexpr (KK > 0) {
+      double sk[KK - 1], wk[KK];
 #pragma unroll
-    for (int e = 0; e < C; ++e) {
-      double chat;
-      const int code = bucketize64(x[e] * inv, cb_s[1], cb_s[0], K, &chat);
-      const int j = coord(e);
+      for (int k = 0; k < KK - 1; ++k) sk[k] = sc * double(cb_s[1][k]);
 #pragma unroll
-      for (int pp = 0; pp < 4; ++pp) pl[pp][j >> 5] |= uint32_t((code >> pp) & 1) << (j & 31);
-      x[e] -= n16 * chat;   // residual against the stored fp16 norm
-      rr += x[e] * x[e];
-    }
-    const uint16_t rn16b = f64_to_f16_sat(sqrt(group4_sum(rr)), &over);
-    uint32_t *rec = reinterpret_cast<uint32_t *>(a.ch.kbits + (size_t(unit) * a.capacity + (valid ? p : 0)) * a.ch.kbytes);
+      for (int k = 0; k < KK; ++k) wk[k] = nb16 * double(cb_s[0][k]);
 #pragma unroll
-    for (int pp = 0; pp < 4; ++pp) {
+      for (int e = 0; e < C; ++e) {
+        int code = 0;
+        double w = wk[0];
 #pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const uint32_t v = group4_or(pl[pp][w]);
-        if (valid && pp < a.bits_k && (w & 3) == q) rec[pp * W + w] = v;
+        for (int k = 0; k < KK - 1; ++k) {
+          const bool ge = x[e] >= sk[k];
+          code += ge ? 1 : 0;
+          w = ge ? wk[k + 1] : w;
+        }
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) {
+          const uint32_t bit = uint32_t((code >> pp) & 1) << (e % HC);
+          if (e < HC) hA[pp] |= bit; else hB[pp] |= bit;
+        }
+        x[e] -= w;
+        rr = fma(x[e], x[e], rr);
+      }
+    } else {
+      const int K = 1 << a.bits_k;
+#pragma unroll
+      for (int e = 0; e < C; ++e) {
+        int code = 0;
+        for (int k = 0; k < K - 1; ++k) code += x[e] >= sc * double(cb_s[1][k]) ? 1 : 0;
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const uint32_t bit = uint32_t((code >> pp) & 1) << (e % HC);
+          if (e < HC) hA[pp] |= bit; else hB[pp] |= bit;
+        }
+        x[e] -= nb16 * double(cb_s[0][code]);
+        rr = fma(x[e], x[e], rr);
       }
     }
+    const uint16_t rn16b = f64_to_f16_sat(sqrt(group4_sum(rr)) * inv_sqrt_b, &over);
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp)
+      if (pp < a.bits_k) store_plane<D>(hA[pp], hB[pp], q, rec + pp * W, valid);
     if (valid && q == 0)
       a.ch.knorm[size_t(unit) * a.capacity + p] = uint32_t(n16b) | (uint32_t(rn16b) << 16);
-    __syncthreads();   // every wave is done with the RoPE table before residuals overwrite it
+  }
+  __syncthreads();   // every wave is done with the RoPE table before residuals overwrite it
+  {
+    // residual r_H = H D x' - fp16(n) sqrt(B) c = sqrt(B) r: same signs of S r
+    float4 *ra = reinterpret_cast<float4 *>(r_s + slot * RS + HC * q);
+    float4 *rb = reinterpret_cast<float4 *>(r_s + slot * RS + H + HC * q);
 #pragma unroll
-    for (int e = 0; e < C; ++e) r_s[slot * RS + coord(e)] = float(x[e]);
-    __syncthreads();
-    // z^T[m x 64 tokens] = S[m x D] . R^T[D x 64]: one 32 x 32 output tile per iteration
-    const int mt_n = a.m / 32;
-    for (int it = wv; it < 2 * mt_n; it += 4) {
-      const int mt = it >> 1, tt = it & 1;
-      v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      const float *srow = a.cp.S + size_t(32 * mt + (lane & 31)) * D + (lane >> 5);
-      const float *rrow = r_s + (32 * tt + (lane & 31)) * RS + (lane >> 5);
-#pragma unroll 8
-      for (int j0 = 0; j0 < D; j0 += 2)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(srow[j0], rrow[j0], acc, 0, 0, 0);
-      uint32_t bits = 0u;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        bits |= uint32_t(acc[r] >= 0.0f) << (8 * (r >> 2) + 4 * (lane >> 5) + (r & 3));
-      bits |= __shfl_xor(bits, 32, 64);
-      const int ts = 32 * tt + (lane & 31);
-      const int pt = p0 + ts;
-      if (lane < 32 && pt >= a.start && pt < end) {
-        uint32_t *rt = reinterpret_cast<uint32_t *>(a.ch.kbits + (size_t(unit) * a.capacity + pt) * a.ch.kbytes);
-        rt[a.bits_k * W + mt] = bits;
-      }
+    for (int i = 0; i < HC / 4; ++i) {
+      ra[i] = make_float4(float(x[4 * i]), float(x[4 * i + 1]), float(x[4 * i + 2]), float(x[4 * i + 3]));
+      rb[i] = make_float4(float(x[HC + 4 * i]), float(x[HC + 4 * i + 1]), float(x[HC + 4 * i + 2]),
+                          float(x[HC + 4 * i + 3]));
     }
   }
 
   // ------------------------------------------------------------ values
   if (a.bits_v > 0) {
-    double x[C];
+    if (valid) {
+      load_chunk<DT, HC>(a.v, row * D + HC * q, x);
+      load_chunk<DT, HC>(a.v, row * D + H + HC * q, x + HC);
+    } else {
 #pragma unroll
-    for (int e = 0; e < C; ++e)
-      x[e] = valid ? load_d<DT>(a.v, row * D + coord(e)) * double(a.cp.D[coord(e)]) : 0.0;
+      for (int e = 0; e < C; ++e) x[e] = 0.0;
+    }
+#pragma unroll
+    for (int e = 0; e < C; ++e) x[e] = ((dmask >> e) & 1u) ? -x[e] : x[e];
     fwht_group4<D>(x, q);
     double ss = 0.0;
 #pragma unroll
-    for (int e = 0; e < C; ++e) {
-      x[e] *= inv_sqrt_b;
-      ss += x[e] * x[e];
-    }
-    const double n = sqrt(group4_sum(ss));
-    const uint16_t n16b = f64_to_f16_sat(n, &over);
-    const double inv = n > 0.0 ? 1.0 / n : 0.0;
-    const int K = 1 << a.bits_v;
+    for (int e = 0; e < C; ++e) ss = fma(x[e], x[e], ss);
+    const double nu = sqrt(group4_sum(ss));
+    const uint16_t n16b = f64_to_f16_sat(nu * inv_sqrt_b, &over);
+    const double sc = nu > 0.0 ? nu : 1.0;
+    uint32_t cw[C / 4];
 #pragma unroll
-    for (int e = 0; e < C; ++e) {
-      double chat;
-      vcode_s[slot][coord(e)] = uint8_t(bucketize64(x[e] * inv, cb_s[3], cb_s[2], K, &chat));
+    for (int i = 0; i < C / 4; ++i) cw[i] = 0u;
+    if constexpr (KV > 0) {
+      double sk[KV - 1];
+#pragma unroll
+      for (int k = 0; k < KV - 1; ++k) sk[k] = sc * double(cb_s[3][k]);
+#pragma unroll
+      for (int e = 0; e < C; ++e) {
+        int code = 0;
+#pragma unroll
+        for (int k = 0; k < KV - 1; ++k) code += x[e] >= sk[k] ? 1 : 0;
+        cw[e / 4] |= uint32_t(code) << (8 * (e % 4));
+      }
+    } else {
+      const int K = 1 << a.bits_v;
+#pragma unroll
+      for (int e = 0; e < C; ++e) {
+        int code = 0;
+        for (int k = 0; k < K - 1; ++k) code += x[e] >= sc * double(cb_s[3][k]) ? 1 : 0;
+        cw[e / 4] |= uint32_t(code) << (8 * (e % 4));
+      }
+    }
+    uint32_t *va = reinterpret_cast<uint32_t *>(&vcode_s[slot][HC * q]);
+    uint32_t *vb = reinterpret_cast<uint32_t *>(&vcode_s[slot][H + HC * q]);
+#pragma unroll
+    for (int i = 0; i < HC / 4; ++i) {
+      va[i] = cw[i];
+      vb[i] = cw[HC / 4 + i];
     }
     if (valid && q == 0) a.ch.vnorm[size_t(unit) * a.capacity + p] = n16b;
-    __syncthreads();
-    // value tiles: one (tile, coordinate) word per thread; tokens outside the written
-    // range keep their previous bits
+  }
+  __syncthreads();
+
+  // ------------------------------------------------------------ QJL signs: z = S r
+  // z^T[32 rows x 64 tokens] per 32-row block of S, both 32-token halves sharing the S
+  // operand.  Step i contracts k = i (lanes 0-31) and k = i + D/2 (lanes 32-63), so every
+  // lane streams contiguous floats of its S row and of its residual row.
+  {
+    const int mt_n = a.m / 32;
+    const int half = lane >> 5;
+    for (int mt = wv; mt < mt_n; mt += 4) {
+      v16f acc0 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      v16f acc1 = acc0;
+      const float4 *srow = reinterpret_cast<const float4 *>(a.cp.S + size_t(32 * mt + (lane & 31)) * D + half * H);
+      const float4 *r0 = reinterpret_cast<const float4 *>(r_s + (lane & 31) * RS + half * H);
+      const float4 *r1 = reinterpret_cast<const float4 *>(r_s + (32 + (lane & 31)) * RS + half * H);
+#pragma unroll 4
+      for (int i = 0; i < H / 4; ++i) {
+        const float4 sv = srow[i], ra = r0[i], rb = r1[i];
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.x, ra.x, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.x, rb.x, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.y, ra.y, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.y, rb.y, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.z, ra.z, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.z, rb.z, acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.w, ra.w, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.w, rb.w, acc1, 0, 0, 0);
+      }
+      // lane holds rows 8 (r / 4) + 4 (lane / 32) + r % 4 of token column lane % 32
+      uint32_t b0 = 0u, b1 = 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int sh = 8 * (r >> 2) + 4 * half + (r & 3);
+        b0 |= uint32_t(acc0[r] >= 0.0f) << sh;
+        b1 |= uint32_t(acc1[r] >= 0.0f) << sh;
+      }
+      b0 |= __shfl_xor(b0, 32, 64);
+      b1 |= __shfl_xor(b1, 32, 64);
+      const int ts = lane & 31;
+      const int pt = p0 + ts + (half ? 32 : 0);
+      if (pt >= a.start && pt < end) {
+        uint32_t *rt = reinterpret_cast<uint32_t *>(a.ch.kbits + (size_t(unit) * a.capacity + pt) * a.ch.kbytes);
+        rt[a.bits_k * W + mt] = half ? b1 : b0;
+      }
+    }
+  }
+
+  // ------------------------------------------------------------ value tiles
+  if (a.bits_v > 0) {
+    // one (tile, coordinate) word group per thread; tokens outside the written range
+    // keep their previous bits
     const int bv = a.bits_v;
     const uint32_t mask = (1u << bv) - 1u;
     for (int wi = tid; wi < 2 * D; wi += 256) {
@@ -1745,6 +1907,8 @@ tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_d
   if (int64_t(start_pos) + int64_t(n_new) > int64_t(desc->capacity)) return TQ_ECAPACITY;
   if (n_new > 0 && (!k || (desc->bits_v > 0) != (v != nullptr))) return TQ_EINVAL;
   if (!std::isfinite(rope_base) || rope_base < 0.0f) return TQ_EINVAL;
+  // the kernels read K and V rows with 16-byte vector loads
+  if ((reinterpret_cast<uintptr_t>(k) & 15) != 0 || (reinterpret_cast<uintptr_t>(v) & 15) != 0) return TQ_EINVAL;
   const int d = desc->d;
   const bool small = (d == 64 || d == 128);
   const bool large = (d == 256 || d == 512 || d == 1024 || d == 1536 || d == 2048);
@@ -1772,7 +1936,14 @@ tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_d
     const int end_tile = (start_pos + n_new + kValueTile - 1) / kValueTile;
     const int windows = (end_tile - first_tile + 1) / 2;
     dim3 grid(windows, a.units);
-#define TQ_QKV(DD, TT) hipLaunchKernelGGL((k_quantize_kv<DD, TT>), grid, dim3(256), 0, s, a)
+    // 2-bit keys with 3-bit values (the 3 bits per value configuration) have their code
+    // counts fixed at compile time; other widths take them from the descriptor
+    const bool k2v3 = desc->bits_k == 2 && desc->bits_v == 3;
+#define TQ_QKV(DD, TT)                                                                              \
+  do {                                                                                              \
+    if (k2v3) hipLaunchKernelGGL((k_quantize_kv<DD, TT, 4, 8>), grid, dim3(256), 0, s, a);          \
+    else hipLaunchKernelGGL((k_quantize_kv<DD, TT, 0, 0>), grid, dim3(256), 0, s, a);               \
+  } while (0)
     if (d == 64) {
       if (dtype == TQ_F32) TQ_QKV(64, TQ_F32); else if (dtype == TQ_BF16) TQ_QKV(64, TQ_BF16); else TQ_QKV(64, TQ_F16);
     } else {
