@@ -87,6 +87,7 @@ __device__ __forceinline__ void fwht_regs(T *x) {
 
 struct CodecPtrs {
   const float *ck, *tk, *cv, *tv, *D, *S, *ST;
+  const __bf16 *Sb[3];   // S split exactly into three bf16 parts, each [m][d]
   int block;
   float qjl_scale, inv_sqrt_block;
 };
@@ -102,6 +103,7 @@ CodecPtrs codec_ptrs(const void *codec_dev, int d, int bits_k, int bits_v, int m
   p.D = reinterpret_cast<const float *>(b + L.D);
   p.S = reinterpret_cast<const float *>(b + L.S);
   p.ST = reinterpret_cast<const float *>(b + L.ST);
+  for (int i = 0; i < 3; ++i) p.Sb[i] = reinterpret_cast<const __bf16 *>(b + L.Sb[i]);
   p.block = L.block;
   p.qjl_scale = m > 0 ? float(std::sqrt(M_PI / 2.0) / m) : 0.0f;
   p.inv_sqrt_block = float(1.0 / std::sqrt(double(L.block)));
@@ -161,6 +163,7 @@ struct QuantArgs {
 };
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 template <int DT>
@@ -332,15 +335,15 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   constexpr int HC = D / 8;     // coordinates per chunk
   constexpr int C = 2 * HC;     // coordinates per lane
   constexpr int W = D / 32;     // dwords per plane
-  constexpr int RS = D + 4;     // padded residual row (floats)
+  constexpr int RS = D + 8;     // padded residual row (bf16 elements)
   constexpr int ROPE_BYTES = 64 * H * 16;
-  constexpr int R_BYTES = 64 * RS * 4;
+  constexpr int R_BYTES = 3 * 64 * RS * 2;
   constexpr int U_BYTES = ROPE_BYTES > R_BYTES ? ROPE_BYTES : R_BYTES;
   __shared__ __align__(16) unsigned char u_s[U_BYTES];   // RoPE table, later residuals
   __shared__ __align__(16) uint8_t vcode_s[64][D];
   __shared__ float cb_s[4][kMaxCodes];
   double2 *rope_s = reinterpret_cast<double2 *>(u_s);   // [64][H]
-  float *r_s = reinterpret_cast<float *>(u_s);           // [64][RS]
+  __bf16 *r_s = reinterpret_cast<__bf16 *>(u_s);         // [3 parts][64][RS]
 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = wv * 16 + (lane >> 2), q = lane & 3;
@@ -468,14 +471,27 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   }
   __syncthreads();   // every wave is done with the RoPE table before residuals overwrite it
   {
-    // residual r_H = H D x' - fp16(n) sqrt(B) c = sqrt(B) r: same signs of S r
-    float4 *ra = reinterpret_cast<float4 *>(r_s + slot * RS + HC * q);
-    float4 *rb = reinterpret_cast<float4 *>(r_s + slot * RS + H + HC * q);
+    // residual r_H = H D x' - fp16(n) sqrt(B) c = sqrt(B) r (same signs of S r), rounded
+    // to fp32 and split exactly into three bf16 parts
 #pragma unroll
-    for (int i = 0; i < HC / 4; ++i) {
-      ra[i] = make_float4(float(x[4 * i]), float(x[4 * i + 1]), float(x[4 * i + 2]), float(x[4 * i + 3]));
-      rb[i] = make_float4(float(x[HC + 4 * i]), float(x[HC + 4 * i + 1]), float(x[HC + 4 * i + 2]),
-                          float(x[HC + 4 * i + 3]));
+    for (int c = 0; c < 2; ++c) {
+      v8bf part[3][HC / 8];
+#pragma unroll
+      for (int e = 0; e < HC; ++e) {
+        float rest = float(x[c * HC + e]);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          const __bf16 b = (__bf16)rest;
+          part[k][e / 8][e % 8] = b;
+          rest -= float(b);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        v8bf *dst = reinterpret_cast<v8bf *>(r_s + (k * 64 + slot) * RS + c * H + HC * q);
+#pragma unroll
+        for (int i = 0; i < HC / 8; ++i) dst[i] = part[k][i];
+      }
     }
   }
 
@@ -533,28 +549,40 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
 
   // ------------------------------------------------------------ QJL signs: z = S r
   // z^T[32 rows x 64 tokens] per 32-row block of S, both 32-token halves sharing the S
-  // operand.  Step i contracts k = i (lanes 0-31) and k = i + D/2 (lanes 32-63), so every
-  // lane streams contiguous floats of its S row and of its residual row.
+  // operand, on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with both operands split exactly into
+  // three bf16 parts: the six products down to 2^-16 relative (hi.hi, hi.mid, mid.hi,
+  // hi.lo, lo.hi, mid.mid) are exact in fp32 and accumulate in fp32.  That keeps the
+  // accuracy of fp32 MFMA with six bf16 MFMAs per 16-wide slice of k instead of eight
+  // fp32 ones (v_mfma_f32_32x32x2f32), about 2.7x fewer MFMA cycles.
+  // Step i contracts k = 16 i + 8 (lane / 32) + 0..7 on both operands.
   {
     const int mt_n = a.m / 32;
     const int half = lane >> 5;
     for (int mt = wv; mt < mt_n; mt += 4) {
       v16f acc0 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       v16f acc1 = acc0;
-      const float4 *srow = reinterpret_cast<const float4 *>(a.cp.S + size_t(32 * mt + (lane & 31)) * D + half * H);
-      const float4 *r0 = reinterpret_cast<const float4 *>(r_s + (lane & 31) * RS + half * H);
-      const float4 *r1 = reinterpret_cast<const float4 *>(r_s + (32 + (lane & 31)) * RS + half * H);
-#pragma unroll 4
-      for (int i = 0; i < H / 4; ++i) {
-        const float4 sv = srow[i], ra = r0[i], rb = r1[i];
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.x, ra.x, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.x, rb.x, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.y, ra.y, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.y, rb.y, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.z, ra.z, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.z, rb.z, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.w, ra.w, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(sv.w, rb.w, acc1, 0, 0, 0);
+      const size_t srow = size_t(32 * mt + (lane & 31)) * D + 8 * half;
+      const __bf16 *r0 = r_s + (lane & 31) * RS + 8 * half;
+      const __bf16 *r1 = r0 + 32 * RS;
+#pragma unroll 2
+      for (int i = 0; i < D / 16; ++i) {
+        v8bf sa[3], ra[3], rb[3];
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+          sa[k] = *reinterpret_cast<const v8bf *>(a.cp.Sb[k] + srow + 16 * i);
+          ra[k] = *reinterpret_cast<const v8bf *>(r0 + k * 64 * RS + 16 * i);
+          rb[k] = *reinterpret_cast<const v8bf *>(r1 + k * 64 * RS + 16 * i);
+        }
+#define TQ_SR(A, B)                                                              \
+  acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[A], ra[B], acc0, 0, 0, 0); \
+  acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[A], rb[B], acc1, 0, 0, 0)
+        TQ_SR(2, 0);
+        TQ_SR(0, 2);
+        TQ_SR(1, 1);
+        TQ_SR(1, 0);
+        TQ_SR(0, 1);
+        TQ_SR(0, 0);
+#undef TQ_SR
       }
       // lane holds rows 8 (r / 4) + 4 (lane / 32) + r % 4 of token column lane % 32
       uint32_t b0 = 0u, b1 = 0u;
@@ -587,8 +615,27 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
       const int tstart = tile * kValueTile;
       if (tstart >= end || tile >= a.ch.tiles) continue;
       uint32_t *wp = a.ch.vcodes + ((size_t(unit) * a.ch.tiles + tile) * D + j) * bv;
-      uint32_t word[4] = {0u, 0u, 0u, 0u};
       const bool full = tstart >= a.start && tstart + kValueTile <= end;
+      if constexpr (KV > 0) {
+        // whole tile with a fixed code width: every shift is a constant
+        constexpr int BV = KV == 2 ? 1 : KV == 4 ? 2 : KV == 8 ? 3 : 4;
+        if (full) {
+          uint32_t fw[BV];
+#pragma unroll
+          for (int k = 0; k < BV; ++k) fw[k] = 0u;
+#pragma unroll
+          for (int i = 0; i < kValueTile; ++i) {
+            const uint32_t code = vcode_s[tloc * kValueTile + i][j];
+            const int bit = BV * i;
+            fw[bit >> 5] |= code << (bit & 31);
+            if ((bit & 31) + BV > 32) fw[(bit >> 5) + 1] |= code >> (32 - (bit & 31));
+          }
+#pragma unroll
+          for (int k = 0; k < BV; ++k) wp[k] = fw[k];
+          continue;
+        }
+      }
+      uint32_t word[4] = {0u, 0u, 0u, 0u};
       if (!full)
         for (int qq = 0; qq < bv; ++qq) word[qq] = wp[qq];
       for (int i = 0; i < kValueTile; ++i) {

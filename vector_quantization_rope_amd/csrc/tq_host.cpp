@@ -60,10 +60,27 @@ CodecLayout codec_layout(int d, int bits_k, int bits_v, int m) {
   L.D = cur; cur = align256(cur + size_t(d) * 4);
   L.S = cur; cur = align256(cur + size_t(m) * size_t(d) * 4);
   L.ST = cur; cur = align256(cur + size_t(m) * size_t(d) * 4);
-  L.Shi = cur; cur = align256(cur + size_t(m) * size_t(d) * 2);
-  L.Slo = cur; cur = align256(cur + size_t(m) * size_t(d) * 2);
+  for (int i = 0; i < 3; ++i) {
+    L.Sb[i] = cur;
+    cur = align256(cur + size_t(m) * size_t(d) * 2);
+  }
   L.total = cur;
   return L;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+static uint16_t bf16_rne(float x) {
+  uint32_t u;
+  std::memcpy(&u, &x, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+static float bf16_value(uint16_t b) {
+  const uint32_t u = uint32_t(b) << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
 }
 
 double round_fp16(double x, uint16_t *bits_out) {
@@ -306,8 +323,8 @@ tq_status tq_codec_build(const tq_codec_desc *desc, void *host_out, size_t bytes
     D[j] = (splitmix64(desc->seed, kStreamSigns + uint64_t(j)) >> 63) ? -1.0f : 1.0f;
   float *S = reinterpret_cast<float *>(base + L.S);
   float *ST = reinterpret_cast<float *>(base + L.ST);
-  uint16_t *Shi = reinterpret_cast<uint16_t *>(base + L.Shi);
-  uint16_t *Slo = reinterpret_cast<uint16_t *>(base + L.Slo);
+  uint16_t *Sb[3];
+  for (int i = 0; i < 3; ++i) Sb[i] = reinterpret_cast<uint16_t *>(base + L.Sb[i]);
   for (int i = 0; i < m; ++i) {
     for (int j = 0; j < d; ++j) {
       const uint64_t n = uint64_t(i) * uint64_t(d) + uint64_t(j);
@@ -317,11 +334,14 @@ tq_status tq_codec_build(const tq_codec_desc *desc, void *host_out, size_t bytes
       const float zf = float(z);
       S[size_t(i) * d + j] = zf;
       ST[size_t(j) * m + i] = zf;
-      uint16_t hb = 0, lb = 0;
-      const double hi = round_fp16(double(zf), &hb);
-      round_fp16(double(zf) - hi, &lb);
-      Shi[size_t(i) * d + j] = hb;
-      Slo[size_t(i) * d + j] = lb;
+      // exact three-part bf16 split: each part is the remainder rounded to 8 significant
+      // bits; 24 bits of fp32 leave nothing after the third part
+      float rest = zf;
+      for (int k = 0; k < 3; ++k) {
+        const uint16_t b = bf16_rne(rest);
+        Sb[k][size_t(i) * d + j] = b;
+        rest -= bf16_value(b);
+      }
     }
   }
   return TQ_OK;

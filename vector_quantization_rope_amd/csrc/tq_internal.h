@@ -30,7 +30,8 @@ struct CacheLayout {
 
 struct CodecLayout {
   // byte offsets inside the codec table
-  size_t ck = 0, tk = 0, cv = 0, tv = 0, D = 0, S = 0, ST = 0, Shi = 0, Slo = 0, total = 0;
+  size_t ck = 0, tk = 0, cv = 0, tv = 0, D = 0, S = 0, ST = 0, total = 0;
+  size_t Sb[3] = {0, 0, 0};   // S = Sb[0] + Sb[1] + Sb[2] exactly, each part bf16
   int block = 0;
 };
 
