@@ -564,12 +564,18 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
       const size_t srow = size_t(32 * mt + (lane & 31)) * D + 8 * half;
       const __bf16 *r0 = r_s + (lane & 31) * RS + 8 * half;
       const __bf16 *r1 = r0 + 32 * RS;
+      // the next step's S slices are requested one step ahead
+      constexpr int NS = D / 16;
+      v8bf sa[3];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) sa[k] = *reinterpret_cast<const v8bf *>(a.cp.Sb[k] + srow);
 #pragma unroll 2
-      for (int i = 0; i < D / 16; ++i) {
-        v8bf sa[3], ra[3], rb[3];
+      for (int i = 0; i < NS; ++i) {
+        v8bf ra[3], rb[3], sn[3];
+        const int inext = i + 1 < NS ? i + 1 : i;
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
-          sa[k] = *reinterpret_cast<const v8bf *>(a.cp.Sb[k] + srow + 16 * i);
+          sn[k] = *reinterpret_cast<const v8bf *>(a.cp.Sb[k] + srow + 16 * inext);
           ra[k] = *reinterpret_cast<const v8bf *>(r0 + k * 64 * RS + 16 * i);
           rb[k] = *reinterpret_cast<const v8bf *>(r1 + k * 64 * RS + 16 * i);
         }
@@ -583,6 +589,8 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
         TQ_SR(0, 1);
         TQ_SR(0, 0);
 #undef TQ_SR
+#pragma unroll
+        for (int k = 0; k < 3; ++k) sa[k] = sn[k];
       }
       // lane holds rows 8 (r / 4) + 4 (lane / 32) + r % 4 of token column lane % 32
       uint32_t b0 = 0u, b1 = 0u;
@@ -992,12 +1000,14 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_split(DecodeArgs a) {
 // ------------------------------------------------------------------ decode (MFMA path)
 // For bits_k = 2, m = d, bits_v = 3, d in {64, 128} and up to 8 q-heads per kv-head.
 //
-// Keys: the G query rows are written as 24-bit fixed point in three signed int8 digits
-// (rows digit * 8 + head of a 32-row A operand) and the packed 0/1 bit planes of 32 tokens
-// are the B operand of v_mfma_i32_32x32x32_i8: the products are exact integers, so
-// q . plane and S q . signs come out exact for the quantized query; the digits recombine
-// in-lane.  With c[code] = c0 + (c1 - c0) b0 + (c2 - c0) b1 (symmetric 2-bit codebook):
+// Keys: with c[code] = c0 + (c1 - c0) b0 + (c2 - c0) b1 (symmetric 2-bit codebook),
 //   score = n (c0 sum q + (c1-c0) q.b0 + (c2-c0) q.b1) + ||r|| sqrt(pi/2)/m (2 sq.s - sum sq).
+// The vectors (c1-c0) q and (c2-c0) q (one shared exponent) and sq = S q are written as
+// 32-bit fixed point in four signed int8 digits (rows digit * 8 + head of a 32-row A
+// operand), and the packed 0/1 bit planes of 32 tokens are the B operand of
+// v_mfma_i32_32x32x32_i8: the products are exact integers, both planes accumulate into one
+// sum, and the digit sums recombine in-lane.  32 bits keep every query element at its fp32
+// precision even when a few outlier coordinates set the exponent.
 // Values: p n_v is split into fp16 hi + lo rows (16 rows for 8 heads) and multiplied on
 // v_mfma_f32_16x16x32_f16 with the fp16 centroids of 32 tokens, looked up 4 codes at a
 // time from a 4096-entry LDS table (the stored centroids are fp16 values, so this B is
@@ -1008,10 +1018,12 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kMfmaMaxG = 8;
 constexpr int kQpackCoef = 8;   // floats per head: k0..k4, padding
+constexpr int kQpackVecs = 3;   // digit-row vectors: (c1 - c0) q, (c2 - c0) q, S q
+constexpr int kDigits = 4;      // int8 digits per value: 32-bit fixed point, rows digit * 8 + head
 
-// Per unit: [2 (q, sq)][32 rows][2 halves][d/32 chunks][16 bytes] of int8 digits, then
+// Per unit: [kQpackVecs][32 rows][2 halves][d/32 chunks][16 bytes] of int8 digits, then
 // [8 heads][kQpackCoef] floats.
-__host__ __device__ constexpr size_t qpack_unit_bytes(int d) { return size_t(2) * 32 * 2 * (d / 32) * 16 + kMfmaMaxG * kQpackCoef * 4; }
+__host__ __device__ constexpr size_t qpack_unit_bytes(int d) { return size_t(kQpackVecs) * 32 * 2 * (d / 32) * 16 + kMfmaMaxG * kQpackCoef * 4; }
 
 struct MfmaArgs {
   const uint8_t *kbits;
@@ -1146,13 +1158,16 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
     }
   }
   __syncthreads();
-  // fp32 rows and sums; maxima for the fixed-point scaling
+  // fp32 rows and sums; maxima for the fixed-point scaling (the two plane vectors
+  // (c1 - c0) q and (c2 - c0) q share one exponent, set by the larger weight)
+  const float dc1 = cp.ck[1] - cp.ck[0], dc2 = cp.ck[2] - cp.ck[0];
+  const float wmax = fmaxf(fabsf(dc1), fabsf(dc2));
   float *o = qrows + size_t(rowi) * qstride;
   float s0 = 0.0f, s1 = 0.0f, m0 = 0.0f, m1 = 0.0f;
   for (int j = tid; j < d; j += 256) {
     o[j] = qs[j];
     s0 += qs[j];
-    m0 = fmaxf(m0, fabsf(qs[j]));
+    m0 = fmaxf(m0, fabsf(qs[j]) * wmax);
   }
   for (int i = tid; i < m; i += 256) {
     o[d + i] = sqs[i];
@@ -1181,19 +1196,20 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
       if (mx > 0.0f) {
         int ex;
         frexpf(mx, &ex);   // mx < 2^ex
-        e = 22 - ex;
+        e = 30 - ex;   // |x| 2^e < 2^30: four signed int8 digits
       }
       sexp[v] = e;
     }
     if (qpack) {
       float *coef = reinterpret_cast<float *>(qpack + size_t(b * kv_heads + g) * qpack_unit_bytes(d) +
-                                              size_t(2) * 32 * 2 * (d / 32) * 16);
-      const float iq = ldexpf(1.0f, -sexp[0]), is = ldexpf(1.0f, -sexp[1]);
-      const float c0 = cp.ck[0], dc1 = cp.ck[1] - cp.ck[0], dc2 = cp.ck[2] - cp.ck[0];
+                                              size_t(kQpackVecs) * 32 * 2 * (d / 32) * 16);
+      // the decode kernel forms a digit sum as hi + lo 2^-16 (= sum / 65536)
+      const float iq = ldexpf(1.0f, 16 - sexp[0]), is = ldexpf(1.0f, 16 - sexp[1]);
+      const float c0 = cp.ck[0];
       float *k = coef + h * kQpackCoef;
       k[0] = c0 * S0;
-      k[1] = dc1 * iq;
-      k[2] = dc2 * iq;
+      k[1] = iq;
+      k[2] = 0.0f;
       k[3] = 2.0f * cp.qjl_scale * is;
       k[4] = cp.qjl_scale * S1;
       k[5] = k[6] = k[7] = 0.0f;
@@ -1206,40 +1222,38 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
   if (!qpack) return;
   const int nch = d / 32;
   uint32_t *o32 = reinterpret_cast<uint32_t *>(qpack + size_t(b * kv_heads + g) * qpack_unit_bytes(d));
-  // this head's rows digit * 8 + h, both vectors: [v][digit][half][chunk][e]
-  const int ndw = 2 * 3 * 2 * nch * 4;
+  // this head's rows digit * 8 + h of the three vectors: [v][digit][half][chunk][e]
+  const int ndw = kQpackVecs * kDigits * 2 * nch * 4;
   for (int i = tid; i < ndw; i += 256) {
     const int e = i & 3, c = (i >> 2) % nch, half = (i / (4 * nch)) & 1;
-    const int digit = (i / (8 * nch)) % 3, v = i / (24 * nch);
-    const float *src = v == 0 ? qs : sqs;
+    const int digit = (i / (8 * nch)) % kDigits, v = i / (8 * kDigits * nch);
+    const float *src = v == 2 ? sqs : qs;
+    const float wgt = v == 0 ? dc1 : (v == 1 ? dc2 : 1.0f);
+    const int ex = sexp[v == 2 ? 1 : 0];
     uint32_t word = 0u;
 #pragma unroll
     for (int beta = 0; beta < 4; ++beta) {
       const int j = 32 * (half * (d / 64) + (c >> 1)) + 8 * beta + 4 * (c & 1) + e;
-      const int xi = int(rintf(ldexpf(src[j], sexp[v])));
+      const int xi = int(rintf(ldexpf(src[j] * wgt, ex)));
       const int d0 = ((xi + 128) & 255) - 128;
       const int x1 = (xi - d0) >> 8;
       const int d1 = ((x1 + 128) & 255) - 128;
-      const int d2 = (x1 - d1) >> 8;
-      const int dg = digit == 0 ? d0 : (digit == 1 ? d1 : d2);
+      const int x2 = (x1 - d1) >> 8;
+      const int d2 = ((x2 + 128) & 255) - 128;
+      const int d3 = (x2 - d2) >> 8;
+      const int dg = digit == 0 ? d0 : (digit == 1 ? d1 : (digit == 2 ? d2 : d3));
       word |= uint32_t(dg & 255) << (8 * beta);
     }
     const int row = digit * 8 + h;
     o32[(((v * 32 + row) * 2 + half) * nch + c) * 4 + e] = word;
   }
-  if (h == 0) {
-    // rows of absent heads and the padding digit row group
-    const int nrow = 32 - 3 * G;
-    for (int i = tid; i < 2 * nrow * 2 * nch * 4; i += 256) {
+  if (h == 0 && G < 8) {
+    // rows (digit, head) of the absent heads h >= G
+    const int nrow = kDigits * (8 - G);
+    for (int i = tid; i < kQpackVecs * nrow * 2 * nch * 4; i += 256) {
       const int e = i & 3, c = (i >> 2) % nch, half = (i / (4 * nch)) & 1;
       const int ri = (i / (8 * nch)) % nrow, v = i / (8 * nch * nrow);
-      int row;
-      if (ri < 8) {
-        row = 24 + ri;
-      } else {
-        const int k = ri - 8;               // (digit, absent head) pairs
-        row = (k / (8 - G)) * 8 + G + k % (8 - G);
-      }
+      const int row = (ri / (8 - G)) * 8 + G + ri % (8 - G);
       o32[(((v * 32 + row) * 2 + half) * nch + c) * 4 + e] = 0u;
     }
   }
@@ -1364,19 +1378,21 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
     lut[i] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
   }
   const uint8_t *qpk = a.qpack + size_t(unit) * qpack_unit_bytes(D);
-  const float *coef = reinterpret_cast<const float *>(qpk + size_t(2) * 32 * 2 * NCH * 16);
+  const float *coef = reinterpret_cast<const float *>(qpk + size_t(kQpackVecs) * 32 * 2 * NCH * 16);
   if (tid < 40) {
     const int hf = tid / 20, k = (tid / 4) % 5, r = tid % 4;
     coef_s[hf][k][r] = coef[(4 * hf + r) * kQpackCoef + k];
   }
   const int row = lane & 31, half = lane >> 5;
-  v4i Aq[NCH], As[NCH];
+  // int8 digit rows: plane 0 weight (c1 - c0) q, plane 1 weight (c2 - c0) q, S q
+  v4i Aq0[NCH], Aq1[NCH], As[NCH];
   {
     const v4i *src = reinterpret_cast<const v4i *>(qpk);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      Aq[c] = src[((0 * 32 + row) * 2 + half) * NCH + c];
-      As[c] = src[((1 * 32 + row) * 2 + half) * NCH + c];
+      Aq0[c] = src[((0 * 32 + row) * 2 + half) * NCH + c];
+      Aq1[c] = src[((1 * 32 + row) * 2 + half) * NCH + c];
+      As[c] = src[((2 * 32 + row) * 2 + half) * NCH + c];
     }
   }
   __syncthreads();
@@ -1406,13 +1422,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
     const int kk = k < nk ? k : nk - 1;
     const int t0 = t_first + 128 * kk;
     const int nv = t_end - t0;   // valid tokens in the tile (1..32)
+    const bool whole = nv >= 32;   // wave-uniform: no clamping needed
     const uint8_t *ksrc = a.kbits + (ubase + t0) * Gm::KB;
     const int last = nv * Gm::KB / Gm::KCH - 1;
     constexpr int kchunks = Gm::KT / Gm::KCH;
 #pragma unroll
     for (int i = 0; i < Gm::NK; ++i) {
       if (64 * i + 64 <= kchunks || lane < kchunks - 64 * i) {
-        const int c = min(64 * i + lane, last);
+        const int c = whole ? 64 * i + lane : min(64 * i + lane, last);
         __builtin_amdgcn_global_load_lds(ksrc + Gm::KCH * c, slot + 64 * Gm::KCH * i, Gm::KCH, 0, 0);
       }
     }
@@ -1424,11 +1441,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
         __builtin_amdgcn_global_load_lds(vsrc + 1024 * i + 16 * lane, slot + Gm::KT + 1024 * i, 16, 0, 0);
     }
     if (lane < 32) {
-      const uint32_t *kn = a.knorm + ubase + t0 + min(lane, nv - 1);
+      const uint32_t *kn = a.knorm + ubase + t0 + (whole ? lane : min(lane, nv - 1));
       __builtin_amdgcn_global_load_lds(kn, slot + Gm::KN, 4, 0, 0);
     }
     if (lane < 17) {
-      // value norms: 17 dwords from the 4-byte boundary at or below token t0's norm
+      // value norms: 17 dwords from the 4-byte boundary at or below token t0's norm, none
+      // past the dword holding the tile's last token (the region may end right there)
       const size_t byte0 = (ubase + t0) * 2;
       const size_t lastb = (ubase + t0 + nv - 1) * 2;
       const size_t dw = min((byte0 & ~size_t(3)) + 4 * size_t(lane), lastb & ~size_t(3));
@@ -1490,42 +1508,43 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
       kw[0] = kw[1] = kw[2] = make_uint2(0u, 0u);
 #endif
     }
-    // ---- key scores on int8 MFMA
-    v16i s0 = {}, s1 = {}, s2 = {};
+    // ---- key scores on int8 MFMA: both code planes accumulate into s01 (their digit rows
+    // carry the plane weights), the sign bits into s2.  The B bytes of coordinate-chunk c
+    // are bits 4 (c & 1) + e, + 8, + 16, + 24 of the lane's plane dword for c / 2; one 64-bit
+    // shift serves the chunks c and c + 2.
+    v16i s01 = {}, s2 = {};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const uint32_t w0 = (c >> 1) ? kw[0].y : kw[0].x;
-      const uint32_t w1 = (c >> 1) ? kw[1].y : kw[1].x;
-      const uint32_t w2 = (c >> 1) ? kw[2].y : kw[2].x;
       v4i b0, b1, b2;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int sh = 4 * (c & 1) + e;
-        b0[e] = int((w0 >> sh) & 0x01010101u);
-        b1[e] = int((w1 >> sh) & 0x01010101u);
-        b2[e] = int((w2 >> sh) & 0x01010101u);
+        const uint64_t u0 = ((uint64_t(kw[0].y) << 32) | kw[0].x) >> sh;
+        const uint64_t u1 = ((uint64_t(kw[1].y) << 32) | kw[1].x) >> sh;
+        const uint64_t u2 = ((uint64_t(kw[2].y) << 32) | kw[2].x) >> sh;
+        b0[e] = int(uint32_t((c >> 1) ? (u0 >> 32) : u0) & 0x01010101u);
+        b1[e] = int(uint32_t((c >> 1) ? (u1 >> 32) : u1) & 0x01010101u);
+        b2[e] = int(uint32_t((c >> 1) ? (u2 >> 32) : u2) & 0x01010101u);
       }
-      s0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq[c], b0, s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq[c], b1, s1, 0, 0, 0);
+      s01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq0[c], b0, s01, 0, 0, 0);
+      s01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq1[c], b1, s01, 0, 0, 0);
       s2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(As[c], b2, s2, 0, 0, 0);
     }
     const float n16 = f16_bits_to_float(nr & 0xFFFFu), rn16 = f16_bits_to_float(nr >> 16);
     const float vnorm = f16_bits_to_float(vnb & 0xFFFFu);
     const float4 k0 = *reinterpret_cast<const float4 *>(coef_s[half][0]);
     const float4 k1 = *reinterpret_cast<const float4 *>(coef_s[half][1]);
-    const float4 k2 = *reinterpret_cast<const float4 *>(coef_s[half][2]);
     const float4 k3 = *reinterpret_cast<const float4 *>(coef_s[half][3]);
     const float4 k4 = *reinterpret_cast<const float4 *>(coef_s[half][4]);
     const float K0[4] = {k0.x, k0.y, k0.z, k0.w}, K1[4] = {k1.x, k1.y, k1.z, k1.w};
-    const float K2[4] = {k2.x, k2.y, k2.z, k2.w}, K3[4] = {k3.x, k3.y, k3.z, k3.w};
-    const float K4[4] = {k4.x, k4.y, k4.z, k4.w};
+    const float K3[4] = {k3.x, k3.y, k3.z, k3.w}, K4[4] = {k4.x, k4.y, k4.z, k4.w};
     float lam[4], sc[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int S0 = s0[r] + 256 * s0[4 + r] + 65536 * s0[8 + r];
-      const int S1 = s1[r] + 256 * s1[4 + r] + 65536 * s1[8 + r];
-      const int S2 = s2[r] + 256 * s2[4 + r] + 65536 * s2[8 + r];
-      sc[r] = n16 * (K0[r] + K1[r] * float(S0) + K2[r] * float(S1)) + rn16 * (K3[r] * float(S2) - K4[r]);
+      // digit sums: rows 8 digit + head are accumulator registers 4 digit + r
+      const float S01 = fmaf(float(s01[r] + 256 * s01[4 + r]), 0x1p-16f, float(s01[8 + r] + 256 * s01[12 + r]));
+      const float S2 = fmaf(float(s2[r] + 256 * s2[4 + r]), 0x1p-16f, float(s2[8 + r] + 256 * s2[12 + r]));
+      sc[r] = n16 * (K0[r] + K1[r] * S01) + rn16 * (K3[r] * S2 - K4[r]);
       lam[r] = (valid && 4 * half + r < a.G) ? sc[r] * a.scale_log2 : -INFINITY;
     }
     if (a.scores) {
@@ -1536,10 +1555,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
       }
     }
     // ---- online softmax (log2 domain); tile maxima and running maxima are wave-uniform.
-    // The tile maxima are reduced only when some score exceeds its head's running max.
+    // The running maxima are raised (and the accumulators rescaled) only when a score
+    // exceeds its head's maximum by more than 8, so p = 2^(lam - M) <= 256 between raises;
+    // a token whose value norm is 255 or more allows no slack, which keeps p * n_v within
+    // fp16 range (256 * 255 < 65504) for the hi/lo split below.
+    const float slack = vnorm < 255.0f ? 8.0f : 0.0f;
     bool above = false;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) above |= lam[r] > (half ? M[4 + r] : M[r]);
+    for (int r = 0; r < 4; ++r) above |= lam[r] > (half ? M[4 + r] : M[r]) + slack;
     if (__builtin_amdgcn_ballot_w64(above) != 0) {
       float tm[kMfmaMaxG];
 #pragma unroll
