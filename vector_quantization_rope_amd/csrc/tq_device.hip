@@ -1347,6 +1347,12 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
   }
 }
 
+// a where mask bits are set, else b (a bitwise select: the compiler keeps it a v_bfi
+// rather than turning a choice between array elements into an indexed stack access)
+__device__ __forceinline__ float pick_bits(uint32_t mask, float a, float b) {
+  return __uint_as_float((mask & __float_as_uint(a)) | (~mask & __float_as_uint(b)));
+}
+
 __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
@@ -1402,9 +1408,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
   const size_t ubase = size_t(unit) * a.capacity;
   const int t_first = t_begin + 32 * wv;
   const int nk = t_end > t_first ? (t_end - t_first + 127) / 128 : 0;
-  float M[kMfmaMaxG], lsum[4];
+  float M[kMfmaMaxG], Mh[4], lsum[4];   // Mh: the running maxima of this lane's 4 heads
+  const uint32_t hmask = half ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-  for (int h = 0; h < kMfmaMaxG; ++h) M[h] = -INFINITY;
+  for (int h = 0; h < kMfmaMaxG; ++h) M[h] = h < a.G ? -INFINITY : 0.0f;   // absent heads: any finite value
+#pragma unroll
+  for (int r = 0; r < 4; ++r) Mh[r] = pick_bits(hmask, M[4 + r], M[r]);
 #pragma unroll
   for (int r = 0; r < 4; ++r) lsum[r] = 0.0f;
   v4f acc[NT];
@@ -1418,6 +1427,11 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
   // Tile k of this wave starts at t_first + 128 k.  Every chunk a lane loads stays inside
   // the tokens [t0, t_end); tiles past the end reload the last one into a slot that is
   // never read, so every step issues the same Gm::NDMA loads.
+  // Each load is a uniform base (per tile, in SGPRs) plus a 32-bit per-lane byte offset;
+  // for whole tiles the offsets are fixed, so a step spends almost no VALU on addresses.
+  uint32_t koff[Gm::NK];
+#pragma unroll
+  for (int i = 0; i < Gm::NK; ++i) koff[i] = uint32_t(Gm::KCH * (64 * i + lane));
   auto issue_dma = [&](int k, uint8_t *slot) {
     const int kk = k < nk ? k : nk - 1;
     const int t0 = t_first + 128 * kk;
@@ -1429,8 +1443,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
 #pragma unroll
     for (int i = 0; i < Gm::NK; ++i) {
       if (64 * i + 64 <= kchunks || lane < kchunks - 64 * i) {
-        const int c = whole ? 64 * i + lane : min(64 * i + lane, last);
-        __builtin_amdgcn_global_load_lds(ksrc + Gm::KCH * c, slot + 64 * Gm::KCH * i, Gm::KCH, 0, 0);
+        const uint32_t o = whole ? koff[i] : uint32_t(Gm::KCH * min(64 * i + lane, last));
+        __builtin_amdgcn_global_load_lds(ksrc + o, slot + 64 * Gm::KCH * i, Gm::KCH, 0, 0);
       }
     }
     const uint8_t *vsrc = vbase + size_t(t0 / kValueTile) * Gm::VT;
@@ -1438,19 +1452,20 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
 #pragma unroll
     for (int i = 0; i < Gm::NV; ++i) {
       if (64 * i + 64 <= vchunks || lane < vchunks - 64 * i)
-        __builtin_amdgcn_global_load_lds(vsrc + 1024 * i + 16 * lane, slot + Gm::KT + 1024 * i, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vsrc + 1024 * i + uint32_t(16 * lane), slot + Gm::KT + 1024 * i, 16, 0, 0);
     }
     if (lane < 32) {
-      const uint32_t *kn = a.knorm + ubase + t0 + (whole ? lane : min(lane, nv - 1));
-      __builtin_amdgcn_global_load_lds(kn, slot + Gm::KN, 4, 0, 0);
+      const uint8_t *kn = reinterpret_cast<const uint8_t *>(a.knorm + ubase + t0);
+      __builtin_amdgcn_global_load_lds(kn + uint32_t(4 * (whole ? lane : min(lane, nv - 1))), slot + Gm::KN, 4, 0, 0);
     }
     if (lane < 17) {
       // value norms: 17 dwords from the 4-byte boundary at or below token t0's norm, none
       // past the dword holding the tile's last token (the region may end right there)
       const size_t byte0 = (ubase + t0) * 2;
       const size_t lastb = (ubase + t0 + nv - 1) * 2;
-      const size_t dw = min((byte0 & ~size_t(3)) + 4 * size_t(lane), lastb & ~size_t(3));
-      __builtin_amdgcn_global_load_lds(vnbase + dw, slot + Gm::VN, 4, 0, 0);
+      const uint32_t span = uint32_t((lastb & ~size_t(3)) - (byte0 & ~size_t(3)));
+      __builtin_amdgcn_global_load_lds(vnbase + (byte0 & ~size_t(3)) + min(uint32_t(4 * lane), span),
+                                       slot + Gm::VN, 4, 0, 0);
     }
   };
 
@@ -1560,10 +1575,10 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
     // a token whose value norm is 255 or more allows no slack, which keeps p * n_v within
     // fp16 range (256 * 255 < 65504) for the hi/lo split below.
     const float slack = vnorm < 255.0f ? 8.0f : 0.0f;
-    bool above = false;
+    uint64_t above = 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) above |= lam[r] > (half ? M[4 + r] : M[r]) + slack;
-    if (__builtin_amdgcn_ballot_w64(above) != 0) {
+    for (int r = 0; r < 4; ++r) above |= __builtin_amdgcn_ballot_w64(lam[r] - slack > Mh[r]);
+    if (above != 0) {
       float tm[kMfmaMaxG];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1585,13 +1600,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= al;
         lsum[r] *= half ? alpha[4 + r] : alpha[r];
+        Mh[r] = pick_bits(hmask, M[4 + r], M[r]);
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * half + r;
-      const float mh = half ? M[4 + r] : M[r];
-      const float p = lam[r] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(lam[r] - mh);
+      // lam = -inf (absent token) gives p = 0: Mh is finite after the first tile
+      const float p = __builtin_amdgcn_exp2f(lam[r] - Mh[r]);
       lsum[r] += p;
       const float pv = p * vnorm;
       const _Float16 hi = (_Float16)pv;
