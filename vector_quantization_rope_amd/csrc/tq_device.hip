@@ -1266,60 +1266,10 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
 // softmax, fp16 MFMA value accumulation, as in the register-fed kernel above.
 constexpr int kRing = 3;
 
-// Reads of a ring slot written by direct global->LDS loads.  They are inline assembly,
-// each block waiting for its own results (lgkmcnt(0)), because the compiler would
-// otherwise wait for every direct-to-LDS load in flight (including the prefetches into
-// the other slots) before any LDS read; the ring's own vmcnt waits order them instead.
-// the two value-code dwords of 8 value tiles (d = 128) or 4 (d = 64), 192 bytes apart
-template <int NT>
-__device__ __forceinline__ void lds_read_vals(uint32_t addr, uint32_t (&w)[NT][2]) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  if constexpr (NT == 8) {
-    asm volatile(
-        "ds_read_b32 %0, %16\n"
-        "ds_read_b32 %1, %16 offset:4\n"
-        "ds_read_b32 %2, %16 offset:192\n"
-        "ds_read_b32 %3, %16 offset:196\n"
-        "ds_read_b32 %4, %16 offset:384\n"
-        "ds_read_b32 %5, %16 offset:388\n"
-        "ds_read_b32 %6, %16 offset:576\n"
-        "ds_read_b32 %7, %16 offset:580\n"
-        "ds_read_b32 %8, %16 offset:768\n"
-        "ds_read_b32 %9, %16 offset:772\n"
-        "ds_read_b32 %10, %16 offset:960\n"
-        "ds_read_b32 %11, %16 offset:964\n"
-        "ds_read_b32 %12, %16 offset:1152\n"
-        "ds_read_b32 %13, %16 offset:1156\n"
-        "ds_read_b32 %14, %16 offset:1344\n"
-        "ds_read_b32 %15, %16 offset:1348\n"
-        "s_waitcnt lgkmcnt(0)\n"
-        : "=v"(w[0][0]), "=v"(w[0][1]), "=v"(w[1][0]), "=v"(w[1][1]), "=v"(w[2][0]), "=v"(w[2][1]),
-          "=v"(w[3][0]), "=v"(w[3][1]), "=v"(w[4][0]), "=v"(w[4][1]), "=v"(w[5][0]), "=v"(w[5][1]),
-          "=v"(w[6][0]), "=v"(w[6][1]), "=v"(w[7][0]), "=v"(w[7][1])
-        : "v"(addr)
-        : "memory");
-  } else {
-    asm volatile(
-        "ds_read_b32 %0, %8\n"
-        "ds_read_b32 %1, %8 offset:4\n"
-        "ds_read_b32 %2, %8 offset:192\n"
-        "ds_read_b32 %3, %8 offset:196\n"
-        "ds_read_b32 %4, %8 offset:384\n"
-        "ds_read_b32 %5, %8 offset:388\n"
-        "ds_read_b32 %6, %8 offset:576\n"
-        "ds_read_b32 %7, %8 offset:580\n"
-        "s_waitcnt lgkmcnt(0)\n"
-        : "=v"(w[0][0]), "=v"(w[0][1]), "=v"(w[1][0]), "=v"(w[1][1]), "=v"(w[2][0]), "=v"(w[2][1]),
-          "=v"(w[3][0]), "=v"(w[3][1])
-        : "v"(addr)
-        : "memory");
-  }
-#else
-  (void)addr;
-  (void)w;
-#endif
-}
-
+// Reads of a ring slot written by direct global->LDS loads are inline assembly, each
+// block waiting for its own results (lgkmcnt(0)), because the compiler would otherwise
+// wait for every direct-to-LDS load in flight (including the prefetches into the other
+// slots) before any LDS read; the ring's own vmcnt waits order them instead.
 template <int D>
 struct LdsGeom {
   static constexpr int KB = 3 * D / 8;     // key record bytes (2 planes + m = d sign bits)
@@ -1480,36 +1430,69 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
     const int t = t0 + row;
     const bool valid = t < t_end;
     const uint32_t sbase = uint32_t(reinterpret_cast<uintptr_t>(slot));
-    // ---- this lane's key words and its token's norms
+    // ---- this lane's key words, its token's norms and its value-code words, read in one
+    // block; the value LUT lookups follow at once so their latency overlaps the key MFMAs
     uint2 kw[3];
     uint32_t nr, vnb;
+    uint32_t vwr[NT][2];
     {
       const uint32_t kaddr = sbase + row * Gm::KB + half * (D / 16);
       const uint32_t naddr = sbase + Gm::KN + 4 * row;
       const uint32_t vaddr = sbase + Gm::VN + uint32_t(((ubase + t0) * 2) & 3) + 2 * row;
+      const uint32_t caddr = sbase + Gm::KT + vn * 12 + 4 * vidx;
 #if defined(__HIP_DEVICE_COMPILE__)
       if constexpr (D >= 128) {
         asm volatile(
-            "ds_read_b64 %0, %5\n"
-            "ds_read_b64 %1, %5 offset:16\n"
-            "ds_read_b64 %2, %5 offset:32\n"
-            "ds_read_b32 %3, %6\n"
-            "ds_read_u16 %4, %7\n"
+            "ds_read_b64 %0, %21\n"
+            "ds_read_b64 %1, %21 offset:16\n"
+            "ds_read_b64 %2, %21 offset:32\n"
+            "ds_read_b32 %3, %22\n"
+            "ds_read_u16 %4, %23\n"
+            "ds_read_b32 %5, %24\n"
+            "ds_read_b32 %6, %24 offset:4\n"
+            "ds_read_b32 %7, %24 offset:192\n"
+            "ds_read_b32 %8, %24 offset:196\n"
+            "ds_read_b32 %9, %24 offset:384\n"
+            "ds_read_b32 %10, %24 offset:388\n"
+            "ds_read_b32 %11, %24 offset:576\n"
+            "ds_read_b32 %12, %24 offset:580\n"
+            "ds_read_b32 %13, %24 offset:768\n"
+            "ds_read_b32 %14, %24 offset:772\n"
+            "ds_read_b32 %15, %24 offset:960\n"
+            "ds_read_b32 %16, %24 offset:964\n"
+            "ds_read_b32 %17, %24 offset:1152\n"
+            "ds_read_b32 %18, %24 offset:1156\n"
+            "ds_read_b32 %19, %24 offset:1344\n"
+            "ds_read_b32 %20, %24 offset:1348\n"
             "s_waitcnt lgkmcnt(0)\n"
-            : "=v"(kw[0]), "=v"(kw[1]), "=v"(kw[2]), "=v"(nr), "=v"(vnb)
-            : "v"(kaddr), "v"(naddr), "v"(vaddr)
+            : "=v"(kw[0]), "=v"(kw[1]), "=v"(kw[2]), "=v"(nr), "=v"(vnb),
+              "=v"(vwr[0][0]), "=v"(vwr[0][1]), "=v"(vwr[1][0]), "=v"(vwr[1][1]), "=v"(vwr[2][0]),
+              "=v"(vwr[2][1]), "=v"(vwr[3][0]), "=v"(vwr[3][1]), "=v"(vwr[4][0]), "=v"(vwr[4][1]),
+              "=v"(vwr[5][0]), "=v"(vwr[5][1]), "=v"(vwr[6][0]), "=v"(vwr[6][1]), "=v"(vwr[7][0]),
+              "=v"(vwr[7][1])
+            : "v"(kaddr), "v"(naddr), "v"(vaddr), "v"(caddr)
             : "memory");
       } else {
         uint32_t x0, x1, x2;
         asm volatile(
-            "ds_read_b32 %0, %5\n"
-            "ds_read_b32 %1, %5 offset:8\n"
-            "ds_read_b32 %2, %5 offset:16\n"
-            "ds_read_b32 %3, %6\n"
-            "ds_read_u16 %4, %7\n"
+            "ds_read_b32 %0, %13\n"
+            "ds_read_b32 %1, %13 offset:8\n"
+            "ds_read_b32 %2, %13 offset:16\n"
+            "ds_read_b32 %3, %14\n"
+            "ds_read_u16 %4, %15\n"
+            "ds_read_b32 %5, %16\n"
+            "ds_read_b32 %6, %16 offset:4\n"
+            "ds_read_b32 %7, %16 offset:192\n"
+            "ds_read_b32 %8, %16 offset:196\n"
+            "ds_read_b32 %9, %16 offset:384\n"
+            "ds_read_b32 %10, %16 offset:388\n"
+            "ds_read_b32 %11, %16 offset:576\n"
+            "ds_read_b32 %12, %16 offset:580\n"
             "s_waitcnt lgkmcnt(0)\n"
-            : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(nr), "=v"(vnb)
-            : "v"(kaddr), "v"(naddr), "v"(vaddr)
+            : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(nr), "=v"(vnb),
+              "=v"(vwr[0][0]), "=v"(vwr[0][1]), "=v"(vwr[1][0]), "=v"(vwr[1][1]), "=v"(vwr[2][0]),
+              "=v"(vwr[2][1]), "=v"(vwr[3][0]), "=v"(vwr[3][1])
+            : "v"(kaddr), "v"(naddr), "v"(vaddr), "v"(caddr)
             : "memory");
         kw[0] = make_uint2(x0, 0u);
         kw[1] = make_uint2(x1, 0u);
@@ -1519,9 +1502,23 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
       (void)kaddr;
       (void)naddr;
       (void)vaddr;
+      (void)caddr;
       nr = vnb = 0u;
       kw[0] = kw[1] = kw[2] = make_uint2(0u, 0u);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) vwr[nt][0] = vwr[nt][1] = 0u;
 #endif
+    }
+    // value B operands: 8 tokens' fp16 centroids of coordinate 16 nt + vn, two LUT lookups
+    v8h Bv[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t lo = vwr[nt][0];
+      const uint32_t hi = vidx < 2 ? vwr[nt][1] : 0u;
+      const uint32_t x = uint32_t(((uint64_t(hi) << 32) | lo) >> vsh);
+      const uint2 e0 = lut[x & 0xFFFu], e1 = lut[(x >> 12) & 0xFFFu];
+      v4i bw = {int(e0.x), int(e0.y), int(e1.x), int(e1.y)};
+      __builtin_memcpy(&Bv[nt], &bw, 16);
     }
     // ---- key scores on int8 MFMA: both code planes accumulate into s01 (their digit rows
     // carry the plane weights), the sign bits into s2.  The B bytes of coordinate-chunk c
@@ -1617,19 +1614,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     const v8h A = *reinterpret_cast<const v8h *>(&pt_s[wv][vn][8 * vq]);
-    uint32_t vwr[NT][2];
-    lds_read_vals<NT>(sbase + Gm::KT + vn * 12 + 4 * vidx, vwr);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const uint32_t lo = vwr[nt][0];
-      const uint32_t hi = vidx < 2 ? vwr[nt][1] : 0u;
-      const uint32_t x = uint32_t(((uint64_t(hi) << 32) | lo) >> vsh);
-      const uint2 e0 = lut[x & 0xFFFu], e1 = lut[(x >> 12) & 0xFFFu];
-      v4i bw = {int(e0.x), int(e0.y), int(e1.x), int(e1.y)};
-      v8h Bv;
-      __builtin_memcpy(&Bv, &bw, 16);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bv, acc[nt], 0, 0, 0);
-    }
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bv[nt], acc[nt], 0, 0, 0);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   };
 
