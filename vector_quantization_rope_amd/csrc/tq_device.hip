@@ -1925,11 +1925,15 @@ bool decode_mfma_path(const tq_cache_desc &c, int q_heads) {
 
 constexpr int kMfmaChunk = 128;   // tokens per block iteration (4 waves x 32)
 
+constexpr int kDecodeBlocks = 512;
+
 int default_splits(const tq_cache_desc &c, int length) {
   if (length <= 0) return 1;
   const int units = c.batch * c.kv_heads;
   const int by_len = (length + kMfmaChunk - 1) / kMfmaChunk;
-  const int want = (1024 + units - 1) / units;
+  // one round of blocks: the split kernel keeps 2 blocks resident per CU and MI355X has
+  // 256 CUs, so 512 blocks start together and none waits for a second round
+  const int want = (kDecodeBlocks + units - 1) / units;
   int s = by_len < want ? by_len : want;
   if (s < 1) s = 1;
   if (s > 4096) s = 4096;
