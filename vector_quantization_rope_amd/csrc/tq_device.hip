@@ -133,6 +133,11 @@ CachePtrs cache_ptrs(void *cache_dev, const tq_cache_desc &c) {
   return p;
 }
 
+__global__ void k_fill_zero(float *p, size_t n) {
+  const size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
 // ------------------------------------------------------------------ cache header
 __global__ void k_cache_init(uint32_t *hdr, tq_cache_desc c) {
   const int i = threadIdx.x;
@@ -2098,8 +2103,10 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
   const int rows = desc->batch * q_heads;
   hipStream_t s = hipStream_t(stream);
   if (length == 0) {
-    if (hipMemsetAsync(out, 0, size_t(rows) * d * 4, s) != hipSuccess) return TQ_EDEVICE;
-    return TQ_OK;
+    // a fill kernel rather than a memset node, so the call can be captured in a graph
+    const size_t n = size_t(rows) * d;
+    hipLaunchKernelGGL(k_fill_zero, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, out, n);
+    return launch_status();
   }
   const CodecPtrs cp = codec_ptrs(codec_dev, d, desc->bits_k, desc->bits_v, m);
   float *qp = static_cast<float *>(ws);
@@ -2111,8 +2118,8 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
   const float sc = scale == 0.0f ? float(1.0 / std::sqrt(double(d))) : scale;
   const bool mfma = decode_mfma_path(*desc, q_heads);
   // symmetric 2-bit codebook on the MFMA path: c[code] = c0 + (c1 - c0) b0 + (c2 - c0) b1
-  hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s, q, int(dtype), d,
-                     m, q_pos, rope_base, cp, qp, qstride, q_heads, G, mfma ? qpack : nullptr);
+  hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s, q,
+                     int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, mfma ? qpack : nullptr);
   const CachePtrs ch = cache_ptrs(const_cast<void *>(cache_dev), *desc);
   int used_splits = S;
   if (mfma) {
