@@ -1913,6 +1913,249 @@ __global__ __launch_bounds__(256) void k_search_merge(const float *cand_s, const
   }
 }
 
+// Inner-product search on int8 MFMA for 3-bit database codes with m = d.  For a symmetric
+// 8-level codebook (c[7 - k] = -c[k]) a centroid is an odd function of the three code
+// bits, c = a0 s0 + a1 s1 + a2 s2 + a3 s0 s1 s2 with s = 2 b - 1 and s0 s1 s2 = 2 (b0^b1^b2) - 1,
+// so <q, c[codes]> = sum_k a_k (2 q.b_k - sum q) over four 0/1 planes (the three code planes
+// and their XOR).  The query rows are written as 32-bit fixed point in four int8 digits
+// (A rows digit * 8 + query, 8 queries per block) and kept in LDS; each wave streams
+// 32-vector database tiles, expands the plane and sign bits to 0/1 bytes (B) and runs five
+// v_mfma_i32_32x32x32_i8 per 32 coordinates (four code planes, the sign bits).  The tile's
+// scores update per-(wave, query) top-k lists in LDS; the block then merges its waves'
+// lists into one candidate list per query.
+constexpr int kSmQ = 8;        // queries per block
+constexpr int kSmWaves = 8;    // waves per block (512 threads), one block per CU
+constexpr int kSmTopMax = 16;  // list length per (wave, query); k <= 16 on this path
+
+struct SearchMfmaArgs {
+  const uint8_t *kbits;
+  const uint32_t *knorm;
+  const float *ck;
+  const float *qp;   // prepared query rows: qr [d], sq [d], sum qr, sum sq
+  float *cand_s;     // [nq][slices][k]
+  int *cand_i;
+  int kbytes, d, n_db, nq, k, slices, per, qstride;
+  float qjl_scale;
+};
+
+__global__ __launch_bounds__(512, 1) void k_search_mfma(SearchMfmaArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  extern __shared__ __align__(16) uint8_t sm_u8[];
+  const int nch = a.d / 32;
+  uint8_t *Aq = sm_u8;                              // [nch][64 lanes][16 B]
+  uint8_t *As = sm_u8 + size_t(nch) * 1024;
+  float *lst_s = reinterpret_cast<float *>(sm_u8 + size_t(nch) * 2048);   // [waves][8][kSmTopMax]
+  int *lst_i = reinterpret_cast<int *>(lst_s + kSmWaves * kSmQ * kSmTopMax);
+  __shared__ int exps[kSmQ][2];
+  __shared__ float sums[kSmQ][2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, half = lane >> 5;
+  const int q0 = blockIdx.x * kSmQ, slice = blockIdx.y;
+  const int nqb = min(kSmQ, a.nq - q0);
+  // ---- per-query exponents and sums (wave w takes query w)
+  {
+    const int qi = wv;
+    float m0 = 0.0f, m1 = 0.0f;
+    if (qi < nqb) {
+      const float *qr = a.qp + size_t(q0 + qi) * a.qstride;
+      for (int j = lane; j < a.d; j += 64) {
+        m0 = fmaxf(m0, fabsf(qr[j]));
+        m1 = fmaxf(m1, fabsf(qr[a.d + j]));
+      }
+    }
+    m0 = wave_max(m0);
+    m1 = wave_max(m1);
+    if (lane == 0) {
+      const float mx[2] = {m0, m1};
+      for (int v = 0; v < 2; ++v) {
+        int e = 0;
+        if (mx[v] > 0.0f) {
+          int ex;
+          frexpf(mx[v], &ex);   // mx < 2^ex
+          e = 30 - ex;          // |x| 2^e < 2^30: four signed int8 digits
+        }
+        exps[qi][v] = e;
+        sums[qi][v] = qi < nqb ? a.qp[size_t(q0 + qi) * a.qstride + 2 * a.d + v] : 0.0f;
+      }
+    }
+  }
+  for (int i = tid; i < kSmWaves * kSmQ * kSmTopMax; i += 512) {
+    lst_s[i] = -INFINITY;
+    lst_i[i] = -1;
+  }
+  __syncthreads();
+  // ---- A digits: lane (row = digit * 8 + query, half h), dword e, byte b of chunk c holds
+  // coordinate 32 c + 8 b + 4 h + e
+  for (int i = tid; i < 2 * nch * 256; i += 512) {
+    const int e = i & 3, ln = (i >> 2) & 63, c = (i >> 8) % nch, v = i / (256 * nch);
+    const int row = ln & 31, h = ln >> 5, digit = row >> 3, qi = row & 7;
+    uint32_t word = 0u;
+    if (qi < nqb) {
+      const float *src = a.qp + size_t(q0 + qi) * a.qstride + (v ? a.d : 0);
+      const int ex = exps[qi][v];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int j = 32 * c + 8 * b + 4 * h + e;
+        const int xi = int(rintf(ldexpf(src[j], ex)));
+        const int d0 = ((xi + 128) & 255) - 128;
+        const int x1v = (xi - d0) >> 8;
+        const int d1 = ((x1v + 128) & 255) - 128;
+        const int x2 = (x1v - d1) >> 8;
+        const int d2 = ((x2 + 128) & 255) - 128;
+        const int d3 = (x2 - d2) >> 8;
+        const int dg = digit == 0 ? d0 : (digit == 1 ? d1 : (digit == 2 ? d2 : d3));
+        word |= uint32_t(dg & 255) << (8 * b);
+      }
+    }
+    reinterpret_cast<uint32_t *>(v ? As : Aq)[i - v * 256 * nch] = word;
+  }
+  __syncthreads();
+  // ---- per-lane constants for its queries 4 half + r
+  const float c4 = a.ck[4], c5 = a.ck[5], c6 = a.ck[6], c7 = a.ck[7];
+  const float al[4] = {0.25f * (c7 - c6 + c5 - c4), 0.25f * (c7 + c6 - c5 - c4),
+                       0.25f * (c7 + c6 + c5 + c4), 0.25f * (c7 - c6 - c5 + c4)};
+  const float alsum = (al[0] + al[1]) + (al[2] + al[3]);
+  float sq_q[4], ss_q[4], cq[4], cs[4], thr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int qi = 4 * half + r;
+    sq_q[r] = ldexpf(2.0f, 16 - exps[qi][0]);   // 2 x (digit sum scale)
+    ss_q[r] = ldexpf(2.0f, 16 - exps[qi][1]);
+    cq[r] = sums[qi][0] * alsum;
+    cs[r] = sums[qi][1];
+    thr[r] = -INFINITY;
+  }
+  const int x0 = slice * a.per;
+  const int x1 = min(a.n_db, x0 + a.per);
+  const int ntile = x1 > x0 ? (x1 - x0 + 31) / 32 : 0;
+  const int pb = a.d / 8;   // plane bytes
+  const v4i *Aq4 = reinterpret_cast<const v4i *>(Aq);
+  const v4i *As4 = reinterpret_cast<const v4i *>(As);
+  const int sh0 = 4 * half;
+  for (int t = wv; t < ntile; t += kSmWaves) {
+    const int n = x0 + 32 * t + (lane & 31);
+    const bool valid = n < x1;
+    const uint8_t *rec = a.kbits + size_t(valid ? n : x0) * a.kbytes;
+    v16i acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {}, accs = {};
+    for (int g = 0; g < nch / 4; ++g) {
+      const uint4 p0 = *reinterpret_cast<const uint4 *>(rec + 16 * g);
+      const uint4 p1 = *reinterpret_cast<const uint4 *>(rec + pb + 16 * g);
+      const uint4 p2 = *reinterpret_cast<const uint4 *>(rec + 2 * pb + 16 * g);
+      const uint4 ps = *reinterpret_cast<const uint4 *>(rec + 3 * pb + 16 * g);
+      const uint32_t w0s[4] = {p0.x, p0.y, p0.z, p0.w}, w1s[4] = {p1.x, p1.y, p1.z, p1.w};
+      const uint32_t w2s[4] = {p2.x, p2.y, p2.z, p2.w}, wss[4] = {ps.x, ps.y, ps.z, ps.w};
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int c = 4 * g + cc;
+        const uint32_t w0 = w0s[cc] >> sh0, w1 = w1s[cc] >> sh0, w2 = w2s[cc] >> sh0;
+        const uint32_t wsg = wss[cc] >> sh0, wx = w0 ^ w1 ^ w2;
+        v4i b0, b1, b2, bx, bs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          b0[e] = int((w0 >> e) & 0x01010101u);
+          b1[e] = int((w1 >> e) & 0x01010101u);
+          b2[e] = int((w2 >> e) & 0x01010101u);
+          bx[e] = int((wx >> e) & 0x01010101u);
+          bs[e] = int((wsg >> e) & 0x01010101u);
+        }
+        const v4i aq = Aq4[c * 64 + lane], as = As4[c * 64 + lane];
+        acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(aq, b0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(aq, b1, acc1, 0, 0, 0);
+        acc2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(aq, b2, acc2, 0, 0, 0);
+        acc3 = __builtin_amdgcn_mfma_i32_32x32x32_i8(aq, bx, acc3, 0, 0, 0);
+        accs = __builtin_amdgcn_mfma_i32_32x32x32_i8(as, bs, accs, 0, 0, 0);
+      }
+    }
+    // scores of vector n for queries 4 half + r (accumulator registers 4 digit + r)
+    const uint32_t nr = valid ? a.knorm[n] : 0u;
+    const float n16 = f16_bits_to_float(nr & 0xFFFFu), rn16 = f16_bits_to_float(nr >> 16);
+    float sc[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#define TQ_DS(acc) fmaf(float(acc[r] + 256 * acc[4 + r]), 0x1p-16f, float(acc[8 + r] + 256 * acc[12 + r]))
+      const float code = (al[0] * TQ_DS(acc0) + al[1] * TQ_DS(acc1) + al[2] * TQ_DS(acc2) + al[3] * TQ_DS(acc3)) *
+                             sq_q[r] - cq[r];
+      const float qjl = TQ_DS(accs) * ss_q[r] - cs[r];
+#undef TQ_DS
+      const bool live = valid && (4 * half + r) < nqb;
+      sc[r] = live ? n16 * code + rn16 * a.qjl_scale * qjl : -INFINITY;
+    }
+    // ---- top-k lists: candidates beating their list's k-th score, lowest lane first
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      bool pending = sc[r] > thr[r];
+      uint64_t mask = __builtin_amdgcn_ballot_w64(pending);
+      while (mask) {
+        const int bl = __builtin_ctzll(mask);
+        const float s = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc[r]), bl));
+        const int qi = (bl < 32 ? 0 : 4) + r;
+        float *ls = lst_s + (wv * kSmQ + qi) * kSmTopMax;
+        int *li = lst_i + (wv * kSmQ + qi) * kSmTopMax;
+        if (lane == 0) {
+          int pos = a.k - 1;
+          while (pos > 0 && s > ls[pos - 1]) {
+            ls[pos] = ls[pos - 1];
+            li[pos] = li[pos - 1];
+            --pos;
+          }
+          ls[pos] = s;
+          li[pos] = x0 + 32 * t + (bl & 31);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const float nt = ls[a.k - 1];
+        if ((bl < 32) == (half == 0)) thr[r] = nt;
+        if (lane == bl) pending = false;
+        pending = pending && sc[r] > thr[r];
+        mask = __builtin_amdgcn_ballot_w64(pending);
+      }
+    }
+  }
+  __syncthreads();
+  // ---- merge the waves' lists: wave w takes query w, k rounds of arg-max over 8 k entries
+  if (wv < nqb) {
+    const int qi = wv;
+    const int ncand = kSmWaves * a.k;
+    float cs0 = -INFINITY, cs1 = -INFINITY;
+    int ci0 = 0x7FFFFFFF, ci1 = 0x7FFFFFFF;
+    if (lane < ncand) {
+      const int w = lane / a.k, e = lane % a.k;
+      cs0 = lst_s[(w * kSmQ + qi) * kSmTopMax + e];
+      ci0 = lst_i[(w * kSmQ + qi) * kSmTopMax + e];
+      if (ci0 < 0) { cs0 = -INFINITY; ci0 = 0x7FFFFFFF; }
+    }
+    if (lane + 64 < ncand) {
+      const int w = (lane + 64) / a.k, e = (lane + 64) % a.k;
+      cs1 = lst_s[(w * kSmQ + qi) * kSmTopMax + e];
+      ci1 = lst_i[(w * kSmQ + qi) * kSmTopMax + e];
+      if (ci1 < 0) { cs1 = -INFINITY; ci1 = 0x7FFFFFFF; }
+    }
+    for (int r = 0; r < a.k; ++r) {
+      float bs;
+      int bi;
+      if (cs1 > cs0 || (cs1 == cs0 && ci1 < ci0)) { bs = cs1; bi = ci1; } else { bs = cs0; bi = ci0; }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float os = __shfl_xor(bs, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (os > bs || (os == bs && oi < bi)) {
+          bs = os;
+          bi = oi;
+        }
+      }
+      if (lane == 0) {
+        const size_t cdx = (size_t(q0 + qi) * a.slices + slice) * a.k + r;
+        a.cand_s[cdx] = bs;
+        a.cand_i[cdx] = bi == 0x7FFFFFFF ? -1 : bi;
+      }
+      // remove the taken entry
+      if (ci0 == bi && cs0 == bs) { cs0 = -INFINITY; ci0 = 0x7FFFFFFF; }
+      if (ci1 == bi && cs1 == bs) { cs1 = -INFINITY; ci1 = 0x7FFFFFFF; }
+    }
+  }
+#else
+  (void)a;
+#endif
+}
+
 // ------------------------------------------------------------------ host-side helpers
 tq_status launch_status() {
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EDEVICE;
@@ -2243,6 +2486,43 @@ tq_status tq_search_topk(const tq_cache_desc *db, const void *codec_dev, const v
   hipLaunchKernelGGL(k_qprep_pack, dim3(nq), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s,
                      static_cast<const void *>(queries), int(TQ_F32), d, m, 0, 0.0f, cp, qp, qstride,
                      nq, 1, static_cast<uint8_t *>(nullptr));
+  // MFMA path: 3-bit codes with m = d, whole 128-coordinate groups, k <= 16.  The codec's
+  // codebooks are exactly symmetric by construction.
+  const bool mfma = db->bits_k == 3 && m == d && d % 128 == 0 && d <= 2048 && k <= kSmTopMax;
+  if (n_db > 0 && mfma) {
+    const int qgroups = (nq + kSmQ - 1) / kSmQ;
+    // about one block per CU (256 on MI355X), at most one slice per 256-vector tile of the
+    // workspace's candidate layout
+    int slices = std::max(1, 256 / qgroups);
+    slices = std::min(slices, ntiles);
+    int per = (n_db + slices - 1) / slices;
+    per = (per + 31) / 32 * 32;
+    slices = (n_db + per - 1) / per;
+    SearchMfmaArgs sa;
+    const CachePtrs ch = cache_ptrs(const_cast<void *>(db_cache), *db);
+    sa.kbits = ch.kbits;
+    sa.knorm = ch.knorm;
+    sa.ck = cp.ck;
+    sa.qp = qp;
+    sa.cand_s = cand_s;
+    sa.cand_i = cand_i;
+    sa.kbytes = ch.kbytes;
+    sa.d = d;
+    sa.n_db = n_db;
+    sa.nq = nq;
+    sa.k = k;
+    sa.slices = slices;
+    sa.per = per;
+    sa.qstride = qstride;
+    sa.qjl_scale = cp.qjl_scale;
+    const size_t shm = size_t(d / 32) * 2048 + size_t(kSmWaves) * kSmQ * kSmTopMax * 8;
+    if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_search_mfma),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess)
+      return TQ_EDEVICE;
+    hipLaunchKernelGGL(k_search_mfma, dim3(qgroups, slices), dim3(512), shm, s, sa);
+    hipLaunchKernelGGL(k_search_merge, dim3(nq), dim3(256), 0, s, cand_s, cand_i, slices, k, idx_out, score_out);
+    return launch_status();
+  }
   if (n_db > 0) {
     SearchArgs a;
     const CachePtrs ch = cache_ptrs(const_cast<void *>(db_cache), *db);

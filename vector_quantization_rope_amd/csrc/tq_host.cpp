@@ -227,6 +227,13 @@ void lloyd_max(int d, int bits, double *c, double *t) {
     }
     if (delta / s < 1e-13) break;
   }
+  // the density is even, so the optimum is odd: c[K-1-k] = -c[k].  Make that exact (the
+  // iterate differs from it only by rounding); the search kernel relies on it.
+  for (int k = 0; k < K / 2; ++k) {
+    const double v = 0.5 * (c[K - 1 - k] - c[k]);
+    c[k] = -v;
+    c[K - 1 - k] = v;
+  }
   for (int k = 0; k + 1 < K; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
 }
 
