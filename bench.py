@@ -12,10 +12,11 @@ throughput in GB/s of algorithmic packed-cache bytes (52 B key + 50 B value per 
 per kv-head) over the whole decode call.  Extra fields give the append throughput
 (Mtokens/s, a token being one position of one sequence with all its kv-heads, K and V),
 the roofline of the dominant kernel (split-K decode; its duration comes from HIP
-events the library records around that kernel), and the CPU oracle timed on a bounded
-sample on this host.
+events the library records around that kernel), the CPU oracle timed on a bounded
+sample on this host, and -- outside the timed steps -- the vector-search workload
+(10^6 x 1536 database build, search of 1024 queries, recall@10).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-search]
 """
 from __future__ import annotations
 
@@ -141,12 +142,56 @@ def cpu_baseline(w, K, V, q, units_total: int, n_units: int = 8):
     }
 
 
+def search_bench(tq, W, dev, ev, stream):
+    """Vector search workload (10^6 x 1536 database, 1024 queries, 3-bit + QJL m = 1536,
+    top-10): database build and search times from HIP events, recall against exact fp32
+    inner products.  Reported beside the decode line, outside its timed region."""
+    import torch
+
+    w = W.VECTOR_SEARCH
+    db, qs = W.gen_search(w, device=dev)
+    codec = tq.Codec(w.d, w.bits, 0, w.m, seed=0, device=dev)
+    cache = tq.PackedCache(1, 1, w.d, w.n_db, w.bits, 0, w.m, device=dev)
+    idx = torch.empty((w.nq, w.k), dtype=torch.int32, device=dev)
+    val = torch.empty((w.nq, w.k), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.search_workspace_bytes(cache.desc, w.n_db, w.nq, w.k), dtype=torch.uint8, device=dev)
+    e = [ev.create() for _ in range(4)]
+    build_ms, search_ms = [], []
+    for _ in range(3):
+        ev.record(e[0], stream)
+        tq.quantize_kv(cache.desc, codec.dev, cache.buf, db[None, None], None, 0, 0.0)
+        ev.record(e[1], stream)
+        tq.search_topk(cache.desc, codec.dev, cache.buf, w.n_db, qs, w.k, idx, val, ws)
+        ev.record(e[2], stream)
+        build_ms.append(ev.elapsed_ms(e[0], e[1]))
+        search_ms.append(ev.elapsed_ms(e[1], e[2]))
+    torch.cuda.synchronize()
+    exact = []
+    for s0 in range(0, w.nq, 128):
+        exact.append(torch.topk(qs[s0:s0 + 128] @ db.T, w.k, dim=1).indices)
+    exact = torch.cat(exact).cpu()
+    got = idx.cpu().long()
+    hit = sum(len(set(got[i].tolist()) & set(exact[i].tolist())) for i in range(w.nq))
+    top1 = sum(int(exact[i, 0].item() in set(got[i].tolist())) for i in range(w.nq))
+    bm, sm = min(build_ms[1:]), min(search_ms[1:])
+    pairs = w.nq * w.n_db
+    return {
+        "workload": (f"vector_search: {w.n_db} database vectors of dim {w.d}, fp32 N(0,1) unit rows, "
+                     f"3-bit codes + QJL m={w.m}, {w.nq} unit queries, top-{w.k}"),
+        "db_build_ms": round(bm, 3), "db_build_mvec_s": round(w.n_db / bm / 1e3, 3),
+        "search_ms": round(sm, 3), "search_gpairs_s": round(pairs / sm / 1e6, 3),
+        "search_equiv_tflops": round(pairs * 2 * (w.d + w.m) / sm / 1e9, 2),
+        "recall_at_10": round(hit / (w.nq * w.k), 4), "recall_1_at_10": round(top1 / w.nq, 4),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-search", action="store_true", help="skip the vector-search measurement")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run a plain device copy of this many MiB (for counter scaling)")
     args = ap.parse_args()
@@ -233,6 +278,12 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] copy calibration: elementwise neg over {n} bytes, 3 launches")
 
+    search = None
+    if not args.no_search:
+        log("[bench] vector search workload ...")
+        search = search_bench(tq, W, dev, ev, stream)
+        log(f"[bench] search {search}")
+
     base = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
@@ -276,6 +327,7 @@ def main():
             "avg_launch_us": round(mean(kern_ms) * 1e3, 2),
         },
         "cpu_baseline": base,
+        "search": search,
     }
     print(json.dumps(rec), flush=True)
 
