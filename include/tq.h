@@ -77,7 +77,9 @@ const char *tq_status_str(tq_status s);
  * host.  The codec stores each centroid rounded to fp16; `centroids` (2^bits values,
  * ascending) receives those stored values and `bounds` (2^bits - 1 values) the exact
  * midpoints between consecutive stored centroids, which are the encoder's decision
- * boundaries.  Supported: 8 <= d <= 4096, 1 <= bits <= 4.  Host only, synchronous. */
+ * boundaries.  The density is even, so the codebook is made exactly odd after the fp64
+ * iteration: c[2^bits - 1 - k] = -c[k].  Supported: 8 <= d <= 4096, 1 <= bits <= 4.
+ * Host only, synchronous. */
 tq_status tq_make_codebook(int32_t d, int32_t bits, float *centroids, float *bounds);
 
 /* Same computation, returning the fp64 Lloyd-Max centroids and boundaries before the
@@ -125,7 +127,8 @@ tq_status tq_cache_init(const tq_cache_desc *desc, void *cache_dev, tq_stream_t 
  *           [(S r)_i >= 0]; stored: planes, sign bits, fp16 n, fp16 ||r||.
  *   values: y = Pi v (no RoPE), codes with the value codebook, fp16 n.
  * k, v: device arrays [batch][kv_heads][n_new][d] of `dtype`, contiguous; v must be NULL
- * iff desc->bits_v == 0.  n_new == 0 is a no-op.  Writes never touch other slots. */
+ * iff desc->bits_v == 0; both must be 16-byte aligned (TQ_EINVAL otherwise).
+ * n_new == 0 is a no-op.  Writes never touch other slots. */
 tq_status tq_quantize_kv(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
                          const void *k, const void *v, tq_dtype dtype, int32_t start_pos,
                          int32_t n_new, float rope_base, tq_stream_t stream);
@@ -190,7 +193,10 @@ size_t tq_search_workspace_bytes(const tq_cache_desc *db, int32_t n_db, int32_t 
  * estimator as in tq_decode_attend (with q_rot = Pi q, no RoPE).  idx_out (device int32
  * [nq][k]) and score_out (device fp32 [nq][k]) receive the k best in descending score,
  * equal scores ordered by lower index; if k > n_db the tail is idx -1, score -inf.
- * 1 <= k <= 64. */
+ * 1 <= k <= 64.  With 3-bit codes, m == d, d a multiple of 128 up to 2048 and k <= 16
+ * the code term runs on int8 matrix cores (each centroid of the odd codebook is a sum
+ * of four +-1 terms of its code bits, and the query is a 32-bit fixed point in four
+ * int8 digits); other shapes use an fp32 path.  Both carry fp32-level accuracy. */
 tq_status tq_search_topk(const tq_cache_desc *db, const void *codec_dev, const void *db_cache,
                          int32_t n_db, const float *queries, int32_t nq, int32_t k,
                          int32_t *idx_out, float *score_out, void *ws, size_t ws_bytes,
