@@ -1009,10 +1009,13 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_split(DecodeArgs a) {
 //   score = n (c0 sum q + (c1-c0) q.b0 + (c2-c0) q.b1) + ||r|| sqrt(pi/2)/m (2 sq.s - sum sq).
 // The vectors (c1-c0) q and (c2-c0) q (one shared exponent) and sq = S q are written as
 // 32-bit fixed point in four signed int8 digits (rows digit * 8 + head of a 32-row A
-// operand), and the packed 0/1 bit planes of 32 tokens are the B operand of
-// v_mfma_i32_32x32x32_i8: the products are exact integers, both planes accumulate into one
-// sum, and the digit sums recombine in-lane.  32 bits keep every query element at its fp32
-// precision even when a few outlier coordinates set the exponent.
+// operand), and the packed bit planes of 32 tokens are the B operand of
+// v_mfma_i32_32x32x32_i8.  A B byte is one plane bit masked in place within its nibble,
+// b 2^e with e in 0..3 (no shifts per bit), and the query element it meets carries 2^-e
+// in its digits, which leaves it 29 to 32 bits.  The products are exact integers, both
+// planes accumulate into one sum, and the digit sums recombine in-lane.  That precision
+// keeps every query element near its fp32 value even when a few outlier coordinates set
+// the exponent.
 // Values: p n_v is split into fp16 hi + lo rows (16 rows for 8 heads) and multiplied on
 // v_mfma_f32_16x16x32_f16 with the fp16 centroids of 32 tokens, looked up 4 codes at a
 // time from a 4096-entry LDS table (the stored centroids are fp16 values, so this B is
@@ -1234,7 +1237,9 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
     const int digit = (i / (8 * nch)) % kDigits, v = i / (8 * kDigits * nch);
     const float *src = v == 2 ? sqs : qs;
     const float wgt = v == 0 ? dc1 : (v == 1 ? dc2 : 1.0f);
-    const int ex = sexp[v == 2 ? 1 : 0];
+    // the decode kernel keeps bit e of each nibble in place (token byte = b 2^e), so the
+    // query element that meets it carries the factor 2^-e
+    const int ex = sexp[v == 2 ? 1 : 0] - e;
     uint32_t word = 0u;
 #pragma unroll
     for (int beta = 0; beta < 4; ++beta) {
@@ -1265,10 +1270,9 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
 }
 
 // LDS-staged split-K decode.  Each wave streams its tiles through a ring of kRing LDS
-// slots filled by direct global->LDS loads (global_load_lds_dwordx3), two tiles ahead of
-// the one it computes, so the packed bytes in flight do not cost registers; the token
-// norms come one tile ahead in registers.  Per tile: int8 MFMA key scores, online
-// softmax, fp16 MFMA value accumulation, as in the register-fed kernel above.
+// slots filled by direct global->LDS loads, two tiles ahead of the one it computes, so the
+// packed bytes in flight do not cost registers.  Per tile: int8 MFMA key scores, online
+// softmax, fp16 MFMA value accumulation.
 constexpr int kRing = 3;
 
 // Reads of a ring slot written by direct global->LDS loads are inline assembly, each
@@ -1329,7 +1333,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
   __shared__ __align__(16) float coef_s[2][5][4];
   __shared__ float red_s[4][2][kMfmaMaxG];
 
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  // the wave index goes through readfirstlane so that everything derived from it (token
+  // ranges, tile addresses) is known to be wave-uniform and lives in scalar registers
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int unit = blockIdx.x, split = blockIdx.y;
   const int b = unit / a.kv_heads, g = unit % a.kv_heads;
   const int hq0 = g * a.G;
@@ -1375,7 +1381,13 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
   const int vq = lane >> 4, vn = lane & 15;
-  const int vidx = (24 * vq) >> 5, vsh = (24 * vq) & 31;
+  // A lane's 8 tokens of a coordinate are bits [24 vq, 24 vq + 24) of the coordinate's 96
+  // bits.  The lane reads the dword pair holding them and funnel-shifts it so that the two
+  // 12-bit LUT indices come out already scaled by the 8-byte entry size: by 24 vq - 3 bits
+  // from dword vidx, or for vq = 0 by 29 bits from the pair that starts one dword earlier
+  // (the 3 bits shifted in from below are masked off).
+  const int vidx = vq == 0 ? -1 : (24 * vq) >> 5;
+  const uint32_t vsh = vq == 0 ? 29u : uint32_t(((24 * vq) & 31) - 3);
   const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.vcodes) + size_t(unit) * a.tiles * Gm::VT;
   const uint8_t *vnbase = reinterpret_cast<const uint8_t *>(a.vnorm);
 
@@ -1516,32 +1528,33 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
     }
     // value B operands: 8 tokens' fp16 centroids of coordinate 16 nt + vn, two LUT lookups
     v8h Bv[NT];
+    const uint8_t *lutb = reinterpret_cast<const uint8_t *>(lut);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const uint32_t lo = vwr[nt][0];
-      const uint32_t hi = vidx < 2 ? vwr[nt][1] : 0u;
-      const uint32_t x = uint32_t(((uint64_t(hi) << 32) | lo) >> vsh);
-      const uint2 e0 = lut[x & 0xFFFu], e1 = lut[(x >> 12) & 0xFFFu];
+      const uint32_t y = __builtin_amdgcn_alignbit(vwr[nt][1], vwr[nt][0], vsh);   // 8 x (low bits junk)
+      const uint2 e0 = *reinterpret_cast<const uint2 *>(lutb + (y & 0x7FF8u));
+      const uint2 e1 = *reinterpret_cast<const uint2 *>(lutb + ((y >> 12) & 0x7FF8u));
       v4i bw = {int(e0.x), int(e0.y), int(e1.x), int(e1.y)};
       __builtin_memcpy(&Bv[nt], &bw, 16);
     }
     // ---- key scores on int8 MFMA: both code planes accumulate into s01 (their digit rows
     // carry the plane weights), the sign bits into s2.  The B bytes of coordinate-chunk c
-    // are bits 4 (c & 1) + e, + 8, + 16, + 24 of the lane's plane dword for c / 2; one 64-bit
-    // shift serves the chunks c and c + 2.
+    // are bit e of the low (c even) or high (c odd) nibble of each byte of the lane's plane
+    // dword for c / 2, masked in place: byte value b 2^e, the 2^-e being in the query digits.
     v16i s01 = {}, s2 = {};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       v4i b0, b1, b2;
+      const uint32_t w0 = (c >> 1) ? kw[0].y : kw[0].x;
+      const uint32_t w1 = (c >> 1) ? kw[1].y : kw[1].x;
+      const uint32_t w2 = (c >> 1) ? kw[2].y : kw[2].x;
+      const uint32_t n0 = (c & 1) ? w0 >> 4 : w0, n1 = (c & 1) ? w1 >> 4 : w1;
+      const uint32_t n2 = (c & 1) ? w2 >> 4 : w2;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int sh = 4 * (c & 1) + e;
-        const uint64_t u0 = ((uint64_t(kw[0].y) << 32) | kw[0].x) >> sh;
-        const uint64_t u1 = ((uint64_t(kw[1].y) << 32) | kw[1].x) >> sh;
-        const uint64_t u2 = ((uint64_t(kw[2].y) << 32) | kw[2].x) >> sh;
-        b0[e] = int(uint32_t((c >> 1) ? (u0 >> 32) : u0) & 0x01010101u);
-        b1[e] = int(uint32_t((c >> 1) ? (u1 >> 32) : u1) & 0x01010101u);
-        b2[e] = int(uint32_t((c >> 1) ? (u2 >> 32) : u2) & 0x01010101u);
+        b0[e] = int(n0 & (0x01010101u << e));
+        b1[e] = int(n1 & (0x01010101u << e));
+        b2[e] = int(n2 & (0x01010101u << e));
       }
       s01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq0[c], b0, s01, 0, 0, 0);
       s01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq1[c], b1, s01, 0, 0, 0);
