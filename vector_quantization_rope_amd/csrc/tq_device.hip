@@ -1043,7 +1043,7 @@ struct MfmaArgs {
   float *part;
   float *scores;
   int kbytes, tiles, capacity, length, chunk, splits, kv_heads, q_heads, G;
-  float scale_log2;
+  float scale_log2, inv_scale_log2;
 };
 
 __device__ __forceinline__ uint32_t f16bits(float x) {
@@ -1270,10 +1270,13 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
 }
 
 // LDS-staged split-K decode.  Each wave streams its tiles through a ring of kRing LDS
-// slots filled by direct global->LDS loads, two tiles ahead of the one it computes, so the
-// packed bytes in flight do not cost registers.  Per tile: int8 MFMA key scores, online
-// softmax, fp16 MFMA value accumulation.
+// slots filled by direct global->LDS loads, kRing - 1 tiles ahead of the one it computes,
+// so the packed bytes in flight do not cost registers.  Per tile: int8 MFMA key scores,
+// online softmax, fp16 MFMA value accumulation.  Blocks of kDecWaves waves,
+// kDecBlocksPerCU of them resident per CU.
 constexpr int kRing = 3;
+constexpr int kDecWaves = 8;
+constexpr int kDecBlocksPerCU = 1;
 
 // Reads of a ring slot written by direct global->LDS loads are inline assembly, each
 // block waiting for its own results (lgkmcnt(0)), because the compiler would otherwise
@@ -1296,14 +1299,12 @@ struct LdsGeom {
   static constexpr int SLOT = VN + 80;
 };
 
-__device__ __forceinline__ void wait_vmcnt_le(int n) {
-  // s_waitcnt with vmcnt = n and expcnt / lgkmcnt left at their "no wait" maxima (gfx9
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  // s_waitcnt with vmcnt = N and expcnt / lgkmcnt left at their "no wait" maxima (gfx9
   // encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14])
-  switch (n) {
-    case 8: __builtin_amdgcn_s_waitcnt(8 | (7 << 4) | (15 << 8)); break;
-    case 12: __builtin_amdgcn_s_waitcnt(12 | (7 << 4) | (15 << 8)); break;
-    default: __builtin_amdgcn_s_waitcnt(0); break;
-  }
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // a where mask bits are set, else b (a bitwise select: the compiler keeps it a v_bfi
@@ -1317,21 +1318,18 @@ __device__ __forceinline__ void wait_lgkm0() {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
+__global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(MfmaArgs a) {
   // The body is device code only (its local lambdas call device builtins); the host pass
   // needs nothing but the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
   using Gm = LdsGeom<D>;
-  constexpr int NCH = D / 32, NT = D / 16;
-  // one LDS array per ring slot: the loads in flight into the other slots are distinct
-  // memory from the slot being read
-  __shared__ __align__(16) uint8_t ring0[4][Gm::SLOT];
-  __shared__ __align__(16) uint8_t ring1[4][Gm::SLOT];
-  __shared__ __align__(16) uint8_t ring2[4][Gm::SLOT];
+  constexpr int NCH = D / 32, NT = D / 16, NW = kDecWaves, NTH = 64 * NW, R = kRing;
+  __shared__ __align__(16) uint8_t ring[R][NW][Gm::SLOT];
   __shared__ uint2 lut[4096];
-  __shared__ __align__(16) _Float16 pt_s[4][16][40];
+  __shared__ __align__(16) _Float16 pt_s[NW][16][40];
   __shared__ __align__(16) float coef_s[2][5][4];
-  __shared__ float red_s[4][2][kMfmaMaxG];
+  __shared__ float red_s[NW][2][kMfmaMaxG];
+  static_assert(NW * 16 * D * 4 <= int(sizeof(ring)), "the waves' accumulators fit in the ring for the merge");
 
   // the wave index goes through readfirstlane so that everything derived from it (token
   // ranges, tile addresses) is known to be wave-uniform and lives in scalar registers
@@ -1339,7 +1337,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
   const int unit = blockIdx.x, split = blockIdx.y;
   const int b = unit / a.kv_heads, g = unit % a.kv_heads;
   const int hq0 = g * a.G;
-  for (int i = tid; i < 4096; i += 256) {
+  for (int i = tid; i < 4096; i += NTH) {
     const uint32_t h0 = f16bits(a.cv[i & 7]), h1 = f16bits(a.cv[(i >> 3) & 7]);
     const uint32_t h2 = f16bits(a.cv[(i >> 6) & 7]), h3 = f16bits(a.cv[(i >> 9) & 7]);
     lut[i] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
@@ -1347,8 +1345,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
   const uint8_t *qpk = a.qpack + size_t(unit) * qpack_unit_bytes(D);
   const float *coef = reinterpret_cast<const float *>(qpk + size_t(kQpackVecs) * 32 * 2 * NCH * 16);
   if (tid < 40) {
+    // the coefficients carry the softmax scale (log2 domain): the loop forms scale * score
     const int hf = tid / 20, k = (tid / 4) % 5, r = tid % 4;
-    coef_s[hf][k][r] = coef[(4 * hf + r) * kQpackCoef + k];
+    coef_s[hf][k][r] = coef[(4 * hf + r) * kQpackCoef + k] * a.scale_log2;
   }
   const int row = lane & 31, half = lane >> 5;
   // int8 digit rows: plane 0 weight (c1 - c0) q, plane 1 weight (c2 - c0) q, S q
@@ -1368,7 +1367,8 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
   const int t_end = min(a.length, t_begin + a.chunk);
   const size_t ubase = size_t(unit) * a.capacity;
   const int t_first = t_begin + 32 * wv;
-  const int nk = t_end > t_first ? (t_end - t_first + 127) / 128 : 0;
+  constexpr int TS = 32 * NW;   // tokens between a wave's consecutive tiles
+  const int nk = t_end > t_first ? (t_end - t_first + TS - 1) / TS : 0;
   float M[kMfmaMaxG], Mh[4], lsum[4];   // Mh: the running maxima of this lane's 4 heads
   const uint32_t hmask = half ? 0xFFFFFFFFu : 0u;
 #pragma unroll
@@ -1391,7 +1391,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
   const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.vcodes) + size_t(unit) * a.tiles * Gm::VT;
   const uint8_t *vnbase = reinterpret_cast<const uint8_t *>(a.vnorm);
 
-  // Tile k of this wave starts at t_first + 128 k.  Every chunk a lane loads stays inside
+  // Tile k of this wave starts at t_first + TS k.  Every chunk a lane loads stays inside
   // the tokens [t0, t_end); tiles past the end reload the last one into a slot that is
   // never read, so every step issues the same Gm::NDMA loads.
   // Each load is a uniform base (per tile, in SGPRs) plus a 32-bit per-lane byte offset;
@@ -1401,7 +1401,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
   for (int i = 0; i < Gm::NK; ++i) koff[i] = uint32_t(Gm::KCH * (64 * i + lane));
   auto issue_dma = [&](int k, uint8_t *slot) {
     const int kk = k < nk ? k : nk - 1;
-    const int t0 = t_first + 128 * kk;
+    const int t0 = t_first + TS * kk;
     const int nv = t_end - t0;   // valid tokens in the tile (1..32)
     const bool whole = nv >= 32;   // wave-uniform: no clamping needed
     const uint8_t *ksrc = a.kbits + (ubase + t0) * Gm::KB;
@@ -1436,14 +1436,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
     }
   };
 
-  auto step = [&](int k, const uint8_t *slot, uint8_t *nxt2) {
+  auto step = [&](int k, const uint8_t *slot, uint8_t *nxt) {
     wait_lgkm0();                 // reads of the slot refilled below are complete
-    issue_dma(k + 2, nxt2);
+    issue_dma(k + R - 1, nxt);
     if (a.scores)
       __builtin_amdgcn_s_waitcnt(0);
     else
-      wait_vmcnt_le(2 * Gm::NDMA);   // this tile's loads are the oldest still counted
-    const int t0 = t_first + 128 * k;
+      wait_vmcnt_le<(R - 1) * Gm::NDMA>();   // this tile's loads are the oldest still counted
+    const int t0 = t_first + TS * k;
     const int t = t0 + row;
     const bool valid = t < t_end;
     const uint32_t sbase = uint32_t(reinterpret_cast<uintptr_t>(slot));
@@ -1568,31 +1568,36 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
     const float4 k4 = *reinterpret_cast<const float4 *>(coef_s[half][4]);
     const float K0[4] = {k0.x, k0.y, k0.z, k0.w}, K1[4] = {k1.x, k1.y, k1.z, k1.w};
     const float K3[4] = {k3.x, k3.y, k3.z, k3.w}, K4[4] = {k4.x, k4.y, k4.z, k4.w};
-    float lam[4], sc[4];
+    // lam = scale * score in the log2 domain; a token past the end gets -inf through the
+    // innermost fma.  Heads h >= G (zero coefficients and digits) get lam = 0: their rows
+    // are carried along and never written out.
+    const float vbias = valid ? 0.0f : -INFINITY;
+    float lam[4], rel[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       // digit sums: rows 8 digit + head are accumulator registers 4 digit + r
       const float S01 = fmaf(float(s01[r] + 256 * s01[4 + r]), 0x1p-16f, float(s01[8 + r] + 256 * s01[12 + r]));
       const float S2 = fmaf(float(s2[r] + 256 * s2[4 + r]), 0x1p-16f, float(s2[8 + r] + 256 * s2[12 + r]));
-      sc[r] = n16 * (K0[r] + K1[r] * S01) + rn16 * (K3[r] * S2 - K4[r]);
-      lam[r] = (valid && 4 * half + r < a.G) ? sc[r] * a.scale_log2 : -INFINITY;
+      lam[r] = fmaf(n16, fmaf(K1[r], S01, K0[r]), fmaf(rn16, fmaf(K3[r], S2, -K4[r]), vbias));
+      rel[r] = lam[r] - Mh[r];
     }
     if (a.scores) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * half + r;
-        if (valid && h < a.G) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.length + t] = sc[r];
+        if (valid && h < a.G) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.length + t] = lam[r] * a.inv_scale_log2;
       }
     }
     // ---- online softmax (log2 domain); tile maxima and running maxima are wave-uniform.
     // The running maxima are raised (and the accumulators rescaled) only when a score
     // exceeds its head's maximum by more than 8, so p = 2^(lam - M) <= 256 between raises;
     // a token whose value norm is 255 or more allows no slack, which keeps p * n_v within
-    // fp16 range (256 * 255 < 65504) for the hi/lo split below.
+    // fp16 range (256 * 255 < 65504) for the hi/lo split below.  In the first tile the
+    // maxima are -inf, so every valid token is above them.
     const float slack = vnorm < 255.0f ? 8.0f : 0.0f;
     uint64_t above = 0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) above |= __builtin_amdgcn_ballot_w64(lam[r] - slack > Mh[r]);
+    for (int r = 0; r < 4; ++r) above |= __builtin_amdgcn_ballot_w64(rel[r] > slack);
     if (above != 0) {
       float tm[kMfmaMaxG];
 #pragma unroll
@@ -1616,13 +1621,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
         for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= al;
         lsum[r] *= half ? alpha[4 + r] : alpha[r];
         Mh[r] = pick_bits(hmask, M[4 + r], M[r]);
+        rel[r] = lam[r] - Mh[r];
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 4 * half + r;
-      // lam = -inf (absent token) gives p = 0: Mh is finite after the first tile
-      const float p = __builtin_amdgcn_exp2f(lam[r] - Mh[r]);
+      // lam = -inf (token past the end) gives p = 0: Mh is finite after the first tile
+      const float p = __builtin_amdgcn_exp2f(rel[r]);
       lsum[r] += p;
       const float pv = p * vnorm;
       const _Float16 hi = (_Float16)pv;
@@ -1638,13 +1644,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
   };
 
   if (nk > 0) {
-    uint8_t *r0 = &ring0[wv][0], *r1 = &ring1[wv][0], *r2 = &ring2[wv][0];
-    issue_dma(0, r0);
-    issue_dma(1, r1);
-    for (int k = 0; k < nk; k += kRing) {
-      step(k, r0, r2);
-      if (k + 1 < nk) step(k + 1, r1, r0);
-      if (k + 2 < nk) step(k + 2, r2, r1);
+#pragma unroll
+    for (int k = 0; k < R - 1; ++k) issue_dma(k, &ring[k][wv][0]);
+    for (int k = 0; k < nk; k += R) {
+#pragma unroll
+      for (int sl = 0; sl < R; ++sl)
+        if (k + sl < nk) step(k + sl, &ring[sl][wv][0], &ring[(sl + R - 1) % R][wv][0]);
     }
     __builtin_amdgcn_s_waitcnt(0);   // drain the tail loads before the slots are reused
   }
@@ -1652,7 +1657,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) lsum[r] = sum32(lsum[r]);
   __syncthreads();
-  float *acc_s = reinterpret_cast<float *>(lut);   // [4 waves][16 rows][D]
+  float *acc_s = reinterpret_cast<float *>(&ring[0][0][0]);   // [NW waves][16 rows][D]
   if (lane == 0 || lane == 32) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) red_s[wv][1][4 * half + r] = lsum[r];
@@ -1666,14 +1671,14 @@ __global__ __launch_bounds__(256, 2) void k_decode_lds(MfmaArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc_s[(wv * 16 + 4 * vq + r) * D + 16 * nt + vn] = acc[nt][r];
   __syncthreads();
-  for (int i = tid; i < a.G * D; i += 256) {
+  for (int i = tid; i < a.G * D; i += NTH) {
     const int h = i / D, j = i % D;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) mx = fmaxf(mx, red_s[w][0][h]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red_s[w][0][h]);
     float v = 0.0f, L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = red_s[w][0][h];
       if (mw == -INFINITY) continue;
       const float f = exp2f(mw - mx);
@@ -2184,9 +2189,9 @@ bool decode_mfma_path(const tq_cache_desc &c, int q_heads) {
          q_heads / c.kv_heads <= kMfmaMaxG;
 }
 
-constexpr int kMfmaChunk = 128;   // tokens per block iteration (4 waves x 32)
+constexpr int kMfmaChunk = 32 * kDecWaves;   // tokens per block iteration (one tile per wave)
 
-constexpr int kDecodeBlocks = 512;
+constexpr int kDecodeBlocks = 256 * kDecBlocksPerCU;   // MI355X: 256 CUs
 
 int default_splits(const tq_cache_desc &c, int length) {
   if (length <= 0) return 1;
@@ -2201,7 +2206,8 @@ int default_splits(const tq_cache_desc &c, int length) {
   return s;
 }
 
-// Tokens per split: a multiple of 128 so that every block works on whole 32-token tiles.
+// Tokens per split: a multiple of kMfmaChunk, so that every wave of a block gets the same
+// number of whole 32-token tiles.
 int split_chunk(int length, int splits) {
   const int per = (length + splits - 1) / splits;
   return (per + kMfmaChunk - 1) / kMfmaChunk * kMfmaChunk;
@@ -2400,12 +2406,13 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
     ma.q_heads = q_heads;
     ma.G = G;
     ma.scale_log2 = sc * 1.4426950408889634f;
+    ma.inv_scale_log2 = 1.0f / ma.scale_log2;
     dim3 grid(units, used_splits);
     if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
     if (d == 64)
-      hipLaunchKernelGGL(k_decode_lds<64>, grid, dim3(256), 0, s, ma);
+      hipLaunchKernelGGL(k_decode_lds<64>, grid, dim3(64 * kDecWaves), 0, s, ma);
     else
-      hipLaunchKernelGGL(k_decode_lds<128>, grid, dim3(256), 0, s, ma);
+      hipLaunchKernelGGL(k_decode_lds<128>, grid, dim3(64 * kDecWaves), 0, s, ma);
     if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
   } else {
     DecodeArgs a;
