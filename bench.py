@@ -16,7 +16,7 @@ events the library records around that kernel), the CPU oracle timed on a bounde
 sample on this host, and -- outside the timed steps -- the vector-search workload
 (10^6 x 1536 database build, search of 1024 queries, recall@10).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline] [--no-search]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--spinup-ms 300] [--no-cpu-baseline] [--no-search]
 """
 from __future__ import annotations
 
@@ -78,6 +78,13 @@ class HipEvents:
         if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
             raise RuntimeError("hipEventElapsedTime failed")
         return float(ms.value)
+
+
+def pct_us(ms):
+    """p10, median and p90 of a list of durations in ms, in microseconds."""
+    v = sorted(ms)
+    at = lambda f: v[min(len(v) - 1, int(f * (len(v) - 1) + 0.5))] * 1e3
+    return [round(at(0.1), 2), round(at(0.5), 2), round(at(0.9), 2)]
 
 
 def kernel_source_hash() -> str:
@@ -188,12 +195,17 @@ def search_bench(tq, W, dev, ev, stream):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--spinup-ms", type=float, default=300.0,
+                    help="untimed steps run for this long before the warmup steps, so that the "
+                         "timed steps see the GPU at its sustained clock (it ramps up over the "
+                         "first tens of milliseconds of load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true", help="skip the vector-search measurement")
-    ap.add_argument("--copy-calibration", type=int, default=0,
-                    help="also run a plain device copy of this many MiB (for counter scaling)")
+    ap.add_argument("--copy-calibration", type=int, default=1024,
+                    help="size in MiB of the plain streaming copy that is timed (measured HBM "
+                         "bandwidth) and whose counters scale the decode kernel's (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the packed-KV path runs on a single device and this "
@@ -242,6 +254,15 @@ def main():
                          events=(E["k0"][i], E["k1"][i]))
         ev.record(E["d1"][i], stream)
 
+    t_spin = time.perf_counter()
+    spin = 0
+    while (time.perf_counter() - t_spin) * 1e3 < args.spinup_ms:
+        step()
+        spin += 1
+        if spin % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    log(f"[bench] spin-up: {spin} untimed steps in {(time.perf_counter() - t_spin) * 1e3:.0f} ms")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -267,16 +288,24 @@ def main():
         f"{mean(kern_ms)*1e3:.1f} us ({kern_gbs:.0f} GB/s), append {mean(append_ms)*1e3:.1f} us "
         f"({append_mtok:.1f} Mtokens/s, {append_bytes/(mean(append_ms)*1e-3)/1e9:.0f} GB/s)")
 
+    stream_gbs = None
     if args.copy_calibration:
-        # a plain streaming kernel of known traffic (reads n bytes, writes n bytes), whose
-        # FETCH_SIZE / WRITE_SIZE readings scale the counters of the decode kernel
+        # a plain streaming kernel of known traffic (reads n bytes, writes n bytes): its time
+        # gives the HBM bandwidth this machine sustains, and its FETCH_SIZE / WRITE_SIZE readings
+        # scale the counters of the decode kernel
         n = args.copy_calibration << 20
         src = torch.ones(n // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        ec = [ev.create() for _ in range(4)]
+        ev.record(ec[0], stream)
         for _ in range(3):
             torch.neg(src, out=dst)
+        ev.record(ec[1], stream)
         torch.cuda.synchronize()
-        log(f"[bench] copy calibration: elementwise neg over {n} bytes, 3 launches")
+        stream_gbs = 2 * n * 3 / (ev.elapsed_ms(ec[0], ec[1]) * 1e-3) / 1e9
+        del src, dst
+        log(f"[bench] streaming copy (elementwise neg, {n} bytes in + out): {stream_gbs:.0f} GB/s")
 
     search = None
     if not args.no_search:
@@ -312,7 +341,9 @@ def main():
         },
         "hbm_frac": round(dec_gbs / HBM_PEAK_GBS, 4),
         "decode_us": round(mean(dec_ms) * 1e3, 2),
+        "decode_us_p10_p50_p90": pct_us(dec_ms),
         "append_us": round(mean(append_ms) * 1e3, 2),
+        "append_us_p10_p50_p90": pct_us(append_ms),
         "quantize_mtokens_s": round(append_mtok, 2),
         "quantize_gbs": round(append_bytes / (mean(append_ms) * 1e-3) / 1e9, 2),
         "roofline": {
@@ -325,6 +356,8 @@ def main():
             "traffic": traffic_from_counters(dec_bytes),
             "algorithmic_bytes_per_launch": dec_bytes,
             "avg_launch_us": round(mean(kern_ms) * 1e3, 2),
+            "launch_us_p10_p50_p90": pct_us(kern_ms),
+            "measured_stream_copy_gbs": None if stream_gbs is None else round(stream_gbs, 1),
         },
         "cpu_baseline": base,
         "search": search,

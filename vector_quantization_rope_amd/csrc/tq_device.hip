@@ -11,7 +11,8 @@
 //                       online softmax, values (fp16 hi/lo against LUT-dequantized
 //                       centroids), accumulated in the rotated basis
 //   k_decode_split      the same on plain fp32 arithmetic for the other bit widths
-//   k_decode_merge      merge of the splits, normalisation, inverse rotation Pi^T
+//   k_decode_merge      merge of the splits, normalisation, inverse rotation Pi^T (a
+//                       one-wave-per-row form, k_decode_merge_wave, for d = 64 and 128)
 //   k_search_tile       packed database scores for a query tile + per-tile top-k
 //   k_search_merge      per-query top-k over the tile candidates
 
@@ -1085,92 +1086,17 @@ __device__ __forceinline__ float sum32(float v) {
   return v;
 }
 
-// Query preparation for the MFMA path, one block per (batch, q-head) row: q_rot =
-// Pi RoPE(q, q_pos) (LDS FWHT), sq = S q_rot, their sums (kept in the fp32 rows for the
-// plain path as well), then the head's three int8 digit rows of the key-score A operand
-// and its score coefficients.  The first head of each kv-head also clears the unused
-// rows (digit 3, heads >= G) of its unit.
-__global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, int d, int m,
-                                                    int q_pos, float rope_base, CodecPtrs cp,
-                                                    float *qrows, int qstride, int q_heads,
-                                                    int G, uint8_t *qpack) {
-  extern __shared__ float qs[];   // d floats (q_rot), m floats (sq), max(1024, m) partial sums
-  float *sqs = qs + d;
-  __shared__ float red[4][4];
-  __shared__ int sexp[2];
-  const int rowi = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int b = rowi / q_heads, hq = rowi % q_heads;
-  const int g = hq / G, h = hq % G;
-  const int kv_heads = q_heads / G;
-  const size_t base = size_t(rowi) * d;
-  const int hh = d / 2;
-  if (rope_base != 0.0f) {
-    for (int j = tid; j < hh; j += 256) {
-      const double theta = pow(double(rope_base), -2.0 * double(j) / double(d));
-      double s, c;
-      sincos(double(q_pos) * theta, &s, &c);
-      const float x0 = load_elem(q, base + j, dtype), x1 = load_elem(q, base + j + hh, dtype);
-      qs[j] = (x0 * float(c) - x1 * float(s)) * cp.D[j];
-      qs[j + hh] = (x0 * float(s) + x1 * float(c)) * cp.D[j + hh];
-    }
-  } else {
-    for (int j = tid; j < d; j += 256) qs[j] = load_elem(q, base + j, dtype) * cp.D[j];
-  }
-  __syncthreads();
-  const int B = cp.block;
-  for (int st = 1; st < B; st <<= 1) {
-    for (int k = tid; k < d / 2; k += 256) {
-      const int blk = k / (B / 2), kk = k % (B / 2);
-      const int i = blk * B + (kk / st) * 2 * st + (kk % st);
-      const float x0 = qs[i], x1 = qs[i + st];
-      qs[i] = x0 + x1;
-      qs[i + st] = x0 - x1;
-    }
-    __syncthreads();
-  }
-  for (int j = tid; j < d; j += 256) qs[j] *= cp.inv_sqrt_block;
-  __syncthreads();
-  // sq = S q_rot: each thread takes 4 consecutive outputs (a float4 of a row of S^T) over
-  // one of `slices` slices of the inner dimension; the slices are summed through LDS
-  if (m > 0) {
-    const int g4 = m / 4;
-    int slices = 1;                                 // largest power of two <= 256 / g4
-    while (2 * slices * g4 <= 256) slices *= 2;
-    const int jl = d / slices;
-    float *part = sqs + m;                          // [slices][m] (shared with the final sq)
-    for (int og = tid % g4 + (tid / g4 >= slices ? g4 : 0), sl = tid / g4; og < g4; og += 256) {
-      const int j0 = (slices > 1 ? sl : 0) * jl, j1 = slices > 1 ? j0 + jl : d;
-      float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-      const float4 *st = reinterpret_cast<const float4 *>(cp.ST) + og;
-#pragma unroll 8
-      for (int j = j0; j < j1; ++j) {
-        const float4 sv = st[size_t(j) * g4];
-        const float x = qs[j];
-        z.x = fmaf(sv.x, x, z.x);
-        z.y = fmaf(sv.y, x, z.y);
-        z.z = fmaf(sv.z, x, z.z);
-        z.w = fmaf(sv.w, x, z.w);
-      }
-      float *o4 = part + (slices > 1 ? sl : 0) * m + 4 * og;
-      o4[0] = z.x;
-      o4[1] = z.y;
-      o4[2] = z.z;
-      o4[3] = z.w;
-      if (slices > 1) break;
-    }
-    __syncthreads();
-    for (int i = tid; i < m; i += 256) {
-      float z = 0.0f;
-      for (int sl = 0; sl < slices; ++sl) z += part[sl * m + i];
-      sqs[i] = z;
-    }
-  }
-  __syncthreads();
+// Tail shared by the two query-prep kernels, run by all 256 threads once q_rot (qs) and
+// sq (sqs) are complete, thread i < d having written sqs[i] itself: the fp32 row, the
+// sums, the two fixed-point exponents, the score coefficients and the int8 digit rows.
+__device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, int d, int m,
+                                           const CodecPtrs &cp, float *o, float (*red)[4], int tid,
+                                           int lane, int wv, int b, int g, int h, int G,
+                                           int kv_heads, uint8_t *qpack) {
   // fp32 rows and sums; maxima for the fixed-point scaling (the two plane vectors
   // (c1 - c0) q and (c2 - c0) q share one exponent, set by the larger weight)
   const float dc1 = cp.ck[1] - cp.ck[0], dc2 = cp.ck[2] - cp.ck[0];
   const float wmax = fmaxf(fabsf(dc1), fabsf(dc2));
-  float *o = qrows + size_t(rowi) * qstride;
   float s0 = 0.0f, s1 = 0.0f, m0 = 0.0f, m1 = 0.0f;
   for (int j = tid; j < d; j += 256) {
     o[j] = qs[j];
@@ -1193,21 +1119,23 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
     red[3][wv] = m1;
   }
   __syncthreads();
+  // every thread derives the two fixed-point exponents from the wave maxima
+  int sexp[2];
+  for (int v = 0; v < 2; ++v) {
+    const float mx = fmaxf(fmaxf(red[2 + v][0], red[2 + v][1]), fmaxf(red[2 + v][2], red[2 + v][3]));
+    int e = 0;
+    if (mx > 0.0f) {
+      int ex;
+      frexpf(mx, &ex);   // mx < 2^ex
+      e = 30 - ex;   // |x| 2^e < 2^30: four signed int8 digits
+    }
+    sexp[v] = e;
+  }
   if (tid == 0) {
     const float S0 = red[0][0] + red[0][1] + red[0][2] + red[0][3];
     const float S1 = red[1][0] + red[1][1] + red[1][2] + red[1][3];
     o[d + m] = S0;
     o[d + m + 1] = S1;
-    for (int v = 0; v < 2; ++v) {
-      const float mx = fmaxf(fmaxf(red[2 + v][0], red[2 + v][1]), fmaxf(red[2 + v][2], red[2 + v][3]));
-      int e = 0;
-      if (mx > 0.0f) {
-        int ex;
-        frexpf(mx, &ex);   // mx < 2^ex
-        e = 30 - ex;   // |x| 2^e < 2^30: four signed int8 digits
-      }
-      sexp[v] = e;
-    }
     if (qpack) {
       float *coef = reinterpret_cast<float *>(qpack + size_t(b * kv_heads + g) * qpack_unit_bytes(d) +
                                               size_t(kQpackVecs) * 32 * 2 * (d / 32) * 16);
@@ -1226,7 +1154,6 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
           for (int i = 0; i < kQpackCoef; ++i) coef[hz * kQpackCoef + i] = 0.0f;
     }
   }
-  __syncthreads();
   if (!qpack) return;
   const int nch = d / 32;
   uint32_t *o32 = reinterpret_cast<uint32_t *>(qpack + size_t(b * kv_heads + g) * qpack_unit_bytes(d));
@@ -1267,6 +1194,200 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
       o32[(((v * 32 + row) * 2 + half) * nch + c) * 4 + e] = 0u;
     }
   }
+}
+
+// Query preparation for the MFMA path, one block per (batch, q-head) row: q_rot =
+// Pi RoPE(q, q_pos) (LDS FWHT), sq = S q_rot, their sums (kept in the fp32 rows for the
+// plain path as well), then the head's three int8 digit rows of the key-score A operand
+// and its score coefficients.  The first head of each kv-head also clears the unused
+// rows (digit 3, heads >= G) of its unit.
+__global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, int d, int m,
+                                                    int q_pos, float rope_base, CodecPtrs cp,
+                                                    float *qrows, int qstride, int q_heads,
+                                                    int G, uint8_t *qpack) {
+  extern __shared__ float qs[];   // d floats (q_rot), m floats (sq), max(1024, m) partial sums
+  float *sqs = qs + d;
+  __shared__ float red[4][4];
+  const int rowi = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = rowi / q_heads, hq = rowi % q_heads;
+  const int g = hq / G, h = hq % G;
+  const int kv_heads = q_heads / G;
+  const size_t base = size_t(rowi) * d;
+  const int hh = d / 2;
+  if (rope_base != 0.0f) {
+    for (int j = tid; j < hh; j += 256) {
+      const double theta = pow(double(rope_base), -2.0 * double(j) / double(d));
+      double s, c;
+      sincos(double(q_pos) * theta, &s, &c);
+      const float x0 = load_elem(q, base + j, dtype), x1 = load_elem(q, base + j + hh, dtype);
+      qs[j] = (x0 * float(c) - x1 * float(s)) * cp.D[j];
+      qs[j + hh] = (x0 * float(s) + x1 * float(c)) * cp.D[j + hh];
+    }
+  } else {
+    for (int j = tid; j < d; j += 256) qs[j] = load_elem(q, base + j, dtype) * cp.D[j];
+  }
+  __syncthreads();
+  const int B = cp.block;
+  if (B == d && d >= 64 && d <= 256) {
+    // one wave: d / 64 consecutive values per lane, the first stages in registers, the
+    // rest across lanes, and the 1/sqrt(B) scale on the way out
+    if (tid < 64) {
+      float x[4];
+      const int E = d / 64;
+      for (int e = 0; e < E; ++e) x[e] = qs[E * tid + e];
+      for (int st = 1; st < E; st <<= 1)
+        for (int e = 0; e < E; ++e)
+          if (!(e & st)) {
+            const float u = x[e], v = x[e + st];
+            x[e] = u + v;
+            x[e + st] = u - v;
+          }
+#pragma unroll
+      for (int msk = 1; msk < 64; msk <<= 1)
+        for (int e = 0; e < E; ++e) {
+          const float pv = __shfl_xor(x[e], msk, 64);
+          x[e] = (tid & msk) ? pv - x[e] : x[e] + pv;
+        }
+      for (int e = 0; e < E; ++e) qs[E * tid + e] = x[e] * cp.inv_sqrt_block;
+    }
+  } else {
+    for (int st = 1; st < B; st <<= 1) {
+      for (int k = tid; k < d / 2; k += 256) {
+        const int blk = k / (B / 2), kk = k % (B / 2);
+        const int i = blk * B + (kk / st) * 2 * st + (kk % st);
+        const float x0 = qs[i], x1 = qs[i + st];
+        qs[i] = x0 + x1;
+        qs[i + st] = x0 - x1;
+      }
+      __syncthreads();
+    }
+    for (int j = tid; j < d; j += 256) qs[j] *= cp.inv_sqrt_block;
+  }
+  __syncthreads();
+  // sq = S q_rot: each thread takes 4 consecutive outputs (a float4 of a row of S^T) over
+  // one of `slices` slices of the inner dimension; the slices are summed through LDS
+  if (m > 0) {
+    const int g4 = m / 4;
+    int slices = 1;                                 // largest power of two <= 256 / g4
+    while (2 * slices * g4 <= 256) slices *= 2;
+    const int jl = d / slices;
+    float *part = sqs + m;                          // [slices][m] (shared with the final sq)
+    for (int og = tid % g4 + (tid / g4 >= slices ? g4 : 0), sl = tid / g4; og < g4; og += 256) {
+      const int j0 = (slices > 1 ? sl : 0) * jl, j1 = slices > 1 ? j0 + jl : d;
+      float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 *st = reinterpret_cast<const float4 *>(cp.ST) + og;
+#pragma unroll 8
+      for (int j = j0; j < j1; ++j) {
+        const float4 sv = st[size_t(j) * g4];
+        const float x = qs[j];
+        z.x = fmaf(sv.x, x, z.x);
+        z.y = fmaf(sv.y, x, z.y);
+        z.z = fmaf(sv.z, x, z.z);
+        z.w = fmaf(sv.w, x, z.w);
+      }
+      float *o4 = part + (slices > 1 ? sl : 0) * m + 4 * og;
+      o4[0] = z.x;
+      o4[1] = z.y;
+      o4[2] = z.z;
+      o4[3] = z.w;
+      if (slices > 1) break;
+    }
+    __syncthreads();
+    for (int i = tid; i < m; i += 256) {
+      float z = 0.0f;
+      for (int sl = 0; sl < slices; ++sl) z += part[sl * m + i];
+      sqs[i] = z;
+    }
+  }
+  __syncthreads();
+  qprep_tail(qs, sqs, d, m, cp, qrows + size_t(rowi) * qstride, red, tid, lane, wv, b, g, h, G, kv_heads, qpack);
+}
+
+// Query preparation for d = m in {64, 128} with Hadamard block d (the decode MFMA path):
+// the same arithmetic as k_qprep_pack in the same order, but every global load (this
+// thread's slice of S^T, the query pair and its signs) is issued before the fp64 RoPE
+// angle is computed, the FWHT runs in one wave's registers, and one barrier less.
+template <int D>
+__global__ __launch_bounds__(256) void k_qprep_fast(const void *q, int dtype, int q_pos, float rope_base,
+                                                    CodecPtrs cp, float *qrows, int qstride,
+                                                    int q_heads, int G, uint8_t *qpack) {
+  constexpr int H2 = D / 2, G4 = D / 4, SL = 256 / G4, JL = D / SL, E = D / 64;
+  __shared__ float qs[D], sqs[D], part[SL * D];
+  __shared__ float red[4][4];
+  const int rowi = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = rowi / q_heads, hq = rowi % q_heads;
+  const int g = hq / G, h = hq % G;
+  const int kv_heads = q_heads / G;
+  const size_t base = size_t(rowi) * D;
+  const int og = tid % G4, sl = tid / G4;
+  float4 sv[JL];
+  const float4 *st = reinterpret_cast<const float4 *>(cp.ST) + og;
+#pragma unroll
+  for (int jj = 0; jj < JL; ++jj) sv[jj] = st[size_t(sl * JL + jj) * G4];
+  if (tid < H2) {
+    const int j = tid;
+    const float x0 = load_elem(q, base + j, dtype), x1 = load_elem(q, base + j + H2, dtype);
+    const float d0 = cp.D[j], d1 = cp.D[j + H2];
+    if (rope_base != 0.0f) {
+      const double theta = pow(double(rope_base), -2.0 * double(j) / double(D));
+      double sn, c;
+      sincos(double(q_pos) * theta, &sn, &c);
+      qs[j] = (x0 * float(c) - x1 * float(sn)) * d0;
+      qs[j + H2] = (x0 * float(sn) + x1 * float(c)) * d1;
+    } else {
+      qs[j] = x0 * d0;
+      qs[j + H2] = x1 * d1;
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float x[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) x[e] = qs[E * tid + e];
+#pragma unroll
+    for (int s = 1; s < E; s <<= 1)
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (!(e & s)) {
+          const float u = x[e], v = x[e + s];
+          x[e] = u + v;
+          x[e + s] = u - v;
+        }
+#pragma unroll
+    for (int msk = 1; msk < 64; msk <<= 1)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float pv = __shfl_xor(x[e], msk, 64);
+        x[e] = (tid & msk) ? pv - x[e] : x[e] + pv;
+      }
+#pragma unroll
+    for (int e = 0; e < E; ++e) qs[E * tid + e] = x[e] * cp.inv_sqrt_block;
+  }
+  __syncthreads();
+  {
+    float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int jj = 0; jj < JL; ++jj) {
+      const float x = qs[sl * JL + jj];
+      z.x = fmaf(sv[jj].x, x, z.x);
+      z.y = fmaf(sv[jj].y, x, z.y);
+      z.z = fmaf(sv[jj].z, x, z.z);
+      z.w = fmaf(sv[jj].w, x, z.w);
+    }
+    float *o4 = part + sl * D + 4 * og;
+    o4[0] = z.x;
+    o4[1] = z.y;
+    o4[2] = z.z;
+    o4[3] = z.w;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float z = 0.0f;
+#pragma unroll
+    for (int s = 0; s < SL; ++s) z += part[s * D + tid];
+    sqs[tid] = z;
+  }
+  qprep_tail(qs, sqs, D, D, cp, qrows + size_t(rowi) * qstride, red, tid, lane, wv, b, g, h, G, kv_heads, qpack);
 }
 
 // LDS-staged split-K decode.  Each wave streams its tiles through a ring of kRing LDS
@@ -1757,6 +1878,90 @@ __global__ __launch_bounds__(256) void k_decode_merge(const float *part, int spl
     __syncthreads();
   }
   for (int j = tid; j < d; j += 256) out[size_t(rowi) * d + j] = os[j] * cp.inv_sqrt_block * cp.D[j];
+}
+
+// The same merge for d = 64 or 128 (Hadamard block = d) with one wave per (batch, q-head)
+// row and no block barriers: lane l holds coordinates E l .. E l + E - 1, the split
+// weights are broadcast from the lanes that computed them, and the FWHT runs in registers
+// and across lanes.
+template <int D>
+__global__ __launch_bounds__(256) void k_decode_merge_wave(const float *part, int splits, int rows,
+                                                           CodecPtrs cp, float *out) {
+  constexpr int E = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int rowi = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rowi >= rows) return;
+  const float *pr = part + size_t(rowi) * splits * (D + 2);
+  float dsc[E];   // output scale D_j / sqrt(B), loaded up front with everything else
+#pragma unroll
+  for (int e = 0; e < E; ++e) dsc[e] = cp.D[E * lane + e] * cp.inv_sqrt_block;
+  float x[E], L = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = 0.0f;
+  constexpr int SMAX = 16;
+  if (splits <= SMAX) {
+    // all loads issued before any arithmetic: one memory round trip
+    float m_s = -INFINITY, l_s = 0.0f, xs[SMAX][E];
+    if (lane < splits) {
+      m_s = pr[size_t(lane) * (D + 2) + D];
+      l_s = pr[size_t(lane) * (D + 2) + D + 1];
+    }
+#pragma unroll
+    for (int u = 0; u < SMAX; ++u)
+#pragma unroll
+      for (int e = 0; e < E; ++e) xs[u][e] = u < splits ? pr[size_t(u) * (D + 2) + E * lane + e] : 0.0f;
+    const float mx = wave_max(m_s);
+    const float w = m_s == -INFINITY ? 0.0f : __expf(m_s - mx);
+    L = w * l_s;
+#pragma unroll
+    for (int u = 0; u < SMAX; ++u) {
+      const float wu = __shfl(w, u, 64);
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = fmaf(xs[u][e], wu, x[e]);
+    }
+  } else {
+  float mx = -INFINITY;
+  for (int s = lane; s < splits; s += 64) mx = fmaxf(mx, pr[size_t(s) * (D + 2) + D]);
+  mx = wave_max(mx);
+  for (int s0 = 0; s0 < splits; s0 += 64) {
+    const int s = s0 + lane;
+    float w = 0.0f;
+    if (s < splits) {
+      const float m_s = pr[size_t(s) * (D + 2) + D];
+      w = m_s == -INFINITY ? 0.0f : __expf(m_s - mx);
+      L += w * pr[size_t(s) * (D + 2) + D + 1];
+    }
+    const int n = min(64, splits - s0);
+    for (int u = 0; u < n; ++u) {
+      const float wu = __shfl(w, u, 64);
+      const float *ps = pr + size_t(s0 + u) * (D + 2) + E * lane;
+#pragma unroll
+      for (int e = 0; e < E; ++e) x[e] = fmaf(ps[e], wu, x[e]);
+    }
+  }
+  }
+  L = wave_sum(L);
+  const float invL = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] *= invL;
+#pragma unroll
+  for (int st = 1; st < E; st <<= 1)
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (!(e & st)) {
+        const float u = x[e], v = x[e + st];
+        x[e] = u + v;
+        x[e + st] = u - v;
+      }
+#pragma unroll
+  for (int msk = 1; msk < 64; msk <<= 1)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float p = __shfl_xor(x[e], msk, 64);
+      x[e] = (lane & msk) ? p - x[e] : x[e] + p;
+    }
+#pragma unroll
+  for (int e = 0; e < E; ++e) out[size_t(rowi) * D + E * lane + e] = x[e] * dsc[e];
 }
 
 // ------------------------------------------------------------------ search
@@ -2380,8 +2585,17 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
   const float sc = scale == 0.0f ? float(1.0 / std::sqrt(double(d))) : scale;
   const bool mfma = decode_mfma_path(*desc, q_heads);
   // symmetric 2-bit codebook on the MFMA path: c[code] = c0 + (c1 - c0) b0 + (c2 - c0) b1
-  hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s, q,
-                     int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, mfma ? qpack : nullptr);
+  if (d == m && (d == 64 || d == 128) && cp.block == d) {
+    if (d == 64)
+      hipLaunchKernelGGL(k_qprep_fast<64>, dim3(rows), dim3(256), 0, s, q, int(dtype), q_pos, rope_base, cp, qp,
+                         qstride, q_heads, G, mfma ? qpack : nullptr);
+    else
+      hipLaunchKernelGGL(k_qprep_fast<128>, dim3(rows), dim3(256), 0, s, q, int(dtype), q_pos, rope_base, cp, qp,
+                         qstride, q_heads, G, mfma ? qpack : nullptr);
+  } else {
+    hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s, q,
+                       int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, mfma ? qpack : nullptr);
+  }
   const CachePtrs ch = cache_ptrs(const_cast<void *>(cache_dev), *desc);
   int used_splits = S;
   if (mfma) {
@@ -2448,8 +2662,16 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
       hipLaunchKernelGGL(k_decode_split<128>, grid, dim3(kDecThreads), shm, s, a);
     if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
   }
-  hipLaunchKernelGGL(k_decode_merge, dim3(rows), dim3(256), size_t(used_splits + d + 256 + d) * 4, s, part,
-                     used_splits, d, cp, out);
+  if ((d == 64 || d == 128) && cp.block == d) {
+    const dim3 mg(unsigned((rows + 3) / 4));
+    if (d == 64)
+      hipLaunchKernelGGL(k_decode_merge_wave<64>, mg, dim3(256), 0, s, part, used_splits, rows, cp, out);
+    else
+      hipLaunchKernelGGL(k_decode_merge_wave<128>, mg, dim3(256), 0, s, part, used_splits, rows, cp, out);
+  } else {
+    hipLaunchKernelGGL(k_decode_merge, dim3(rows), dim3(256), size_t(used_splits + d + 256 + d) * 4, s, part,
+                       used_splits, d, cp, out);
+  }
   return launch_status();
 }
 
