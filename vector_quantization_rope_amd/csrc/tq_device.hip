@@ -429,7 +429,38 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
     constexpr int NP = KK == 2 ? 1 : KK == 4 ? 2 : KK == 8 ? 3 : 4;
     uint32_t hA[4] = {0u, 0u, 0u, 0u}, hB[4] = {0u, 0u, 0u, 0u};
     double rr = 0.0;
-    if constexpr (KK > 0) {
+    if constexpr (KK == 4) {
+      // The stored codebook is odd (c[3 - k] = -c[k], t = {-s, 0, s} / sc), so with
+      // g0 = [x >= 0] and g1 = [x >= copysign(s, x)] the code is 2 g0 + g1: the same
+      // comparisons as x >= sc t_k for each k, taken from the sign bit of an exact fp64
+      // difference rather than as lane masks.  The centroid is +-(inner or outer).
+      const double s1 = sc * double(cb_s[1][2]);
+      const double wo = nb16 * double(cb_s[0][3]), wi = nb16 * double(cb_s[0][2]);
+      const uint64_t uo = uint64_t(__double_as_longlong(wo)), ui = uint64_t(__double_as_longlong(wi));
+      uint32_t n0A = 0u, n0B = 0u, n1A = 0u, n1B = 0u;   // inverted plane bits
+#pragma unroll
+      for (int e = 0; e < C; ++e) {
+        const double xs = x[e] + 0.0;   // -0 -> +0: x >= 0 holds for both zeros
+        const uint32_t n0 = uint32_t(uint64_t(__double_as_longlong(xs)) >> 63);            // x < 0
+        const uint32_t n1 = uint32_t(uint64_t(__double_as_longlong(x[e] - copysign(s1, xs))) >> 63);
+        const uint64_t m = uint64_t(0) - uint64_t(n0 ^ n1);   // inner centroid when g0 != g1
+        const double w = copysign(__longlong_as_double(int64_t((uo & ~m) | (ui & m))), xs);
+        if (e < HC) {
+          n0A |= n0 << e;
+          n1A |= n1 << e;
+        } else {
+          n0B |= n0 << (e - HC);
+          n1B |= n1 << (e - HC);
+        }
+        x[e] -= w;
+        rr = fma(x[e], x[e], rr);
+      }
+      constexpr uint32_t hm = HC >= 32 ? 0xFFFFFFFFu : (1u << HC) - 1u;
+      hA[0] = ~n1A & hm;
+      hB[0] = ~n1B & hm;
+      hA[1] = ~n0A & hm;
+      hB[1] = ~n0B & hm;
+    } else if constexpr (KK > 0) {
       double sk[KK - 1], wk[KK];
 #pragma unroll
       for (int k = 0; k < KK - 1; ++k) sk[k] = sc * double(cb_s[1][k]);
@@ -523,15 +554,23 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
 #pragma unroll
     for (int i = 0; i < C / 4; ++i) cw[i] = 0u;
     if constexpr (KV > 0) {
-      double sk[KV - 1];
+      // odd codebook: the code is h [x >= 0] + #{i : x >= copysign(s_i, x)} over the h - 1
+      // positive thresholds s_i = sc t_{h-1+i} (the same comparisons as x >= sc t_k for
+      // every k, from the sign bits of exact fp64 differences)
+      constexpr int h = KV / 2;
+      double sp[h > 1 ? h - 1 : 1];
 #pragma unroll
-      for (int k = 0; k < KV - 1; ++k) sk[k] = sc * double(cb_s[3][k]);
+      for (int i = 1; i < h; ++i) sp[i - 1] = sc * double(cb_s[3][h - 1 + i]);
 #pragma unroll
       for (int e = 0; e < C; ++e) {
-        int code = 0;
+        const double xs = x[e] + 0.0;   // -0 -> +0
+        const uint32_t n0 = uint32_t(uint64_t(__double_as_longlong(xs)) >> 63);
+        uint32_t nb = 0u;
 #pragma unroll
-        for (int k = 0; k < KV - 1; ++k) code += x[e] >= sk[k] ? 1 : 0;
-        cw[e / 4] |= uint32_t(code) << (8 * (e % 4));
+        for (int i = 1; i < h; ++i)
+          nb += uint32_t(uint64_t(__double_as_longlong(x[e] - copysign(sp[i - 1], xs))) >> 63);
+        const uint32_t code = uint32_t(h) * (1u - n0) + uint32_t(h - 1) - nb;
+        cw[e / 4] |= code << (8 * (e % 4));
       }
     } else {
       const int K = 1 << a.bits_v;
