@@ -125,6 +125,25 @@ def test_gqa_ragged_and_appends(tq, P, d, G, T, chunks):
     check_case(tq, P, w, K, V, q, chunks=chunks, label=f"gqa d{d} G{G}")
 
 
+@pytest.mark.parametrize("bk,d,G,T,dist", [
+    (1, 128, 8, 700, "laplace"),
+    (3, 128, 8, 700, "laplace"),
+    (1, 64, 4, 500, "laplace"),
+    (3, 64, 2, 530, "laplace"),
+    (3, 64, 1, 1024, "student_t3"),
+])
+def test_mfma_key_widths(tq, P, bk, d, G, T, dist):
+    """1-bit and 3-bit keys (+ QJL) with 3-bit values on the MFMA decode path: for 3-bit
+    codes the code term is split over the three bit planes and their parity."""
+    w = W.LONG_CONTEXT.scaled(batch=1, kv_heads=2, q_heads=2 * G, d=d, m=d, context=T, bits_k=bk,
+                              dist=dist, outliers=3 if dist == "student_t3" else 4,
+                              outlier_scale=15.0 if dist == "student_t3" else 20.0,
+                              rope_base=10000.0 if dist == "student_t3" else 500000.0)
+    K, V = W.gen_kv(w)
+    q = W.gen_q(w)
+    check_case(tq, P, w, K, V, q, label=f"mfma keys {bk}-bit d{d} G{G} {dist}")
+
+
 @pytest.mark.parametrize("bk,bv,m", [(1, 2, 64), (3, 4, 128), (4, 1, 32), (2, 3, 0)])
 def test_other_bit_widths(tq, P, bk, bv, m):
     w = W.LLAMA3_8B.scaled(batch=1, kv_heads=2, q_heads=4, context=300, bits_k=bk, bits_v=bv, m=m)

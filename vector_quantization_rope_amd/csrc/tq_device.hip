@@ -1066,7 +1066,8 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kMfmaMaxG = 8;
 constexpr int kQpackCoef = 8;   // floats per head: k0..k4, padding
-constexpr int kQpackVecs = 3;   // digit-row vectors: (c1 - c0) q, (c2 - c0) q, S q
+constexpr int kQpackVecs = 5;   // digit-row vector slots: up to 4 key-plane weight vectors, S q
+constexpr int kSqVec = 4;       // slot of the S q vector
 constexpr int kDigits = 4;      // int8 digits per value: 32-bit fixed point, rows digit * 8 + head
 
 // Per unit: [kQpackVecs][32 rows][2 halves][d/32 chunks][16 bytes] of int8 digits, then
@@ -1131,11 +1132,31 @@ __device__ __forceinline__ float sum32(float v) {
 __device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, int d, int m,
                                            const CodecPtrs &cp, float *o, float (*red)[4], int tid,
                                            int lane, int wv, int b, int g, int h, int G,
-                                           int kv_heads, uint8_t *qpack) {
+                                           int kv_heads, int bits_k, uint8_t *qpack) {
   // fp32 rows and sums; maxima for the fixed-point scaling (the two plane vectors
   // (c1 - c0) q and (c2 - c0) q share one exponent, set by the larger weight)
-  const float dc1 = cp.ck[1] - cp.ck[0], dc2 = cp.ck[2] - cp.ck[0];
-  const float wmax = fmaxf(fabsf(dc1), fabsf(dc2));
+  // Key-plane weights of the odd codebook: c[code] = c0 + sum_p pw[p] bit_p(code).  For
+  // 3-bit codes, c = a0 s0 + a1 s1 + a2 s2 + a3 s0 s1 s2 (s = 2 bit - 1; the only odd
+  // multilinear terms), and s0 s1 s2 = 2 (b0 ^ b1 ^ b2) - 1, so the parity of the three
+  // bits is a fourth plane: pw = 2 a.  All planes share one exponent (the largest weight).
+  float pw[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  int np = 0;
+  if (bits_k == 1) {
+    np = 1;
+    pw[0] = cp.ck[1] - cp.ck[0];
+  } else if (bits_k == 2) {
+    np = 2;
+    pw[0] = cp.ck[1] - cp.ck[0];
+    pw[1] = cp.ck[2] - cp.ck[0];
+  } else if (bits_k == 3) {
+    np = 4;
+    const float c4 = cp.ck[4], c5 = cp.ck[5], c6 = cp.ck[6], c7 = cp.ck[7];
+    pw[0] = 0.5f * (c7 - c6 + c5 - c4);
+    pw[1] = 0.5f * (c7 + c6 - c5 - c4);
+    pw[2] = 0.5f * (c7 + c6 + c5 + c4);
+    pw[3] = 0.5f * (c7 - c6 - c5 + c4);
+  }
+  const float wmax = fmaxf(fmaxf(fabsf(pw[0]), fabsf(pw[1])), fmaxf(fabsf(pw[2]), fabsf(pw[3])));
   float s0 = 0.0f, s1 = 0.0f, m0 = 0.0f, m1 = 0.0f;
   for (int j = tid; j < d; j += 256) {
     o[j] = qs[j];
@@ -1196,16 +1217,19 @@ __device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, in
   if (!qpack) return;
   const int nch = d / 32;
   uint32_t *o32 = reinterpret_cast<uint32_t *>(qpack + size_t(b * kv_heads + g) * qpack_unit_bytes(d));
-  // this head's rows digit * 8 + h of the three vectors: [v][digit][half][chunk][e]
-  const int ndw = kQpackVecs * kDigits * 2 * nch * 4;
+  // this head's rows digit * 8 + h of the np plane vectors and the S q vector (slot
+  // kSqVec): [slot][digit][half][chunk][e]
+  const int ndw = (np + 1) * kDigits * 2 * nch * 4;
   for (int i = tid; i < ndw; i += 256) {
     const int e = i & 3, c = (i >> 2) % nch, half = (i / (4 * nch)) & 1;
-    const int digit = (i / (8 * nch)) % kDigits, v = i / (8 * kDigits * nch);
-    const float *src = v == 2 ? sqs : qs;
-    const float wgt = v == 0 ? dc1 : (v == 1 ? dc2 : 1.0f);
+    const int digit = (i / (8 * nch)) % kDigits, vi = i / (8 * kDigits * nch);
+    const bool is_sq = vi == np;
+    const int v = is_sq ? kSqVec : vi;
+    const float *src = is_sq ? sqs : qs;
+    const float wgt = is_sq ? 1.0f : pw[vi];
     // the decode kernel keeps bit e of each nibble in place (token byte = b 2^e), so the
     // query element that meets it carries the factor 2^-e
-    const int ex = sexp[v == 2 ? 1 : 0] - e;
+    const int ex = sexp[is_sq ? 1 : 0] - e;
     uint32_t word = 0u;
 #pragma unroll
     for (int beta = 0; beta < 4; ++beta) {
@@ -1228,7 +1252,7 @@ __device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, in
     const int nrow = kDigits * (8 - G);
     for (int i = tid; i < kQpackVecs * nrow * 2 * nch * 4; i += 256) {
       const int e = i & 3, c = (i >> 2) % nch, half = (i / (4 * nch)) & 1;
-      const int ri = (i / (8 * nch)) % nrow, v = i / (8 * nch * nrow);
+      const int ri = (i / (8 * nch)) % nrow, v = i / (8 * nch * nrow);   // every slot
       const int row = (ri / (8 - G)) * 8 + G + ri % (8 - G);
       o32[(((v * 32 + row) * 2 + half) * nch + c) * 4 + e] = 0u;
     }
@@ -1243,7 +1267,7 @@ __device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, in
 __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, int d, int m,
                                                     int q_pos, float rope_base, CodecPtrs cp,
                                                     float *qrows, int qstride, int q_heads,
-                                                    int G, uint8_t *qpack) {
+                                                    int G, int bits_k, uint8_t *qpack) {
   extern __shared__ float qs[];   // d floats (q_rot), m floats (sq), max(1024, m) partial sums
   float *sqs = qs + d;
   __shared__ float red[4][4];
@@ -1339,7 +1363,7 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
     }
   }
   __syncthreads();
-  qprep_tail(qs, sqs, d, m, cp, qrows + size_t(rowi) * qstride, red, tid, lane, wv, b, g, h, G, kv_heads, qpack);
+  qprep_tail(qs, sqs, d, m, cp, qrows + size_t(rowi) * qstride, red, tid, lane, wv, b, g, h, G, kv_heads, bits_k, qpack);
 }
 
 // Query preparation for d = m in {64, 128} with Hadamard block d (the decode MFMA path):
@@ -1349,7 +1373,7 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
 template <int D>
 __global__ __launch_bounds__(256) void k_qprep_fast(const void *q, int dtype, int q_pos, float rope_base,
                                                     CodecPtrs cp, float *qrows, int qstride,
-                                                    int q_heads, int G, uint8_t *qpack) {
+                                                    int q_heads, int G, int bits_k, uint8_t *qpack) {
   constexpr int H2 = D / 2, G4 = D / 4, SL = 256 / G4, JL = D / SL, E = D / 64;
   __shared__ float qs[D], sqs[D], part[SL * D];
   __shared__ float red[4][4];
@@ -1426,7 +1450,7 @@ __global__ __launch_bounds__(256) void k_qprep_fast(const void *q, int dtype, in
     for (int s = 0; s < SL; ++s) z += part[s * D + tid];
     sqs[tid] = z;
   }
-  qprep_tail(qs, sqs, D, D, cp, qrows + size_t(rowi) * qstride, red, tid, lane, wv, b, g, h, G, kv_heads, qpack);
+  qprep_tail(qs, sqs, D, D, cp, qrows + size_t(rowi) * qstride, red, tid, lane, wv, b, g, h, G, kv_heads, bits_k, qpack);
 }
 
 // LDS-staged split-K decode.  Each wave streams its tiles through a ring of kRing LDS
@@ -1442,15 +1466,15 @@ constexpr int kDecBlocksPerCU = 1;
 // block waiting for its own results (lgkmcnt(0)), because the compiler would otherwise
 // wait for every direct-to-LDS load in flight (including the prefetches into the other
 // slots) before any LDS read; the ring's own vmcnt waits order them instead.
-template <int D>
+template <int D, int KBITS>
 struct LdsGeom {
-  static constexpr int KB = 3 * D / 8;     // key record bytes (2 planes + m = d sign bits)
+  static constexpr int KB = (KBITS + 1) * D / 8;   // key record bytes (KBITS planes + m = d sign bits)
   static constexpr int KT = 32 * KB;       // key bytes per 32-token tile
   static constexpr int VT = 12 * D;        // value-code bytes per 32-token tile
-  // direct-to-LDS loads land lane-contiguously for 4- and 16-byte sizes: keys of d = 128
-  // and all value tiles go as 16-byte chunks (96 or 48 lanes), the 24-byte key records of
-  // d = 64 (not 16-byte aligned in general) as dwords
-  static constexpr int KCH = D >= 128 ? 16 : 4;   // key chunk bytes
+  // direct-to-LDS loads land lane-contiguously for 4- and 16-byte sizes: key records whose
+  // size is a multiple of 16 and all value tiles go as 16-byte chunks, other key records
+  // (24 bytes at d = 64 with 2-bit codes: not 16-byte aligned in general) as dwords
+  static constexpr int KCH = KB % 16 == 0 ? 16 : 4;   // key chunk bytes
   static constexpr int NK = (KT / KCH + 63) / 64; // key DMA instructions
   static constexpr int NV = (VT / 16 + 63) / 64;  // value DMA instructions
   static constexpr int NDMA = NK + NV + 2;        // + key norms + value norms
@@ -1477,13 +1501,17 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
 }
 
-template <int D>
+// KBITS = key code bits (1, 2 or 3).  The key score's code term is a weighted sum of
+// NP 0/1 planes: the code bits, and for 3-bit codes also their parity (odd codebook).
+template <int D, int KBITS>
 __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(MfmaArgs a) {
   // The body is device code only (its local lambdas call device builtins); the host pass
   // needs nothing but the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-  using Gm = LdsGeom<D>;
+  using Gm = LdsGeom<D, KBITS>;
   constexpr int NCH = D / 32, NT = D / 16, NW = kDecWaves, NTH = 64 * NW, R = kRing;
+  constexpr int NP = KBITS == 3 ? 4 : KBITS;
+  static_assert(KBITS >= 1 && KBITS <= 3, "key planes");
   __shared__ __align__(16) uint8_t ring[R][NW][Gm::SLOT];
   __shared__ uint2 lut[4096];
   __shared__ __align__(16) _Float16 pt_s[NW][16][40];
@@ -1510,15 +1538,15 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
     coef_s[hf][k][r] = coef[(4 * hf + r) * kQpackCoef + k] * a.scale_log2;
   }
   const int row = lane & 31, half = lane >> 5;
-  // int8 digit rows: plane 0 weight (c1 - c0) q, plane 1 weight (c2 - c0) q, S q
-  v4i Aq0[NCH], Aq1[NCH], As[NCH];
+  // int8 digit rows: the NP plane-weight vectors and S q
+  v4i Aq[NP][NCH], As[NCH];
   {
     const v4i *src = reinterpret_cast<const v4i *>(qpk);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      Aq0[c] = src[((0 * 32 + row) * 2 + half) * NCH + c];
-      Aq1[c] = src[((1 * 32 + row) * 2 + half) * NCH + c];
-      As[c] = src[((2 * 32 + row) * 2 + half) * NCH + c];
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) Aq[pp][c] = src[((pp * 32 + row) * 2 + half) * NCH + c];
+      As[c] = src[((kSqVec * 32 + row) * 2 + half) * NCH + c];
     }
   }
   __syncthreads();
@@ -1609,7 +1637,10 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
     const uint32_t sbase = uint32_t(reinterpret_cast<uintptr_t>(slot));
     // ---- this lane's key words, its token's norms and its value-code words, read in one
     // block; the value LUT lookups follow at once so their latency overlaps the key MFMAs
-    uint2 kw[3];
+    // four key words per lane: the planes of the record (D / 8 bytes each, the lane's half
+    // of them) and its sign bits; with fewer than three planes the extra reads fall on the
+    // next record or the value region of the slot and are not used
+    uint2 kw[4];
     uint32_t nr, vnb;
     uint32_t vwr[NT][2];
     {
@@ -1620,29 +1651,30 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
 #if defined(__HIP_DEVICE_COMPILE__)
       if constexpr (D >= 128) {
         asm volatile(
-            "ds_read_b64 %0, %21\n"
-            "ds_read_b64 %1, %21 offset:16\n"
-            "ds_read_b64 %2, %21 offset:32\n"
-            "ds_read_b32 %3, %22\n"
-            "ds_read_u16 %4, %23\n"
-            "ds_read_b32 %5, %24\n"
-            "ds_read_b32 %6, %24 offset:4\n"
-            "ds_read_b32 %7, %24 offset:192\n"
-            "ds_read_b32 %8, %24 offset:196\n"
-            "ds_read_b32 %9, %24 offset:384\n"
-            "ds_read_b32 %10, %24 offset:388\n"
-            "ds_read_b32 %11, %24 offset:576\n"
-            "ds_read_b32 %12, %24 offset:580\n"
-            "ds_read_b32 %13, %24 offset:768\n"
-            "ds_read_b32 %14, %24 offset:772\n"
-            "ds_read_b32 %15, %24 offset:960\n"
-            "ds_read_b32 %16, %24 offset:964\n"
-            "ds_read_b32 %17, %24 offset:1152\n"
-            "ds_read_b32 %18, %24 offset:1156\n"
-            "ds_read_b32 %19, %24 offset:1344\n"
-            "ds_read_b32 %20, %24 offset:1348\n"
+            "ds_read_b64 %0, %22\n"
+            "ds_read_b64 %1, %22 offset:16\n"
+            "ds_read_b64 %2, %22 offset:32\n"
+            "ds_read_b64 %3, %22 offset:48\n"
+            "ds_read_b32 %4, %23\n"
+            "ds_read_u16 %5, %24\n"
+            "ds_read_b32 %6, %25\n"
+            "ds_read_b32 %7, %25 offset:4\n"
+            "ds_read_b32 %8, %25 offset:192\n"
+            "ds_read_b32 %9, %25 offset:196\n"
+            "ds_read_b32 %10, %25 offset:384\n"
+            "ds_read_b32 %11, %25 offset:388\n"
+            "ds_read_b32 %12, %25 offset:576\n"
+            "ds_read_b32 %13, %25 offset:580\n"
+            "ds_read_b32 %14, %25 offset:768\n"
+            "ds_read_b32 %15, %25 offset:772\n"
+            "ds_read_b32 %16, %25 offset:960\n"
+            "ds_read_b32 %17, %25 offset:964\n"
+            "ds_read_b32 %18, %25 offset:1152\n"
+            "ds_read_b32 %19, %25 offset:1156\n"
+            "ds_read_b32 %20, %25 offset:1344\n"
+            "ds_read_b32 %21, %25 offset:1348\n"
             "s_waitcnt lgkmcnt(0)\n"
-            : "=v"(kw[0]), "=v"(kw[1]), "=v"(kw[2]), "=v"(nr), "=v"(vnb),
+            : "=v"(kw[0]), "=v"(kw[1]), "=v"(kw[2]), "=v"(kw[3]), "=v"(nr), "=v"(vnb),
               "=v"(vwr[0][0]), "=v"(vwr[0][1]), "=v"(vwr[1][0]), "=v"(vwr[1][1]), "=v"(vwr[2][0]),
               "=v"(vwr[2][1]), "=v"(vwr[3][0]), "=v"(vwr[3][1]), "=v"(vwr[4][0]), "=v"(vwr[4][1]),
               "=v"(vwr[5][0]), "=v"(vwr[5][1]), "=v"(vwr[6][0]), "=v"(vwr[6][1]), "=v"(vwr[7][0]),
@@ -1650,23 +1682,24 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
             : "v"(kaddr), "v"(naddr), "v"(vaddr), "v"(caddr)
             : "memory");
       } else {
-        uint32_t x0, x1, x2;
+        uint32_t x0, x1, x2, x3;
         asm volatile(
-            "ds_read_b32 %0, %13\n"
-            "ds_read_b32 %1, %13 offset:8\n"
-            "ds_read_b32 %2, %13 offset:16\n"
-            "ds_read_b32 %3, %14\n"
-            "ds_read_u16 %4, %15\n"
-            "ds_read_b32 %5, %16\n"
-            "ds_read_b32 %6, %16 offset:4\n"
-            "ds_read_b32 %7, %16 offset:192\n"
-            "ds_read_b32 %8, %16 offset:196\n"
-            "ds_read_b32 %9, %16 offset:384\n"
-            "ds_read_b32 %10, %16 offset:388\n"
-            "ds_read_b32 %11, %16 offset:576\n"
-            "ds_read_b32 %12, %16 offset:580\n"
+            "ds_read_b32 %0, %14\n"
+            "ds_read_b32 %1, %14 offset:8\n"
+            "ds_read_b32 %2, %14 offset:16\n"
+            "ds_read_b32 %3, %14 offset:24\n"
+            "ds_read_b32 %4, %15\n"
+            "ds_read_u16 %5, %16\n"
+            "ds_read_b32 %6, %17\n"
+            "ds_read_b32 %7, %17 offset:4\n"
+            "ds_read_b32 %8, %17 offset:192\n"
+            "ds_read_b32 %9, %17 offset:196\n"
+            "ds_read_b32 %10, %17 offset:384\n"
+            "ds_read_b32 %11, %17 offset:388\n"
+            "ds_read_b32 %12, %17 offset:576\n"
+            "ds_read_b32 %13, %17 offset:580\n"
             "s_waitcnt lgkmcnt(0)\n"
-            : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(nr), "=v"(vnb),
+            : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3), "=v"(nr), "=v"(vnb),
               "=v"(vwr[0][0]), "=v"(vwr[0][1]), "=v"(vwr[1][0]), "=v"(vwr[1][1]), "=v"(vwr[2][0]),
               "=v"(vwr[2][1]), "=v"(vwr[3][0]), "=v"(vwr[3][1])
             : "v"(kaddr), "v"(naddr), "v"(vaddr), "v"(caddr)
@@ -1674,6 +1707,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
         kw[0] = make_uint2(x0, 0u);
         kw[1] = make_uint2(x1, 0u);
         kw[2] = make_uint2(x2, 0u);
+        kw[3] = make_uint2(x3, 0u);
       }
 #else
       (void)kaddr;
@@ -1681,7 +1715,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
       (void)vaddr;
       (void)caddr;
       nr = vnb = 0u;
-      kw[0] = kw[1] = kw[2] = make_uint2(0u, 0u);
+      kw[0] = kw[1] = kw[2] = kw[3] = make_uint2(0u, 0u);
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) vwr[nt][0] = vwr[nt][1] = 0u;
 #endif
@@ -1697,28 +1731,30 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
       v4i bw = {int(e0.x), int(e0.y), int(e1.x), int(e1.y)};
       __builtin_memcpy(&Bv[nt], &bw, 16);
     }
-    // ---- key scores on int8 MFMA: both code planes accumulate into s01 (their digit rows
-    // carry the plane weights), the sign bits into s2.  The B bytes of coordinate-chunk c
+    // ---- key scores on int8 MFMA: every code plane accumulates into s01 (its digit rows
+    // carry the plane weight), the sign bits into s2.  The B bytes of coordinate-chunk c
     // are bit e of the low (c even) or high (c odd) nibble of each byte of the lane's plane
     // dword for c / 2, masked in place: byte value b 2^e, the 2^-e being in the query digits.
+    // Plane words: the code bits, then for 3-bit codes their parity; signs follow the codes.
+    uint2 pl[NP + 1];
+#pragma unroll
+    for (int pp = 0; pp < KBITS; ++pp) pl[pp] = kw[pp];
+    if constexpr (KBITS == 3) pl[3] = make_uint2(kw[0].x ^ kw[1].x ^ kw[2].x, kw[0].y ^ kw[1].y ^ kw[2].y);
+    pl[NP] = kw[KBITS];
     v16i s01 = {}, s2 = {};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      v4i b0, b1, b2;
-      const uint32_t w0 = (c >> 1) ? kw[0].y : kw[0].x;
-      const uint32_t w1 = (c >> 1) ? kw[1].y : kw[1].x;
-      const uint32_t w2 = (c >> 1) ? kw[2].y : kw[2].x;
-      const uint32_t n0 = (c & 1) ? w0 >> 4 : w0, n1 = (c & 1) ? w1 >> 4 : w1;
-      const uint32_t n2 = (c & 1) ? w2 >> 4 : w2;
+      v4i bp[NP + 1];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        b0[e] = int(n0 & (0x01010101u << e));
-        b1[e] = int(n1 & (0x01010101u << e));
-        b2[e] = int(n2 & (0x01010101u << e));
+      for (int pp = 0; pp <= NP; ++pp) {
+        const uint32_t w = (c >> 1) ? pl[pp].y : pl[pp].x;
+        const uint32_t nb = (c & 1) ? w >> 4 : w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bp[pp][e] = int(nb & (0x01010101u << e));
       }
-      s01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq0[c], b0, s01, 0, 0, 0);
-      s01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq1[c], b1, s01, 0, 0, 0);
-      s2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(As[c], b2, s2, 0, 0, 0);
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) s01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq[pp][c], bp[pp], s01, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(As[c], bp[NP], s2, 0, 0, 0);
     }
     const float n16 = f16_bits_to_float(nr & 0xFFFFu), rn16 = f16_bits_to_float(nr >> 16);
     const float vnorm = f16_bits_to_float(vnb & 0xFFFFu);
@@ -2429,7 +2465,7 @@ bool decode_supported(const tq_cache_desc &c) {
 
 // The MFMA path covers the 2-bit + QJL (m = d) keys, 3-bit values configuration.
 bool decode_mfma_path(const tq_cache_desc &c, int q_heads) {
-  return (c.d == 64 || c.d == 128) && c.bits_k == 2 && c.bits_v == 3 && c.m == c.d &&
+  return (c.d == 64 || c.d == 128) && c.bits_k >= 1 && c.bits_k <= 3 && c.bits_v == 3 && c.m == c.d &&
          q_heads / c.kv_heads <= kMfmaMaxG;
 }
 
@@ -2623,17 +2659,18 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
   const int G = q_heads / desc->kv_heads;
   const float sc = scale == 0.0f ? float(1.0 / std::sqrt(double(d))) : scale;
   const bool mfma = decode_mfma_path(*desc, q_heads);
-  // symmetric 2-bit codebook on the MFMA path: c[code] = c0 + (c1 - c0) b0 + (c2 - c0) b1
+  // odd key codebook on the MFMA path: c[code] = c0 + a weighted sum of bit planes
+  const int bk = desc->bits_k;
   if (d == m && (d == 64 || d == 128) && cp.block == d) {
     if (d == 64)
       hipLaunchKernelGGL(k_qprep_fast<64>, dim3(rows), dim3(256), 0, s, q, int(dtype), q_pos, rope_base, cp, qp,
-                         qstride, q_heads, G, mfma ? qpack : nullptr);
+                         qstride, q_heads, G, bk, mfma ? qpack : nullptr);
     else
       hipLaunchKernelGGL(k_qprep_fast<128>, dim3(rows), dim3(256), 0, s, q, int(dtype), q_pos, rope_base, cp, qp,
-                         qstride, q_heads, G, mfma ? qpack : nullptr);
+                         qstride, q_heads, G, bk, mfma ? qpack : nullptr);
   } else {
     hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s, q,
-                       int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, mfma ? qpack : nullptr);
+                       int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, bk, mfma ? qpack : nullptr);
   }
   const CachePtrs ch = cache_ptrs(const_cast<void *>(cache_dev), *desc);
   int used_splits = S;
@@ -2662,10 +2699,16 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
     ma.inv_scale_log2 = 1.0f / ma.scale_log2;
     dim3 grid(units, used_splits);
     if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
-    if (d == 64)
-      hipLaunchKernelGGL(k_decode_lds<64>, grid, dim3(64 * kDecWaves), 0, s, ma);
-    else
-      hipLaunchKernelGGL(k_decode_lds<128>, grid, dim3(64 * kDecWaves), 0, s, ma);
+    const dim3 blk(64 * kDecWaves);
+    if (d == 64) {
+      if (bk == 1) hipLaunchKernelGGL((k_decode_lds<64, 1>), grid, blk, 0, s, ma);
+      if (bk == 2) hipLaunchKernelGGL((k_decode_lds<64, 2>), grid, blk, 0, s, ma);
+      if (bk == 3) hipLaunchKernelGGL((k_decode_lds<64, 3>), grid, blk, 0, s, ma);
+    } else {
+      if (bk == 1) hipLaunchKernelGGL((k_decode_lds<128, 1>), grid, blk, 0, s, ma);
+      if (bk == 2) hipLaunchKernelGGL((k_decode_lds<128, 2>), grid, blk, 0, s, ma);
+      if (bk == 3) hipLaunchKernelGGL((k_decode_lds<128, 3>), grid, blk, 0, s, ma);
+    }
     if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
   } else {
     DecodeArgs a;
@@ -2766,7 +2809,7 @@ tq_status tq_search_topk(const tq_cache_desc *db, const void *codec_dev, const v
   int *cand_i = reinterpret_cast<int *>(wb + align256(size_t(nq) * qstride * 4) + align256(cand * 4));
   hipLaunchKernelGGL(k_qprep_pack, dim3(nq), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s,
                      static_cast<const void *>(queries), int(TQ_F32), d, m, 0, 0.0f, cp, qp, qstride,
-                     nq, 1, static_cast<uint8_t *>(nullptr));
+                     nq, 1, db->bits_k, static_cast<uint8_t *>(nullptr));
   // MFMA path: 3-bit codes with m = d, whole 128-coordinate groups, k <= 16.  The codec's
   // codebooks are exactly symmetric by construction.
   const bool mfma = db->bits_k == 3 && m == d && d % 128 == 0 && d <= 2048 && k <= kSmTopMax;
