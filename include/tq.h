@@ -148,7 +148,9 @@ int32_t tq_decode_splits(const tq_cache_desc *desc, int32_t q_heads, int32_t len
  * q-head h reads kv-head floor(h * kv_heads / q_heads); q_heads must be a multiple of
  * kv_heads.  q: device [batch][q_heads][d] of `dtype`.  out: device fp32
  * [batch][q_heads][d].  scores: NULL or device fp32 [batch][q_heads][length], receiving
- * the unscaled score_t.  length == 0 writes out = 0.  ws: device workspace of at least
+ * the unscaled score_t.  out == NULL (scores required) computes the logits only: the
+ * scores are written and no softmax, value or output work is done.  length == 0 writes
+ * out = 0.  ws: device workspace of at least
  * tq_decode_workspace_bytes bytes, overwritten. */
 tq_status tq_decode_attend(const tq_cache_desc *desc, const void *codec_dev,
                            const void *cache_dev, int32_t length, const void *q,

@@ -144,6 +144,39 @@ def test_mfma_key_widths(tq, P, bk, d, G, T, dist):
     check_case(tq, P, w, K, V, q, label=f"mfma keys {bk}-bit d{d} G{G} {dist}")
 
 
+@pytest.mark.parametrize("bk,bv,d,G,T", [
+    (2, 3, 128, 8, 1300), (3, 3, 128, 4, 700), (1, 3, 64, 8, 530), (3, 3, 64, 2, 300), (3, 4, 128, 4, 300),
+])
+def test_logits_only(tq, P, bk, bv, d, G, T):
+    """out = NULL: the scores alone (the MFMA key formats run a logits-only kernel; other
+    formats the full split kernel without the merge), against the oracle's scores and the
+    scores of a full decode."""
+    w = W.LONG_CONTEXT.scaled(batch=2, kv_heads=2, q_heads=2 * G, d=d, m=d, context=T, bits_k=bk, bits_v=bv)
+    K, V = W.gen_kv(w)
+    q = W.gen_q(w)
+    codec, cache = build(tq, w, K.cuda(), V.cuda())
+    codec_o = O.make_codec(w.d, w.bits_k, w.bits_v, w.m, 0)
+    fields, _, sc_o = oracle_side(P, w, K, V, q, T, codec_o)
+    img = P.oracle_image(cache.desc.as_dict(), fields)
+    ocache = tq.PackedCache(w.batch, w.kv_heads, d, T, w.bits_k, w.bits_v, w.m)
+    ocache.buf.copy_(torch.from_numpy(img))
+    B, Hq = q.shape[0], q.shape[1]
+    sc = torch.full((B, Hq, T), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tq.decode_workspace_bytes(ocache.desc, Hq, T), dtype=torch.uint8, device="cuda")
+    tq.decode_attend(ocache.desc, codec.dev, ocache.buf, T, q.cuda(), w.q_pos, w.rope_base, None,
+                     scores=sc, ws=ws)
+    torch.cuda.synchronize()
+    got = sc.cpu().numpy()
+    assert np.isfinite(got).all()
+    e = P.max_abs(got, sc_o)
+    _, sc_full = decode(tq, codec, ocache, q.cuda(), T, w.q_pos, w.rope_base)
+    full = sc_full.cpu().numpy()[:, :, :T]
+    e_full = P.max_abs(got, full)
+    say(f"    logits only k{bk} v{bv} d{d} G{G}: vs oracle {e:.2e}, vs full decode {e_full:.2e}")
+    # the full decode forms scale * score and divides the scale out again: a few fp32 ulps
+    assert e <= TOL and e_full <= 1e-6 * max(1.0, float(np.abs(full).max()))
+
+
 @pytest.mark.parametrize("bk,bv,m", [(1, 2, 64), (3, 4, 128), (4, 1, 32), (2, 3, 0)])
 def test_other_bit_widths(tq, P, bk, bv, m):
     w = W.LLAMA3_8B.scaled(batch=1, kv_heads=2, q_heads=4, context=300, bits_k=bk, bits_v=bv, m=m)

@@ -1893,6 +1893,102 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
 #endif
 }
 
+// Attention logits only (tq_decode_attend with out = NULL): the key-score half of
+// k_decode_lds, for the same key formats and query digit rows, writing the unscaled
+// estimates.  With no value stream to stage, each lane loads its own token's key words
+// (its half of every plane and of the signs) and norms straight into registers one tile
+// ahead; 4 waves per block, wave w taking tiles w, w + 4, ... of the block's chunk.
+template <int D, int KBITS>
+__global__ __launch_bounds__(256) void k_logits(MfmaArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NCH = D / 32, NP = KBITS == 3 ? 4 : KBITS, KB = (KBITS + 1) * D / 8;
+  __shared__ __align__(16) float coef_s[2][5][4];
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int unit = blockIdx.x, split = blockIdx.y;
+  const int b = unit / a.kv_heads, g = unit % a.kv_heads;
+  const int hq0 = g * a.G;
+  const uint8_t *qpk = a.qpack + size_t(unit) * qpack_unit_bytes(D);
+  const float *coef = reinterpret_cast<const float *>(qpk + size_t(kQpackVecs) * 32 * 2 * NCH * 16);
+  if (tid < 40) {
+    const int hf = tid / 20, k = (tid / 4) % 5, r = tid % 4;
+    coef_s[hf][k][r] = coef[(4 * hf + r) * kQpackCoef + k];
+  }
+  const int row = lane & 31, half = lane >> 5;
+  v4i Aq[NP][NCH], As[NCH];
+  {
+    const v4i *src = reinterpret_cast<const v4i *>(qpk);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) Aq[pp][c] = src[((pp * 32 + row) * 2 + half) * NCH + c];
+      As[c] = src[((kSqVec * 32 + row) * 2 + half) * NCH + c];
+    }
+  }
+  __syncthreads();
+  const int t_begin = split * a.chunk;
+  const int t_end = min(a.length, t_begin + a.chunk);
+  const size_t ubase = size_t(unit) * a.capacity;
+  const int t_first = t_begin + 32 * wv;
+  const int nk = t_end > t_first ? (t_end - t_first + 127) / 128 : 0;
+  // a lane's words of tile k (tokens past the end read the last token of the range)
+  auto load = [&](int k, uint2 (&kw)[KBITS + 1], uint32_t &nr) {
+    const int tc = min(t_first + 128 * k + row, t_end - 1);
+    const uint8_t *rec = a.kbits + (ubase + tc) * KB + half * (D / 16);
+#pragma unroll
+    for (int pp = 0; pp <= KBITS; ++pp) {
+      if constexpr (D >= 128)
+        kw[pp] = *reinterpret_cast<const uint2 *>(rec + pp * (D / 8));
+      else
+        kw[pp] = make_uint2(*reinterpret_cast<const uint32_t *>(rec + pp * (D / 8)), 0u);
+    }
+    nr = a.knorm[ubase + tc];
+  };
+  uint2 kwn[KBITS + 1];
+  uint32_t nrn = 0u;
+  if (nk > 0) load(0, kwn, nrn);
+  for (int k = 0; k < nk; ++k) {
+    uint2 kw[KBITS + 1];
+#pragma unroll
+    for (int pp = 0; pp <= KBITS; ++pp) kw[pp] = kwn[pp];
+    const uint32_t nr = nrn;
+    if (k + 1 < nk) load(k + 1, kwn, nrn);
+    uint2 pl[NP + 1];
+#pragma unroll
+    for (int pp = 0; pp < KBITS; ++pp) pl[pp] = kw[pp];
+    if constexpr (KBITS == 3) pl[3] = make_uint2(kw[0].x ^ kw[1].x ^ kw[2].x, kw[0].y ^ kw[1].y ^ kw[2].y);
+    pl[NP] = kw[KBITS];
+    v16i s01 = {}, s2 = {};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      v4i bp[NP + 1];
+#pragma unroll
+      for (int pp = 0; pp <= NP; ++pp) {
+        const uint32_t w = (c >> 1) ? pl[pp].y : pl[pp].x;
+        const uint32_t nb = (c & 1) ? w >> 4 : w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bp[pp][e] = int(nb & (0x01010101u << e));
+      }
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) s01 = __builtin_amdgcn_mfma_i32_32x32x32_i8(Aq[pp][c], bp[pp], s01, 0, 0, 0);
+      s2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(As[c], bp[NP], s2, 0, 0, 0);
+    }
+    const float n16 = f16_bits_to_float(nr & 0xFFFFu), rn16 = f16_bits_to_float(nr >> 16);
+    const int t = t_first + 128 * k + row;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float S01 = fmaf(float(s01[r] + 256 * s01[4 + r]), 0x1p-16f, float(s01[8 + r] + 256 * s01[12 + r]));
+      const float S2 = fmaf(float(s2[r] + 256 * s2[4 + r]), 0x1p-16f, float(s2[8 + r] + 256 * s2[12 + r]));
+      const float sc = fmaf(n16, fmaf(coef_s[half][1][r], S01, coef_s[half][0][r]),
+                            rn16 * fmaf(coef_s[half][3][r], S2, -coef_s[half][4][r]));
+      const int h = 4 * half + r;
+      if (t < t_end && h < a.G) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.length + t] = sc;
+    }
+  }
+#else
+  (void)a;
+#endif
+}
+
 // Merge of the splits and inverse rotation: out = D .* (H o) / sqrt(B) = Pi^T o.
 // One block per (batch, q-head) row; split maxima and sums go through LDS first.
 __global__ __launch_bounds__(256) void k_decode_merge(const float *part, int splits, int d,
@@ -2472,13 +2568,14 @@ bool decode_mfma_path(const tq_cache_desc &c, int q_heads) {
 constexpr int kMfmaChunk = 32 * kDecWaves;   // tokens per block iteration (one tile per wave)
 
 constexpr int kDecodeBlocks = 256 * kDecBlocksPerCU;   // MI355X: 256 CUs
+constexpr int kLogitsBlocks = 1024;                    // logits-only kernel: 4 blocks per CU
 
 int default_splits(const tq_cache_desc &c, int length) {
   if (length <= 0) return 1;
   const int units = c.batch * c.kv_heads;
   const int by_len = (length + kMfmaChunk - 1) / kMfmaChunk;
-  // one round of blocks: the split kernel keeps 2 blocks resident per CU and MI355X has
-  // 256 CUs, so 512 blocks start together and none waits for a second round
+  // one round of blocks: the split kernel keeps kDecBlocksPerCU blocks resident per CU
+  // and MI355X has 256 CUs, so all blocks start together and none waits for a second round
   const int want = (kDecodeBlocks + units - 1) / units;
   int s = by_len < want ? by_len : want;
   if (s < 1) s = 1;
@@ -2629,7 +2726,8 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
                                     float rope_base, float scale, float *out, float *scores,
                                     int32_t splits, void *ws, size_t ws_bytes,
                                     void *ev_start, void *ev_stop, tq_stream_t stream) {
-  if (!desc || !codec_dev || !cache_dev || !q || !out || !ws) return TQ_EINVAL;
+  // out == NULL asks for the logits only (scores required)
+  if (!desc || !codec_dev || !cache_dev || !q || (!out && !scores) || !ws) return TQ_EINVAL;
   if (!cache_desc_valid(*desc)) return TQ_EUNSUPPORTED;
   if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_EINVAL;
   if (q_heads < 1 || q_heads % desc->kv_heads != 0) return TQ_EINVAL;
@@ -2645,6 +2743,7 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
   const int rows = desc->batch * q_heads;
   hipStream_t s = hipStream_t(stream);
   if (length == 0) {
+    if (!out) return TQ_OK;   // no tokens, no logits
     // a fill kernel rather than a memset node, so the call can be captured in a graph
     const size_t n = size_t(rows) * d;
     hipLaunchKernelGGL(k_fill_zero, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, out, n);
@@ -2697,6 +2796,28 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
     ma.G = G;
     ma.scale_log2 = sc * 1.4426950408889634f;
     ma.inv_scale_log2 = 1.0f / ma.scale_log2;
+    if (!out) {
+      // logits only: 4-wave blocks, about four per CU unless the caller fixed the splits
+      const int by_len = (length + 127) / 128;
+      int ls = splits != 0 ? splits : (kLogitsBlocks + units - 1) / units;
+      ls = std::max(1, std::min(ls, by_len));
+      const int lchunk = ((length + ls - 1) / ls + 127) / 128 * 128;
+      ma.chunk = lchunk;
+      ma.splits = (length + lchunk - 1) / lchunk;
+      const dim3 lgrid(units, ma.splits);
+      if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
+      if (d == 64) {
+        if (bk == 1) hipLaunchKernelGGL((k_logits<64, 1>), lgrid, dim3(256), 0, s, ma);
+        if (bk == 2) hipLaunchKernelGGL((k_logits<64, 2>), lgrid, dim3(256), 0, s, ma);
+        if (bk == 3) hipLaunchKernelGGL((k_logits<64, 3>), lgrid, dim3(256), 0, s, ma);
+      } else {
+        if (bk == 1) hipLaunchKernelGGL((k_logits<128, 1>), lgrid, dim3(256), 0, s, ma);
+        if (bk == 2) hipLaunchKernelGGL((k_logits<128, 2>), lgrid, dim3(256), 0, s, ma);
+        if (bk == 3) hipLaunchKernelGGL((k_logits<128, 3>), lgrid, dim3(256), 0, s, ma);
+      }
+      if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
+      return launch_status();
+    }
     dim3 grid(units, used_splits);
     if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
     const dim3 blk(64 * kDecWaves);
@@ -2743,6 +2864,7 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
     else
       hipLaunchKernelGGL(k_decode_split<128>, grid, dim3(kDecThreads), shm, s, a);
     if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
+    if (!out) return launch_status();   // logits only: the scores are written, no merge
   }
   if ((d == 64 || d == 128) && cp.block == d) {
     const dim3 mg(unsigned((rows + 3) / 4));
