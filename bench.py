@@ -192,6 +192,83 @@ def search_bench(tq, W, dev, ev, stream):
     }
 
 
+def key_width_bench(tq, W, w, K, V, q, dev, ev, stream, reps: int = 30):
+    """Key bit-width variants on the same long-context shape, outside the timed steps:
+    full decode of 1-, 2- and 3-bit keys (+ QJL, 3-bit values), and attention logits only
+    (scores, out = NULL) for packed 3- and 4-bit keys next to the same logits computed from
+    unquantized fp32 and bf16 keys with a batched matmul (the pages' "up to 8x" compares
+    4-bit keys against 32-bit ones)."""
+    import torch
+
+    T, units, G = w.context, w.batch * w.kv_heads, w.q_heads // w.kv_heads
+    vrec = w.d * 3 // 8 + 2
+    med = lambda v: sorted(v)[len(v) // 2]
+    E = [[ev.create() for _ in range(4)] for _ in range(reps)]
+    out = torch.empty((w.batch, w.q_heads, w.d), dtype=torch.float32, device=dev)
+    sc = torch.empty((w.batch, w.q_heads, T), dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        # back to back, one synchronisation at the end, after 80 ms of the same calls: the
+        # cache build before each variant idles the GPU and its clock ramps up again
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 0.08:
+            fn(None)
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
+        for i in range(reps):
+            ev.record(E[i][0], stream)
+            fn((E[i][1], E[i][2]))
+            ev.record(E[i][3], stream)
+        torch.cuda.synchronize()
+        call = [ev.elapsed_ms(e[0], e[3]) * 1e3 for e in E]
+        kern = [ev.elapsed_ms(e[1], e[2]) * 1e3 for e in E]
+        return med(call), med(kern)
+
+    decode, logits = {}, {}
+    for bk in (1, 2, 3):
+        codec = tq.Codec(w.d, bk, w.bits_v, w.d, seed=0, device=dev)
+        cache = tq.PackedCache(w.batch, w.kv_heads, w.d, T, bk, w.bits_v, w.d, device=dev)
+        tq.quantize_kv(cache.desc, codec.dev, cache.buf, K, V, 0, w.rope_base)
+        ws = torch.empty(tq.decode_workspace_bytes(cache.desc, w.q_heads, T), dtype=torch.uint8, device=dev)
+        krec = (bk + 1) * w.d // 8 + 4
+        call, kern = timed(lambda e: tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos,
+                                                       w.rope_base, out, ws=ws, events=e))
+        nbytes = units * T * (krec + vrec)
+        decode[f"keys_{bk}bit_qjl"] = {
+            "bits_per_key_coordinate": bk + 1, "record_bytes_per_token": krec + vrec,
+            "decode_call_us": round(call, 2), "split_kernel_us": round(kern, 2),
+            "split_kernel_gbs": round(nbytes / (kern * 1e-6) / 1e9, 1),
+            "split_kernel_hbm_frac": round(nbytes / (kern * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+        if bk >= 2:
+            call, kern = timed(lambda e: tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos,
+                                                           w.rope_base, None, scores=sc, ws=ws, events=e))
+            lb = units * T * (krec + 4 * G)
+            logits[f"packed_{bk + 1}bit_keys"] = {
+                "call_us": round(call, 2), "kernel_us": round(kern, 2),
+                "kernel_gbs": round(lb / (kern * 1e-6) / 1e9, 1)}
+        del cache, ws, codec
+    # unquantized keys: scores[u, t, g] = K[u, t, :] . q[u, g, :] as one batched matmul
+    qf = q.float().reshape(units, G, w.d).transpose(1, 2).contiguous()
+    for name, kdt in (("fp32_keys", torch.float32), ("bf16_keys", torch.bfloat16)):
+        Ku = K.reshape(units, T, w.d).to(kdt).contiguous()
+        qu = qf.to(kdt).contiguous()
+        res = torch.empty((units, T, G), dtype=kdt, device=dev)
+        call, _ = timed(lambda e: torch.matmul(Ku, qu, out=res) if e is None else
+                        (ev.record(e[0], stream), torch.matmul(Ku, qu, out=res), ev.record(e[1], stream)))
+        eb = torch.finfo(kdt).bits // 8
+        lb = units * T * (w.d + G) * eb
+        logits[name] = {"call_us": round(call, 2), "gbs": round(lb / (call * 1e-6) / 1e9, 1)}
+        del Ku, qu, res
+    base = logits["fp32_keys"]["call_us"]
+    for k in ("packed_3bit_keys", "packed_4bit_keys"):
+        logits[k]["speedup_vs_fp32_keys"] = round(base / logits[k]["call_us"], 2)
+        logits[k]["speedup_vs_bf16_keys"] = round(logits["bf16_keys"]["call_us"] / logits[k]["call_us"], 2)
+    return {"workload": ("long_context shape (4 x 8 units x 131072 tokens, 8 q-heads per kv-head, d 128), "
+                         "3-bit values; medians over %d calls" % reps),
+            "decode": decode, "logits": logits}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +384,12 @@ def main():
         del src, dst
         log(f"[bench] streaming copy (elementwise neg, {n} bytes in + out): {stream_gbs:.0f} GB/s")
 
+    widths = None
+    if not args.no_search:
+        log("[bench] key bit-width variants and logits-only ...")
+        widths = key_width_bench(tq, W, w, K, V, q, dev, ev, stream)
+        log(f"[bench] key widths {widths}")
+
     search = None
     if not args.no_search:
         log("[bench] vector search workload ...")
@@ -360,6 +443,7 @@ def main():
             "measured_stream_copy_gbs": None if stream_gbs is None else round(stream_gbs, 1),
         },
         "cpu_baseline": base,
+        "key_widths": widths,
         "search": search,
     }
     print(json.dumps(rec), flush=True)

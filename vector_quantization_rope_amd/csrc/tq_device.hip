@@ -1896,7 +1896,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
 // Attention logits only (tq_decode_attend with out = NULL): the key-score half of
 // k_decode_lds, for the same key formats and query digit rows, writing the unscaled
 // estimates.  With no value stream to stage, each lane loads its own token's key words
-// (its half of every plane and of the signs) and norms straight into registers one tile
+// (its half of every plane and of the signs) and norms straight into registers two tiles
 // ahead; 4 waves per block, wave w taking tiles w, w + 4, ... of the block's chunk.
 template <int D, int KBITS>
 __global__ __launch_bounds__(256) void k_logits(MfmaArgs a) {
@@ -1943,15 +1943,20 @@ __global__ __launch_bounds__(256) void k_logits(MfmaArgs a) {
     }
     nr = a.knorm[ubase + tc];
   };
-  uint2 kwn[KBITS + 1];
-  uint32_t nrn = 0u;
+  uint2 kwn[KBITS + 1], kwm[KBITS + 1];   // tiles k + 1 and k + 2 in flight
+  uint32_t nrn = 0u, nrm = 0u;
   if (nk > 0) load(0, kwn, nrn);
+  if (nk > 1) load(1, kwm, nrm);
   for (int k = 0; k < nk; ++k) {
     uint2 kw[KBITS + 1];
 #pragma unroll
-    for (int pp = 0; pp <= KBITS; ++pp) kw[pp] = kwn[pp];
+    for (int pp = 0; pp <= KBITS; ++pp) {
+      kw[pp] = kwn[pp];
+      kwn[pp] = kwm[pp];
+    }
     const uint32_t nr = nrn;
-    if (k + 1 < nk) load(k + 1, kwn, nrn);
+    nrn = nrm;
+    if (k + 2 < nk) load(k + 2, kwm, nrm);
     uint2 pl[NP + 1];
 #pragma unroll
     for (int pp = 0; pp < KBITS; ++pp) pl[pp] = kw[pp];
