@@ -25,7 +25,10 @@ Sources (titles of the pages; sections as they appear there):
               Lloyd-Max boundaries/reconstruction values and per-dimension coding,
               "Performances en recherche vectorielle" (recall 1@k, top-k search).
   [NSNQuant]  "NSNQuant ..." technical summary section 2 (randomized Hadamard
-              transform) -- cited for the choice of a seeded-sign Hadamard rotation.
+              transform) -- cited for the choice of a seeded-sign Hadamard rotation;
+              section 4 (implementation details, residuals: the cache is a quantized
+              part plus a full-precision residual that is quantized and appended once
+              full) -- attention over packed tokens and a full-precision window.
 
 Readings where the pages are silent (each is also listed in the design doc):
   * PRNG: SplitMix64 (Steele, Lea & Flood 2014) used as a counter-based generator;
@@ -55,7 +58,7 @@ __all__ = [
     "sphere_marginal_cdf", "sphere_marginal_pdf", "sphere_partial_mean", "lloyd_max",
     "Codebook", "make_codebook", "hadamard", "rotation_matrix", "rope",
     "fp16_sat", "Codec", "make_codec", "encode", "pack_cache", "unpack_cache",
-    "cache_layout", "attend", "search_scores", "topk", "exact_topk",
+    "cache_layout", "attend", "attend_window", "search_scores", "topk", "exact_topk",
 ]
 
 _GOLDEN_GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -520,6 +523,57 @@ def attend(fields: dict, q, codec: Codec, *, q_pos: int, rope_base: float, scale
             vhat = fields["vn16"][b, g, :length, None] * codec.cb_v.c[fields["vcodes"][b, g, :length]]
             o_rot = p @ vhat
             out[b, h] = codec.Pi.T @ o_rot
+    return out, scores
+
+
+def attend_window(fields: dict, win_k, win_v, q, codec: Codec, *, q_pos: int, rope_base: float,
+                  scale: float, kv_heads: int, length: int, win_len: int):
+    """fp64 decode attention of q [B, Hq, d] over packed tokens [0, length) of `fields`
+    and a full-precision window of win_len tokens at positions length, ..., length +
+    win_len - 1 ([NSNQuant] section 4, residuals).  win_k, win_v: [B, Hkv, >= win_len, d]
+    raw keys (before RoPE) and values.
+
+    A window token's score is the exact <RoPE(q, q_pos), RoPE(k, pos)>, the rotation
+    being orthogonal ([TurboESM] 2.A); packed tokens use the estimator.  One softmax over
+    both sets; the packed part's value sum is rotated back by Pi^T, the window's values
+    enter as they are.  Returns (out [B, Hq, d], scores [B, Hq, length + win_len])."""
+    q = np.asarray(q, dtype=np.float64)
+    wk = np.asarray(win_k, dtype=np.float64)
+    wv = np.asarray(win_v, dtype=np.float64)
+    B, Hq, d = q.shape
+    n = length + win_len
+    out = np.zeros((B, Hq, d))
+    scores = np.zeros((B, Hq, n))
+    if scale == 0:
+        scale = 1.0 / math.sqrt(d)
+    pos = length + np.arange(win_len)
+    for b in range(B):
+        for h in range(Hq):
+            g = (h * kv_heads) // Hq
+            qp = rope(q[b, h][None, :], [q_pos], rope_base)[0] if rope_base != 0 else q[b, h]
+            qr = codec.Pi @ qp
+            sq = codec.S @ qr if codec.m > 0 else None
+            if n == 0:
+                continue
+            s = np.zeros(n)
+            if length > 0:
+                s[:length] = estimate_scores(qr, sq, fields["kcodes"][b, g, :length],
+                                             fields["n16"][b, g, :length], fields["rn16"][b, g, :length],
+                                             fields["bits"][b, g, :length], codec)
+            if win_len > 0:
+                kr = rope(wk[b, g, :win_len], pos, rope_base) if rope_base != 0 else wk[b, g, :win_len]
+                s[length:] = kr @ qp
+            scores[b, h] = s
+            lam = scale * s
+            p = np.exp(lam - np.max(lam))
+            p = p / np.sum(p)
+            o = np.zeros(d)
+            if length > 0:
+                vhat = fields["vn16"][b, g, :length, None] * codec.cb_v.c[fields["vcodes"][b, g, :length]]
+                o += codec.Pi.T @ (p[:length] @ vhat)
+            if win_len > 0:
+                o += p[length:] @ wv[b, g, :win_len]
+            out[b, h] = o
     return out, scores
 
 

@@ -302,6 +302,51 @@ def test_attend_reduces_to_textbook_softmax_attention(O):
             np.testing.assert_allclose(out[b, h], w @ V, rtol=1e-11, atol=1e-11)
 
 
+def test_attend_window_is_textbook_attention_over_both_sets(O):
+    # packed tokens on the codebook lattice with zero residual (exact estimator) and a
+    # full-precision window after them: the result must be softmax(q K^T scale) V over the
+    # concatenation, with the window keys rotary-embedded at positions length + t, the
+    # packed keys being the stored (already embedded) ones, and GQA mapping.
+    d, B, Hkv, Hq, T, Wn = 64, 2, 2, 4, 23, 9
+    codec = O.make_codec(d, 2, 3, d, seed=5)
+    rng = np.random.default_rng(11)
+    kc = rng.integers(0, 4, (B, Hkv, T, d))
+    vc = rng.integers(0, 8, (B, Hkv, T, d))
+    n16 = rng.uniform(1, 8, (B, Hkv, T)).astype(np.float16).astype(np.float64)
+    vn16 = rng.uniform(1, 8, (B, Hkv, T)).astype(np.float16).astype(np.float64)
+    fields = _fields_from_khat(O, codec, kc, n16, vc, vn16)
+    wk = rng.standard_normal((B, Hkv, Wn + 3, d))
+    wv = rng.standard_normal((B, Hkv, Wn + 3, d)) * 3
+    q = rng.standard_normal((B, Hq, d))
+    q_pos, base, scale = T + Wn, 10000.0, 0.2
+    out, scores = O.attend_window(fields, wk, wv, q, codec, q_pos=q_pos, rope_base=base, scale=scale,
+                                  kv_heads=Hkv, length=T, win_len=Wn)
+    assert scores.shape == (B, Hq, T + Wn)
+    P = codec.Pi
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            Kp = (n16[b, g][:, None] * codec.cb_k.c[kc[b, g]]) @ P
+            Vp = (vn16[b, g][:, None] * codec.cb_v.c[vc[b, g]]) @ P
+            Kw = np.stack([O.rope(wk[b, g, t][None], [T + t], base)[0] for t in range(Wn)])
+            Kall, Vall = np.concatenate([Kp, Kw]), np.concatenate([Vp, wv[b, g, :Wn]])
+            qq = O.rope(q[b, h][None], [q_pos], base)[0]
+            sc = Kall @ qq
+            w = np.exp(scale * sc - np.max(scale * sc))
+            w /= w.sum()
+            np.testing.assert_allclose(scores[b, h], sc, rtol=1e-11, atol=1e-11)
+            np.testing.assert_allclose(out[b, h], w @ Vall, rtol=1e-11, atol=1e-11)
+    # no window: the packed-only attention; no packed tokens: the window alone
+    o0, s0 = O.attend_window(fields, wk, wv, q, codec, q_pos=q_pos, rope_base=base, scale=scale,
+                             kv_heads=Hkv, length=T, win_len=0)
+    o1, s1 = O.attend(fields, q, codec, q_pos=q_pos, rope_base=base, scale=scale, kv_heads=Hkv, length=T)
+    np.testing.assert_allclose(o0, o1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(s0, s1, rtol=1e-12, atol=1e-12)
+    o2, _ = O.attend_window(fields, wk, wv, q, codec, q_pos=q_pos, rope_base=0.0, scale=0.0,
+                            kv_heads=Hkv, length=0, win_len=1)
+    np.testing.assert_allclose(o2[0, 0], wv[0, 0, 0], atol=1e-12)   # one token: its value
+
+
 def test_attend_single_token_and_empty(O):
     d = 64
     codec = O.make_codec(d, 2, 3, d, seed=3)
