@@ -185,6 +185,29 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
                                     int32_t splits, void *ws, size_t ws_bytes,
                                     void *ev_start, void *ev_stop, tq_stream_t stream);
 
+/* Workspace bytes tq_decode_attend_window needs for this shape. */
+size_t tq_decode_window_workspace_bytes(const tq_cache_desc *desc, int32_t q_heads, int32_t length);
+
+/* Decode attention over the packed tokens [0, length) and a full-precision window of the
+ * most recent tokens ([NSNQuant] section 4, implementation details, residuals: the KV
+ * cache is a quantized part plus a full-precision residual, which is quantized and
+ * appended once full).  win_k, win_v: device [batch][kv_heads][win_cap][d] of win_dtype,
+ * the raw keys (before RoPE) and values of positions length, ..., length + win_len - 1 in
+ * slots 0 .. win_len - 1; 0 <= win_len <= win_cap <= 4096, d = 64 or 128, bits_v > 0.
+ * A window token scores exactly <RoPE(q, q_pos), RoPE(k, pos)> (equal to the rotated-basis
+ * product, Pi being orthogonal: [TurboESM] 2.A); one softmax runs over both sets.  out,
+ * scale, q and the rest as tq_decode_attend (out may be NULL for logits only); scores:
+ * NULL or [batch][q_heads][length + win_len], packed tokens first.  ws: at least
+ * tq_decode_window_workspace_bytes bytes.  Flushing a full window into the cache is
+ * tq_quantize_kv(desc, codec, cache, win_k, win_v, win_dtype, length, win_cap, rope_base),
+ * the window buffer being exactly that call's [batch][kv_heads][n_new][d] input. */
+tq_status tq_decode_attend_window(const tq_cache_desc *desc, const void *codec_dev,
+                                  const void *cache_dev, int32_t length, const void *win_k,
+                                  const void *win_v, tq_dtype win_dtype, int32_t win_len,
+                                  int32_t win_cap, const void *q, tq_dtype dtype, int32_t q_heads,
+                                  int32_t q_pos, float rope_base, float scale, float *out,
+                                  float *scores, void *ws, size_t ws_bytes, tq_stream_t stream);
+
 /* Workspace bytes tq_search_topk needs. */
 size_t tq_search_workspace_bytes(const tq_cache_desc *db, int32_t n_db, int32_t nq, int32_t k);
 

@@ -33,9 +33,9 @@ def oracle_encode_unitwise(K, V, codec, positions, rope_base):
                   positions=np.tile(positions, B * H), rope_base=rope_base)
     out = {
         "kcodes": ke["codes"].reshape(B, H, T, d), "n16": ke["n16"].reshape(B, H, T),
-        "rn16": ke["rn16"].reshape(B, H, T), "bits": ke["bits"].reshape(B, H, T, -1),
+        "rn16": ke["rn16"].reshape(B, H, T), "bits": ke["bits"].reshape(B, H, T, codec.m),
         "ku": ke["u"].reshape(B, H, T, d), "kn": ke["n"].reshape(B, H, T),
-        "krn": ke["rn"].reshape(B, H, T), "kz": ke["z"].reshape(B, H, T, -1),
+        "krn": ke["rn"].reshape(B, H, T), "kz": ke["z"].reshape(B, H, T, codec.m),
         "overflow": ke["overflow"].reshape(B, H, T),
     }
     if V is not None:

@@ -177,6 +177,68 @@ def test_logits_only(tq, P, bk, bv, d, G, T):
     assert e <= TOL and e_full <= 1e-6 * max(1.0, float(np.abs(full).max()))
 
 
+@pytest.mark.parametrize("bk,bv,d,G,L,Wn,cap,dt", [
+    (2, 3, 128, 8, 700, 45, 64, "bf16"),   # MFMA path, partial window
+    (3, 3, 64, 2, 300, 64, 64, "bf16"),    # full window
+    (2, 3, 128, 4, 0, 100, 128, "bf16"),   # window only
+    (2, 3, 64, 4, 257, 0, 32, "bf16"),     # empty window
+    (1, 3, 64, 8, 130, 200, 256, "f32"),   # fp32 inputs, window longer than the packed part
+    (3, 4, 128, 4, 190, 70, 80, "f32"),    # fp32 decode path
+])
+def test_window_attention(tq, P, bk, bv, d, G, L, Wn, cap, dt):
+    """Packed tokens [0, L) plus a full-precision window of Wn raw tokens (NSNQuant's
+    residual): outputs and scores against the oracle over the same packed fields; logits
+    only; and, for a full window, the flush through tq_quantize_kv."""
+    T = L + Wn
+    w = W.LONG_CONTEXT.scaled(batch=2, kv_heads=2, q_heads=2 * G, d=d, m=d, context=T, bits_k=bk, bits_v=bv,
+                              dtype=dt)
+    K, V = W.gen_kv(w)
+    q = W.gen_q(w)
+    codec_o = O.make_codec(d, bk, bv, d, 0)
+    Kd, Vd = P.to_f64(K), P.to_f64(V)
+    fields = P.oracle_encode_unitwise(Kd[:, :, :L], Vd[:, :, :L], codec_o, np.arange(L), w.rope_base)
+    out_o, sc_o = O.attend_window(fields, Kd[:, :, L:], Vd[:, :, L:], P.to_f64(q), codec_o, q_pos=w.q_pos,
+                                  rope_base=w.rope_base, scale=0.0, kv_heads=w.kv_heads, length=L, win_len=Wn)
+    codec = tq.Codec(d, bk, bv, d, seed=0)
+    cap_t = max(T, 1)
+    cache = tq.PackedCache(w.batch, w.kv_heads, d, cap_t, bk, bv, d)
+    if L > 0:
+        cache.buf.copy_(torch.from_numpy(P.oracle_image(cache.desc.as_dict(), fields)))
+    wk = torch.zeros((w.batch, w.kv_heads, cap, d), dtype=K.dtype)
+    wv = torch.zeros_like(wk)
+    wk[:, :, :Wn] = K[:, :, L:]
+    wv[:, :, :Wn] = V[:, :, L:]
+    wk, wv = wk.cuda(), wv.cuda()
+    B, Hq = q.shape[0], q.shape[1]
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+    sc = torch.full((B, Hq, max(T, 1)), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tq.decode_window_workspace_bytes(cache.desc, Hq, L), dtype=torch.uint8, device="cuda")
+    tq.decode_attend_window(cache.desc, codec.dev, cache.buf, L, wk, wv, Wn, q.cuda(), w.q_pos, w.rope_base,
+                            out, scores=sc, ws=ws)
+    torch.cuda.synchronize()
+    e_out = P.max_abs(out.cpu().numpy(), out_o)
+    e_sc = P.max_abs(sc.cpu().numpy()[:, :, :T], sc_o)
+    # logits only
+    sc2 = torch.full_like(sc, float("nan"))
+    tq.decode_attend_window(cache.desc, codec.dev, cache.buf, L, wk, wv, Wn, q.cuda(), w.q_pos, w.rope_base,
+                            None, scores=sc2, ws=ws)
+    torch.cuda.synchronize()
+    e_lg = P.max_abs(sc2.cpu().numpy()[:, :, :T], sc_o)
+    say(f"    window k{bk} v{bv} d{d} G{G} L{L} W{Wn} {dt}: out {e_out:.2e} scores {e_sc:.2e} logits-only {e_lg:.2e}")
+    assert e_out <= TOL and e_sc <= TOL and e_lg <= TOL
+    if Wn == cap and L > 0:
+        # flush the full window into the packed cache, then a plain decode over L + Wn
+        # tokens matches the oracle over the GPU-encoded cache
+        tq.quantize_kv(cache.desc, codec.dev, cache.buf, wk, wv, L, w.rope_base)
+        out3, _ = decode(tq, codec, cache, q.cuda(), T, w.q_pos, w.rope_base, want_scores=False)
+        g = P.gpu_fields(cache, T)
+        o3, _ = O.attend(g, P.to_f64(q), codec_o, q_pos=w.q_pos, rope_base=w.rope_base, scale=0.0,
+                         kv_heads=w.kv_heads, length=T)
+        e3 = P.max_abs(out3.cpu().numpy(), o3)
+        say(f"    after flush: out {e3:.2e}")
+        assert e3 <= TOL
+
+
 @pytest.mark.parametrize("bk,bv,m", [(1, 2, 64), (3, 4, 128), (4, 1, 32), (2, 3, 0)])
 def test_other_bit_widths(tq, P, bk, bv, m):
     w = W.LLAMA3_8B.scaled(batch=1, kv_heads=2, q_heads=4, context=300, bits_k=bk, bits_v=bv, m=m)

@@ -854,7 +854,8 @@ struct DecodeArgs {
   const float *qp;   // prepared queries, row stride qstride
   int qstride;
   float *part;       // [B*Hq][splits][d + 2]
-  float *scores;     // optional [B][Hq][length]
+  float *scores;     // optional [B][Hq][score_stride]
+  int score_stride;  // length, or length + the full-precision window's tokens
 };
 
 constexpr int kDecThreads = 256;
@@ -952,7 +953,7 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_split(DecodeArgs a) {
         if (h < G) {
           // <sq, 2 s - 1> = 2 sum_{s=1} sq - sum sq
           const float score = n16 * dot[h] + rn16 * a.cp.qjl_scale * (2.0f * qj[h] - sumsq[h]);
-          if (a.scores) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.length + t] = score;
+          if (a.scores) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.score_stride + t] = score;
           lam[h] = a.scale * score;
         } else {
           lam[h] = -INFINITY;
@@ -1084,6 +1085,7 @@ struct MfmaArgs {
   float *part;
   float *scores;
   int kbytes, tiles, capacity, length, chunk, splits, kv_heads, q_heads, G;
+  int score_stride;   // row stride of scores: length, or length + the window's tokens
   float scale_log2, inv_scale_log2;
 };
 
@@ -1781,7 +1783,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * half + r;
-        if (valid && h < a.G) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.length + t] = lam[r] * a.inv_scale_log2;
+        if (valid && h < a.G) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.score_stride + t] = lam[r] * a.inv_scale_log2;
       }
     }
     // ---- online softmax (log2 domain); tile maxima and running maxima are wave-uniform.
@@ -1986,12 +1988,168 @@ __global__ __launch_bounds__(256) void k_logits(MfmaArgs a) {
       const float sc = fmaf(n16, fmaf(coef_s[half][1][r], S01, coef_s[half][0][r]),
                             rn16 * fmaf(coef_s[half][3][r], S2, -coef_s[half][4][r]));
       const int h = 4 * half + r;
-      if (t < t_end && h < a.G) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.length + t] = sc;
+      if (t < t_end && h < a.G) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.score_stride + t] = sc;
     }
   }
 #else
   (void)a;
 #endif
+}
+
+// ------------------------------------------------------------------ full-precision window
+// The recent tokens not yet packed ([NSNQuant] section 4, residuals: a quantized part plus
+// a full-precision residual that is quantized and appended once full).  One block per
+// (batch, kv-head) unit scores its G q-heads against the window exactly,
+// <RoPE(q, q_pos), RoPE(k, pos)> (the rotation Pi being orthogonal, the same score as in
+// the rotated basis, [TurboESM] 2.A), runs the online softmax over 64-token chunks,
+// accumulates the raw values, rotates the sum once by Pi and stores it as one more split
+// partial (max, sum, acc) for the merge, which then weighs it against the packed splits.
+struct WindowArgs {
+  const void *k, *v;          // [batch][kv_heads][cap][d] of dtype: raw keys, values
+  const void *q;              // [batch][q_heads][d] of qdtype
+  const float *Dsg;           // rotation signs
+  float *part;                // [B*Hq][splits_total][d + 2]
+  float *scores;              // optional [B][Hq][score_stride]
+  int dtype, qdtype, len, cap, length, q_pos, kv_heads, q_heads, G;
+  int splits_total, split_idx, score_stride;
+  float rope_base, scale_log2, inv_sqrt_block;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void k_window(WindowArgs a) {
+  constexpr int H2 = D / 2, CH = 64, RS = D + 1;   // padded rows: conflict-free column reads
+  constexpr int NGRP = 256 / H2, TPG = CH / NGRP;   // RoPE: token groups per pair index
+  constexpr int HS = 256 / D, HPT = (kMaxG + HS - 1) / HS;   // value phase: heads per thread
+  __shared__ float qr[kMaxG][D];
+  __shared__ float kr[CH * RS];
+  __shared__ float vr[CH * RS];
+  __shared__ float ps[kMaxG][CH];
+  __shared__ float mstat[3][kMaxG];   // running max (log2 units), sum, this chunk's rescale
+  const int tid = threadIdx.x, unit = blockIdx.x;
+  const int b = unit / a.kv_heads, g = unit % a.kv_heads, G = a.G, hq0 = g * G;
+  const bool rope = a.rope_base != 0.0f;
+  // fp64 frequency of this thread's pair index (the keys' RoPE steps token by token)
+  const int jp = tid % H2, grp = tid / H2;
+  const double theta = rope ? pow(double(a.rope_base), -2.0 * double(jp) / double(D)) : 0.0;
+  double sd = 0.0, cd = 1.0;
+  if (rope) sincos(theta, &sd, &cd);
+  // RoPE(q) of the unit's heads, unrotated
+  for (int i = tid; i < G * H2; i += 256) {
+    const int h = i / H2, j = i % H2;
+    const size_t base = (size_t(b) * a.q_heads + hq0 + h) * D;
+    const float x0 = load_elem(a.q, base + j, a.qdtype), x1 = load_elem(a.q, base + j + H2, a.qdtype);
+    if (rope) {
+      const double th = pow(double(a.rope_base), -2.0 * double(j) / double(D));
+      double sn, c;
+      sincos(double(a.q_pos) * th, &sn, &c);
+      qr[h][j] = x0 * float(c) - x1 * float(sn);
+      qr[h][j + H2] = x0 * float(sn) + x1 * float(c);
+    } else {
+      qr[h][j] = x0;
+      qr[h][j + H2] = x1;
+    }
+  }
+  if (tid < kMaxG) {
+    mstat[0][tid] = -INFINITY;
+    mstat[1][tid] = 0.0f;
+  }
+  const int jv = tid % D, hs = tid / D;
+  float acc[HPT];
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) acc[k] = 0.0f;
+  const size_t ubase = size_t(unit) * a.cap;
+  for (int c0 = 0; c0 < a.len; c0 += CH) {
+    const int cn = min(CH, a.len - c0);
+    __syncthreads();   // the previous chunk's readers are done
+    {
+      // keys: pair jp of tokens grp * TPG .. + TPG, angles stepped from one fp64 sincos
+      const int t0 = grp * TPG;
+      double sn = 0.0, c = 1.0;
+      if (rope) sincos(double(a.length + c0 + t0) * theta, &sn, &c);
+      for (int i = 0; i < TPG; ++i) {
+        const int t = t0 + i;
+        if (t < cn) {
+          const size_t base = (ubase + c0 + t) * D;
+          const float x0 = load_elem(a.k, base + jp, a.dtype), x1 = load_elem(a.k, base + jp + H2, a.dtype);
+          kr[t * RS + jp] = x0 * float(c) - x1 * float(sn);
+          kr[t * RS + jp + H2] = x0 * float(sn) + x1 * float(c);
+        }
+        const double cn2 = c * cd - sn * sd;
+        sn = sn * cd + c * sd;
+        c = cn2;
+      }
+    }
+    for (int i = tid; i < cn * D; i += 256) {
+      const int t = i / D, j = i % D;
+      vr[t * RS + j] = load_elem(a.v, (ubase + c0 + t) * D + j, a.dtype);
+    }
+    __syncthreads();
+    for (int i = tid; i < G * CH; i += 256) {
+      const int h = i / CH, t = i % CH;
+      if (t < cn) {
+        float sdot = 0.0f;
+#pragma unroll 8
+        for (int j = 0; j < D; ++j) sdot = fmaf(qr[h][j], kr[t * RS + j], sdot);
+        ps[h][t] = sdot;
+        if (a.scores) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.score_stride + a.length + c0 + t] = sdot;
+      }
+    }
+    __syncthreads();
+    if (tid < G) {
+      const int h = tid;
+      float cmax = -INFINITY;
+      for (int t = 0; t < cn; ++t) cmax = fmaxf(cmax, ps[h][t] * a.scale_log2);
+      const float mold = mstat[0][h], mnew = fmaxf(mold, cmax);
+      const float alpha = mold == -INFINITY ? 0.0f : exp2f(mold - mnew);
+      float l = mstat[1][h] * alpha;
+      for (int t = 0; t < cn; ++t) {
+        const float pt = exp2f(ps[h][t] * a.scale_log2 - mnew);
+        ps[h][t] = pt;
+        l += pt;
+      }
+      mstat[0][h] = mnew;
+      mstat[1][h] = l;
+      mstat[2][h] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+      const int h = hs + k * HS;
+      if (h < G) {
+        float o = acc[k] * mstat[2][h];
+        for (int t = 0; t < cn; ++t) o = fmaf(ps[h][t], vr[t * RS + jv], o);
+        acc[k] = o;
+      }
+    }
+  }
+  __syncthreads();
+  // Pi acc = H (D .* acc) / sqrt(B) per head (Hadamard block = d here), then the partial
+  float *ys = kr;   // [kMaxG][D]
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) {
+    const int h = hs + k * HS;
+    if (h < G) ys[h * D + jv] = acc[k] * a.Dsg[jv];
+  }
+  __syncthreads();
+  for (int st = 1; st < D; st <<= 1) {
+    for (int i = tid; i < G * H2; i += 256) {
+      const int h = i / H2, kk = i % H2;
+      const int j = (kk / st) * 2 * st + (kk % st);
+      const float x0 = ys[h * D + j], x1 = ys[h * D + j + st];
+      ys[h * D + j] = x0 + x1;
+      ys[h * D + j + st] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < G * D; i += 256) {
+    const int h = i / D, j = i % D;
+    float *o = a.part + ((size_t(b) * a.q_heads + hq0 + h) * a.splits_total + a.split_idx) * (D + 2);
+    o[j] = ys[h * D + j] * a.inv_sqrt_block;
+    if (j == 0) {
+      o[D] = mstat[0][h] * 0.69314718055994531f;   // natural-log units, as the packed splits
+      o[D + 1] = mstat[1][h];
+    }
+  }
 }
 
 // Merge of the splits and inverse rotation: out = D .* (H o) / sqrt(B) = Pi^T o.
@@ -2574,6 +2732,7 @@ constexpr int kMfmaChunk = 32 * kDecWaves;   // tokens per block iteration (one 
 
 constexpr int kDecodeBlocks = 256 * kDecBlocksPerCU;   // MI355X: 256 CUs
 constexpr int kLogitsBlocks = 1024;                    // logits-only kernel: 4 blocks per CU
+constexpr int kMaxWindow = 4096;                      // full-precision window capacity
 
 int default_splits(const tq_cache_desc &c, int length) {
   if (length <= 0) return 1;
@@ -2725,12 +2884,20 @@ size_t tq_decode_workspace_bytes(const tq_cache_desc *desc, int32_t q_heads, int
   return decode_ws(*desc, q_heads, default_splits(*desc, length));
 }
 
-tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec_dev,
-                                    const void *cache_dev, int32_t length, const void *q,
-                                    tq_dtype dtype, int32_t q_heads, int32_t q_pos,
-                                    float rope_base, float scale, float *out, float *scores,
-                                    int32_t splits, void *ws, size_t ws_bytes,
-                                    void *ev_start, void *ev_stop, tq_stream_t stream) {
+namespace {
+struct WindowIn {
+  const void *k, *v;
+  tq_dtype dtype;
+  int len, cap;
+};
+}  // namespace
+
+static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
+                             const void *cache_dev, int32_t length, const WindowIn *win,
+                             const void *q, tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                             float rope_base, float scale, float *out, float *scores,
+                             int32_t splits, void *ws, size_t ws_bytes,
+                             void *ev_start, void *ev_stop, tq_stream_t stream) {
   // out == NULL asks for the logits only (scores required)
   if (!desc || !codec_dev || !cache_dev || !q || (!out && !scores) || !ws) return TQ_EINVAL;
   if (!cache_desc_valid(*desc)) return TQ_EUNSUPPORTED;
@@ -2742,12 +2909,20 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
   if (!std::isfinite(rope_base) || rope_base < 0.0f || !std::isfinite(scale)) return TQ_EINVAL;
   if (!decode_supported(*desc)) return TQ_EUNSUPPORTED;
   if (desc->m > 512) return TQ_EUNSUPPORTED;
+  const int wlen = win ? win->len : 0;
+  if (win) {
+    if (win->len < 0 || win->cap < win->len || win->cap > kMaxWindow) return TQ_EINVAL;
+    if (win->len > 0 && (!win->k || !win->v)) return TQ_EINVAL;
+    if (win->dtype != TQ_F32 && win->dtype != TQ_BF16 && win->dtype != TQ_F16) return TQ_EINVAL;
+    if (desc->d != 64 && desc->d != 128) return TQ_EUNSUPPORTED;
+    if (desc->bits_v == 0) return TQ_EUNSUPPORTED;
+  }
   const int S = splits == 0 ? default_splits(*desc, length) : splits;
-  if (ws_bytes < decode_ws(*desc, q_heads, S)) return TQ_ENOSPACE;
+  if (ws_bytes < decode_ws(*desc, q_heads, S + (win ? 1 : 0))) return TQ_ENOSPACE;
   const int d = desc->d, m = desc->m;
   const int rows = desc->batch * q_heads;
   hipStream_t s = hipStream_t(stream);
-  if (length == 0) {
+  if (length == 0 && wlen == 0) {
     if (!out) return TQ_OK;   // no tokens, no logits
     // a fill kernel rather than a memset node, so the call can be captured in a graph
     const size_t n = size_t(rows) * d;
@@ -2755,6 +2930,7 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
     return launch_status();
   }
   const CodecPtrs cp = codec_ptrs(codec_dev, d, desc->bits_k, desc->bits_v, m);
+  if (win && cp.block != d) return TQ_EUNSUPPORTED;   // the window rotates with one d-point block
   float *qp = static_cast<float *>(ws);
   const int qstride = d + m + 2;
   const int units = desc->batch * desc->kv_heads;
@@ -2765,6 +2941,10 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
   const bool mfma = decode_mfma_path(*desc, q_heads);
   // odd key codebook on the MFMA path: c[code] = c0 + a weighted sum of bit planes
   const int bk = desc->bits_k;
+  const int wsplit = wlen > 0 ? 1 : 0;   // the window's partial follows the packed splits
+  const int score_stride = length + wlen;
+  int used_splits = 0;
+  if (length > 0) {
   if (d == m && (d == 64 || d == 128) && cp.block == d) {
     if (d == 64)
       hipLaunchKernelGGL(k_qprep_fast<64>, dim3(rows), dim3(256), 0, s, q, int(dtype), q_pos, rope_base, cp, qp,
@@ -2777,7 +2957,7 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
                        int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, bk, mfma ? qpack : nullptr);
   }
   const CachePtrs ch = cache_ptrs(const_cast<void *>(cache_dev), *desc);
-  int used_splits = S;
+  used_splits = S;
   if (mfma) {
     const int chunk = split_chunk(length, S);
     used_splits = (length + chunk - 1) / chunk;
@@ -2795,7 +2975,8 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
     ma.capacity = desc->capacity;
     ma.length = length;
     ma.chunk = chunk;
-    ma.splits = used_splits;
+    ma.splits = used_splits + wsplit;
+    ma.score_stride = score_stride;
     ma.kv_heads = desc->kv_heads;
     ma.q_heads = q_heads;
     ma.G = G;
@@ -2808,8 +2989,8 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
       ls = std::max(1, std::min(ls, by_len));
       const int lchunk = ((length + ls - 1) / ls + 127) / 128 * 128;
       ma.chunk = lchunk;
-      ma.splits = (length + lchunk - 1) / lchunk;
-      const dim3 lgrid(units, ma.splits);
+      const int lsplits = (length + lchunk - 1) / lchunk;
+      const dim3 lgrid(units, lsplits);
       if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
       if (d == 64) {
         if (bk == 1) hipLaunchKernelGGL((k_logits<64, 1>), lgrid, dim3(256), 0, s, ma);
@@ -2821,8 +3002,9 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
         if (bk == 3) hipLaunchKernelGGL((k_logits<128, 3>), lgrid, dim3(256), 0, s, ma);
       }
       if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
-      return launch_status();
+      used_splits = 0;   // no partials: only the window (if any) still writes scores
     }
+    if (out) {
     dim3 grid(units, used_splits);
     if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
     const dim3 blk(64 * kDecWaves);
@@ -2836,6 +3018,7 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
       if (bk == 3) hipLaunchKernelGGL((k_decode_lds<128, 3>), grid, blk, 0, s, ma);
     }
     if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
+    }
   } else {
     DecodeArgs a;
     a.cp = cp;
@@ -2853,8 +3036,9 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
     a.q_heads = q_heads;
     a.G = G;
     a.length = length;
-    a.splits = S;
+    a.splits = S + wsplit;
     a.chunk = (length + S - 1) / S;
+    a.score_stride = score_stride;
     a.scale = sc;
     a.qp = qp;
     a.qstride = qstride;
@@ -2869,8 +3053,38 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
     else
       hipLaunchKernelGGL(k_decode_split<128>, grid, dim3(kDecThreads), shm, s, a);
     if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
-    if (!out) return launch_status();   // logits only: the scores are written, no merge
   }
+  }   // length > 0
+  if (wlen > 0) {
+    WindowArgs wa;
+    wa.k = win->k;
+    wa.v = win->v;
+    wa.q = q;
+    wa.Dsg = cp.D;
+    wa.part = part;
+    wa.scores = scores;
+    wa.dtype = int(win->dtype);
+    wa.qdtype = int(dtype);
+    wa.len = wlen;
+    wa.cap = win->cap;
+    wa.length = length;
+    wa.q_pos = q_pos;
+    wa.kv_heads = desc->kv_heads;
+    wa.q_heads = q_heads;
+    wa.G = G;
+    wa.splits_total = used_splits + 1;
+    wa.split_idx = used_splits;
+    wa.score_stride = score_stride;
+    wa.rope_base = rope_base;
+    wa.scale_log2 = sc * 1.4426950408889634f;
+    wa.inv_sqrt_block = cp.inv_sqrt_block;
+    if (d == 64)
+      hipLaunchKernelGGL(k_window<64>, dim3(units), dim3(256), 0, s, wa);
+    else
+      hipLaunchKernelGGL(k_window<128>, dim3(units), dim3(256), 0, s, wa);
+  }
+  if (!out) return launch_status();   // logits only: the scores are written, no merge
+  used_splits += wsplit;
   if ((d == 64 || d == 128) && cp.block == d) {
     const dim3 mg(unsigned((rows + 3) / 4));
     if (d == 64)
@@ -2882,6 +3096,32 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
                        used_splits, d, cp, out);
   }
   return launch_status();
+}
+
+tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec_dev,
+                                    const void *cache_dev, int32_t length, const void *q,
+                                    tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                                    float rope_base, float scale, float *out, float *scores,
+                                    int32_t splits, void *ws, size_t ws_bytes,
+                                    void *ev_start, void *ev_stop, tq_stream_t stream) {
+  return decode_impl(desc, codec_dev, cache_dev, length, nullptr, q, dtype, q_heads, q_pos, rope_base,
+                     scale, out, scores, splits, ws, ws_bytes, ev_start, ev_stop, stream);
+}
+
+size_t tq_decode_window_workspace_bytes(const tq_cache_desc *desc, int32_t q_heads, int32_t length) {
+  if (!desc || !cache_desc_valid(*desc) || q_heads < 1 || length < 0) return 0;
+  return decode_ws(*desc, q_heads, default_splits(*desc, length) + 1);
+}
+
+tq_status tq_decode_attend_window(const tq_cache_desc *desc, const void *codec_dev,
+                                  const void *cache_dev, int32_t length, const void *win_k,
+                                  const void *win_v, tq_dtype win_dtype, int32_t win_len,
+                                  int32_t win_cap, const void *q, tq_dtype dtype, int32_t q_heads,
+                                  int32_t q_pos, float rope_base, float scale, float *out,
+                                  float *scores, void *ws, size_t ws_bytes, tq_stream_t stream) {
+  const WindowIn w{win_k, win_v, win_dtype, win_len, win_cap};
+  return decode_impl(desc, codec_dev, cache_dev, length, &w, q, dtype, q_heads, q_pos, rope_base, scale,
+                     out, scores, 0, ws, ws_bytes, nullptr, nullptr, stream);
 }
 
 tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_dev,

@@ -30,7 +30,7 @@ EXPORTS = [
     "tq_decode_workspace_bytes", "tq_decode_splits", "tq_decode_attend",
     "tq_decode_workspace_bytes_splits", "tq_decode_attend_splits",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_quantize_kv_profiled",
-    "tq_decode_attend_profiled",
+    "tq_decode_attend_profiled", "tq_decode_window_workspace_bytes", "tq_decode_attend_window",
 ]
 
 
@@ -83,6 +83,10 @@ _quantize_kv_prof = _sig("tq_quantize_kv_profiled", ctypes.c_int,
                          [_KD, _P, _P, _P, _P, ctypes.c_int, _I, _I, _F, _P, _P, _P])
 _decode_attend_prof = _sig("tq_decode_attend_profiled", ctypes.c_int,
                            [_KD, _P, _P, _I, _P, ctypes.c_int, _I, _I, _F, _F, _P, _P, _I, _P, _S, _P, _P, _P])
+_decode_win_ws = _sig("tq_decode_window_workspace_bytes", _S, [_KD, _I, _I])
+_decode_attend_win = _sig("tq_decode_attend_window", ctypes.c_int,
+                          [_KD, _P, _P, _I, _P, _P, ctypes.c_int, _I, _I, _P, ctypes.c_int, _I, _I, _F, _F,
+                           _P, _P, _P, _S, _P])
 _search_ws = _sig("tq_search_workspace_bytes", _S, [_KD, _I, _I, _I])
 _search_topk = _sig("tq_search_topk", ctypes.c_int,
                     [_KD, _P, _P, _I, _P, _I, _I, _P, _P, _P, _S, _P])
@@ -201,6 +205,35 @@ def decode_attend(desc: CacheDesc, codec_dev, cache, length: int, q, q_pos: int,
                                float(scale), _ptr(out), _ptr(scores), int(splits), _ptr(ws),
                                int(ws_bytes), ev0, ev1, _stream(stream)),
            "tq_decode_attend")
+
+
+def decode_window_workspace_bytes(desc: CacheDesc, q_heads: int, length: int) -> int:
+    return _decode_win_ws(ctypes.byref(desc), q_heads, length)
+
+
+def decode_attend_window(desc: CacheDesc, codec_dev, cache, length: int, win_k, win_v, win_len: int, q,
+                         q_pos: int, rope_base: float, out, scores=None, ws=None, scale: float = 0.0,
+                         stream=None, ws_bytes: int | None = None):
+    """win_k, win_v: [batch, kv_heads, cap, d] raw keys and values of positions length ...
+    length + win_len - 1 (contiguous, one dtype); scores, if given, rows of length + win_len."""
+    q_heads = int(q.shape[1])
+    if win_k is None or win_v is None:
+        raise ValueError("decode_attend_window: window tensors required (win_len may be 0)")
+    want = (desc.batch, desc.kv_heads, int(win_k.shape[2]), desc.d)
+    for t in (win_k, win_v):
+        if t.dim() != 4 or tuple(t.shape) != want or not t.is_contiguous() or t.dtype != win_k.dtype:
+            raise ValueError(f"decode_attend_window: window tensors must be contiguous {want} of one dtype")
+    if not 0 <= win_len <= int(win_k.shape[2]):
+        raise ValueError("decode_attend_window: win_len outside [0, cap]")
+    if scores is not None and scores.numel() < desc.batch * q_heads * (length + win_len):
+        raise ValueError("decode_attend_window: scores smaller than batch x q_heads x (length + win_len)")
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_decode_attend_win(ctypes.byref(desc), _ptr(codec_dev), _ptr(cache), int(length), _ptr(win_k),
+                              _ptr(win_v), _dtype_code(win_k), int(win_len), int(win_k.shape[2]), _ptr(q),
+                              _dtype_code(q), q_heads, int(q_pos), float(rope_base), float(scale), _ptr(out),
+                              _ptr(scores), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "tq_decode_attend_window")
 
 
 def search_workspace_bytes(desc: CacheDesc, n_db: int, nq: int, k: int) -> int:
