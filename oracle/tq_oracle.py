@@ -58,7 +58,7 @@ __all__ = [
     "sphere_marginal_cdf", "sphere_marginal_pdf", "sphere_partial_mean", "lloyd_max",
     "Codebook", "make_codebook", "hadamard", "rotation_matrix", "rope",
     "fp16_sat", "Codec", "make_codec", "encode", "pack_cache", "unpack_cache",
-    "cache_layout", "attend", "attend_window", "search_scores", "topk", "exact_topk",
+    "cache_layout", "attend", "attend_window", "decode_step", "search_scores", "topk", "exact_topk",
 ]
 
 _GOLDEN_GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -575,6 +575,45 @@ def attend_window(fields: dict, win_k, win_v, q, codec: Codec, *, q_pos: int, ro
                 o += p[length:] @ wv[b, g, :win_len]
             out[b, h] = o
     return out, scores
+
+
+_ATTEND_FIELDS = ("kcodes", "n16", "rn16", "bits", "vcodes", "vn16")
+
+
+def decode_step(state: dict, new_k, new_v, q, codec: Codec, *, q_pos: int, rope_base: float,
+                scale: float, kv_heads: int):
+    """One generation step over a packed part and a full-precision window ([NSNQuant]
+    section 4, residuals: recent tokens stay unquantized in a residual buffer, which is
+    quantized and appended to the packed part once it is full).
+
+    state (updated in place): "fields" (packed tokens, [B, Hkv, length, ...] arrays as for
+    attend), "length", "win_k", "win_v" ([B, Hkv, cap, d] raw keys and values), "win_len".
+    new_k, new_v: [B, Hkv, d], the keys and values of position length + win_len.
+
+    Reading (the pages do not fix the moment of the flush): a window holding cap tokens is
+    flushed when the next token needs its room, so attention always sees between 1 and
+    cap full-precision tokens; the flushed keys are rotary-embedded at their own
+    positions.  Returns attend_window's (out, scores) after the append."""
+    wk, wv = state["win_k"], state["win_v"]
+    B, H, cap, d = wk.shape
+    if state["win_len"] == cap:
+        pos = state["length"] + np.arange(cap)
+        ke = encode(wk.reshape(-1, d), codec, kind="key", positions=np.tile(pos, B * H), rope_base=rope_base)
+        ve = encode(wv.reshape(-1, d), codec, kind="value")
+        new = {"kcodes": ke["codes"].reshape(B, H, cap, d), "n16": ke["n16"].reshape(B, H, cap),
+               "rn16": ke["rn16"].reshape(B, H, cap), "bits": ke["bits"].reshape(B, H, cap, codec.m),
+               "vcodes": ve["codes"].reshape(B, H, cap, d), "vn16": ve["n16"].reshape(B, H, cap)}
+        old = state["fields"]
+        state["fields"] = {f: np.concatenate([np.asarray(old[f])[:, :, :state["length"]], new[f]], axis=2)
+                           for f in _ATTEND_FIELDS}
+        state["length"] += cap
+        state["win_len"] = 0
+    w = state["win_len"]
+    wk[:, :, w] = np.asarray(new_k, dtype=np.float64)
+    wv[:, :, w] = np.asarray(new_v, dtype=np.float64)
+    state["win_len"] = w + 1
+    return attend_window(state["fields"], wk, wv, q, codec, q_pos=q_pos, rope_base=rope_base, scale=scale,
+                         kv_heads=kv_heads, length=state["length"], win_len=state["win_len"])
 
 
 # ----------------------------------------------------------------------------------

@@ -347,6 +347,59 @@ def test_attend_window_is_textbook_attention_over_both_sets(O):
     np.testing.assert_allclose(o2[0, 0], wv[0, 0, 0], atol=1e-12)   # one token: its value
 
 
+def _encode_fields(O, codec, K, V, base):
+    B, H, T, d = K.shape
+    ke = O.encode(K.reshape(-1, d), codec, kind="key", positions=np.tile(np.arange(T), B * H), rope_base=base)
+    ve = O.encode(V.reshape(-1, d), codec, kind="value")
+    return {"kcodes": ke["codes"].reshape(B, H, T, d), "n16": ke["n16"].reshape(B, H, T),
+            "rn16": ke["rn16"].reshape(B, H, T), "bits": ke["bits"].reshape(B, H, T, codec.m),
+            "vcodes": ve["codes"].reshape(B, H, T, d), "vn16": ve["n16"].reshape(B, H, T)}
+
+
+def test_decode_step_flush_schedule(O):
+    # A generation loop through decode_step against a closed form of its schedule: with L0
+    # tokens packed up front and a window of cap, after step s (0-based) the packed part
+    # holds L0 + cap * floor(s / cap) tokens and the window the other s % cap + 1, all
+    # encoded at their own positions.  Checked by one-shot encoding of that prefix and
+    # attend_window over the raw rest; with no flush yet, also against textbook attention.
+    d, B, Hkv, Hq, L0, cap, steps = 64, 1, 2, 4, 5, 4, 11
+    codec = O.make_codec(d, 2, 3, d, seed=9)
+    rng = np.random.default_rng(21)
+    K = rng.standard_normal((B, Hkv, L0 + steps, d))
+    V = rng.standard_normal((B, Hkv, L0 + steps, d))
+    base, scale = 10000.0, 0.0
+    st = {"fields": _encode_fields(O, codec, K[:, :, :L0], V[:, :, :L0], base), "length": L0,
+          "win_k": np.zeros((B, Hkv, cap, d)), "win_v": np.zeros((B, Hkv, cap, d)), "win_len": 0}
+    for s in range(steps):
+        n = L0 + s + 1
+        q = rng.standard_normal((B, Hq, d))
+        out, sc = O.decode_step(st, K[:, :, n - 1], V[:, :, n - 1], q, codec, q_pos=n - 1, rope_base=base,
+                                scale=scale, kv_heads=Hkv)
+        P = L0 + cap * (s // cap)
+        assert (st["length"], st["win_len"]) == (P, n - P)
+        ref = _encode_fields(O, codec, K[:, :, :P], V[:, :, :P], base)
+        for f in ref:
+            np.testing.assert_array_equal(st["fields"][f], ref[f])
+        o2, s2 = O.attend_window(ref, K[:, :, P:n], V[:, :, P:n], q, codec, q_pos=n - 1, rope_base=base,
+                                 scale=scale, kv_heads=Hkv, length=P, win_len=n - P)
+        np.testing.assert_allclose(out, o2, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(sc, s2, rtol=0, atol=1e-12)
+    # no packed tokens and a window that never fills: exact softmax attention over RoPE'd keys
+    st = {"fields": _encode_fields(O, codec, K[:, :, :0], V[:, :, :0], base), "length": 0,
+          "win_k": np.zeros((B, Hkv, 8, d)), "win_v": np.zeros((B, Hkv, 8, d)), "win_len": 0}
+    for t in range(6):
+        q = rng.standard_normal((B, Hq, d))
+        out, _ = O.decode_step(st, K[:, :, t], V[:, :, t], q, codec, q_pos=t, rope_base=base, scale=0.0,
+                               kv_heads=Hkv)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        kr = O.rope(K[0, g, :6], np.arange(6), base)
+        qq = O.rope(q[0, h][None], [5], base)[0]
+        lam = kr @ qq / np.sqrt(d)
+        w = np.exp(lam - lam.max())
+        np.testing.assert_allclose(out[0, h], (w / w.sum()) @ V[0, g, :6], rtol=0, atol=1e-12)
+
+
 def test_attend_single_token_and_empty(O):
     d = 64
     codec = O.make_codec(d, 2, 3, d, seed=3)
