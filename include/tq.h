@@ -208,6 +208,26 @@ tq_status tq_decode_attend_window(const tq_cache_desc *desc, const void *codec_d
                                   int32_t q_pos, float rope_base, float scale, float *out,
                                   float *scores, void *ws, size_t ws_bytes, tq_stream_t stream);
 
+/* One generation step with the window managed in place ([NSNQuant] section 4, residuals:
+ * the full-precision residual is quantized and appended to the packed part once full).
+ * *length packed tokens and *win_len window tokens (host in/out; 0 <= *win_len <= win_cap)
+ * precede the new token, whose raw key and value new_k, new_v (device
+ * [batch][kv_heads][d] of win_dtype) sit at position *length + *win_len.  If the window
+ * is full (*win_len == win_cap) its rows are first quantized into the packed cache at
+ * positions *length ... (the tq_quantize_kv launch above, 16-byte aligned buffers), and
+ * the window starts empty; the new token is then stored into row *win_len of win_k, win_v
+ * by the attention kernel itself, and q attends over the packed tokens and the window
+ * with it, as tq_decode_attend_window.  On TQ_OK *length and *win_len hold the new counts
+ * and scores (optional) has rows of *length + *win_len; on a validation error nothing
+ * was launched and nothing changes.  ws: tq_decode_window_workspace_bytes for the
+ * packed length after the step (the cache capacity always suffices). */
+tq_status tq_decode_step(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
+                         int32_t *length, void *win_k, void *win_v, tq_dtype win_dtype,
+                         int32_t *win_len, int32_t win_cap, const void *new_k, const void *new_v,
+                         const void *q, tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                         float rope_base, float scale, float *out, float *scores, void *ws,
+                         size_t ws_bytes, tq_stream_t stream);
+
 /* Workspace bytes tq_search_topk needs. */
 size_t tq_search_workspace_bytes(const tq_cache_desc *db, int32_t n_db, int32_t nq, int32_t k);
 

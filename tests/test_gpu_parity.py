@@ -239,6 +239,57 @@ def test_window_attention(tq, P, bk, bv, d, G, L, Wn, cap, dt):
         assert e3 <= TOL
 
 
+@pytest.mark.parametrize("bk,bv,d,G,L0,cap,steps,dt", [
+    (2, 3, 128, 4, 300, 16, 40, "bf16"),   # MFMA path, two flushes
+    (3, 4, 64, 8, 0, 8, 20, "f32"),        # fp32 path, starting from an empty cache
+])
+def test_decode_step_loop(tq, P, bk, bv, d, G, L0, cap, steps, dt):
+    """A generation loop through tq_decode_step (flush of a full window, append inside the
+    window kernel, attention) against the oracle's decode_step, step by step; then the
+    packed cache the flushes wrote against the oracle's codes, and the window rows."""
+    T = L0 + steps
+    w = W.LONG_CONTEXT.scaled(batch=2, kv_heads=2, q_heads=2 * G, d=d, m=d, context=T, bits_k=bk, bits_v=bv,
+                              dtype=dt)
+    K, V = W.gen_kv(w)
+    Kd, Vd = P.to_f64(K), P.to_f64(V)
+    codec_o = O.make_codec(d, bk, bv, d, 0)
+    codec = tq.Codec(d, bk, bv, d, seed=0)
+    cache = tq.PackedCache(w.batch, w.kv_heads, d, T, bk, bv, d)
+    fields = P.oracle_encode_unitwise(Kd[:, :, :L0], Vd[:, :, :L0], codec_o, np.arange(L0), w.rope_base)
+    if L0 > 0:
+        cache.buf.copy_(torch.from_numpy(P.oracle_image(cache.desc.as_dict(), fields)))
+    st = {"fields": fields, "length": L0, "win_k": np.zeros((w.batch, w.kv_heads, cap, d)),
+          "win_v": np.zeros((w.batch, w.kv_heads, cap, d)), "win_len": 0}
+    wk = torch.zeros((w.batch, w.kv_heads, cap, d), dtype=K.dtype, device="cuda")
+    wv = torch.zeros_like(wk)
+    Kc, Vc = K.cuda(), V.cuda()
+    Hq = w.q_heads
+    ws = torch.empty(tq.decode_window_workspace_bytes(cache.desc, Hq, T), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, Hq, d), dtype=torch.float32, device="cuda")
+    sc = torch.empty((w.batch, Hq, T), dtype=torch.float32, device="cuda")
+    L, Wn, worst = L0, 0, 0.0
+    for s in range(steps):
+        n = L0 + s + 1
+        q = W.gen_q(w, seed=100 + s)
+        nk, nv = Kc[:, :, n - 1].contiguous(), Vc[:, :, n - 1].contiguous()
+        L, Wn = tq.decode_step(cache.desc, codec.dev, cache.buf, L, wk, wv, Wn, nk, nv, q.cuda(), n - 1,
+                               w.rope_base, out, scores=sc, ws=ws)
+        o_o, s_o = O.decode_step(st, Kd[:, :, n - 1], Vd[:, :, n - 1], P.to_f64(q), codec_o, q_pos=n - 1,
+                                 rope_base=w.rope_base, scale=0.0, kv_heads=w.kv_heads)
+        assert (L, Wn) == (st["length"], st["win_len"])
+        torch.cuda.synchronize()
+        e_out = P.max_abs(out.cpu().numpy(), o_o)
+        e_sc = P.max_abs(sc.view(-1)[:w.batch * Hq * n].view(w.batch, Hq, n).cpu().numpy(), s_o)
+        worst = max(worst, e_out, e_sc)
+        assert e_out <= TOL and e_sc <= TOL, (s, e_out, e_sc)
+    rep = {}
+    P.compare_codes(P.gpu_fields(cache, L), P.oracle_encode_unitwise(Kd[:, :, :L], Vd[:, :, :L], codec_o,
+                                                                    np.arange(L), w.rope_base), codec_o, rep)
+    assert torch.equal(wk[:, :, :Wn].cpu(), K[:, :, L:L + Wn]) and torch.equal(wv[:, :, :Wn].cpu(), V[:, :, L:L + Wn])
+    say(f"    step loop k{bk} v{bv} d{d} G{G} L0 {L0} cap {cap}: {steps} steps, final ({L}, {Wn}), "
+        f"worst {worst:.2e}, codes {rep}")
+
+
 @pytest.mark.parametrize("bk,bv,m", [(1, 2, 64), (3, 4, 128), (4, 1, 32), (2, 3, 0)])
 def test_other_bit_widths(tq, P, bk, bv, m):
     w = W.LLAMA3_8B.scaled(batch=1, kv_heads=2, q_heads=4, context=300, bits_k=bk, bits_v=bv, m=m)

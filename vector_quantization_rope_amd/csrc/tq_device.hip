@@ -36,6 +36,13 @@ __device__ __forceinline__ float load_elem(const void *p, size_t i, int dtype) {
   return float(h);
 }
 
+__device__ __forceinline__ void copy_elem(void *dst, const void *src, size_t di, size_t si, int dtype) {
+  if (dtype == TQ_F32)
+    static_cast<float *>(dst)[di] = static_cast<const float *>(src)[si];
+  else
+    static_cast<uint16_t *>(dst)[di] = static_cast<const uint16_t *>(src)[si];
+}
+
 // fp32 -> fp16 bits, round to nearest even; values that would round to infinity are
 // stored as 65504 and reported through *over.
 __device__ __forceinline__ uint16_t f16_sat_bits(float x, bool *over) {
@@ -2006,6 +2013,8 @@ __global__ __launch_bounds__(256) void k_logits(MfmaArgs a) {
 // partial (max, sum, acc) for the merge, which then weighs it against the packed splits.
 struct WindowArgs {
   const void *k, *v;          // [batch][kv_heads][cap][d] of dtype: raw keys, values
+  const void *nk, *nv;        // optional [batch][kv_heads][d]: token len - 1, appended here
+  void *ak, *av;              // the window buffers the appended token is stored into
   const void *q;              // [batch][q_heads][d] of qdtype
   const float *Dsg;           // rotation signs
   float *part;                // [B*Hq][splits_total][d + 2]
@@ -2070,7 +2079,14 @@ __global__ __launch_bounds__(256) void k_window(WindowArgs a) {
         const int t = t0 + i;
         if (t < cn) {
           const size_t base = (ubase + c0 + t) * D;
-          const float x0 = load_elem(a.k, base + jp, a.dtype), x1 = load_elem(a.k, base + jp + H2, a.dtype);
+          const bool fresh = a.nk && c0 + t == a.len - 1;   // the token this call appends
+          const void *src = fresh ? a.nk : a.k;
+          const size_t sb = fresh ? size_t(unit) * D : base;
+          const float x0 = load_elem(src, sb + jp, a.dtype), x1 = load_elem(src, sb + jp + H2, a.dtype);
+          if (fresh) {
+            copy_elem(a.ak, src, base + jp, sb + jp, a.dtype);
+            copy_elem(a.ak, src, base + jp + H2, sb + jp + H2, a.dtype);
+          }
           kr[t * RS + jp] = x0 * float(c) - x1 * float(sn);
           kr[t * RS + jp + H2] = x0 * float(sn) + x1 * float(c);
         }
@@ -2081,7 +2097,14 @@ __global__ __launch_bounds__(256) void k_window(WindowArgs a) {
     }
     for (int i = tid; i < cn * D; i += 256) {
       const int t = i / D, j = i % D;
-      vr[t * RS + j] = load_elem(a.v, (ubase + c0 + t) * D + j, a.dtype);
+      const size_t di = (ubase + c0 + t) * D + j;
+      if (a.nv && c0 + t == a.len - 1) {
+        const size_t si = size_t(unit) * D + j;
+        vr[t * RS + j] = load_elem(a.nv, si, a.dtype);
+        copy_elem(a.av, a.nv, di, si, a.dtype);
+      } else {
+        vr[t * RS + j] = load_elem(a.v, di, a.dtype);
+      }
     }
     __syncthreads();
     for (int i = tid; i < G * CH; i += 256) {
@@ -2888,7 +2911,10 @@ namespace {
 struct WindowIn {
   const void *k, *v;
   tq_dtype dtype;
-  int len, cap;
+  int len, cap;            // tokens attended (including an appended one), buffer rows
+  const void *nk, *nv;     // decode step: the token appended at row len - 1, or null
+  void *ak, *av;           // decode step: writable window buffers
+  bool flush;              // decode step: rows [0, cap) go to the packed cache first
 };
 }  // namespace
 
@@ -2931,6 +2957,14 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
   }
   const CodecPtrs cp = codec_ptrs(codec_dev, d, desc->bits_k, desc->bits_v, m);
   if (win && cp.block != d) return TQ_EUNSUPPORTED;   // the window rotates with one d-point block
+  if (win && win->flush) {
+    // the full window becomes packed tokens [length - cap, length) before anything reads them
+    if (length < win->cap) return TQ_EINVAL;
+    const tq_status st = tq_quantize_kv_profiled(desc, codec_dev, const_cast<void *>(cache_dev), win->k, win->v,
+                                                 win->dtype, length - win->cap, win->cap, rope_base, nullptr,
+                                                 nullptr, stream);
+    if (st != TQ_OK) return st;
+  }
   float *qp = static_cast<float *>(ws);
   const int qstride = d + m + 2;
   const int units = desc->batch * desc->kv_heads;
@@ -3059,6 +3093,10 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
     WindowArgs wa;
     wa.k = win->k;
     wa.v = win->v;
+    wa.nk = win->nk;
+    wa.nv = win->nv;
+    wa.ak = win->ak;
+    wa.av = win->av;
     wa.q = q;
     wa.Dsg = cp.D;
     wa.part = part;
@@ -3119,9 +3157,31 @@ tq_status tq_decode_attend_window(const tq_cache_desc *desc, const void *codec_d
                                   int32_t win_cap, const void *q, tq_dtype dtype, int32_t q_heads,
                                   int32_t q_pos, float rope_base, float scale, float *out,
                                   float *scores, void *ws, size_t ws_bytes, tq_stream_t stream) {
-  const WindowIn w{win_k, win_v, win_dtype, win_len, win_cap};
+  const WindowIn w{win_k, win_v, win_dtype, win_len, win_cap, nullptr, nullptr, nullptr, nullptr, false};
   return decode_impl(desc, codec_dev, cache_dev, length, &w, q, dtype, q_heads, q_pos, rope_base, scale,
                      out, scores, 0, ws, ws_bytes, nullptr, nullptr, stream);
+}
+
+tq_status tq_decode_step(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
+                         int32_t *length, void *win_k, void *win_v, tq_dtype win_dtype,
+                         int32_t *win_len, int32_t win_cap, const void *new_k, const void *new_v,
+                         const void *q, tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                         float rope_base, float scale, float *out, float *scores, void *ws,
+                         size_t ws_bytes, tq_stream_t stream) {
+  if (!length || !win_len || !win_k || !win_v || !new_k || !new_v) return TQ_EINVAL;
+  if (*length < 0 || win_cap < 1 || *win_len < 0 || *win_len > win_cap) return TQ_EINVAL;
+  const bool flush = *win_len == win_cap;
+  const int64_t packed = int64_t(*length) + (flush ? win_cap : 0);
+  if (packed > INT32_MAX) return TQ_ECAPACITY;
+  const int n_win = (flush ? 0 : *win_len) + 1;
+  const WindowIn w{win_k, win_v, win_dtype, n_win, win_cap, new_k, new_v, win_k, win_v, flush};
+  const tq_status st = decode_impl(desc, codec_dev, cache_dev, int32_t(packed), &w, q, dtype, q_heads, q_pos,
+                                   rope_base, scale, out, scores, 0, ws, ws_bytes, nullptr, nullptr, stream);
+  if (st == TQ_OK) {
+    *length = int32_t(packed);
+    *win_len = n_win;
+  }
+  return st;
 }
 
 tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_dev,

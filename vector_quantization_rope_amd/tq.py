@@ -31,6 +31,7 @@ EXPORTS = [
     "tq_decode_workspace_bytes_splits", "tq_decode_attend_splits",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_quantize_kv_profiled",
     "tq_decode_attend_profiled", "tq_decode_window_workspace_bytes", "tq_decode_attend_window",
+    "tq_decode_step",
 ]
 
 
@@ -87,6 +88,10 @@ _decode_win_ws = _sig("tq_decode_window_workspace_bytes", _S, [_KD, _I, _I])
 _decode_attend_win = _sig("tq_decode_attend_window", ctypes.c_int,
                           [_KD, _P, _P, _I, _P, _P, ctypes.c_int, _I, _I, _P, ctypes.c_int, _I, _I, _F, _F,
                            _P, _P, _P, _S, _P])
+_IP = ctypes.POINTER(ctypes.c_int32)
+_decode_step = _sig("tq_decode_step", ctypes.c_int,
+                    [_KD, _P, _P, _IP, _P, _P, ctypes.c_int, _IP, _I, _P, _P, _P, ctypes.c_int, _I, _I, _F, _F,
+                     _P, _P, _P, _S, _P])
 _search_ws = _sig("tq_search_workspace_bytes", _S, [_KD, _I, _I, _I])
 _search_topk = _sig("tq_search_topk", ctypes.c_int,
                     [_KD, _P, _P, _I, _P, _I, _I, _P, _P, _P, _S, _P])
@@ -234,6 +239,35 @@ def decode_attend_window(desc: CacheDesc, codec_dev, cache, length: int, win_k, 
                               _dtype_code(q), q_heads, int(q_pos), float(rope_base), float(scale), _ptr(out),
                               _ptr(scores), _ptr(ws), int(ws_bytes), _stream(stream)),
            "tq_decode_attend_window")
+
+
+def decode_step(desc: CacheDesc, codec_dev, cache, length: int, win_k, win_v, win_len: int, new_k, new_v, q,
+                q_pos: int, rope_base: float, out, scores=None, ws=None, scale: float = 0.0, stream=None,
+                ws_bytes: int | None = None):
+    """One generation step: flush a full window into the packed cache, append new_k, new_v
+    ([batch, kv_heads, d], the window's dtype) to the window, attend.  Returns the new
+    (length, win_len)."""
+    q_heads = int(q.shape[1])
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    cap = int(win_k.shape[2])
+    want = (desc.batch, desc.kv_heads, cap, desc.d)
+    for t in (win_k, win_v):
+        if t.dim() != 4 or tuple(t.shape) != want or not t.is_contiguous() or t.dtype != win_k.dtype:
+            raise ValueError(f"decode_step: window tensors must be contiguous {want} of one dtype")
+    for t in (new_k, new_v):
+        if t.numel() != desc.batch * desc.kv_heads * desc.d or not t.is_contiguous() or t.dtype != win_k.dtype:
+            raise ValueError("decode_step: new_k, new_v must be contiguous [batch, kv_heads, d] of the window dtype")
+    n_after = (length + cap + 1) if win_len == cap else (length + win_len + 1)
+    if scores is not None and scores.numel() < desc.batch * q_heads * n_after:
+        raise ValueError("decode_step: scores smaller than batch x q_heads x tokens after the step")
+    L, Wn = ctypes.c_int32(length), ctypes.c_int32(win_len)
+    _check(_decode_step(ctypes.byref(desc), _ptr(codec_dev), _ptr(cache), ctypes.byref(L), _ptr(win_k), _ptr(win_v),
+                        _dtype_code(win_k), ctypes.byref(Wn), cap, _ptr(new_k), _ptr(new_v), _ptr(q), _dtype_code(q),
+                        q_heads, int(q_pos), float(rope_base), float(scale), _ptr(out), _ptr(scores), _ptr(ws),
+                        int(ws_bytes), _stream(stream)),
+           "tq_decode_step")
+    return int(L.value), int(Wn.value)
 
 
 def search_workspace_bytes(desc: CacheDesc, n_db: int, nq: int, k: int) -> int:
