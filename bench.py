@@ -269,6 +269,82 @@ def key_width_bench(tq, W, w, K, V, q, dev, ev, stream, reps: int = 30):
             "decode": decode, "logits": logits}
 
 
+def window_bench(tq, w, K, V, q, cache, codec, dev, ev, stream, cap: int = 128, cycles: int = 3):
+    """The full-precision recent-token window on the long-context cache, outside the timed
+    steps: (1) the same T tokens attended as T - cap packed + cap raw ones, next to plain
+    decode over T packed tokens; (2) a generation loop of tq_decode_step calls (one flush
+    of the cap-token window every cap steps, the new token stored by the window kernel),
+    per-step call times split into steps with and without the flush.  The loop rewrites
+    packed tokens the cache already holds, so the cache stays as it was."""
+    import torch
+
+    T, B, Hkv, d = w.context, w.batch, w.kv_heads, w.d
+    med = lambda v: sorted(v)[len(v) // 2]
+    out = torch.empty((B, w.q_heads, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.decode_window_workspace_bytes(cache.desc, w.q_heads, T), dtype=torch.uint8, device=dev)
+    wk = K[:, :, T - cap:].contiguous()
+    wv = V[:, :, T - cap:].contiguous()
+    reps = 40
+    E = [[ev.create() for _ in range(2)] for _ in range(reps)]
+
+    def timed(fn):
+        t0, n = time.perf_counter(), 0
+        while time.perf_counter() - t0 < 0.08:
+            fn()
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
+        for i in range(reps):
+            ev.record(E[i][0], stream)
+            fn()
+            ev.record(E[i][1], stream)
+        torch.cuda.synchronize()
+        return med([ev.elapsed_ms(e[0], e[1]) * 1e3 for e in E])
+
+    plain = timed(lambda: tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos, w.rope_base, out,
+                                           ws=ws))
+    win = timed(lambda: tq.decode_attend_window(cache.desc, codec.dev, cache.buf, T - cap, wk, wv, cap, q,
+                                                w.q_pos, w.rope_base, out, ws=ws))
+    # generation loop
+    n = cap * cycles
+    L0 = T - n - cap
+    Kn = K[:, :, L0:L0 + n].permute(2, 0, 1, 3).contiguous()
+    Vn = V[:, :, L0:L0 + n].permute(2, 0, 1, 3).contiguous()
+    bk = torch.zeros((B, Hkv, cap, d), dtype=K.dtype, device=dev)
+    bv = torch.zeros_like(bk)
+    SE = [[ev.create() for _ in range(2)] for _ in range(n)]
+
+    def loop(events):
+        L, Wn = L0, 0
+        for s in range(n):
+            if events:
+                ev.record(SE[s][0], stream)
+            L, Wn = tq.decode_step(cache.desc, codec.dev, cache.buf, L, bk, bv, Wn, Kn[s], Vn[s], q, L0 + s,
+                                   w.rope_base, out, ws=ws)
+            if events:
+                ev.record(SE[s][1], stream)
+        return L, Wn
+
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 0.08:
+        loop(False)
+    torch.cuda.synchronize()
+    L, Wn = loop(True)
+    torch.cuda.synchronize()
+    st = [ev.elapsed_ms(e[0], e[1]) * 1e3 for e in SE]
+    flush = [st[s] for s in range(cap, n, cap)]
+    plain_steps = [st[s] for s in range(n) if s % cap != 0]
+    return {"workload": (f"long_context shape (4 x 8 units, d 128, G 8), {T} tokens; window of {cap} "
+                         f"tokens; loop of {n} steps from {L0} packed tokens; medians"),
+            "plain_decode_call_us": round(plain, 2),
+            "packed_plus_window_call_us": round(win, 2),
+            "window_overhead_us": round(win - plain, 2),
+            "step_call_us_no_flush": round(med(plain_steps), 2),
+            "step_call_us_with_flush": round(med(flush), 2) if flush else None,
+            "step_call_us_mean": round(sum(st) / len(st), 2),
+            "final_length_window": [L, Wn]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -390,6 +466,12 @@ def main():
         widths = key_width_bench(tq, W, w, K, V, q, dev, ev, stream)
         log(f"[bench] key widths {widths}")
 
+    window = None
+    if not args.no_search:
+        log("[bench] full-precision window and decode steps ...")
+        window = window_bench(tq, w, K, V, q, cache, codec, dev, ev, stream)
+        log(f"[bench] window {window}")
+
     search = None
     if not args.no_search:
         log("[bench] vector search workload ...")
@@ -444,6 +526,7 @@ def main():
         },
         "cpu_baseline": base,
         "key_widths": widths,
+        "window": window,
         "search": search,
     }
     print(json.dumps(rec), flush=True)

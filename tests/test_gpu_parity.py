@@ -184,6 +184,7 @@ def test_logits_only(tq, P, bk, bv, d, G, T):
     (2, 3, 64, 4, 257, 0, 32, "bf16"),     # empty window
     (1, 3, 64, 8, 130, 200, 256, "f32"),   # fp32 inputs, window longer than the packed part
     (3, 4, 128, 4, 190, 70, 80, "f32"),    # fp32 decode path
+    (2, 3, 64, 16, 150, 600, 640, "f16"),  # f16, 16 q-heads per kv-head (fp32 decode path), 10 chunks
 ])
 def test_window_attention(tq, P, bk, bv, d, G, L, Wn, cap, dt):
     """Packed tokens [0, L) plus a full-precision window of Wn raw tokens (NSNQuant's

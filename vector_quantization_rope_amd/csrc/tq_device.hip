@@ -2021,133 +2021,286 @@ struct WindowArgs {
   float *scores;              // optional [B][Hq][score_stride]
   int dtype, qdtype, len, cap, length, q_pos, kv_heads, q_heads, G;
   int splits_total, split_idx, score_stride;
+  int chunks_per_block;       // 64-token chunks per block; blockIdx.y picks the block's range
   float rope_base, scale_log2, inv_sqrt_block;
 };
 
-template <int D>
+// 16-byte vector of window elements -> fp32 (bf16, f16: 8 elements; f32: 4)
+template <int ES>
+__device__ __forceinline__ void unpack_vec(const uint4 &r, bool bf, float *dst) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  if constexpr (ES == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(w[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (bf) {
+        dst[2 * e] = __uint_as_float(w[e] << 16);
+        dst[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+      } else {
+        const uint16_t lo = uint16_t(w[e]), hi = uint16_t(w[e] >> 16);
+        _Float16 a, b;
+        __builtin_memcpy(&a, &lo, 2);
+        __builtin_memcpy(&b, &hi, 2);
+        dst[2 * e] = float(a);
+        dst[2 * e + 1] = float(b);
+      }
+    }
+  }
+}
+
+// D: head dim; ES: element bytes of the window (2: bf16 / f16, 4: f32).  A chunk of 64
+// tokens of K and V is read with 16-byte loads (the next chunk's are in flight while the
+// current one is scored), converted into LDS, rotary-embedded there by a per-pair fp64
+// angle recurrence, scored against the G rotary-embedded queries, and folded into the
+// online softmax (one lane per token) and the value sums.
+template <int D, int ES, int GM>
 __global__ __launch_bounds__(256) void k_window(WindowArgs a) {
-  constexpr int H2 = D / 2, CH = 64, RS = D + 1;   // padded rows: conflict-free column reads
-  constexpr int NGRP = 256 / H2, TPG = CH / NGRP;   // RoPE: token groups per pair index
-  constexpr int HS = 256 / D, HPT = (kMaxG + HS - 1) / HS;   // value phase: heads per thread
-  __shared__ float qr[kMaxG][D];
+  constexpr int H2 = D / 2, CH = 64, RS = D + 1;     // padded rows: conflict-free column reads
+  constexpr int VPR = D * ES / 16, EPV = 16 / ES;    // 16-byte vectors per row, elements per vector
+  constexpr int NV = CH * VPR / 256;                 // vectors per thread per chunk, K and V each
+  static_assert(NV * 256 == CH * VPR, "a chunk splits evenly over the block");
+  constexpr int NGRP = 256 / H2, TPG = CH / NGRP;    // RoPE: token groups per pair index
+  // GM: heads per unit rounded up (8 or 16); every thread runs HPT head slots without a
+  // branch per head, slots past G working on zero rows
+  constexpr int HS = 256 / D, HPT = GM / HS;
+  static_assert(GM == 8 || GM == 16, "head slots");
+  __shared__ __align__(16) float qr[GM][D];
   __shared__ float kr[CH * RS];
   __shared__ float vr[CH * RS];
-  __shared__ float ps[kMaxG][CH];
-  __shared__ float mstat[3][kMaxG];   // running max (log2 units), sum, this chunk's rescale
-  const int tid = threadIdx.x, unit = blockIdx.x;
+  __shared__ __align__(16) float ps[GM][CH];
+  __shared__ float mstat[3][GM];   // running max (log2 units), sum, this chunk's rescale
+  __shared__ float qrot[2][H2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, unit = blockIdx.x;
   const int b = unit / a.kv_heads, g = unit % a.kv_heads, G = a.G, hq0 = g * G;
-  const bool rope = a.rope_base != 0.0f;
+  const bool rope = a.rope_base != 0.0f, bf = a.dtype == TQ_BF16;
+  const size_t ubase = size_t(unit) * a.cap;
+  // this block's tokens: chunks [blockIdx.y * cpb, ...) of the window
+  const int t_begin = blockIdx.y * a.chunks_per_block * CH;
+  const int t_end = min(a.len, t_begin + a.chunks_per_block * CH);
+  const char *kb = static_cast<const char *>(a.k), *vb = static_cast<const char *>(a.v);
+  uint4 kreg[NV], vreg[NV];
+  // chunk c0 into registers; the token this call appends (row len - 1) comes from nk, nv
+  auto fetch = [&](int c0) {
+    const int cn = min(CH, t_end - c0);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = tid + k * 256, t = vi / VPR, col = (vi % VPR) * EPV;
+      if (t < cn) {
+        const bool fresh = a.nk && c0 + t == a.len - 1;
+        const size_t off = (fresh ? size_t(unit) * D + col : (ubase + c0 + t) * D + col) * ES;
+        kreg[k] = *reinterpret_cast<const uint4 *>((fresh ? static_cast<const char *>(a.nk) : kb) + off);
+        vreg[k] = *reinterpret_cast<const uint4 *>((fresh ? static_cast<const char *>(a.nv) : vb) + off);
+      }
+    }
+  };
+  fetch(t_begin);
   // fp64 frequency of this thread's pair index (the keys' RoPE steps token by token)
   const int jp = tid % H2, grp = tid / H2;
-  const double theta = rope ? pow(double(a.rope_base), -2.0 * double(jp) / double(D)) : 0.0;
-  double sd = 0.0, cd = 1.0;
-  if (rope) sincos(theta, &sd, &cd);
+  const double theta = rope ? exp2(-2.0 * double(jp) / double(D) * log2(double(a.rope_base))) : 0.0;
+  // angle of token grp * TPG of this block's first chunk, stepped by theta within a chunk
+  // and by (CH - TPG) theta from one chunk to the next, all in fp64
+  double sd = 0.0, cd = 1.0, sj = 0.0, cj = 1.0, sg = 0.0, cg = 1.0;
+  if (rope) {
+    sincos(theta, &sd, &cd);
+    sincos(double(CH - TPG) * theta, &sj, &cj);
+    sincos(double(a.length + t_begin + grp * TPG) * theta, &sg, &cg);
+  }
+  if (tid < H2) {
+    double sn = 0.0, c = 1.0;
+    if (rope) sincos(double(a.q_pos) * theta, &sn, &c);
+    qrot[0][tid] = float(c);
+    qrot[1][tid] = float(sn);
+  }
+  if (tid < GM) {
+    mstat[0][tid] = -INFINITY;
+    mstat[1][tid] = 0.0f;
+    mstat[2][tid] = 0.0f;
+  }
+  for (int i = tid; i < GM * CH; i += 256) (&ps[0][0])[i] = 0.0f;
+  for (int i = G * D + tid; i < GM * D; i += 256) (&qr[0][0])[i] = 0.0f;
+  __syncthreads();
   // RoPE(q) of the unit's heads, unrotated
   for (int i = tid; i < G * H2; i += 256) {
     const int h = i / H2, j = i % H2;
     const size_t base = (size_t(b) * a.q_heads + hq0 + h) * D;
     const float x0 = load_elem(a.q, base + j, a.qdtype), x1 = load_elem(a.q, base + j + H2, a.qdtype);
     if (rope) {
-      const double th = pow(double(a.rope_base), -2.0 * double(j) / double(D));
-      double sn, c;
-      sincos(double(a.q_pos) * th, &sn, &c);
-      qr[h][j] = x0 * float(c) - x1 * float(sn);
-      qr[h][j + H2] = x0 * float(sn) + x1 * float(c);
+      const float c = qrot[0][j], sn = qrot[1][j];
+      qr[h][j] = x0 * c - x1 * sn;
+      qr[h][j + H2] = x0 * sn + x1 * c;
     } else {
       qr[h][j] = x0;
       qr[h][j + H2] = x1;
     }
   }
-  if (tid < kMaxG) {
-    mstat[0][tid] = -INFINITY;
-    mstat[1][tid] = 0.0f;
-  }
   const int jv = tid % D, hs = tid / D;
   float acc[HPT];
 #pragma unroll
   for (int k = 0; k < HPT; ++k) acc[k] = 0.0f;
-  const size_t ubase = size_t(unit) * a.cap;
-  for (int c0 = 0; c0 < a.len; c0 += CH) {
-    const int cn = min(CH, a.len - c0);
+  for (int c0 = t_begin; c0 < t_end; c0 += CH) {
+    const int cn = min(CH, t_end - c0);
     __syncthreads();   // the previous chunk's readers are done
-    {
-      // keys: pair jp of tokens grp * TPG .. + TPG, angles stepped from one fp64 sincos
-      const int t0 = grp * TPG;
-      double sn = 0.0, c = 1.0;
-      if (rope) sincos(double(a.length + c0 + t0) * theta, &sn, &c);
-      for (int i = 0; i < TPG; ++i) {
-        const int t = t0 + i;
-        if (t < cn) {
-          const size_t base = (ubase + c0 + t) * D;
-          const bool fresh = a.nk && c0 + t == a.len - 1;   // the token this call appends
-          const void *src = fresh ? a.nk : a.k;
-          const size_t sb = fresh ? size_t(unit) * D : base;
-          const float x0 = load_elem(src, sb + jp, a.dtype), x1 = load_elem(src, sb + jp + H2, a.dtype);
-          if (fresh) {
-            copy_elem(a.ak, src, base + jp, sb + jp, a.dtype);
-            copy_elem(a.ak, src, base + jp + H2, sb + jp + H2, a.dtype);
-          }
-          kr[t * RS + jp] = x0 * float(c) - x1 * float(sn);
-          kr[t * RS + jp + H2] = x0 * float(sn) + x1 * float(c);
+    // rows past the chunk's end are zero, so the loops below run over whole chunks
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int vi = tid + k * 256, t = vi / VPR, col = (vi % VPR) * EPV;
+      if (t < cn) {
+        unpack_vec<ES>(kreg[k], bf, &kr[t * RS + col]);
+        unpack_vec<ES>(vreg[k], bf, &vr[t * RS + col]);
+        if (a.nk && c0 + t == a.len - 1) {   // store the appended token into its window row
+          const size_t off = ((ubase + c0 + t) * D + col) * ES;
+          *reinterpret_cast<uint4 *>(static_cast<char *>(a.ak) + off) = kreg[k];
+          *reinterpret_cast<uint4 *>(static_cast<char *>(a.av) + off) = vreg[k];
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          kr[t * RS + col + e] = 0.0f;
+          vr[t * RS + col + e] = 0.0f;
+        }
+      }
+    }
+    if (c0 + CH < t_end) fetch(c0 + CH);
+    __syncthreads();
+    if (rope) {
+      // pair jp of tokens grp * TPG .. + TPG: angles stepped from one fp64 sincos, then
+      // all reads, then all rotations
+      const int t0 = grp * TPG;
+      float cf[TPG], sf[TPG], x0[TPG], x1[TPG];
+      double sn = sg, c = cg;
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) {
+        cf[i] = float(c);
+        sf[i] = float(sn);
         const double cn2 = c * cd - sn * sd;
         sn = sn * cd + c * sd;
         c = cn2;
       }
-    }
-    for (int i = tid; i < cn * D; i += 256) {
-      const int t = i / D, j = i % D;
-      const size_t di = (ubase + c0 + t) * D + j;
-      if (a.nv && c0 + t == a.len - 1) {
-        const size_t si = size_t(unit) * D + j;
-        vr[t * RS + j] = load_elem(a.nv, si, a.dtype);
-        copy_elem(a.av, a.nv, di, si, a.dtype);
-      } else {
-        vr[t * RS + j] = load_elem(a.v, di, a.dtype);
+      {   // the same token group of the next chunk
+        const double cn2 = c * cj - sn * sj;
+        sg = sn * cj + c * sj;
+        cg = cn2;
       }
-    }
-    __syncthreads();
-    for (int i = tid; i < G * CH; i += 256) {
-      const int h = i / CH, t = i % CH;
-      if (t < cn) {
-        float sdot = 0.0f;
-#pragma unroll 8
-        for (int j = 0; j < D; ++j) sdot = fmaf(qr[h][j], kr[t * RS + j], sdot);
-        ps[h][t] = sdot;
-        if (a.scores) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.score_stride + a.length + c0 + t] = sdot;
-      }
-    }
-    __syncthreads();
-    if (tid < G) {
-      const int h = tid;
-      float cmax = -INFINITY;
-      for (int t = 0; t < cn; ++t) cmax = fmaxf(cmax, ps[h][t] * a.scale_log2);
-      const float mold = mstat[0][h], mnew = fmaxf(mold, cmax);
-      const float alpha = mold == -INFINITY ? 0.0f : exp2f(mold - mnew);
-      float l = mstat[1][h] * alpha;
-      for (int t = 0; t < cn; ++t) {
-        const float pt = exp2f(ps[h][t] * a.scale_log2 - mnew);
-        ps[h][t] = pt;
-        l += pt;
-      }
-      mstat[0][h] = mnew;
-      mstat[1][h] = l;
-      mstat[2][h] = alpha;
-    }
-    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < HPT; ++k) {
-      const int h = hs + k * HS;
-      if (h < G) {
-        float o = acc[k] * mstat[2][h];
-        for (int t = 0; t < cn; ++t) o = fmaf(ps[h][t], vr[t * RS + jv], o);
-        acc[k] = o;
+      for (int i = 0; i < TPG; ++i) {
+        x0[i] = kr[(t0 + i) * RS + jp];
+        x1[i] = kr[(t0 + i) * RS + jp + H2];
       }
+#pragma unroll
+      for (int i = 0; i < TPG; ++i) {
+        kr[(t0 + i) * RS + jp] = x0[i] * cf[i] - x1[i] * sf[i];
+        kr[(t0 + i) * RS + jp + H2] = x0[i] * sf[i] + x1[i] * cf[i];
+      }
+      __syncthreads();
+    }
+    // scores: token = lane, heads wv + 8i and wv + 8i + 4; one read of the key row serves both
+    for (int h0 = wv; h0 < G; h0 += 8) {
+      const int t = lane;
+      const float *krow = &kr[t * RS];
+      if (h0 + 4 < G) {
+        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll 8
+        for (int j = 0; j < D; j += 4) {
+          const float4 qa = *reinterpret_cast<const float4 *>(&qr[h0][j]);
+          const float4 qb = *reinterpret_cast<const float4 *>(&qr[h0 + 4][j]);
+          const float k0 = krow[j], k1 = krow[j + 1], k2 = krow[j + 2], k3 = krow[j + 3];
+          s0 = fmaf(qa.x, k0, s0);
+          s1 = fmaf(qa.y, k1, s1);
+          s0 = fmaf(qa.z, k2, s0);
+          s1 = fmaf(qa.w, k3, s1);
+          s2 = fmaf(qb.x, k0, s2);
+          s3 = fmaf(qb.y, k1, s3);
+          s2 = fmaf(qb.z, k2, s2);
+          s3 = fmaf(qb.w, k3, s3);
+        }
+        ps[h0][t] = s0 + s1;
+        ps[h0 + 4][t] = s2 + s3;
+      } else {
+        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll 8
+        for (int j = 0; j < D; j += 4) {
+          const float4 qa = *reinterpret_cast<const float4 *>(&qr[h0][j]);
+          s0 = fmaf(qa.x, krow[j], s0);
+          s1 = fmaf(qa.y, krow[j + 1], s1);
+          s2 = fmaf(qa.z, krow[j + 2], s2);
+          s3 = fmaf(qa.w, krow[j + 3], s3);
+        }
+        ps[h0][t] = (s0 + s1) + (s2 + s3);
+      }
+    }
+    __syncthreads();
+    // online softmax, one lane per token, heads h0 and h0 + 4 of a wave side by side (the
+    // second is a zero row when h0 + 4 >= G); the scores go out unscaled
+    for (int h0 = wv; h0 < G; h0 += 8) {
+      const int h1 = h0 + 4;
+      const bool two = h1 < G;
+      const float s0 = ps[h0][lane], s1 = ps[h1 < GM ? h1 : h0][lane];
+      if (a.scores && lane < cn) {
+        float *srow = a.scores + (size_t(b) * a.q_heads + hq0) * a.score_stride + a.length + c0 + lane;
+        srow[size_t(h0) * a.score_stride] = s0;
+        if (two) srow[size_t(h1) * a.score_stride] = s1;
+      }
+      float v0 = lane < cn ? s0 * a.scale_log2 : -INFINITY;
+      float v1 = lane < cn ? s1 * a.scale_log2 : -INFINITY;
+      float m0 = v0, m1 = v1;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        m0 = fmaxf(m0, __shfl_xor(m0, o, 64));
+        m1 = fmaxf(m1, __shfl_xor(m1, o, 64));
+      }
+      const float mold0 = mstat[0][h0], mnew0 = fmaxf(mold0, m0);
+      const float mold1 = two ? mstat[0][h1] : -INFINITY, mnew1 = fmaxf(mold1, m1);
+      const float al0 = mold0 == -INFINITY ? 0.0f : exp2f(mold0 - mnew0);
+      const float al1 = mold1 == -INFINITY ? 0.0f : exp2f(mold1 - mnew1);
+      const float p0 = lane < cn ? exp2f(v0 - mnew0) : 0.0f;
+      const float p1 = lane < cn ? exp2f(v1 - mnew1) : 0.0f;
+      float l0 = p0, l1 = p1;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        l0 += __shfl_xor(l0, o, 64);
+        l1 += __shfl_xor(l1, o, 64);
+      }
+      ps[h0][lane] = p0;
+      if (two) ps[h1][lane] = p1;
+      if (lane == 0) {
+        mstat[0][h0] = mnew0;
+        mstat[1][h0] = mstat[1][h0] * al0 + l0;
+        mstat[2][h0] = al0;
+        if (two) {
+          mstat[0][h1] = mnew1;
+          mstat[1][h1] = mstat[1][h1] * al1 + l1;
+          mstat[2][h1] = al1;
+        }
+      }
+    }
+    __syncthreads();
+    // values: one read of vr per token serves all of this thread's heads
+    {
+      float o[HPT];
+#pragma unroll
+      for (int k = 0; k < HPT; ++k) o[k] = acc[k] * mstat[2][hs + k * HS];
+#pragma unroll 4
+      for (int t = 0; t < CH; t += 4) {
+        const float v0 = vr[t * RS + jv], v1 = vr[(t + 1) * RS + jv];
+        const float v2 = vr[(t + 2) * RS + jv], v3 = vr[(t + 3) * RS + jv];
+#pragma unroll
+        for (int k = 0; k < HPT; ++k) {
+          const float4 p = *reinterpret_cast<const float4 *>(&ps[hs + k * HS][t]);
+          o[k] = fmaf(p.x, v0, o[k]);
+          o[k] = fmaf(p.y, v1, o[k]);
+          o[k] = fmaf(p.z, v2, o[k]);
+          o[k] = fmaf(p.w, v3, o[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < HPT; ++k) acc[k] = o[k];
     }
   }
   __syncthreads();
   // Pi acc = H (D .* acc) / sqrt(B) per head (Hadamard block = d here), then the partial
-  float *ys = kr;   // [kMaxG][D]
+  float *ys = kr;   // [GM][D]
 #pragma unroll
   for (int k = 0; k < HPT; ++k) {
     const int h = hs + k * HS;
@@ -2166,7 +2319,7 @@ __global__ __launch_bounds__(256) void k_window(WindowArgs a) {
   }
   for (int i = tid; i < G * D; i += 256) {
     const int h = i / D, j = i % D;
-    float *o = a.part + ((size_t(b) * a.q_heads + hq0 + h) * a.splits_total + a.split_idx) * (D + 2);
+    float *o = a.part + ((size_t(b) * a.q_heads + hq0 + h) * a.splits_total + a.split_idx + blockIdx.y) * (D + 2);
     o[j] = ys[h * D + j] * a.inv_sqrt_block;
     if (j == 0) {
       o[D] = mstat[0][h] * 0.69314718055994531f;   // natural-log units, as the packed splits
@@ -2756,6 +2909,7 @@ constexpr int kMfmaChunk = 32 * kDecWaves;   // tokens per block iteration (one 
 constexpr int kDecodeBlocks = 256 * kDecBlocksPerCU;   // MI355X: 256 CUs
 constexpr int kLogitsBlocks = 1024;                    // logits-only kernel: 4 blocks per CU
 constexpr int kMaxWindow = 4096;                      // full-precision window capacity
+constexpr int kWinMaxSplits = 8;                      // window partials per unit, at most
 
 int default_splits(const tq_cache_desc &c, int length) {
   if (length <= 0) return 1;
@@ -2942,9 +3096,17 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
     if (win->dtype != TQ_F32 && win->dtype != TQ_BF16 && win->dtype != TQ_F16) return TQ_EINVAL;
     if (desc->d != 64 && desc->d != 128) return TQ_EUNSUPPORTED;
     if (desc->bits_v == 0) return TQ_EUNSUPPORTED;
+    // the window kernel reads and writes rows with 16-byte vectors
+    for (const void *p : {win->k, win->v, win->nk, win->nv, static_cast<const void *>(win->ak),
+                          static_cast<const void *>(win->av)})
+      if ((reinterpret_cast<uintptr_t>(p) & 15) != 0) return TQ_EINVAL;
   }
   const int S = splits == 0 ? default_splits(*desc, length) : splits;
-  if (ws_bytes < decode_ws(*desc, q_heads, S + (win ? 1 : 0))) return TQ_ENOSPACE;
+  // the window's 64-token chunks over at most kWinMaxSplits blocks per unit, one partial each
+  const int wchunks = (wlen + 63) / 64;
+  const int wcpb = wchunks > 0 ? (wchunks + kWinMaxSplits - 1) / kWinMaxSplits : 1;
+  const int wsplit = (wchunks + wcpb - 1) / wcpb;   // the window's partials follow the packed splits
+  if (ws_bytes < decode_ws(*desc, q_heads, S + wsplit)) return TQ_ENOSPACE;
   const int d = desc->d, m = desc->m;
   const int rows = desc->batch * q_heads;
   hipStream_t s = hipStream_t(stream);
@@ -2975,7 +3137,6 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
   const bool mfma = decode_mfma_path(*desc, q_heads);
   // odd key codebook on the MFMA path: c[code] = c0 + a weighted sum of bit planes
   const int bk = desc->bits_k;
-  const int wsplit = wlen > 0 ? 1 : 0;   // the window's partial follows the packed splits
   const int score_stride = length + wlen;
   int used_splits = 0;
   if (length > 0) {
@@ -3110,16 +3271,32 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
     wa.kv_heads = desc->kv_heads;
     wa.q_heads = q_heads;
     wa.G = G;
-    wa.splits_total = used_splits + 1;
+    wa.splits_total = used_splits + wsplit;
     wa.split_idx = used_splits;
+    wa.chunks_per_block = wcpb;
     wa.score_stride = score_stride;
     wa.rope_base = rope_base;
     wa.scale_log2 = sc * 1.4426950408889634f;
     wa.inv_sqrt_block = cp.inv_sqrt_block;
-    if (d == 64)
-      hipLaunchKernelGGL(k_window<64>, dim3(units), dim3(256), 0, s, wa);
-    else
-      hipLaunchKernelGGL(k_window<128>, dim3(units), dim3(256), 0, s, wa);
+    const bool f32 = win->dtype == TQ_F32;
+    const dim3 wgrid(units, wsplit);
+    if (d == 64) {
+      if (G <= 8) {
+        if (f32) hipLaunchKernelGGL((k_window<64, 4, 8>), wgrid, dim3(256), 0, s, wa);
+        else hipLaunchKernelGGL((k_window<64, 2, 8>), wgrid, dim3(256), 0, s, wa);
+      } else {
+        if (f32) hipLaunchKernelGGL((k_window<64, 4, 16>), wgrid, dim3(256), 0, s, wa);
+        else hipLaunchKernelGGL((k_window<64, 2, 16>), wgrid, dim3(256), 0, s, wa);
+      }
+    } else {
+      if (G <= 8) {
+        if (f32) hipLaunchKernelGGL((k_window<128, 4, 8>), wgrid, dim3(256), 0, s, wa);
+        else hipLaunchKernelGGL((k_window<128, 2, 8>), wgrid, dim3(256), 0, s, wa);
+      } else {
+        if (f32) hipLaunchKernelGGL((k_window<128, 4, 16>), wgrid, dim3(256), 0, s, wa);
+        else hipLaunchKernelGGL((k_window<128, 2, 16>), wgrid, dim3(256), 0, s, wa);
+      }
+    }
   }
   if (!out) return launch_status();   // logits only: the scores are written, no merge
   used_splits += wsplit;
@@ -3148,7 +3325,7 @@ tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec
 
 size_t tq_decode_window_workspace_bytes(const tq_cache_desc *desc, int32_t q_heads, int32_t length) {
   if (!desc || !cache_desc_valid(*desc) || q_heads < 1 || length < 0) return 0;
-  return decode_ws(*desc, q_heads, default_splits(*desc, length) + 1);
+  return decode_ws(*desc, q_heads, default_splits(*desc, length) + kWinMaxSplits);
 }
 
 tq_status tq_decode_attend_window(const tq_cache_desc *desc, const void *codec_dev,
