@@ -87,9 +87,24 @@ def pct_us(ms):
     return [round(at(0.1), 2), round(at(0.5), 2), round(at(0.9), 2)]
 
 
+# Source regions the decode kernel is built from: the shared helpers at the top of the
+# device source, the MFMA decode section (argument block, query prep, k_decode_lds) and the
+# host-side launch constants. Counters taken on other sources stay valid while these match.
+_DECODE_REGIONS = (("", "// ------------------------------------------------------------------ quantize"),
+                   ("// ------------------------------------------------------------------ decode (MFMA path)",
+                    "// ------------------------------------------------------------------ full-precision window"),
+                   ("// ------------------------------------------------------------------ host-side helpers",
+                    "}  // namespace tq"))
+
+
 def kernel_source_hash() -> str:
-    with open(DEVICE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(DEVICE_SRC, encoding="utf-8") as f:
+        src = f.read()
+    h = hashlib.sha256()
+    for start, end in _DECODE_REGIONS:
+        i = src.index(start) if start else 0
+        h.update(src[i:src.index(end, i)].encode())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_counters(launch_bytes: float):
