@@ -58,7 +58,8 @@ __all__ = [
     "sphere_marginal_cdf", "sphere_marginal_pdf", "sphere_partial_mean", "lloyd_max",
     "Codebook", "make_codebook", "hadamard", "rotation_matrix", "rope",
     "fp16_sat", "Codec", "make_codec", "encode", "pack_cache", "unpack_cache",
-    "cache_layout", "attend", "attend_window", "decode_step", "search_scores", "topk", "exact_topk",
+    "cache_layout", "attend", "attend_window", "decode_step", "search_scores",
+    "nsn_mean", "nsn_rotated_mean", "topk", "exact_topk",
 ]
 
 _GOLDEN_GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -306,17 +307,26 @@ def _nearest(u: np.ndarray, c: np.ndarray) -> np.ndarray:
     return best
 
 
-def encode(x, codec: Codec, *, kind: str, positions=None, rope_base: float = 0.0):
+def encode(x, codec: Codec, *, kind: str, positions=None, rope_base: float = 0.0, nsn_o=None):
     """Encode rows of x ([N, d], any float dtype; converted exactly to fp64).
 
     kind = 'key' (RoPE if rope_base != 0, scalar codes with bits_k, QJL residual sketch),
            'value' (scalar codes with bits_v), 'db' (like 'key' without RoPE).
+    nsn_o: NSN channel mean ([d] or [N, d], fp32 values; see nsn_mean).  Each token then
+    gives s1 = ||x|| / sqrt(d) (fp16, s1_16) and is encoded as w = x - s1_16 o, the
+    subtraction done in the rotated basis with Pi o rounded to fp32 (the stored form).
     Returns a dict with y (rotated, fp64), u, codes, n16, and for keys rn16, bits, z,
-    plus overflow flags."""
+    plus overflow flags (and s1_16, po with nsn_o)."""
     x = np.asarray(x, dtype=np.float64)
     if kind == "key" and rope_base != 0:
         x = rope(x, positions, rope_base)
     y = x @ codec.Pi.T
+    extra = {}
+    if nsn_o is not None:
+        po = nsn_rotated_mean(nsn_o, codec)
+        s1_16, over_s = fp16_sat(np.sqrt(np.sum(y * y, axis=-1)) / math.sqrt(codec.d))
+        y = y - s1_16[..., None] * po
+        extra = {"s1_16": s1_16, "po": po, "over_s": over_s}
     n = np.sqrt(np.sum(y * y, axis=-1))
     safe = np.where(n > 0, n, 1.0)
     u = np.where(n[..., None] > 0, y / safe[..., None], 0.0)
@@ -324,6 +334,9 @@ def encode(x, codec: Codec, *, kind: str, positions=None, rope_base: float = 0.0
     codes = _nearest(u, cb.c)
     n16, over_n = fp16_sat(n)
     out = {"y": y, "u": u, "codes": codes, "n": n, "n16": n16, "overflow": over_n.copy()}
+    if extra:
+        out["s1_16"], out["po"] = extra["s1_16"], extra["po"]
+        out["overflow"] = out["overflow"] | extra["over_s"]
     if kind in ("key", "db"):
         r = y - n16[..., None] * cb.c[codes]
         rn = np.sqrt(np.sum(r * r, axis=-1))
@@ -332,6 +345,36 @@ def encode(x, codec: Codec, *, kind: str, positions=None, rope_base: float = 0.0
         out.update(r=r, rn=rn, rn16=rn16, z=z, bits=(z >= 0).astype(np.int64))
         out["overflow"] = out["overflow"] | over_r
     return out
+
+
+# ----------------------------------------------------------------------------------
+# NSN pre-transform ([NSNQuant] section 1, normalize-shift-normalize, and section 4 for
+# keys).  A token v becomes u = sqrt(d) v / ||v|| (s1 = ||v|| / sqrt(d)), the channel mean
+# o of the u is subtracted, and the result is normalized again (s2); v = s1 (s2 x + o).
+# The codec stores a norm and a direction, so quantizing w = v - s1 o = s1 s2 x gives NSN's
+# x as the direction and s1 s2 sqrt(d) as the norm: the second normalization is the
+# codec's own.  Keys are rotary-embedded first (the same order as the plain path).
+# ----------------------------------------------------------------------------------
+def nsn_mean(x, *, positions=None, rope_base: float = 0.0):
+    """o = mean over the rows of x ([n, d]) of sqrt(d) x_i / ||x_i|| (keys: of RoPE(x_i)),
+    in fp64; zero rows contribute zero vectors; no rows give o = 0."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if len(x) == 0:
+        return np.zeros(d)
+    if rope_base != 0:
+        x = rope(x, positions, rope_base)
+    n = np.sqrt(np.sum(x * x, axis=-1))
+    u = np.zeros_like(x)
+    nz = n > 0
+    u[nz] = math.sqrt(d) * x[nz] / n[nz][:, None]
+    return np.sum(u, axis=0) / len(x)
+
+
+def nsn_rotated_mean(o, codec: Codec) -> np.ndarray:
+    """Pi o for the stored fp32 mean o, rounded to fp32 (the form the cache stores)."""
+    o32 = np.asarray(o, dtype=np.float32).astype(np.float64)
+    return (o32 @ codec.Pi.T).astype(np.float32).astype(np.float64)
 
 
 # ----------------------------------------------------------------------------------
@@ -348,6 +391,9 @@ def encode(x, codec: Codec, *, kind: str, positions=None, rope_base: float = 0.0
 #           tokens and coordinate j, a (32*bits_v)-bit little-endian integer whose bits
 #           [bits_v*i, bits_v*(i+1)) hold the value code of token 32*tile + i.
 #   Vnorm:  [batch][kv_heads][capacity] fp16 n.
+#   NSN caches (desc nsn = 1, written after the desc in the header): Knorm records are 8
+#   bytes {fp16 n, fp16 ||r||, fp16 s1, 0}, Vnorm records 4 bytes {fp16 n, fp16 s1}, and a
+#   last region holds per unit [o_K, o_V, Pi o_K, Pi o_V] as fp32 [d] each.
 #   Each region starts at a multiple of 256 bytes.
 # ----------------------------------------------------------------------------------
 CACHE_MAGIC = 0x564B5154
@@ -359,21 +405,24 @@ def _align(x, a=256):
     return (x + a - 1) // a * a
 
 
-def cache_layout(batch, kv_heads, d, capacity, bits_k, bits_v, m):
+def cache_layout(batch, kv_heads, d, capacity, bits_k, bits_v, m, nsn=0):
     kbytes = (bits_k * d + m) // 8
     units = batch * kv_heads
     tiles = (capacity + 31) // 32
-    off = {}
+    off = {"knrec": 8 if nsn else 4, "vnrec": 4 if nsn else 2}
     cur = HEADER_BYTES
     off["kbits"] = cur
     cur = _align(cur + units * capacity * kbytes)
     off["knorm"] = cur
-    cur = _align(cur + units * capacity * 4)
+    cur = _align(cur + units * capacity * off["knrec"])
     if bits_v > 0:
         off["vcodes"] = cur
         cur = _align(cur + units * tiles * d * 4 * bits_v)
         off["vnorm"] = cur
-        cur = _align(cur + units * capacity * 2)
+        cur = _align(cur + units * capacity * off["vnrec"])
+    if nsn:
+        off["nsn"] = cur
+        cur = _align(cur + units * 4 * d * 4)
     off["total"] = cur
     off["kbytes"] = kbytes
     off["tiles"] = tiles
@@ -393,17 +442,22 @@ def pack_cache(desc: dict, fields: dict, start_pos: int = 0, image: np.ndarray |
     """Write tokens [start_pos, start_pos + n) of every (batch, kv-head) unit.
 
     fields: kcodes [B, H, n, d], n16 [B, H, n], rn16 [B, H, n], bits [B, H, n, m],
-            and if bits_v > 0: vcodes [B, H, n, d], vn16 [B, H, n]."""
+            and if bits_v > 0: vcodes [B, H, n, d], vn16 [B, H, n];
+            NSN caches also ks1, vs1 [B, H, n] and the unit means ok, ov, pok, pov [B, H, d]."""
     B, H, d, cap = desc["batch"], desc["kv_heads"], desc["d"], desc["capacity"]
     bk, bv, m = desc["bits_k"], desc["bits_v"], desc["m"]
-    lay = cache_layout(B, H, d, cap, bk, bv, m)
+    nsn = int(desc.get("nsn", 0))
+    lay = cache_layout(B, H, d, cap, bk, bv, m, nsn)
     if image is None:
         image = np.zeros(lay["total"], dtype=np.uint8)
     hdr = np.zeros(HEADER_BYTES // 4, dtype=np.uint32)
     hdr[0], hdr[1], hdr[2] = CACHE_MAGIC, CACHE_VERSION, flags
-    hdr[4:11] = np.array([B, H, d, cap, bk, bv, m], dtype=np.int64).astype(np.uint32)
+    hdr[4:12] = np.array([B, H, d, cap, bk, bv, m, nsn], dtype=np.int64).astype(np.uint32)
     hdr[2] |= np.uint32(image[8:12].view(np.uint32)[0])
     image[:HEADER_BYTES] = hdr.view(np.uint8)
+    if nsn:
+        means = np.stack([np.asarray(fields[f], dtype=np.float32) for f in ("ok", "ov", "pok", "pov")], axis=2)
+        image[lay["nsn"]:lay["nsn"] + B * H * 4 * d * 4] = means.reshape(-1).view(np.uint8)
 
     kcodes = np.asarray(fields["kcodes"])
     n = kcodes.shape[2]
@@ -416,9 +470,12 @@ def pack_cache(desc: dict, fields: dict, start_pos: int = 0, image: np.ndarray |
     rec = _bits_to_bytes(kbitsm)  # [B,H,n,kb]
     kreg = image[lay["kbits"]:lay["kbits"] + B * H * cap * kb].reshape(B, H, cap, kb)
     kreg[:, :, start_pos:start_pos + n, :] = rec
-    norms = np.stack([np.asarray(fields["n16"]), np.asarray(fields["rn16"])], axis=-1)
-    nreg = image[lay["knorm"]:lay["knorm"] + B * H * cap * 4].view(np.float16).reshape(B, H, cap, 2)
-    nreg[:, :, start_pos:start_pos + n, :] = norms.astype(np.float16)
+    kn = lay["knrec"] // 2
+    norms = [np.asarray(fields["n16"]), np.asarray(fields["rn16"])]
+    if nsn:
+        norms += [np.asarray(fields["ks1"]), np.zeros_like(np.asarray(fields["n16"]))]
+    nreg = image[lay["knorm"]:lay["knorm"] + B * H * cap * 2 * kn].view(np.float16).reshape(B, H, cap, kn)
+    nreg[:, :, start_pos:start_pos + n, :] = np.stack(norms, axis=-1).astype(np.float16)
     if bv > 0:
         vcodes = np.asarray(fields["vcodes"]).astype(np.int64)
         tiles = lay["tiles"]
@@ -434,8 +491,10 @@ def pack_cache(desc: dict, fields: dict, start_pos: int = 0, image: np.ndarray |
                 cur = vreg[:, :, tile, :, byte].astype(np.int64)
                 cur = (cur & ~(1 << sh)) | (bit << sh)
                 vreg[:, :, tile, :, byte] = cur.astype(np.uint8)
-        vnreg = image[lay["vnorm"]:lay["vnorm"] + B * H * cap * 2].view(np.float16).reshape(B, H, cap)
-        vnreg[:, :, start_pos:start_pos + n] = np.asarray(fields["vn16"]).astype(np.float16)
+        vn = lay["vnrec"] // 2
+        vnorms = [np.asarray(fields["vn16"])] + ([np.asarray(fields["vs1"])] if nsn else [])
+        vnreg = image[lay["vnorm"]:lay["vnorm"] + B * H * cap * 2 * vn].view(np.float16).reshape(B, H, cap, vn)
+        vnreg[:, :, start_pos:start_pos + n, :] = np.stack(vnorms, axis=-1).astype(np.float16)
     return image
 
 
@@ -443,7 +502,8 @@ def unpack_cache(image: np.ndarray, desc: dict, length: int) -> dict:
     """Inverse of pack_cache for tokens [0, length).  Codes and bits come back as uint8."""
     B, H, d, cap = desc["batch"], desc["kv_heads"], desc["d"], desc["capacity"]
     bk, bv, m = desc["bits_k"], desc["bits_v"], desc["m"]
-    lay = cache_layout(B, H, d, cap, bk, bv, m)
+    nsn = int(desc.get("nsn", 0))
+    lay = cache_layout(B, H, d, cap, bk, bv, m, nsn)
     image = np.asarray(image, dtype=np.uint8)
     hdr = image[:HEADER_BYTES].view(np.uint32)
     kb = lay["kbytes"]
@@ -456,9 +516,15 @@ def unpack_cache(image: np.ndarray, desc: dict, length: int) -> dict:
         "magic": int(hdr[0]), "version": int(hdr[1]), "flags": int(hdr[2]),
         "kcodes": kcodes, "bits": bitsall[..., bk * d:bk * d + m],
     }
-    nreg = image[lay["knorm"]:lay["knorm"] + B * H * cap * 4].view(np.float16).reshape(B, H, cap, 2)
+    kn = lay["knrec"] // 2
+    nreg = image[lay["knorm"]:lay["knorm"] + B * H * cap * 2 * kn].view(np.float16).reshape(B, H, cap, kn)
     out["n16"] = nreg[:, :, :length, 0].astype(np.float64)
     out["rn16"] = nreg[:, :, :length, 1].astype(np.float64)
+    if nsn:
+        out["ks1"] = nreg[:, :, :length, 2].astype(np.float64)
+        means = image[lay["nsn"]:lay["nsn"] + B * H * 4 * d * 4].view(np.float32).reshape(B, H, 4, d)
+        for i, f in enumerate(("ok", "ov", "pok", "pov")):
+            out[f] = means[:, :, i].astype(np.float64)
     if bv > 0:
         tiles = lay["tiles"]
         wbytes = 4 * bv
@@ -471,8 +537,11 @@ def unpack_cache(image: np.ndarray, desc: dict, length: int) -> dict:
         for p in range(bv):
             codes |= vbits[..., p] << np.uint8(p)
         out["vcodes"] = codes.transpose(0, 1, 2, 4, 3).reshape(B, H, used * 32, d)[:, :, :length]
-        vnreg = image[lay["vnorm"]:lay["vnorm"] + B * H * cap * 2].view(np.float16).reshape(B, H, cap)
-        out["vn16"] = vnreg[:, :, :length].astype(np.float64)
+        vn = lay["vnrec"] // 2
+        vnreg = image[lay["vnorm"]:lay["vnorm"] + B * H * cap * 2 * vn].view(np.float16).reshape(B, H, cap, vn)
+        out["vn16"] = vnreg[:, :, :length, 0].astype(np.float64)
+        if nsn:
+            out["vs1"] = vnreg[:, :, :length, 1].astype(np.float64)
     return out
 
 
@@ -516,11 +585,15 @@ def attend(fields: dict, q, codec: Codec, *, q_pos: int, rope_base: float, scale
                 continue
             s = estimate_scores(qr, sq, fields["kcodes"][b, g, :length], fields["n16"][b, g, :length],
                                 fields["rn16"][b, g, :length], fields["bits"][b, g, :length], codec)
+            if "ks1" in fields:   # NSN: the mean's share s1 <q, o>, in the rotated basis
+                s = s + fields["ks1"][b, g, :length] * (fields["pok"][b, g] @ qr)
             scores[b, h] = s
             lam = scale * s
             p = np.exp(lam - np.max(lam))
             p = p / np.sum(p)
             vhat = fields["vn16"][b, g, :length, None] * codec.cb_v.c[fields["vcodes"][b, g, :length]]
+            if "vs1" in fields:
+                vhat = vhat + fields["vs1"][b, g, :length, None] * fields["pov"][b, g][None, :]
             o_rot = p @ vhat
             out[b, h] = codec.Pi.T @ o_rot
     return out, scores
@@ -560,6 +633,8 @@ def attend_window(fields: dict, win_k, win_v, q, codec: Codec, *, q_pos: int, ro
                 s[:length] = estimate_scores(qr, sq, fields["kcodes"][b, g, :length],
                                              fields["n16"][b, g, :length], fields["rn16"][b, g, :length],
                                              fields["bits"][b, g, :length], codec)
+                if "ks1" in fields:
+                    s[:length] += fields["ks1"][b, g, :length] * (fields["pok"][b, g] @ qr)
             if win_len > 0:
                 kr = rope(wk[b, g, :win_len], pos, rope_base) if rope_base != 0 else wk[b, g, :win_len]
                 s[length:] = kr @ qp
@@ -570,6 +645,8 @@ def attend_window(fields: dict, win_k, win_v, q, codec: Codec, *, q_pos: int, ro
             o = np.zeros(d)
             if length > 0:
                 vhat = fields["vn16"][b, g, :length, None] * codec.cb_v.c[fields["vcodes"][b, g, :length]]
+                if "vs1" in fields:
+                    vhat = vhat + fields["vs1"][b, g, :length, None] * fields["pov"][b, g][None, :]
                 o += codec.Pi.T @ (p[:length] @ vhat)
             if win_len > 0:
                 o += p[length:] @ wv[b, g, :win_len]
@@ -598,14 +675,25 @@ def decode_step(state: dict, new_k, new_v, q, codec: Codec, *, q_pos: int, rope_
     B, H, cap, d = wk.shape
     if state["win_len"] == cap:
         pos = state["length"] + np.arange(cap)
-        ke = encode(wk.reshape(-1, d), codec, kind="key", positions=np.tile(pos, B * H), rope_base=rope_base)
-        ve = encode(wv.reshape(-1, d), codec, kind="value")
+        old = state["fields"]
+        nsn = "ok" in old   # NSN cache: the flushed tokens use the stored means
+        ok = np.repeat(np.asarray(old["ok"]).reshape(B * H, 1, d), cap, axis=1).reshape(-1, d) if nsn else None
+        ov = np.repeat(np.asarray(old["ov"]).reshape(B * H, 1, d), cap, axis=1).reshape(-1, d) if nsn else None
+        ke = encode(wk.reshape(-1, d), codec, kind="key", positions=np.tile(pos, B * H), rope_base=rope_base,
+                    nsn_o=ok)
+        ve = encode(wv.reshape(-1, d), codec, kind="value", nsn_o=ov)
         new = {"kcodes": ke["codes"].reshape(B, H, cap, d), "n16": ke["n16"].reshape(B, H, cap),
                "rn16": ke["rn16"].reshape(B, H, cap), "bits": ke["bits"].reshape(B, H, cap, codec.m),
                "vcodes": ve["codes"].reshape(B, H, cap, d), "vn16": ve["n16"].reshape(B, H, cap)}
-        old = state["fields"]
+        names = _ATTEND_FIELDS
+        if nsn:
+            new["ks1"] = ke["s1_16"].reshape(B, H, cap)
+            new["vs1"] = ve["s1_16"].reshape(B, H, cap)
+            names = names + ("ks1", "vs1")
         state["fields"] = {f: np.concatenate([np.asarray(old[f])[:, :, :state["length"]], new[f]], axis=2)
-                           for f in _ATTEND_FIELDS}
+                           for f in names}
+        if nsn:
+            state["fields"].update({f: old[f] for f in ("ok", "ov", "pok", "pov")})
         state["length"] += cap
         state["win_len"] = 0
     w = state["win_len"]

@@ -347,16 +347,36 @@ def test_attend_window_is_textbook_attention_over_both_sets(O):
     np.testing.assert_allclose(o2[0, 0], wv[0, 0, 0], atol=1e-12)   # one token: its value
 
 
-def _encode_fields(O, codec, K, V, base):
+def _encode_fields(O, codec, K, V, base, means=None):
+    """Tokens [0, T) of every unit; means = (o_K, o_V) [B, H, d] fp32 for an NSN cache."""
     B, H, T, d = K.shape
-    ke = O.encode(K.reshape(-1, d), codec, kind="key", positions=np.tile(np.arange(T), B * H), rope_base=base)
-    ve = O.encode(V.reshape(-1, d), codec, kind="value")
-    return {"kcodes": ke["codes"].reshape(B, H, T, d), "n16": ke["n16"].reshape(B, H, T),
-            "rn16": ke["rn16"].reshape(B, H, T), "bits": ke["bits"].reshape(B, H, T, codec.m),
-            "vcodes": ve["codes"].reshape(B, H, T, d), "vn16": ve["n16"].reshape(B, H, T)}
+    ok = ov = None
+    if means is not None:
+        ok = np.repeat(means[0].reshape(B * H, 1, d), T, axis=1).reshape(-1, d)
+        ov = np.repeat(means[1].reshape(B * H, 1, d), T, axis=1).reshape(-1, d)
+    ke = O.encode(K.reshape(-1, d), codec, kind="key", positions=np.tile(np.arange(T), B * H), rope_base=base,
+                  nsn_o=ok)
+    ve = O.encode(V.reshape(-1, d), codec, kind="value", nsn_o=ov)
+    f = {"kcodes": ke["codes"].reshape(B, H, T, d), "n16": ke["n16"].reshape(B, H, T),
+         "rn16": ke["rn16"].reshape(B, H, T), "bits": ke["bits"].reshape(B, H, T, codec.m),
+         "vcodes": ve["codes"].reshape(B, H, T, d), "vn16": ve["n16"].reshape(B, H, T)}
+    if means is not None:
+        f.update(ks1=ke["s1_16"].reshape(B, H, T), vs1=ve["s1_16"].reshape(B, H, T), ok=means[0], ov=means[1],
+                 pok=O.nsn_rotated_mean(means[0].reshape(-1, d), codec).reshape(B, H, d),
+                 pov=O.nsn_rotated_mean(means[1].reshape(-1, d), codec).reshape(B, H, d))
+    return f
 
 
-def test_decode_step_flush_schedule(O):
+def _prefill_means(O, K, V, base):
+    """NSN means of each unit over its tokens (keys at positions 0, 1, ...), fp32."""
+    B, H, T, d = K.shape
+    ok = np.stack([[O.nsn_mean(K[b, h], positions=np.arange(T), rope_base=base) for h in range(H)] for b in range(B)])
+    ov = np.stack([[O.nsn_mean(V[b, h]) for h in range(H)] for b in range(B)])
+    return ok.astype(np.float32), ov.astype(np.float32)
+
+
+@pytest.mark.parametrize("nsn", [False, True])
+def test_decode_step_flush_schedule(O, nsn):
     # A generation loop through decode_step against a closed form of its schedule: with L0
     # tokens packed up front and a window of cap, after step s (0-based) the packed part
     # holds L0 + cap * floor(s / cap) tokens and the window the other s % cap + 1, all
@@ -368,7 +388,9 @@ def test_decode_step_flush_schedule(O):
     K = rng.standard_normal((B, Hkv, L0 + steps, d))
     V = rng.standard_normal((B, Hkv, L0 + steps, d))
     base, scale = 10000.0, 0.0
-    st = {"fields": _encode_fields(O, codec, K[:, :, :L0], V[:, :, :L0], base), "length": L0,
+    # NSN: the means come from the prefill (the append at position 0) and stay
+    means = _prefill_means(O, K[:, :, :L0], V[:, :, :L0], base) if nsn else None
+    st = {"fields": _encode_fields(O, codec, K[:, :, :L0], V[:, :, :L0], base, means), "length": L0,
           "win_k": np.zeros((B, Hkv, cap, d)), "win_v": np.zeros((B, Hkv, cap, d)), "win_len": 0}
     for s in range(steps):
         n = L0 + s + 1
@@ -377,13 +399,15 @@ def test_decode_step_flush_schedule(O):
                                 scale=scale, kv_heads=Hkv)
         P = L0 + cap * (s // cap)
         assert (st["length"], st["win_len"]) == (P, n - P)
-        ref = _encode_fields(O, codec, K[:, :, :P], V[:, :, :P], base)
+        ref = _encode_fields(O, codec, K[:, :, :P], V[:, :, :P], base, means)
         for f in ref:
             np.testing.assert_array_equal(st["fields"][f], ref[f])
         o2, s2 = O.attend_window(ref, K[:, :, P:n], V[:, :, P:n], q, codec, q_pos=n - 1, rope_base=base,
                                  scale=scale, kv_heads=Hkv, length=P, win_len=n - P)
         np.testing.assert_allclose(out, o2, rtol=0, atol=1e-12)
         np.testing.assert_allclose(sc, s2, rtol=0, atol=1e-12)
+    if nsn:
+        return
     # no packed tokens and a window that never fills: exact softmax attention over RoPE'd keys
     st = {"fields": _encode_fields(O, codec, K[:, :, :0], V[:, :, :0], base), "length": 0,
           "win_k": np.zeros((B, Hkv, 8, d)), "win_v": np.zeros((B, Hkv, 8, d)), "win_len": 0}
@@ -517,3 +541,124 @@ def test_search_scores_match_attention_estimator_and_recall(O):
     gt, _ = O.exact_topk(db, qs, 10)
     recall1 = np.mean([gt[i, 0] in idx[i] for i in range(20)])
     assert recall1 >= 0.8
+
+
+# ------------------------------------------------------------------ NSN ([NSNQuant] 1, 4)
+def test_nsn_mean_worked_cases(O):
+    # two tokens along different axes: each is scaled to norm sqrt(4) = 2, o is their mean
+    x = np.array([[2.0, 0, 0, 0], [0, 0, 0, 3.0]])
+    np.testing.assert_allclose(O.nsn_mean(x), [1.0, 0, 0, 1.0], atol=1e-15)
+    # zero tokens count as zero vectors; no tokens give zero
+    np.testing.assert_allclose(O.nsn_mean(np.vstack([x, np.zeros(4)])), [2 / 3, 0, 0, 2 / 3], atol=1e-15)
+    np.testing.assert_array_equal(O.nsn_mean(np.zeros((0, 4))), np.zeros(4))
+    # keys are rotary-embedded first: d = 2 rotates position p by p radians, so (r, 0) at
+    # positions 0 and 1 normalize to sqrt(2) (1, 0) and sqrt(2) (cos 1, sin 1)
+    k = np.array([[5.0, 0.0], [0.5, 0.0]])
+    want = math.sqrt(2) / 2 * np.array([1 + math.cos(1.0), math.sin(1.0)])
+    np.testing.assert_allclose(O.nsn_mean(k, positions=[0, 1], rope_base=10000.0), want, atol=1e-14)
+
+
+def test_nsn_encode_decomposition_and_zero_mean_case(O):
+    # NSN writes v = s1 (s2 x + o); the encoder quantizes w = v - s1_16 o (rotated, with the
+    # stored fp32 Pi o), so Pi^T w + s1_16 Pi^T (Pi o) gives back v, |w| = s1 s2 sqrt(d)
+    # up to the fp16 rounding of s1, and with o = 0 every code equals the plain encoder's
+    d = 64
+    codec = O.make_codec(d, 2, 3, d, seed=2)
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((40, d)) * 3 + 5.0           # a strong common offset
+    o = O.nsn_mean(v).astype(np.float32)
+    e = O.encode(v, codec, kind="value", nsn_o=o)
+    s1 = np.linalg.norm(v, axis=1) / math.sqrt(d)
+    np.testing.assert_array_equal(e["s1_16"], s1.astype(np.float16).astype(np.float64))
+    back = e["y"] @ codec.Pi + e["s1_16"][:, None] * (e["po"] @ codec.Pi)
+    np.testing.assert_allclose(back, v, atol=1e-11)
+    u = math.sqrt(d) * v / np.linalg.norm(v, axis=1, keepdims=True)
+    w_page = u - o.astype(np.float64)                     # the page's shifted token
+    s2 = np.linalg.norm(w_page, axis=1) / math.sqrt(d)
+    np.testing.assert_allclose(e["n"], s1 * s2 * math.sqrt(d), rtol=2e-3)   # fp16 s1, fp32 o
+    z = O.encode(v, codec, kind="value", nsn_o=np.zeros(d, np.float32))
+    p = O.encode(v, codec, kind="value")
+    np.testing.assert_array_equal(z["codes"], p["codes"])
+    np.testing.assert_array_equal(z["n16"], p["n16"])
+
+
+def test_nsn_lowers_error_on_offset_tokens(O):
+    # the point of the shift: tokens sharing a large common direction are reconstructed
+    # more accurately after NSN than by the plain codec (same bits); a sign error in the
+    # shift or its reconstruction would make NSN worse, not better
+    d = 128
+    codec = O.make_codec(d, 2, 3, d, seed=1)
+    rng = np.random.default_rng(8)
+    mu = rng.standard_normal(d) * 4
+    v = mu + rng.standard_normal((300, d))
+    o = O.nsn_mean(v).astype(np.float32)
+
+    def recon(e, nsn):
+        r = (e["n16"][:, None] * codec.cb_v.c[e["codes"]]) @ codec.Pi
+        return r + e["s1_16"][:, None] * (e["po"] @ codec.Pi) if nsn else r
+
+    err_plain = np.mean(np.sum((recon(O.encode(v, codec, kind="value"), False) - v) ** 2, axis=1))
+    err_nsn = np.mean(np.sum((recon(O.encode(v, codec, kind="value", nsn_o=o), True) - v) ** 2, axis=1))
+    assert err_nsn < 0.2 * err_plain
+
+
+def test_nsn_attention_is_textbook_on_the_lattice(O):
+    # packed tokens whose shifted part lies on the codebook lattice (zero residual): the
+    # NSN attention must equal softmax(q K^T scale) V with K = Pi^T (n c[code]) + s1 o_K and
+    # V = Pi^T (n_v c[code_v]) + s1_v o_V, the means entering through the stored Pi o
+    d, B, Hkv, Hq, T = 64, 1, 2, 4, 29
+    codec = O.make_codec(d, 2, 3, d, seed=4)
+    rng = np.random.default_rng(9)
+    kc = rng.integers(0, 4, (B, Hkv, T, d))
+    vc = rng.integers(0, 8, (B, Hkv, T, d))
+    f16 = lambda a: np.asarray(a).astype(np.float16).astype(np.float64)
+    fields = _fields_from_khat(O, codec, kc, f16(rng.uniform(1, 9, (B, Hkv, T))), vc,
+                               f16(rng.uniform(1, 9, (B, Hkv, T))))
+    ok = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+    ov = rng.standard_normal((B, Hkv, d)).astype(np.float32)
+    fields.update(ks1=f16(rng.uniform(0.5, 3, (B, Hkv, T))), vs1=f16(rng.uniform(0.5, 3, (B, Hkv, T))),
+                  ok=ok, ov=ov, pok=O.nsn_rotated_mean(ok.reshape(-1, d), codec).reshape(B, Hkv, d),
+                  pov=O.nsn_rotated_mean(ov.reshape(-1, d), codec).reshape(B, Hkv, d))
+    q = rng.standard_normal((B, Hq, d))
+    q_pos, base, scale = 50, 10000.0, 0.3
+    out, scores = O.attend(fields, q, codec, q_pos=q_pos, rope_base=base, scale=scale, kv_heads=Hkv, length=T)
+    P = codec.Pi
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        K = (fields["n16"][0, g][:, None] * codec.cb_k.c[kc[0, g]]) @ P + fields["ks1"][0, g][:, None] * (fields["pok"][0, g] @ P)
+        V = (fields["vn16"][0, g][:, None] * codec.cb_v.c[vc[0, g]]) @ P + fields["vs1"][0, g][:, None] * (fields["pov"][0, g] @ P)
+        qq = O.rope(q[0, h][None], [q_pos], base)[0]
+        sc = K @ qq
+        w = np.exp(scale * sc - np.max(scale * sc))
+        np.testing.assert_allclose(scores[0, h], sc, rtol=1e-11, atol=1e-10)
+        np.testing.assert_allclose(out[0, h], (w / w.sum()) @ V, rtol=1e-11, atol=1e-10)
+    # the same tokens plus an empty window through attend_window: identical
+    o2, s2 = O.attend_window(fields, np.zeros((B, Hkv, 1, d)), np.zeros((B, Hkv, 1, d)), q, codec, q_pos=q_pos,
+                             rope_base=base, scale=scale, kv_heads=Hkv, length=T, win_len=0)
+    np.testing.assert_allclose(o2, out, atol=1e-12)
+    np.testing.assert_allclose(s2, scores, atol=1e-12)
+
+
+def test_nsn_pack_layout(O):
+    # NSN records: key norms {n, |r|, s1, 0} (8 bytes), value norms {n, s1} (4 bytes), and
+    # per unit [o_K, o_V, Pi o_K, Pi o_V] as fp32 after the value norms; nsn in the header
+    desc = dict(batch=1, kv_heads=2, d=8, capacity=5, bits_k=2, bits_v=3, m=8, nsn=1)
+    lay = O.cache_layout(1, 2, 8, 5, 2, 3, 8, 1)
+    n = 2
+    z = np.zeros((1, 2, n))
+    means = {k: np.arange(16, dtype=np.float32).reshape(1, 2, 8) + 100 * i
+             for i, k in enumerate(("ok", "ov", "pok", "pov"))}
+    f = dict(kcodes=np.zeros((1, 2, n, 8), int), bits=np.zeros((1, 2, n, 8), int), n16=z + 1.5, rn16=z + 0.25,
+             ks1=z + 3.0, vcodes=np.zeros((1, 2, n, 8), int), vn16=z + 2.0, vs1=z + 0.5, **means)
+    img = O.pack_cache(desc, f, start_pos=3)
+    assert list(img[16:48].view(np.int32)) == [1, 2, 8, 5, 2, 3, 8, 1]
+    # unit 1, token 4: key record at knorm + (5 + 4) * 8, value record at vnorm + (5 + 4) * 4
+    assert list(img[lay["knorm"] + 72:lay["knorm"] + 80].view(np.float16)) == [1.5, 0.25, 3.0, 0.0]
+    assert list(img[lay["vnorm"] + 36:lay["vnorm"] + 40].view(np.float16)) == [2.0, 0.5]
+    blk = img[lay["nsn"]:lay["nsn"] + 2 * 4 * 8 * 4].view(np.float32).reshape(2, 4, 8)
+    assert blk[1, 2, 3] == means["pok"][0, 1, 3] and blk[0, 1, 7] == means["ov"][0, 0, 7]
+    u = O.unpack_cache(img, desc, 5)
+    np.testing.assert_array_equal(u["ks1"][:, :, 3:], z + 3.0)
+    np.testing.assert_array_equal(u["vs1"][:, :, 3:], z + 0.5)
+    for k in means:
+        np.testing.assert_array_equal(u[k], means[k])
