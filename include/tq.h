@@ -58,9 +58,16 @@ typedef struct {
   uint64_t seed;
 } tq_codec_desc;
 
-/* Packed cache shape: `batch` x `kv_heads` units of `capacity` token slots each. */
+/* Packed cache shape: `batch` x `kv_heads` units of `capacity` token slots each.
+ * nsn = 1 selects the NSN pre-transform ([NSNQuant] section 1: tokens normalized to norm
+ * sqrt(d), the channel mean shifted out, normalized again) for keys and values: each
+ * token v is stored as the codec of w = v - s1 o with s1 = ||v|| / sqrt(d) kept in fp16
+ * and o the unit's channel mean (tq_nsn_set_means); the codec's own norm and direction
+ * are NSN's second normalization.  Requires bits_v > 0 and d = 64 or 128; nsn = 0 is the
+ * plain codec. */
 typedef struct {
   int32_t batch, kv_heads, d, capacity, bits_k, bits_v, m;
+  int32_t nsn;
 } tq_cache_desc;
 
 typedef void *tq_stream_t; /* hipStream_t */
@@ -101,8 +108,9 @@ size_t tq_codec_bytes(const tq_codec_desc *desc);
 tq_status tq_codec_build(const tq_codec_desc *desc, void *host_out, size_t bytes);
 
 /* Size in bytes of a packed cache (header + key bits + key norms [+ value codes + value
- * norms]), format version 1:
- *   header  256 B: u32 magic 0x564B5154, u32 version 1, u32 flags, u32 0, then the desc.
+ * norms] [+ NSN means]), format version 1:
+ *   header  256 B: u32 magic 0x564B5154, u32 version 1, u32 flags, u32 0, then the desc
+ *           (eight i32, nsn last).
  *   Kbits   [batch][kv_heads][capacity][(bits_k d + m)/8]: bit p of each key code as
  *           plane p (coordinate j at byte j/8, bit j%8), planes p = 0..bits_k-1, then the
  *           m QJL sign bits.
@@ -111,11 +119,15 @@ tq_status tq_codec_build(const tq_codec_desc *desc, void *host_out, size_t bytes
  *           coordinate, token i's value code in bits [bits_v i, bits_v (i+1)) of a
  *           little-endian integer.
  *   Vnorm   [batch][kv_heads][capacity] fp16 ||y||.
+ *   NSN caches: Knorm records are {fp16 ||y||, fp16 ||r||, fp16 s1, 0} (8 bytes), Vnorm
+ *           records {fp16 ||y||, fp16 s1} (4 bytes), and a last region holds per unit
+ *           [o_K, o_V, Pi o_K, Pi o_V], fp32 [d] each (the keys' mean taken after RoPE).
  * Regions start at multiples of 256 bytes.  Returns 0 if the desc is invalid. */
 size_t tq_cache_bytes(const tq_cache_desc *desc);
 
-/* Write the cache header (magic, version, desc) and clear the flags word.  Token slots
- * are not touched.  Enqueued on `stream`. */
+/* Write the cache header (magic, version, desc) and clear the flags word; for an NSN
+ * cache also set the means to zero.  Token slots are not touched.  Enqueued on
+ * `stream`. */
 tq_status tq_cache_init(const tq_cache_desc *desc, void *cache_dev, tq_stream_t stream);
 
 /* Append tokens [start_pos, start_pos + n_new) of every (batch, kv-head) unit to the
@@ -126,6 +138,9 @@ tq_status tq_cache_init(const tq_cache_desc *desc, void *cache_dev, tq_stream_t 
  *           of boundaries t with y_j/n >= t; r = y - fp16(n) c[code]; QJL bit i =
  *           [(S r)_i >= 0]; stored: planes, sign bits, fp16 n, fp16 ||r||.
  *   values: y = Pi v (no RoPE), codes with the value codebook, fp16 n.
+ *   NSN caches: before the norm, s1 = ||y|| / sqrt(d) is rounded to fp16 and
+ *           y = y - s1 (Pi o) with the unit's stored fp32 Pi o (keys o_K, values o_V);
+ *           s1 is stored next to the norms.
  * k, v: device arrays [batch][kv_heads][n_new][d] of `dtype`, contiguous; v must be NULL
  * iff desc->bits_v == 0; both must be 16-byte aligned (TQ_EINVAL otherwise).
  * n_new == 0 is a no-op.  Writes never touch other slots. */
@@ -227,6 +242,23 @@ tq_status tq_decode_step(const tq_cache_desc *desc, const void *codec_dev, void 
                          const void *q, tq_dtype dtype, int32_t q_heads, int32_t q_pos,
                          float rope_base, float scale, float *out, float *scores, void *ws,
                          size_t ws_bytes, tq_stream_t stream);
+
+/* Workspace bytes tq_nsn_set_means needs for n tokens per unit. */
+size_t tq_nsn_means_workspace_bytes(const tq_cache_desc *desc, int32_t n);
+
+/* Channel means of an NSN cache ([NSNQuant] section 1, the shift step; section 4 puts
+ * NSN on keys before RoPE, here after it as for the plain codec): for every unit,
+ * o_K = mean over its n tokens of sqrt(d) RoPE(k, pos) / ||k|| (positions start_pos ...)
+ * and o_V = mean of sqrt(d) v / ||v||, accumulated in fp64 in a fixed order and stored in
+ * fp32, then Pi o_K and Pi o_V (fp64, stored in fp32).  A zero token counts as a zero
+ * vector.  Later tq_quantize_kv calls on the cache shift their tokens by these means;
+ * typically k, v are the prefill and the call precedes its tq_quantize_kv.  k, v:
+ * [batch][kv_heads][n][d] of `dtype`, 16-byte aligned; n >= 1; ws: at least
+ * tq_nsn_means_workspace_bytes.  TQ_EINVAL on a cache without nsn. */
+tq_status tq_nsn_set_means(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
+                           const void *k, const void *v, tq_dtype dtype, int32_t start_pos,
+                           int32_t n, float rope_base, void *ws, size_t ws_bytes,
+                           tq_stream_t stream);
 
 /* Workspace bytes tq_search_topk needs. */
 size_t tq_search_workspace_bytes(const tq_cache_desc *db, int32_t n_db, int32_t nq, int32_t k);

@@ -324,9 +324,10 @@ def encode(x, codec: Codec, *, kind: str, positions=None, rope_base: float = 0.0
     extra = {}
     if nsn_o is not None:
         po = nsn_rotated_mean(nsn_o, codec)
-        s1_16, over_s = fp16_sat(np.sqrt(np.sum(y * y, axis=-1)) / math.sqrt(codec.d))
+        s1 = np.sqrt(np.sum(y * y, axis=-1)) / math.sqrt(codec.d)
+        s1_16, over_s = fp16_sat(s1)
         y = y - s1_16[..., None] * po
-        extra = {"s1_16": s1_16, "po": po, "over_s": over_s}
+        extra = {"s1": s1, "s1_16": s1_16, "po": po, "over_s": over_s}
     n = np.sqrt(np.sum(y * y, axis=-1))
     safe = np.where(n > 0, n, 1.0)
     u = np.where(n[..., None] > 0, y / safe[..., None], 0.0)
@@ -335,7 +336,7 @@ def encode(x, codec: Codec, *, kind: str, positions=None, rope_base: float = 0.0
     n16, over_n = fp16_sat(n)
     out = {"y": y, "u": u, "codes": codes, "n": n, "n16": n16, "overflow": over_n.copy()}
     if extra:
-        out["s1_16"], out["po"] = extra["s1_16"], extra["po"]
+        out["s1"], out["s1_16"], out["po"] = extra["s1"], extra["s1_16"], extra["po"]
         out["overflow"] = out["overflow"] | extra["over_s"]
     if kind in ("key", "db"):
         r = y - n16[..., None] * cb.c[codes]

@@ -240,11 +240,63 @@ def test_window_attention(tq, P, bk, bv, d, G, L, Wn, cap, dt):
         assert e3 <= TOL
 
 
-@pytest.mark.parametrize("bk,bv,d,G,L0,cap,steps,dt", [
-    (2, 3, 128, 4, 300, 16, 40, "bf16"),   # MFMA path, two flushes
-    (3, 4, 64, 8, 0, 8, 20, "f32"),        # fp32 path, starting from an empty cache
+@pytest.mark.parametrize("bk,d,G,L0,T,dist", [
+    (2, 128, 8, 700, 900, "laplace"),      # MFMA path, means from a prefill, ragged append
+    (3, 64, 4, 300, 530, "student_t3"),
+    (1, 128, 2, 64, 64, "normal"),         # means over the whole cache
 ])
-def test_decode_step_loop(tq, P, bk, bv, d, G, L0, cap, steps, dt):
+def test_nsn_codes_and_decode(tq, P, bk, d, G, L0, T, dist):
+    """NSN caches (NSNQuant section 1): the means over the prefill, codes and s1 of every
+    token against the oracle's NSN encode; decode and logits over the oracle's NSN cache
+    and end to end over the GPU's own."""
+    w = W.LONG_CONTEXT.scaled(batch=2, kv_heads=2, q_heads=2 * G, d=d, m=d, context=T, bits_k=bk, bits_v=3,
+                              dist=dist)
+    K, V = W.gen_kv(w)
+    q = W.gen_q(w)
+    Kd, Vd = P.to_f64(K), P.to_f64(V)
+    codec_o = O.make_codec(d, bk, 3, d, 0)
+    means = P.oracle_means(Kd[:, :, :L0], Vd[:, :, :L0], np.arange(L0), w.rope_base)
+    fields = P.oracle_encode_unitwise(Kd, Vd, codec_o, np.arange(T), w.rope_base, means)
+    codec = tq.Codec(d, bk, 3, d, seed=0)
+    cache = tq.PackedCache(w.batch, w.kv_heads, d, T, bk, 3, d, nsn=1)
+    Kc, Vc = K.cuda(), V.cuda()
+    ws = torch.empty(tq.nsn_means_workspace_bytes(cache.desc, L0), dtype=torch.uint8, device="cuda")
+    tq.nsn_set_means(cache.desc, codec.dev, cache.buf, Kc[:, :, :L0].contiguous(), Vc[:, :, :L0].contiguous(), 0,
+                     w.rope_base, ws)
+    for s0, s1 in ((0, L0), (L0, T)):
+        if s1 > s0:
+            tq.quantize_kv(cache.desc, codec.dev, cache.buf, Kc[:, :, s0:s1].contiguous(),
+                           Vc[:, :, s0:s1].contiguous(), s0, w.rope_base)
+    torch.cuda.synchronize()
+    rep = {}
+    P.compare_codes(P.gpu_fields(cache, T), fields, codec_o, rep)
+    ocache = tq.PackedCache(w.batch, w.kv_heads, d, T, bk, 3, d, nsn=1)
+    ocache.buf.copy_(torch.from_numpy(P.oracle_image(ocache.desc.as_dict(), fields)))
+    out, sc = decode(tq, codec, ocache, q.cuda(), T, w.q_pos, w.rope_base)
+    out_o, sc_o = O.attend(fields, P.to_f64(q), codec_o, q_pos=w.q_pos, rope_base=w.rope_base, scale=0.0,
+                           kv_heads=w.kv_heads, length=T)
+    e_out = P.max_abs(out.cpu().numpy(), out_o)
+    e_sc = P.max_abs(sc.cpu().numpy()[:, :, :T], sc_o)
+    out2, _ = decode(tq, codec, cache, q.cuda(), T, w.q_pos, w.rope_base, want_scores=False)
+    e_e2e = P.max_abs(out2.cpu().numpy(), out_o)
+    sc3 = torch.full((w.batch, w.q_heads, T), float("nan"), dtype=torch.float32, device="cuda")
+    ws3 = torch.empty(tq.decode_workspace_bytes(ocache.desc, w.q_heads, T), dtype=torch.uint8, device="cuda")
+    tq.decode_attend(ocache.desc, codec.dev, ocache.buf, T, q.cuda(), w.q_pos, w.rope_base, None, scores=sc3, ws=ws3)
+    torch.cuda.synchronize()
+    e_lg = P.max_abs(sc3.cpu().numpy(), sc_o)
+    say(f"    nsn k{bk} d{d} G{G} L0 {L0} T {T} {dist}: codes {rep} | out {e_out:.2e} scores {e_sc:.2e} "
+        f"e2e {e_e2e:.2e} logits {e_lg:.2e}")
+    assert e_out <= TOL and e_sc <= TOL and e_lg <= TOL
+    if rep["excused"] == 0:
+        assert e_e2e <= TOL
+
+
+@pytest.mark.parametrize("bk,bv,d,G,L0,cap,steps,dt,nsn", [
+    (2, 3, 128, 4, 300, 16, 40, "bf16", 0),   # MFMA path, two flushes
+    (3, 4, 64, 8, 0, 8, 20, "f32", 0),        # fp32 path, starting from an empty cache
+    (2, 3, 128, 4, 200, 32, 70, "bf16", 1),   # NSN cache: flushes shifted by the prefill means
+])
+def test_decode_step_loop(tq, P, bk, bv, d, G, L0, cap, steps, dt, nsn):
     """A generation loop through tq_decode_step (flush of a full window, append inside the
     window kernel, attention) against the oracle's decode_step, step by step; then the
     packed cache the flushes wrote against the oracle's codes, and the window rows."""
@@ -255,8 +307,9 @@ def test_decode_step_loop(tq, P, bk, bv, d, G, L0, cap, steps, dt):
     Kd, Vd = P.to_f64(K), P.to_f64(V)
     codec_o = O.make_codec(d, bk, bv, d, 0)
     codec = tq.Codec(d, bk, bv, d, seed=0)
-    cache = tq.PackedCache(w.batch, w.kv_heads, d, T, bk, bv, d)
-    fields = P.oracle_encode_unitwise(Kd[:, :, :L0], Vd[:, :, :L0], codec_o, np.arange(L0), w.rope_base)
+    cache = tq.PackedCache(w.batch, w.kv_heads, d, T, bk, bv, d, nsn=nsn)
+    means = P.oracle_means(Kd[:, :, :L0], Vd[:, :, :L0], np.arange(L0), w.rope_base) if nsn else None
+    fields = P.oracle_encode_unitwise(Kd[:, :, :L0], Vd[:, :, :L0], codec_o, np.arange(L0), w.rope_base, means)
     if L0 > 0:
         cache.buf.copy_(torch.from_numpy(P.oracle_image(cache.desc.as_dict(), fields)))
     st = {"fields": fields, "length": L0, "win_k": np.zeros((w.batch, w.kv_heads, cap, d)),
@@ -285,9 +338,9 @@ def test_decode_step_loop(tq, P, bk, bv, d, G, L0, cap, steps, dt):
         assert e_out <= TOL and e_sc <= TOL, (s, e_out, e_sc)
     rep = {}
     P.compare_codes(P.gpu_fields(cache, L), P.oracle_encode_unitwise(Kd[:, :, :L], Vd[:, :, :L], codec_o,
-                                                                    np.arange(L), w.rope_base), codec_o, rep)
+                                                                    np.arange(L), w.rope_base, means), codec_o, rep)
     assert torch.equal(wk[:, :, :Wn].cpu(), K[:, :, L:L + Wn]) and torch.equal(wv[:, :, :Wn].cpu(), V[:, :, L:L + Wn])
-    say(f"    step loop k{bk} v{bv} d{d} G{G} L0 {L0} cap {cap}: {steps} steps, final ({L}, {Wn}), "
+    say(f"    step loop k{bk} v{bv} d{d} G{G} L0 {L0} cap {cap} nsn {nsn}: {steps} steps, final ({L}, {Wn}), "
         f"worst {worst:.2e}, codes {rep}")
 
 

@@ -80,6 +80,15 @@ def test_cache_layout_matches_oracle(tq, O):
                  (2, 2, 128, 33, 4, 1, 32)]:
         desc = tq.CacheDesc(*args)
         assert tq.cache_bytes(desc) == O.cache_layout(*args)["total"]
+    # NSN caches: wider norm records and the per-unit means region
+    for args in [(1, 1, 128, 1024, 2, 3, 128), (3, 5, 64, 100, 3, 4, 64), (2, 2, 128, 33, 1, 3, 128)]:
+        assert tq.cache_bytes(tq.CacheDesc(*args, 1)) == O.cache_layout(*args, 1)["total"]
+    # NSN needs values and d = 64 or 128
+    assert tq.cache_bytes(tq.CacheDesc(1, 1, 128, 64, 2, 0, 128, 1)) == 0
+    assert tq.cache_bytes(tq.CacheDesc(1, 1, 256, 64, 2, 3, 256, 1)) == 0
+    assert tq.cache_bytes(tq.CacheDesc(1, 1, 128, 64, 2, 3, 128, 2)) == 0
+    assert tq.nsn_means_workspace_bytes(tq.CacheDesc(2, 4, 128, 64, 2, 3, 128, 1), 5000) > 0
+    assert tq.nsn_means_workspace_bytes(tq.CacheDesc(2, 4, 128, 64, 2, 3, 128), 5000) == 0
 
 
 def test_argument_errors_return_status(tq):
@@ -93,6 +102,7 @@ def test_argument_errors_return_status(tq):
     assert e.value.status == tq.TQ_EUNSUPPORTED
     # device entry points: every check runs before anything is enqueued (no GPU needed)
     P = 0x1000  # never dereferenced: each call fails validation first
+    nsn = tq.CacheDesc(1, 1, 128, 64, 2, 3, 128, 1)
     cases = [
         (lambda: tq._quantize_kv(ctypes.byref(good), None, P, P, P, 0, 0, 1, 0.0, None), tq.TQ_EINVAL),
         (lambda: tq._quantize_kv(ctypes.byref(good), P, P, P, P, 0, 60, 5, 0.0, None), tq.TQ_ECAPACITY),
@@ -111,6 +121,12 @@ def test_argument_errors_return_status(tq):
         (lambda: tq._decode_attend_splits(ctypes.byref(good), P, P, 10, None, 0, 1, 0, 0.0, 0.0, P, None, 0,
                                           P, 1 << 30, None), tq.TQ_EINVAL),
         (lambda: tq._search_topk(ctypes.byref(good), P, P, 10, P, 4, 10, P, P, P, 1 << 30, None), tq.TQ_EINVAL),
+        # NSN: means only on NSN caches, n >= 1, enough workspace; decode on the MFMA path only
+        (lambda: tq._nsn_set(ctypes.byref(good), P, P, P, P, 1, 0, 10, 0.0, P, 1 << 30, None), tq.TQ_EINVAL),
+        (lambda: tq._nsn_set(ctypes.byref(nsn), P, P, P, P, 1, 0, 0, 0.0, P, 1 << 30, None), tq.TQ_EINVAL),
+        (lambda: tq._nsn_set(ctypes.byref(nsn), P, P, P, P, 1, 0, 10, 0.0, P, 8, None), tq.TQ_ENOSPACE),
+        (lambda: tq._decode_attend_splits(ctypes.byref(tq.CacheDesc(1, 1, 128, 64, 4, 3, 128, 1)), P, P, 10, P,
+                                          0, 1, 0, 0.0, 0.0, P, None, 0, P, 1 << 30, None), tq.TQ_EUNSUPPORTED),
         (lambda: tq._search_topk(ctypes.byref(tq.CacheDesc(1, 1, 128, 64, 3, 0, 128)), P, P, 65, P, 4, 10,
                                  P, P, P, 1 << 30, None), tq.TQ_ECAPACITY),
         (lambda: tq._search_topk(ctypes.byref(tq.CacheDesc(1, 1, 128, 64, 3, 0, 128)), P, P, 10, P, 4, 65,

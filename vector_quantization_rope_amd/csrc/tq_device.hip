@@ -124,6 +124,7 @@ struct CachePtrs {
   uint32_t *vcodes;
   uint16_t *vnorm;
   uint32_t *flags;
+  float *nsn;   // NSN caches: per unit [o_K, o_V, Pi o_K, Pi o_V] fp32 [d] each; else null
   int kbytes, tiles;
 };
 
@@ -136,6 +137,7 @@ CachePtrs cache_ptrs(void *cache_dev, const tq_cache_desc &c) {
   p.vcodes = c.bits_v > 0 ? reinterpret_cast<uint32_t *>(b + L.vcodes) : nullptr;
   p.vnorm = c.bits_v > 0 ? reinterpret_cast<uint16_t *>(b + L.vnorm) : nullptr;
   p.flags = reinterpret_cast<uint32_t *>(b + 8);
+  p.nsn = c.nsn ? reinterpret_cast<float *>(b + L.nsn) : nullptr;
   p.kbytes = L.kbytes;
   p.tiles = L.tiles;
   return p;
@@ -161,6 +163,7 @@ __global__ void k_cache_init(uint32_t *hdr, tq_cache_desc c) {
     case 8: v = uint32_t(c.bits_k); break;
     case 9: v = uint32_t(c.bits_v); break;
     case 10: v = uint32_t(c.m); break;
+    case 11: v = uint32_t(c.nsn); break;
     default: v = 0;
   }
   hdr[i] = v;
@@ -333,6 +336,27 @@ __device__ __forceinline__ void store_plane(uint32_t hA, uint32_t hB, int q, uin
   }
 }
 
+// NSN shift ([NSNQuant] section 1) of one token spread over a lane group as in
+// fwht_group4 (x in H-units, sqrt(B) times the rotated coordinates): s1 = ||y|| / sqrt(d)
+// is rounded to fp16, then y -= s1 (Pi o) with the unit's stored fp32 Pi o.  The codec's
+// norm and direction of what remains are NSN's second normalization.
+template <int D>
+__device__ __forceinline__ void nsn_shift(double *x, int q, const float *po, double sqrt_b, double inv_sqrt_b,
+                                          uint16_t *s1b, bool *over) {
+  constexpr int HC = D / 8, H = D / 2, C = 2 * HC;
+  double ss = 0.0;
+#pragma unroll
+  for (int e = 0; e < C; ++e) ss = fma(x[e], x[e], ss);
+  const double nu = sqrt(group4_sum(ss));   // sqrt(B) ||y||
+  *s1b = f64_to_f16_sat(nu * inv_sqrt_b / sqrt(double(D)), over);
+  const double s1h = double(f16_bits_to_float(*s1b)) * sqrt_b;
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    const int j = e < HC ? HC * q + e : H + HC * q + (e - HC);
+    x[e] = fma(-s1h, double(po[j]), x[e]);
+  }
+}
+
 // One workgroup (4 waves) per 64-token window aligned to value tiles; 4 lanes per token.
 // Keys: RoPE (fp64 angles from an LDS table built by the fp64 rotation recurrence), the
 // seeded signs D, the unnormalised FWHT H_B, norm, codes and residual in fp64, with the
@@ -424,6 +448,8 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
 #pragma unroll
   for (int e = 0; e < C; ++e) x[e] = ((dmask >> e) & 1u) ? -x[e] : x[e];
   fwht_group4<D>(x, q);
+  uint16_t ks1b = 0;
+  if (a.ch.nsn) nsn_shift<D>(x, q, a.ch.nsn + size_t(unit) * 4 * D + 2 * D, sqrt_b, inv_sqrt_b, &ks1b, &over);
   {
     double ss = 0.0;
 #pragma unroll
@@ -510,8 +536,13 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
 #pragma unroll
     for (int pp = 0; pp < NP; ++pp)
       if (pp < a.bits_k) store_plane<D>(hA[pp], hB[pp], q, rec + pp * W, valid);
-    if (valid && q == 0)
-      a.ch.knorm[size_t(unit) * a.capacity + p] = uint32_t(n16b) | (uint32_t(rn16b) << 16);
+    if (valid && q == 0) {
+      const uint32_t nw = uint32_t(n16b) | (uint32_t(rn16b) << 16);
+      if (a.ch.nsn)
+        reinterpret_cast<uint2 *>(a.ch.knorm)[size_t(unit) * a.capacity + p] = make_uint2(nw, uint32_t(ks1b));
+      else
+        a.ch.knorm[size_t(unit) * a.capacity + p] = nw;
+    }
   }
   __syncthreads();   // every wave is done with the RoPE table before residuals overwrite it
   {
@@ -551,6 +582,8 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
 #pragma unroll
     for (int e = 0; e < C; ++e) x[e] = ((dmask >> e) & 1u) ? -x[e] : x[e];
     fwht_group4<D>(x, q);
+    uint16_t vs1b = 0;
+    if (a.ch.nsn) nsn_shift<D>(x, q, a.ch.nsn + size_t(unit) * 4 * D + 3 * D, sqrt_b, inv_sqrt_b, &vs1b, &over);
     double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < C; ++e) ss = fma(x[e], x[e], ss);
@@ -595,7 +628,12 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
       va[i] = cw[i];
       vb[i] = cw[HC / 4 + i];
     }
-    if (valid && q == 0) a.ch.vnorm[size_t(unit) * a.capacity + p] = n16b;
+    if (valid && q == 0) {
+      if (a.ch.nsn)
+        reinterpret_cast<uint32_t *>(a.ch.vnorm)[size_t(unit) * a.capacity + p] = uint32_t(n16b) | (uint32_t(vs1b) << 16);
+      else
+        a.ch.vnorm[size_t(unit) * a.capacity + p] = n16b;
+    }
   }
   __syncthreads();
 
@@ -1091,6 +1129,7 @@ struct MfmaArgs {
   const uint8_t *qpack;
   float *part;
   float *scores;
+  const float *nsn;   // NSN caches: per unit [o_K, o_V, Pi o_K, Pi o_V]; else null
   int kbytes, tiles, capacity, length, chunk, splits, kv_heads, q_heads, G;
   int score_stride;   // row stride of scores: length, or length + the window's tokens
   float scale_log2, inv_scale_log2;
@@ -1138,10 +1177,12 @@ __device__ __forceinline__ float sum32(float v) {
 // Tail shared by the two query-prep kernels, run by all 256 threads once q_rot (qs) and
 // sq (sqs) are complete, thread i < d having written sqs[i] itself: the fp32 row, the
 // sums, the two fixed-point exponents, the score coefficients and the int8 digit rows.
+// nsn: the cache's NSN means (null for a plain cache); the head's coefficient 2 is then
+// <q_rot, Pi o_K>, the score of the keys' mean per unit of s1.
 __device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, int d, int m,
                                            const CodecPtrs &cp, float *o, float (*red)[4], int tid,
                                            int lane, int wv, int b, int g, int h, int G,
-                                           int kv_heads, int bits_k, uint8_t *qpack) {
+                                           int kv_heads, int bits_k, uint8_t *qpack, const float *nsn) {
   // fp32 rows and sums; maxima for the fixed-point scaling (the two plane vectors
   // (c1 - c0) q and (c2 - c0) q share one exponent, set by the larger weight)
   // Key-plane weights of the odd codebook: c[code] = c0 + sum_p pw[p] bit_p(code).  For
@@ -1166,11 +1207,13 @@ __device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, in
     pw[3] = 0.5f * (c7 - c6 - c5 + c4);
   }
   const float wmax = fmaxf(fmaxf(fabsf(pw[0]), fabsf(pw[1])), fmaxf(fabsf(pw[2]), fabsf(pw[3])));
-  float s0 = 0.0f, s1 = 0.0f, m0 = 0.0f, m1 = 0.0f;
+  float s0 = 0.0f, s1 = 0.0f, m0 = 0.0f, m1 = 0.0f, sb = 0.0f;
+  const float *pok = nsn ? nsn + size_t(b * kv_heads + g) * 4 * d + 2 * d : nullptr;
   for (int j = tid; j < d; j += 256) {
     o[j] = qs[j];
     s0 += qs[j];
     m0 = fmaxf(m0, fabsf(qs[j]) * wmax);
+    if (pok) sb = fmaf(qs[j], pok[j], sb);
   }
   for (int i = tid; i < m; i += 256) {
     o[d + i] = sqs[i];
@@ -1181,11 +1224,13 @@ __device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, in
   s1 = wave_sum(s1);
   m0 = wave_max(m0);
   m1 = wave_max(m1);
+  sb = wave_sum(sb);
   if (lane == 0) {
     red[0][wv] = s0;
     red[1][wv] = s1;
     red[2][wv] = m0;
     red[3][wv] = m1;
+    red[4][wv] = sb;
   }
   __syncthreads();
   // every thread derives the two fixed-point exponents from the wave maxima
@@ -1214,7 +1259,7 @@ __device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, in
       float *k = coef + h * kQpackCoef;
       k[0] = c0 * S0;
       k[1] = iq;
-      k[2] = 0.0f;
+      k[2] = (red[4][0] + red[4][1]) + (red[4][2] + red[4][3]);   // NSN: <q_rot, Pi o_K>
       k[3] = 2.0f * cp.qjl_scale * is;
       k[4] = cp.qjl_scale * S1;
       k[5] = k[6] = k[7] = 0.0f;
@@ -1276,10 +1321,10 @@ __device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, in
 __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, int d, int m,
                                                     int q_pos, float rope_base, CodecPtrs cp,
                                                     float *qrows, int qstride, int q_heads,
-                                                    int G, int bits_k, uint8_t *qpack) {
+                                                    int G, int bits_k, uint8_t *qpack, const float *nsn) {
   extern __shared__ float qs[];   // d floats (q_rot), m floats (sq), max(1024, m) partial sums
   float *sqs = qs + d;
-  __shared__ float red[4][4];
+  __shared__ float red[5][4];
   const int rowi = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int b = rowi / q_heads, hq = rowi % q_heads;
   const int g = hq / G, h = hq % G;
@@ -1372,7 +1417,8 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
     }
   }
   __syncthreads();
-  qprep_tail(qs, sqs, d, m, cp, qrows + size_t(rowi) * qstride, red, tid, lane, wv, b, g, h, G, kv_heads, bits_k, qpack);
+  qprep_tail(qs, sqs, d, m, cp, qrows + size_t(rowi) * qstride, red, tid, lane, wv, b, g, h, G, kv_heads, bits_k, qpack,
+             nsn);
 }
 
 // Query preparation for d = m in {64, 128} with Hadamard block d (the decode MFMA path):
@@ -1382,10 +1428,11 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
 template <int D>
 __global__ __launch_bounds__(256) void k_qprep_fast(const void *q, int dtype, int q_pos, float rope_base,
                                                     CodecPtrs cp, float *qrows, int qstride,
-                                                    int q_heads, int G, int bits_k, uint8_t *qpack) {
+                                                    int q_heads, int G, int bits_k, uint8_t *qpack,
+                                                    const float *nsn) {
   constexpr int H2 = D / 2, G4 = D / 4, SL = 256 / G4, JL = D / SL, E = D / 64;
   __shared__ float qs[D], sqs[D], part[SL * D];
-  __shared__ float red[4][4];
+  __shared__ float red[5][4];
   const int rowi = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int b = rowi / q_heads, hq = rowi % q_heads;
   const int g = hq / G, h = hq % G;
@@ -1459,7 +1506,8 @@ __global__ __launch_bounds__(256) void k_qprep_fast(const void *q, int dtype, in
     for (int s = 0; s < SL; ++s) z += part[s * D + tid];
     sqs[tid] = z;
   }
-  qprep_tail(qs, sqs, D, D, cp, qrows + size_t(rowi) * qstride, red, tid, lane, wv, b, g, h, G, kv_heads, bits_k, qpack);
+  qprep_tail(qs, sqs, D, D, cp, qrows + size_t(rowi) * qstride, red, tid, lane, wv, b, g, h, G, kv_heads, bits_k, qpack,
+             nsn);
 }
 
 // LDS-staged split-K decode.  Each wave streams its tiles through a ring of kRing LDS
@@ -1475,7 +1523,7 @@ constexpr int kDecBlocksPerCU = 1;
 // block waiting for its own results (lgkmcnt(0)), because the compiler would otherwise
 // wait for every direct-to-LDS load in flight (including the prefetches into the other
 // slots) before any LDS read; the ring's own vmcnt waits order them instead.
-template <int D, int KBITS>
+template <int D, int KBITS, bool NSN = false>
 struct LdsGeom {
   static constexpr int KB = (KBITS + 1) * D / 8;   // key record bytes (KBITS planes + m = d sign bits)
   static constexpr int KT = 32 * KB;       // key bytes per 32-token tile
@@ -1487,9 +1535,12 @@ struct LdsGeom {
   static constexpr int NK = (KT / KCH + 63) / 64; // key DMA instructions
   static constexpr int NV = (VT / 16 + 63) / 64;  // value DMA instructions
   static constexpr int NDMA = NK + NV + 2;        // + key norms + value norms
-  static constexpr int KN = KT + VT;       // offset of the 32 key norms (128 B)
-  static constexpr int VN = KN + 128;      // offset of the value norms (68 B: 17 dwords)
-  static constexpr int SLOT = VN + 80;
+  // key norm records: 4 bytes, or 8 with NSN ({n, |r|, s1, 0}); value norm records: 2
+  // bytes (read as 17 dwords from the dword at or below the tile's first), or 4 with NSN
+  static constexpr int KNR = NSN ? 8 : 4;
+  static constexpr int KN = KT + VT;       // offset of the 32 key norms
+  static constexpr int VN = KN + 32 * KNR; // offset of the value norms
+  static constexpr int SLOT = VN + (NSN ? 128 : 80);
 };
 
 template <int N>
@@ -1512,12 +1563,15 @@ __device__ __forceinline__ void wait_lgkm0() {
 
 // KBITS = key code bits (1, 2 or 3).  The key score's code term is a weighted sum of
 // NP 0/1 planes: the code bits, and for 3-bit codes also their parity (odd codebook).
-template <int D, int KBITS>
+// NSN: the cache's tokens carry fp16 s1 next to the norms; a key's score gains
+// s1 <q, o_K> (the query coefficient 2) and a value's share of s1 Pi o_V is summed per head
+// next to the softmax sum and added to the accumulator at the end.
+template <int D, int KBITS, bool NSN>
 __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(MfmaArgs a) {
   // The body is device code only (its local lambdas call device builtins); the host pass
   // needs nothing but the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-  using Gm = LdsGeom<D, KBITS>;
+  using Gm = LdsGeom<D, KBITS, NSN>;
   constexpr int NCH = D / 32, NT = D / 16, NW = kDecWaves, NTH = 64 * NW, R = kRing;
   constexpr int NP = KBITS == 3 ? 4 : KBITS;
   static_assert(KBITS >= 1 && KBITS <= 3, "key planes");
@@ -1525,7 +1579,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
   __shared__ uint2 lut[4096];
   __shared__ __align__(16) _Float16 pt_s[NW][16][40];
   __shared__ __align__(16) float coef_s[2][5][4];
-  __shared__ float red_s[NW][2][kMfmaMaxG];
+  __shared__ float red_s[NW][3][kMfmaMaxG];
   static_assert(NW * 16 * D * 4 <= int(sizeof(ring)), "the waves' accumulators fit in the ring for the merge");
 
   // the wave index goes through readfirstlane so that everything derived from it (token
@@ -1567,6 +1621,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
   constexpr int TS = 32 * NW;   // tokens between a wave's consecutive tiles
   const int nk = t_end > t_first ? (t_end - t_first + TS - 1) / TS : 0;
   float M[kMfmaMaxG], Mh[4], lsum[4];   // Mh: the running maxima of this lane's 4 heads
+  float so[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // NSN: sum of p s1_v per head
   const uint32_t hmask = half ? 0xFFFFFFFFu : 0u;
 #pragma unroll
   for (int h = 0; h < kMfmaMaxG; ++h) M[h] = h < a.G ? -INFINITY : 0.0f;   // absent heads: any finite value
@@ -1618,6 +1673,16 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
       if (64 * i + 64 <= vchunks || lane < vchunks - 64 * i)
         __builtin_amdgcn_global_load_lds(vsrc + 1024 * i + uint32_t(16 * lane), slot + Gm::KT + 1024 * i, 16, 0, 0);
     }
+    if constexpr (NSN) {
+      // 32 key norm records of 8 bytes (64 dwords), 32 value norm records of 4 bytes
+      const uint8_t *kn = reinterpret_cast<const uint8_t *>(a.knorm) + (ubase + t0) * 8;
+      const uint32_t tk = uint32_t(whole ? lane >> 1 : min(lane >> 1, nv - 1));
+      __builtin_amdgcn_global_load_lds(kn + 8 * tk + 4 * uint32_t(lane & 1), slot + Gm::KN, 4, 0, 0);
+      if (lane < 32) {
+        const uint8_t *vn4 = vnbase + (ubase + t0) * 4;
+        __builtin_amdgcn_global_load_lds(vn4 + 4 * uint32_t(whole ? lane : min(lane, nv - 1)), slot + Gm::VN, 4, 0, 0);
+      }
+    } else {
     if (lane < 32) {
       const uint8_t *kn = reinterpret_cast<const uint8_t *>(a.knorm + ubase + t0);
       __builtin_amdgcn_global_load_lds(kn + uint32_t(4 * (whole ? lane : min(lane, nv - 1))), slot + Gm::KN, 4, 0, 0);
@@ -1630,6 +1695,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
       const uint32_t span = uint32_t((lastb & ~size_t(3)) - (byte0 & ~size_t(3)));
       __builtin_amdgcn_global_load_lds(vnbase + (byte0 & ~size_t(3)) + min(uint32_t(4 * lane), span),
                                        slot + Gm::VN, 4, 0, 0);
+    }
     }
   };
 
@@ -1654,8 +1720,8 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
     uint32_t vwr[NT][2];
     {
       const uint32_t kaddr = sbase + row * Gm::KB + half * (D / 16);
-      const uint32_t naddr = sbase + Gm::KN + 4 * row;
-      const uint32_t vaddr = sbase + Gm::VN + uint32_t(((ubase + t0) * 2) & 3) + 2 * row;
+      const uint32_t naddr = sbase + Gm::KN + Gm::KNR * row;
+      const uint32_t vaddr = NSN ? sbase + Gm::VN + 4 * row : sbase + Gm::VN + uint32_t(((ubase + t0) * 2) & 3) + 2 * row;
       const uint32_t caddr = sbase + Gm::KT + vn * 12 + 4 * vidx;
 #if defined(__HIP_DEVICE_COMPILE__)
       if constexpr (D >= 128) {
@@ -1767,12 +1833,34 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
     }
     const float n16 = f16_bits_to_float(nr & 0xFFFFu), rn16 = f16_bits_to_float(nr >> 16);
     const float vnorm = f16_bits_to_float(vnb & 0xFFFFu);
+    float ks1 = 0.0f, vs1 = 0.0f;
+    if constexpr (NSN) {
+      // the s1 halves of this token's norm records (LDS reads, waited for in the block)
+      uint32_t k1b = 0u, v1b = 0u;
+      asm volatile(
+          "ds_read_u16 %0, %2 offset:4\n"
+          "ds_read_u16 %1, %3 offset:2\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=v"(k1b), "=v"(v1b)
+          : "v"(sbase + Gm::KN + 8 * row), "v"(sbase + Gm::VN + 4 * row)
+          : "memory");
+      ks1 = f16_bits_to_float(k1b);
+      vs1 = f16_bits_to_float(v1b);
+    }
     const float4 k0 = *reinterpret_cast<const float4 *>(coef_s[half][0]);
     const float4 k1 = *reinterpret_cast<const float4 *>(coef_s[half][1]);
     const float4 k3 = *reinterpret_cast<const float4 *>(coef_s[half][3]);
     const float4 k4 = *reinterpret_cast<const float4 *>(coef_s[half][4]);
     const float K0[4] = {k0.x, k0.y, k0.z, k0.w}, K1[4] = {k1.x, k1.y, k1.z, k1.w};
     const float K3[4] = {k3.x, k3.y, k3.z, k3.w}, K4[4] = {k4.x, k4.y, k4.z, k4.w};
+    float K2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (NSN) {
+      const float4 k2 = *reinterpret_cast<const float4 *>(coef_s[half][2]);
+      K2[0] = k2.x;
+      K2[1] = k2.y;
+      K2[2] = k2.z;
+      K2[3] = k2.w;
+    }
     // lam = scale * score in the log2 domain; a token past the end gets -inf through the
     // innermost fma.  Heads h >= G (zero coefficients and digits) get lam = 0: their rows
     // are carried along and never written out.
@@ -1783,7 +1871,8 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
       // digit sums: rows 8 digit + head are accumulator registers 4 digit + r
       const float S01 = fmaf(float(s01[r] + 256 * s01[4 + r]), 0x1p-16f, float(s01[8 + r] + 256 * s01[12 + r]));
       const float S2 = fmaf(float(s2[r] + 256 * s2[4 + r]), 0x1p-16f, float(s2[8 + r] + 256 * s2[12 + r]));
-      lam[r] = fmaf(n16, fmaf(K1[r], S01, K0[r]), fmaf(rn16, fmaf(K3[r], S2, -K4[r]), vbias));
+      const float vb = NSN ? fmaf(ks1, K2[r], vbias) : vbias;   // NSN: + s1 <q, o_K>
+      lam[r] = fmaf(n16, fmaf(K1[r], S01, K0[r]), fmaf(rn16, fmaf(K3[r], S2, -K4[r]), vb));
       rel[r] = lam[r] - Mh[r];
     }
     if (a.scores) {
@@ -1825,6 +1914,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= al;
         lsum[r] *= half ? alpha[4 + r] : alpha[r];
+        if constexpr (NSN) so[r] *= half ? alpha[4 + r] : alpha[r];
         Mh[r] = pick_bits(hmask, M[4 + r], M[r]);
         rel[r] = lam[r] - Mh[r];
       }
@@ -1835,6 +1925,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
       // lam = -inf (token past the end) gives p = 0: Mh is finite after the first tile
       const float p = __builtin_amdgcn_exp2f(rel[r]);
       lsum[r] += p;
+      if constexpr (NSN) so[r] = fmaf(p, vs1, so[r]);
       const float pv = p * vnorm;
       const _Float16 hi = (_Float16)pv;
       const _Float16 lo = (_Float16)(pv - float(hi));
@@ -1861,11 +1952,19 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
   // ---- merge the block's waves
 #pragma unroll
   for (int r = 0; r < 4; ++r) lsum[r] = sum32(lsum[r]);
+  if constexpr (NSN) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) so[r] = sum32(so[r]);
+  }
   __syncthreads();
   float *acc_s = reinterpret_cast<float *>(&ring[0][0][0]);   // [NW waves][16 rows][D]
   if (lane == 0 || lane == 32) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) red_s[wv][1][4 * half + r] = lsum[r];
+    if constexpr (NSN) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red_s[wv][2][4 * half + r] = so[r];
+    }
   }
   if (lane == 0) {
 #pragma unroll
@@ -1881,7 +1980,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red_s[w][0][h]);
-    float v = 0.0f, L = 0.0f;
+    float v = 0.0f, L = 0.0f, SO = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       const float mw = red_s[w][0][h];
@@ -1889,7 +1988,10 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
       const float f = exp2f(mw - mx);
       v += (acc_s[(w * 16 + h) * D + j] + acc_s[(w * 16 + 8 + h) * D + j]) * f;
       L += red_s[w][1][h] * f;
+      if constexpr (NSN) SO += red_s[w][2][h] * f;
     }
+    // NSN: the values' mean, sum_t p_t s1_t Pi o_V, joins the rotated accumulator
+    if constexpr (NSN) v = fmaf(SO, a.nsn[size_t(unit) * 4 * D + 3 * D + j], v);
     float *o = a.part + ((size_t(b * a.q_heads + hq0 + h) * a.splits) + split) * (D + 2);
     o[j] = v;
     if (j == 0) {
@@ -1907,7 +2009,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
 // estimates.  With no value stream to stage, each lane loads its own token's key words
 // (its half of every plane and of the signs) and norms straight into registers two tiles
 // ahead; 4 waves per block, wave w taking tiles w, w + 4, ... of the block's chunk.
-template <int D, int KBITS>
+template <int D, int KBITS, bool NSN>
 __global__ __launch_bounds__(256) void k_logits(MfmaArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NCH = D / 32, NP = KBITS == 3 ? 4 : KBITS, KB = (KBITS + 1) * D / 8;
@@ -1940,7 +2042,7 @@ __global__ __launch_bounds__(256) void k_logits(MfmaArgs a) {
   const int t_first = t_begin + 32 * wv;
   const int nk = t_end > t_first ? (t_end - t_first + 127) / 128 : 0;
   // a lane's words of tile k (tokens past the end read the last token of the range)
-  auto load = [&](int k, uint2 (&kw)[KBITS + 1], uint32_t &nr) {
+  auto load = [&](int k, uint2 (&kw)[KBITS + 1], uint32_t &nr, uint32_t &ns) {
     const int tc = min(t_first + 128 * k + row, t_end - 1);
     const uint8_t *rec = a.kbits + (ubase + tc) * KB + half * (D / 16);
 #pragma unroll
@@ -1950,12 +2052,19 @@ __global__ __launch_bounds__(256) void k_logits(MfmaArgs a) {
       else
         kw[pp] = make_uint2(*reinterpret_cast<const uint32_t *>(rec + pp * (D / 8)), 0u);
     }
-    nr = a.knorm[ubase + tc];
+    if constexpr (NSN) {
+      const uint2 r = reinterpret_cast<const uint2 *>(a.knorm)[ubase + tc];   // {n | |r|, s1}
+      nr = r.x;
+      ns = r.y;
+    } else {
+      nr = a.knorm[ubase + tc];
+      ns = 0u;
+    }
   };
   uint2 kwn[KBITS + 1], kwm[KBITS + 1];   // tiles k + 1 and k + 2 in flight
-  uint32_t nrn = 0u, nrm = 0u;
-  if (nk > 0) load(0, kwn, nrn);
-  if (nk > 1) load(1, kwm, nrm);
+  uint32_t nrn = 0u, nrm = 0u, nsn_n = 0u, nsn_m = 0u;
+  if (nk > 0) load(0, kwn, nrn, nsn_n);
+  if (nk > 1) load(1, kwm, nrm, nsn_m);
   for (int k = 0; k < nk; ++k) {
     uint2 kw[KBITS + 1];
 #pragma unroll
@@ -1963,9 +2072,10 @@ __global__ __launch_bounds__(256) void k_logits(MfmaArgs a) {
       kw[pp] = kwn[pp];
       kwn[pp] = kwm[pp];
     }
-    const uint32_t nr = nrn;
+    const uint32_t nr = nrn, ns = nsn_n;
     nrn = nrm;
-    if (k + 2 < nk) load(k + 2, kwm, nrm);
+    nsn_n = nsn_m;
+    if (k + 2 < nk) load(k + 2, kwm, nrm, nsn_m);
     uint2 pl[NP + 1];
 #pragma unroll
     for (int pp = 0; pp < KBITS; ++pp) pl[pp] = kw[pp];
@@ -1987,13 +2097,15 @@ __global__ __launch_bounds__(256) void k_logits(MfmaArgs a) {
       s2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(As[c], bp[NP], s2, 0, 0, 0);
     }
     const float n16 = f16_bits_to_float(nr & 0xFFFFu), rn16 = f16_bits_to_float(nr >> 16);
+    const float ks1 = NSN ? f16_bits_to_float(ns & 0xFFFFu) : 0.0f;
     const int t = t_first + 128 * k + row;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float S01 = fmaf(float(s01[r] + 256 * s01[4 + r]), 0x1p-16f, float(s01[8 + r] + 256 * s01[12 + r]));
       const float S2 = fmaf(float(s2[r] + 256 * s2[4 + r]), 0x1p-16f, float(s2[8 + r] + 256 * s2[12 + r]));
-      const float sc = fmaf(n16, fmaf(coef_s[half][1][r], S01, coef_s[half][0][r]),
-                            rn16 * fmaf(coef_s[half][3][r], S2, -coef_s[half][4][r]));
+      float sc = fmaf(n16, fmaf(coef_s[half][1][r], S01, coef_s[half][0][r]),
+                      rn16 * fmaf(coef_s[half][3][r], S2, -coef_s[half][4][r]));
+      if constexpr (NSN) sc = fmaf(ks1, coef_s[half][2][r], sc);   // + s1 <q, o_K>
       const int h = 4 * half + r;
       if (t < t_end && h < a.G) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.score_stride + t] = sc;
     }
@@ -2889,6 +3001,123 @@ __global__ __launch_bounds__(512, 1) void k_search_mfma(SearchMfmaArgs a) {
 #endif
 }
 
+// ------------------------------------------------------------------ NSN means
+// [NSNQuant] section 1, the shift: o = mean over a unit's tokens of sqrt(d) x / ||x||,
+// keys rotary-embedded first.  k_nsn_partial: grid (units, slices); wave w of a block
+// takes tokens t0 + TPW w + 4 TPW i of its slice, lane j % H2 the pair (j, j + H2) of
+// token TPW-subgroup j / H2, with the fp64 RoPE angle stepped by 4 TPW theta per
+// iteration.  Sums in fp64, combined in a fixed order (deterministic).
+struct NsnArgs {
+  const void *k, *v;
+  double *part;   // [units][slices][2][D]
+  int n, start, slices, per;
+  float rope_base;
+};
+
+template <int D, int DT>
+__global__ __launch_bounds__(256) void k_nsn_partial(NsnArgs a) {
+  constexpr int H2 = D / 2, TPW = 64 / H2, STEP = 4 * TPW;
+  __shared__ double acc_s[4][2][D];
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int j = lane % H2, sub = lane / H2;
+  const int unit = blockIdx.x, sl = blockIdx.y;
+  const int t0 = sl * a.per, t1 = min(a.n, t0 + a.per);
+  const bool rope = a.rope_base != 0.0f;
+  const double sqd = sqrt(double(D));
+  double c = 1.0, sn = 0.0, cs = 1.0, ss = 0.0;
+  if (rope) {
+    const double theta = pow(double(a.rope_base), -2.0 * double(j) / double(D));
+    sincos(double(a.start + t0 + TPW * wv + sub) * theta, &sn, &c);
+    sincos(double(STEP) * theta, &ss, &cs);
+  }
+  double ak0 = 0.0, ak1 = 0.0, av0 = 0.0, av1 = 0.0;
+  const size_t ub = size_t(unit) * a.n;
+  for (int tb = t0 + TPW * wv; tb < t1; tb += STEP) {   // wave-uniform
+    const int t = tb + sub;
+    double k0 = 0.0, k1 = 0.0, v0 = 0.0, v1 = 0.0;
+    if (t < t1) {
+      k0 = load_d<DT>(a.k, (ub + t) * D + j);
+      k1 = load_d<DT>(a.k, (ub + t) * D + j + H2);
+      v0 = load_d<DT>(a.v, (ub + t) * D + j);
+      v1 = load_d<DT>(a.v, (ub + t) * D + j + H2);
+    }
+    if (rope) {
+      const double r0 = k0 * c - k1 * sn, r1 = k0 * sn + k1 * c;
+      k0 = r0;
+      k1 = r1;
+      const double cn = c * cs - sn * ss;
+      sn = sn * cs + c * ss;
+      c = cn;
+    }
+    double nk = fma(k0, k0, k1 * k1), nv = fma(v0, v0, v1 * v1);
+#pragma unroll
+    for (int o = 1; o < H2; o <<= 1) {
+      nk += __shfl_xor(nk, o, 64);
+      nv += __shfl_xor(nv, o, 64);
+    }
+    const double fk = nk > 0.0 ? sqd / sqrt(nk) : 0.0, fv = nv > 0.0 ? sqd / sqrt(nv) : 0.0;
+    ak0 = fma(k0, fk, ak0);
+    ak1 = fma(k1, fk, ak1);
+    av0 = fma(v0, fv, av0);
+    av1 = fma(v1, fv, av1);
+  }
+  if constexpr (TPW == 2) {
+    ak0 += __shfl_xor(ak0, 32, 64);
+    ak1 += __shfl_xor(ak1, 32, 64);
+    av0 += __shfl_xor(av0, 32, 64);
+    av1 += __shfl_xor(av1, 32, 64);
+  }
+  if (sub == 0) {
+    acc_s[wv][0][j] = ak0;
+    acc_s[wv][0][j + H2] = ak1;
+    acc_s[wv][1][j] = av0;
+    acc_s[wv][1][j + H2] = av1;
+  }
+  __syncthreads();
+  for (int i = tid; i < 2 * D; i += 256) {
+    const int kv = i / D, jj = i % D;
+    a.part[((size_t(unit) * a.slices + sl) * 2 + kv) * D + jj] =
+        (acc_s[0][kv][jj] + acc_s[1][kv][jj]) + (acc_s[2][kv][jj] + acc_s[3][kv][jj]);
+  }
+}
+
+// o = (sum of the slices' partials) / n, stored in fp32, then Pi o = H (D .* o) / sqrt(B)
+// in fp64 (LDS FWHT), stored in fp32: per unit [o_K, o_V, Pi o_K, Pi o_V].
+template <int D>
+__global__ __launch_bounds__(256) void k_nsn_final(const double *part, int slices, int n, const float *Dsg,
+                                                   float *nsn) {
+  __shared__ double y_s[2][D];
+  const int tid = threadIdx.x, unit = blockIdx.x;
+  float *dst = nsn + size_t(unit) * 4 * D;
+  for (int i = tid; i < 2 * D; i += 256) {
+    const int kv = i / D, jj = i % D;
+    double acc = 0.0;
+    for (int sl = 0; sl < slices; ++sl) acc += part[((size_t(unit) * slices + sl) * 2 + kv) * D + jj];
+    const float o32 = float(acc / double(n));
+    dst[kv * D + jj] = o32;
+    y_s[kv][jj] = double(o32) * double(Dsg[jj]);
+  }
+  __syncthreads();
+  for (int st = 1; st < D; st <<= 1) {
+    for (int i = tid; i < D; i += 256) {   // D / 2 butterflies per vector, two vectors
+      const int kv = i / (D / 2), kk = i % (D / 2);
+      const int jj = (kk / st) * 2 * st + (kk % st);
+      const double x0 = y_s[kv][jj], x1 = y_s[kv][jj + st];
+      y_s[kv][jj] = x0 + x1;
+      y_s[kv][jj + st] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  const double isb = 1.0 / sqrt(double(D));
+  for (int i = tid; i < 2 * D; i += 256) dst[2 * D + i] = float(y_s[i / D][i % D] * isb);
+}
+
+int nsn_slices(int n, int units) {
+  const int want = (1024 + units - 1) / units;   // about four blocks per CU in all
+  const int by_n = (n + 255) / 256;
+  return std::max(1, std::min(want, by_n));
+}
+
 // ------------------------------------------------------------------ host-side helpers
 tq_status launch_status() {
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_EDEVICE;
@@ -2946,6 +3175,26 @@ int search_tiles(int n_db) { return (n_db + kSearchTile - 1) / kSearchTile; }
 
 using namespace tq;
 
+// MFMA-path kernels by head dim, key bits and NSN: the logits-only kernel or the split
+// decode kernel.
+template <bool LOGITS, bool NSN>
+static void launch_mfma(int d, int bk, dim3 grid, dim3 blk, hipStream_t s, const MfmaArgs &ma) {
+#define TQ_MFMA(DD, BK)                                                          \
+  if (d == DD && bk == BK) {                                                     \
+    if constexpr (LOGITS)                                                        \
+      hipLaunchKernelGGL((k_logits<DD, BK, NSN>), grid, blk, 0, s, ma);          \
+    else                                                                         \
+      hipLaunchKernelGGL((k_decode_lds<DD, BK, NSN>), grid, blk, 0, s, ma);      \
+  }
+  TQ_MFMA(64, 1)
+  TQ_MFMA(64, 2)
+  TQ_MFMA(64, 3)
+  TQ_MFMA(128, 1)
+  TQ_MFMA(128, 2)
+  TQ_MFMA(128, 3)
+#undef TQ_MFMA
+}
+
 extern "C" {
 
 tq_status tq_cache_init(const tq_cache_desc *desc, void *cache_dev, tq_stream_t stream) {
@@ -2953,6 +3202,12 @@ tq_status tq_cache_init(const tq_cache_desc *desc, void *cache_dev, tq_stream_t 
   if (!cache_desc_valid(*desc)) return TQ_EUNSUPPORTED;
   hipLaunchKernelGGL(k_cache_init, dim3(1), dim3(64), 0, hipStream_t(stream),
                      static_cast<uint32_t *>(cache_dev), *desc);
+  if (desc->nsn) {
+    // means start at zero: a fill kernel rather than a memset node, for graph capture
+    const size_t n = size_t(desc->batch) * desc->kv_heads * 4 * desc->d;
+    hipLaunchKernelGGL(k_fill_zero, dim3(unsigned((n + 255) / 256)), dim3(256), 0, hipStream_t(stream),
+                       cache_ptrs(cache_dev, *desc).nsn, n);
+  }
   return launch_status();
 }
 
@@ -3119,6 +3374,8 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
   }
   const CodecPtrs cp = codec_ptrs(codec_dev, d, desc->bits_k, desc->bits_v, m);
   if (win && cp.block != d) return TQ_EUNSUPPORTED;   // the window rotates with one d-point block
+  // NSN caches decode on the MFMA path only (its kernels carry the mean terms)
+  if (desc->nsn && !decode_mfma_path(*desc, q_heads)) return TQ_EUNSUPPORTED;
   if (win && win->flush) {
     // the full window becomes packed tokens [length - cap, length) before anything reads them
     if (length < win->cap) return TQ_EINVAL;
@@ -3139,19 +3396,20 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
   const int bk = desc->bits_k;
   const int score_stride = length + wlen;
   int used_splits = 0;
+  const CachePtrs ch = cache_ptrs(const_cast<void *>(cache_dev), *desc);
   if (length > 0) {
   if (d == m && (d == 64 || d == 128) && cp.block == d) {
     if (d == 64)
       hipLaunchKernelGGL(k_qprep_fast<64>, dim3(rows), dim3(256), 0, s, q, int(dtype), q_pos, rope_base, cp, qp,
-                         qstride, q_heads, G, bk, mfma ? qpack : nullptr);
+                         qstride, q_heads, G, bk, mfma ? qpack : nullptr, ch.nsn);
     else
       hipLaunchKernelGGL(k_qprep_fast<128>, dim3(rows), dim3(256), 0, s, q, int(dtype), q_pos, rope_base, cp, qp,
-                         qstride, q_heads, G, bk, mfma ? qpack : nullptr);
+                         qstride, q_heads, G, bk, mfma ? qpack : nullptr, ch.nsn);
   } else {
     hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s, q,
-                       int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, bk, mfma ? qpack : nullptr);
+                       int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, bk, mfma ? qpack : nullptr,
+                       ch.nsn);
   }
-  const CachePtrs ch = cache_ptrs(const_cast<void *>(cache_dev), *desc);
   used_splits = S;
   if (mfma) {
     const int chunk = split_chunk(length, S);
@@ -3165,6 +3423,7 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
     ma.qpack = qpack;
     ma.part = part;
     ma.scores = scores;
+    ma.nsn = ch.nsn;
     ma.kbytes = ch.kbytes;
     ma.tiles = ch.tiles;
     ma.capacity = desc->capacity;
@@ -3187,15 +3446,10 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
       const int lsplits = (length + lchunk - 1) / lchunk;
       const dim3 lgrid(units, lsplits);
       if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
-      if (d == 64) {
-        if (bk == 1) hipLaunchKernelGGL((k_logits<64, 1>), lgrid, dim3(256), 0, s, ma);
-        if (bk == 2) hipLaunchKernelGGL((k_logits<64, 2>), lgrid, dim3(256), 0, s, ma);
-        if (bk == 3) hipLaunchKernelGGL((k_logits<64, 3>), lgrid, dim3(256), 0, s, ma);
-      } else {
-        if (bk == 1) hipLaunchKernelGGL((k_logits<128, 1>), lgrid, dim3(256), 0, s, ma);
-        if (bk == 2) hipLaunchKernelGGL((k_logits<128, 2>), lgrid, dim3(256), 0, s, ma);
-        if (bk == 3) hipLaunchKernelGGL((k_logits<128, 3>), lgrid, dim3(256), 0, s, ma);
-      }
+      if (desc->nsn)
+        launch_mfma<true, true>(d, bk, lgrid, dim3(256), s, ma);
+      else
+        launch_mfma<true, false>(d, bk, lgrid, dim3(256), s, ma);
       if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
       used_splits = 0;   // no partials: only the window (if any) still writes scores
     }
@@ -3203,15 +3457,10 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
     dim3 grid(units, used_splits);
     if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
     const dim3 blk(64 * kDecWaves);
-    if (d == 64) {
-      if (bk == 1) hipLaunchKernelGGL((k_decode_lds<64, 1>), grid, blk, 0, s, ma);
-      if (bk == 2) hipLaunchKernelGGL((k_decode_lds<64, 2>), grid, blk, 0, s, ma);
-      if (bk == 3) hipLaunchKernelGGL((k_decode_lds<64, 3>), grid, blk, 0, s, ma);
-    } else {
-      if (bk == 1) hipLaunchKernelGGL((k_decode_lds<128, 1>), grid, blk, 0, s, ma);
-      if (bk == 2) hipLaunchKernelGGL((k_decode_lds<128, 2>), grid, blk, 0, s, ma);
-      if (bk == 3) hipLaunchKernelGGL((k_decode_lds<128, 3>), grid, blk, 0, s, ma);
-    }
+    if (desc->nsn)
+      launch_mfma<false, true>(d, bk, grid, blk, s, ma);
+    else
+      launch_mfma<false, false>(d, bk, grid, blk, s, ma);
     if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
     }
   } else {
@@ -3361,6 +3610,54 @@ tq_status tq_decode_step(const tq_cache_desc *desc, const void *codec_dev, void 
   return st;
 }
 
+size_t tq_nsn_means_workspace_bytes(const tq_cache_desc *desc, int32_t n) {
+  if (!desc || !cache_desc_valid(*desc) || !desc->nsn || n < 1) return 0;
+  const int units = desc->batch * desc->kv_heads;
+  return size_t(units) * size_t(nsn_slices(n, units)) * 2 * size_t(desc->d) * sizeof(double);
+}
+
+tq_status tq_nsn_set_means(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
+                           const void *k, const void *v, tq_dtype dtype, int32_t start_pos,
+                           int32_t n, float rope_base, void *ws, size_t ws_bytes,
+                           tq_stream_t stream) {
+  if (!desc || !codec_dev || !cache_dev || !k || !v || !ws) return TQ_EINVAL;
+  if (!cache_desc_valid(*desc)) return TQ_EUNSUPPORTED;
+  if (!desc->nsn) return TQ_EINVAL;
+  if (dtype != TQ_F32 && dtype != TQ_BF16 && dtype != TQ_F16) return TQ_EINVAL;
+  if (n < 1 || start_pos < 0) return TQ_EINVAL;
+  if (!std::isfinite(rope_base) || rope_base < 0.0f) return TQ_EINVAL;
+  if (ws_bytes < tq_nsn_means_workspace_bytes(desc, n)) return TQ_ENOSPACE;
+  const int units = desc->batch * desc->kv_heads, d = desc->d;
+  const int S = nsn_slices(n, units);
+  NsnArgs na;
+  na.k = k;
+  na.v = v;
+  na.part = static_cast<double *>(ws);
+  na.n = n;
+  na.start = start_pos;
+  na.slices = S;
+  na.per = (n + S - 1) / S;
+  na.rope_base = rope_base;
+  const CodecPtrs cp = codec_ptrs(codec_dev, d, desc->bits_k, desc->bits_v, desc->m);
+  const CachePtrs ch = cache_ptrs(cache_dev, *desc);
+  hipStream_t s = hipStream_t(stream);
+  const dim3 grid(units, S);
+#define TQ_NSN(DD, DT)                                                                    \
+  if (d == DD && dtype == DT) hipLaunchKernelGGL((k_nsn_partial<DD, DT>), grid, dim3(256), 0, s, na);
+  TQ_NSN(64, TQ_F32)
+  TQ_NSN(64, TQ_BF16)
+  TQ_NSN(64, TQ_F16)
+  TQ_NSN(128, TQ_F32)
+  TQ_NSN(128, TQ_BF16)
+  TQ_NSN(128, TQ_F16)
+#undef TQ_NSN
+  if (d == 64)
+    hipLaunchKernelGGL(k_nsn_final<64>, dim3(units), dim3(256), 0, s, na.part, S, n, cp.D, ch.nsn);
+  else
+    hipLaunchKernelGGL(k_nsn_final<128>, dim3(units), dim3(256), 0, s, na.part, S, n, cp.D, ch.nsn);
+  return launch_status();
+}
+
 tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_dev,
                                   const void *cache_dev, int32_t length, const void *q,
                                   tq_dtype dtype, int32_t q_heads, int32_t q_pos,
@@ -3393,6 +3690,7 @@ tq_status tq_search_topk(const tq_cache_desc *db, const void *codec_dev, const v
                          tq_stream_t stream) {
   if (!db || !codec_dev || !db_cache || !idx_out || !score_out || !ws) return TQ_EINVAL;
   if (!cache_desc_valid(*db)) return TQ_EUNSUPPORTED;
+  if (db->nsn) return TQ_EUNSUPPORTED;   // database vectors use the plain codec
   if (db->batch != 1 || db->kv_heads != 1 || db->bits_v != 0) return TQ_EINVAL;
   if (n_db < 0 || nq < 0 || k < 1 || k > 64) return TQ_EINVAL;
   if (n_db > db->capacity) return TQ_ECAPACITY;
@@ -3413,7 +3711,7 @@ tq_status tq_search_topk(const tq_cache_desc *db, const void *codec_dev, const v
   int *cand_i = reinterpret_cast<int *>(wb + align256(size_t(nq) * qstride * 4) + align256(cand * 4));
   hipLaunchKernelGGL(k_qprep_pack, dim3(nq), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s,
                      static_cast<const void *>(queries), int(TQ_F32), d, m, 0, 0.0f, cp, qp, qstride,
-                     nq, 1, db->bits_k, static_cast<uint8_t *>(nullptr));
+                     nq, 1, db->bits_k, static_cast<uint8_t *>(nullptr), nullptr);
   // MFMA path: 3-bit codes with m = d, whole 128-coordinate groups, k <= 16.  The codec's
   // codebooks are exactly symmetric by construction.
   const bool mfma = db->bits_k == 3 && m == d && d % 128 == 0 && d <= 2048 && k <= kSmTopMax;

@@ -22,6 +22,8 @@ bool cache_desc_valid(const tq_cache_desc &c) {
   tq_codec_desc cd{c.d, c.bits_k, c.bits_v, c.m, 0};
   if (!codec_desc_valid(cd)) return false;
   if (c.batch < 1 || c.kv_heads < 1 || c.capacity < 0) return false;
+  if (c.nsn != 0 && c.nsn != 1) return false;
+  if (c.nsn && (c.bits_v == 0 || (c.d != 64 && c.d != 128))) return false;
   return true;
 }
 
@@ -34,13 +36,19 @@ CacheLayout cache_layout(const tq_cache_desc &c) {
   size_t cur = kHeaderBytes;
   L.kbits = cur;
   cur = align256(cur + units * size_t(c.capacity) * size_t(L.kbytes));
+  L.knrec = c.nsn ? 8 : 4;
+  L.vnrec = c.nsn ? 4 : 2;
   L.knorm = cur;
-  cur = align256(cur + units * size_t(c.capacity) * 4);
+  cur = align256(cur + units * size_t(c.capacity) * size_t(L.knrec));
   if (c.bits_v > 0) {
     L.vcodes = cur;
     cur = align256(cur + units * size_t(L.tiles) * size_t(c.d) * size_t(4 * c.bits_v));
     L.vnorm = cur;
-    cur = align256(cur + units * size_t(c.capacity) * 2);
+    cur = align256(cur + units * size_t(c.capacity) * size_t(L.vnrec));
+  }
+  if (c.nsn) {
+    L.nsn = cur;   // per unit [o_K, o_V, Pi o_K, Pi o_V], fp32 [d] each
+    cur = align256(cur + units * 4 * size_t(c.d) * 4);
   }
   L.total = cur;
   return L;

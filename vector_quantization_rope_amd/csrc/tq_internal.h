@@ -22,8 +22,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int hadamard_block(int d) { return d & (-d); }
 
 struct CacheLayout {
-  size_t kbits = 0, knorm = 0, vcodes = 0, vnorm = 0, total = 0;
+  size_t kbits = 0, knorm = 0, vcodes = 0, vnorm = 0, nsn = 0, total = 0;
   int kbytes = 0;   // bytes of one key record (planes + sign bits)
+  int knrec = 4;    // bytes of one key norm record (8 with NSN: + fp16 s1, padding)
+  int vnrec = 2;    // bytes of one value norm record (4 with NSN: + fp16 s1)
   int tiles = 0;    // value tiles per unit
   int vwords = 0;   // dwords per (tile, coordinate) = bits_v
 };
@@ -49,8 +51,8 @@ static_assert(sizeof(CodecHeader) == 256, "codec header is 256 bytes");
 
 struct CacheHeader {
   uint32_t magic, version, flags, zero;
-  int32_t batch, kv_heads, d, capacity, bits_k, bits_v, m;
-  uint32_t reserved[53];
+  int32_t batch, kv_heads, d, capacity, bits_k, bits_v, m, nsn;
+  uint32_t reserved[52];
 };
 static_assert(sizeof(CacheHeader) == 256, "cache header is 256 bytes");
 

@@ -31,7 +31,7 @@ EXPORTS = [
     "tq_decode_workspace_bytes_splits", "tq_decode_attend_splits",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_quantize_kv_profiled",
     "tq_decode_attend_profiled", "tq_decode_window_workspace_bytes", "tq_decode_attend_window",
-    "tq_decode_step",
+    "tq_decode_step", "tq_nsn_means_workspace_bytes", "tq_nsn_set_means",
 ]
 
 
@@ -43,7 +43,7 @@ class CodecDesc(ctypes.Structure):
 class CacheDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("bits_k", ctypes.c_int32),
-                ("bits_v", ctypes.c_int32), ("m", ctypes.c_int32)]
+                ("bits_v", ctypes.c_int32), ("m", ctypes.c_int32), ("nsn", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -92,6 +92,8 @@ _IP = ctypes.POINTER(ctypes.c_int32)
 _decode_step = _sig("tq_decode_step", ctypes.c_int,
                     [_KD, _P, _P, _IP, _P, _P, ctypes.c_int, _IP, _I, _P, _P, _P, ctypes.c_int, _I, _I, _F, _F,
                      _P, _P, _P, _S, _P])
+_nsn_ws = _sig("tq_nsn_means_workspace_bytes", _S, [_KD, _I])
+_nsn_set = _sig("tq_nsn_set_means", ctypes.c_int, [_KD, _P, _P, _P, _P, ctypes.c_int, _I, _I, _F, _P, _S, _P])
 _search_ws = _sig("tq_search_workspace_bytes", _S, [_KD, _I, _I, _I])
 _search_topk = _sig("tq_search_topk", ctypes.c_int,
                     [_KD, _P, _P, _I, _P, _I, _I, _P, _P, _P, _S, _P])
@@ -270,6 +272,25 @@ def decode_step(desc: CacheDesc, codec_dev, cache, length: int, win_k, win_v, wi
     return int(L.value), int(Wn.value)
 
 
+def nsn_means_workspace_bytes(desc: CacheDesc, n: int) -> int:
+    return _nsn_ws(ctypes.byref(desc), n)
+
+
+def nsn_set_means(desc: CacheDesc, codec_dev, cache, k, v, start_pos: int, rope_base: float, ws=None,
+                  stream=None, ws_bytes: int | None = None):
+    """NSN channel means of every unit over the tokens k, v ([batch, kv_heads, n, d])."""
+    n = int(k.shape[-2])
+    want = (desc.batch, desc.kv_heads, n, desc.d)
+    for t in (k, v):
+        if t.dim() != 4 or tuple(t.shape) != want or not t.is_contiguous() or t.dtype != k.dtype:
+            raise ValueError(f"nsn_set_means: k, v must be contiguous {want} of one dtype")
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(_nsn_set(ctypes.byref(desc), _ptr(codec_dev), _ptr(cache), _ptr(k), _ptr(v), _dtype_code(k),
+                    int(start_pos), n, float(rope_base), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "tq_nsn_set_means")
+
+
 def search_workspace_bytes(desc: CacheDesc, n_db: int, nq: int, k: int) -> int:
     return _search_ws(ctypes.byref(desc), n_db, nq, k)
 
@@ -298,9 +319,9 @@ class Codec:
 class PackedCache:
     """A packed cache buffer (torch uint8 tensor) plus its descriptor."""
 
-    def __init__(self, batch, kv_heads, d, capacity, bits_k, bits_v, m, device="cuda", stream=None):
+    def __init__(self, batch, kv_heads, d, capacity, bits_k, bits_v, m, device="cuda", stream=None, nsn=0):
         import torch
-        self.desc = CacheDesc(batch, kv_heads, d, capacity, bits_k, bits_v, m)
+        self.desc = CacheDesc(batch, kv_heads, d, capacity, bits_k, bits_v, m, nsn)
         n = cache_bytes(self.desc)
         if n == 0:
             raise TQError(TQ_EUNSUPPORTED, "tq_cache_bytes")
