@@ -207,6 +207,76 @@ def search_bench(tq, W, dev, ev, stream):
     }
 
 
+def timed_calls(fn, ev, stream, E):
+    """Median call and kernel times (us) of fn over len(E) back-to-back calls, after 80 ms of
+    the same calls (the work before idles the GPU and its clock ramps up again); fn(events)
+    records its kernel between the given pair of events, fn(None) records nothing."""
+    import torch
+
+    med = lambda v: sorted(v)[len(v) // 2]
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < 0.08:
+        fn(None)
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    for e in E:
+        ev.record(e[0], stream)
+        fn((e[1], e[2]))
+        ev.record(e[3], stream)
+    torch.cuda.synchronize()
+    return med([ev.elapsed_ms(e[0], e[3]) * 1e3 for e in E]), med([ev.elapsed_ms(e[1], e[2]) * 1e3 for e in E])
+
+
+def nsn_bench(tq, w, K, V, q, dev, ev, stream, reps: int = 30):
+    """NSN cache (normalize-shift-normalize before the codec) on the long-context shape,
+    outside the timed steps: the prefill means (tq_nsn_set_means over 126976 tokens per
+    unit), the 4096-token append, decode and logits only, medians of back-to-back calls."""
+    import torch
+
+    T, A = w.context, w.append
+    pre = T - A
+    units, G = w.batch * w.kv_heads, w.q_heads // w.kv_heads
+    E = [[ev.create() for _ in range(4)] for _ in range(reps)]
+    codec = tq.Codec(w.d, w.bits_k, w.bits_v, w.m, seed=0, device=dev)
+    cache = tq.PackedCache(w.batch, w.kv_heads, w.d, T, w.bits_k, w.bits_v, w.m, device=dev, nsn=1)
+    Kp, Vp = K[:, :, :pre].contiguous(), V[:, :, :pre].contiguous()
+    Ka, Va = K[:, :, pre:].contiguous(), V[:, :, pre:].contiguous()
+    wsm = torch.empty(tq.nsn_means_workspace_bytes(cache.desc, pre), dtype=torch.uint8, device=dev)
+    def means(e):
+        if e:
+            ev.record(e[0], stream)
+        tq.nsn_set_means(cache.desc, codec.dev, cache.buf, Kp, Vp, 0, w.rope_base, wsm)
+        if e:
+            ev.record(e[1], stream)
+
+    means_call, _ = timed_calls(means, ev, stream, E[:5])
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, Kp, Vp, 0, w.rope_base)
+    del Kp, Vp
+    app_call, app_kern = timed_calls(lambda e: tq.quantize_kv(cache.desc, codec.dev, cache.buf, Ka, Va, pre,
+                                                              w.rope_base, events=e), ev, stream, E)
+    out = torch.empty((w.batch, w.q_heads, w.d), dtype=torch.float32, device=dev)
+    sc = torch.empty((w.batch, w.q_heads, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.decode_workspace_bytes(cache.desc, w.q_heads, T), dtype=torch.uint8, device=dev)
+    dec_call, dec_kern = timed_calls(lambda e: tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos,
+                                                                w.rope_base, out, ws=ws, events=e), ev, stream, E)
+    lg_call, lg_kern = timed_calls(lambda e: tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos,
+                                                              w.rope_base, None, scores=sc, ws=ws, events=e),
+                                   ev, stream, E)
+    rec = KEY_RECORD + 4 + VALUE_RECORD + 2   # norm records grow by fp16 s1 (+ padding for keys)
+    dbytes = units * T * rec
+    return {"workload": ("long_context shape, NSN cache: means over the 126976-token prefill, append of "
+                         "4096 tokens, decode and logits at 131072; medians over %d calls" % reps),
+            "record_bytes_per_token": rec,
+            "means_call_us": round(means_call, 1),
+            "append_kernel_us": round(app_kern, 2),
+            "append_mtokens_s": round(w.batch * A / (app_kern * 1e-6) / 1e6, 1),
+            "decode_call_us": round(dec_call, 2), "split_kernel_us": round(dec_kern, 2),
+            "split_kernel_gbs": round(dbytes / (dec_kern * 1e-6) / 1e9, 1),
+            "split_kernel_hbm_frac": round(dbytes / (dec_kern * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "logits_call_us": round(lg_call, 2), "logits_kernel_us": round(lg_kern, 2)}
+
+
 def key_width_bench(tq, W, w, K, V, q, dev, ev, stream, reps: int = 30):
     """Key bit-width variants on the same long-context shape, outside the timed steps:
     full decode of 1-, 2- and 3-bit keys (+ QJL, 3-bit values), and attention logits only
@@ -223,22 +293,7 @@ def key_width_bench(tq, W, w, K, V, q, dev, ev, stream, reps: int = 30):
     sc = torch.empty((w.batch, w.q_heads, T), dtype=torch.float32, device=dev)
 
     def timed(fn):
-        # back to back, one synchronisation at the end, after 80 ms of the same calls: the
-        # cache build before each variant idles the GPU and its clock ramps up again
-        t0, n = time.perf_counter(), 0
-        while time.perf_counter() - t0 < 0.08:
-            fn(None)
-            n += 1
-            if n % 16 == 0:
-                torch.cuda.synchronize()
-        for i in range(reps):
-            ev.record(E[i][0], stream)
-            fn((E[i][1], E[i][2]))
-            ev.record(E[i][3], stream)
-        torch.cuda.synchronize()
-        call = [ev.elapsed_ms(e[0], e[3]) * 1e3 for e in E]
-        kern = [ev.elapsed_ms(e[1], e[2]) * 1e3 for e in E]
-        return med(call), med(kern)
+        return timed_calls(fn, ev, stream, E)
 
     decode, logits = {}, {}
     for bk in (1, 2, 3):
@@ -481,6 +536,12 @@ def main():
         widths = key_width_bench(tq, W, w, K, V, q, dev, ev, stream)
         log(f"[bench] key widths {widths}")
 
+    nsn = None
+    if not args.no_search:
+        log("[bench] NSN cache ...")
+        nsn = nsn_bench(tq, w, K, V, q, dev, ev, stream)
+        log(f"[bench] nsn {nsn}")
+
     window = None
     if not args.no_search:
         log("[bench] full-precision window and decode steps ...")
@@ -542,6 +603,7 @@ def main():
         "cpu_baseline": base,
         "key_widths": widths,
         "window": window,
+        "nsn": nsn,
         "search": search,
     }
     print(json.dumps(rec), flush=True)

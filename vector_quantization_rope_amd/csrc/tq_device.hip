@@ -3014,6 +3014,23 @@ struct NsnArgs {
   float rope_base;
 };
 
+// Sum of a double over each row of 16 lanes, in every lane of the row (DPP: quad swaps,
+// then rotations by 4 and 8 within the row), and its total over rows lo..lo+nr-1 read
+// lane by lane (wave-uniform).
+__device__ __forceinline__ double row_sum_f64(double x) {
+  x += dpp_f64<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_f64<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_f64<0x124>(x);   // row_ror:4
+  x += dpp_f64<0x128>(x);   // row_ror:8
+  return x;
+}
+__device__ __forceinline__ double readlane_f64(double x, int l) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b)), l));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b >> 32)), l));
+  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
+}
+
 template <int D, int DT>
 __global__ __launch_bounds__(256) void k_nsn_partial(NsnArgs a) {
   constexpr int H2 = D / 2, TPW = 64 / H2, STEP = 4 * TPW;
@@ -3032,34 +3049,59 @@ __global__ __launch_bounds__(256) void k_nsn_partial(NsnArgs a) {
   }
   double ak0 = 0.0, ak1 = 0.0, av0 = 0.0, av1 = 0.0;
   const size_t ub = size_t(unit) * a.n;
-  for (int tb = t0 + TPW * wv; tb < t1; tb += STEP) {   // wave-uniform
-    const int t = tb + sub;
-    double k0 = 0.0, k1 = 0.0, v0 = 0.0, v1 = 0.0;
-    if (t < t1) {
-      k0 = load_d<DT>(a.k, (ub + t) * D + j);
-      k1 = load_d<DT>(a.k, (ub + t) * D + j + H2);
-      v0 = load_d<DT>(a.v, (ub + t) * D + j);
-      v1 = load_d<DT>(a.v, (ub + t) * D + j + H2);
-    }
-    if (rope) {
-      const double r0 = k0 * c - k1 * sn, r1 = k0 * sn + k1 * c;
-      k0 = r0;
-      k1 = r1;
-      const double cn = c * cs - sn * ss;
-      sn = sn * cs + c * ss;
-      c = cn;
-    }
-    double nk = fma(k0, k0, k1 * k1), nv = fma(v0, v0, v1 * v1);
+  constexpr int U = 4;   // tokens per lane per iteration: their loads are issued together
+  for (int tb = t0 + TPW * wv; tb < t1; tb += U * STEP) {   // wave-uniform
+    double k0[U], k1[U], v0[U], v1[U];
 #pragma unroll
-    for (int o = 1; o < H2; o <<= 1) {
-      nk += __shfl_xor(nk, o, 64);
-      nv += __shfl_xor(nv, o, 64);
+    for (int u = 0; u < U; ++u) {
+      const int t = tb + u * STEP + sub;
+      k0[u] = k1[u] = v0[u] = v1[u] = 0.0;
+      if (t < t1) {
+        k0[u] = load_d<DT>(a.k, (ub + t) * D + j);
+        k1[u] = load_d<DT>(a.k, (ub + t) * D + j + H2);
+        v0[u] = load_d<DT>(a.v, (ub + t) * D + j);
+        v1[u] = load_d<DT>(a.v, (ub + t) * D + j + H2);
+      }
     }
-    const double fk = nk > 0.0 ? sqd / sqrt(nk) : 0.0, fv = nv > 0.0 ? sqd / sqrt(nv) : 0.0;
-    ak0 = fma(k0, fk, ak0);
-    ak1 = fma(k1, fk, ak1);
-    av0 = fma(v0, fv, av0);
-    av1 = fma(v1, fv, av1);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      double x0 = k0[u], x1 = k1[u];
+      if (rope) {
+        const double r0 = x0 * c - x1 * sn, r1 = x0 * sn + x1 * c;
+        x0 = r0;
+        x1 = r1;
+        const double cn = c * cs - sn * ss;
+        sn = sn * cs + c * ss;
+        c = cn;
+      }
+      // squared norms over the token's H2 lanes: row sums, then the rows of the token
+      double nk = row_sum_f64(fma(x0, x0, x1 * x1)), nv = row_sum_f64(fma(v0[u], v0[u], v1[u] * v1[u]));
+      {
+        const double k01 = readlane_f64(nk, 0) + readlane_f64(nk, 16);
+        const double k23 = readlane_f64(nk, 32) + readlane_f64(nk, 48);
+        const double v01 = readlane_f64(nv, 0) + readlane_f64(nv, 16);
+        const double v23 = readlane_f64(nv, 32) + readlane_f64(nv, 48);
+        if constexpr (TPW == 1) {
+          nk = k01 + k23;
+          nv = v01 + v23;
+        } else {
+          nk = sub ? k23 : k01;
+          nv = sub ? v23 : v01;
+        }
+      }
+      // sqrt(d) / ||x||: hardware reciprocal square root refined by two Newton steps (each
+      // squares the relative error; the mean is rounded to fp32)
+      double rk = __builtin_amdgcn_rsq(nk), rv = __builtin_amdgcn_rsq(nv);
+      rk *= fma(-0.5 * nk * rk, rk, 1.5);
+      rv *= fma(-0.5 * nv * rv, rv, 1.5);
+      rk *= fma(-0.5 * nk * rk, rk, 1.5);
+      rv *= fma(-0.5 * nv * rv, rv, 1.5);
+      const double fk = nk > 0.0 ? sqd * rk : 0.0, fv = nv > 0.0 ? sqd * rv : 0.0;
+      ak0 = fma(x0, fk, ak0);
+      ak1 = fma(x1, fk, ak1);
+      av0 = fma(v0[u], fv, av0);
+      av1 = fma(v1[u], fv, av1);
+    }
   }
   if constexpr (TPW == 2) {
     ak0 += __shfl_xor(ak0, 32, 64);
