@@ -59,7 +59,9 @@ __all__ = [
     "Codebook", "make_codebook", "hadamard", "rotation_matrix", "rope",
     "fp16_sat", "Codec", "make_codec", "encode", "pack_cache", "unpack_cache",
     "cache_layout", "attend", "attend_window", "decode_step", "search_scores",
-    "nsn_mean", "nsn_rotated_mean", "topk", "exact_topk",
+    "nsn_mean", "nsn_rotated_mean", "polar_angle_pdf", "polar_angle_cdf", "polar_level_codebook",
+    "make_polar_codebook", "polar_encode_angles", "polar_decode", "polar_encode", "polar_pack_codes",
+    "polar_unpack_codes", "estimate_scores_polar", "topk", "exact_topk",
 ]
 
 _GOLDEN_GAMMA = np.uint64(0x9E3779B97F4A7C15)
@@ -349,6 +351,180 @@ def encode(x, codec: Codec, *, kind: str, positions=None, rope_base: float = 0.0
 
 
 # ----------------------------------------------------------------------------------
+# PolarQuant stage 1 ([TurboQuant] news summary, "PolarQuant": adjacent coordinates are
+# paired and turned into (radius, angle); the radii are paired again, recursively, down to
+# one radius and d - 1 angles; the angles go on fixed grids whose boundaries are known in
+# advance, with no per-vector normalization).  Readings: d = 2^L, pairs (2i, 2i + 1) at
+# every level; a level-1 angle atan2(y_{2i+1}, y_{2i}) in [0, 2 pi) is uniform for a
+# rotated vector and gets a 4-bit uniform grid; a level-l angle (l >= 2) is
+# atan2(r_{2i+1}, r_{2i}) in [0, pi/2] with sin^2 psi ~ Beta(m/2, m/2), m = 2^(l-1), and
+# gets a 2-bit Lloyd-Max grid for that density; the last radius is the norm (fp16).  That
+# is 3 d - 2 bits of angles per vector.  Decoding uses each centroid's cos and sin rounded
+# to fp32 (the stored form).
+# ----------------------------------------------------------------------------------
+POLAR_B1, POLAR_BH = 4, 2
+
+
+def polar_angle_pdf(psi, m: int):
+    """Density of psi = atan2(|b|, |a|) for independent m-dim standard Gaussian a, b:
+    2^(2-m) sin^(m-1)(2 psi) / B(m/2, m/2) on [0, pi/2]."""
+    psi = np.asarray(psi, dtype=np.float64)
+    logc = (2 - m) * math.log(2.0) - (2 * gammaln(m / 2.0) - gammaln(float(m)))
+    with np.errstate(divide="ignore"):
+        s = np.sin(2.0 * psi)
+        out = np.where((psi > 0) & (psi < math.pi / 2), np.exp(logc + (m - 1) * np.log(np.abs(s))), 0.0)
+    return out
+
+
+def polar_angle_cdf(psi, m: int):
+    """F(psi) = I_{sin^2 psi}(m/2, m/2)."""
+    psi = np.clip(np.asarray(psi, dtype=np.float64), 0.0, math.pi / 2)
+    return betainc(m / 2.0, m / 2.0, np.sin(psi) ** 2)
+
+
+def polar_level_codebook(level: int):
+    """(centroids, boundaries) in fp64 of a level's angle grid, ascending."""
+    if level == 1:
+        K = 1 << POLAR_B1
+        w = 2.0 * math.pi / K
+        return np.array([(k + 0.5) * w for k in range(K)]), np.array([k * w for k in range(1, K)])
+    from scipy import integrate
+    m = 1 << (level - 1)
+    K = 1 << POLAR_BH
+    # start from equal-mass cells, then the Lloyd iteration with quadrature cell means
+    c = np.array([math.pi / 2 * (k + 0.5) / K for k in range(K)])
+    for _ in range(500):
+        t = 0.5 * (c[:-1] + c[1:])
+        edges = np.concatenate(([0.0], t, [math.pi / 2]))
+        P = np.diff(polar_angle_cdf(edges, m))
+        mom = np.array([integrate.quad(lambda x: x * polar_angle_pdf(x, m), edges[k], edges[k + 1],
+                                       epsabs=1e-15, epsrel=1e-13, limit=200)[0] for k in range(K)])
+        c_new = mom / P
+        delta = np.max(np.abs(c_new - c))
+        c = c_new
+        if delta < 1e-13:
+            break
+    return c, 0.5 * (c[:-1] + c[1:])
+
+
+class PolarCodebook:
+    """Angle grids of every level for d = 2^L, with the stored fp32 cos / sin."""
+
+    def __init__(self, d: int):
+        self.d, self.L = d, int(round(math.log2(d)))
+        assert 1 << self.L == d
+        self.c, self.t, self.cos, self.sin = {}, {}, {}, {}
+        for lv in range(1, self.L + 1):
+            c, t = polar_level_codebook(lv)
+            self.c[lv], self.t[lv] = c, t
+            self.cos[lv] = np.cos(c).astype(np.float32).astype(np.float64)
+            self.sin[lv] = np.sin(c).astype(np.float32).astype(np.float64)
+
+
+_POLAR_CACHE: dict = {}
+
+
+def make_polar_codebook(d: int) -> PolarCodebook:
+    if d not in _POLAR_CACHE:
+        _POLAR_CACHE[d] = PolarCodebook(d)
+    return _POLAR_CACHE[d]
+
+
+def polar_encode_angles(y, pc: PolarCodebook):
+    """y [N, d] -> (codes {level: [N, d / 2^level]}, angles {level: ...}, norm [N])."""
+    r = np.asarray(y, dtype=np.float64)
+    codes, angles = {}, {}
+    for lv in range(1, pc.L + 1):
+        a, b = r[:, 0::2], r[:, 1::2]
+        psi = np.arctan2(b, a)
+        if lv == 1:
+            psi = np.where(psi < 0, psi + 2 * math.pi, psi)
+        angles[lv] = psi
+        codes[lv] = np.sum(psi[..., None] >= pc.t[lv], axis=-1)
+        r = np.sqrt(a * a + b * b)
+    return codes, angles, r[:, 0]
+
+
+def polar_decode(codes, n, pc: PolarCodebook):
+    """Reconstruction from the angle codes and the norm n [N]: radii from the top level
+    down, each split by the stored cos / sin of its angle's centroid."""
+    r = np.asarray(n, dtype=np.float64)[:, None]
+    for lv in range(pc.L, 0, -1):
+        cd = np.asarray(codes[lv])
+        out = np.empty((r.shape[0], 2 * r.shape[1]))
+        out[:, 0::2] = r * pc.cos[lv][cd]
+        out[:, 1::2] = r * pc.sin[lv][cd]
+        r = out
+    return r
+
+
+def polar_encode(x, codec: "Codec", *, kind: str, positions=None, rope_base: float = 0.0):
+    """PolarQuant encode of rows of x: y = Pi RoPE(x) (keys) or Pi x (values), angle codes,
+    fp16 norm, and for keys the residual r = y - decode(codes, fp16(n)) with its QJL sketch
+    as in encode (the estimator is unchanged)."""
+    x = np.asarray(x, dtype=np.float64)
+    if kind == "key" and rope_base != 0:
+        x = rope(x, positions, rope_base)
+    y = x @ codec.Pi.T
+    pc = make_polar_codebook(codec.d)
+    codes, angles, n = polar_encode_angles(y, pc)
+    n16, over = fp16_sat(n)
+    yhat = polar_decode(codes, n16, pc)
+    out = {"y": y, "pcodes": codes, "angles": angles, "n": n, "n16": n16, "yhat": yhat, "overflow": over.copy()}
+    if kind == "key":
+        r = y - yhat
+        rn = np.sqrt(np.sum(r * r, axis=-1))
+        rn16, over_r = fp16_sat(rn)
+        z = r @ codec.S.T if codec.m > 0 else np.zeros(r.shape[:-1] + (0,))
+        out.update(r=r, rn=rn, rn16=rn16, z=z, bits=(z >= 0).astype(np.int64))
+        out["overflow"] = out["overflow"] | over_r
+    return out
+
+
+def polar_pack_codes(codes, d: int) -> np.ndarray:
+    """Angle codes {level: [N, d / 2^level]} -> [N, 3 d / 8] bytes: level-1 code i in bits
+    [4 i, 4 i + 4), then the levels 2, 3, ... one after the other, 2 bits each, from bit 2 d;
+    the last 2 bits are zero."""
+    L = int(round(math.log2(d)))
+    N = np.asarray(codes[1]).shape[0]
+    bits = np.zeros((N, 3 * d), dtype=np.uint8)
+    c1 = np.asarray(codes[1])
+    for k in range(POLAR_B1):
+        bits[:, k:2 * d:POLAR_B1] = (c1 >> k) & 1
+    pos = 2 * d
+    for lv in range(2, L + 1):
+        cl = np.asarray(codes[lv])
+        for j in range(cl.shape[1]):
+            for k in range(POLAR_BH):
+                bits[:, pos + POLAR_BH * j + k] = (cl[:, j] >> k) & 1
+        pos += POLAR_BH * cl.shape[1]
+    return _bits_to_bytes(bits)
+
+
+def polar_unpack_codes(rec, d: int):
+    """Inverse of polar_pack_codes."""
+    L = int(round(math.log2(d)))
+    bits = np.unpackbits(np.asarray(rec, dtype=np.uint8), axis=-1, bitorder="little").astype(np.int64)
+    codes = {1: sum(bits[..., k:2 * d:POLAR_B1] << k for k in range(POLAR_B1))}
+    pos = 2 * d
+    for lv in range(2, L + 1):
+        n = d >> lv
+        codes[lv] = sum(bits[..., pos + k:pos + POLAR_BH * n:POLAR_BH] << k for k in range(POLAR_BH))
+        pos += POLAR_BH * n
+    return codes
+
+
+def estimate_scores_polar(qr, sq, pcodes, n16, rn16, bits, codec: "Codec"):
+    """score_t = <qr, decode(codes_t, n16_t)> + rn16_t sqrt(pi/2)/m <sq, 2 bits_t - 1>."""
+    pc = make_polar_codebook(codec.d)
+    yhat = polar_decode(pcodes, n16, pc)
+    s = yhat @ qr
+    if codec.m > 0:
+        s = s + rn16 * codec.qjl_scale * ((2.0 * bits - 1.0) @ sq)
+    return s
+
+
+# ----------------------------------------------------------------------------------
 # NSN pre-transform ([NSNQuant] section 1, normalize-shift-normalize, and section 4 for
 # keys).  A token v becomes u = sqrt(d) v / ||v|| (s1 = ||v|| / sqrt(d)), the channel mean
 # o of the u is subtracted, and the result is normalized again (s2); v = s1 (s2 x + o).
@@ -395,6 +571,9 @@ def nsn_rotated_mean(o, codec: Codec) -> np.ndarray:
 #   NSN caches (desc nsn = 1, written after the desc in the header): Knorm records are 8
 #   bytes {fp16 n, fp16 ||r||, fp16 s1, 0}, Vnorm records 4 bytes {fp16 n, fp16 s1}, and a
 #   last region holds per unit [o_K, o_V, Pi o_K, Pi o_V] as fp32 [d] each.
+#   PolarQuant caches (desc polar = 1, bits_k = bits_v = 3): a key record is the 3 d / 8
+#   bytes of polar_pack_codes followed by the m QJL sign bits; values are token records of
+#   3 d / 8 bytes [batch][kv_heads][capacity] in place of the tiles; norms as above.
 #   Each region starts at a multiple of 256 bytes.
 # ----------------------------------------------------------------------------------
 CACHE_MAGIC = 0x564B5154
@@ -406,8 +585,8 @@ def _align(x, a=256):
     return (x + a - 1) // a * a
 
 
-def cache_layout(batch, kv_heads, d, capacity, bits_k, bits_v, m, nsn=0):
-    kbytes = (bits_k * d + m) // 8
+def cache_layout(batch, kv_heads, d, capacity, bits_k, bits_v, m, nsn=0, polar=0):
+    kbytes = (bits_k * d + m) // 8   # polar: 3 d / 8 angle bytes + m / 8 (bits_k = 3)
     units = batch * kv_heads
     tiles = (capacity + 31) // 32
     off = {"knrec": 8 if nsn else 4, "vnrec": 4 if nsn else 2}
@@ -418,7 +597,7 @@ def cache_layout(batch, kv_heads, d, capacity, bits_k, bits_v, m, nsn=0):
     cur = _align(cur + units * capacity * off["knrec"])
     if bits_v > 0:
         off["vcodes"] = cur
-        cur = _align(cur + units * tiles * d * 4 * bits_v)
+        cur = _align(cur + (units * capacity * 3 * d // 8 if polar else units * tiles * d * 4 * bits_v))
         off["vnorm"] = cur
         cur = _align(cur + units * capacity * off["vnrec"])
     if nsn:
@@ -447,28 +626,33 @@ def pack_cache(desc: dict, fields: dict, start_pos: int = 0, image: np.ndarray |
             NSN caches also ks1, vs1 [B, H, n] and the unit means ok, ov, pok, pov [B, H, d]."""
     B, H, d, cap = desc["batch"], desc["kv_heads"], desc["d"], desc["capacity"]
     bk, bv, m = desc["bits_k"], desc["bits_v"], desc["m"]
-    nsn = int(desc.get("nsn", 0))
-    lay = cache_layout(B, H, d, cap, bk, bv, m, nsn)
+    nsn, polar = int(desc.get("nsn", 0)), int(desc.get("polar", 0))
+    lay = cache_layout(B, H, d, cap, bk, bv, m, nsn, polar)
     if image is None:
         image = np.zeros(lay["total"], dtype=np.uint8)
     hdr = np.zeros(HEADER_BYTES // 4, dtype=np.uint32)
     hdr[0], hdr[1], hdr[2] = CACHE_MAGIC, CACHE_VERSION, flags
-    hdr[4:12] = np.array([B, H, d, cap, bk, bv, m, nsn], dtype=np.int64).astype(np.uint32)
+    hdr[4:13] = np.array([B, H, d, cap, bk, bv, m, nsn, polar], dtype=np.int64).astype(np.uint32)
     hdr[2] |= np.uint32(image[8:12].view(np.uint32)[0])
     image[:HEADER_BYTES] = hdr.view(np.uint8)
     if nsn:
         means = np.stack([np.asarray(fields[f], dtype=np.float32) for f in ("ok", "ov", "pok", "pov")], axis=2)
         image[lay["nsn"]:lay["nsn"] + B * H * 4 * d * 4] = means.reshape(-1).view(np.uint8)
 
-    kcodes = np.asarray(fields["kcodes"])
-    n = kcodes.shape[2]
+    n = np.asarray(fields["n16"]).shape[2]
     if n == 0:
         return image
     assert start_pos + n <= cap
     kb = lay["kbytes"]
-    planes = [((kcodes >> p) & 1) for p in range(bk)]
-    kbitsm = np.concatenate(planes + [np.asarray(fields["bits"])], axis=-1)  # [B,H,n,bk*d+m]
-    rec = _bits_to_bytes(kbitsm)  # [B,H,n,kb]
+    if polar:
+        ang = polar_pack_codes({lv: np.asarray(c).reshape(B * H * n, -1) for lv, c in fields["kpc"].items()}, d)
+        sgn = _bits_to_bytes(np.asarray(fields["bits"]).reshape(B * H * n, m)) if m else np.zeros((B * H * n, 0), np.uint8)
+        rec = np.concatenate([ang, sgn], axis=-1).reshape(B, H, n, kb)
+    else:
+        kcodes = np.asarray(fields["kcodes"])
+        planes = [((kcodes >> p) & 1) for p in range(bk)]
+        kbitsm = np.concatenate(planes + [np.asarray(fields["bits"])], axis=-1)  # [B,H,n,bk*d+m]
+        rec = _bits_to_bytes(kbitsm)  # [B,H,n,kb]
     kreg = image[lay["kbits"]:lay["kbits"] + B * H * cap * kb].reshape(B, H, cap, kb)
     kreg[:, :, start_pos:start_pos + n, :] = rec
     kn = lay["knrec"] // 2
@@ -477,7 +661,14 @@ def pack_cache(desc: dict, fields: dict, start_pos: int = 0, image: np.ndarray |
         norms += [np.asarray(fields["ks1"]), np.zeros_like(np.asarray(fields["n16"]))]
     nreg = image[lay["knorm"]:lay["knorm"] + B * H * cap * 2 * kn].view(np.float16).reshape(B, H, cap, kn)
     nreg[:, :, start_pos:start_pos + n, :] = np.stack(norms, axis=-1).astype(np.float16)
-    if bv > 0:
+    if bv > 0 and polar:
+        vb = 3 * d // 8
+        vreg = image[lay["vcodes"]:lay["vcodes"] + B * H * cap * vb].reshape(B, H, cap, vb)
+        ang = polar_pack_codes({lv: np.asarray(c).reshape(B * H * n, -1) for lv, c in fields["vpc"].items()}, d)
+        vreg[:, :, start_pos:start_pos + n, :] = ang.reshape(B, H, n, vb)
+        vnreg = image[lay["vnorm"]:lay["vnorm"] + B * H * cap * 2].view(np.float16).reshape(B, H, cap)
+        vnreg[:, :, start_pos:start_pos + n] = np.asarray(fields["vn16"]).astype(np.float16)
+    elif bv > 0:
         vcodes = np.asarray(fields["vcodes"]).astype(np.int64)
         tiles = lay["tiles"]
         wbytes = 4 * bv
@@ -503,20 +694,23 @@ def unpack_cache(image: np.ndarray, desc: dict, length: int) -> dict:
     """Inverse of pack_cache for tokens [0, length).  Codes and bits come back as uint8."""
     B, H, d, cap = desc["batch"], desc["kv_heads"], desc["d"], desc["capacity"]
     bk, bv, m = desc["bits_k"], desc["bits_v"], desc["m"]
-    nsn = int(desc.get("nsn", 0))
-    lay = cache_layout(B, H, d, cap, bk, bv, m, nsn)
+    nsn, polar = int(desc.get("nsn", 0)), int(desc.get("polar", 0))
+    lay = cache_layout(B, H, d, cap, bk, bv, m, nsn, polar)
     image = np.asarray(image, dtype=np.uint8)
     hdr = image[:HEADER_BYTES].view(np.uint32)
     kb = lay["kbytes"]
     kreg = image[lay["kbits"]:lay["kbits"] + B * H * cap * kb].reshape(B, H, cap, kb)[:, :, :length]
     bitsall = np.unpackbits(kreg, axis=-1, bitorder="little")
-    kcodes = np.zeros((B, H, length, d), dtype=np.uint8)
-    for p in range(bk):
-        kcodes |= bitsall[..., p * d:(p + 1) * d] << np.uint8(p)
-    out = {
-        "magic": int(hdr[0]), "version": int(hdr[1]), "flags": int(hdr[2]),
-        "kcodes": kcodes, "bits": bitsall[..., bk * d:bk * d + m],
-    }
+    out = {"magic": int(hdr[0]), "version": int(hdr[1]), "flags": int(hdr[2]),
+           "bits": bitsall[..., bk * d:bk * d + m]}
+    if polar:
+        pcs = polar_unpack_codes(kreg[..., :3 * d // 8].reshape(B * H * length, -1), d)
+        out["kpc"] = {lv: c.reshape(B, H, length, -1) for lv, c in pcs.items()}
+    else:
+        kcodes = np.zeros((B, H, length, d), dtype=np.uint8)
+        for p in range(bk):
+            kcodes |= bitsall[..., p * d:(p + 1) * d] << np.uint8(p)
+        out["kcodes"] = kcodes
     kn = lay["knrec"] // 2
     nreg = image[lay["knorm"]:lay["knorm"] + B * H * cap * 2 * kn].view(np.float16).reshape(B, H, cap, kn)
     out["n16"] = nreg[:, :, :length, 0].astype(np.float64)
@@ -526,7 +720,14 @@ def unpack_cache(image: np.ndarray, desc: dict, length: int) -> dict:
         means = image[lay["nsn"]:lay["nsn"] + B * H * 4 * d * 4].view(np.float32).reshape(B, H, 4, d)
         for i, f in enumerate(("ok", "ov", "pok", "pov")):
             out[f] = means[:, :, i].astype(np.float64)
-    if bv > 0:
+    if bv > 0 and polar:
+        vb = 3 * d // 8
+        vreg = image[lay["vcodes"]:lay["vcodes"] + B * H * cap * vb].reshape(B, H, cap, vb)[:, :, :length]
+        pcs = polar_unpack_codes(vreg.reshape(B * H * length, -1), d)
+        out["vpc"] = {lv: c.reshape(B, H, length, -1) for lv, c in pcs.items()}
+        vnreg = image[lay["vnorm"]:lay["vnorm"] + B * H * cap * 2].view(np.float16).reshape(B, H, cap)
+        out["vn16"] = vnreg[:, :, :length].astype(np.float64)
+    elif bv > 0:
         tiles = lay["tiles"]
         wbytes = 4 * bv
         vreg = image[lay["vcodes"]:lay["vcodes"] + B * H * tiles * d * wbytes].reshape(B, H, tiles, d, wbytes)
@@ -562,6 +763,32 @@ def estimate_scores(qr: np.ndarray, sq: np.ndarray, kcodes, n16, rn16, bits, cod
     return mse + qjl
 
 
+def _packed_scores(fields, b, g, length, qr, sq, codec):
+    """Score estimates of the packed tokens [0, length) of unit (b, g): scalar codes or
+    PolarQuant angles, plus the NSN mean term when the fields carry one."""
+    if "kpc" in fields:
+        s = estimate_scores_polar(qr, sq, {lv: c[b, g, :length] for lv, c in fields["kpc"].items()},
+                                  fields["n16"][b, g, :length], fields["rn16"][b, g, :length],
+                                  fields["bits"][b, g, :length], codec)
+    else:
+        s = estimate_scores(qr, sq, fields["kcodes"][b, g, :length], fields["n16"][b, g, :length],
+                            fields["rn16"][b, g, :length], fields["bits"][b, g, :length], codec)
+    if "ks1" in fields:   # NSN: the mean's share s1 <q, o>, in the rotated basis
+        s = s + fields["ks1"][b, g, :length] * (fields["pok"][b, g] @ qr)
+    return s
+
+
+def _packed_values(fields, b, g, length, codec):
+    """Reconstructed rotated values [length, d] of unit (b, g)."""
+    if "vpc" in fields:
+        return polar_decode({lv: c[b, g, :length] for lv, c in fields["vpc"].items()},
+                            fields["vn16"][b, g, :length], make_polar_codebook(codec.d))
+    vhat = fields["vn16"][b, g, :length, None] * codec.cb_v.c[fields["vcodes"][b, g, :length]]
+    if "vs1" in fields:
+        vhat = vhat + fields["vs1"][b, g, :length, None] * fields["pov"][b, g][None, :]
+    return vhat
+
+
 def attend(fields: dict, q, codec: Codec, *, q_pos: int, rope_base: float, scale: float,
            kv_heads: int, length: int):
     """fp64 decode attention of q [B, Hq, d] over tokens [0, length) of `fields`
@@ -584,18 +811,12 @@ def attend(fields: dict, q, codec: Codec, *, q_pos: int, rope_base: float, scale
             sq = codec.S @ qr if codec.m > 0 else None
             if length == 0:
                 continue
-            s = estimate_scores(qr, sq, fields["kcodes"][b, g, :length], fields["n16"][b, g, :length],
-                                fields["rn16"][b, g, :length], fields["bits"][b, g, :length], codec)
-            if "ks1" in fields:   # NSN: the mean's share s1 <q, o>, in the rotated basis
-                s = s + fields["ks1"][b, g, :length] * (fields["pok"][b, g] @ qr)
+            s = _packed_scores(fields, b, g, length, qr, sq, codec)
             scores[b, h] = s
             lam = scale * s
             p = np.exp(lam - np.max(lam))
             p = p / np.sum(p)
-            vhat = fields["vn16"][b, g, :length, None] * codec.cb_v.c[fields["vcodes"][b, g, :length]]
-            if "vs1" in fields:
-                vhat = vhat + fields["vs1"][b, g, :length, None] * fields["pov"][b, g][None, :]
-            o_rot = p @ vhat
+            o_rot = p @ _packed_values(fields, b, g, length, codec)
             out[b, h] = codec.Pi.T @ o_rot
     return out, scores
 
@@ -631,11 +852,7 @@ def attend_window(fields: dict, win_k, win_v, q, codec: Codec, *, q_pos: int, ro
                 continue
             s = np.zeros(n)
             if length > 0:
-                s[:length] = estimate_scores(qr, sq, fields["kcodes"][b, g, :length],
-                                             fields["n16"][b, g, :length], fields["rn16"][b, g, :length],
-                                             fields["bits"][b, g, :length], codec)
-                if "ks1" in fields:
-                    s[:length] += fields["ks1"][b, g, :length] * (fields["pok"][b, g] @ qr)
+                s[:length] = _packed_scores(fields, b, g, length, qr, sq, codec)
             if win_len > 0:
                 kr = rope(wk[b, g, :win_len], pos, rope_base) if rope_base != 0 else wk[b, g, :win_len]
                 s[length:] = kr @ qp
@@ -645,10 +862,7 @@ def attend_window(fields: dict, win_k, win_v, q, codec: Codec, *, q_pos: int, ro
             p = p / np.sum(p)
             o = np.zeros(d)
             if length > 0:
-                vhat = fields["vn16"][b, g, :length, None] * codec.cb_v.c[fields["vcodes"][b, g, :length]]
-                if "vs1" in fields:
-                    vhat = vhat + fields["vs1"][b, g, :length, None] * fields["pov"][b, g][None, :]
-                o += codec.Pi.T @ (p[:length] @ vhat)
+                o += codec.Pi.T @ (p[:length] @ _packed_values(fields, b, g, length, codec))
             if win_len > 0:
                 o += p[length:] @ wv[b, g, :win_len]
             out[b, h] = o

@@ -662,3 +662,125 @@ def test_nsn_pack_layout(O):
     np.testing.assert_array_equal(u["vs1"][:, :, 3:], z + 0.5)
     for k in means:
         np.testing.assert_array_equal(u[k], means[k])
+
+
+# ------------------------------------------------------------------ PolarQuant ([TurboQuant] "PolarQuant")
+@pytest.mark.parametrize("m", [2, 4, 64])
+def test_polar_angle_law_by_quadrature_and_sampling(O, m):
+    # the angle between two independent m-dim Gaussian blocks' norms: density integrates to
+    # 1, the closed-form CDF (incomplete beta) matches quadrature of the density, and a
+    # sample of atan2(|b|, |a|) follows it (KS)
+    f = lambda x: O.polar_angle_pdf(np.array([x]), m)[0]
+    assert abs(integrate.quad(f, 0, math.pi / 2, limit=200, epsabs=1e-14)[0] - 1.0) < 1e-10
+    for x in (0.3, math.pi / 4, 1.2):
+        assert abs(integrate.quad(f, 0, x, limit=200, epsabs=1e-14)[0] - O.polar_angle_cdf(x, m)) < 1e-10
+    rng = np.random.default_rng(m)
+    a = np.linalg.norm(rng.standard_normal((40000, m)), axis=1)
+    b = np.linalg.norm(rng.standard_normal((40000, m)), axis=1)
+    assert stats.kstest(np.arctan2(b, a), lambda x: O.polar_angle_cdf(x, m)).pvalue > 1e-4
+
+
+@pytest.mark.parametrize("level", [1, 2, 3, 7])
+def test_polar_grids_are_lloyd_max(O, level):
+    c, t = O.polar_level_codebook(level)
+    np.testing.assert_allclose(t, 0.5 * (c[:-1] + c[1:]), rtol=0, atol=1e-15)
+    if level == 1:   # uniform on [0, 2 pi): equal sectors, centroids at their middles
+        w = 2 * math.pi / 16
+        np.testing.assert_allclose(c, (np.arange(16) + 0.5) * w, atol=1e-15)
+        return
+    m = 1 << (level - 1)
+    np.testing.assert_allclose(c + c[::-1], math.pi / 2, atol=1e-13)   # the law is symmetric about pi/4
+    f = lambda x: O.polar_angle_pdf(np.array([x]), m)[0]
+    edges = np.concatenate(([0.0], t, [math.pi / 2]))
+    for k in range(len(c)):
+        mass = integrate.quad(f, edges[k], edges[k + 1], limit=400, epsabs=1e-15)[0]
+        mom = integrate.quad(lambda x: x * f(x), edges[k], edges[k + 1], limit=400, epsabs=1e-15)[0]
+        assert abs(mom / mass - c[k]) < 1e-10
+
+
+def test_polar_encode_worked_example(O):
+    # d = 4, y = (1, 1, 0, 2): level-1 angles pi/4 and pi/2 (sectors of pi/8: codes 2 and
+    # 4), radii sqrt 2 and 2; level-2 angle atan(sqrt 2) against the m = 2 grid; norm sqrt 6
+    pc = O.make_polar_codebook(4)
+    codes, angles, n = O.polar_encode_angles(np.array([[1.0, 1.0, 0.0, 2.0]]), pc)
+    assert list(codes[1][0]) == [2, 4]
+    np.testing.assert_allclose(angles[2][0, 0], math.atan(math.sqrt(2)), atol=1e-15)
+    assert codes[2][0, 0] == int(np.sum(math.atan(math.sqrt(2)) >= pc.t[2]))
+    np.testing.assert_allclose(n[0], math.sqrt(6), atol=1e-15)
+    # a negative-angle pair lands in [pi, 2 pi): (1, -1) is at 7 pi / 4, code 14
+    c2, _, _ = O.polar_encode_angles(np.array([[1.0, -1.0, 1.0, 0.0]]), pc)
+    assert list(c2[1][0]) == [14, 0]
+
+
+def test_polar_decode_norm_and_grid_points(O):
+    d = 64
+    pc = O.make_polar_codebook(d)
+    rng = np.random.default_rng(12)
+    codes = {lv: rng.integers(0, 16 if lv == 1 else 4, (50, d >> lv)) for lv in range(1, pc.L + 1)}
+    n = rng.uniform(0.5, 9, 50)
+    y = O.polar_decode(codes, n, pc)
+    # every level splits a radius by a stored (cos, sin) pair: the norm survives up to their
+    # fp32 rounding
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), n, rtol=1e-6)
+    # points built from the exact centroid angles encode back to the same codes
+    exact = {lv: pc.c[lv][codes[lv]] for lv in codes}
+    r = n[:, None]
+    for lv in range(pc.L, 0, -1):
+        out = np.empty((50, 2 * r.shape[1]))
+        out[:, 0::2] = r * np.cos(exact[lv])
+        out[:, 1::2] = r * np.sin(exact[lv])
+        r = out
+    back, _, nn = O.polar_encode_angles(r, pc)
+    for lv in codes:
+        np.testing.assert_array_equal(back[lv], codes[lv])
+    np.testing.assert_allclose(O.polar_decode(back, nn, pc), r, rtol=0, atol=1e-6 * n.max())
+
+
+def test_polar_reconstruction_error(O):
+    # rotated Gaussian vectors at 3 - 2/d bits: the level-1 sectors alone cost
+    # 2 - 2 sin(pi/16) / (pi/16) ~ 0.0128 of the squared norm; all levels together stay
+    # well below the error of a swapped cos / sin or a wrong level order (order 1)
+    d = 128
+    codec = O.make_codec(d, 3, 3, d, seed=2)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((400, d))
+    e = O.polar_encode(x, codec, kind="value")
+    rel = np.mean(np.sum((e["yhat"] - e["y"]) ** 2, axis=1) / np.sum(e["y"] ** 2, axis=1))
+    lvl1 = 2 - 2 * math.sin(math.pi / 16) / (math.pi / 16)
+    assert lvl1 < rel < 4 * lvl1
+
+
+def test_polar_pack_bit_positions(O):
+    # d = 8: four level-1 nibbles (bits 0..15), two level-2 codes (16..19), one level-3 code
+    # (20..21), two zero bits
+    codes = {1: np.array([[1, 15, 0, 6]]), 2: np.array([[3, 1]]), 3: np.array([[2]])}
+    rec = O.polar_pack_codes(codes, 8)
+    assert list(rec[0]) == [0xF1, 0x60, 0x27]
+    back = O.polar_unpack_codes(rec, 8)
+    for lv in codes:
+        np.testing.assert_array_equal(back[lv], codes[lv])
+
+
+def test_polar_attention_is_textbook(O):
+    # packed polar keys with zero residual and polar values: attention equals softmax over
+    # K = Pi^T decode(codes, n) and V = Pi^T decode(codes_v, n_v), with RoPE on q and GQA
+    d, B, Hkv, Hq, T = 64, 1, 2, 4, 21
+    codec = O.make_codec(d, 3, 3, d, seed=6)
+    pc = O.make_polar_codebook(d)
+    rng = np.random.default_rng(14)
+    mk = lambda: {lv: rng.integers(0, 16 if lv == 1 else 4, (B, Hkv, T, d >> lv)) for lv in range(1, pc.L + 1)}
+    kpc, vpc = mk(), mk()
+    f16 = lambda a: np.asarray(a).astype(np.float16).astype(np.float64)
+    fields = {"kpc": kpc, "vpc": vpc, "n16": f16(rng.uniform(1, 9, (B, Hkv, T))), "rn16": np.zeros((B, Hkv, T)),
+              "bits": np.ones((B, Hkv, T, d)), "vn16": f16(rng.uniform(1, 9, (B, Hkv, T)))}
+    q = rng.standard_normal((B, Hq, d))
+    out, scores = O.attend(fields, q, codec, q_pos=30, rope_base=10000.0, scale=0.25, kv_heads=Hkv, length=T)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        K = O.polar_decode({lv: c[0, g] for lv, c in kpc.items()}, fields["n16"][0, g], pc) @ codec.Pi
+        V = O.polar_decode({lv: c[0, g] for lv, c in vpc.items()}, fields["vn16"][0, g], pc) @ codec.Pi
+        qq = O.rope(q[0, h][None], [30], 10000.0)[0]
+        sc = K @ qq
+        w = np.exp(0.25 * (sc - sc.max()))
+        np.testing.assert_allclose(scores[0, h], sc, rtol=1e-11, atol=1e-10)
+        np.testing.assert_allclose(out[0, h], (w / w.sum()) @ V, rtol=1e-11, atol=1e-10)
