@@ -436,7 +436,7 @@ def polar_encode_angles(y, pc: PolarCodebook):
     codes, angles = {}, {}
     for lv in range(1, pc.L + 1):
         a, b = r[:, 0::2], r[:, 1::2]
-        psi = np.arctan2(b, a)
+        psi = np.arctan2(b + 0.0, a + 0.0)   # signed zeros count as +0 (a zero pair has angle 0)
         if lv == 1:
             psi = np.where(psi < 0, psi + 2 * math.pi, psi)
         angles[lv] = psi

@@ -67,6 +67,68 @@ def oracle_encode_unitwise(K, V, codec, positions, rope_base, means=None):
     return out
 
 
+def oracle_encode_polar(K, V, codec, positions, rope_base):
+    """PolarQuant fields of every unit: kpc / vpc {level: [B, H, T, d / 2^level]}, norms,
+    QJL bits, plus the oracle's angles and exact norms for the parity rule."""
+    B, H, T, d = K.shape
+    ke = O.polar_encode(K.reshape(-1, d), codec, kind="key", positions=np.tile(positions, B * H),
+                        rope_base=rope_base)
+    ve = O.polar_encode(V.reshape(-1, d), codec, kind="value")
+    rs = lambda a: np.asarray(a).reshape((B, H, T) + np.asarray(a).shape[1:])
+    return {"kpc": {lv: rs(c) for lv, c in ke["pcodes"].items()}, "kang": {lv: rs(c) for lv, c in ke["angles"].items()},
+            "n16": rs(ke["n16"]), "kn": rs(ke["n"]), "rn16": rs(ke["rn16"]), "krn": rs(ke["rn"]),
+            "bits": rs(ke["bits"]), "kz": rs(ke["z"]),
+            "vpc": {lv: rs(c) for lv, c in ve["pcodes"].items()}, "vang": {lv: rs(c) for lv, c in ve["angles"].items()},
+            "vn16": rs(ve["n16"]), "vn": rs(ve["n"])}
+
+
+def compare_polar_codes(gpu: dict, orc: dict, codec, report=None):
+    """PolarQuant records under the parity rule: an angle code may differ only when the
+    oracle's angle lies within 1e-6 rad of one of its level's boundaries, a norm only next to
+    an fp16 midpoint; a key whose codes or norm differ has a different residual, so its QJL
+    bits and residual norm are compared only when they agree."""
+    pc = O.make_polar_codebook(codec.d)
+    res = {"codes": 0, "excused": 0, "dependent": 0}
+    shape = orc["n16"].shape
+    for side in ("k", "v"):
+        pcs, ang = orc[side + "pc"], orc[side + "ang"]
+        tok_bad = np.zeros(shape, bool)
+        for lv in pcs:
+            bad = gpu[side + "pc"][lv] != pcs[lv]
+            res["codes"] += pcs[lv].size
+            if np.any(bad):
+                near = np.min(np.abs(ang[lv][..., None] - pc.t[lv]), axis=-1) <= MARGIN
+                assert np.all(near[bad]), f"{int(np.sum(bad & ~near))} {side} angle codes (level {lv}) differ away from a boundary"
+                res["excused"] += int(np.sum(bad))
+                tok_bad |= np.any(bad, axis=-1)
+        nf, nx = ("n16", "kn") if side == "k" else ("vn16", "vn")
+        nb = gpu[nf] != orc[nf]
+        if np.any(nb):
+            ok = _near_fp16_midpoint(orc[nx])
+            assert np.all(ok[nb]), f"{int(np.sum(nb & ~ok))} {side} norms differ"
+            res["excused"] += int(np.sum(nb))
+            tok_bad |= nb
+        if side == "k" and codec.m > 0:
+            same = ~tok_bad
+            b_bad = (gpu["bits"] != orc["bits"]) & same[..., None]
+            res["codes"] += orc["bits"].size
+            if np.any(b_bad):
+                scale = np.where(orc["krn"] > 0, orc["krn"], 1.0)[..., None]
+                ok = np.abs(orc["kz"]) / scale <= MARGIN
+                assert np.all(ok[b_bad]), f"{int(np.sum(b_bad & ~ok))} QJL bits differ away from zero"
+                res["excused"] += int(np.sum(b_bad))
+            rn_bad = (gpu["rn16"] != orc["rn16"]) & same
+            if np.any(rn_bad):
+                ok = _near_fp16_midpoint(orc["krn"])
+                assert np.all(ok[rn_bad]), f"{int(np.sum(rn_bad & ~ok))} residual norms differ"
+                res["excused"] += int(np.sum(rn_bad))
+            res["dependent"] += int(np.sum((gpu["bits"] != orc["bits"]) & ~same[..., None]))
+    assert res["excused"] <= MARGIN * res["codes"], f"excused mismatches over budget: {res}"
+    if report is not None:
+        report.update(res)
+    return res
+
+
 def _near_boundary(u, t):
     return np.min(np.abs(u[..., None] - t), axis=-1) <= MARGIN
 

@@ -291,6 +291,52 @@ def test_nsn_codes_and_decode(tq, P, bk, d, G, L0, T, dist):
         assert e_e2e <= TOL
 
 
+@pytest.mark.parametrize("d,G,T,chunks,dist", [
+    (128, 8, 700, [(0, 300), (300, 700)], "laplace"),   # two appends, a ragged tail
+    (64, 4, 530, None, "student_t3"),
+    (128, 2, 64, None, "normal"),
+])
+def test_polar_codes_and_decode(tq, P, d, G, T, chunks, dist):
+    """PolarQuant caches ([TurboQuant] "PolarQuant" as stage 1, QJL on the key residual):
+    every angle code, norm and QJL bit against the oracle's polar encode; decode and logits
+    over the oracle's polar cache; decode end to end over the GPU's own."""
+    w = W.LONG_CONTEXT.scaled(batch=2, kv_heads=2, q_heads=2 * G, d=d, m=d, context=T, bits_k=3, bits_v=3,
+                              dist=dist)
+    K, V = W.gen_kv(w)
+    q = W.gen_q(w)
+    Kd, Vd = P.to_f64(K), P.to_f64(V)
+    codec_o = O.make_codec(d, 3, 3, d, 0)
+    fields = P.oracle_encode_polar(Kd, Vd, codec_o, np.arange(T), w.rope_base)
+    codec = tq.Codec(d, 3, 3, d, seed=0)
+    cache = tq.PackedCache(w.batch, w.kv_heads, d, T, 3, 3, d, polar=1)
+    Kc, Vc = K.cuda(), V.cuda()
+    for s0, s1 in chunks or [(0, T)]:
+        tq.quantize_kv(cache.desc, codec.dev, cache.buf, Kc[:, :, s0:s1].contiguous(), Vc[:, :, s0:s1].contiguous(),
+                       s0, w.rope_base)
+    torch.cuda.synchronize()
+    rep = {}
+    P.compare_polar_codes(P.gpu_fields(cache, T), fields, codec_o, rep)
+    ocache = tq.PackedCache(w.batch, w.kv_heads, d, T, 3, 3, d, polar=1)
+    ocache.buf.copy_(torch.from_numpy(P.oracle_image(ocache.desc.as_dict(), fields)))
+    out, sc = decode(tq, codec, ocache, q.cuda(), T, w.q_pos, w.rope_base)
+    out_o, sc_o = O.attend(fields, P.to_f64(q), codec_o, q_pos=w.q_pos, rope_base=w.rope_base, scale=0.0,
+                           kv_heads=w.kv_heads, length=T)
+    e_out = P.max_abs(out.cpu().numpy(), out_o)
+    e_sc = P.max_abs(sc.cpu().numpy()[:, :, :T], sc_o)
+    out2, _ = decode(tq, codec, cache, q.cuda(), T, w.q_pos, w.rope_base, want_scores=False)
+    e_e2e = P.max_abs(out2.cpu().numpy(), out_o)
+    sc3 = torch.full((w.batch, w.q_heads, T), float("nan"), dtype=torch.float32, device="cuda")
+    ws3 = torch.empty(tq.decode_workspace_bytes(ocache.desc, w.q_heads, T), dtype=torch.uint8, device="cuda")
+    tq.decode_attend(ocache.desc, codec.dev, ocache.buf, T, q.cuda(), w.q_pos, w.rope_base, None, scores=sc3, ws=ws3)
+    torch.cuda.synchronize()
+    e_lg = P.max_abs(sc3.cpu().numpy(), sc_o)
+    say(f"    polar d{d} G{G} T {T} {dist}: codes {rep} | out {e_out:.2e} scores {e_sc:.2e} e2e {e_e2e:.2e} "
+        f"logits {e_lg:.2e}")
+    assert e_out <= TOL and e_sc <= TOL and e_lg <= TOL
+    if rep["excused"] == 0:
+        assert e_e2e <= TOL
+
+
 @pytest.mark.parametrize("bk,bv,d,G,L0,cap,steps,dt,nsn", [
     (2, 3, 128, 4, 300, 16, 40, "bf16", 0),   # MFMA path, two flushes
     (3, 4, 64, 8, 0, 8, 20, "f32", 0),        # fp32 path, starting from an empty cache

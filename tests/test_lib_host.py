@@ -83,6 +83,12 @@ def test_cache_layout_matches_oracle(tq, O):
     # NSN caches: wider norm records and the per-unit means region
     for args in [(1, 1, 128, 1024, 2, 3, 128), (3, 5, 64, 100, 3, 4, 64), (2, 2, 128, 33, 1, 3, 128)]:
         assert tq.cache_bytes(tq.CacheDesc(*args, 1)) == O.cache_layout(*args, 1)["total"]
+    # PolarQuant caches: the same region sizes as 3-bit keys and values (token records)
+    for args in [(1, 1, 128, 1024, 3, 3, 128), (3, 5, 64, 100, 3, 3, 64), (2, 2, 128, 33, 3, 0, 64)]:
+        assert tq.cache_bytes(tq.CacheDesc(*args, 0, 1)) == O.cache_layout(*args, 0, 1)["total"]
+    assert tq.cache_bytes(tq.CacheDesc(1, 1, 128, 64, 2, 3, 128, 0, 1)) == 0    # bits must be 3
+    assert tq.cache_bytes(tq.CacheDesc(1, 1, 128, 64, 3, 3, 128, 1, 1)) == 0    # not with NSN
+    assert tq.cache_bytes(tq.CacheDesc(1, 1, 256, 64, 3, 0, 256, 0, 1)) == 0    # d = 64 or 128
     # NSN needs values and d = 64 or 128
     assert tq.cache_bytes(tq.CacheDesc(1, 1, 128, 64, 2, 0, 128, 1)) == 0
     assert tq.cache_bytes(tq.CacheDesc(1, 1, 256, 64, 2, 3, 256, 1)) == 0
@@ -144,3 +150,29 @@ def test_decode_split_choice_and_workspace(tq):
     s = tq.decode_splits(d, 64, 131072)
     assert s >= 1
     assert tq.decode_workspace_bytes(d, 64, 131072) == tq.decode_workspace_bytes(d, 64, 0, splits=s)
+
+
+@pytest.mark.parametrize("level", [1, 2, 3, 4, 5, 6, 7])
+def test_polar_grids_match_oracle(tq, O, level):
+    # two independent Lloyd iterations (C++ Gauss-Legendre cells, scipy quadrature) agree
+    c, t = tq.make_polar_grid(level)
+    co, to = O.polar_level_codebook(level)
+    np.testing.assert_allclose(c, co, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(t, to, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_codec_polar_tables_match_oracle(tq, O, d):
+    # the codec table's stored cos / sin (fp32) and boundaries (fp64) of every level of d
+    blob = tq.codec_build(tq.CodecDesc(d, 3, 3, d, 0))
+    pc = O.make_polar_codebook(d)
+    al = lambda n: (n + 255) // 256 * 256
+    pt_off = len(blob) - al(11 * 16 * 8)              # fp64 boundaries, the last section
+    pcs_off = pt_off - al(11 * 16 * 2 * 4)            # fp32 cos / sin just before
+    pt = blob[pt_off:pt_off + 11 * 16 * 8].view(np.float64).reshape(11, 16)
+    pcs = blob[pcs_off:pcs_off + 11 * 16 * 2 * 4].view(np.float32).reshape(11, 16, 2)
+    for lv in range(1, pc.L + 1):
+        K = 16 if lv == 1 else 4
+        assert np.count_nonzero(pcs[lv - 1, :K, 0] != pc.cos[lv]) == 0
+        assert np.count_nonzero(pcs[lv - 1, :K, 1] != pc.sin[lv]) == 0
+        np.testing.assert_allclose(pt[lv - 1, :K - 1], pc.t[lv], rtol=0, atol=1e-12)
