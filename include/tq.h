@@ -64,10 +64,17 @@ typedef struct {
  * token v is stored as the codec of w = v - s1 o with s1 = ||v|| / sqrt(d) kept in fp16
  * and o the unit's channel mean (tq_nsn_set_means); the codec's own norm and direction
  * are NSN's second normalization.  Requires bits_v > 0 and d = 64 or 128; nsn = 0 is the
- * plain codec. */
+ * plain codec.
+ * polar = 1 selects PolarQuant ([TurboQuant] news summary, "PolarQuant") as stage 1 in
+ * place of the per-coordinate codes: the rotated vector's adjacent coordinates are turned
+ * into (radius, angle) pairs, the radii paired again recursively down to one radius (the
+ * norm, fp16) and d - 1 angles, each angle coded on a fixed grid (tq_make_polar_grid):
+ * 4 bits for a level-1 angle, 2 bits above, 3 d - 2 bits in all; keys keep the QJL sketch
+ * of their residual.  Requires d = 64 or 128, bits_k = 3, bits_v = 0 or 3, nsn = 0. */
 typedef struct {
   int32_t batch, kv_heads, d, capacity, bits_k, bits_v, m;
   int32_t nsn;
+  int32_t polar;
 } tq_cache_desc;
 
 typedef void *tq_stream_t; /* hipStream_t */
@@ -92,6 +99,16 @@ tq_status tq_make_codebook(int32_t d, int32_t bits, float *centroids, float *bou
 /* Same computation, returning the fp64 Lloyd-Max centroids and boundaries before the
  * fp16 rounding (for checking the iteration itself). */
 tq_status tq_make_codebook_f64(int32_t d, int32_t bits, double *centroids, double *bounds);
+
+/* PolarQuant angle grid of one level in fp64.  Level 1 (an angle atan2(y_{2i+1}, y_{2i})
+ * in [0, 2 pi), uniform for a rotated vector): 16 equal cells, centroids (k + 1/2) pi / 8,
+ * boundaries k pi / 8.  Level l >= 2 (atan2(r_{2i+1}, r_{2i}) of two radii of the level
+ * below, in [0, pi/2], with sin^2 psi ~ Beta(m/2, m/2), m = 2^(l-1), density proportional
+ * to sin^(m-1)(2 psi)): the 4-cell Lloyd-Max grid, iterated in fp64 with composite
+ * Gauss-Legendre cell integrals to a change below 1e-13.  centroids: 16 or 4 values,
+ * bounds: 15 or 3, ascending.  The codec table stores each centroid's cos and sin in fp32
+ * and the boundaries in fp64 for the levels of d.  Host only. */
+tq_status tq_make_polar_grid(int32_t level, double *centroids, double *bounds);
 
 /* Size in bytes of the codec table built by tq_codec_build (0 if the desc is invalid). */
 size_t tq_codec_bytes(const tq_codec_desc *desc);
@@ -119,6 +136,10 @@ tq_status tq_codec_build(const tq_codec_desc *desc, void *host_out, size_t bytes
  *           coordinate, token i's value code in bits [bits_v i, bits_v (i+1)) of a
  *           little-endian integer.
  *   Vnorm   [batch][kv_heads][capacity] fp16 ||y||.
+ *   PolarQuant caches: a Kbits record is the 3 d / 8 bytes of angle codes (level-1 code i
+ *           in bits [4 i, 4 i + 4), then levels 2, 3, ... in order, 2 bits per code, from
+ *           bit 2 d; 2 zero bits last) followed by the m QJL sign bits; Vcodes holds token
+ *           records of the same 3 d / 8 angle bytes, [batch][kv_heads][capacity].
  *   NSN caches: Knorm records are {fp16 ||y||, fp16 ||r||, fp16 s1, 0} (8 bytes), Vnorm
  *           records {fp16 ||y||, fp16 s1} (4 bytes), and a last region holds per unit
  *           [o_K, o_V, Pi o_K, Pi o_V], fp32 [d] each (the keys' mean taken after RoPE).

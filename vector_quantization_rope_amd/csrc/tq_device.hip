@@ -96,6 +96,8 @@ __device__ __forceinline__ void fwht_regs(T *x) {
 struct CodecPtrs {
   const float *ck, *tk, *cv, *tv, *D, *S, *ST;
   const __bf16 *Sb[3];   // S split exactly into three bf16 parts, each [m][d]
+  const float *pcs;      // PolarQuant: cos, sin of each angle centroid, [level - 1][16][2]
+  const double *pt;      // PolarQuant: angle boundaries, [level - 1][16]
   int block;
   float qjl_scale, inv_sqrt_block;
 };
@@ -112,6 +114,8 @@ CodecPtrs codec_ptrs(const void *codec_dev, int d, int bits_k, int bits_v, int m
   p.S = reinterpret_cast<const float *>(b + L.S);
   p.ST = reinterpret_cast<const float *>(b + L.ST);
   for (int i = 0; i < 3; ++i) p.Sb[i] = reinterpret_cast<const __bf16 *>(b + L.Sb[i]);
+  p.pcs = reinterpret_cast<const float *>(b + L.pcs);
+  p.pt = reinterpret_cast<const double *>(b + L.pt);
   p.block = L.block;
   p.qjl_scale = m > 0 ? float(std::sqrt(M_PI / 2.0) / m) : 0.0f;
   p.inv_sqrt_block = float(1.0 / std::sqrt(double(L.block)));
@@ -164,6 +168,7 @@ __global__ void k_cache_init(uint32_t *hdr, tq_cache_desc c) {
     case 9: v = uint32_t(c.bits_v); break;
     case 10: v = uint32_t(c.m); break;
     case 11: v = uint32_t(c.nsn); break;
+    case 12: v = uint32_t(c.polar); break;
     default: v = 0;
   }
   hdr[i] = v;
@@ -336,6 +341,178 @@ __device__ __forceinline__ void store_plane(uint32_t hA, uint32_t hB, int q, uin
   }
 }
 
+// ------------------------------------------------------------------ PolarQuant encode
+// Code of a level-1 angle psi = atan2(b, a) in [0, 2 pi) (signed zeros taken as +0): the
+// number of boundaries k pi / 8 (k = 1..15) at or below psi.
+__device__ __forceinline__ int polar_code1(double a, double b) {
+  double psi = atan2(b + 0.0, a + 0.0);
+  if (psi < 0.0) psi += 2.0 * M_PI;
+  constexpr double w = 2.0 * M_PI / 16.0;
+  int c = min(int(psi / w), 15);
+  if (c < 15 && psi >= double(c + 1) * w) ++c;
+  if (c > 0 && psi < double(c) * w) --c;
+  return c;
+}
+
+// Code of a higher-level angle psi = atan2(r1, r0) in [0, pi/2] against the level's three
+// fp64 boundaries.
+__device__ __forceinline__ int polar_codeh(double r0, double r1, const double *t) {
+  const double psi = atan2(r1, r0);
+  return int(psi >= t[0]) + int(psi >= t[1]) + int(psi >= t[2]);
+}
+
+__device__ __forceinline__ double hyp(double a, double b) { return sqrt(fma(a, a, b * b)); }
+
+// The in-chunk levels of HC consecutive coordinates (a power of two): codes stored level
+// by level, level 1 first (HC/2 codes), the chunk's top level last (one code at HC - 2);
+// returns the chunk's radius.
+template <int HC>
+__device__ __forceinline__ double polar_encode_chunk(const double *x, const double *pt, int *cc) {
+  double r[HC / 2];
+#pragma unroll
+  for (int i = 0; i < HC / 2; ++i) {
+    cc[i] = polar_code1(x[2 * i], x[2 * i + 1]);
+    r[i] = hyp(x[2 * i], x[2 * i + 1]);
+  }
+#pragma unroll
+  for (int lv = 2; (1 << lv) <= HC; ++lv) {
+    const int n = HC >> lv, base = HC - 2 * n;
+#pragma unroll
+    for (int i = 0; i < n; ++i) {
+      cc[base + i] = polar_codeh(r[2 * i], r[2 * i + 1], pt + (lv - 1) * kPolarCodes);
+      r[i] = hyp(r[2 * i], r[2 * i + 1]);
+    }
+  }
+  return r[0];
+}
+
+// Reconstruction of a chunk from its radius R and codes, top level down, each radius split
+// by the stored fp32 cos and sin of its angle's centroid.
+template <int HC>
+__device__ __forceinline__ void polar_decode_chunk(double R, const int *cc, const float *pcs, double *y) {
+  constexpr int LIN = HC == 16 ? 4 : HC == 8 ? 3 : HC == 4 ? 2 : 1;   // log2 HC
+  double r[HC / 2];
+  r[0] = R;
+#pragma unroll
+  for (int lv = 0; (1 << lv) < HC / 2; ++lv) {
+    // level LIN - lv has 2^lv codes at HC - 2^(lv+1)
+    const int n = 1 << lv, base = HC - 2 * n, lvl = LIN - lv;
+#pragma unroll
+    for (int i = n - 1; i >= 0; --i) {
+      const float *cs = pcs + ((lvl - 1) * kPolarCodes + cc[base + i]) * 2;
+      const double rr = r[i];
+      r[2 * i] = rr * double(cs[0]);
+      r[2 * i + 1] = rr * double(cs[1]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < HC / 2; ++i) {
+    const float *cs = pcs + cc[i] * 2;
+    y[2 * i] = r[i] * double(cs[0]);
+    y[2 * i + 1] = r[i] * double(cs[1]);
+  }
+}
+
+// OR a bit field into the record words (fields never straddle a dword).
+template <int NW>
+__device__ __forceinline__ void put_bits(uint32_t (&w)[NW], int bit, uint32_t val) {
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    if ((bit >> 5) == i) w[i] |= val << (bit & 31);
+}
+
+// PolarQuant encode of one token spread over a lane group (x as in fwht_group4, in
+// H-units: lane q holds chunk A, coordinates HC q .. + HC, and chunk B, D/2 + HC q .. + HC).
+// In-chunk levels in registers; the next level pairs the chunks of lanes q, q ^ 1 (codes on
+// even lanes), the next those of lanes 0 and 2, the last the two halves (lane 0).  Every
+// lane ends with the whole record (3 D / 32 dwords); lane 0's *nh is the norm in H-units.
+// With recon, x becomes the reconstruction error x - yhat, yhat built from the fp16 norm.
+template <int D>
+__device__ __forceinline__ void polar_encode_group(double *x, int q, const CodecPtrs &cp, uint32_t (&w)[3 * D / 32],
+                                                   double *nh, bool recon, double sqrt_b, double inv_sqrt_b,
+                                                   uint16_t *n16b, bool *over) {
+  constexpr int HC = D / 8, L1 = (HC == 16 ? 4 : 3);   // in-chunk levels
+  constexpr int LC1 = L1 + 1, LC2 = L1 + 2, LT = L1 + 3;
+  static_assert(HC == 8 || HC == 16, "d = 64 or 128");
+  const double *pt = cp.pt;
+  int ccA[HC - 1], ccB[HC - 1];
+  const double RA = polar_encode_chunk<HC>(x, pt, ccA), RB = polar_encode_chunk<HC>(x + HC, pt, ccB);
+  // chunk pairs (q, q ^ 1): the even lane's chunk is the lower one
+  const double RA1 = dpp_f64<kDppXor1>(RA), RB1 = dpp_f64<kDppXor1>(RB);
+  const int cA1 = polar_codeh(RA, RA1, pt + (LC1 - 1) * kPolarCodes);
+  const int cB1 = polar_codeh(RB, RB1, pt + (LC1 - 1) * kPolarCodes);
+  const double RA2 = hyp(RA, RA1), RB2 = hyp(RB, RB1);
+  // block pairs (lanes 0 and 2), then the halves (lane 0)
+  const double RA2p = dpp_f64<kDppXor2>(RA2), RB2p = dpp_f64<kDppXor2>(RB2);
+  const int cA2 = polar_codeh(RA2, RA2p, pt + (LC2 - 1) * kPolarCodes);
+  const int cB2 = polar_codeh(RB2, RB2p, pt + (LC2 - 1) * kPolarCodes);
+  const double RA3 = hyp(RA2, RA2p), RB3 = hyp(RB2, RB2p);
+  const int cT = polar_codeh(RA3, RB3, pt + (LT - 1) * kPolarCodes);
+  *nh = hyp(RA3, RB3);
+  bool ov = false;
+  *n16b = f64_to_f16_sat(*nh * inv_sqrt_b, &ov);
+  if (q == 0) *over |= ov;
+  // record words: level-1 nibbles, then each level's 2-bit codes from bit 2 D
+#pragma unroll
+  for (int i = 0; i < 3 * D / 32; ++i) w[i] = 0u;
+  auto lvl_bit = [](int lv, int j) { return 2 * D + 2 * (D / 2 - (D >> (lv - 1)) + j); };
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int *cc = c ? ccB : ccA;
+    const int start = c * (D / 2) + HC * q;   // first coordinate of the chunk
+    uint32_t nib = 0u;
+#pragma unroll
+    for (int i = 0; i < HC / 2; ++i) nib |= uint32_t(cc[i]) << (4 * i);
+    put_bits(w, 2 * start, nib);   // code of pair start / 2 + i at bit 4 (start / 2 + i)
+#pragma unroll
+    for (int lv = 2; (1 << lv) <= HC; ++lv) {
+      const int n = HC >> lv, base = HC - 2 * n;
+      uint32_t f = 0u;
+#pragma unroll
+      for (int i = 0; i < n; ++i) f |= uint32_t(cc[base + i]) << (2 * i);
+      put_bits(w, lvl_bit(lv, start >> lv), f);
+    }
+  }
+  if ((q & 1) == 0) {
+    put_bits(w, lvl_bit(LC1, (HC * q) >> LC1), uint32_t(cA1));
+    put_bits(w, lvl_bit(LC1, (D / 2 + HC * q) >> LC1), uint32_t(cB1));
+  }
+  if (q == 0) {
+    put_bits(w, lvl_bit(LC2, 0), uint32_t(cA2));
+    put_bits(w, lvl_bit(LC2, 1), uint32_t(cB2));
+    put_bits(w, lvl_bit(LT, 0), uint32_t(cT));
+  }
+#pragma unroll
+  for (int i = 0; i < 3 * D / 32; ++i) {
+    w[i] |= dpp_u32<kDppXor1>(w[i]);
+    w[i] |= dpp_u32<kDppXor2>(w[i]);
+  }
+  if (!recon) return;
+  // reconstruction from the fp16 norm, top down: lane 0 splits the halves and the blocks,
+  // lane 2 takes its block radius from lane 0, odd lanes their chunk radius from the even
+  const float *pcs = cp.pcs;
+  const double nb = double(f16_bits_to_float(*n16b)) * sqrt_b;
+  const float *cst = pcs + ((LT - 1) * kPolarCodes + cT) * 2;
+  const double hA = nb * double(cst[0]), hB = nb * double(cst[1]);
+  const float *csa = pcs + ((LC2 - 1) * kPolarCodes + cA2) * 2, *csb = pcs + ((LC2 - 1) * kPolarCodes + cB2) * 2;
+  const double bA0 = hA * double(csa[0]), bA2 = hA * double(csa[1]);
+  const double bB0 = hB * double(csb[0]), bB2 = hB * double(csb[1]);
+  const double tA2 = dpp_f64<kDppXor2>(bA2), tB2 = dpp_f64<kDppXor2>(bB2);
+  const double rA = q == 0 ? bA0 : tA2, rB = q == 0 ? bB0 : tB2;   // meaningful on lanes 0, 2
+  const float *c1a = pcs + ((LC1 - 1) * kPolarCodes + cA1) * 2, *c1b = pcs + ((LC1 - 1) * kPolarCodes + cB1) * 2;
+  const double oA = rA * double(c1a[0]), pA = rA * double(c1a[1]);
+  const double oB = rB * double(c1b[0]), pB = rB * double(c1b[1]);
+  const double qA = dpp_f64<kDppXor1>(pA), qB = dpp_f64<kDppXor1>(pB);
+  const double RAh = (q & 1) ? qA : oA, RBh = (q & 1) ? qB : oB;
+  double y[HC];
+  polar_decode_chunk<HC>(RAh, ccA, pcs, y);
+#pragma unroll
+  for (int e = 0; e < HC; ++e) x[e] -= y[e];
+  polar_decode_chunk<HC>(RBh, ccB, pcs, y);
+#pragma unroll
+  for (int e = 0; e < HC; ++e) x[HC + e] -= y[e];
+}
+
 // NSN shift ([NSNQuant] section 1) of one token spread over a lane group as in
 // fwht_group4 (x in H-units, sqrt(B) times the rotated coordinates): s1 = ||y|| / sqrt(d)
 // is rounded to fp16, then y -= s1 (Pi o) with the unit's stored fp32 Pi o.  The codec's
@@ -366,7 +543,7 @@ __device__ __forceinline__ void nsn_shift(double *x, int q, const float *po, dou
 // KK / KV: number of key / value codes when known at compile time (0: from the
 // descriptor, a slower loop).  Codes compare the unnormalised coordinate y_j with
 // ||y|| * t_k, which is u_j >= t_k up to one rounding.
-template <int D, int DT, int KK, int KV>
+template <int D, int DT, int KK, int KV, bool POLAR = false>
 __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   constexpr int H = D / 2;
   constexpr int HC = D / 8;     // coordinates per chunk
@@ -450,7 +627,21 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   fwht_group4<D>(x, q);
   uint16_t ks1b = 0;
   if (a.ch.nsn) nsn_shift<D>(x, q, a.ch.nsn + size_t(unit) * 4 * D + 2 * D, sqrt_b, inv_sqrt_b, &ks1b, &over);
-  {
+  if constexpr (POLAR) {
+    // PolarQuant: angle codes of the rotated key, the reconstruction error left in x
+    uint32_t w[3 * D / 32];
+    double nh;
+    uint16_t n16b;
+    polar_encode_group<D>(x, q, a.cp, w, &nh, true, sqrt_b, inv_sqrt_b, &n16b, &over);
+#pragma unroll
+    for (int i = 0; i < 3 * D / 32; ++i)
+      if ((i & 3) == q && valid) rec[i] = w[i];
+    double rr = 0.0;
+#pragma unroll
+    for (int e = 0; e < C; ++e) rr = fma(x[e], x[e], rr);
+    const uint16_t rn16b = f64_to_f16_sat(sqrt(group4_sum(rr)) * inv_sqrt_b, &over);
+    if (valid && q == 0) a.ch.knorm[size_t(unit) * a.capacity + p] = uint32_t(n16b) | (uint32_t(rn16b) << 16);
+  } else {
     double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < C; ++e) ss = fma(x[e], x[e], ss);
@@ -543,7 +734,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
       else
         a.ch.knorm[size_t(unit) * a.capacity + p] = nw;
     }
-  }
+  }   // scalar codes
   __syncthreads();   // every wave is done with the RoPE table before residuals overwrite it
   {
     // residual r_H = H D x' - fp16(n) sqrt(B) c = sqrt(B) r (same signs of S r), rounded
@@ -584,6 +775,19 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
     fwht_group4<D>(x, q);
     uint16_t vs1b = 0;
     if (a.ch.nsn) nsn_shift<D>(x, q, a.ch.nsn + size_t(unit) * 4 * D + 3 * D, sqrt_b, inv_sqrt_b, &vs1b, &over);
+    if constexpr (POLAR) {
+      // PolarQuant values: token records of 3 D / 8 bytes in the value region
+      uint32_t w[3 * D / 32];
+      double nh;
+      uint16_t n16b;
+      polar_encode_group<D>(x, q, a.cp, w, &nh, false, sqrt_b, inv_sqrt_b, &n16b, &over);
+      uint32_t *vrec = reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(a.ch.vcodes) +
+                                                    (size_t(unit) * a.capacity + (valid ? p : 0)) * (3 * D / 8));
+#pragma unroll
+      for (int i = 0; i < 3 * D / 32; ++i)
+        if ((i & 3) == q && valid) vrec[i] = w[i];
+      if (valid && q == 0) a.ch.vnorm[size_t(unit) * a.capacity + p] = n16b;
+    } else {
     double ss = 0.0;
 #pragma unroll
     for (int e = 0; e < C; ++e) ss = fma(x[e], x[e], ss);
@@ -634,6 +838,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
       else
         a.ch.vnorm[size_t(unit) * a.capacity + p] = n16b;
     }
+    }   // scalar codes
   }
   __syncthreads();
 
@@ -702,7 +907,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   }
 
   // ------------------------------------------------------------ value tiles
-  if (a.bits_v > 0) {
+  if (!POLAR && a.bits_v > 0) {
     // one (tile, coordinate) word group per thread; tokens outside the written range
     // keep their previous bits
     const int bv = a.bits_v;
@@ -2440,6 +2645,277 @@ __global__ __launch_bounds__(256) void k_window(WindowArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ PolarQuant decode
+// Split-K decode over PolarQuant records ([TurboQuant] "PolarQuant" as stage 1, QJL on
+// the key residual).  Per 64-token chunk of the block's range: the records come in with
+// 16-byte loads (the next chunk's in flight while this one is scored) and are staged in
+// LDS; four threads per token decode its angle tree, one quarter of the coordinates each
+// (the two top levels give the quarter's radius, its own subtree the rest), into fp32
+// rows of the rotated key direction and of the rotated value times its norm; the key
+// score is n <q_rot, yhat> plus the QJL term, whose sign-bit sum comes from a per-head
+// table over nibbles; then the online softmax and value sums of the window kernel.  The
+// sums stay in the rotated basis: the partials are the merge's usual input.
+struct PolarArgs {
+  const uint8_t *krec;     // [units][capacity][kb]: 3 D / 8 angle bytes, m / 8 sign bytes
+  const uint32_t *knorm;   // {fp16 n, fp16 |r|}
+  const uint8_t *vrec;     // [units][capacity][3 D / 8]
+  const uint16_t *vnorm;
+  const float *qp;         // query rows: Pi RoPE(q) [D], S q [m], sum q_rot, sum S q
+  const float *pcs;        // cos, sin of the angle centroids [level - 1][16][2]
+  float *part, *scores;
+  int kb, capacity, length, chunk, splits, kv_heads, q_heads, G, m, qstride, score_stride;
+  float scale_log2, qjl_scale;
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void k_decode_polar(PolarArgs a) {
+  constexpr int L = D == 128 ? 7 : 6, CH = 64, RS = D + 1, GM = 8, MMAX = 128;
+  constexpr int VB = 3 * D / 8;                 // value record bytes
+  constexpr int HS = 256 / D, HPT = GM / HS;    // value phase: head slots per thread
+  constexpr int NQ = D / 4;                     // coordinates per decode quarter
+  __shared__ __align__(16) float qr[GM][D];
+  __shared__ float kr[CH * RS];
+  __shared__ float vr[CH * RS];
+  __shared__ __align__(16) float ps[GM][CH];
+  __shared__ float nib[GM][MMAX / 4][16];      // sum of S q over the set bits of a nibble
+  __shared__ float s1q[GM];                    // sum of S q
+  __shared__ float mstat[3][GM];
+  __shared__ float cs_s[L][16][2];
+  constexpr int KWMAX = (3 * D / 8 + MMAX / 8) / 4;   // key record dwords at most
+  constexpr int NKD = (CH * KWMAX + 255) / 256, NVD = (CH * VB / 4 + 255) / 256;
+  __shared__ uint32_t krs[CH * KWMAX];           // the chunk's key records, kw dwords each
+  __shared__ uint32_t vrs[CH * (VB / 4)];
+  __shared__ uint32_t kns[CH];
+  __shared__ float vns[CH];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int unit = blockIdx.x, split = blockIdx.y;
+  const int b = unit / a.kv_heads, g = unit % a.kv_heads, G = a.G, hq0 = g * G;
+  const int t_begin = split * a.chunk, t_end = min(a.length, t_begin + a.chunk);
+  const size_t ubase = size_t(unit) * a.capacity;
+  const int kw = a.kb / 4;                      // key record dwords
+  // one chunk's records as dwords (records are whole dwords, so each load stays inside
+  // the chunk's valid tokens), the next chunk's in registers while this one is scored
+  uint32_t kreg[NKD], vreg[NVD];
+  uint32_t knr = 0u;
+  float vnr = 0.0f;
+  auto fetch = [&](int c0) {
+    const int cn = min(CH, t_end - c0);
+    const uint32_t *ks = reinterpret_cast<const uint32_t *>(a.krec + (ubase + c0) * a.kb);
+    const uint32_t *vs = reinterpret_cast<const uint32_t *>(a.vrec + (ubase + c0) * VB);
+#pragma unroll
+    for (int i = 0; i < NKD; ++i) {
+      const int k = tid + 256 * i;
+      kreg[i] = k < cn * kw ? ks[k] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < NVD; ++i) {
+      const int k = tid + 256 * i;
+      vreg[i] = k < cn * (VB / 4) ? vs[k] : 0u;
+    }
+    if (tid < cn) {
+      knr = a.knorm[ubase + c0 + tid];
+      vnr = f16_bits_to_float(a.vnorm[ubase + c0 + tid]);
+    }
+  };
+  if (t_begin < t_end) fetch(t_begin);
+  for (int i = tid; i < L * 32; i += 256) (&cs_s[0][0][0])[i] = a.pcs[i];
+  for (int i = tid; i < GM * D; i += 256) {
+    const int h = i / D, j = i % D;
+    qr[h][j] = h < G ? a.qp[size_t(b * a.q_heads + hq0 + h) * a.qstride + j] : 0.0f;
+  }
+  for (int i = tid; i < GM * (MMAX / 4) * 16; i += 256) {
+    const int h = i / (MMAX / 4 * 16), k = (i / 16) % (MMAX / 4), v = i % 16;
+    float acc = 0.0f;
+    if (h < G && 4 * k < a.m) {
+      const float *sq = a.qp + size_t(b * a.q_heads + hq0 + h) * a.qstride + D;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if ((v >> e) & 1) acc += sq[4 * k + e];
+    }
+    nib[h][k][v] = acc;
+  }
+  if (tid < GM) {
+    s1q[tid] = tid < G ? a.qp[size_t(b * a.q_heads + hq0 + tid) * a.qstride + D + a.m + 1] : 0.0f;
+    mstat[0][tid] = -INFINITY;
+    mstat[1][tid] = 0.0f;
+    mstat[2][tid] = 0.0f;
+  }
+  for (int i = tid; i < GM * CH; i += 256) (&ps[0][0])[i] = 0.0f;
+  const int jv = tid % D, hs = tid / D;
+  float acc[HPT];
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) acc[k] = 0.0f;
+  // decode role: token tt, quarter qq
+  const int tt = tid >> 2, qq = tid & 3;
+  for (int c0 = t_begin; c0 < t_end; c0 += CH) {
+    const int cn = min(CH, t_end - c0);
+    __syncthreads();   // the previous chunk's readers are done
+#pragma unroll
+    for (int i = 0; i < NKD; ++i)
+      if (tid + 256 * i < CH * kw) krs[tid + 256 * i] = kreg[i];
+#pragma unroll
+    for (int i = 0; i < NVD; ++i)
+      if (tid + 256 * i < CH * (VB / 4)) vrs[tid + 256 * i] = vreg[i];
+    if (tid < CH) {
+      kns[tid] = tid < cn ? knr : 0u;
+      vns[tid] = tid < cn ? vnr : 0.0f;
+    }
+    if (c0 + CH < t_end) fetch(c0 + CH);
+    __syncthreads();
+    // ---- decode: quarter qq of token tt (rows past the chunk's end become zero)
+    {
+      const uint32_t *kwd = &krs[tt * kw];
+      const uint32_t *vwd = &vrs[tt * (VB / 4)];
+      const bool live = tt < cn;
+      auto field = [&](const uint32_t *w, int bit, int width) {
+        return (w[bit >> 5] >> (bit & 31)) & ((1u << width) - 1u);
+      };
+      auto lbit = [](int lv, int j) { return 2 * D + 2 * (D / 2 - (D >> (lv - 1)) + j); };
+#pragma unroll
+      for (int kv = 0; kv < 2; ++kv) {
+        const uint32_t *w = kv ? vwd : kwd;
+        float *row = (kv ? vr : kr) + tt * RS + qq * NQ;
+        const float scale = kv ? vns[tt] : 1.0f;
+        // quarter radius from the two top levels
+        const int cT = int(field(w, lbit(L, 0), 2)), cH = int(field(w, lbit(L - 1, qq >> 1), 2));
+        float r[NQ / 2];
+        r[0] = scale * cs_s[L - 1][cT][qq >> 1] * cs_s[L - 2][cH][qq & 1];
+#pragma unroll
+        for (int lv = L - 2, n = 1; lv >= 2; --lv, n <<= 1) {
+          // level lv: n codes inside the quarter, from index qq n
+#pragma unroll
+          for (int i = n - 1; i >= 0; --i) {
+            const int c = int(field(w, lbit(lv, qq * n + i), 2));
+            const float rr = r[i];
+            r[2 * i] = rr * cs_s[lv - 1][c][0];
+            r[2 * i + 1] = rr * cs_s[lv - 1][c][1];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NQ / 2; ++i) {
+          const int c = int(field(w, 4 * (qq * (NQ / 2) + i), 4));
+          row[2 * i] = live ? r[i] * cs_s[0][c][0] : 0.0f;
+          row[2 * i + 1] = live ? r[i] * cs_s[0][c][1] : 0.0f;
+        }
+      }
+    }
+    __syncthreads();
+    // ---- scores: token = lane, heads h0 and h0 + 4
+    {
+      const int t = lane;
+      const float *krow = &kr[t * RS];
+      const uint32_t nrm = kns[t];
+      const float n16 = f16_bits_to_float(nrm & 0xFFFFu), rn16 = f16_bits_to_float(nrm >> 16);
+      const uint32_t *sg = &krs[t * kw + 3 * D / 32];   // sign bits
+      for (int h0 = wv; h0 < G; h0 += 8) {
+        const int h1 = h0 + 4;
+        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll 8
+        for (int j = 0; j < D; j += 4) {
+          const float4 qa = *reinterpret_cast<const float4 *>(&qr[h0][j]);
+          const float4 qb = *reinterpret_cast<const float4 *>(&qr[h1 < GM ? h1 : h0][j]);
+          const float k0 = krow[j], k1 = krow[j + 1], k2 = krow[j + 2], k3 = krow[j + 3];
+          s0 = fmaf(qa.x, k0, s0);
+          s1 = fmaf(qa.y, k1, s1);
+          s0 = fmaf(qa.z, k2, s0);
+          s1 = fmaf(qa.w, k3, s1);
+          s2 = fmaf(qb.x, k0, s2);
+          s3 = fmaf(qb.y, k1, s3);
+          s2 = fmaf(qb.z, k2, s2);
+          s3 = fmaf(qb.w, k3, s3);
+        }
+        float b0 = 0.0f, b1 = 0.0f;
+        for (int k = 0; k < a.m / 4; ++k) {
+          const uint32_t v = (sg[k >> 3] >> (4 * (k & 7))) & 15u;
+          b0 += nib[h0][k][v];
+          if (h1 < G) b1 += nib[h1][k][v];
+        }
+        ps[h0][t] = fmaf(n16, s0 + s1, a.qjl_scale * rn16 * fmaf(2.0f, b0, -s1q[h0]));
+        if (h1 < G) ps[h1][t] = fmaf(n16, s2 + s3, a.qjl_scale * rn16 * fmaf(2.0f, b1, -s1q[h1]));
+      }
+    }
+    __syncthreads();
+    // ---- online softmax, one lane per token, heads h0 and h0 + 4 side by side
+    for (int h0 = wv; h0 < G; h0 += 8) {
+      const int h1 = h0 + 4;
+      const bool two = h1 < G;
+      const float x0 = ps[h0][lane], x1 = ps[h1 < GM ? h1 : h0][lane];
+      if (a.scores && lane < cn) {
+        float *srow = a.scores + (size_t(b) * a.q_heads + hq0) * a.score_stride + c0 + lane;
+        srow[size_t(h0) * a.score_stride] = x0;
+        if (two) srow[size_t(h1) * a.score_stride] = x1;
+      }
+      const float v0 = lane < cn ? x0 * a.scale_log2 : -INFINITY;
+      const float v1 = lane < cn ? x1 * a.scale_log2 : -INFINITY;
+      float m0 = v0, m1 = v1;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        m0 = fmaxf(m0, __shfl_xor(m0, o, 64));
+        m1 = fmaxf(m1, __shfl_xor(m1, o, 64));
+      }
+      const float mold0 = mstat[0][h0], mnew0 = fmaxf(mold0, m0);
+      const float mold1 = two ? mstat[0][h1] : -INFINITY, mnew1 = fmaxf(mold1, m1);
+      const float al0 = mold0 == -INFINITY ? 0.0f : exp2f(mold0 - mnew0);
+      const float al1 = mold1 == -INFINITY ? 0.0f : exp2f(mold1 - mnew1);
+      const float p0 = lane < cn ? exp2f(v0 - mnew0) : 0.0f;
+      const float p1 = lane < cn ? exp2f(v1 - mnew1) : 0.0f;
+      float l0 = p0, l1 = p1;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        l0 += __shfl_xor(l0, o, 64);
+        l1 += __shfl_xor(l1, o, 64);
+      }
+      ps[h0][lane] = p0;
+      if (two) ps[h1][lane] = p1;
+      if (lane == 0) {
+        mstat[0][h0] = mnew0;
+        mstat[1][h0] = mstat[1][h0] * al0 + l0;
+        mstat[2][h0] = al0;
+        if (two) {
+          mstat[0][h1] = mnew1;
+          mstat[1][h1] = mstat[1][h1] * al1 + l1;
+          mstat[2][h1] = al1;
+        }
+      }
+    }
+    __syncthreads();
+    // ---- values: one read of vr per token serves all of this thread's head slots
+    {
+      float o[HPT];
+#pragma unroll
+      for (int k = 0; k < HPT; ++k) o[k] = acc[k] * mstat[2][hs + k * HS];
+#pragma unroll 4
+      for (int t = 0; t < CH; t += 4) {
+        const float v0 = vr[t * RS + jv], v1 = vr[(t + 1) * RS + jv];
+        const float v2 = vr[(t + 2) * RS + jv], v3 = vr[(t + 3) * RS + jv];
+#pragma unroll
+        for (int k = 0; k < HPT; ++k) {
+          const float4 p = *reinterpret_cast<const float4 *>(&ps[hs + k * HS][t]);
+          o[k] = fmaf(p.x, v0, o[k]);
+          o[k] = fmaf(p.y, v1, o[k]);
+          o[k] = fmaf(p.z, v2, o[k]);
+          o[k] = fmaf(p.w, v3, o[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < HPT; ++k) acc[k] = o[k];
+    }
+  }
+  // partial (rotated basis): acc, max (natural log), sum
+#pragma unroll
+  for (int k = 0; k < HPT; ++k) {
+    const int h = hs + k * HS;
+    if (h < G) {
+      float *o = a.part + ((size_t(b) * a.q_heads + hq0 + h) * a.splits + split) * (D + 2);
+      o[jv] = acc[k];
+      if (jv == 0) {
+        o[D] = mstat[0][h] == -INFINITY ? -INFINITY : mstat[0][h] * 0.69314718055994531f;
+        o[D + 1] = mstat[1][h];
+      }
+    }
+  }
+}
+
 // Merge of the splits and inverse rotation: out = D .* (H o) / sqrt(B) = Pi^T o.
 // One block per (batch, q-head) row; split maxima and sums go through LDS first.
 __global__ __launch_bounds__(256) void k_decode_merge(const float *part, int splits, int d,
@@ -3171,8 +3647,8 @@ bool decode_supported(const tq_cache_desc &c) {
 
 // The MFMA path covers the 2-bit + QJL (m = d) keys, 3-bit values configuration.
 bool decode_mfma_path(const tq_cache_desc &c, int q_heads) {
-  return (c.d == 64 || c.d == 128) && c.bits_k >= 1 && c.bits_k <= 3 && c.bits_v == 3 && c.m == c.d &&
-         q_heads / c.kv_heads <= kMfmaMaxG;
+  return !c.polar && (c.d == 64 || c.d == 128) && c.bits_k >= 1 && c.bits_k <= 3 && c.bits_v == 3 &&
+         c.m == c.d && q_heads / c.kv_heads <= kMfmaMaxG;
 }
 
 constexpr int kMfmaChunk = 32 * kDecWaves;   // tokens per block iteration (one tile per wave)
@@ -3299,7 +3775,8 @@ tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_d
     const bool k2v3 = desc->bits_k == 2 && desc->bits_v == 3;
 #define TQ_QKV(DD, TT)                                                                              \
   do {                                                                                              \
-    if (k2v3) hipLaunchKernelGGL((k_quantize_kv<DD, TT, 4, 8>), grid, dim3(256), 0, s, a);          \
+    if (desc->polar) hipLaunchKernelGGL((k_quantize_kv<DD, TT, 0, 0, true>), grid, dim3(256), 0, s, a); \
+    else if (k2v3) hipLaunchKernelGGL((k_quantize_kv<DD, TT, 4, 8>), grid, dim3(256), 0, s, a);     \
     else hipLaunchKernelGGL((k_quantize_kv<DD, TT, 0, 0>), grid, dim3(256), 0, s, a);               \
   } while (0)
     if (d == 64) {
@@ -3416,8 +3893,10 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
   }
   const CodecPtrs cp = codec_ptrs(codec_dev, d, desc->bits_k, desc->bits_v, m);
   if (win && cp.block != d) return TQ_EUNSUPPORTED;   // the window rotates with one d-point block
-  // NSN caches decode on the MFMA path only (its kernels carry the mean terms)
+  // NSN caches decode on the MFMA path only (its kernels carry the mean terms); PolarQuant
+  // caches on their own kernel (8 head slots, QJL rows up to 128)
   if (desc->nsn && !decode_mfma_path(*desc, q_heads)) return TQ_EUNSUPPORTED;
+  if (desc->polar && (q_heads / desc->kv_heads > 8 || desc->m > 128)) return TQ_EUNSUPPORTED;
   if (win && win->flush) {
     // the full window becomes packed tokens [length - cap, length) before anything reads them
     if (length < win->cap) return TQ_EINVAL;
@@ -3505,6 +3984,38 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
       launch_mfma<false, false>(d, bk, grid, blk, s, ma);
     if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
     }
+  } else if (desc->polar) {
+    const int pchunk = (((length + S - 1) / S) + 63) / 64 * 64;
+    used_splits = (length + pchunk - 1) / pchunk;
+    PolarArgs pa;
+    pa.krec = ch.kbits;
+    pa.knorm = ch.knorm;
+    pa.vrec = reinterpret_cast<const uint8_t *>(ch.vcodes);
+    pa.vnorm = ch.vnorm;
+    pa.qp = qp;
+    pa.pcs = cp.pcs;
+    pa.part = part;
+    pa.scores = scores;
+    pa.kb = ch.kbytes;
+    pa.capacity = desc->capacity;
+    pa.length = length;
+    pa.chunk = pchunk;
+    pa.splits = used_splits + wsplit;
+    pa.kv_heads = desc->kv_heads;
+    pa.q_heads = q_heads;
+    pa.G = G;
+    pa.m = m;
+    pa.qstride = qstride;
+    pa.score_stride = score_stride;
+    pa.scale_log2 = sc * 1.4426950408889634f;
+    pa.qjl_scale = cp.qjl_scale;
+    const dim3 grid(units, used_splits);
+    if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
+    if (d == 64)
+      hipLaunchKernelGGL(k_decode_polar<64>, grid, dim3(256), 0, s, pa);
+    else
+      hipLaunchKernelGGL(k_decode_polar<128>, grid, dim3(256), 0, s, pa);
+    if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
   } else {
     DecodeArgs a;
     a.cp = cp;
@@ -3732,7 +4243,7 @@ tq_status tq_search_topk(const tq_cache_desc *db, const void *codec_dev, const v
                          tq_stream_t stream) {
   if (!db || !codec_dev || !db_cache || !idx_out || !score_out || !ws) return TQ_EINVAL;
   if (!cache_desc_valid(*db)) return TQ_EUNSUPPORTED;
-  if (db->nsn) return TQ_EUNSUPPORTED;   // database vectors use the plain codec
+  if (db->nsn || db->polar) return TQ_EUNSUPPORTED;   // database vectors use the plain codec
   if (db->batch != 1 || db->kv_heads != 1 || db->bits_v != 0) return TQ_EINVAL;
   if (n_db < 0 || nq < 0 || k < 1 || k > 64) return TQ_EINVAL;
   if (n_db > db->capacity) return TQ_ECAPACITY;

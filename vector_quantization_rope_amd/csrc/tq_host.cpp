@@ -24,6 +24,10 @@ bool cache_desc_valid(const tq_cache_desc &c) {
   if (c.batch < 1 || c.kv_heads < 1 || c.capacity < 0) return false;
   if (c.nsn != 0 && c.nsn != 1) return false;
   if (c.nsn && (c.bits_v == 0 || (c.d != 64 && c.d != 128))) return false;
+  if (c.polar != 0 && c.polar != 1) return false;
+  // PolarQuant: 3 d - 2 bits of angles per vector, recorded as bits_k = bits_v = 3
+  if (c.polar && (c.nsn || (c.d != 64 && c.d != 128) || c.bits_k != 3 || (c.bits_v != 0 && c.bits_v != 3)))
+    return false;
   return true;
 }
 
@@ -41,8 +45,9 @@ CacheLayout cache_layout(const tq_cache_desc &c) {
   L.knorm = cur;
   cur = align256(cur + units * size_t(c.capacity) * size_t(L.knrec));
   if (c.bits_v > 0) {
-    L.vcodes = cur;
-    cur = align256(cur + units * size_t(L.tiles) * size_t(c.d) * size_t(4 * c.bits_v));
+    L.vcodes = cur;   // polar: token records of 3 d / 8 bytes instead of tiles
+    cur = align256(cur + (c.polar ? units * size_t(c.capacity) * size_t(3 * c.d / 8)
+                                  : units * size_t(L.tiles) * size_t(c.d) * size_t(4 * c.bits_v)));
     L.vnorm = cur;
     cur = align256(cur + units * size_t(c.capacity) * size_t(L.vnrec));
   }
@@ -72,6 +77,10 @@ CodecLayout codec_layout(int d, int bits_k, int bits_v, int m) {
     L.Sb[i] = cur;
     cur = align256(cur + size_t(m) * size_t(d) * 2);
   }
+  L.pcs = cur;
+  cur = align256(cur + size_t(kPolarLevels) * kPolarCodes * 2 * 4);
+  L.pt = cur;
+  cur = align256(cur + size_t(kPolarLevels) * kPolarCodes * 8);
   L.total = cur;
   return L;
 }
@@ -246,6 +255,28 @@ void lloyd_max(int d, int bits, double *c, double *t) {
 }
 
 // SplitMix64 as a counter generator: output k of the generator seeded with `seed`.
+// PolarQuant angle law of level l >= 2: psi = atan2(|b|, |a|) for independent
+// m-dimensional standard Gaussian a, b (m = 2^(l-1)), density proportional to
+// sin^(m-1)(2 psi) on [0, pi/2].  Cell mass and first moment by composite Gauss-Legendre.
+void polar_cell(int m, double a, double b, double *mass, double *mom) {
+  const GaussLegendre &g = gl20();
+  constexpr int P = 64;
+  double s0 = 0.0, s1 = 0.0;
+  const double h = (b - a) / P;
+  for (int p = 0; p < P; ++p) {
+    const double lo = a + p * h, mid = lo + 0.5 * h;
+    for (size_t i = 0; i < g.x.size(); ++i) {
+      const double x = mid + 0.5 * h * g.x[i];
+      const double s = std::sin(2.0 * x);
+      const double f = s > 0.0 ? std::exp((m - 1) * std::log(s)) : 0.0;
+      s0 += g.w[i] * f;
+      s1 += g.w[i] * f * x;
+    }
+  }
+  *mass = 0.5 * h * s0;
+  *mom = 0.5 * h * s1;
+}
+
 inline uint64_t splitmix64(uint64_t seed, uint64_t k) {
   uint64_t z = seed + (k + 1) * 0x9E3779B97F4A7C15ull;
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
@@ -258,6 +289,34 @@ constexpr uint64_t kStreamGauss = 2ull << 32;
 inline double uniform_open(uint64_t x) { return (double(x >> 11) + 0.5) * 0x1.0p-53; }
 
 }  // namespace
+
+void polar_grid(int level, double *c, double *t) {
+  if (level == 1) {
+    const double w = 2.0 * M_PI / 16.0;
+    for (int k = 0; k < 16; ++k) c[k] = (k + 0.5) * w;
+    for (int k = 1; k < 16; ++k) t[k - 1] = k * w;
+    return;
+  }
+  const int m = 1 << (level - 1), K = 4;
+  for (int k = 0; k < K; ++k) c[k] = 0.5 * M_PI * (k + 0.5) / K;
+  for (int it = 0; it < 1000; ++it) {
+    double edges[K + 1];
+    edges[0] = 0.0;
+    edges[K] = 0.5 * M_PI;
+    for (int k = 1; k < K; ++k) edges[k] = 0.5 * (c[k - 1] + c[k]);
+    double delta = 0.0;
+    for (int k = 0; k < K; ++k) {
+      double mass, mom;
+      polar_cell(m, edges[k], edges[k + 1], &mass, &mom);
+      const double cn = mom / mass;
+      delta = std::max(delta, std::fabs(cn - c[k]));
+      c[k] = cn;
+    }
+    if (delta < 1e-13) break;
+  }
+  for (int k = 1; k < K; ++k) t[k - 1] = 0.5 * (c[k - 1] + c[k]);
+}
+
 }  // namespace tq
 
 using namespace tq;
@@ -359,6 +418,29 @@ tq_status tq_codec_build(const tq_codec_desc *desc, void *host_out, size_t bytes
       }
     }
   }
+  // PolarQuant grids of the levels a vector of dimension d has (d a power of two): the
+  // cos and sin of each centroid rounded to fp32, the boundaries in fp64
+  float *pcs = reinterpret_cast<float *>(base + L.pcs);
+  double *pt = reinterpret_cast<double *>(base + L.pt);
+  if ((d & (d - 1)) == 0) {
+    for (int lv = 1; (1 << lv) <= d && lv <= kPolarLevels; ++lv) {
+      double c[kPolarCodes], t[kPolarCodes];
+      polar_grid(lv, c, t);
+      const int K = lv == 1 ? 16 : 4;
+      for (int k = 0; k < K; ++k) {
+        pcs[((lv - 1) * kPolarCodes + k) * 2] = float(std::cos(c[k]));
+        pcs[((lv - 1) * kPolarCodes + k) * 2 + 1] = float(std::sin(c[k]));
+      }
+      for (int k = 0; k < K - 1; ++k) pt[(lv - 1) * kPolarCodes + k] = t[k];
+    }
+  }
+  return TQ_OK;
+}
+
+tq_status tq_make_polar_grid(int32_t level, double *centroids, double *bounds) {
+  if (!centroids || !bounds) return TQ_EINVAL;
+  if (level < 1 || level > kPolarLevels) return TQ_EUNSUPPORTED;
+  polar_grid(level, centroids, bounds);
   return TQ_OK;
 }
 

@@ -30,10 +30,16 @@ struct CacheLayout {
   int vwords = 0;   // dwords per (tile, coordinate) = bits_v
 };
 
+// PolarQuant angle grids: levels 1..kPolarLevels, up to kPolarCodes cells per level.
+constexpr int kPolarLevels = 11;
+constexpr int kPolarCodes = 16;
+
 struct CodecLayout {
   // byte offsets inside the codec table
   size_t ck = 0, tk = 0, cv = 0, tv = 0, D = 0, S = 0, ST = 0, total = 0;
   size_t Sb[3] = {0, 0, 0};   // S = Sb[0] + Sb[1] + Sb[2] exactly, each part bf16
+  size_t pcs = 0;   // fp32 [kPolarLevels][kPolarCodes][2]: cos, sin of each angle centroid
+  size_t pt = 0;    // fp64 [kPolarLevels][kPolarCodes]: angle boundaries (level l at l - 1)
   int block = 0;
 };
 
@@ -51,8 +57,8 @@ static_assert(sizeof(CodecHeader) == 256, "codec header is 256 bytes");
 
 struct CacheHeader {
   uint32_t magic, version, flags, zero;
-  int32_t batch, kv_heads, d, capacity, bits_k, bits_v, m, nsn;
-  uint32_t reserved[52];
+  int32_t batch, kv_heads, d, capacity, bits_k, bits_v, m, nsn, polar;
+  uint32_t reserved[51];
 };
 static_assert(sizeof(CacheHeader) == 256, "cache header is 256 bytes");
 
@@ -60,6 +66,10 @@ bool codec_desc_valid(const tq_codec_desc &c);
 bool cache_desc_valid(const tq_cache_desc &c);
 CacheLayout cache_layout(const tq_cache_desc &c);
 CodecLayout codec_layout(int d, int bits_k, int bits_v, int m);
+
+// PolarQuant grid of one level in fp64: level 1, 16 centroids and 15 boundaries; level
+// l >= 2, 4 centroids and 3 boundaries.
+void polar_grid(int level, double *c, double *t);
 
 // fp64 -> fp16 (round to nearest even); returns the fp16 value as a double and its bits.
 double round_fp16(double x, uint16_t *bits_out = nullptr);

@@ -31,7 +31,7 @@ EXPORTS = [
     "tq_decode_workspace_bytes_splits", "tq_decode_attend_splits",
     "tq_search_workspace_bytes", "tq_search_topk", "tq_quantize_kv_profiled",
     "tq_decode_attend_profiled", "tq_decode_window_workspace_bytes", "tq_decode_attend_window",
-    "tq_decode_step", "tq_nsn_means_workspace_bytes", "tq_nsn_set_means",
+    "tq_decode_step", "tq_nsn_means_workspace_bytes", "tq_nsn_set_means", "tq_make_polar_grid",
 ]
 
 
@@ -43,7 +43,8 @@ class CodecDesc(ctypes.Structure):
 class CacheDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("d", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("bits_k", ctypes.c_int32),
-                ("bits_v", ctypes.c_int32), ("m", ctypes.c_int32), ("nsn", ctypes.c_int32)]
+                ("bits_v", ctypes.c_int32), ("m", ctypes.c_int32), ("nsn", ctypes.c_int32),
+                ("polar", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -92,6 +93,7 @@ _IP = ctypes.POINTER(ctypes.c_int32)
 _decode_step = _sig("tq_decode_step", ctypes.c_int,
                     [_KD, _P, _P, _IP, _P, _P, ctypes.c_int, _IP, _I, _P, _P, _P, ctypes.c_int, _I, _I, _F, _F,
                      _P, _P, _P, _S, _P])
+_polar_grid = _sig("tq_make_polar_grid", ctypes.c_int, [_I, _P, _P])
 _nsn_ws = _sig("tq_nsn_means_workspace_bytes", _S, [_KD, _I])
 _nsn_set = _sig("tq_nsn_set_means", ctypes.c_int, [_KD, _P, _P, _P, _P, ctypes.c_int, _I, _I, _F, _P, _S, _P])
 _search_ws = _sig("tq_search_workspace_bytes", _S, [_KD, _I, _I, _I])
@@ -272,6 +274,15 @@ def decode_step(desc: CacheDesc, codec_dev, cache, length: int, win_k, win_v, wi
     return int(L.value), int(Wn.value)
 
 
+def make_polar_grid(level: int):
+    """fp64 (centroids, boundaries) of a PolarQuant angle level (host)."""
+    K = 16 if level == 1 else 4
+    c = np.zeros(K, dtype=np.float64)
+    t = np.zeros(K - 1, dtype=np.float64)
+    _check(_polar_grid(int(level), c.ctypes.data, t.ctypes.data), "tq_make_polar_grid")
+    return c, t
+
+
 def nsn_means_workspace_bytes(desc: CacheDesc, n: int) -> int:
     return _nsn_ws(ctypes.byref(desc), n)
 
@@ -319,9 +330,10 @@ class Codec:
 class PackedCache:
     """A packed cache buffer (torch uint8 tensor) plus its descriptor."""
 
-    def __init__(self, batch, kv_heads, d, capacity, bits_k, bits_v, m, device="cuda", stream=None, nsn=0):
+    def __init__(self, batch, kv_heads, d, capacity, bits_k, bits_v, m, device="cuda", stream=None, nsn=0,
+                 polar=0):
         import torch
-        self.desc = CacheDesc(batch, kv_heads, d, capacity, bits_k, bits_v, m, nsn)
+        self.desc = CacheDesc(batch, kv_heads, d, capacity, bits_k, bits_v, m, nsn, polar)
         n = cache_bytes(self.desc)
         if n == 0:
             raise TQError(TQ_EUNSUPPORTED, "tq_cache_bytes")
