@@ -277,6 +277,48 @@ def nsn_bench(tq, w, K, V, q, dev, ev, stream, reps: int = 30):
             "logits_call_us": round(lg_call, 2), "logits_kernel_us": round(lg_kern, 2)}
 
 
+def polar_bench(tq, w, K, V, q, dev, ev, stream, reps: int = 20):
+    """PolarQuant caches (recursive polar angles as stage 1, QJL on the key residual) on the
+    long-context shape, outside the timed steps: the 4096-token append, decode and logits
+    only, medians of back-to-back calls.  The decode kernel decodes every token's angle
+    tree and runs fp32 dot products: it is bound by vector ALU work, not by its bytes."""
+    import torch
+
+    T, A = w.context, w.append
+    pre = T - A
+    units, G, d = w.batch * w.kv_heads, w.q_heads // w.kv_heads, w.d
+    E = [[ev.create() for _ in range(4)] for _ in range(reps)]
+    codec = tq.Codec(d, 3, 3, d, seed=0, device=dev)
+    cache = tq.PackedCache(w.batch, w.kv_heads, d, T, 3, 3, d, device=dev, polar=1)
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, K[:, :, :pre].contiguous(), V[:, :, :pre].contiguous(), 0,
+                   w.rope_base)
+    Ka, Va = K[:, :, pre:].contiguous(), V[:, :, pre:].contiguous()
+    app_call, app_kern = timed_calls(lambda e: tq.quantize_kv(cache.desc, codec.dev, cache.buf, Ka, Va, pre,
+                                                              w.rope_base, events=e), ev, stream, E)
+    out = torch.empty((w.batch, w.q_heads, d), dtype=torch.float32, device=dev)
+    sc = torch.empty((w.batch, w.q_heads, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.decode_workspace_bytes(cache.desc, w.q_heads, T), dtype=torch.uint8, device=dev)
+    dec_call, dec_kern = timed_calls(lambda e: tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos,
+                                                                w.rope_base, out, ws=ws, events=e), ev, stream, E)
+    lg_call, _ = timed_calls(lambda e: tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos,
+                                                         w.rope_base, None, scores=sc, ws=ws, events=e), ev, stream, E)
+    rec = 3 * d // 8 + d // 8 + 4 + 3 * d // 8 + 2          # angles + signs + norms, keys and values
+    dbytes = units * T * rec
+    # vector work per token and head pair: decode ~3 d, scores and values 2 d G each, QJL d G / 4
+    flops = units * T * (3 * d + 4 * d * G + d * G // 4)
+    return {"workload": ("long_context shape, PolarQuant keys (3 - 2/d bits of angles + QJL m = d) and values; "
+                         "append of 4096 tokens, decode and logits at 131072; medians over %d calls" % reps),
+            "record_bytes_per_token": rec,
+            "append_kernel_us": round(app_kern, 2),
+            "append_mtokens_s": round(w.batch * A / (app_kern * 1e-6) / 1e6, 1),
+            "decode_call_us": round(dec_call, 2), "split_kernel_us": round(dec_kern, 2),
+            "split_kernel_gbs": round(dbytes / (dec_kern * 1e-6) / 1e9, 1),
+            "split_kernel_hbm_frac": round(dbytes / (dec_kern * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "split_kernel_alu_tflops": round(flops / (dec_kern * 1e-6) / 1e12, 2),
+            "split_kernel_alu_frac_fp32": round(flops / (dec_kern * 1e-6) / 1e12 / 157.3, 4),
+            "logits_call_us": round(lg_call, 2)}
+
+
 def key_width_bench(tq, W, w, K, V, q, dev, ev, stream, reps: int = 30):
     """Key bit-width variants on the same long-context shape, outside the timed steps:
     full decode of 1-, 2- and 3-bit keys (+ QJL, 3-bit values), and attention logits only
@@ -542,6 +584,12 @@ def main():
         nsn = nsn_bench(tq, w, K, V, q, dev, ev, stream)
         log(f"[bench] nsn {nsn}")
 
+    polar = None
+    if not args.no_search:
+        log("[bench] PolarQuant cache ...")
+        polar = polar_bench(tq, w, K, V, q, dev, ev, stream)
+        log(f"[bench] polar {polar}")
+
     window = None
     if not args.no_search:
         log("[bench] full-precision window and decode steps ...")
@@ -604,6 +652,7 @@ def main():
         "key_widths": widths,
         "window": window,
         "nsn": nsn,
+        "polar": polar,
         "search": search,
     }
     print(json.dumps(rec), flush=True)

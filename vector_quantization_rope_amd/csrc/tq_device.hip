@@ -2645,6 +2645,28 @@ __global__ __launch_bounds__(256) void k_window(WindowArgs a) {
   }
 }
 
+// Max / sum over the 64 lanes, in every lane: DPP within rows of 16 (quad swaps, rotations
+// by 4 and 8), then the four row results read lane by lane.
+__device__ __forceinline__ float row_dpp_f32(float x, bool mx) {
+  const auto op = [mx](float u, float v) { return mx ? fmaxf(u, v) : u + v; };
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, true)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true)));
+  return x;
+}
+__device__ __forceinline__ float lane_f32(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = row_dpp_f32(x, true);
+  return fmaxf(fmaxf(lane_f32(x, 0), lane_f32(x, 16)), fmaxf(lane_f32(x, 32), lane_f32(x, 48)));
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+  x = row_dpp_f32(x, false);
+  return (lane_f32(x, 0) + lane_f32(x, 16)) + (lane_f32(x, 32) + lane_f32(x, 48));
+}
+
 // ------------------------------------------------------------------ PolarQuant decode
 // Split-K decode over PolarQuant records ([TurboQuant] "PolarQuant" as stage 1, QJL on
 // the key residual).  Per 64-token chunk of the block's range: the records come in with
@@ -2668,23 +2690,26 @@ struct PolarArgs {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void k_decode_polar(PolarArgs a) {
-  constexpr int L = D == 128 ? 7 : 6, CH = 64, RS = D + 1, GM = 8, MMAX = 128;
-  constexpr int VB = 3 * D / 8;                 // value record bytes
-  constexpr int HS = 256 / D, HPT = GM / HS;    // value phase: head slots per thread
+__global__ __launch_bounds__(512, 2) void k_decode_polar(PolarArgs a) {
+  // m = D QJL rows; 8 waves: decode by eighths of a token (key or value, one quarter of
+  // the coordinates), scores and softmax one head per wave, values by coordinate
+  constexpr int L = D == 128 ? 7 : 6, CH = 64, RS = D + 1, GM = 8, NT = 512;
+  constexpr int VB = 3 * D / 8, KW = (3 * D / 8 + D / 8) / 4, VW = VB / 4;   // record dwords
+  constexpr int KWP = KW + 1, VWP = VW + 1;     // odd LDS strides: one token per bank
+  constexpr int HS = NT / D, HPT = GM / HS;     // value phase: head slots per thread
   constexpr int NQ = D / 4;                     // coordinates per decode quarter
+  constexpr int NKD = (CH * KW + NT - 1) / NT, NVD = (CH * VW + NT - 1) / NT;
+  constexpr int HI0 = 2 * D / 32, NHI = KW - D / 32 - HI0;   // dwords of the 2-bit codes
   __shared__ __align__(16) float qr[GM][D];
-  __shared__ float kr[CH * RS];
+  __shared__ float psk[4][GM][CH];              // key score parts by quarter
   __shared__ float vr[CH * RS];
   __shared__ __align__(16) float ps[GM][CH];
-  __shared__ float nib[GM][MMAX / 4][16];      // sum of S q over the set bits of a nibble
+  __shared__ float nib[GM][D / 4][16];         // sum of S q over the set bits of a nibble
   __shared__ float s1q[GM];                    // sum of S q
   __shared__ float mstat[3][GM];
-  __shared__ float cs_s[L][16][2];
-  constexpr int KWMAX = (3 * D / 8 + MMAX / 8) / 4;   // key record dwords at most
-  constexpr int NKD = (CH * KWMAX + 255) / 256, NVD = (CH * VB / 4 + 255) / 256;
-  __shared__ uint32_t krs[CH * KWMAX];           // the chunk's key records, kw dwords each
-  __shared__ uint32_t vrs[CH * (VB / 4)];
+  __shared__ float cs1[16][2];                 // level-1 centroids' cos, sin
+  __shared__ uint32_t krs[CH * KWP];
+  __shared__ uint32_t vrs[CH * VWP];
   __shared__ uint32_t kns[CH];
   __shared__ float vns[CH];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -2692,25 +2717,22 @@ __global__ __launch_bounds__(256) void k_decode_polar(PolarArgs a) {
   const int b = unit / a.kv_heads, g = unit % a.kv_heads, G = a.G, hq0 = g * G;
   const int t_begin = split * a.chunk, t_end = min(a.length, t_begin + a.chunk);
   const size_t ubase = size_t(unit) * a.capacity;
-  const int kw = a.kb / 4;                      // key record dwords
-  // one chunk's records as dwords (records are whole dwords, so each load stays inside
-  // the chunk's valid tokens), the next chunk's in registers while this one is scored
   uint32_t kreg[NKD], vreg[NVD];
   uint32_t knr = 0u;
   float vnr = 0.0f;
   auto fetch = [&](int c0) {
     const int cn = min(CH, t_end - c0);
-    const uint32_t *ks = reinterpret_cast<const uint32_t *>(a.krec + (ubase + c0) * a.kb);
+    const uint32_t *ks = reinterpret_cast<const uint32_t *>(a.krec + (ubase + c0) * (KW * 4));
     const uint32_t *vs = reinterpret_cast<const uint32_t *>(a.vrec + (ubase + c0) * VB);
 #pragma unroll
     for (int i = 0; i < NKD; ++i) {
-      const int k = tid + 256 * i;
-      kreg[i] = k < cn * kw ? ks[k] : 0u;
+      const int k = tid + NT * i;
+      kreg[i] = k < cn * KW ? ks[k] : 0u;
     }
 #pragma unroll
     for (int i = 0; i < NVD; ++i) {
-      const int k = tid + 256 * i;
-      vreg[i] = k < cn * (VB / 4) ? vs[k] : 0u;
+      const int k = tid + NT * i;
+      vreg[i] = k < cn * VW ? vs[k] : 0u;
     }
     if (tid < cn) {
       knr = a.knorm[ubase + c0 + tid];
@@ -2718,15 +2740,26 @@ __global__ __launch_bounds__(256) void k_decode_polar(PolarArgs a) {
     }
   };
   if (t_begin < t_end) fetch(t_begin);
-  for (int i = tid; i < L * 32; i += 256) (&cs_s[0][0][0])[i] = a.pcs[i];
-  for (int i = tid; i < GM * D; i += 256) {
+  // decode role: lane = token, wave = key (kv = 0) or value (kv = 1) and quarter qq
+  const int tt = lane, kv = wv >> 2, qq = wv & 3;
+  // cos, sin of the higher levels' centroids in registers: [level - 2][code]
+  float hc[L - 1][4], hs_[L - 1][4];
+#pragma unroll
+  for (int lv = 2; lv <= L; ++lv)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      hc[lv - 2][c] = a.pcs[((lv - 1) * 16 + c) * 2];
+      hs_[lv - 2][c] = a.pcs[((lv - 1) * 16 + c) * 2 + 1];
+    }
+  if (tid < 32) (&cs1[0][0])[tid] = a.pcs[tid];
+  for (int i = tid; i < GM * D; i += NT) {
     const int h = i / D, j = i % D;
     qr[h][j] = h < G ? a.qp[size_t(b * a.q_heads + hq0 + h) * a.qstride + j] : 0.0f;
   }
-  for (int i = tid; i < GM * (MMAX / 4) * 16; i += 256) {
-    const int h = i / (MMAX / 4 * 16), k = (i / 16) % (MMAX / 4), v = i % 16;
+  for (int i = tid; i < GM * (D / 4) * 16; i += NT) {
+    const int h = i / (D / 4 * 16), k = (i / 16) % (D / 4), v = i % 16;
     float acc = 0.0f;
-    if (h < G && 4 * k < a.m) {
+    if (h < G) {
       const float *sq = a.qp + size_t(b * a.q_heads + hq0 + h) * a.qstride + D;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -2735,147 +2768,136 @@ __global__ __launch_bounds__(256) void k_decode_polar(PolarArgs a) {
     nib[h][k][v] = acc;
   }
   if (tid < GM) {
-    s1q[tid] = tid < G ? a.qp[size_t(b * a.q_heads + hq0 + tid) * a.qstride + D + a.m + 1] : 0.0f;
+    s1q[tid] = tid < G ? a.qp[size_t(b * a.q_heads + hq0 + tid) * a.qstride + D + D + 1] : 0.0f;
     mstat[0][tid] = -INFINITY;
     mstat[1][tid] = 0.0f;
     mstat[2][tid] = 0.0f;
   }
-  for (int i = tid; i < GM * CH; i += 256) (&ps[0][0])[i] = 0.0f;
-  const int jv = tid % D, hs = tid / D;
+  for (int i = tid; i < GM * CH; i += NT) (&ps[0][0])[i] = 0.0f;
+  const int jv = tid % D, hsl = tid / D;
   float acc[HPT];
 #pragma unroll
   for (int k = 0; k < HPT; ++k) acc[k] = 0.0f;
-  // decode role: token tt, quarter qq
-  const int tt = tid >> 2, qq = tid & 3;
+  auto lbit = [](int lv, int j) { return 2 * D + 2 * (D / 2 - (D >> (lv - 1)) + j); };
   for (int c0 = t_begin; c0 < t_end; c0 += CH) {
     const int cn = min(CH, t_end - c0);
     __syncthreads();   // the previous chunk's readers are done
 #pragma unroll
-    for (int i = 0; i < NKD; ++i)
-      if (tid + 256 * i < CH * kw) krs[tid + 256 * i] = kreg[i];
+    for (int i = 0; i < NKD; ++i) {
+      const int k = tid + NT * i;
+      if (k < CH * KW) krs[(k / KW) * KWP + k % KW] = kreg[i];
+    }
 #pragma unroll
-    for (int i = 0; i < NVD; ++i)
-      if (tid + 256 * i < CH * (VB / 4)) vrs[tid + 256 * i] = vreg[i];
+    for (int i = 0; i < NVD; ++i) {
+      const int k = tid + NT * i;
+      if (k < CH * VW) vrs[(k / VW) * VWP + k % VW] = vreg[i];
+    }
     if (tid < CH) {
       kns[tid] = tid < cn ? knr : 0u;
       vns[tid] = tid < cn ? vnr : 0.0f;
     }
     if (c0 + CH < t_end) fetch(c0 + CH);
     __syncthreads();
-    // ---- decode: quarter qq of token tt (rows past the chunk's end become zero)
+    // ---- decode one quarter (rows past the chunk's end become zero)
     {
-      const uint32_t *kwd = &krs[tt * kw];
-      const uint32_t *vwd = &vrs[tt * (VB / 4)];
-      const bool live = tt < cn;
-      auto field = [&](const uint32_t *w, int bit, int width) {
-        return (w[bit >> 5] >> (bit & 31)) & ((1u << width) - 1u);
+      const uint32_t *w = kv ? &vrs[tt * VWP] : &krs[tt * KWP];
+      // the quarter's level-1 nibbles and every 2-bit code, read together
+      constexpr int N1 = D / 64;   // dwords of a quarter's level-1 nibbles
+      uint32_t n1[N1], hi[NHI];
+#pragma unroll
+      for (int i = 0; i < N1; ++i) n1[i] = w[qq * N1 + i];
+#pragma unroll
+      for (int i = 0; i < NHI; ++i) hi[i] = w[HI0 + i];
+      auto code2 = [&](int bit) {   // a 2-bit code in the high dwords (bit >= 2 D)
+        const int wd = (bit >> 5) - HI0;
+        uint32_t x = hi[0];
+#pragma unroll
+        for (int i = 1; i < NHI; ++i) x = wd == i ? hi[i] : x;
+        return int((x >> (bit & 31)) & 3u);
       };
-      auto lbit = [](int lv, int j) { return 2 * D + 2 * (D / 2 - (D >> (lv - 1)) + j); };
+      auto pick = [](const float (&t)[4], int c) {
+        return c == 0 ? t[0] : c == 1 ? t[1] : c == 2 ? t[2] : t[3];
+      };
+      const float scale = kv ? vns[tt] : 1.0f;
+      const int cT = code2(lbit(L, 0)), cH = code2(lbit(L - 1, qq >> 1));
+      float r[NQ / 2];
+      r[0] = scale * ((qq >> 1) ? pick(hs_[L - 2], cT) : pick(hc[L - 2], cT)) *
+             ((qq & 1) ? pick(hs_[L - 3], cH) : pick(hc[L - 3], cH));
 #pragma unroll
-      for (int kv = 0; kv < 2; ++kv) {
-        const uint32_t *w = kv ? vwd : kwd;
-        float *row = (kv ? vr : kr) + tt * RS + qq * NQ;
-        const float scale = kv ? vns[tt] : 1.0f;
-        // quarter radius from the two top levels
-        const int cT = int(field(w, lbit(L, 0), 2)), cH = int(field(w, lbit(L - 1, qq >> 1), 2));
-        float r[NQ / 2];
-        r[0] = scale * cs_s[L - 1][cT][qq >> 1] * cs_s[L - 2][cH][qq & 1];
+      for (int lv = L - 2, n = 1; lv >= 2; --lv, n <<= 1) {
 #pragma unroll
-        for (int lv = L - 2, n = 1; lv >= 2; --lv, n <<= 1) {
-          // level lv: n codes inside the quarter, from index qq n
-#pragma unroll
-          for (int i = n - 1; i >= 0; --i) {
-            const int c = int(field(w, lbit(lv, qq * n + i), 2));
-            const float rr = r[i];
-            r[2 * i] = rr * cs_s[lv - 1][c][0];
-            r[2 * i + 1] = rr * cs_s[lv - 1][c][1];
-          }
+        for (int i = n - 1; i >= 0; --i) {
+          const int c = code2(lbit(lv, qq * n + i));
+          const float rr = r[i];
+          r[2 * i] = rr * pick(hc[lv - 2], c);
+          r[2 * i + 1] = rr * pick(hs_[lv - 2], c);
         }
+      }
+      const bool live = tt < cn;
+      if (kv) {
+        float *row = vr + tt * RS + qq * NQ;
 #pragma unroll
         for (int i = 0; i < NQ / 2; ++i) {
-          const int c = int(field(w, 4 * (qq * (NQ / 2) + i), 4));
-          row[2 * i] = live ? r[i] * cs_s[0][c][0] : 0.0f;
-          row[2 * i + 1] = live ? r[i] * cs_s[0][c][1] : 0.0f;
+          const int c = int((n1[i >> 3] >> (4 * (i & 7))) & 15u);
+          row[2 * i] = live ? r[i] * cs1[c][0] : 0.0f;
+          row[2 * i + 1] = live ? r[i] * cs1[c][1] : 0.0f;
+        }
+      } else {
+        // the key's quarter stays in registers: its share of every head's score
+        float y[NQ];
+#pragma unroll
+        for (int i = 0; i < NQ / 2; ++i) {
+          const int c = int((n1[i >> 3] >> (4 * (i & 7))) & 15u);
+          y[2 * i] = r[i] * cs1[c][0];
+          y[2 * i + 1] = r[i] * cs1[c][1];
+        }
+#pragma unroll
+        for (int h = 0; h < GM; ++h) {
+          if (h < G) {
+            float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+            for (int j = 0; j < NQ; j += 4) {
+              const float4 qa = *reinterpret_cast<const float4 *>(&qr[h][qq * NQ + j]);
+              d0 = fmaf(qa.x, y[j], d0);
+              d1 = fmaf(qa.y, y[j + 1], d1);
+              d0 = fmaf(qa.z, y[j + 2], d0);
+              d1 = fmaf(qa.w, y[j + 3], d1);
+            }
+            psk[qq][h][tt] = live ? d0 + d1 : 0.0f;
+          }
         }
       }
     }
     __syncthreads();
-    // ---- scores: token = lane, heads h0 and h0 + 4
-    {
-      const int t = lane;
-      const float *krow = &kr[t * RS];
+    // ---- scores: wave = head, lane = token
+    if (wv < G) {
+      const int h = wv, t = lane;
       const uint32_t nrm = kns[t];
       const float n16 = f16_bits_to_float(nrm & 0xFFFFu), rn16 = f16_bits_to_float(nrm >> 16);
-      const uint32_t *sg = &krs[t * kw + 3 * D / 32];   // sign bits
-      for (int h0 = wv; h0 < G; h0 += 8) {
-        const int h1 = h0 + 4;
-        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-#pragma unroll 8
-        for (int j = 0; j < D; j += 4) {
-          const float4 qa = *reinterpret_cast<const float4 *>(&qr[h0][j]);
-          const float4 qb = *reinterpret_cast<const float4 *>(&qr[h1 < GM ? h1 : h0][j]);
-          const float k0 = krow[j], k1 = krow[j + 1], k2 = krow[j + 2], k3 = krow[j + 3];
-          s0 = fmaf(qa.x, k0, s0);
-          s1 = fmaf(qa.y, k1, s1);
-          s0 = fmaf(qa.z, k2, s0);
-          s1 = fmaf(qa.w, k3, s1);
-          s2 = fmaf(qb.x, k0, s2);
-          s3 = fmaf(qb.y, k1, s3);
-          s2 = fmaf(qb.z, k2, s2);
-          s3 = fmaf(qb.w, k3, s3);
-        }
-        float b0 = 0.0f, b1 = 0.0f;
-        for (int k = 0; k < a.m / 4; ++k) {
-          const uint32_t v = (sg[k >> 3] >> (4 * (k & 7))) & 15u;
-          b0 += nib[h0][k][v];
-          if (h1 < G) b1 += nib[h1][k][v];
-        }
-        ps[h0][t] = fmaf(n16, s0 + s1, a.qjl_scale * rn16 * fmaf(2.0f, b0, -s1q[h0]));
-        if (h1 < G) ps[h1][t] = fmaf(n16, s2 + s3, a.qjl_scale * rn16 * fmaf(2.0f, b1, -s1q[h1]));
-      }
-    }
-    __syncthreads();
-    // ---- online softmax, one lane per token, heads h0 and h0 + 4 side by side
-    for (int h0 = wv; h0 < G; h0 += 8) {
-      const int h1 = h0 + 4;
-      const bool two = h1 < G;
-      const float x0 = ps[h0][lane], x1 = ps[h1 < GM ? h1 : h0][lane];
-      if (a.scores && lane < cn) {
-        float *srow = a.scores + (size_t(b) * a.q_heads + hq0) * a.score_stride + c0 + lane;
-        srow[size_t(h0) * a.score_stride] = x0;
-        if (two) srow[size_t(h1) * a.score_stride] = x1;
-      }
-      const float v0 = lane < cn ? x0 * a.scale_log2 : -INFINITY;
-      const float v1 = lane < cn ? x1 * a.scale_log2 : -INFINITY;
-      float m0 = v0, m1 = v1;
+      uint32_t sg[D / 32];
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        m0 = fmaxf(m0, __shfl_xor(m0, o, 64));
-        m1 = fmaxf(m1, __shfl_xor(m1, o, 64));
-      }
-      const float mold0 = mstat[0][h0], mnew0 = fmaxf(mold0, m0);
-      const float mold1 = two ? mstat[0][h1] : -INFINITY, mnew1 = fmaxf(mold1, m1);
-      const float al0 = mold0 == -INFINITY ? 0.0f : exp2f(mold0 - mnew0);
-      const float al1 = mold1 == -INFINITY ? 0.0f : exp2f(mold1 - mnew1);
-      const float p0 = lane < cn ? exp2f(v0 - mnew0) : 0.0f;
-      const float p1 = lane < cn ? exp2f(v1 - mnew1) : 0.0f;
-      float l0 = p0, l1 = p1;
+      for (int i = 0; i < D / 32; ++i) sg[i] = krs[t * KWP + 3 * D / 32 + i];
+      const float s0 = psk[0][h][t], s1 = psk[1][h][t], s2 = psk[2][h][t], s3 = psk[3][h][t];
+      float q0 = 0.0f, q1 = 0.0f;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        l0 += __shfl_xor(l0, o, 64);
-        l1 += __shfl_xor(l1, o, 64);
+      for (int k = 0; k < D / 4; k += 2) {
+        q0 += nib[h][k][(sg[k >> 3] >> (4 * (k & 7))) & 15u];
+        q1 += nib[h][k + 1][(sg[(k + 1) >> 3] >> (4 * ((k + 1) & 7))) & 15u];
       }
-      ps[h0][lane] = p0;
-      if (two) ps[h1][lane] = p1;
+      const float sc = fmaf(n16, (s0 + s1) + (s2 + s3), a.qjl_scale * rn16 * fmaf(2.0f, q0 + q1, -s1q[h]));
+      ps[h][t] = sc;
+      if (a.scores && t < cn) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.score_stride + c0 + t] = sc;
+      // online softmax of this head over the chunk
+      const float v = t < cn ? sc * a.scale_log2 : -INFINITY;
+      const float mold = mstat[0][h], mnew = fmaxf(mold, wave_max_dpp(v));
+      const float al = mold == -INFINITY ? 0.0f : exp2f(mold - mnew);
+      const float p = t < cn ? exp2f(v - mnew) : 0.0f;
+      const float l = wave_sum_dpp(p);
+      ps[h][t] = p;
       if (lane == 0) {
-        mstat[0][h0] = mnew0;
-        mstat[1][h0] = mstat[1][h0] * al0 + l0;
-        mstat[2][h0] = al0;
-        if (two) {
-          mstat[0][h1] = mnew1;
-          mstat[1][h1] = mstat[1][h1] * al1 + l1;
-          mstat[2][h1] = al1;
-        }
+        mstat[0][h] = mnew;
+        mstat[1][h] = mstat[1][h] * al + l;
+        mstat[2][h] = al;
       }
     }
     __syncthreads();
@@ -2883,18 +2905,18 @@ __global__ __launch_bounds__(256) void k_decode_polar(PolarArgs a) {
     {
       float o[HPT];
 #pragma unroll
-      for (int k = 0; k < HPT; ++k) o[k] = acc[k] * mstat[2][hs + k * HS];
+      for (int k = 0; k < HPT; ++k) o[k] = acc[k] * mstat[2][hsl + k * HS];
 #pragma unroll 4
       for (int t = 0; t < CH; t += 4) {
         const float v0 = vr[t * RS + jv], v1 = vr[(t + 1) * RS + jv];
         const float v2 = vr[(t + 2) * RS + jv], v3 = vr[(t + 3) * RS + jv];
 #pragma unroll
         for (int k = 0; k < HPT; ++k) {
-          const float4 p = *reinterpret_cast<const float4 *>(&ps[hs + k * HS][t]);
-          o[k] = fmaf(p.x, v0, o[k]);
-          o[k] = fmaf(p.y, v1, o[k]);
-          o[k] = fmaf(p.z, v2, o[k]);
-          o[k] = fmaf(p.w, v3, o[k]);
+          const float4 pp = *reinterpret_cast<const float4 *>(&ps[hsl + k * HS][t]);
+          o[k] = fmaf(pp.x, v0, o[k]);
+          o[k] = fmaf(pp.y, v1, o[k]);
+          o[k] = fmaf(pp.z, v2, o[k]);
+          o[k] = fmaf(pp.w, v3, o[k]);
         }
       }
 #pragma unroll
@@ -2904,7 +2926,7 @@ __global__ __launch_bounds__(256) void k_decode_polar(PolarArgs a) {
   // partial (rotated basis): acc, max (natural log), sum
 #pragma unroll
   for (int k = 0; k < HPT; ++k) {
-    const int h = hs + k * HS;
+    const int h = hsl + k * HS;
     if (h < G) {
       float *o = a.part + ((size_t(b) * a.q_heads + hq0 + h) * a.splits + split) * (D + 2);
       o[jv] = acc[k];
@@ -3664,7 +3686,8 @@ int default_splits(const tq_cache_desc &c, int length) {
   const int by_len = (length + kMfmaChunk - 1) / kMfmaChunk;
   // one round of blocks: the split kernel keeps kDecBlocksPerCU blocks resident per CU
   // and MI355X has 256 CUs, so all blocks start together and none waits for a second round
-  const int want = (kDecodeBlocks + units - 1) / units;
+  // (PolarQuant's decode kernel fits two blocks per CU: twice the blocks)
+  const int want = ((c.polar ? 2 : 1) * kDecodeBlocks + units - 1) / units;
   int s = by_len < want ? by_len : want;
   if (s < 1) s = 1;
   if (s > 4096) s = 4096;
@@ -3894,9 +3917,9 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
   const CodecPtrs cp = codec_ptrs(codec_dev, d, desc->bits_k, desc->bits_v, m);
   if (win && cp.block != d) return TQ_EUNSUPPORTED;   // the window rotates with one d-point block
   // NSN caches decode on the MFMA path only (its kernels carry the mean terms); PolarQuant
-  // caches on their own kernel (8 head slots, QJL rows up to 128)
+  // caches on their own kernel (8 head slots, m = d QJL rows)
   if (desc->nsn && !decode_mfma_path(*desc, q_heads)) return TQ_EUNSUPPORTED;
-  if (desc->polar && (q_heads / desc->kv_heads > 8 || desc->m > 128)) return TQ_EUNSUPPORTED;
+  if (desc->polar && (q_heads / desc->kv_heads > 8 || desc->m != desc->d)) return TQ_EUNSUPPORTED;
   if (win && win->flush) {
     // the full window becomes packed tokens [length - cap, length) before anything reads them
     if (length < win->cap) return TQ_EINVAL;
@@ -4012,9 +4035,9 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
     const dim3 grid(units, used_splits);
     if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
     if (d == 64)
-      hipLaunchKernelGGL(k_decode_polar<64>, grid, dim3(256), 0, s, pa);
+      hipLaunchKernelGGL(k_decode_polar<64>, grid, dim3(512), 0, s, pa);
     else
-      hipLaunchKernelGGL(k_decode_polar<128>, grid, dim3(256), 0, s, pa);
+      hipLaunchKernelGGL(k_decode_polar<128>, grid, dim3(512), 0, s, pa);
     if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
   } else {
     DecodeArgs a;
