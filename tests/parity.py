@@ -84,7 +84,8 @@ def oracle_encode_polar(K, V, codec, positions, rope_base):
 
 def compare_polar_codes(gpu: dict, orc: dict, codec, report=None):
     """PolarQuant records under the parity rule: an angle code may differ only when the
-    oracle's angle lies within 1e-6 rad of one of its level's boundaries, a norm only next to
+    oracle's angle lies within 1e-6 rad of one of its level's boundaries (for level 1 also
+    the wrap-around at 0 = 2 pi), a norm only next to
     an fp16 midpoint; a key whose codes or norm differ has a different residual, so its QJL
     bits and residual norm are compared only when they agree."""
     pc = O.make_polar_codebook(codec.d)
@@ -97,7 +98,9 @@ def compare_polar_codes(gpu: dict, orc: dict, codec, report=None):
             bad = gpu[side + "pc"][lv] != pcs[lv]
             res["codes"] += pcs[lv].size
             if np.any(bad):
-                near = np.min(np.abs(ang[lv][..., None] - pc.t[lv]), axis=-1) <= MARGIN
+                # level-1 angles live on a circle: 0 = 2 pi is a decision boundary as well
+                tb = np.concatenate(([0.0], pc.t[lv], [2 * math.pi])) if lv == 1 else pc.t[lv]
+                near = np.min(np.abs(ang[lv][..., None] - tb), axis=-1) <= MARGIN
                 assert np.all(near[bad]), f"{int(np.sum(bad & ~near))} {side} angle codes (level {lv}) differ away from a boundary"
                 res["excused"] += int(np.sum(bad))
                 tok_bad |= np.any(bad, axis=-1)
@@ -229,16 +232,20 @@ def unit_fields(cache: "tq.PackedCache", unit: int, length: int) -> dict:
     Copies only that unit's slices of each region (the layout of the format description,
     as the oracle computes it) into a one-unit image and unpacks it with the oracle."""
     desc = cache.desc.as_dict()
+    nsn, polar = desc.get("nsn", 0), desc.get("polar", 0)
     lay = O.cache_layout(desc["batch"], desc["kv_heads"], desc["d"], desc["capacity"],
-                         desc["bits_k"], desc["bits_v"], desc["m"])
+                         desc["bits_k"], desc["bits_v"], desc["m"], nsn, polar)
     sub = dict(desc, batch=1, kv_heads=1)
-    sl = O.cache_layout(1, 1, sub["d"], sub["capacity"], sub["bits_k"], sub["bits_v"], sub["m"])
+    sl = O.cache_layout(1, 1, sub["d"], sub["capacity"], sub["bits_k"], sub["bits_v"], sub["m"], nsn, polar)
     img = np.zeros(sl["total"], dtype=np.uint8)
     img[:256] = cache.buf[:256].cpu().numpy()
     cap = desc["capacity"]
-    sizes = {"kbits": cap * lay["kbytes"], "knorm": cap * 4}
+    sizes = {"kbits": cap * lay["kbytes"], "knorm": cap * lay["knrec"]}
     if desc["bits_v"] > 0:
-        sizes.update(vcodes=lay["tiles"] * desc["d"] * 4 * desc["bits_v"], vnorm=cap * 2)
+        vbytes = cap * 3 * desc["d"] // 8 if polar else lay["tiles"] * desc["d"] * 4 * desc["bits_v"]
+        sizes.update(vcodes=vbytes, vnorm=cap * lay["vnrec"])
+    if nsn:
+        sizes["nsn"] = 4 * desc["d"] * 4
     for name, n in sizes.items():
         src = cache.buf[lay[name] + unit * n: lay[name] + (unit + 1) * n]
         img[sl[name]: sl[name] + n] = src.cpu().numpy()

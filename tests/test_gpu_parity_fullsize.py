@@ -8,6 +8,9 @@
     the unit's 8 q-head outputs with the oracle attending over the GPU-produced cache.
   * Llama-3-8B-shaped layer (batch 16, 32 q / 8 kv heads, 32768 tokens): the same checks
     on sampled units of one layer.
+  * the same long-context shape as an NSN cache (means over the prefill), as a PolarQuant
+    cache, and with its last 128 tokens as a full-precision window, as bench.py's sections
+    build them: a sampled unit's codes and outputs against the oracle.
   * vector search (10^6 x 1536 database, 1024 queries, 3-bit + QJL m = 1536, top-10):
     codes of sampled database vectors; the returned scores of sampled queries against the
     oracle's estimate of the returned vectors; and, for two queries, the complete top-10
@@ -95,6 +98,117 @@ def test_long_context_full_size_bench_config(tq, P):
     say(f"    decode splits {tq.decode_splits(cache.desc, w.q_heads, T)}")
     assert torch.isfinite(out).all()
     check_units(tq, P, w, K, V, q, cache, out, [(0, 0), (3, 5)], "long_context")
+
+
+def _long_context_inputs(tq, w):
+    K, V = W.gen_kv(w, device="cuda")
+    q = W.gen_q(w, device="cuda")
+    return K, V, q
+
+
+def test_long_context_nsn_full_size(tq, P):
+    """NSN cache at the long-context shape, built as bench.py's NSN section builds it
+    (means over the 126976-token prefill, prefill, 4096-token append) and decoded with the
+    default split count; a sampled unit's means, codes, s1 and outputs against the oracle."""
+    w = W.LONG_CONTEXT
+    T, A = w.context, w.append
+    pre = T - A
+    K, V, q = _long_context_inputs(tq, w)
+    codec = tq.Codec(w.d, w.bits_k, w.bits_v, w.m, seed=0)
+    cache = tq.PackedCache(w.batch, w.kv_heads, w.d, T, w.bits_k, w.bits_v, w.m, nsn=1)
+    Kp, Vp = K[:, :, :pre].contiguous(), V[:, :, :pre].contiguous()
+    ws = torch.empty(tq.nsn_means_workspace_bytes(cache.desc, pre), dtype=torch.uint8, device="cuda")
+    tq.nsn_set_means(cache.desc, codec.dev, cache.buf, Kp, Vp, 0, w.rope_base, ws)
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, Kp, Vp, 0, w.rope_base)
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, K[:, :, pre:].contiguous(), V[:, :, pre:].contiguous(),
+                   pre, w.rope_base)
+    del Kp, Vp
+    out = torch.empty((w.batch, w.q_heads, w.d), dtype=torch.float32, device="cuda")
+    wsd = torch.empty(tq.decode_workspace_bytes(cache.desc, w.q_heads, T), dtype=torch.uint8, device="cuda")
+    tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos, w.rope_base, out, ws=wsd)
+    torch.cuda.synchronize()
+    codec_o = O.make_codec(w.d, w.bits_k, w.bits_v, w.m, 0)
+    G = w.q_heads // w.kv_heads
+    b, g = 2, 3
+    t0 = time.time()
+    gf = P.unit_fields(cache, b * w.kv_heads + g, T)
+    Kd = K[b:b + 1, g:g + 1].to("cpu").to(torch.float64).numpy()
+    Vd = V[b:b + 1, g:g + 1].to("cpu").to(torch.float64).numpy()
+    means = P.oracle_means(Kd[:, :, :pre], Vd[:, :, :pre], np.arange(pre), w.rope_base)
+    orc = P.oracle_encode_unitwise(Kd, Vd, codec_o, np.arange(T), w.rope_base, means)
+    rep = P.compare_codes(gf, orc, codec_o)
+    qd = q[b:b + 1, g * G:(g + 1) * G].to("cpu").to(torch.float64).numpy()
+    out_o, _ = O.attend(gf, qd, codec_o, q_pos=w.q_pos, rope_base=w.rope_base, scale=0.0, kv_heads=1, length=T)
+    err = P.max_abs(out[b, g * G:(g + 1) * G].cpu().numpy(), out_o[0])
+    say(f"[long_context nsn] unit (b={b}, kv={g}) codes {rep} out max-abs {err:.2e} ({time.time() - t0:.1f} s)")
+    assert err <= TOL
+
+
+def test_long_context_polar_full_size(tq, P):
+    """PolarQuant cache at the long-context shape (prefill, 4096-token append, default
+    split count, as bench.py's PolarQuant section): a sampled unit's angle codes, norms,
+    QJL bits and outputs against the oracle."""
+    w = W.LONG_CONTEXT
+    T, A = w.context, w.append
+    pre = T - A
+    K, V, q = _long_context_inputs(tq, w)
+    d = w.d
+    codec = tq.Codec(d, 3, 3, d, seed=0)
+    cache = tq.PackedCache(w.batch, w.kv_heads, d, T, 3, 3, d, polar=1)
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, K[:, :, :pre].contiguous(), V[:, :, :pre].contiguous(), 0,
+                   w.rope_base)
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, K[:, :, pre:].contiguous(), V[:, :, pre:].contiguous(),
+                   pre, w.rope_base)
+    out = torch.empty((w.batch, w.q_heads, d), dtype=torch.float32, device="cuda")
+    wsd = torch.empty(tq.decode_workspace_bytes(cache.desc, w.q_heads, T), dtype=torch.uint8, device="cuda")
+    tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos, w.rope_base, out, ws=wsd)
+    torch.cuda.synchronize()
+    codec_o = O.make_codec(d, 3, 3, d, 0)
+    G = w.q_heads // w.kv_heads
+    b, g = 1, 6
+    t0 = time.time()
+    gf = P.unit_fields(cache, b * w.kv_heads + g, T)
+    Kd = K[b:b + 1, g:g + 1].to("cpu").to(torch.float64).numpy()
+    Vd = V[b:b + 1, g:g + 1].to("cpu").to(torch.float64).numpy()
+    orc = P.oracle_encode_polar(Kd, Vd, codec_o, np.arange(T), w.rope_base)
+    rep = P.compare_polar_codes(gf, orc, codec_o)
+    qd = q[b:b + 1, g * G:(g + 1) * G].to("cpu").to(torch.float64).numpy()
+    out_o, _ = O.attend(gf, qd, codec_o, q_pos=w.q_pos, rope_base=w.rope_base, scale=0.0, kv_heads=1, length=T)
+    err = P.max_abs(out[b, g * G:(g + 1) * G].cpu().numpy(), out_o[0])
+    say(f"[long_context polar] unit (b={b}, kv={g}) codes {rep} out max-abs {err:.2e} ({time.time() - t0:.1f} s)")
+    assert err <= TOL
+
+
+def test_long_context_window_full_size(tq, P):
+    """The long-context cache with its last 128 tokens as a full-precision window (bench.py's
+    window section: 130944 packed tokens + 128 raw ones): a sampled unit's outputs against
+    the oracle attending over the GPU-produced packed part and the raw window."""
+    w = W.LONG_CONTEXT
+    T, cap = w.context, 128
+    L = T - cap
+    K, V, q = _long_context_inputs(tq, w)
+    codec = tq.Codec(w.d, w.bits_k, w.bits_v, w.m, seed=0)
+    cache = tq.PackedCache(w.batch, w.kv_heads, w.d, T, w.bits_k, w.bits_v, w.m)
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, K[:, :, :L].contiguous(), V[:, :, :L].contiguous(), 0,
+                   w.rope_base)
+    wk, wv = K[:, :, L:].contiguous(), V[:, :, L:].contiguous()
+    out = torch.empty((w.batch, w.q_heads, w.d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(tq.decode_window_workspace_bytes(cache.desc, w.q_heads, L), dtype=torch.uint8, device="cuda")
+    tq.decode_attend_window(cache.desc, codec.dev, cache.buf, L, wk, wv, cap, q, w.q_pos, w.rope_base, out, ws=ws)
+    torch.cuda.synchronize()
+    codec_o = O.make_codec(w.d, w.bits_k, w.bits_v, w.m, 0)
+    G = w.q_heads // w.kv_heads
+    b, g = 3, 1
+    t0 = time.time()
+    gf = P.unit_fields(cache, b * w.kv_heads + g, L)
+    qd = q[b:b + 1, g * G:(g + 1) * G].to("cpu").to(torch.float64).numpy()
+    wkd = wk[b:b + 1, g:g + 1].to("cpu").to(torch.float64).numpy()
+    wvd = wv[b:b + 1, g:g + 1].to("cpu").to(torch.float64).numpy()
+    out_o, _ = O.attend_window(gf, wkd, wvd, qd, codec_o, q_pos=w.q_pos, rope_base=w.rope_base, scale=0.0,
+                               kv_heads=1, length=L, win_len=cap)
+    err = P.max_abs(out[b, g * G:(g + 1) * G].cpu().numpy(), out_o[0])
+    say(f"[long_context window] unit (b={b}, kv={g}) out max-abs {err:.2e} ({time.time() - t0:.1f} s)")
+    assert err <= TOL
 
 
 def test_llama3_8b_layer_sampled_units(tq, P):
