@@ -1762,16 +1762,12 @@ __device__ __forceinline__ float pick_bits(uint32_t mask, float a, float b) {
   return __uint_as_float((mask & __float_as_uint(a)) | (~mask & __float_as_uint(b)));
 }
 
-__device__ __forceinline__ void wait_lgkm0() {
-  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-}
-
 // KBITS = key code bits (1, 2 or 3).  The key score's code term is a weighted sum of
 // NP 0/1 planes: the code bits, and for 3-bit codes also their parity (odd codebook).
 // NSN: the cache's tokens carry fp16 s1 next to the norms; a key's score gains
 // s1 <q, o_K> (the query coefficient 2) and a value's share of s1 Pi o_V is summed per head
 // next to the softmax sum and added to the accumulator at the end.
-template <int D, int KBITS, bool NSN>
+template <int D, int KBITS, bool NSN, bool SCORES>
 __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(MfmaArgs a) {
   // The body is device code only (its local lambdas call device builtins); the host pass
   // needs nothing but the launch stub.
@@ -1780,8 +1776,12 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
   constexpr int NCH = D / 32, NT = D / 16, NW = kDecWaves, NTH = 64 * NW, R = kRing;
   constexpr int NP = KBITS == 3 ? 4 : KBITS;
   static_assert(KBITS >= 1 && KBITS <= 3, "key planes");
+  // The 32 KB LUT has the largest alignment, so it is laid out first, at address 0: a
+  // lookup's address is then its masked index itself, with no base to add per lookup.
+  // (Separate arrays, not one struct: the compiler then knows that the direct-to-LDS loads
+  // into the ring cannot alias the LUT or the other arrays, and waits for none of them.)
+  __shared__ __align__(32768) uint2 lut[4096];
   __shared__ __align__(16) uint8_t ring[R][NW][Gm::SLOT];
-  __shared__ uint2 lut[4096];
   __shared__ __align__(16) _Float16 pt_s[NW][16][40];
   __shared__ __align__(16) float coef_s[2][5][4];
   __shared__ float red_s[NW][3][kMfmaMaxG];
@@ -1819,6 +1819,22 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
   }
   __syncthreads();
 
+  // this lane's 4 heads' score coefficients: held in registers for the whole loop, except
+  // with 3-bit keys, whose two more digit-row vectors leave no registers for them (they are
+  // then read from LDS each tile)
+  constexpr bool kCoefRegs = KBITS < 3;
+  float K0[4], K1[4], K2[4], K3[4], K4[4];
+  auto load_coef = [&]() {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      K0[r] = coef_s[half][0][r];
+      K1[r] = coef_s[half][1][r];
+      K2[r] = NSN ? coef_s[half][2][r] : 0.0f;
+      K3[r] = coef_s[half][3][r];
+      K4[r] = coef_s[half][4][r];
+    }
+  };
+  if constexpr (kCoefRegs) load_coef();
   const int t_begin = split * a.chunk;
   const int t_end = min(a.length, t_begin + a.chunk);
   const size_t ubase = size_t(unit) * a.capacity;
@@ -1856,12 +1872,18 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
   uint32_t koff[Gm::NK];
 #pragma unroll
   for (int i = 0; i < Gm::NK; ++i) koff[i] = uint32_t(Gm::KCH * (64 * i + lane));
+  // the wave's first tile in each stream; tile k is a fixed stride further
+  const uint8_t *kb0 = a.kbits + (ubase + t_first) * Gm::KB;
+  const uint8_t *vb0 = vbase + size_t(t_first / kValueTile) * Gm::VT;
+  const uint8_t *kn0 = reinterpret_cast<const uint8_t *>(a.knorm) + (ubase + t_first) * Gm::KNR;
+  const uint8_t *vn0 = vnbase + (ubase + t_first) * (NSN ? 4 : 2);
   auto issue_dma = [&](int k, uint8_t *slot) {
     const int kk = k < nk ? k : nk - 1;
     const int t0 = t_first + TS * kk;
     const int nv = t_end - t0;   // valid tokens in the tile (1..32)
     const bool whole = nv >= 32;   // wave-uniform: no clamping needed
-    const uint8_t *ksrc = a.kbits + (ubase + t0) * Gm::KB;
+    const size_t tk0 = size_t(kk) * TS;   // the tile's first token, from the wave's first
+    const uint8_t *ksrc = kb0 + tk0 * Gm::KB;
     const int last = nv * Gm::KB / Gm::KCH - 1;
     constexpr int kchunks = Gm::KT / Gm::KCH;
 #pragma unroll
@@ -1871,7 +1893,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
         __builtin_amdgcn_global_load_lds(ksrc + o, slot + 64 * Gm::KCH * i, Gm::KCH, 0, 0);
       }
     }
-    const uint8_t *vsrc = vbase + size_t(t0 / kValueTile) * Gm::VT;
+    const uint8_t *vsrc = vb0 + (tk0 / kValueTile) * Gm::VT;
     constexpr int vchunks = Gm::VT / 16;
 #pragma unroll
     for (int i = 0; i < Gm::NV; ++i) {
@@ -1880,34 +1902,35 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
     }
     if constexpr (NSN) {
       // 32 key norm records of 8 bytes (64 dwords), 32 value norm records of 4 bytes
-      const uint8_t *kn = reinterpret_cast<const uint8_t *>(a.knorm) + (ubase + t0) * 8;
+      const uint8_t *kn = kn0 + tk0 * 8;
       const uint32_t tk = uint32_t(whole ? lane >> 1 : min(lane >> 1, nv - 1));
       __builtin_amdgcn_global_load_lds(kn + 8 * tk + 4 * uint32_t(lane & 1), slot + Gm::KN, 4, 0, 0);
       if (lane < 32) {
-        const uint8_t *vn4 = vnbase + (ubase + t0) * 4;
+        const uint8_t *vn4 = vn0 + tk0 * 4;
         __builtin_amdgcn_global_load_lds(vn4 + 4 * uint32_t(whole ? lane : min(lane, nv - 1)), slot + Gm::VN, 4, 0, 0);
       }
     } else {
     if (lane < 32) {
-      const uint8_t *kn = reinterpret_cast<const uint8_t *>(a.knorm + ubase + t0);
+      const uint8_t *kn = kn0 + tk0 * 4;
       __builtin_amdgcn_global_load_lds(kn + uint32_t(4 * (whole ? lane : min(lane, nv - 1))), slot + Gm::KN, 4, 0, 0);
     }
     if (lane < 17) {
       // value norms: 17 dwords from the 4-byte boundary at or below token t0's norm, none
       // past the dword holding the tile's last token (the region may end right there)
-      const size_t byte0 = (ubase + t0) * 2;
-      const size_t lastb = (ubase + t0 + nv - 1) * 2;
-      const uint32_t span = uint32_t((lastb & ~size_t(3)) - (byte0 & ~size_t(3)));
-      __builtin_amdgcn_global_load_lds(vnbase + (byte0 & ~size_t(3)) + min(uint32_t(4 * lane), span),
-                                       slot + Gm::VN, 4, 0, 0);
+      // (tiles are TS tokens = a multiple of 4 bytes of norms apart, so the dword offset of
+      // token t0's norm, r, is the same for all of the wave's tiles)
+      const uint8_t *v2 = vn0 + tk0 * 2;
+      const uint32_t r = uint32_t(reinterpret_cast<uintptr_t>(vn0)) & 3u;
+      const uint32_t span = (r + 2u * uint32_t(nv - 1)) & ~3u;
+      __builtin_amdgcn_global_load_lds(v2 - r + min(uint32_t(4 * lane), span), slot + Gm::VN, 4, 0, 0);
     }
     }
   };
 
   auto step = [&](int k, const uint8_t *slot, uint8_t *nxt) {
-    wait_lgkm0();                 // reads of the slot refilled below are complete
+    // every read of the slot refilled here was waited for inside its own read block
     issue_dma(k + R - 1, nxt);
-    if (a.scores)
+    if constexpr (SCORES)
       __builtin_amdgcn_s_waitcnt(0);
     else
       wait_vmcnt_le<(R - 1) * Gm::NDMA>();   // this tile's loads are the oldest still counted
@@ -1929,6 +1952,8 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
       const uint32_t vaddr = NSN ? sbase + Gm::VN + 4 * row : sbase + Gm::VN + uint32_t(((ubase + t0) * 2) & 3) + 2 * row;
       const uint32_t caddr = sbase + Gm::KT + vn * 12 + 4 * vidx;
 #if defined(__HIP_DEVICE_COMPILE__)
+      // The outputs are early-clobber ("=&v"): a read's destination must not share a
+      // register with an address that a later read of the block still uses.
       if constexpr (D >= 128) {
         asm volatile(
             "ds_read_b64 %0, %22\n"
@@ -1954,11 +1979,11 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
             "ds_read_b32 %20, %25 offset:1344\n"
             "ds_read_b32 %21, %25 offset:1348\n"
             "s_waitcnt lgkmcnt(0)\n"
-            : "=v"(kw[0]), "=v"(kw[1]), "=v"(kw[2]), "=v"(kw[3]), "=v"(nr), "=v"(vnb),
-              "=v"(vwr[0][0]), "=v"(vwr[0][1]), "=v"(vwr[1][0]), "=v"(vwr[1][1]), "=v"(vwr[2][0]),
-              "=v"(vwr[2][1]), "=v"(vwr[3][0]), "=v"(vwr[3][1]), "=v"(vwr[4][0]), "=v"(vwr[4][1]),
-              "=v"(vwr[5][0]), "=v"(vwr[5][1]), "=v"(vwr[6][0]), "=v"(vwr[6][1]), "=v"(vwr[7][0]),
-              "=v"(vwr[7][1])
+            : "=&v"(kw[0]), "=&v"(kw[1]), "=&v"(kw[2]), "=&v"(kw[3]), "=&v"(nr), "=&v"(vnb),
+              "=&v"(vwr[0][0]), "=&v"(vwr[0][1]), "=&v"(vwr[1][0]), "=&v"(vwr[1][1]), "=&v"(vwr[2][0]),
+              "=&v"(vwr[2][1]), "=&v"(vwr[3][0]), "=&v"(vwr[3][1]), "=&v"(vwr[4][0]), "=&v"(vwr[4][1]),
+              "=&v"(vwr[5][0]), "=&v"(vwr[5][1]), "=&v"(vwr[6][0]), "=&v"(vwr[6][1]), "=&v"(vwr[7][0]),
+              "=&v"(vwr[7][1])
             : "v"(kaddr), "v"(naddr), "v"(vaddr), "v"(caddr)
             : "memory");
       } else {
@@ -1979,9 +2004,9 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
             "ds_read_b32 %12, %17 offset:576\n"
             "ds_read_b32 %13, %17 offset:580\n"
             "s_waitcnt lgkmcnt(0)\n"
-            : "=v"(x0), "=v"(x1), "=v"(x2), "=v"(x3), "=v"(nr), "=v"(vnb),
-              "=v"(vwr[0][0]), "=v"(vwr[0][1]), "=v"(vwr[1][0]), "=v"(vwr[1][1]), "=v"(vwr[2][0]),
-              "=v"(vwr[2][1]), "=v"(vwr[3][0]), "=v"(vwr[3][1])
+            : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3), "=&v"(nr), "=&v"(vnb),
+              "=&v"(vwr[0][0]), "=&v"(vwr[0][1]), "=&v"(vwr[1][0]), "=&v"(vwr[1][1]), "=&v"(vwr[2][0]),
+              "=&v"(vwr[2][1]), "=&v"(vwr[3][0]), "=&v"(vwr[3][1])
             : "v"(kaddr), "v"(naddr), "v"(vaddr), "v"(caddr)
             : "memory");
         kw[0] = make_uint2(x0, 0u);
@@ -2046,29 +2071,16 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
           "ds_read_u16 %0, %2 offset:4\n"
           "ds_read_u16 %1, %3 offset:2\n"
           "s_waitcnt lgkmcnt(0)\n"
-          : "=v"(k1b), "=v"(v1b)
+          : "=&v"(k1b), "=&v"(v1b)
           : "v"(sbase + Gm::KN + 8 * row), "v"(sbase + Gm::VN + 4 * row)
           : "memory");
       ks1 = f16_bits_to_float(k1b);
       vs1 = f16_bits_to_float(v1b);
     }
-    const float4 k0 = *reinterpret_cast<const float4 *>(coef_s[half][0]);
-    const float4 k1 = *reinterpret_cast<const float4 *>(coef_s[half][1]);
-    const float4 k3 = *reinterpret_cast<const float4 *>(coef_s[half][3]);
-    const float4 k4 = *reinterpret_cast<const float4 *>(coef_s[half][4]);
-    const float K0[4] = {k0.x, k0.y, k0.z, k0.w}, K1[4] = {k1.x, k1.y, k1.z, k1.w};
-    const float K3[4] = {k3.x, k3.y, k3.z, k3.w}, K4[4] = {k4.x, k4.y, k4.z, k4.w};
-    float K2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if constexpr (NSN) {
-      const float4 k2 = *reinterpret_cast<const float4 *>(coef_s[half][2]);
-      K2[0] = k2.x;
-      K2[1] = k2.y;
-      K2[2] = k2.z;
-      K2[3] = k2.w;
-    }
     // lam = scale * score in the log2 domain; a token past the end gets -inf through the
     // innermost fma.  Heads h >= G (zero coefficients and digits) get lam = 0: their rows
     // are carried along and never written out.
+    if constexpr (!kCoefRegs) load_coef();
     const float vbias = valid ? 0.0f : -INFINITY;
     float lam[4], rel[4];
 #pragma unroll
@@ -2080,7 +2092,7 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
       lam[r] = fmaf(n16, fmaf(K1[r], S01, K0[r]), fmaf(rn16, fmaf(K3[r], S2, -K4[r]), vb));
       rel[r] = lam[r] - Mh[r];
     }
-    if (a.scores) {
+    if constexpr (SCORES) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * half + r;
@@ -3717,15 +3729,17 @@ int search_tiles(int n_db) { return (n_db + kSearchTile - 1) / kSearchTile; }
 using namespace tq;
 
 // MFMA-path kernels by head dim, key bits and NSN: the logits-only kernel or the split
-// decode kernel.
+// decode kernel (with or without the scores output, so that the loop carries no test of it).
 template <bool LOGITS, bool NSN>
 static void launch_mfma(int d, int bk, dim3 grid, dim3 blk, hipStream_t s, const MfmaArgs &ma) {
-#define TQ_MFMA(DD, BK)                                                          \
-  if (d == DD && bk == BK) {                                                     \
-    if constexpr (LOGITS)                                                        \
-      hipLaunchKernelGGL((k_logits<DD, BK, NSN>), grid, blk, 0, s, ma);          \
-    else                                                                         \
-      hipLaunchKernelGGL((k_decode_lds<DD, BK, NSN>), grid, blk, 0, s, ma);      \
+#define TQ_MFMA(DD, BK)                                                                 \
+  if (d == DD && bk == BK) {                                                            \
+    if constexpr (LOGITS)                                                               \
+      hipLaunchKernelGGL((k_logits<DD, BK, NSN>), grid, blk, 0, s, ma);                 \
+    else if (ma.scores)                                                                 \
+      hipLaunchKernelGGL((k_decode_lds<DD, BK, NSN, true>), grid, blk, 0, s, ma);       \
+    else                                                                                \
+      hipLaunchKernelGGL((k_decode_lds<DD, BK, NSN, false>), grid, blk, 0, s, ma);      \
   }
   TQ_MFMA(64, 1)
   TQ_MFMA(64, 2)
