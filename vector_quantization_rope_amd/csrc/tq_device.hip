@@ -20,6 +20,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <type_traits>
 
 #include "tq_internal.h"
 
@@ -2719,12 +2720,14 @@ __global__ __launch_bounds__(512, 2) void k_decode_polar(PolarArgs a) {
   __shared__ float nib[GM][D / 4][16];         // sum of S q over the set bits of a nibble
   __shared__ float s1q[GM];                    // sum of S q
   __shared__ float mstat[3][GM];
-  __shared__ float cs1[16][2];                 // level-1 centroids' cos, sin
+  __shared__ float2 cs1[16];                   // level-1 centroids' (cos, sin)
+  __shared__ float2 csh[L - 1][4];             // higher levels' (cos, sin): [level - 2][code]
   __shared__ uint32_t krs[CH * KWP];
   __shared__ uint32_t vrs[CH * VWP];
   __shared__ uint32_t kns[CH];
   __shared__ float vns[CH];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // the wave index is made wave-uniform, so that the decode role's quarter is a scalar choice
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = blockIdx.x, split = blockIdx.y;
   const int b = unit / a.kv_heads, g = unit % a.kv_heads, G = a.G, hq0 = g * G;
   const int t_begin = split * a.chunk, t_end = min(a.length, t_begin + a.chunk);
@@ -2754,16 +2757,11 @@ __global__ __launch_bounds__(512, 2) void k_decode_polar(PolarArgs a) {
   if (t_begin < t_end) fetch(t_begin);
   // decode role: lane = token, wave = key (kv = 0) or value (kv = 1) and quarter qq
   const int tt = lane, kv = wv >> 2, qq = wv & 3;
-  // cos, sin of the higher levels' centroids in registers: [level - 2][code]
-  float hc[L - 1][4], hs_[L - 1][4];
-#pragma unroll
-  for (int lv = 2; lv <= L; ++lv)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      hc[lv - 2][c] = a.pcs[((lv - 1) * 16 + c) * 2];
-      hs_[lv - 2][c] = a.pcs[((lv - 1) * 16 + c) * 2 + 1];
-    }
-  if (tid < 32) (&cs1[0][0])[tid] = a.pcs[tid];
+  if (tid < 16) cs1[tid] = make_float2(a.pcs[2 * tid], a.pcs[2 * tid + 1]);
+  if (tid < 4 * (L - 1)) {
+    const int lv = 2 + tid / 4, c = tid % 4;
+    csh[lv - 2][c] = make_float2(a.pcs[((lv - 1) * 16 + c) * 2], a.pcs[((lv - 1) * 16 + c) * 2 + 1]);
+  }
   for (int i = tid; i < GM * D; i += NT) {
     const int h = i / D, j = i % D;
     qr[h][j] = h < G ? a.qp[size_t(b * a.q_heads + hq0 + h) * a.qstride + j] : 0.0f;
@@ -2810,58 +2808,53 @@ __global__ __launch_bounds__(512, 2) void k_decode_polar(PolarArgs a) {
     }
     if (c0 + CH < t_end) fetch(c0 + CH);
     __syncthreads();
-    // ---- decode one quarter (rows past the chunk's end become zero)
-    {
+    // ---- decode one quarter (rows past the chunk's end become zero).  The quarter is a
+    // compile-time constant in each branch, so every code's bit position is too: a code is
+    // a shift and a mask of a known record dword, and its (cos, sin) one LDS read.
+    auto decode_quarter = [&](auto qc) {
+      constexpr int QQ = decltype(qc)::value;
       const uint32_t *w = kv ? &vrs[tt * VWP] : &krs[tt * KWP];
       // the quarter's level-1 nibbles and every 2-bit code, read together
       constexpr int N1 = D / 64;   // dwords of a quarter's level-1 nibbles
       uint32_t n1[N1], hi[NHI];
 #pragma unroll
-      for (int i = 0; i < N1; ++i) n1[i] = w[qq * N1 + i];
+      for (int i = 0; i < N1; ++i) n1[i] = w[QQ * N1 + i];
 #pragma unroll
       for (int i = 0; i < NHI; ++i) hi[i] = w[HI0 + i];
       auto code2 = [&](int bit) {   // a 2-bit code in the high dwords (bit >= 2 D)
-        const int wd = (bit >> 5) - HI0;
-        uint32_t x = hi[0];
-#pragma unroll
-        for (int i = 1; i < NHI; ++i) x = wd == i ? hi[i] : x;
-        return int((x >> (bit & 31)) & 3u);
-      };
-      auto pick = [](const float (&t)[4], int c) {
-        return c == 0 ? t[0] : c == 1 ? t[1] : c == 2 ? t[2] : t[3];
+        return int((hi[(bit >> 5) - HI0] >> (bit & 31)) & 3u);
       };
       const float scale = kv ? vns[tt] : 1.0f;
-      const int cT = code2(lbit(L, 0)), cH = code2(lbit(L - 1, qq >> 1));
+      const float2 cT = csh[L - 2][code2(lbit(L, 0))], cH = csh[L - 3][code2(lbit(L - 1, QQ >> 1))];
       float r[NQ / 2];
-      r[0] = scale * ((qq >> 1) ? pick(hs_[L - 2], cT) : pick(hc[L - 2], cT)) *
-             ((qq & 1) ? pick(hs_[L - 3], cH) : pick(hc[L - 3], cH));
+      r[0] = scale * ((QQ >> 1) ? cT.y : cT.x) * ((QQ & 1) ? cH.y : cH.x);
 #pragma unroll
       for (int lv = L - 2, n = 1; lv >= 2; --lv, n <<= 1) {
 #pragma unroll
         for (int i = n - 1; i >= 0; --i) {
-          const int c = code2(lbit(lv, qq * n + i));
+          const float2 cs = csh[lv - 2][code2(lbit(lv, QQ * n + i))];
           const float rr = r[i];
-          r[2 * i] = rr * pick(hc[lv - 2], c);
-          r[2 * i + 1] = rr * pick(hs_[lv - 2], c);
+          r[2 * i] = rr * cs.x;
+          r[2 * i + 1] = rr * cs.y;
         }
       }
       const bool live = tt < cn;
       if (kv) {
-        float *row = vr + tt * RS + qq * NQ;
+        float *row = vr + tt * RS + QQ * NQ;
 #pragma unroll
         for (int i = 0; i < NQ / 2; ++i) {
-          const int c = int((n1[i >> 3] >> (4 * (i & 7))) & 15u);
-          row[2 * i] = live ? r[i] * cs1[c][0] : 0.0f;
-          row[2 * i + 1] = live ? r[i] * cs1[c][1] : 0.0f;
+          const float2 cs = cs1[(n1[i >> 3] >> (4 * (i & 7))) & 15u];
+          row[2 * i] = live ? r[i] * cs.x : 0.0f;
+          row[2 * i + 1] = live ? r[i] * cs.y : 0.0f;
         }
       } else {
         // the key's quarter stays in registers: its share of every head's score
         float y[NQ];
 #pragma unroll
         for (int i = 0; i < NQ / 2; ++i) {
-          const int c = int((n1[i >> 3] >> (4 * (i & 7))) & 15u);
-          y[2 * i] = r[i] * cs1[c][0];
-          y[2 * i + 1] = r[i] * cs1[c][1];
+          const float2 cs = cs1[(n1[i >> 3] >> (4 * (i & 7))) & 15u];
+          y[2 * i] = r[i] * cs.x;
+          y[2 * i + 1] = r[i] * cs.y;
         }
 #pragma unroll
         for (int h = 0; h < GM; ++h) {
@@ -2869,16 +2862,22 @@ __global__ __launch_bounds__(512, 2) void k_decode_polar(PolarArgs a) {
             float d0 = 0.0f, d1 = 0.0f;
 #pragma unroll
             for (int j = 0; j < NQ; j += 4) {
-              const float4 qa = *reinterpret_cast<const float4 *>(&qr[h][qq * NQ + j]);
+              const float4 qa = *reinterpret_cast<const float4 *>(&qr[h][QQ * NQ + j]);
               d0 = fmaf(qa.x, y[j], d0);
               d1 = fmaf(qa.y, y[j + 1], d1);
               d0 = fmaf(qa.z, y[j + 2], d0);
               d1 = fmaf(qa.w, y[j + 3], d1);
             }
-            psk[qq][h][tt] = live ? d0 + d1 : 0.0f;
+            psk[QQ][h][tt] = live ? d0 + d1 : 0.0f;
           }
         }
       }
+    };
+    switch (qq) {
+      case 0: decode_quarter(std::integral_constant<int, 0>{}); break;
+      case 1: decode_quarter(std::integral_constant<int, 1>{}); break;
+      case 2: decode_quarter(std::integral_constant<int, 2>{}); break;
+      default: decode_quarter(std::integral_constant<int, 3>{}); break;
     }
     __syncthreads();
     // ---- scores: wave = head, lane = token
