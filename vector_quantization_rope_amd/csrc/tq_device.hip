@@ -2703,23 +2703,31 @@ struct PolarArgs {
 };
 
 template <int D>
-__global__ __launch_bounds__(512, 2) void k_decode_polar(PolarArgs a) {
+__global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
   // m = D QJL rows; 8 waves: decode by eighths of a token (key or value, one quarter of
-  // the coordinates), scores and softmax one head per wave, values by coordinate
-  constexpr int L = D == 128 ? 7 : 6, CH = 64, RS = D + 1, GM = 8, NT = 512;
+  // the coordinates), scores and softmax one head per wave, values on fp16 MFMA by blocks
+  // of 16 coordinates
+  constexpr int L = D == 128 ? 7 : 6, CH = 64, GM = 8, NT = 512;
   constexpr int VB = 3 * D / 8, KW = (3 * D / 8 + D / 8) / 4, VW = VB / 4;   // record dwords
   constexpr int KWP = KW + 1, VWP = VW + 1;     // odd LDS strides: one token per bank
-  constexpr int HS = NT / D, HPT = GM / HS;     // value phase: head slots per thread
   constexpr int NQ = D / 4;                     // coordinates per decode quarter
+  constexpr int NCB = D / 16, TP = CH + 8;      // value coordinate blocks; padded token rows
+  // p is carried as 256 p in the fp16 hi + lo parts (more of the small ones stay normal);
+  // the sums are scaled back at the end
+  constexpr float kPScale = 256.0f;
   constexpr int NKD = (CH * KW + NT - 1) / NT, NVD = (CH * VW + NT - 1) / NT;
   constexpr int HI0 = 2 * D / 32, NHI = KW - D / 32 - HI0;   // dwords of the 2-bit codes
   __shared__ __align__(16) float qr[GM][D];
   __shared__ float psk[4][GM][CH];              // key score parts by quarter
-  __shared__ float vr[CH * RS];
-  __shared__ __align__(16) float ps[GM][CH];
+  // value rows times the value norm as fp16 hi + lo, transposed ([coordinate][token]) so
+  // that an MFMA B operand (8 tokens of one coordinate) is one 16-byte read; and the
+  // softmax weights in the A operand's order: rows 0..7 the heads' hi parts, 8..15 lo
+  __shared__ __align__(16) _Float16 vth[D][TP];
+  __shared__ __align__(16) _Float16 vtl[D][TP];
+  __shared__ __align__(16) _Float16 pt[16][TP];
   __shared__ float nib[GM][D / 4][16];         // sum of S q over the set bits of a nibble
   __shared__ float s1q[GM];                    // sum of S q
-  __shared__ float mstat[3][GM];
+  __shared__ __align__(16) float mstat[3][GM];
   __shared__ float2 cs1[16];                   // level-1 centroids' (cos, sin)
   __shared__ float2 csh[L - 1][4];             // higher levels' (cos, sin): [level - 2][code]
   __shared__ uint32_t krs[CH * KWP];
@@ -2783,11 +2791,10 @@ __global__ __launch_bounds__(512, 2) void k_decode_polar(PolarArgs a) {
     mstat[1][tid] = 0.0f;
     mstat[2][tid] = 0.0f;
   }
-  for (int i = tid; i < GM * CH; i += NT) (&ps[0][0])[i] = 0.0f;
-  const int jv = tid % D, hsl = tid / D;
-  float acc[HPT];
-#pragma unroll
-  for (int k = 0; k < HPT; ++k) acc[k] = 0.0f;
+  for (int i = tid; i < 16 * TP; i += NT) (&pt[0][0])[i] = _Float16(0.0f);   // absent heads stay 0
+  // value MFMA role (waves below NCB): coordinate block wv, lane = (row or column, k group)
+  const int vn = lane & 15, vq = lane >> 4;
+  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
   auto lbit = [](int lv, int j) { return 2 * D + 2 * (D / 2 - (D >> (lv - 1)) + j); };
   for (int c0 = t_begin; c0 < t_end; c0 += CH) {
     const int cn = min(CH, t_end - c0);
@@ -2840,12 +2847,16 @@ __global__ __launch_bounds__(512, 2) void k_decode_polar(PolarArgs a) {
       }
       const bool live = tt < cn;
       if (kv) {
-        float *row = vr + tt * RS + QQ * NQ;
 #pragma unroll
         for (int i = 0; i < NQ / 2; ++i) {
           const float2 cs = cs1[(n1[i >> 3] >> (4 * (i & 7))) & 15u];
-          row[2 * i] = live ? r[i] * cs.x : 0.0f;
-          row[2 * i + 1] = live ? r[i] * cs.y : 0.0f;
+          const float v0 = live ? r[i] * cs.x : 0.0f, v1 = live ? r[i] * cs.y : 0.0f;
+          const _Float16 h0 = _Float16(v0), h1 = _Float16(v1);
+          const int c = QQ * NQ + 2 * i;
+          vth[c][tt] = h0;
+          vtl[c][tt] = _Float16(v0 - float(h0));
+          vth[c + 1][tt] = h1;
+          vtl[c + 1][tt] = _Float16(v1 - float(h1));
         }
       } else {
         // the key's quarter stays in registers: its share of every head's score
@@ -2896,7 +2907,6 @@ __global__ __launch_bounds__(512, 2) void k_decode_polar(PolarArgs a) {
         q1 += nib[h][k + 1][(sg[(k + 1) >> 3] >> (4 * ((k + 1) & 7))) & 15u];
       }
       const float sc = fmaf(n16, (s0 + s1) + (s2 + s3), a.qjl_scale * rn16 * fmaf(2.0f, q0 + q1, -s1q[h]));
-      ps[h][t] = sc;
       if (a.scores && t < cn) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.score_stride + c0 + t] = sc;
       // online softmax of this head over the chunk
       const float v = t < cn ? sc * a.scale_log2 : -INFINITY;
@@ -2904,7 +2914,10 @@ __global__ __launch_bounds__(512, 2) void k_decode_polar(PolarArgs a) {
       const float al = mold == -INFINITY ? 0.0f : exp2f(mold - mnew);
       const float p = t < cn ? exp2f(v - mnew) : 0.0f;
       const float l = wave_sum_dpp(p);
-      ps[h][t] = p;
+      const float ps_ = p * kPScale;
+      const _Float16 ph = _Float16(ps_);
+      pt[h][t] = ph;
+      pt[8 + h][t] = _Float16(ps_ - float(ph));
       if (lane == 0) {
         mstat[0][h] = mnew;
         mstat[1][h] = mstat[1][h] * al + l;
@@ -2912,39 +2925,45 @@ __global__ __launch_bounds__(512, 2) void k_decode_polar(PolarArgs a) {
       }
     }
     __syncthreads();
-    // ---- values: one read of vr per token serves all of this thread's head slots
-    {
-      float o[HPT];
+    // ---- values: acc[16 rows x 16 coordinates] += P[rows x tokens] V[tokens x coordinates]
+    // for coordinate block wv, with P and V each split into fp16 hi + lo (rows h and 8 + h
+    // carry P's parts, two MFMAs V's: every product above 2^-22 relative is kept)
+    if (wv < NCB) {
+      const float4 al4 = *reinterpret_cast<const float4 *>(&mstat[2][4 * (vq & 1)]);
+      acc[0] *= al4.x;
+      acc[1] *= al4.y;
+      acc[2] *= al4.z;
+      acc[3] *= al4.w;
 #pragma unroll
-      for (int k = 0; k < HPT; ++k) o[k] = acc[k] * mstat[2][hsl + k * HS];
-#pragma unroll 4
-      for (int t = 0; t < CH; t += 4) {
-        const float v0 = vr[t * RS + jv], v1 = vr[(t + 1) * RS + jv];
-        const float v2 = vr[(t + 2) * RS + jv], v3 = vr[(t + 3) * RS + jv];
-#pragma unroll
-        for (int k = 0; k < HPT; ++k) {
-          const float4 pp = *reinterpret_cast<const float4 *>(&ps[hsl + k * HS][t]);
-          o[k] = fmaf(pp.x, v0, o[k]);
-          o[k] = fmaf(pp.y, v1, o[k]);
-          o[k] = fmaf(pp.z, v2, o[k]);
-          o[k] = fmaf(pp.w, v3, o[k]);
-        }
+      for (int tb = 0; tb < CH / 32; ++tb) {
+        const v8h A = *reinterpret_cast<const v8h *>(&pt[vn][32 * tb + 8 * vq]);
+        const v8h Bh = *reinterpret_cast<const v8h *>(&vth[16 * wv + vn][32 * tb + 8 * vq]);
+        const v8h Bl = *reinterpret_cast<const v8h *>(&vtl[16 * wv + vn][32 * tb + 8 * vq]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
       }
-#pragma unroll
-      for (int k = 0; k < HPT; ++k) acc[k] = o[k];
     }
   }
-  // partial (rotated basis): acc, max (natural log), sum
+  // partial (rotated basis): the hi and lo rows of each head summed, max (natural log), sum
+  __syncthreads();
+  float *ys = &psk[0][0][0];   // [GM][D]: the key score parts are no longer needed
+  if (wv < NCB && vq < 2) {
 #pragma unroll
-  for (int k = 0; k < HPT; ++k) {
-    const int h = hsl + k * HS;
-    if (h < G) {
-      float *o = a.part + ((size_t(b) * a.q_heads + hq0 + h) * a.splits + split) * (D + 2);
-      o[jv] = acc[k];
-      if (jv == 0) {
-        o[D] = mstat[0][h] == -INFINITY ? -INFINITY : mstat[0][h] * 0.69314718055994531f;
-        o[D + 1] = mstat[1][h];
-      }
+    for (int j = 0; j < 4; ++j) ys[(4 * vq + j) * D + 16 * wv + vn] = acc[j];
+  }
+  __syncthreads();
+  if (wv < NCB && vq >= 2) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ys[(4 * (vq - 2) + j) * D + 16 * wv + vn] += acc[j];
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += NT) {
+    const int h = i / D, j = i % D;
+    float *o = a.part + ((size_t(b) * a.q_heads + hq0 + h) * a.splits + split) * (D + 2);
+    o[j] = ys[h * D + j] * (1.0f / kPScale);
+    if (j == 0) {
+      o[D] = mstat[0][h] == -INFINITY ? -INFINITY : mstat[0][h] * 0.69314718055994531f;
+      o[D + 1] = mstat[1][h];
     }
   }
 }
