@@ -2685,11 +2685,12 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
 // the key residual).  Per 64-token chunk of the block's range: the records come in with
 // 16-byte loads (the next chunk's in flight while this one is scored) and are staged in
 // LDS; four threads per token decode its angle tree, one quarter of the coordinates each
-// (the two top levels give the quarter's radius, its own subtree the rest), into fp32
-// rows of the rotated key direction and of the rotated value times its norm; the key
-// score is n <q_rot, yhat> plus the QJL term, whose sign-bit sum comes from a per-head
-// table over nibbles; then the online softmax and value sums of the window kernel.  The
-// sums stay in the rotated basis: the partials are the merge's usual input.
+// (the two top levels give the quarter's radius, its own subtree the rest).  A key
+// quarter is dotted with every head's rotated query in registers; a value quarter, times
+// the value norm, goes to LDS as fp16 hi + lo.  The key score is n <q_rot, yhat> plus the
+// QJL term, whose sign-bit sum comes from a per-head table over nibbles; then the online
+// softmax (one head per wave) and the value sums on fp16 MFMA.  The sums stay in the
+// rotated basis: the partials are the merge's usual input.
 struct PolarArgs {
   const uint8_t *krec;     // [units][capacity][kb]: 3 D / 8 angle bytes, m / 8 sign bytes
   const uint32_t *knorm;   // {fp16 n, fp16 |r|}
