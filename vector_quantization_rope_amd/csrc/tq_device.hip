@@ -20,7 +20,6 @@
 
 #include <cmath>
 #include <cstring>
-#include <type_traits>
 
 #include "tq_internal.h"
 
@@ -2691,6 +2690,12 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
 // QJL term, whose sign-bit sum comes from a per-head table over nibbles; then the online
 // softmax (one head per wave) and the value sums on fp16 MFMA.  The sums stay in the
 // rotated basis: the partials are the merge's usual input.
+// a compile-time int carried by a value (selects a templated lambda body)
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
+
 struct PolarArgs {
   const uint8_t *krec;     // [units][capacity][kb]: 3 D / 8 angle bytes, m / 8 sign bytes
   const uint32_t *knorm;   // {fp16 n, fp16 |r|}
@@ -2886,10 +2891,10 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
       }
     };
     switch (qq) {
-      case 0: decode_quarter(std::integral_constant<int, 0>{}); break;
-      case 1: decode_quarter(std::integral_constant<int, 1>{}); break;
-      case 2: decode_quarter(std::integral_constant<int, 2>{}); break;
-      default: decode_quarter(std::integral_constant<int, 3>{}); break;
+      case 0: decode_quarter(IntTag<0>{}); break;
+      case 1: decode_quarter(IntTag<1>{}); break;
+      case 2: decode_quarter(IntTag<2>{}); break;
+      default: decode_quarter(IntTag<3>{}); break;
     }
     __syncthreads();
     // ---- scores: wave = head, lane = token
