@@ -3537,10 +3537,11 @@ __global__ __launch_bounds__(512, 1) void k_search_mfma(SearchMfmaArgs a) {
 
 // ------------------------------------------------------------------ NSN means
 // [NSNQuant] section 1, the shift: o = mean over a unit's tokens of sqrt(d) x / ||x||,
-// keys rotary-embedded first.  k_nsn_partial: grid (units, slices); wave w of a block
-// takes tokens t0 + TPW w + 4 TPW i of its slice, lane j % H2 the pair (j, j + H2) of
-// token TPW-subgroup j / H2, with the fp64 RoPE angle stepped by 4 TPW theta per
-// iteration.  Sums in fp64, combined in a fixed order (deterministic).
+// keys rotary-embedded first.  k_nsn_partial: grid (units, slices); a token is spread over
+// LPT lanes, each holding NP rotary pairs (j, j + D/2) of it (two 4-element loads), so a
+// wave takes TPW tokens at once: wave w of a block takes tokens t0 + TPW (w + 4 i) + sub,
+// with the fp64 RoPE angles of its pairs stepped by 4 TPW theta per iteration.  Sums in
+// fp64, combined in a fixed order (deterministic).
 struct NsnArgs {
   const void *k, *v;
   double *part;   // [units][slices][2][D]
@@ -3548,106 +3549,154 @@ struct NsnArgs {
   float rope_base;
 };
 
-// Sum of a double over each row of 16 lanes, in every lane of the row (DPP: quad swaps,
-// then rotations by 4 and 8 within the row), and its total over rows lo..lo+nr-1 read
-// lane by lane (wave-uniform).
-__device__ __forceinline__ double row_sum_f64(double x) {
+// Raw bits of 4 consecutive input elements starting at element `off` (one 8-byte load for
+// 16-bit types, 16 bytes for fp32; off * sizeof(element) is a multiple of that size).
+template <int DT>
+struct Raw4 {
+  using T = uint2;
+};
+template <>
+struct Raw4<TQ_F32> {
+  using T = uint4;
+};
+template <int DT>
+__device__ __forceinline__ typename Raw4<DT>::T load_raw4(const void *base, size_t off) {
+  if constexpr (DT == TQ_F32)
+    return *reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + off);
+  else
+    return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(base) + off);
+}
+template <int DT>
+__device__ __forceinline__ void raw4_to_f64(const typename Raw4<DT>::T &r, double *x) {
+  if constexpr (DT == TQ_F32) {
+    x[0] = __uint_as_float(r.x);
+    x[1] = __uint_as_float(r.y);
+    x[2] = __uint_as_float(r.z);
+    x[3] = __uint_as_float(r.w);
+  } else if constexpr (DT == TQ_BF16) {
+    x[0] = __uint_as_float(r.x << 16);
+    x[1] = __uint_as_float(r.x & 0xFFFF0000u);
+    x[2] = __uint_as_float(r.y << 16);
+    x[3] = __uint_as_float(r.y & 0xFFFF0000u);
+  } else {
+    x[0] = f16_bits_to_float(r.x & 0xFFFFu);
+    x[1] = f16_bits_to_float(r.x >> 16);
+    x[2] = f16_bits_to_float(r.y & 0xFFFFu);
+    x[3] = f16_bits_to_float(r.y >> 16);
+  }
+}
+
+// Sum of a double over each aligned group of N lanes (N = 8 or 16), in every lane of the
+// group (DPP: quad swaps, then the half-row mirror, then a rotation by 8 in the row).
+template <int N>
+__device__ __forceinline__ double group_sum_f64(double x) {
+  static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
   x += dpp_f64<0xB1>(x);    // quad_perm [1,0,3,2]
   x += dpp_f64<0x4E>(x);    // quad_perm [2,3,0,1]
-  x += dpp_f64<0x124>(x);   // row_ror:4
-  x += dpp_f64<0x128>(x);   // row_ror:8
+  x += dpp_f64<0x141>(x);   // row_half_mirror: the other quad of the half row
+  if constexpr (N == 16) x += dpp_f64<0x128>(x);   // row_ror:8: the other half row
   return x;
-}
-__device__ __forceinline__ double readlane_f64(double x, int l) {
-  const uint64_t b = __builtin_bit_cast(uint64_t, x);
-  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b)), l));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(b >> 32)), l));
-  return __builtin_bit_cast(double, (uint64_t(hi) << 32) | lo);
 }
 
 template <int D, int DT>
 __global__ __launch_bounds__(256) void k_nsn_partial(NsnArgs a) {
-  constexpr int H2 = D / 2, TPW = 64 / H2, STEP = 4 * TPW;
+  constexpr int H2 = D / 2, NP = 4, LPT = H2 / NP, TPW = 64 / LPT, STEP = 4 * TPW;
+  constexpr int U = 4;   // iterations whose loads are issued together
   __shared__ double acc_s[4][2][D];
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  const int j = lane % H2, sub = lane / H2;
+  const int jg = lane % LPT, sub = lane / LPT, j0 = NP * jg;
   const int unit = blockIdx.x, sl = blockIdx.y;
   const int t0 = sl * a.per, t1 = min(a.n, t0 + a.per);
   const bool rope = a.rope_base != 0.0f;
   const double sqd = sqrt(double(D));
-  double c = 1.0, sn = 0.0, cs = 1.0, ss = 0.0;
-  if (rope) {
-    const double theta = pow(double(a.rope_base), -2.0 * double(j) / double(D));
-    sincos(double(a.start + t0 + TPW * wv + sub) * theta, &sn, &c);
-    sincos(double(STEP) * theta, &ss, &cs);
+  // this lane's pairs: (cos, sin) at its current token and the step rotation
+  double c[NP], sn[NP], cs[NP], ss[NP];
+#pragma unroll
+  for (int e = 0; e < NP; ++e) {
+    c[e] = 1.0;
+    sn[e] = 0.0;
+    cs[e] = 1.0;
+    ss[e] = 0.0;
+    if (rope) {
+      const double theta = pow(double(a.rope_base), -2.0 * double(j0 + e) / double(D));
+      sincos(double(a.start + t0 + TPW * wv + sub) * theta, &sn[e], &c[e]);
+      sincos(double(STEP) * theta, &ss[e], &cs[e]);
+    }
   }
-  double ak0 = 0.0, ak1 = 0.0, av0 = 0.0, av1 = 0.0;
+  double ak[2 * NP], av[2 * NP];
+#pragma unroll
+  for (int e = 0; e < 2 * NP; ++e) ak[e] = av[e] = 0.0;
   const size_t ub = size_t(unit) * a.n;
-  constexpr int U = 4;   // tokens per lane per iteration: their loads are issued together
+  using R4 = typename Raw4<DT>::T;
   for (int tb = t0 + TPW * wv; tb < t1; tb += U * STEP) {   // wave-uniform
-    double k0[U], k1[U], v0[U], v1[U];
+    R4 rk[U][2], rv[U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int t = tb + u * STEP + sub;
-      k0[u] = k1[u] = v0[u] = v1[u] = 0.0;
-      if (t < t1) {
-        k0[u] = load_d<DT>(a.k, (ub + t) * D + j);
-        k1[u] = load_d<DT>(a.k, (ub + t) * D + j + H2);
-        v0[u] = load_d<DT>(a.v, (ub + t) * D + j);
-        v1[u] = load_d<DT>(a.v, (ub + t) * D + j + H2);
-      }
+      const size_t o = (ub + size_t(t < t1 ? t : t0)) * D + j0;
+      rk[u][0] = load_raw4<DT>(a.k, o);
+      rk[u][1] = load_raw4<DT>(a.k, o + H2);
+      rv[u][0] = load_raw4<DT>(a.v, o);
+      rv[u][1] = load_raw4<DT>(a.v, o + H2);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      double x0 = k0[u], x1 = k1[u];
+      const bool live = tb + u * STEP + sub < t1;
+      double x[2 * NP], y[2 * NP];
+      raw4_to_f64<DT>(rk[u][0], x);
+      raw4_to_f64<DT>(rk[u][1], x + NP);
+      raw4_to_f64<DT>(rv[u][0], y);
+      raw4_to_f64<DT>(rv[u][1], y + NP);
       if (rope) {
-        const double r0 = x0 * c - x1 * sn, r1 = x0 * sn + x1 * c;
-        x0 = r0;
-        x1 = r1;
-        const double cn = c * cs - sn * ss;
-        sn = sn * cs + c * ss;
-        c = cn;
-      }
-      // squared norms over the token's H2 lanes: row sums, then the rows of the token
-      double nk = row_sum_f64(fma(x0, x0, x1 * x1)), nv = row_sum_f64(fma(v0[u], v0[u], v1[u] * v1[u]));
-      {
-        const double k01 = readlane_f64(nk, 0) + readlane_f64(nk, 16);
-        const double k23 = readlane_f64(nk, 32) + readlane_f64(nk, 48);
-        const double v01 = readlane_f64(nv, 0) + readlane_f64(nv, 16);
-        const double v23 = readlane_f64(nv, 32) + readlane_f64(nv, 48);
-        if constexpr (TPW == 1) {
-          nk = k01 + k23;
-          nv = v01 + v23;
-        } else {
-          nk = sub ? k23 : k01;
-          nv = sub ? v23 : v01;
+#pragma unroll
+        for (int e = 0; e < NP; ++e) {
+          const double r0 = x[e] * c[e] - x[NP + e] * sn[e], r1 = x[e] * sn[e] + x[NP + e] * c[e];
+          x[e] = r0;
+          x[NP + e] = r1;
+          const double cn = c[e] * cs[e] - sn[e] * ss[e];
+          sn[e] = sn[e] * cs[e] + c[e] * ss[e];
+          c[e] = cn;
         }
       }
+      double nk = 0.0, nv = 0.0;
+#pragma unroll
+      for (int e = 0; e < 2 * NP; ++e) {
+        nk = fma(x[e], x[e], nk);
+        nv = fma(y[e], y[e], nv);
+      }
+      nk = group_sum_f64<LPT>(nk);
+      nv = group_sum_f64<LPT>(nv);
       // sqrt(d) / ||x||: hardware reciprocal square root refined by two Newton steps (each
       // squares the relative error; the mean is rounded to fp32)
-      double rk = __builtin_amdgcn_rsq(nk), rv = __builtin_amdgcn_rsq(nv);
-      rk *= fma(-0.5 * nk * rk, rk, 1.5);
-      rv *= fma(-0.5 * nv * rv, rv, 1.5);
-      rk *= fma(-0.5 * nk * rk, rk, 1.5);
-      rv *= fma(-0.5 * nv * rv, rv, 1.5);
-      const double fk = nk > 0.0 ? sqd * rk : 0.0, fv = nv > 0.0 ? sqd * rv : 0.0;
-      ak0 = fma(x0, fk, ak0);
-      ak1 = fma(x1, fk, ak1);
-      av0 = fma(v0[u], fv, av0);
-      av1 = fma(v1[u], fv, av1);
+      double rk_ = __builtin_amdgcn_rsq(nk), rv_ = __builtin_amdgcn_rsq(nv);
+      rk_ *= fma(-0.5 * nk * rk_, rk_, 1.5);
+      rv_ *= fma(-0.5 * nv * rv_, rv_, 1.5);
+      rk_ *= fma(-0.5 * nk * rk_, rk_, 1.5);
+      rv_ *= fma(-0.5 * nv * rv_, rv_, 1.5);
+      const double fk = live && nk > 0.0 ? sqd * rk_ : 0.0, fv = live && nv > 0.0 ? sqd * rv_ : 0.0;
+#pragma unroll
+      for (int e = 0; e < 2 * NP; ++e) {
+        ak[e] = fma(x[e], fk, ak[e]);
+        av[e] = fma(y[e], fv, av[e]);
+      }
     }
   }
-  if constexpr (TPW == 2) {
-    ak0 += __shfl_xor(ak0, 32, 64);
-    ak1 += __shfl_xor(ak1, 32, 64);
-    av0 += __shfl_xor(av0, 32, 64);
-    av1 += __shfl_xor(av1, 32, 64);
-  }
+  // the wave's token groups: lanes with the same pairs, in a fixed order
+#pragma unroll
+  for (int msk = LPT; msk < 64; msk <<= 1)
+#pragma unroll
+    for (int e = 0; e < 2 * NP; ++e) {
+      ak[e] += __shfl_xor(ak[e], msk, 64);
+      av[e] += __shfl_xor(av[e], msk, 64);
+    }
   if (sub == 0) {
-    acc_s[wv][0][j] = ak0;
-    acc_s[wv][0][j + H2] = ak1;
-    acc_s[wv][1][j] = av0;
-    acc_s[wv][1][j + H2] = av1;
+#pragma unroll
+    for (int e = 0; e < NP; ++e) {
+      acc_s[wv][0][j0 + e] = ak[e];
+      acc_s[wv][0][H2 + j0 + e] = ak[NP + e];
+      acc_s[wv][1][j0 + e] = av[e];
+      acc_s[wv][1][H2 + j0 + e] = av[NP + e];
+    }
   }
   __syncthreads();
   for (int i = tid; i < 2 * D; i += 256) {
