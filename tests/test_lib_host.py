@@ -65,14 +65,22 @@ def test_codec_tables_match_oracle(tq, O, d, m, seed):
     off_st = off_s + ((4 * m * d + 255) // 256) * 256
     ST = blob[off_st:off_st + 4 * m * d].view(np.float32).reshape(d, m)
     np.testing.assert_array_equal(ST, S.T)
-    # three bf16 parts after S^T, summing exactly to S, each the nearest bf16 of what is left
+    # three fp16 parts after S^T, each the nearest fp16 of what is left: their sum is S
+    # exactly where |S| >= 1/2 (the last remainder is a multiple of the fp16 subnormal
+    # step 2^-24) and within half that step elsewhere
     off_b = off_st + ((4 * m * d + 255) // 256) * 256
     step = ((2 * m * d + 255) // 256) * 256
-    parts = [(blob[off_b + i * step: off_b + i * step + 2 * m * d].view(np.uint16).astype(np.uint32) << 16)
-             .view(np.float32).reshape(m, d).astype(np.float64) for i in range(3)]
-    np.testing.assert_array_equal(parts[0] + parts[1] + parts[2], S.astype(np.float64))
-    assert np.all(np.abs(parts[1]) <= np.abs(parts[0]) * 2.0 ** -8)
-    assert np.all(np.abs(parts[2]) <= np.abs(parts[1]) * 2.0 ** -8)
+    parts = [blob[off_b + i * step: off_b + i * step + 2 * m * d].view(np.float16).reshape(m, d)
+             .astype(np.float64) for i in range(3)]
+    S64 = S.astype(np.float64)
+    rest = S64.copy()
+    for p in parts:
+        np.testing.assert_array_equal(p, rest.astype(np.float16).astype(np.float64))
+        rest = rest - p
+    total = parts[0] + parts[1] + parts[2]
+    big = np.abs(S64) >= 0.5
+    np.testing.assert_array_equal(total[big], S64[big])
+    assert np.all(np.abs(total - S64) <= 2.0 ** -25)
 
 
 def test_cache_layout_matches_oracle(tq, O):

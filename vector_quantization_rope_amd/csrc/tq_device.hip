@@ -95,7 +95,7 @@ __device__ __forceinline__ void fwht_regs(T *x) {
 
 struct CodecPtrs {
   const float *ck, *tk, *cv, *tv, *D, *S, *ST;
-  const __bf16 *Sb[3];   // S split exactly into three bf16 parts, each [m][d]
+  const _Float16 *Sh[3];   // S split into three fp16 parts, each [m][d]
   const float *pcs;      // PolarQuant: cos, sin of each angle centroid, [level - 1][16][2]
   const double *pt;      // PolarQuant: angle boundaries, [level - 1][16]
   int block;
@@ -113,7 +113,7 @@ CodecPtrs codec_ptrs(const void *codec_dev, int d, int bits_k, int bits_v, int m
   p.D = reinterpret_cast<const float *>(b + L.D);
   p.S = reinterpret_cast<const float *>(b + L.S);
   p.ST = reinterpret_cast<const float *>(b + L.ST);
-  for (int i = 0; i < 3; ++i) p.Sb[i] = reinterpret_cast<const __bf16 *>(b + L.Sb[i]);
+  for (int i = 0; i < 3; ++i) p.Sh[i] = reinterpret_cast<const _Float16 *>(b + L.Sh[i]);
   p.pcs = reinterpret_cast<const float *>(b + L.pcs);
   p.pt = reinterpret_cast<const double *>(b + L.pt);
   p.block = L.block;
@@ -184,7 +184,7 @@ struct QuantArgs {
 };
 
 typedef float v16f __attribute__((ext_vector_type(16)));
-typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 template <int DT>
@@ -549,15 +549,15 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   constexpr int HC = D / 8;     // coordinates per chunk
   constexpr int C = 2 * HC;     // coordinates per lane
   constexpr int W = D / 32;     // dwords per plane
-  constexpr int RS = D + 8;     // padded residual row (bf16 elements)
+  constexpr int RS = D + 8;     // padded residual row (fp16 elements)
   constexpr int ROPE_BYTES = 64 * H * 16;
-  constexpr int R_BYTES = 3 * 64 * RS * 2;
+  constexpr int R_BYTES = 2 * 64 * RS * 2;
   constexpr int U_BYTES = ROPE_BYTES > R_BYTES ? ROPE_BYTES : R_BYTES;
   __shared__ __align__(16) unsigned char u_s[U_BYTES];   // RoPE table, later residuals
   __shared__ __align__(16) uint8_t vcode_s[64][D];
   __shared__ float cb_s[4][kMaxCodes];
   double2 *rope_s = reinterpret_cast<double2 *>(u_s);   // [64][H]
-  __bf16 *r_s = reinterpret_cast<__bf16 *>(u_s);         // [3 parts][64][RS]
+  _Float16 *r_s = reinterpret_cast<_Float16 *>(u_s);     // [2 parts][64][RS]
 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
   const int slot = wv * 16 + (lane >> 2), q = lane & 3;
@@ -738,23 +738,27 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   __syncthreads();   // every wave is done with the RoPE table before residuals overwrite it
   {
     // residual r_H = H D x' - fp16(n) sqrt(B) c = sqrt(B) r (same signs of S r), rounded
-    // to fp32 and split exactly into three bf16 parts
+    // to fp32, scaled by a power of two that brings the token's largest |r_j| into
+    // [2^13, 2^14) (the signs of S r do not change), and split into fp16 hi + lo parts
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < C; ++e) amax = fmaxf(amax, fabsf(float(x[e])));
+    amax = fmaxf(amax, __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(amax))));
+    amax = fmaxf(amax, __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(amax))));
+    const float rscale = amax > 0.0f ? __builtin_ldexpf(1.0f, 14 - __builtin_amdgcn_frexp_expf(amax)) : 1.0f;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      v8bf part[3][HC / 8];
+      v8h part[2][HC / 8];
 #pragma unroll
       for (int e = 0; e < HC; ++e) {
-        float rest = float(x[c * HC + e]);
-#pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          const __bf16 b = (__bf16)rest;
-          part[k][e / 8][e % 8] = b;
-          rest -= float(b);
-        }
+        const float rr = float(x[c * HC + e]) * rscale;
+        const _Float16 hv = _Float16(rr);
+        part[0][e / 8][e % 8] = hv;
+        part[1][e / 8][e % 8] = _Float16(rr - float(hv));
       }
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        v8bf *dst = reinterpret_cast<v8bf *>(r_s + (k * 64 + slot) * RS + c * H + HC * q);
+      for (int k = 0; k < 2; ++k) {
+        v8h *dst = reinterpret_cast<v8h *>(r_s + (k * 64 + slot) * RS + c * H + HC * q);
 #pragma unroll
         for (int i = 0; i < HC / 8; ++i) dst[i] = part[k][i];
       }
@@ -844,11 +848,11 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
 
   // ------------------------------------------------------------ QJL signs: z = S r
   // z^T[32 rows x 64 tokens] per 32-row block of S, both 32-token halves sharing the S
-  // operand, on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with both operands split exactly into
-  // three bf16 parts: the six products down to 2^-16 relative (hi.hi, hi.mid, mid.hi,
-  // hi.lo, lo.hi, mid.mid) are exact in fp32 and accumulate in fp32.  That keeps the
-  // accuracy of fp32 MFMA with six bf16 MFMAs per 16-wide slice of k instead of eight
-  // fp32 ones (v_mfma_f32_32x32x2f32), about 2.7x fewer MFMA cycles.
+  // operand, on fp16 MFMA (v_mfma_f32_32x32x16_f16): S in three fp16 parts (hi, mid, lo),
+  // the scaled residual in two (hi, lo).  The four products hi.hi, mid.hi, hi.lo and
+  // lo.hi leave out only mid.lo and lo.lo (2^-22 and 2^-33 of the leading term), and the
+  // residual's own split costs 2^-23: z to about 2^-22 relative, which moves a sign only
+  // for |z| a few 1e-7 of |r|, against the 2^-24 of fp32 MFMA at half the MFMA cycles.
   // Step i contracts k = 16 i + 8 (lane / 32) + 0..7 on both operands.
   {
     const int mt_n = a.m / 32;
@@ -857,31 +861,30 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
       v16f acc0 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       v16f acc1 = acc0;
       const size_t srow = size_t(32 * mt + (lane & 31)) * D + 8 * half;
-      const __bf16 *r0 = r_s + (lane & 31) * RS + 8 * half;
-      const __bf16 *r1 = r0 + 32 * RS;
+      const _Float16 *r0 = r_s + (lane & 31) * RS + 8 * half;
+      const _Float16 *r1 = r0 + 32 * RS;
       // the next step's S slices are requested one step ahead
       constexpr int NS = D / 16;
-      v8bf sa[3];
+      v8h sa[3];
 #pragma unroll
-      for (int k = 0; k < 3; ++k) sa[k] = *reinterpret_cast<const v8bf *>(a.cp.Sb[k] + srow);
+      for (int k = 0; k < 3; ++k) sa[k] = *reinterpret_cast<const v8h *>(a.cp.Sh[k] + srow);
 #pragma unroll 2
       for (int i = 0; i < NS; ++i) {
-        v8bf ra[3], rb[3], sn[3];
+        v8h ra[2], rb[2], sn[3];
         const int inext = i + 1 < NS ? i + 1 : i;
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          sn[k] = *reinterpret_cast<const v8bf *>(a.cp.Sb[k] + srow + 16 * inext);
-          ra[k] = *reinterpret_cast<const v8bf *>(r0 + k * 64 * RS + 16 * i);
-          rb[k] = *reinterpret_cast<const v8bf *>(r1 + k * 64 * RS + 16 * i);
+        for (int k = 0; k < 3; ++k) sn[k] = *reinterpret_cast<const v8h *>(a.cp.Sh[k] + srow + 16 * inext);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          ra[k] = *reinterpret_cast<const v8h *>(r0 + k * 64 * RS + 16 * i);
+          rb[k] = *reinterpret_cast<const v8h *>(r1 + k * 64 * RS + 16 * i);
         }
-#define TQ_SR(A, B)                                                              \
-  acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[A], ra[B], acc0, 0, 0, 0); \
-  acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[A], rb[B], acc1, 0, 0, 0)
+#define TQ_SR(A, B)                                                             \
+  acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[A], ra[B], acc0, 0, 0, 0); \
+  acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[A], rb[B], acc1, 0, 0, 0)
         TQ_SR(2, 0);
-        TQ_SR(0, 2);
-        TQ_SR(1, 1);
-        TQ_SR(1, 0);
         TQ_SR(0, 1);
+        TQ_SR(1, 0);
         TQ_SR(0, 0);
 #undef TQ_SR
 #pragma unroll
@@ -1313,7 +1316,6 @@ __global__ __launch_bounds__(kDecThreads) void k_decode_split(DecodeArgs a) {
 // exact).  Accumulation is fp32 in the rotated basis; the combine applies Pi^T.
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kMfmaMaxG = 8;
 constexpr int kQpackCoef = 8;   // floats per head: k0..k4, padding

@@ -74,7 +74,7 @@ CodecLayout codec_layout(int d, int bits_k, int bits_v, int m) {
   L.S = cur; cur = align256(cur + size_t(m) * size_t(d) * 4);
   L.ST = cur; cur = align256(cur + size_t(m) * size_t(d) * 4);
   for (int i = 0; i < 3; ++i) {
-    L.Sb[i] = cur;
+    L.Sh[i] = cur;
     cur = align256(cur + size_t(m) * size_t(d) * 2);
   }
   L.pcs = cur;
@@ -83,21 +83,6 @@ CodecLayout codec_layout(int d, int bits_k, int bits_v, int m) {
   cur = align256(cur + size_t(kPolarLevels) * kPolarCodes * 8);
   L.total = cur;
   return L;
-}
-
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-static uint16_t bf16_rne(float x) {
-  uint32_t u;
-  std::memcpy(&u, &x, 4);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
-
-static float bf16_value(uint16_t b) {
-  const uint32_t u = uint32_t(b) << 16;
-  float f;
-  std::memcpy(&f, &u, 4);
-  return f;
 }
 
 double round_fp16(double x, uint16_t *bits_out) {
@@ -397,8 +382,8 @@ tq_status tq_codec_build(const tq_codec_desc *desc, void *host_out, size_t bytes
     D[j] = (splitmix64(desc->seed, kStreamSigns + uint64_t(j)) >> 63) ? -1.0f : 1.0f;
   float *S = reinterpret_cast<float *>(base + L.S);
   float *ST = reinterpret_cast<float *>(base + L.ST);
-  uint16_t *Sb[3];
-  for (int i = 0; i < 3; ++i) Sb[i] = reinterpret_cast<uint16_t *>(base + L.Sb[i]);
+  uint16_t *Sh[3];
+  for (int i = 0; i < 3; ++i) Sh[i] = reinterpret_cast<uint16_t *>(base + L.Sh[i]);
   for (int i = 0; i < m; ++i) {
     for (int j = 0; j < d; ++j) {
       const uint64_t n = uint64_t(i) * uint64_t(d) + uint64_t(j);
@@ -408,13 +393,15 @@ tq_status tq_codec_build(const tq_codec_desc *desc, void *host_out, size_t bytes
       const float zf = float(z);
       S[size_t(i) * d + j] = zf;
       ST[size_t(j) * m + i] = zf;
-      // exact three-part bf16 split: each part is the remainder rounded to 8 significant
-      // bits; 24 bits of fp32 leave nothing after the third part
-      float rest = zf;
+      // three-part fp16 split: each part is the remainder rounded to fp16 (11 significant
+      // bits); exact when |S| >= 1/2, where the last remainder is a multiple of the fp16
+      // subnormal step, else within half of that step
+      double rest = double(zf);
       for (int k = 0; k < 3; ++k) {
-        const uint16_t b = bf16_rne(rest);
-        Sb[k][size_t(i) * d + j] = b;
-        rest -= bf16_value(b);
+        uint16_t hb = 0;
+        const double hv = round_fp16(rest, &hb);
+        Sh[k][size_t(i) * d + j] = hb;
+        rest -= hv;
       }
     }
   }

@@ -37,7 +37,7 @@ constexpr int kPolarCodes = 16;
 struct CodecLayout {
   // byte offsets inside the codec table
   size_t ck = 0, tk = 0, cv = 0, tv = 0, D = 0, S = 0, ST = 0, total = 0;
-  size_t Sb[3] = {0, 0, 0};   // S = Sb[0] + Sb[1] + Sb[2] exactly, each part bf16
+  size_t Sh[3] = {0, 0, 0};   // S = Sh[0] + Sh[1] + Sh[2], fp16 parts (exact for |S| >= 1/2)
   size_t pcs = 0;   // fp32 [kPolarLevels][kPolarCodes][2]: cos, sin of each angle centroid
   size_t pt = 0;    // fp64 [kPolarLevels][kPolarCodes]: angle boundaries (level l at l - 1)
   int block = 0;
