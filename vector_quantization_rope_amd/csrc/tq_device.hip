@@ -2704,10 +2704,11 @@ struct PolarArgs {
   const uint8_t *vrec;     // [units][capacity][3 D / 8]
   const uint16_t *vnorm;
   const float *qp;         // query rows: Pi RoPE(q) [D], S q [m], sum q_rot, sum S q
+  const uint8_t *qpack;    // per unit: int8 digit rows (the S q rows are used) and coefficients
   const float *pcs;        // cos, sin of the angle centroids [level - 1][16][2]
   float *part, *scores;
   int kb, capacity, length, chunk, splits, kv_heads, q_heads, G, m, qstride, score_stride;
-  float scale_log2, qjl_scale;
+  float scale_log2;
 };
 
 template <int D>
@@ -2733,8 +2734,8 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
   __shared__ __align__(16) _Float16 vth[D][TP];
   __shared__ __align__(16) _Float16 vtl[D][TP];
   __shared__ __align__(16) _Float16 pt[16][TP];
-  __shared__ float nib[GM][D / 4][16];         // sum of S q over the set bits of a nibble
-  __shared__ float s1q[GM];                    // sum of S q
+  __shared__ float qj[GM][CH];                 // QJL term of every (head, token) of the chunk
+  __shared__ float qjc[2][GM];                 // its coefficients: 2 qjl 2^16 / 2^e and qjl sum S q
   __shared__ __align__(16) float mstat[3][GM];
   __shared__ float2 cs1[16];                   // level-1 centroids' (cos, sin)
   __shared__ float2 csh[L - 1][4];             // higher levels' (cos, sin): [level - 2][code]
@@ -2782,19 +2783,19 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
     const int h = i / D, j = i % D;
     qr[h][j] = h < G ? a.qp[size_t(b * a.q_heads + hq0 + h) * a.qstride + j] : 0.0f;
   }
-  for (int i = tid; i < GM * (D / 4) * 16; i += NT) {
-    const int h = i / (D / 4 * 16), k = (i / 16) % (D / 4), v = i % 16;
-    float acc = 0.0f;
-    if (h < G) {
-      const float *sq = a.qp + size_t(b * a.q_heads + hq0 + h) * a.qstride + D;
+  // the S q digit rows of this unit's heads (the int8 MFMA A operand of the QJL sums, rows
+  // digit * 8 + head) and the two QJL coefficients per head (zero for absent heads)
+  const uint8_t *qpk = a.qpack + size_t(unit) * qpack_unit_bytes(D);
+  v4i As[D / 32];
+  {
+    const v4i *src = reinterpret_cast<const v4i *>(qpk);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if ((v >> e) & 1) acc += sq[4 * k + e];
-    }
-    nib[h][k][v] = acc;
+    for (int c = 0; c < D / 32; ++c) As[c] = src[((kSqVec * 32 + (lane & 31)) * 2 + (lane >> 5)) * (D / 32) + c];
   }
   if (tid < GM) {
-    s1q[tid] = tid < G ? a.qp[size_t(b * a.q_heads + hq0 + tid) * a.qstride + D + D + 1] : 0.0f;
+    const float *coef = reinterpret_cast<const float *>(qpk + size_t(kQpackVecs) * 32 * 2 * (D / 32) * 16);
+    qjc[0][tid] = coef[tid * kQpackCoef + 3];
+    qjc[1][tid] = coef[tid * kQpackCoef + 4];
     mstat[0][tid] = -INFINITY;
     mstat[1][tid] = 0.0f;
     mstat[2][tid] = 0.0f;
@@ -2898,23 +2899,39 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
       case 2: decode_quarter(IntTag<2>{}); break;
       default: decode_quarter(IntTag<3>{}); break;
     }
+    // ---- the QJL sums of 32-token tile qq, by value waves 0 and 1: the sign bits as int8
+    // bytes (bit e of each nibble in place, as in the packed-cache decode) against the S q
+    // digit rows, one v_mfma_i32_32x32x32_i8 per 32 signs; lane = (token, half of the rows)
+    if (kv && qq < CH / 32) {
+      const int row = lane & 31, hf = lane >> 5, t2 = 32 * qq + row;
+      const uint32_t *sgw = &krs[t2 * KWP + 3 * D / 32 + hf * (D / 64)];
+      const uint2 sw = make_uint2(sgw[0], D >= 128 ? sgw[1] : 0u);
+      v16i s2 = {};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        const uint32_t w = (c >> 1) ? sw.y : sw.x;
+        const uint32_t nb = (c & 1) ? w >> 4 : w;
+        v4i bp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bp[e] = int(nb & (0x01010101u << e));
+        s2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(As[c], bp, s2, 0, 0, 0);
+      }
+      const float rn16 = f16_bits_to_float(kns[t2] >> 16);   // 0 past the chunk's end
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 4 * hf + r;
+        // digit sums: rows 8 digit + head are accumulator registers 4 digit + r
+        const float S2 = fmaf(float(s2[r] + 256 * s2[4 + r]), 0x1p-16f, float(s2[8 + r] + 256 * s2[12 + r]));
+        qj[h][t2] = rn16 * fmaf(qjc[0][h], S2, -qjc[1][h]);
+      }
+    }
     __syncthreads();
     // ---- scores: wave = head, lane = token
     if (wv < G) {
       const int h = wv, t = lane;
-      const uint32_t nrm = kns[t];
-      const float n16 = f16_bits_to_float(nrm & 0xFFFFu), rn16 = f16_bits_to_float(nrm >> 16);
-      uint32_t sg[D / 32];
-#pragma unroll
-      for (int i = 0; i < D / 32; ++i) sg[i] = krs[t * KWP + 3 * D / 32 + i];
+      const float n16 = f16_bits_to_float(kns[t] & 0xFFFFu);
       const float s0 = psk[0][h][t], s1 = psk[1][h][t], s2 = psk[2][h][t], s3 = psk[3][h][t];
-      float q0 = 0.0f, q1 = 0.0f;
-#pragma unroll
-      for (int k = 0; k < D / 4; k += 2) {
-        q0 += nib[h][k][(sg[k >> 3] >> (4 * (k & 7))) & 15u];
-        q1 += nib[h][k + 1][(sg[(k + 1) >> 3] >> (4 * ((k + 1) & 7))) & 15u];
-      }
-      const float sc = fmaf(n16, (s0 + s1) + (s2 + s3), a.qjl_scale * rn16 * fmaf(2.0f, q0 + q1, -s1q[h]));
+      const float sc = fmaf(n16, (s0 + s1) + (s2 + s3), qj[h][t]);
       if (a.scores && t < cn) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.score_stride + c0 + t] = sc;
       // online softmax of this head over the chunk
       const float v = t < cn ? sc * a.scale_log2 : -INFINITY;
@@ -4025,6 +4042,8 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
   const int G = q_heads / desc->kv_heads;
   const float sc = scale == 0.0f ? float(1.0 / std::sqrt(double(d))) : scale;
   const bool mfma = decode_mfma_path(*desc, q_heads);
+  // the int8 digit rows: the MFMA path's key and QJL scores, PolarQuant's QJL sums
+  const bool with_qpack = mfma || desc->polar;
   // odd key codebook on the MFMA path: c[code] = c0 + a weighted sum of bit planes
   const int bk = desc->bits_k;
   const int score_stride = length + wlen;
@@ -4034,14 +4053,14 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
   if (d == m && (d == 64 || d == 128) && cp.block == d) {
     if (d == 64)
       hipLaunchKernelGGL(k_qprep_fast<64>, dim3(rows), dim3(256), 0, s, q, int(dtype), q_pos, rope_base, cp, qp,
-                         qstride, q_heads, G, bk, mfma ? qpack : nullptr, ch.nsn);
+                         qstride, q_heads, G, bk, with_qpack ? qpack : nullptr, ch.nsn);
     else
       hipLaunchKernelGGL(k_qprep_fast<128>, dim3(rows), dim3(256), 0, s, q, int(dtype), q_pos, rope_base, cp, qp,
-                         qstride, q_heads, G, bk, mfma ? qpack : nullptr, ch.nsn);
+                         qstride, q_heads, G, bk, with_qpack ? qpack : nullptr, ch.nsn);
   } else {
     hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s, q,
-                       int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, bk, mfma ? qpack : nullptr,
-                       ch.nsn);
+                       int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, bk,
+                       with_qpack ? qpack : nullptr, ch.nsn);
   }
   used_splits = S;
   if (mfma) {
@@ -4105,6 +4124,7 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
     pa.vrec = reinterpret_cast<const uint8_t *>(ch.vcodes);
     pa.vnorm = ch.vnorm;
     pa.qp = qp;
+    pa.qpack = qpack;
     pa.pcs = cp.pcs;
     pa.part = part;
     pa.scores = scores;
@@ -4120,7 +4140,6 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
     pa.qstride = qstride;
     pa.score_stride = score_stride;
     pa.scale_log2 = sc * 1.4426950408889634f;
-    pa.qjl_scale = cp.qjl_scale;
     const dim3 grid(units, used_splits);
     if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
     if (d == 64)
