@@ -2689,9 +2689,10 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
 // (the two top levels give the quarter's radius, its own subtree the rest).  A key
 // quarter is dotted with every head's rotated query in registers; a value quarter, times
 // the value norm, goes to LDS as fp16 hi + lo.  The key score is n <q_rot, yhat> plus the
-// QJL term, whose sign-bit sum comes from a per-head table over nibbles; then the online
-// softmax (one head per wave) and the value sums on fp16 MFMA.  The sums stay in the
-// rotated basis: the partials are the merge's usual input.
+// QJL term, whose sign-bit sums run on int8 MFMA against the query's S q digit rows; then
+// the online softmax (one head per wave) and the value sums on fp16 MFMA.  The sums stay
+// in the rotated basis: the partials are the merge's usual input.
+
 // a compile-time int carried by a value (selects a templated lambda body)
 template <int V>
 struct IntTag {
