@@ -36,26 +36,6 @@ __device__ __forceinline__ float load_elem(const void *p, size_t i, int dtype) {
   return float(h);
 }
 
-__device__ __forceinline__ void copy_elem(void *dst, const void *src, size_t di, size_t si, int dtype) {
-  if (dtype == TQ_F32)
-    static_cast<float *>(dst)[di] = static_cast<const float *>(src)[si];
-  else
-    static_cast<uint16_t *>(dst)[di] = static_cast<const uint16_t *>(src)[si];
-}
-
-// fp32 -> fp16 bits, round to nearest even; values that would round to infinity are
-// stored as 65504 and reported through *over.
-__device__ __forceinline__ uint16_t f16_sat_bits(float x, bool *over) {
-  if (!(x < 65520.0f)) {  // also catches +inf / NaN norms
-    *over = true;
-    return 0x7BFF;
-  }
-  _Float16 h = (_Float16)x;
-  uint16_t b;
-  __builtin_memcpy(&b, &h, 2);
-  return b;
-}
-
 __device__ __forceinline__ float f16_bits_to_float(uint32_t b) {
   uint16_t s = uint16_t(b);
   _Float16 h;
@@ -1347,12 +1327,6 @@ __device__ __forceinline__ uint32_t f16bits(float x) {
   uint16_t b;
   __builtin_memcpy(&b, &h, 2);
   return b;
-}
-
-__device__ __forceinline__ float max32(float v) {   // max over the 32 lanes of a half
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
 }
 
 // Max over each group of 32 lanes with DPP row operations: within rows of 16 (quad
