@@ -291,6 +291,30 @@ def test_nsn_codes_and_decode(tq, P, bk, d, G, L0, T, dist):
         assert e_e2e <= TOL
 
 
+@pytest.mark.parametrize("d,dt,T", [(128, torch.float32, 333), (64, torch.float16, 260)])
+def test_nsn_means_input_dtypes(tq, P, d, dt, T):
+    """NSN means (and the shifted codes) from fp32 and fp16 inputs, whose element loads in
+    the means kernel differ from the bf16 ones: the means over the whole cache, every code,
+    norm and s1 against the oracle on the same input values."""
+    w = W.LONG_CONTEXT.scaled(batch=1, kv_heads=2, q_heads=4, d=d, m=d, context=T, bits_k=2, bits_v=3)
+    K, V = W.gen_kv(w)
+    K, V = K.to(dt).contiguous(), V.to(dt).contiguous()
+    Kd, Vd = P.to_f64(K), P.to_f64(V)
+    codec_o = O.make_codec(d, 2, 3, d, 0)
+    means = P.oracle_means(Kd, Vd, np.arange(T), w.rope_base)
+    fields = P.oracle_encode_unitwise(Kd, Vd, codec_o, np.arange(T), w.rope_base, means)
+    codec = tq.Codec(d, 2, 3, d, seed=0)
+    cache = tq.PackedCache(w.batch, w.kv_heads, d, T, 2, 3, d, nsn=1)
+    Kc, Vc = K.cuda(), V.cuda()
+    ws = torch.empty(tq.nsn_means_workspace_bytes(cache.desc, T), dtype=torch.uint8, device="cuda")
+    tq.nsn_set_means(cache.desc, codec.dev, cache.buf, Kc, Vc, 0, w.rope_base, ws)
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, Kc, Vc, 0, w.rope_base)
+    torch.cuda.synchronize()
+    rep = {}
+    P.compare_codes(P.gpu_fields(cache, T), fields, codec_o, rep)
+    say(f"    nsn means d{d} {dt}: codes {rep}")
+
+
 @pytest.mark.parametrize("d,G,T,chunks,dist", [
     (128, 8, 700, [(0, 300), (300, 700)], "laplace"),   # two appends, a ragged tail
     (64, 4, 530, None, "student_t3"),
