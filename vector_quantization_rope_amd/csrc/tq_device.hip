@@ -530,13 +530,16 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   constexpr int C = 2 * HC;     // coordinates per lane
   constexpr int W = D / 32;     // dwords per plane
   constexpr int RS = D + 8;     // padded residual row (fp16 elements)
-  constexpr int ROPE_BYTES = 64 * H * 16;
+  // RoPE table rows padded by one entry: the 16 tokens of a wave read the same columns, and
+  // an unpadded row stride (a multiple of the bank width) sent them all to the same banks
+  constexpr int RH = H + 1;
+  constexpr int ROPE_BYTES = 64 * RH * 16;
   constexpr int R_BYTES = 2 * 64 * RS * 2;
   constexpr int U_BYTES = ROPE_BYTES > R_BYTES ? ROPE_BYTES : R_BYTES;
   __shared__ __align__(16) unsigned char u_s[U_BYTES];   // RoPE table, later residuals
   __shared__ __align__(16) uint8_t vcode_s[64][D];
   __shared__ float cb_s[4][kMaxCodes];
-  double2 *rope_s = reinterpret_cast<double2 *>(u_s);   // [64][H]
+  double2 *rope_s = reinterpret_cast<double2 *>(u_s);   // [64][RH]
   _Float16 *r_s = reinterpret_cast<_Float16 *>(u_s);     // [2 parts][64][RS]
 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
@@ -565,7 +568,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
     sincos(double(p0 + i0) * theta, &s, &c);
     sincos(theta, &sd, &cd);
     for (int i = 0; i < per; ++i) {
-      rope_s[(i0 + i) * H + j] = make_double2(c, s);
+      rope_s[(i0 + i) * RH + j] = make_double2(c, s);
       const double cn = c * cd - s * sd;
       s = s * cd + c * sd;
       c = cn;
@@ -596,7 +599,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   if (use_rope) {
 #pragma unroll
     for (int e = 0; e < HC; ++e) {
-      const double2 cs = rope_s[slot * H + HC * q + e];
+      const double2 cs = rope_s[slot * RH + HC * q + e];
       const double x0 = x[e], x1 = x[HC + e];
       x[e] = x0 * cs.x - x1 * cs.y;
       x[HC + e] = x0 * cs.y + x1 * cs.x;
