@@ -537,7 +537,9 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   constexpr int R_BYTES = 2 * 64 * RS * 2;
   constexpr int U_BYTES = ROPE_BYTES > R_BYTES ? ROPE_BYTES : R_BYTES;
   __shared__ __align__(16) unsigned char u_s[U_BYTES];   // RoPE table, later residuals
-  __shared__ __align__(16) uint8_t vcode_s[64][D];
+  // value codes, one byte each; rows padded by a dword so that the 16 tokens of a wave,
+  // which write the same columns, land on different banks
+  __shared__ __align__(16) uint8_t vcode_s[64][D + 4];
   __shared__ float cb_s[4][kMaxCodes];
   double2 *rope_s = reinterpret_cast<double2 *>(u_s);   // [64][RH]
   _Float16 *r_s = reinterpret_cast<_Float16 *>(u_s);     // [2 parts][64][RS]
