@@ -2406,6 +2406,21 @@ __global__ __launch_bounds__(256) void k_window(WindowArgs a) {
     }
   };
   fetch(t_begin);
+  // this thread's query pairs, loaded before the fp64 angles are computed
+  constexpr int QPT = GM * H2 / 256;
+  static_assert(QPT * 256 == GM * H2, "query pairs split evenly over the block");
+  float qx0[QPT], qx1[QPT];
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + k * 256, h = i / H2, j = i % H2;
+    qx0[k] = 0.0f;
+    qx1[k] = 0.0f;
+    if (i < G * H2) {
+      const size_t base = (size_t(b) * a.q_heads + hq0 + h) * D;
+      qx0[k] = load_elem(a.q, base + j, a.qdtype);
+      qx1[k] = load_elem(a.q, base + j + H2, a.qdtype);
+    }
+  }
   // fp64 frequency of this thread's pair index (the keys' RoPE steps token by token)
   const int jp = tid % H2, grp = tid / H2;
   const double theta = rope ? exp2(-2.0 * double(jp) / double(D) * log2(double(a.rope_base))) : 0.0;
@@ -2432,10 +2447,11 @@ __global__ __launch_bounds__(256) void k_window(WindowArgs a) {
   for (int i = G * D + tid; i < GM * D; i += 256) (&qr[0][0])[i] = 0.0f;
   __syncthreads();
   // RoPE(q) of the unit's heads, unrotated
-  for (int i = tid; i < G * H2; i += 256) {
-    const int h = i / H2, j = i % H2;
-    const size_t base = (size_t(b) * a.q_heads + hq0 + h) * D;
-    const float x0 = load_elem(a.q, base + j, a.qdtype), x1 = load_elem(a.q, base + j + H2, a.qdtype);
+#pragma unroll
+  for (int k = 0; k < QPT; ++k) {
+    const int i = tid + k * 256, h = i / H2, j = i % H2;
+    if (i >= G * H2) break;
+    const float x0 = qx0[k], x1 = qx1[k];
     if (rope) {
       const float c = qrot[0][j], sn = qrot[1][j];
       qr[h][j] = x0 * c - x1 * sn;
