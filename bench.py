@@ -401,7 +401,7 @@ def window_bench(tq, w, K, V, q, cache, codec, dev, ev, stream, cap: int = 128, 
 
     def timed(fn):
         t0, n = time.perf_counter(), 0
-        while time.perf_counter() - t0 < 0.08:
+        while time.perf_counter() - t0 < 0.3:
             fn()
             n += 1
             if n % 16 == 0:
@@ -438,7 +438,7 @@ def window_bench(tq, w, K, V, q, cache, codec, dev, ev, stream, cap: int = 128, 
         return L, Wn
 
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 0.08:
+    while time.perf_counter() - t0 < 0.3:
         loop(False)
     torch.cuda.synchronize()
     L, Wn = loop(True)
