@@ -120,6 +120,19 @@ def test_stored_codebook_is_fp16_rounding_with_midpoint_boundaries(O):
     np.testing.assert_array_equal(cb.t.astype(np.float32).astype(np.float64), cb.t)
 
 
+@pytest.mark.parametrize("d", [8, 64, 128, 1536])
+def test_codebook_is_odd(O, d):
+    # the marginal density of a rotated coordinate is even, so the Lloyd-Max optimum is an
+    # odd function: c[K-1-k] = -c[k], t[K-2-k] = -t[k].  The oracle's fp64 iterate is odd up
+    # to rounding, and the stored (fp16-rounded) codebook is odd exactly -- the form the
+    # 2- and 3-bit plane identities of the decode and search rest on.
+    for bits in (1, 2, 3, 4):
+        cb = O.make_codebook(d, bits)
+        np.testing.assert_allclose(cb.c64[::-1], -cb.c64, rtol=0, atol=2e-14)
+        np.testing.assert_array_equal(cb.c[::-1], -cb.c)
+        np.testing.assert_array_equal(cb.t[::-1], -cb.t)
+
+
 # ------------------------------------------------------------------ rotation / RoPE
 def test_hadamard_small_cases(O):
     np.testing.assert_array_equal(O.hadamard(2), [[1, 1], [1, -1]])
@@ -236,23 +249,69 @@ def test_residual_is_against_fp16_norm(O):
 
 
 # ------------------------------------------------------------------ QJL estimator
+def _qjl_estimates_over_seeds(O, n_seeds, d=64, m=64):
+    """For one fixed key x and query q, the oracle's own score estimates under n_seeds codec
+    seeds: through attend (scalar codes), search_scores and attend over a PolarQuant cache.
+    Each seed draws a new rotation and a new S, so the residual changes from seed to seed.
+    Also returns, per seed and path, the closed-form conditional variance of the QJL term,
+    ||r||^2/m ((pi/2)||q||^2 - (q_rot . r_hat)^2), from the oracle's residual r."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(d)
+    q = x + 0.5 * rng.standard_normal(d)   # correlated with x, so <q_rot, r> has a nonzero mean
+    est = {"attend": np.empty(n_seeds), "search": np.empty(n_seeds), "polar": np.empty(n_seeds)}
+    cvar = {k: np.empty(n_seeds) for k in est}
+    one = lambda a: np.asarray(a).reshape((1, 1, 1) + np.asarray(a).shape[1:])
+    for s in range(n_seeds):
+        codec = O.make_codec(d, 2, 3, m, seed=1000 + s)
+        qr = codec.Pi @ q
+        ke = O.encode(x[None], codec, kind="key")
+        f = {"kcodes": one(ke["codes"]), "n16": one(ke["n16"]), "rn16": one(ke["rn16"]), "bits": one(ke["bits"]),
+             "vcodes": np.zeros((1, 1, 1, d), np.int64), "vn16": np.zeros((1, 1, 1))}
+        _, sc = O.attend(f, q[None, None], codec, q_pos=0, rope_base=0.0, scale=0.0, kv_heads=1, length=1)
+        est["attend"][s] = sc[0, 0, 0]
+        de = O.encode(x[None], codec, kind="db")
+        est["search"][s] = O.search_scores({"kcodes": de["codes"], "n16": de["n16"], "rn16": de["rn16"],
+                                            "bits": de["bits"]}, q[None], codec)[0, 0]
+        pe = O.polar_encode(x[None], codec, kind="key")
+        pcodes = {lv: one(c) for lv, c in pe["pcodes"].items()}
+        fp = {"kpc": pcodes, "n16": one(pe["n16"]), "rn16": one(pe["rn16"]), "bits": one(pe["bits"]),
+              "vpc": pcodes, "vn16": np.zeros((1, 1, 1))}
+        _, sc = O.attend(fp, q[None, None], codec, q_pos=0, rope_base=0.0, scale=0.0, kv_heads=1, length=1)
+        est["polar"][s] = sc[0, 0, 0]
+        for k, r in (("attend", ke["r"][0]), ("search", de["r"][0]), ("polar", pe["r"][0])):
+            rh = r / np.linalg.norm(r)
+            cvar[k][s] = (r @ r) / m * (math.pi / 2 * (q @ q) - (qr @ rh) ** 2)
+    return x, q, est, cvar
+
+
 def test_qjl_estimator_unbiased_over_seeds(O):
-    # E_S[ ||r|| sqrt(pi/2)/m <S q, sign(S r)> ] = <q, r>, checked over 10^4 seeds
-    d = m = 64
-    rng = np.random.default_rng(0)
-    q, r = rng.standard_normal(d), rng.standard_normal(d)
-    est = np.empty(10000)
-    for s in range(est.size):
-        S = O.gaussian_projection(m, d, seed=1000 + s).astype(np.float64)
-        sgn = np.where(S @ r >= 0, 1.0, -1.0)
-        est[s] = np.linalg.norm(r) * math.sqrt(math.pi / 2) / m * ((S @ q) @ sgn)
-    err = est - q @ r
-    sigma = err.std()
-    assert abs(err.mean()) < 3 * sigma / math.sqrt(est.size)
-    # variance: ||r||^2/m ((pi/2)||q||^2 - (q . r_hat)^2)
-    rh = r / np.linalg.norm(r)
-    var = (r @ r) / m * (math.pi / 2 * (q @ q) - (q @ rh) ** 2)
-    assert abs(est.var() / var - 1.0) < 0.06
+    # [TurboQuant] "QJL : une technique 1 bit a surcharge nulle": the sign sketch of the
+    # residual, met by the full-precision projected query, gives an unbiased inner product.
+    # With Pi orthogonal, <Pi q, n16 c_hat + r> = <q, x> for every seed, so the estimate's
+    # error against <q, x> is the QJL term's error alone: over 10^4 seeds its mean must be
+    # within 3 sigma / sqrt(N) of zero, and its variance must equal the mean of the
+    # closed-form conditional variance ||r||^2/m ((pi/2)||q||^2 - (q_rot . r_hat)^2)
+    # (E[sign(s.r)(s.q)] = sqrt(2/pi) q.r_hat for s ~ N(0, I)).  A wrong constant, a flipped
+    # sign or a dropped QJL term biases the mean by a multiple of E<q_rot, r> > 0.
+    n = 10000
+    x, q, est, cvar = _qjl_estimates_over_seeds(O, n)
+    truth = q @ x
+    for path in ("attend", "search", "polar"):
+        err = est[path] - truth
+        sigma = err.std()
+        assert abs(err.mean()) < 3 * sigma / math.sqrt(n), (path, err.mean(), sigma)
+        assert abs(err.var() / cvar[path].mean() - 1.0) < 0.06, (path, err.var(), cvar[path].mean())
+
+
+def test_qjl_estimator_beats_the_codes_alone(O):
+    # the QJL term carries the residual's share of <q, x>: over seeds the estimate's mean
+    # squared error is the conditional variance, while dropping the term leaves the whole
+    # residual product <q_rot, r> (bias about ||r||^2 here, q being correlated with x)
+    x, q, est, cvar = _qjl_estimates_over_seeds(O, 400)
+    truth = q @ x
+    for path in ("attend", "search", "polar"):
+        mse = np.mean((est[path] - truth) ** 2)
+        assert mse < 1.5 * cvar[path].mean(), (path, mse, cvar[path].mean())
 
 
 def test_qjl_zero_residual_gives_exact_score(O):
