@@ -185,6 +185,9 @@ def test_logits_only(tq, P, bk, bv, d, G, T):
     (1, 3, 64, 8, 130, 200, 256, "f32"),   # fp32 inputs, window longer than the packed part
     (3, 4, 128, 4, 190, 70, 80, "f32"),    # fp32 decode path
     (2, 3, 64, 16, 150, 600, 640, "f16"),  # f16, 16 q-heads per kv-head (fp32 decode path), 10 chunks
+    (2, 3, 128, 16, 260, 90, 128, "bf16"), # d 128 with 16 head slots
+    (2, 3, 128, 12, 200, 64, 64, "f32"),   # d 128, fp32 window, 12 q-heads per kv-head (not a power of two)
+    (3, 3, 64, 16, 100, 33, 64, "f32"),    # d 64, fp32 window with 16 head slots
 ])
 def test_window_attention(tq, P, bk, bv, d, G, L, Wn, cap, dt):
     """Packed tokens [0, L) plus a full-precision window of Wn raw tokens (NSNQuant's

@@ -288,15 +288,18 @@ def test_vector_search_full_size(tq, P):
         assert len(set(idx[i].tolist())) == w.k
         np.testing.assert_allclose(val[i], s, atol=1e-6)
 
-    # complete top-10 of two queries over all 10^6 packed vectors
-    q2 = np.array([int(qsel[0]), int(qsel[1])])
-    qd = qs[torch.from_numpy(q2).cuda()].double().cpu().numpy()
-    scores = np.empty((2, w.n_db))
+    # complete top-10 of 64 queries (the 16 above and 48 more) over all 10^6 packed vectors
+    rest = np.setdiff1d(np.arange(w.nq), qsel)
+    q64 = np.concatenate([qsel, rng.choice(rest, 48, replace=False)]).astype(np.int64)
+    qd = qs[torch.from_numpy(q64).cuda()].double().cpu().numpy()
+    scores = np.empty((len(q64), w.n_db))
     t0 = time.time()
     step = 4096
     for i0 in range(0, w.n_db, step):
         i1 = min(w.n_db, i0 + step)
         scores[:, i0:i1] = O.search_scores(_db_rows_fields(kbits, knorm, desc, slice(i0, i1)), qd, codec_o)
+        if i0 % (step * 64) == 0:
+            say(f"    oracle scoring: {i1} of {w.n_db} vectors, {time.time() - t0:.1f} s")
     idx_o, val_o = O.topk(scores, w.k)
-    say(f"    oracle scored 2 queries x {w.n_db} vectors in {time.time() - t0:.1f} s")
-    check_topk(idx[q2], val[q2], scores, idx_o, val_o, stol=1e-6)
+    say(f"    oracle scored {len(q64)} queries x {w.n_db} vectors in {time.time() - t0:.1f} s")
+    check_topk(idx[q64], val[q64], scores, idx_o, val_o, stol=1e-6)

@@ -184,3 +184,38 @@ def test_codec_polar_tables_match_oracle(tq, O, d):
         assert np.count_nonzero(pcs[lv - 1, :K, 0] != pc.cos[lv]) == 0
         assert np.count_nonzero(pcs[lv - 1, :K, 1] != pc.sin[lv]) == 0
         np.testing.assert_allclose(pt[lv - 1, :K - 1], pc.t[lv], rtol=0, atol=1e-12)
+
+
+def test_binding_rejects_bad_tensors_before_the_call(tq):
+    # the binding checks shapes, contiguity and dtypes on the host; each case below fails
+    # there, so no pointer reaches the library (CPU tensors, no GPU needed)
+    import torch
+    desc = tq.CacheDesc(2, 4, 128, 64, 2, 3, 128)
+    k = torch.zeros((2, 4, 8, 128), dtype=torch.bfloat16)
+    cases = [
+        lambda: tq.quantize_kv(desc, 1, 1, k.transpose(2, 3).contiguous().transpose(2, 3), k, 0, 0.0),
+        lambda: tq.quantize_kv(desc, 1, 1, k[:, :3], k[:, :3], 0, 0.0),                    # kv_heads 3
+        lambda: tq.quantize_kv(desc, 1, 1, k, k.float(), 0, 0.0),                           # mixed dtypes
+        lambda: tq.quantize_kv(desc, 1, 1, k, None, 0, 0.0),                                # no values
+        lambda: tq.quantize_kv(desc, 1, 1, k[:, :, ::2], k[:, :, ::2], 0, 0.0),             # strided
+        lambda: tq.decode_attend(desc, 1, 1, 64, torch.zeros((2, 16, 64)), 64, 0.0,
+                                 torch.zeros((2, 16, 128)), ws=1, ws_bytes=1 << 20),        # q of d 64
+        lambda: tq.decode_attend(desc, 1, 1, 64, torch.zeros((2, 16, 128)), 64, 0.0,
+                                 torch.zeros((2, 16, 127)), ws=1, ws_bytes=1 << 20),        # short out
+        lambda: tq.decode_attend(desc, 1, 1, 64, torch.zeros((2, 16, 128)), 64, 0.0,
+                                 torch.zeros((2, 16, 128), dtype=torch.float64), ws=1, ws_bytes=1 << 20),
+        lambda: tq.decode_attend(desc, 1, 1, 64, torch.zeros((2, 16, 128)), 64, 0.0,
+                                 torch.zeros((2, 16, 128)), scores=torch.zeros((2, 16, 63)), ws=1,
+                                 ws_bytes=1 << 20),                                         # short scores
+        lambda: tq.search_topk(tq.CacheDesc(1, 1, 128, 64, 3, 0, 128), 1, 1, 64, torch.zeros((4, 128)), 10,
+                               torch.zeros((4, 10), dtype=torch.int64), torch.zeros((4, 10)), 1, ws_bytes=1),
+        lambda: tq.search_topk(tq.CacheDesc(1, 1, 128, 64, 3, 0, 128), 1, 1, 64, torch.zeros((4, 128)), 10,
+                               torch.zeros((4, 9), dtype=torch.int32), torch.zeros((4, 10)), 1, ws_bytes=1),
+        lambda: tq.search_topk(tq.CacheDesc(1, 1, 128, 64, 3, 0, 128), 1, 1, 64,
+                               torch.zeros((128, 4)).t(), 10, torch.zeros((4, 10), dtype=torch.int32),
+                               torch.zeros((4, 10)), 1, ws_bytes=1),                        # strided queries
+    ]
+    for i, fn in enumerate(cases):
+        with pytest.raises(ValueError):
+            fn()
+            pytest.fail(f"case {i} was not rejected")

@@ -128,6 +128,27 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _require(t, name: str, *, shape=None, numel=None, dtypes=None, where: str):
+    """Host-side checks of a tensor argument before its pointer crosses the C ABI (a raw
+    integer pointer is passed through unchecked).  A strided view would make the kernels
+    read the wrong rows, and a short or mistyped output would take writes past its end."""
+    if t is None or isinstance(t, int):
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{where}: {name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{where}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{where}: {name} has {t.numel()} elements, needs at least {numel}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{where}: {name} has dtype {t.dtype}, expected one of {dtypes}")
+
+
+def _float_types():
+    import torch
+    return (torch.float32, torch.bfloat16, torch.float16)
+
+
 def _dtype_code(t) -> int:
     import torch
     return {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16, torch.float16: TQ_F16}[t.dtype]
@@ -184,6 +205,13 @@ def quantize_kv(desc: CacheDesc, codec_dev, cache, k, v, start_pos: int, rope_ba
     """events: optional (start, stop) hipEvent_t handles recorded around the kernel."""
     if n_new is None:
         n_new = 0 if k is None else int(k.shape[-2])
+    if k is not None and not isinstance(k, int):
+        want = (desc.batch, desc.kv_heads, int(n_new), desc.d)
+        _require(k, "k", shape=want, dtypes=_float_types(), where="quantize_kv")
+        if desc.bits_v > 0:
+            if v is None:
+                raise ValueError("quantize_kv: v is required when the cache has value codes")
+            _require(v, "v", shape=want, dtypes=(k.dtype,), where="quantize_kv")
     code = dtype if dtype is not None else (_dtype_code(k) if k is not None else TQ_F32)
     ev0, ev1 = events if events else (None, None)
     _check(_quantize_kv_prof(ctypes.byref(desc), _ptr(codec_dev), _ptr(cache), _ptr(k), _ptr(v), code,
@@ -206,6 +234,12 @@ def decode_attend(desc: CacheDesc, codec_dev, cache, length: int, q, q_pos: int,
                   ws_bytes: int | None = None, events=None):
     """events: optional (start, stop) hipEvent_t handles recorded around the split-K kernel."""
     q_heads = int(q.shape[1])
+    import torch
+    _require(q, "q", shape=(desc.batch, q_heads, desc.d), dtypes=_float_types(), where="decode_attend")
+    _require(out, "out", numel=desc.batch * q_heads * desc.d, dtypes=(torch.float32,), where="decode_attend")
+    _require(scores, "scores", numel=desc.batch * q_heads * int(length), dtypes=(torch.float32,),
+             where="decode_attend")
+    _require(ws, "ws", where="decode_attend")
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     ev0, ev1 = events if events else (None, None)
@@ -308,6 +342,12 @@ def search_workspace_bytes(desc: CacheDesc, n_db: int, nq: int, k: int) -> int:
 
 def search_topk(desc: CacheDesc, codec_dev, db_cache, n_db: int, queries, k: int, idx_out,
                 score_out, ws, stream=None, ws_bytes: int | None = None):
+    import torch
+    nq = int(queries.shape[0])
+    _require(queries, "queries", shape=(nq, desc.d), dtypes=(torch.float32,), where="search_topk")
+    _require(idx_out, "idx_out", numel=nq * int(k), dtypes=(torch.int32,), where="search_topk")
+    _require(score_out, "score_out", numel=nq * int(k), dtypes=(torch.float32,), where="search_topk")
+    _require(ws, "ws", where="search_topk")
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
     _check(_search_topk(ctypes.byref(desc), _ptr(codec_dev), _ptr(db_cache), int(n_db), _ptr(queries),
