@@ -47,6 +47,9 @@ typedef enum {
   TQ_EDEVICE = 5        /* a HIP launch or runtime call failed */
 } tq_status;
 
+/* Element types of the K, V and query inputs.  Entry points take the value as an int32_t
+ * (any other value is TQ_EINVAL), so a C caller's out-of-range integer is checked rather
+ * than loaded as an enum. */
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
 /* Codec parameters.  d: vector dimension; bits_k: scalar bits of keys / database
@@ -58,7 +61,9 @@ typedef struct {
   uint64_t seed;
 } tq_codec_desc;
 
-/* Packed cache shape: `batch` x `kv_heads` units of `capacity` token slots each.
+/* Packed cache shape: `batch` x `kv_heads` units of `capacity` token slots each
+ * (batch x kv_heads <= 65535 and capacity <= 2^30; a larger shape is TQ_EUNSUPPORTED and
+ * tq_cache_bytes returns 0 for it).
  * nsn = 1 selects the NSN pre-transform ([NSNQuant] section 1: tokens normalized to norm
  * sqrt(d), the channel mean shifted out, normalized again) for keys and values: each
  * token v is stored as the codec of w = v - s1 o with s1 = ||v|| / sqrt(d) kept in fp16
@@ -82,8 +87,9 @@ typedef void *tq_stream_t; /* hipStream_t */
 /* Version string of the library and of the packed format ("libtq <x.y> format 1"). */
 const char *tq_version(void);
 
-/* Human-readable name of a status code (static storage). */
-const char *tq_status_str(tq_status s);
+/* Human-readable name of a status code (static storage; "unknown status" for a value
+ * that is not a tq_status). */
+const char *tq_status_str(int32_t s);
 
 /* Lloyd-Max codebook ([TurboQuant] "Etape 1" and the reader comment on Lloyd-Max
  * boundaries; [TurboESM] 2.C) for one coordinate of a uniformly random unit vector in
@@ -166,7 +172,7 @@ tq_status tq_cache_init(const tq_cache_desc *desc, void *cache_dev, tq_stream_t 
  * iff desc->bits_v == 0; both must be 16-byte aligned (TQ_EINVAL otherwise).
  * n_new == 0 is a no-op.  Writes never touch other slots. */
 tq_status tq_quantize_kv(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
-                         const void *k, const void *v, tq_dtype dtype, int32_t start_pos,
+                         const void *k, const void *v, int32_t dtype, int32_t start_pos,
                          int32_t n_new, float rope_base, tq_stream_t stream);
 
 /* Workspace bytes tq_decode_attend needs for this shape (splits chosen by the library). */
@@ -190,7 +196,7 @@ int32_t tq_decode_splits(const tq_cache_desc *desc, int32_t q_heads, int32_t len
  * tq_decode_workspace_bytes bytes, overwritten. */
 tq_status tq_decode_attend(const tq_cache_desc *desc, const void *codec_dev,
                            const void *cache_dev, int32_t length, const void *q,
-                           tq_dtype dtype, int32_t q_heads, int32_t q_pos, float rope_base,
+                           int32_t dtype, int32_t q_heads, int32_t q_pos, float rope_base,
                            float scale, float *out, float *scores, void *ws, size_t ws_bytes,
                            tq_stream_t stream);
 
@@ -200,7 +206,7 @@ size_t tq_decode_workspace_bytes_splits(const tq_cache_desc *desc, int32_t q_hea
                                         int32_t splits);
 tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_dev,
                                   const void *cache_dev, int32_t length, const void *q,
-                                  tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                                  int32_t dtype, int32_t q_heads, int32_t q_pos,
                                   float rope_base, float scale, float *out, float *scores,
                                   int32_t splits, void *ws, size_t ws_bytes,
                                   tq_stream_t stream);
@@ -211,12 +217,12 @@ tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_d
  * quantize kernel; the split-K decode kernel) on `stream`.  Either event may be NULL. */
 tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_dev,
                                   void *cache_dev, const void *k, const void *v,
-                                  tq_dtype dtype, int32_t start_pos, int32_t n_new,
+                                  int32_t dtype, int32_t start_pos, int32_t n_new,
                                   float rope_base, void *ev_start, void *ev_stop,
                                   tq_stream_t stream);
 tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec_dev,
                                     const void *cache_dev, int32_t length, const void *q,
-                                    tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                                    int32_t dtype, int32_t q_heads, int32_t q_pos,
                                     float rope_base, float scale, float *out, float *scores,
                                     int32_t splits, void *ws, size_t ws_bytes,
                                     void *ev_start, void *ev_stop, tq_stream_t stream);
@@ -239,8 +245,8 @@ size_t tq_decode_window_workspace_bytes(const tq_cache_desc *desc, int32_t q_hea
  * the window buffer being exactly that call's [batch][kv_heads][n_new][d] input. */
 tq_status tq_decode_attend_window(const tq_cache_desc *desc, const void *codec_dev,
                                   const void *cache_dev, int32_t length, const void *win_k,
-                                  const void *win_v, tq_dtype win_dtype, int32_t win_len,
-                                  int32_t win_cap, const void *q, tq_dtype dtype, int32_t q_heads,
+                                  const void *win_v, int32_t win_dtype, int32_t win_len,
+                                  int32_t win_cap, const void *q, int32_t dtype, int32_t q_heads,
                                   int32_t q_pos, float rope_base, float scale, float *out,
                                   float *scores, void *ws, size_t ws_bytes, tq_stream_t stream);
 
@@ -258,9 +264,9 @@ tq_status tq_decode_attend_window(const tq_cache_desc *desc, const void *codec_d
  * was launched and nothing changes.  ws: tq_decode_window_workspace_bytes for the
  * packed length after the step (the cache capacity always suffices). */
 tq_status tq_decode_step(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
-                         int32_t *length, void *win_k, void *win_v, tq_dtype win_dtype,
+                         int32_t *length, void *win_k, void *win_v, int32_t win_dtype,
                          int32_t *win_len, int32_t win_cap, const void *new_k, const void *new_v,
-                         const void *q, tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                         const void *q, int32_t dtype, int32_t q_heads, int32_t q_pos,
                          float rope_base, float scale, float *out, float *scores, void *ws,
                          size_t ws_bytes, tq_stream_t stream);
 
@@ -277,7 +283,7 @@ size_t tq_nsn_means_workspace_bytes(const tq_cache_desc *desc, int32_t n);
  * [batch][kv_heads][n][d] of `dtype`, 16-byte aligned; n >= 1; ws: at least
  * tq_nsn_means_workspace_bytes.  TQ_EINVAL on a cache without nsn. */
 tq_status tq_nsn_set_means(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
-                           const void *k, const void *v, tq_dtype dtype, int32_t start_pos,
+                           const void *k, const void *v, int32_t dtype, int32_t start_pos,
                            int32_t n, float rope_base, void *ws, size_t ws_bytes,
                            tq_stream_t stream);
 

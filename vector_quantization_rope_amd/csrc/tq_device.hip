@@ -3754,7 +3754,7 @@ __global__ __launch_bounds__(256) void k_nsn_final(const double *part, int slice
 
 int nsn_slices(int n, int units) {
   const int want = (1024 + units - 1) / units;   // about four blocks per CU in all
-  const int by_n = (n + 255) / 256;
+  const int by_n = int((int64_t(n) + 255) / 256);
   return std::max(1, std::min(want, by_n));
 }
 
@@ -3856,7 +3856,7 @@ tq_status tq_cache_init(const tq_cache_desc *desc, void *cache_dev, tq_stream_t 
 
 tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_dev,
                                   void *cache_dev, const void *k, const void *v,
-                                  tq_dtype dtype, int32_t start_pos, int32_t n_new,
+                                  int32_t dtype, int32_t start_pos, int32_t n_new,
                                   float rope_base, void *ev_start, void *ev_stop,
                                   tq_stream_t stream) {
   if (!desc || !codec_dev || !cache_dev) return TQ_EINVAL;
@@ -3938,7 +3938,7 @@ tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_d
 }
 
 tq_status tq_quantize_kv(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
-                         const void *k, const void *v, tq_dtype dtype, int32_t start_pos,
+                         const void *k, const void *v, int32_t dtype, int32_t start_pos,
                          int32_t n_new, float rope_base, tq_stream_t stream) {
   return tq_quantize_kv_profiled(desc, codec_dev, cache_dev, k, v, dtype, start_pos, n_new,
                                  rope_base, nullptr, nullptr, stream);
@@ -3963,7 +3963,7 @@ size_t tq_decode_workspace_bytes(const tq_cache_desc *desc, int32_t q_heads, int
 namespace {
 struct WindowIn {
   const void *k, *v;
-  tq_dtype dtype;
+  int32_t dtype;
   int len, cap;            // tokens attended (including an appended one), buffer rows
   const void *nk, *nv;     // decode step: the token appended at row len - 1, or null
   void *ak, *av;           // decode step: writable window buffers
@@ -3973,7 +3973,7 @@ struct WindowIn {
 
 static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
                              const void *cache_dev, int32_t length, const WindowIn *win,
-                             const void *q, tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                             const void *q, int32_t dtype, int32_t q_heads, int32_t q_pos,
                              float rope_base, float scale, float *out, float *scores,
                              int32_t splits, void *ws, size_t ws_bytes,
                              void *ev_start, void *ev_stop, tq_stream_t stream) {
@@ -4244,7 +4244,7 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
 
 tq_status tq_decode_attend_profiled(const tq_cache_desc *desc, const void *codec_dev,
                                     const void *cache_dev, int32_t length, const void *q,
-                                    tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                                    int32_t dtype, int32_t q_heads, int32_t q_pos,
                                     float rope_base, float scale, float *out, float *scores,
                                     int32_t splits, void *ws, size_t ws_bytes,
                                     void *ev_start, void *ev_stop, tq_stream_t stream) {
@@ -4259,8 +4259,8 @@ size_t tq_decode_window_workspace_bytes(const tq_cache_desc *desc, int32_t q_hea
 
 tq_status tq_decode_attend_window(const tq_cache_desc *desc, const void *codec_dev,
                                   const void *cache_dev, int32_t length, const void *win_k,
-                                  const void *win_v, tq_dtype win_dtype, int32_t win_len,
-                                  int32_t win_cap, const void *q, tq_dtype dtype, int32_t q_heads,
+                                  const void *win_v, int32_t win_dtype, int32_t win_len,
+                                  int32_t win_cap, const void *q, int32_t dtype, int32_t q_heads,
                                   int32_t q_pos, float rope_base, float scale, float *out,
                                   float *scores, void *ws, size_t ws_bytes, tq_stream_t stream) {
   const WindowIn w{win_k, win_v, win_dtype, win_len, win_cap, nullptr, nullptr, nullptr, nullptr, false};
@@ -4269,9 +4269,9 @@ tq_status tq_decode_attend_window(const tq_cache_desc *desc, const void *codec_d
 }
 
 tq_status tq_decode_step(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
-                         int32_t *length, void *win_k, void *win_v, tq_dtype win_dtype,
+                         int32_t *length, void *win_k, void *win_v, int32_t win_dtype,
                          int32_t *win_len, int32_t win_cap, const void *new_k, const void *new_v,
-                         const void *q, tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                         const void *q, int32_t dtype, int32_t q_heads, int32_t q_pos,
                          float rope_base, float scale, float *out, float *scores, void *ws,
                          size_t ws_bytes, tq_stream_t stream) {
   if (!length || !win_len || !win_k || !win_v || !new_k || !new_v) return TQ_EINVAL;
@@ -4297,7 +4297,7 @@ size_t tq_nsn_means_workspace_bytes(const tq_cache_desc *desc, int32_t n) {
 }
 
 tq_status tq_nsn_set_means(const tq_cache_desc *desc, const void *codec_dev, void *cache_dev,
-                           const void *k, const void *v, tq_dtype dtype, int32_t start_pos,
+                           const void *k, const void *v, int32_t dtype, int32_t start_pos,
                            int32_t n, float rope_base, void *ws, size_t ws_bytes,
                            tq_stream_t stream) {
   if (!desc || !codec_dev || !cache_dev || !k || !v || !ws) return TQ_EINVAL;
@@ -4340,7 +4340,7 @@ tq_status tq_nsn_set_means(const tq_cache_desc *desc, const void *codec_dev, voi
 
 tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_dev,
                                   const void *cache_dev, int32_t length, const void *q,
-                                  tq_dtype dtype, int32_t q_heads, int32_t q_pos,
+                                  int32_t dtype, int32_t q_heads, int32_t q_pos,
                                   float rope_base, float scale, float *out, float *scores,
                                   int32_t splits, void *ws, size_t ws_bytes,
                                   tq_stream_t stream) {
@@ -4350,7 +4350,7 @@ tq_status tq_decode_attend_splits(const tq_cache_desc *desc, const void *codec_d
 }
 
 tq_status tq_decode_attend(const tq_cache_desc *desc, const void *codec_dev, const void *cache_dev,
-                           int32_t length, const void *q, tq_dtype dtype, int32_t q_heads,
+                           int32_t length, const void *q, int32_t dtype, int32_t q_heads,
                            int32_t q_pos, float rope_base, float scale, float *out, float *scores,
                            void *ws, size_t ws_bytes, tq_stream_t stream) {
   return tq_decode_attend_splits(desc, codec_dev, cache_dev, length, q, dtype, q_heads, q_pos,

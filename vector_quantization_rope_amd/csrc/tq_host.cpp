@@ -22,6 +22,9 @@ bool cache_desc_valid(const tq_cache_desc &c) {
   tq_codec_desc cd{c.d, c.bits_k, c.bits_v, c.m, 0};
   if (!codec_desc_valid(cd)) return false;
   if (c.batch < 1 || c.kv_heads < 1 || c.capacity < 0) return false;
+  // units index a grid dimension (at most 65535), token positions and tile counts stay
+  // in int, and every region size stays far inside size_t
+  if (int64_t(c.batch) * int64_t(c.kv_heads) > kMaxUnits || c.capacity > kMaxCapacity) return false;
   if (c.nsn != 0 && c.nsn != 1) return false;
   if (c.nsn && (c.bits_v == 0 || (c.d != 64 && c.d != 128))) return false;
   if (c.polar != 0 && c.polar != 1) return false;
@@ -214,6 +217,11 @@ void lloyd_max(int d, int bits, double *c, double *t) {
   // cells far in the tails carry no mass: clip the integration range at 40 sigma
   const double lim = std::min(1.0, 40.0 * s);
   std::vector<double> e(K + 1), mass(K);
+  // the step shrinks geometrically until rounding sets a floor; where that floor lies above
+  // the tolerance (d = 4096 with 16 cells) stop once the step has not reached a new low
+  // for a while
+  double best = INFINITY;
+  int stalled = 0;
   for (int it = 0; it < 200000; ++it) {
     e[0] = -lim;
     e[K] = lim;
@@ -228,6 +236,12 @@ void lloyd_max(int d, int bits, double *c, double *t) {
       c[k] = cn;
     }
     if (delta / s < 1e-13) break;
+    if (delta < best) {
+      best = delta;
+      stalled = 0;
+    } else if (++stalled >= 200) {
+      break;
+    }
   }
   // the density is even, so the optimum is odd: c[K-1-k] = -c[k].  Make that exact (the
   // iterate differs from it only by rounding); the search kernel relies on it.
@@ -310,7 +324,7 @@ extern "C" {
 
 const char *tq_version(void) { return "libtq 1.0 format 1"; }
 
-const char *tq_status_str(tq_status s) {
+const char *tq_status_str(int32_t s) {
   switch (s) {
     case TQ_OK: return "ok";
     case TQ_EINVAL: return "invalid argument";

@@ -15,6 +15,8 @@ constexpr uint32_t kFormatVersion = 1;
 constexpr size_t kHeaderBytes = 256;
 constexpr int kValueTile = 32;   // tokens per value-code tile
 constexpr int kMaxCodes = 16;    // 2^4 centroids at most
+constexpr int64_t kMaxUnits = 65535;         // batch x kv_heads of one cache
+constexpr int32_t kMaxCapacity = 1 << 30;    // token slots per unit
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
