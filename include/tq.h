@@ -287,6 +287,29 @@ tq_status tq_nsn_set_means(const tq_cache_desc *desc, const void *codec_dev, voi
                            int32_t n, float rope_base, void *ws, size_t ws_bytes,
                            tq_stream_t stream);
 
+/* Bytes of the device scratch array behind tq_decode_attend_noalloc (per GPU). */
+#define TQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* tq_decode_attend without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It computes exactly what tq_decode_attend computes with the library's own
+ * split count (the same kernels; outputs are bitwise equal), and calls no hipMalloc,
+ * hipFree or other allocating routine.  The workspace lives in a file-scope device array of
+ * TQ_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until the process
+ * ends; the first call on a device looks up its address (hipGetSymbolAddress, with that
+ * device made current for the lookup).  Shapes whose workspace,
+ * tq_decode_workspace_bytes(desc, q_heads, length), exceeds TQ_NOALLOC_SCRATCH_BYTES
+ * return TQ_ENOSPACE and enqueue nothing.  All calls on one GPU share that GPU's array,
+ * which keeps the last call's contents (nothing in it needs to start at zero): calls that
+ * overlap on one GPU (different streams or threads without ordering between them) race,
+ * so the caller orders them, e.g. on one stream.  Arguments, errors and the device
+ * chosen (the device of `stream`; the current device for the null stream) are as
+ * tq_decode_attend. */
+tq_status tq_decode_attend_noalloc(const tq_cache_desc *desc, const void *codec_dev,
+                                   const void *cache_dev, int32_t length, const void *q,
+                                   int32_t dtype, int32_t q_heads, int32_t q_pos, float rope_base,
+                                   float scale, float *out, float *scores, tq_stream_t stream);
+
 /* Workspace bytes tq_search_topk needs. */
 size_t tq_search_workspace_bytes(const tq_cache_desc *db, int32_t n_db, int32_t nq, int32_t k);
 

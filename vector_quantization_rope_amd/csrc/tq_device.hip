@@ -20,6 +20,7 @@
 
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "tq_internal.h"
 
@@ -4355,6 +4356,64 @@ tq_status tq_decode_attend(const tq_cache_desc *desc, const void *codec_dev, con
                            void *ws, size_t ws_bytes, tq_stream_t stream) {
   return tq_decode_attend_splits(desc, codec_dev, cache_dev, length, q, dtype, q_heads, q_pos,
                                  rope_base, scale, out, scores, 0, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ allocation-free decode
+// tq_decode_attend_noalloc keeps the decode workspace (query pack and split partials) in
+// this file-scope device array instead of a caller buffer.  Every GPU the library runs on
+// holds its own copy until the process ends.  On the host the array's name is only a
+// stand-in symbol, never a device address: host code uses the address hipGetSymbolAddress
+// returns, looked up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that runs `s` (the current device for the
+// null stream).
+tq_status scratch_for_stream(hipStream_t s, void **out) {
+  int dev = -1;
+  if (s ? hipStreamGetDevice(s, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess) return TQ_EDEVICE;
+  if (dev < 0 || dev >= kMaxDevices) return TQ_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return TQ_EDEVICE;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return TQ_EDEVICE;
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return TQ_EDEVICE;
+    if (e != hipSuccess || !p) return TQ_EDEVICE;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return TQ_OK;
+}
+}  // namespace
+
+extern "C" {
+
+tq_status tq_decode_attend_noalloc(const tq_cache_desc *desc, const void *codec_dev,
+                                   const void *cache_dev, int32_t length, const void *q,
+                                   int32_t dtype, int32_t q_heads, int32_t q_pos, float rope_base,
+                                   float scale, float *out, float *scores, tq_stream_t stream) {
+  // the workspace tq_decode_attend would take for this shape, at the library's split count
+  const bool shaped = desc && cache_desc_valid(*desc) && q_heads >= 1 && length >= 0;
+  const size_t need = shaped ? decode_ws(*desc, q_heads, default_splits(*desc, length)) : 0;
+  if (need > TQ_NOALLOC_SCRATCH_BYTES) return TQ_ENOSPACE;
+  // an unshaped call fails decode_impl's argument checks before anything reads the
+  // workspace, so the scratch is looked up only for calls that can run
+  void *ws = reinterpret_cast<void *>(uintptr_t(256));
+  if (shaped) {
+    const tq_status st = scratch_for_stream(hipStream_t(stream), &ws);
+    if (st != TQ_OK) return st;
+  }
+  return decode_impl(desc, codec_dev, cache_dev, length, nullptr, q, dtype, q_heads, q_pos, rope_base, scale,
+                     out, scores, 0, ws, TQ_NOALLOC_SCRATCH_BYTES, nullptr, nullptr, stream);
 }
 
 size_t tq_search_workspace_bytes(const tq_cache_desc *db, int32_t n_db, int32_t nq, int32_t k) {

@@ -32,7 +32,10 @@ EXPORTS = [
     "tq_search_workspace_bytes", "tq_search_topk", "tq_quantize_kv_profiled",
     "tq_decode_attend_profiled", "tq_decode_window_workspace_bytes", "tq_decode_attend_window",
     "tq_decode_step", "tq_nsn_means_workspace_bytes", "tq_nsn_set_means", "tq_make_polar_grid",
+    "tq_decode_attend_noalloc",
 ]
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # TQ_NOALLOC_SCRATCH_BYTES
 
 
 class CodecDesc(ctypes.Structure):
@@ -85,6 +88,8 @@ _quantize_kv_prof = _sig("tq_quantize_kv_profiled", ctypes.c_int,
                          [_KD, _P, _P, _P, _P, ctypes.c_int, _I, _I, _F, _P, _P, _P])
 _decode_attend_prof = _sig("tq_decode_attend_profiled", ctypes.c_int,
                            [_KD, _P, _P, _I, _P, ctypes.c_int, _I, _I, _F, _F, _P, _P, _I, _P, _S, _P, _P, _P])
+_decode_attend_noalloc = _sig("tq_decode_attend_noalloc", ctypes.c_int,
+                              [_KD, _P, _P, _I, _P, ctypes.c_int, _I, _I, _F, _F, _P, _P, _P])
 _decode_win_ws = _sig("tq_decode_window_workspace_bytes", _S, [_KD, _I, _I])
 _decode_attend_win = _sig("tq_decode_attend_window", ctypes.c_int,
                           [_KD, _P, _P, _I, _P, _P, ctypes.c_int, _I, _I, _P, ctypes.c_int, _I, _I, _F, _F,
@@ -248,6 +253,23 @@ def decode_attend(desc: CacheDesc, codec_dev, cache, length: int, q, q_pos: int,
                                float(scale), _ptr(out), _ptr(scores), int(splits), _ptr(ws),
                                int(ws_bytes), ev0, ev1, _stream(stream)),
            "tq_decode_attend")
+
+
+def decode_attend_noalloc(desc: CacheDesc, codec_dev, cache, length: int, q, q_pos: int, rope_base: float,
+                          out, scores=None, scale: float = 0.0, stream=None):
+    """tq_decode_attend_noalloc: decode attention with the library's own device scratch (no
+    workspace argument, no allocation); calls that overlap on one GPU race."""
+    import torch
+    q_heads = int(q.shape[1])
+    _require(q, "q", shape=(desc.batch, q_heads, desc.d), dtypes=_float_types(), where="decode_attend_noalloc")
+    _require(out, "out", numel=desc.batch * q_heads * desc.d, dtypes=(torch.float32,),
+             where="decode_attend_noalloc")
+    _require(scores, "scores", numel=desc.batch * q_heads * int(length), dtypes=(torch.float32,),
+             where="decode_attend_noalloc")
+    _check(_decode_attend_noalloc(ctypes.byref(desc), _ptr(codec_dev), _ptr(cache), int(length), _ptr(q),
+                                  _dtype_code(q), q_heads, int(q_pos), float(rope_base), float(scale), _ptr(out),
+                                  _ptr(scores), _stream(stream)),
+           "tq_decode_attend_noalloc")
 
 
 def decode_window_workspace_bytes(desc: CacheDesc, q_heads: int, length: int) -> int:
