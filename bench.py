@@ -16,7 +16,8 @@ events the library records around that kernel), the CPU oracle timed on a bounde
 sample on this host, and -- outside the timed steps -- the vector-search workload
 (10^6 x 1536 database build, search of 1024 queries, recall@10).
 
-    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--spinup-ms 300] [--no-cpu-baseline] [--no-search]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 20] [--spinup-ms 300] [--no-cpu-baseline]
+                    [--sections widths,nsn,polar,window,configs,search] [--no-search]
 """
 from __future__ import annotations
 
@@ -205,6 +206,139 @@ def search_bench(tq, W, dev, ev, stream):
         "search_equiv_tflops": round(pairs * 2 * (w.d + w.m) / sm / 1e9, 2),
         "recall_at_10": round(hit / (w.nq * w.k), 4), "recall_1_at_10": round(top1 / w.nq, 4),
     }
+
+
+def time_us(fn, ev, stream, reps: int = 20, warm_ms: float = 100.0):
+    """p10 / median / p90 (us) of fn() over `reps` calls, each bracketed by HIP events on the
+    stream, after `warm_ms` of untimed calls (the clock ramps up under load)."""
+    import torch
+
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < warm_ms * 1e-3:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    E = [(ev.create(), ev.create()) for _ in range(reps)]
+    for e0, e1 in E:
+        ev.record(e0, stream)
+        fn()
+        ev.record(e1, stream)
+    torch.cuda.synchronize()
+    return pct_us([ev.elapsed_ms(e0, e1) for e0, e1 in E])
+
+
+def configs_bench(tq, W, dev, ev, stream):
+    """The other decode workloads, outside the timed steps (medians of event-timed calls):
+      * llama3_8b: one decode step over all 32 layers (32 tq_decode_attend calls, one per
+        layer cache, 13.69 GB of packed records), and the quantize of one layer's prefill;
+      * esm2_650m: the quantize of all 33 layers' 1024 tokens, and one decode step over
+        the 33 layers (36.5 MB of packed records: it fits in the 256 MB last-level cache, so
+        the step is latency-bound and reported in us per layer);
+      * single_head: quantize of the 1024 fp32 tokens and one decode with its 1024 scores."""
+    import torch
+
+    out_rec = {}
+    rec_bytes = lambda w: (w.bits_k * w.d + w.m) // 8 + 4 + w.bits_v * w.d // 8 + 2
+
+    # ---- llama3_8b: 32 layers, 16 x 8 units x 32768 tokens
+    w = W.LLAMA3_8B
+    T, units = w.context, w.batch * w.kv_heads
+    codec = tq.Codec(w.d, w.bits_k, w.bits_v, w.m, seed=0, device=dev)
+    caches, qs = [], []
+    prefill_us = None
+    for layer in range(w.layers):
+        K, V = W.gen_kv(w, layer, device=dev)
+        c = tq.PackedCache(w.batch, w.kv_heads, w.d, T, w.bits_k, w.bits_v, w.m, device=dev)
+        if layer == 0:
+            prefill_us = time_us(lambda: tq.quantize_kv(c.desc, codec.dev, c.buf, K, V, 0, w.rope_base), ev,
+                                 stream, reps=5, warm_ms=50.0)
+        tq.quantize_kv(c.desc, codec.dev, c.buf, K, V, 0, w.rope_base)
+        del K, V
+        caches.append(c)
+        qs.append(W.gen_q(w, layer, device=dev))
+    torch.cuda.synchronize()
+    out = torch.empty((w.batch, w.q_heads, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.decode_workspace_bytes(caches[0].desc, w.q_heads, T), dtype=torch.uint8, device=dev)
+
+    def llama_step():
+        for layer in range(w.layers):
+            tq.decode_attend(caches[layer].desc, codec.dev, caches[layer].buf, T, qs[layer], w.q_pos, w.rope_base,
+                             out, ws=ws)
+
+    st = time_us(llama_step, ev, stream, reps=20)
+    step_bytes = w.layers * units * T * rec_bytes(w)
+    out_rec["llama3_8b"] = {
+        "workload": ("llama3_8b: 32 layers, 32 q-heads / 8 kv-heads, d 128, batch 16, context 32768, bf16 N(0,1) "
+                     "+ 3 channels x10, RoPE 500000; one decode step = one tq_decode_attend per layer"),
+        "step_us_p10_p50_p90": st, "layer_us": round(st[1] / w.layers, 2),
+        "packed_bytes_per_step": step_bytes,
+        "step_gbs": round(step_bytes / (st[1] * 1e-6) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (st[1] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_splits": tq.decode_splits(caches[0].desc, w.q_heads, T),
+        "prefill_quantize_us_p10_p50_p90": prefill_us,
+        "prefill_quantize_mtokens_s": round(w.batch * T / (prefill_us[1] * 1e-6) / 1e6, 1),
+    }
+    del caches, qs, out, ws
+    torch.cuda.empty_cache()
+    log(f"[bench] llama3_8b {out_rec['llama3_8b']}")
+
+    # ---- esm2_650m: 33 layers, 20 heads (G = 1), d 64, 1024 tokens
+    w = W.ESM2_650M
+    T, units = w.context, w.batch * w.kv_heads
+    codec = tq.Codec(w.d, w.bits_k, w.bits_v, w.m, seed=0, device=dev)
+    kvs = [W.gen_kv(w, layer, device=dev) for layer in range(w.layers)]
+    qs = [W.gen_q(w, layer, device=dev) for layer in range(w.layers)]
+    caches = [tq.PackedCache(w.batch, w.kv_heads, w.d, T, w.bits_k, w.bits_v, w.m, device=dev)
+              for _ in range(w.layers)]
+
+    def esm_quantize():
+        for layer in range(w.layers):
+            tq.quantize_kv(caches[layer].desc, codec.dev, caches[layer].buf, kvs[layer][0], kvs[layer][1], 0,
+                           w.rope_base)
+
+    qt = time_us(esm_quantize, ev, stream, reps=10, warm_ms=50.0)
+    out = torch.empty((w.batch, w.q_heads, w.d), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.decode_workspace_bytes(caches[0].desc, w.q_heads, T), dtype=torch.uint8, device=dev)
+
+    def esm_step():
+        for layer in range(w.layers):
+            tq.decode_attend(caches[layer].desc, codec.dev, caches[layer].buf, T, qs[layer], w.q_pos, w.rope_base,
+                             out, ws=ws)
+
+    st = time_us(esm_step, ev, stream, reps=20)
+    step_bytes = w.layers * units * T * rec_bytes(w)
+    out_rec["esm2_650m"] = {
+        "workload": ("esm2_650m: 33 layers x 20 heads x d 64, batch 1, 1024 tokens, bf16 Student-t (nu 3) + 3 "
+                     "channels x15, RoPE 10000; keys 2-bit + QJL m 64, values 3-bit"),
+        "quantize_all_layers_us_p10_p50_p90": qt,
+        "quantize_mtokens_s": round(w.layers * T / (qt[1] * 1e-6) / 1e6, 2),
+        "step_us_p10_p50_p90": st, "layer_us": round(st[1] / w.layers, 2),
+        "packed_bytes_per_step": step_bytes,
+        "cache_resident": "MALL (36.5 MB of records in the 256 MB last-level cache): latency-bound, no HBM roofline",
+    }
+    del kvs, qs, caches, out, ws
+    log(f"[bench] esm2_650m {out_rec['esm2_650m']}")
+
+    # ---- single_head: d 128, 1024 fp32 tokens, one query, no RoPE
+    w = W.SINGLE_HEAD
+    T = w.context
+    codec = tq.Codec(w.d, w.bits_k, w.bits_v, w.m, seed=0, device=dev)
+    K, V = W.gen_kv(w, device=dev)
+    q = W.gen_q(w, device=dev)
+    c = tq.PackedCache(1, 1, w.d, T, w.bits_k, w.bits_v, w.m, device=dev)
+    qt = time_us(lambda: tq.quantize_kv(c.desc, codec.dev, c.buf, K, V, 0, 0.0), ev, stream, reps=20)
+    out = torch.empty((1, 1, w.d), dtype=torch.float32, device=dev)
+    sc = torch.empty((1, 1, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.decode_workspace_bytes(c.desc, 1, T), dtype=torch.uint8, device=dev)
+    st = time_us(lambda: tq.decode_attend(c.desc, codec.dev, c.buf, T, q, w.q_pos, 0.0, out, scores=sc, ws=ws),
+                 ev, stream, reps=20)
+    out_rec["single_head"] = {
+        "workload": "single_head: d 128, 1024 fp32 N(0,1) tokens + 4 channels x20, no RoPE, one query",
+        "quantize_us_p10_p50_p90": qt, "decode_with_scores_us_p10_p50_p90": st,
+    }
+    log(f"[bench] single_head {out_rec['single_head']}")
+    return out_rec
 
 
 def timed_calls(fn, ev, stream, E):
@@ -468,6 +602,9 @@ def main():
                          "first tens of milliseconds of load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-search", action="store_true", help="skip the vector-search measurement")
+    ap.add_argument("--sections", default="widths,nsn,polar,window,configs,search",
+                    help="comma-separated measurements beside the timed steps (any of widths, nsn, "
+                         "polar, window, configs, search; empty for none)")
     ap.add_argument("--copy-calibration", type=int, default=1024,
                     help="size in MiB of the plain streaming copy that is timed (measured HBM "
                          "bandwidth) and whose counters scale the decode kernel's (0: skip)")
@@ -572,32 +709,40 @@ def main():
         del src, dst
         log(f"[bench] streaming copy (elementwise neg, {n} bytes in + out): {stream_gbs:.0f} GB/s")
 
+    sections = set(x for x in args.sections.split(",") if x)
+    if args.no_search:
+        sections = set()
     widths = None
-    if not args.no_search:
+    if "widths" in sections:
         log("[bench] key bit-width variants and logits-only ...")
         widths = key_width_bench(tq, W, w, K, V, q, dev, ev, stream)
         log(f"[bench] key widths {widths}")
 
     nsn = None
-    if not args.no_search:
+    if "nsn" in sections:
         log("[bench] NSN cache ...")
         nsn = nsn_bench(tq, w, K, V, q, dev, ev, stream)
         log(f"[bench] nsn {nsn}")
 
     polar = None
-    if not args.no_search:
+    if "polar" in sections:
         log("[bench] PolarQuant cache ...")
         polar = polar_bench(tq, w, K, V, q, dev, ev, stream)
         log(f"[bench] polar {polar}")
 
     window = None
-    if not args.no_search:
+    if "window" in sections:
         log("[bench] full-precision window and decode steps ...")
         window = window_bench(tq, w, K, V, q, cache, codec, dev, ev, stream)
         log(f"[bench] window {window}")
 
+    configs = None
+    if "configs" in sections:
+        log("[bench] other decode workloads (llama3_8b 32 layers, esm2_650m 33 layers, single head) ...")
+        configs = configs_bench(tq, W, dev, ev, stream)
+
     search = None
-    if not args.no_search:
+    if "search" in sections:
         log("[bench] vector search workload ...")
         search = search_bench(tq, W, dev, ev, stream)
         log(f"[bench] search {search}")
@@ -654,6 +799,7 @@ def main():
         "nsn": nsn,
         "polar": polar,
         "search": search,
+        "configs": configs,
     }
     print(json.dumps(rec), flush=True)
 
