@@ -156,12 +156,19 @@ __global__ void k_cache_init(uint32_t *hdr, tq_cache_desc c) {
 }
 
 // ------------------------------------------------------------------ quantize
+// RoPE frequencies of one append: theta_j = base^(-2j/d) and its cos and sin in fp64, for
+// j < d/2 (d <= 128), computed once per call on the host and passed with the arguments.
+struct RopeFreq {
+  double theta[64], c[64], s[64];
+};
+
 struct QuantArgs {
   CodecPtrs cp;
   CachePtrs ch;
   const void *k, *v;
   int start, n_new, capacity, bits_k, bits_v, m, units;
   float rope_base;
+  RopeFreq rf;
 };
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -566,10 +573,10 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   if (use_rope) {
     constexpr int nblk = 256 / H, per = 64 / nblk;
     const int j = tid % H, i0 = (tid / H) * per;
-    const double theta = pow(double(a.rope_base), -2.0 * double(j) / double(D));
-    double s, c, sd, cd;
-    sincos(double(p0 + i0) * theta, &s, &c);
-    sincos(theta, &sd, &cd);
+    // the angle of the thread's first row; the rows below it by the rotation recurrence
+    const double cd = a.rf.c[j], sd = a.rf.s[j];
+    double s, c;
+    sincos(double(p0 + i0) * a.rf.theta[j], &s, &c);
     for (int i = 0; i < per; ++i) {
       rope_s[(i0 + i) * RH + j] = make_double2(c, s);
       const double cn = c * cd - s * sd;
@@ -3889,6 +3896,14 @@ tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_d
   a.m = desc->m;
   a.units = desc->batch * desc->kv_heads;
   a.rope_base = rope_base;
+  if (rope_base != 0.0f && small) {
+    for (int j = 0; j < d / 2; ++j) {
+      const double th = std::pow(double(rope_base), -2.0 * double(j) / double(d));
+      a.rf.theta[j] = th;
+      a.rf.c[j] = std::cos(th);
+      a.rf.s[j] = std::sin(th);
+    }
+  }
   hipStream_t s = hipStream_t(stream);
   if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
   if (small) {
