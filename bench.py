@@ -783,6 +783,9 @@ def main():
         "roofline": {
             "kernel": "k_decode_lds<128> (split-K decode over the packed cache)",
             "bound": "hbm",
+            "limiter": ("instruction issue, not HBM: VALU + MFMA keep the SIMDs busy 72% of the launch "
+                        "with HBM traffic 1.01x the algorithmic bytes "
+                        "(profiles/decode_lds_long_context.md)"),
             "achieved": round(kern_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
