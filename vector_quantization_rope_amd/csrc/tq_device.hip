@@ -647,36 +647,41 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
     uint32_t hA[4] = {0u, 0u, 0u, 0u}, hB[4] = {0u, 0u, 0u, 0u};
     double rr = 0.0;
     if constexpr (KK == 4) {
-      // The stored codebook is odd (c[3 - k] = -c[k], t = {-s, 0, s} / sc), so with
-      // g0 = [x >= 0] and g1 = [x >= copysign(s, x)] the code is 2 g0 + g1: the same
-      // comparisons as x >= sc t_k for each k, taken from the sign bit of an exact fp64
-      // difference rather than as lane masks.  The centroid is +-(inner or outer).
+      // The stored codebook is odd (c[3 - k] = -c[k], t = {-s, 0, s} / sc).  With a = |x|
+      // and d = a - s, the code's upper bit is [x >= 0] and its lower bit
+      // [x >= copysign(s, x)]: the sign bits of x and of d agree.  The centroid is
+      // +-outer when d >= 0, else +-inner, with the sign of x.  The sign bits come from
+      // the fp64 high words and are shifted into the plane words (top coordinate first);
+      // an exact tie a = s falls to the sign of d's zero, on a decision boundary.  A zero
+      // coordinate can carry a negative sign only in a zero vector, fixed after the loop.
       const double s1 = sc * double(cb_s[1][2]);
       const double wo = nb16 * double(cb_s[0][3]), wi = nb16 * double(cb_s[0][2]);
       const uint64_t uo = uint64_t(__double_as_longlong(wo)), ui = uint64_t(__double_as_longlong(wi));
-      uint32_t n0A = 0u, n0B = 0u, n1A = 0u, n1B = 0u;   // inverted plane bits
+      const uint32_t olo = uint32_t(uo), ohi = uint32_t(uo >> 32), ilo = uint32_t(ui), ihi = uint32_t(ui >> 32);
+      uint32_t sxA = 0u, sxB = 0u, sgA = 0u, sgB = 0u;   // sign bits of x; sign(x) xor sign(d)
+      auto code2 = [&](double &xe, uint32_t &sx, uint32_t &sg) {
+        const uint32_t xh = uint32_t(uint64_t(__double_as_longlong(xe)) >> 32);
+        const uint32_t dh = uint32_t(uint64_t(__double_as_longlong(fabs(xe) - s1)) >> 32);
+        sx = __builtin_amdgcn_alignbit(sx, xh, 31);        // sx << 1 | sign(x)
+        sg = __builtin_amdgcn_alignbit(sg, xh ^ dh, 31);   // sg << 1 | (sign(x) != sign(d))
+        const uint32_t m = uint32_t(int32_t(dh) >> 31);    // all ones: the inner centroid
+        const uint32_t wl = (ilo & m) | (olo & ~m);
+        const uint32_t wh = (((ihi & m) | (ohi & ~m)) & 0x7FFFFFFFu) | (xh & 0x80000000u);
+        xe -= __longlong_as_double(int64_t((uint64_t(wh) << 32) | wl));
+        rr = fma(xe, xe, rr);
+      };
 #pragma unroll
-      for (int e = 0; e < C; ++e) {
-        const double xs = x[e] + 0.0;   // -0 -> +0: x >= 0 holds for both zeros
-        const uint32_t n0 = uint32_t(uint64_t(__double_as_longlong(xs)) >> 63);            // x < 0
-        const uint32_t n1 = uint32_t(uint64_t(__double_as_longlong(x[e] - copysign(s1, xs))) >> 63);
-        const uint64_t m = uint64_t(0) - uint64_t(n0 ^ n1);   // inner centroid when g0 != g1
-        const double w = copysign(__longlong_as_double(int64_t((uo & ~m) | (ui & m))), xs);
-        if (e < HC) {
-          n0A |= n0 << e;
-          n1A |= n1 << e;
-        } else {
-          n0B |= n0 << (e - HC);
-          n1B |= n1 << (e - HC);
-        }
-        x[e] -= w;
-        rr = fma(x[e], x[e], rr);
+      for (int e = HC - 1; e >= 0; --e) {
+        code2(x[e], sxA, sgA);
+        code2(x[HC + e], sxB, sgB);
       }
       constexpr uint32_t hm = HC >= 32 ? 0xFFFFFFFFu : (1u << HC) - 1u;
-      hA[0] = ~n1A & hm;
-      hB[0] = ~n1B & hm;
-      hA[1] = ~n0A & hm;
-      hB[1] = ~n0B & hm;
+      // a zero vector takes code 2 (the first positive centroid) everywhere
+      const uint32_t zm = nu > 0.0 ? 0u : 0xFFFFFFFFu;
+      hA[0] = ~sgA & hm & ~zm;
+      hB[0] = ~sgB & hm & ~zm;
+      hA[1] = (~sxA | zm) & hm;
+      hB[1] = (~sxB | zm) & hm;
     } else if constexpr (KK > 0) {
       double sk[KK - 1], wk[KK];
 #pragma unroll
@@ -795,23 +800,28 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
 #pragma unroll
     for (int i = 0; i < C / 4; ++i) cw[i] = 0u;
     if constexpr (KV > 0) {
-      // odd codebook: the code is h [x >= 0] + #{i : x >= copysign(s_i, x)} over the h - 1
-      // positive thresholds s_i = sc t_{h-1+i} (the same comparisons as x >= sc t_k for
-      // every k, from the sign bits of exact fp64 differences)
+      // odd codebook: the code counts the boundaries at or below x; with the h - 1 positive
+      // thresholds s_i = sc t_{h-1+i} it follows from |x| against them and the sign of x
       constexpr int h = KV / 2;
       double sp[h > 1 ? h - 1 : 1];
 #pragma unroll
       for (int i = 1; i < h; ++i) sp[i - 1] = sc * double(cb_s[3][h - 1 + i]);
 #pragma unroll
       for (int e = 0; e < C; ++e) {
-        const double xs = x[e] + 0.0;   // -0 -> +0
-        const uint32_t n0 = uint32_t(uint64_t(__double_as_longlong(xs)) >> 63);
+        // nb = the thresholds above |x|: the code is nb for x < 0 and 2h - 1 - nb =
+        // nb ^ (2h - 1) for x >= 0 (h a power of two); sign bits from the fp64 high words
+        const uint32_t xh = uint32_t(uint64_t(__double_as_longlong(x[e])) >> 32);
+        const double ax = fabs(x[e]);
         uint32_t nb = 0u;
 #pragma unroll
-        for (int i = 1; i < h; ++i)
-          nb += uint32_t(uint64_t(__double_as_longlong(x[e] - copysign(sp[i - 1], xs))) >> 63);
-        const uint32_t code = uint32_t(h) * (1u - n0) + uint32_t(h - 1) - nb;
+        for (int i = 1; i < h; ++i) nb += uint32_t(uint64_t(__double_as_longlong(ax - sp[i - 1])) >> 63);
+        const uint32_t code = nb ^ ((2u * uint32_t(h) - 1u) & ~uint32_t(int32_t(xh) >> 31));
         cw[e / 4] |= code << (8 * (e % 4));
+      }
+      // a zero vector (whose coordinates may carry negative zeros) takes code h everywhere
+      if (!(nu > 0.0)) {
+#pragma unroll
+        for (int i = 0; i < C / 4; ++i) cw[i] = uint32_t(h) * 0x01010101u;
       }
     } else {
       const int K = 1 << a.bits_v;
