@@ -272,35 +272,38 @@ __device__ __forceinline__ void fwht_group4(double *x, int q) {
   for (int e = 0; e < 2 * HC; ++e) x[e] = fma(s2, x[e], dpp_f64<kDppXor2>(x[e]));
 }
 
-// N consecutive input elements starting at element `off`, converted exactly to fp64
-// (16-byte vector loads; off * sizeof(element) is a multiple of 16).
+// The 16-byte vectors of N consecutive input elements (off * sizeof(element) a multiple of
+// 16), loaded into registers now and converted by raw_to_f64 later, so that the load's
+// latency overlaps other work.
 template <int DT, int N>
-__device__ __forceinline__ void load_chunk(const void *base, size_t off, double *x) {
-  if constexpr (DT == TQ_F32) {
-    const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off);
+struct RawRow {
+  static constexpr int NV = DT == TQ_F32 ? N / 4 : N / 8;
+  uint4 v[NV];
+};
+
+template <int DT, int N>
+__device__ __forceinline__ void load_raw(const void *base, size_t off, RawRow<DT, N> &r) {
+  const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const char *>(base) +
+                                                   off * (DT == TQ_F32 ? 4 : 2));
 #pragma unroll
-    for (int i = 0; i < N / 4; ++i) {
-      const float4 v = p[i];
-      x[4 * i] = v.x;
-      x[4 * i + 1] = v.y;
-      x[4 * i + 2] = v.z;
-      x[4 * i + 3] = v.w;
-    }
-  } else {
-    const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off);
+  for (int i = 0; i < RawRow<DT, N>::NV; ++i) r.v[i] = p[i];
+}
+
+template <int DT, int N>
+__device__ __forceinline__ void raw_to_f64(const RawRow<DT, N> &r, double *x) {
 #pragma unroll
-    for (int i = 0; i < N / 8; ++i) {
-      const uint4 v = p[i];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int i = 0; i < RawRow<DT, N>::NV; ++i) {
+    const uint32_t w[4] = {r.v[i].x, r.v[i].y, r.v[i].z, r.v[i].w};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if constexpr (DT == TQ_BF16) {
-          x[8 * i + 2 * k] = double(__uint_as_float(w[k] << 16));
-          x[8 * i + 2 * k + 1] = double(__uint_as_float(w[k] & 0xFFFF0000u));
-        } else {
-          x[8 * i + 2 * k] = double(f16_bits_to_float(w[k] & 0xFFFFu));
-          x[8 * i + 2 * k + 1] = double(f16_bits_to_float(w[k] >> 16));
-        }
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (DT == TQ_F32) {
+        x[4 * i + k] = double(__uint_as_float(w[k]));
+      } else if constexpr (DT == TQ_BF16) {
+        x[8 * i + 2 * k] = double(__uint_as_float(w[k] << 16));
+        x[8 * i + 2 * k + 1] = double(__uint_as_float(w[k] & 0xFFFF0000u));
+      } else {
+        x[8 * i + 2 * k] = double(f16_bits_to_float(w[k] & 0xFFFFu));
+        x[8 * i + 2 * k + 1] = double(f16_bits_to_float(w[k] >> 16));
       }
     }
   }
@@ -563,6 +566,19 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   const size_t row = size_t(unit) * size_t(a.n_new) + size_t(valid ? p - a.start : 0);
   bool over = false;
 
+  // the token's key row, and for 2-byte inputs its value row, are requested before the
+  // RoPE table is built, so that their latency overlaps the table and the key work
+  constexpr bool kEarlyV = DT != TQ_F32;
+  RawRow<DT, HC> rk0, rk1, rv0, rv1;
+  if (valid) {
+    load_raw<DT, HC>(a.k, row * D + HC * q, rk0);
+    load_raw<DT, HC>(a.k, row * D + H + HC * q, rk1);
+    if (kEarlyV && a.bits_v > 0) {
+      load_raw<DT, HC>(a.v, row * D + HC * q, rv0);
+      load_raw<DT, HC>(a.v, row * D + H + HC * q, rv1);
+    }
+  }
+
   if (tid < kMaxCodes) {
     cb_s[0][tid] = a.cp.ck[tid];
     cb_s[1][tid] = a.cp.tk[tid];
@@ -600,8 +616,8 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   // ------------------------------------------------------------ keys
   double x[C];
   if (valid) {
-    load_chunk<DT, HC>(a.k, row * D + HC * q, x);
-    load_chunk<DT, HC>(a.k, row * D + H + HC * q, x + HC);
+    raw_to_f64<DT, HC>(rk0, x);
+    raw_to_f64<DT, HC>(rk1, x + HC);
   } else {
 #pragma unroll
     for (int e = 0; e < C; ++e) x[e] = 0.0;
@@ -766,8 +782,12 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   // ------------------------------------------------------------ values
   if (a.bits_v > 0) {
     if (valid) {
-      load_chunk<DT, HC>(a.v, row * D + HC * q, x);
-      load_chunk<DT, HC>(a.v, row * D + H + HC * q, x + HC);
+      if constexpr (!kEarlyV) {
+        load_raw<DT, HC>(a.v, row * D + HC * q, rv0);
+        load_raw<DT, HC>(a.v, row * D + H + HC * q, rv1);
+      }
+      raw_to_f64<DT, HC>(rv0, x);
+      raw_to_f64<DT, HC>(rv1, x + HC);
     } else {
 #pragma unroll
       for (int e = 0; e < C; ++e) x[e] = 0.0;
