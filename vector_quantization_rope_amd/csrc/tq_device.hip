@@ -2716,21 +2716,90 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
 
 // ------------------------------------------------------------------ PolarQuant decode
 // Split-K decode over PolarQuant records ([TurboQuant] "PolarQuant" as stage 1, QJL on
-// the key residual).  Per 64-token chunk of the block's range: the records come in with
-// 16-byte loads (the next chunk's in flight while this one is scored) and are staged in
-// LDS; four threads per token decode its angle tree, one quarter of the coordinates each
-// (the two top levels give the quarter's radius, its own subtree the rest).  A key
-// quarter is dotted with every head's rotated query in registers; a value quarter, times
-// the value norm, goes to LDS as fp16 hi + lo.  The key score is n <q_rot, yhat> plus the
-// QJL term, whose sign-bit sums run on int8 MFMA against the query's S q digit rows; then
-// the online softmax (one head per wave) and the value sums on fp16 MFMA.  The sums stay
-// in the rotated basis: the partials are the merge's usual input.
+// the key residual).  Each of a block's 8 waves walks its own 32-token steps of the
+// block's range with its own online-softmax state (a split inside the split); the block
+// combines the 8 states at the end.  A step's records come in with 16- and 8-byte loads
+// (the wave's next step in flight meanwhile) and are staged in the wave's own LDS rows.
+//   keys: lane = (token, quarter of the coordinates): the lane decodes its quarter's
+//         angle subtree (the two top levels give the quarter's radius), splits the
+//         coordinates into fp16 hi + lo and feeds them to v_mfma_f32_16x16x32_f16 as the
+//         B operand; the A rows are the heads' rotated queries as fp16 hi + lo, so the
+//         four cross products of hi and lo parts all land in fp32.
+//   QJL:  the sign bits against the S q digit rows on v_mfma_i32_32x32x32_i8.
+//   values: lane = (subtree of d / 16 coordinates, token of a group of 4): the decoded
+//         coordinates, times the value norm, are the B operand of v_mfma_f32_16x16x4_f32
+//         with the softmax weights as A, so the value sums never leave fp32 and need no
+//         transposition through LDS.
+// The sums stay in the rotated basis: the partials are the merge's usual input.
 
 // a compile-time int carried by a value (selects a templated lambda body)
 template <int V>
 struct IntTag {
   static constexpr int value = V;
 };
+
+// f(IntTag<B>), f(IntTag<B - 1>), ..., f(IntTag<E>)
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for_down(F &&f) {
+  if constexpr (B >= E) {
+    f(IntTag<B>{});
+    static_for_down<B - 1, E>(f);
+  }
+}
+
+// First bit of the 2-bit angle codes of level lv >= 2 in a PolarQuant record of d
+// coordinates: the d / 2 level-1 codes (4 bits each) come first, then every level's
+// nodes in order, root last.
+__host__ __device__ constexpr int polar_level_bit(int d, int lv) { return 2 * d + 2 * (d / 2 - (d >> (lv - 1))); }
+
+// Bits from C + W j on of a record held as dwords, for 0 <= j < JN: one read of a fixed
+// dword when every j's W bits lie in the dword holding bit C.
+template <int C, int W, int JN>
+__device__ __forceinline__ uint32_t rec_bits(const uint32_t *w, int j) {
+  if constexpr ((C & 31) + W * JN <= 32) {
+    return w[C >> 5] >> ((C & 31) + W * j);
+  } else {
+    const int p = C + W * j;
+    return w[p >> 5] >> (p & 31);
+  }
+}
+
+// Radii of the level-1 pairs of subtree J (root at level S, 0 <= J < JN) of a record:
+// r0 times cos or sin of each ancestor's angle (the branch J takes), then each subtree
+// level splits every radius into its cos and sin parts.  r gets 2^(S-1) radii.
+template <int D, int S, int JN>
+__device__ __forceinline__ void polar_pair_radii(const uint32_t *w, int J, float r0, const float2 (*csh)[4],
+                                                 float *r) {
+  constexpr int L = D == 128 ? 7 : 6;
+  static_for_down<L, S + 1>([&](auto t) {
+    constexpr int lv = decltype(t)::value, up = lv - S;
+    constexpr int nodes = (JN + (1 << up) - 1) >> up;
+    const uint32_t code = rec_bits<polar_level_bit(D, lv), 2, nodes>(w, J >> up) & 3u;
+    const float2 cs = csh[lv - 2][code];
+    r0 *= ((J >> (up - 1)) & 1) ? cs.y : cs.x;
+  });
+  r[0] = r0;
+  static_for_down<S, 2>([&](auto t) {
+    constexpr int lv = decltype(t)::value, n = 1 << (S - lv);
+    const uint32_t f = rec_bits<polar_level_bit(D, lv), 2 * n, JN>(w, J);
+#pragma unroll
+    for (int i = n - 1; i >= 0; --i) {
+      const float2 cs = csh[lv - 2][(f >> (2 * i)) & 3u];
+      const float rr = r[i];
+      r[2 * i] = rr * cs.x;
+      r[2 * i + 1] = rr * cs.y;
+    }
+  });
+}
+
+// Orders a wave's LDS writes before its later reads of other lanes' data (and the reads
+// before later writes): the LDS serves one wave's requests in order, so only the
+// compiler's ordering is at stake.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 struct PolarArgs {
   const uint8_t *krec;     // [units][capacity][kb]: 3 D / 8 angle bytes, m / 8 sign bytes
@@ -2745,284 +2814,349 @@ struct PolarArgs {
   float scale_log2;
 };
 
+typedef __fp16 h2v __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
 template <int D>
 __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
-  // m = D QJL rows; 8 waves: decode by eighths of a token (key or value, one quarter of
-  // the coordinates), scores and softmax one head per wave, values on fp16 MFMA by blocks
-  // of 16 coordinates
-  constexpr int L = D == 128 ? 7 : 6, CH = 64, GM = 8, NT = 512;
-  constexpr int VB = 3 * D / 8, KW = (3 * D / 8 + D / 8) / 4, VW = VB / 4;   // record dwords
+  // m = D QJL rows, at most 8 heads
+  constexpr int L = D == 128 ? 7 : 6, NW = 8, ST = 32;
+  constexpr int KW = D / 8, VW = 3 * D / 32;    // record dwords: key (angles, signs), value
   constexpr int KWP = KW + 1, VWP = VW + 1;     // odd LDS strides: one token per bank
-  constexpr int NQ = D / 4;                     // coordinates per decode quarter
-  constexpr int NCB = D / 16, TP = CH + 8;      // value coordinate blocks; padded token rows
-  // p is carried as 256 p in the fp16 hi + lo parts (more of the small ones stay normal);
-  // the sums are scaled back at the end
-  constexpr float kPScale = 256.0f;
-  constexpr int NKD = (CH * KW + NT - 1) / NT, NVD = (CH * VW + NT - 1) / NT;
-  constexpr int HI0 = 2 * D / 32, NHI = KW - D / 32 - HI0;   // dwords of the 2-bit codes
-  __shared__ __align__(16) float qr[GM][D];
-  __shared__ float psk[4][GM][CH];              // key score parts by quarter
-  // value rows times the value norm as fp16 hi + lo, transposed ([coordinate][token]) so
-  // that an MFMA B operand (8 tokens of one coordinate) is one 16-byte read; and the
-  // softmax weights in the A operand's order: rows 0..7 the heads' hi parts, 8..15 lo
-  __shared__ __align__(16) _Float16 vth[D][TP];
-  __shared__ __align__(16) _Float16 vtl[D][TP];
-  __shared__ __align__(16) _Float16 pt[16][TP];
-  __shared__ float qj[GM][CH];                 // QJL term of every (head, token) of the chunk
-  __shared__ float qjc[2][GM];                 // its coefficients: 2 qjl 2^16 / 2^e and qjl sum S q
-  __shared__ __align__(16) float mstat[3][GM];
-  __shared__ float2 cs1[16];                   // level-1 centroids' (cos, sin)
-  __shared__ float2 csh[L - 1][4];             // higher levels' (cos, sin): [level - 2][code]
-  __shared__ uint32_t krs[CH * KWP];
-  __shared__ uint32_t vrs[CH * VWP];
-  __shared__ uint32_t kns[CH];
-  __shared__ float vns[CH];
-  // the wave index is made wave-uniform, so that the decode role's quarter is a scalar choice
+  constexpr int NQ = D / 4, NK = D / 32;        // key quarter; f16 MFMAs per hi or lo part
+  constexpr int CPL = D / 16;                   // value coordinates per lane (a subtree)
+  constexpr int SK = L - 2, SV = CPL == 8 ? 3 : 2;
+  constexpr int KQ = ST * KW / 4, KQL = (KQ + 63) / 64;   // 16-byte key loads per step, per lane
+  constexpr int VQ = ST * VW / 2, VQL = (VQ + 63) / 64;   // 8-byte value loads
+  // the decoded key coordinates (|y| <= 1) are scaled by 2^8 before the split, and each
+  // head's query by a power of two that brings its largest element into [2^7, 2^8): the
+  // fp16 parts stay normal and far from overflow; the dot products are scaled back
+  constexpr float kYScale = 256.0f;
+  __shared__ __align__(16) v8h qa[NK][64];      // key A operands in lane order
+  __shared__ __align__(16) v4i qsa[NK][64];     // QJL A operands (S q digit rows) in lane order
+  __shared__ float2 cs1[16];                    // level-1 centroids' (cos, sin)
+  __shared__ float2 csh[L - 1][4];              // higher levels' (cos, sin): [level - 2][code]
+  __shared__ float qsc[8], qiv[8];              // query scale per head and 1 / (scale 2^8)
+  __shared__ float qjc[2][8];                   // 2 qjl 2^16 / 2^e and qjl sum S q per head
+  __shared__ uint32_t krs[NW][ST * KWP];        // each wave's staged records
+  __shared__ uint32_t vrs[NW][ST * VWP];
+  __shared__ uint32_t kns[NW][ST];
+  __shared__ float vns[NW][ST];
+  __shared__ __align__(16) float dts[NW][ST][8];   // <q_rot, yhat> by token and head
+  __shared__ __align__(16) float pts[NW][ST][8];   // softmax weights by token and head
+  __shared__ float wst[2][NW][8];               // per wave: reference maximum and sum per head
+  __shared__ float ys[8][D];                    // the block's value sums
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = blockIdx.x, split = blockIdx.y;
   const int b = unit / a.kv_heads, g = unit % a.kv_heads, G = a.G, hq0 = g * G;
   const int t_begin = split * a.chunk, t_end = min(a.length, t_begin + a.chunk);
   const size_t ubase = size_t(unit) * a.capacity;
-  uint32_t kreg[NKD], vreg[NVD];
-  uint32_t knr = 0u;
-  float vnr = 0.0f;
-  auto fetch = [&](int c0) {
-    const int cn = min(CH, t_end - c0);
-    const uint32_t *ks = reinterpret_cast<const uint32_t *>(a.krec + (ubase + c0) * (KW * 4));
-    const uint32_t *vs = reinterpret_cast<const uint32_t *>(a.vrec + (ubase + c0) * VB);
-#pragma unroll
-    for (int i = 0; i < NKD; ++i) {
-      const int k = tid + NT * i;
-      kreg[i] = k < cn * KW ? ks[k] : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < NVD; ++i) {
-      const int k = tid + NT * i;
-      vreg[i] = k < cn * VW ? vs[k] : 0u;
-    }
-    if (tid < cn) {
-      knr = a.knorm[ubase + c0 + tid];
-      vnr = f16_bits_to_float(a.vnorm[ubase + c0 + tid]);
-    }
-  };
-  if (t_begin < t_end) fetch(t_begin);
-  // decode role: lane = token, wave = key (kv = 0) or value (kv = 1) and quarter qq
-  const int tt = lane, kv = wv >> 2, qq = wv & 3;
+  const float *qrow = a.qp + size_t(b * a.q_heads + hq0) * a.qstride;
   if (tid < 16) cs1[tid] = make_float2(a.pcs[2 * tid], a.pcs[2 * tid + 1]);
   if (tid < 4 * (L - 1)) {
     const int lv = 2 + tid / 4, c = tid % 4;
     csh[lv - 2][c] = make_float2(a.pcs[((lv - 1) * 16 + c) * 2], a.pcs[((lv - 1) * 16 + c) * 2 + 1]);
   }
-  for (int i = tid; i < GM * D; i += NT) {
-    const int h = i / D, j = i % D;
-    qr[h][j] = h < G ? a.qp[size_t(b * a.q_heads + hq0 + h) * a.qstride + j] : 0.0f;
-  }
-  // the S q digit rows of this unit's heads (the int8 MFMA A operand of the QJL sums, rows
-  // digit * 8 + head) and the two QJL coefficients per head (zero for absent heads)
   const uint8_t *qpk = a.qpack + size_t(unit) * qpack_unit_bytes(D);
-  v4i As[D / 32];
-  {
-    const v4i *src = reinterpret_cast<const v4i *>(qpk);
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) As[c] = src[((kSqVec * 32 + (lane & 31)) * 2 + (lane >> 5)) * (D / 32) + c];
-  }
-  if (tid < GM) {
-    const float *coef = reinterpret_cast<const float *>(qpk + size_t(kQpackVecs) * 32 * 2 * (D / 32) * 16);
+  if (tid < 8) {
+    const float *coef = reinterpret_cast<const float *>(qpk + size_t(kQpackVecs) * 32 * 2 * NK * 16);
     qjc[0][tid] = coef[tid * kQpackCoef + 3];
     qjc[1][tid] = coef[tid * kQpackCoef + 4];
-    mstat[0][tid] = -INFINITY;
-    mstat[1][tid] = 0.0f;
-    mstat[2][tid] = 0.0f;
   }
-  for (int i = tid; i < 16 * TP; i += NT) (&pt[0][0])[i] = _Float16(0.0f);   // absent heads stay 0
-  // value MFMA role (waves below NCB): coordinate block wv, lane = (row or column, k group)
-  const int vn = lane & 15, vq = lane >> 4;
-  v4f acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto lbit = [](int lv, int j) { return 2 * D + 2 * (D / 2 - (D >> (lv - 1)) + j); };
-  for (int c0 = t_begin; c0 < t_end; c0 += CH) {
-    const int cn = min(CH, t_end - c0);
-    __syncthreads();   // the previous chunk's readers are done
+  for (int i = tid; i < 8 * D; i += 512) (&ys[0][0])[i] = 0.0f;
+  {
+    // wave h: the scale of head h's query
+    const int h = wv;
+    float mx = 0.0f;
+    if (h < G)
+      for (int j = lane; j < D; j += 64) mx = fmaxf(mx, fabsf(qrow[size_t(h) * a.qstride + j]));
+    mx = wave_max_dpp(mx);
+    if (lane == 0) {
+      int ex = 0;
+      if (mx > 0.0f) frexpf(mx, &ex);   // mx < 2^ex
+      const float s = mx > 0.0f ? ldexpf(1.0f, 8 - ex) : 1.0f;
+      qsc[h] = h < G ? s : 0.0f;
+      qiv[h] = h < G ? 1.0f / (s * kYScale) : 0.0f;
+    }
+  }
+  __syncthreads();
+  // key A operand of MFMA k: lane (row m, group q) holds coordinates q NQ + 8 k .. + 7 of
+  // row m; rows 4 i .. 4 i + 3 are head 2 i hi, lo and head 2 i + 1 hi, lo, so that the
+  // lanes of result row group i hold both parts of two heads
+  for (int i = tid; i < NK * 64; i += 512) {
+    const int k = i / 64, l = i % 64, mrow = l & 15, qg = l >> 4;
+    const int h = 2 * (mrow >> 2) + ((mrow >> 1) & 1), part = mrow & 1;
+    v8h v;
 #pragma unroll
-    for (int i = 0; i < NKD; ++i) {
-      const int k = tid + NT * i;
-      if (k < CH * KW) krs[(k / KW) * KWP + k % KW] = kreg[i];
+    for (int j = 0; j < 8; ++j) {
+      const float q = h < G ? qrow[size_t(h) * a.qstride + qg * NQ + 8 * k + j] * qsc[h] : 0.0f;
+      const _Float16 hi = _Float16(q);
+      v[j] = part ? _Float16(q - float(hi)) : hi;
+    }
+    qa[k][l] = v;
+  }
+  {
+    const v4i *src = reinterpret_cast<const v4i *>(qpk);
+    for (int i = tid; i < NK * 64; i += 512) {
+      const int c = i / 64, l = i % 64;
+      qsa[c][l] = src[((kSqVec * 32 + (l & 31)) * 2 + (l >> 5)) * NK + c];
+    }
+  }
+  __syncthreads();
+
+  const int nsteps = t_end > t_begin ? (t_end - t_begin + ST - 1) / ST : 0;
+  float mref[4], lsum[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mref[r] = -INFINITY;
+    lsum[r] = 0.0f;
+  }
+  v4f acc[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) acc[j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  uint4 pk[KQL];
+  uint2 pv[VQL];
+  uint32_t pn = 0u;
+  auto fetch = [&](int s) {
+    const int t0 = t_begin + s * ST, cn = min(ST, t_end - t0);
+    const int t32 = lane & 31, hf = lane >> 5;
+    const size_t tb = ubase + size_t(t0);   // uniform bases, lane offsets below 2^31
+    const uint4 *ks = reinterpret_cast<const uint4 *>(a.krec + tb * (KW * 4));
+    const uint2 *vs = reinterpret_cast<const uint2 *>(a.vrec + tb * (VW * 4));
+    const uint32_t *kn = a.knorm + tb;
+    const uint16_t *vn = a.vnorm + tb;
+#pragma unroll
+    for (int r = 0; r < KQL; ++r) {
+      const int i = lane + 64 * r;
+      pk[r] = i < KQ && i / (KW / 4) < cn ? ks[i] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int i = 0; i < NVD; ++i) {
-      const int k = tid + NT * i;
-      if (k < CH * VW) vrs[(k / VW) * VWP + k % VW] = vreg[i];
+    for (int r = 0; r < VQL; ++r) {
+      const int i = lane + 64 * r;
+      pv[r] = i < VQ && i / (VW / 2) < cn ? vs[i] : make_uint2(0u, 0u);
     }
-    if (tid < CH) {
-      kns[tid] = tid < cn ? knr : 0u;
-      vns[tid] = tid < cn ? vnr : 0.0f;
+    if (hf == 0)
+      pn = t32 < cn ? kn[t32] : 0u;
+    else
+      pn = t32 < cn ? uint32_t(vn[t32]) : 0u;
+  };
+  if (wv < nsteps) fetch(wv);
+  for (int s = wv; s < nsteps; s += NW) {
+    const int t0 = t_begin + s * ST, cn = min(ST, t_end - t0);
+    // the lane index is made opaque to the compiler in each step, so that the many lane
+    // dependent LDS addresses and shifts below are formed where they are used instead of
+    // being held in registers across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int n16 = ln & 15, grp = ln >> 4;   // MFMA column and lane group
+    const int t32 = ln & 31, hf = ln >> 5;    // QJL / softmax: token and half of the heads
+    // ---- stage this step's records (rows past the range are zero), then start the next
+    wave_lds_sync();
+#pragma unroll
+    for (int r = 0; r < KQL; ++r) {
+      const int i = lane + 64 * r;
+      if (i < KQ) {
+        uint32_t *d = &krs[wv][(i / (KW / 4)) * KWP + (i % (KW / 4)) * 4];
+        d[0] = pk[r].x;
+        d[1] = pk[r].y;
+        d[2] = pk[r].z;
+        d[3] = pk[r].w;
+      }
     }
-    if (c0 + CH < t_end) fetch(c0 + CH);
-    __syncthreads();
-    // ---- decode one quarter (rows past the chunk's end become zero).  The quarter is a
-    // compile-time constant in each branch, so every code's bit position is too: a code is
-    // a shift and a mask of a known record dword, and its (cos, sin) one LDS read.
-    auto decode_quarter = [&](auto qc) {
-      constexpr int QQ = decltype(qc)::value;
-      const uint32_t *w = kv ? &vrs[tt * VWP] : &krs[tt * KWP];
-      // the quarter's level-1 nibbles and every 2-bit code, read together
-      constexpr int N1 = D / 64;   // dwords of a quarter's level-1 nibbles
-      uint32_t n1[N1], hi[NHI];
 #pragma unroll
-      for (int i = 0; i < N1; ++i) n1[i] = w[QQ * N1 + i];
-#pragma unroll
-      for (int i = 0; i < NHI; ++i) hi[i] = w[HI0 + i];
-      auto code2 = [&](int bit) {   // a 2-bit code in the high dwords (bit >= 2 D)
-        return int((hi[(bit >> 5) - HI0] >> (bit & 31)) & 3u);
-      };
-      const float scale = kv ? vns[tt] : 1.0f;
-      const float2 cT = csh[L - 2][code2(lbit(L, 0))], cH = csh[L - 3][code2(lbit(L - 1, QQ >> 1))];
+    for (int r = 0; r < VQL; ++r) {
+      const int i = lane + 64 * r;
+      if (i < VQ) {
+        uint32_t *d = &vrs[wv][(i / (VW / 2)) * VWP + (i % (VW / 2)) * 2];
+        d[0] = pv[r].x;
+        d[1] = pv[r].y;
+      }
+    }
+    if (hf == 0)
+      kns[wv][t32] = pn;
+    else
+      vns[wv][t32] = f16_bits_to_float(pn);
+    if (s + NW < nsteps) fetch(s + NW);
+    wave_lds_sync();
+
+    // ---- keys, 16 tokens at a time: lane = (token n16, quarter grp)
+#pragma unroll 1
+    for (int sb = 0; sb < 2; ++sb) {
+      const uint32_t *w = &krs[wv][(16 * sb + n16) * KWP];
       float r[NQ / 2];
-      r[0] = scale * ((QQ >> 1) ? cT.y : cT.x) * ((QQ & 1) ? cH.y : cH.x);
+      polar_pair_radii<D, SK, 4>(w, grp, kYScale, csh, r);
+      v4f kacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int lv = L - 2, n = 1; lv >= 2; --lv, n <<= 1) {
+      for (int k = 0; k < NK; ++k) {
+        // coordinates 8 k .. 8 k + 7 of the quarter: level-1 pairs 4 k .. 4 k + 3
+        const uint32_t nib = w[(2 * NQ * grp + 16 * k) >> 5] >> ((16 * k) & 31);
+        v4u hb, lb;
 #pragma unroll
-        for (int i = n - 1; i >= 0; --i) {
-          const float2 cs = csh[lv - 2][code2(lbit(lv, QQ * n + i))];
-          const float rr = r[i];
-          r[2 * i] = rr * cs.x;
-          r[2 * i + 1] = rr * cs.y;
+        for (int p = 0; p < 4; ++p) {
+          const float2 cs = cs1[(nib >> (4 * p)) & 15u];
+          const float y0 = r[4 * k + p] * cs.x, y1 = r[4 * k + p] * cs.y;
+          const h2v hh = __builtin_amdgcn_cvt_pkrtz(y0, y1);
+          const h2v hl = __builtin_amdgcn_cvt_pkrtz(y0 - float(hh.x), y1 - float(hh.y));
+          hb[p] = __builtin_bit_cast(uint32_t, hh);
+          lb[p] = __builtin_bit_cast(uint32_t, hl);
         }
+        const v8h A = qa[k][lane];
+        kacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(v8h, hb), kacc, 0, 0, 0);
+        kacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, __builtin_bit_cast(v8h, lb), kacc, 0, 0, 0);
       }
-      const bool live = tt < cn;
-      if (kv) {
-#pragma unroll
-        for (int i = 0; i < NQ / 2; ++i) {
-          const float2 cs = cs1[(n1[i >> 3] >> (4 * (i & 7))) & 15u];
-          const float v0 = live ? r[i] * cs.x : 0.0f, v1 = live ? r[i] * cs.y : 0.0f;
-          const _Float16 h0 = _Float16(v0), h1 = _Float16(v1);
-          const int c = QQ * NQ + 2 * i;
-          vth[c][tt] = h0;
-          vtl[c][tt] = _Float16(v0 - float(h0));
-          vth[c + 1][tt] = h1;
-          vtl[c + 1][tt] = _Float16(v1 - float(h1));
-        }
-      } else {
-        // the key's quarter stays in registers: its share of every head's score
-        float y[NQ];
-#pragma unroll
-        for (int i = 0; i < NQ / 2; ++i) {
-          const float2 cs = cs1[(n1[i >> 3] >> (4 * (i & 7))) & 15u];
-          y[2 * i] = r[i] * cs.x;
-          y[2 * i + 1] = r[i] * cs.y;
-        }
-#pragma unroll
-        for (int h = 0; h < GM; ++h) {
-          if (h < G) {
-            float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-            for (int j = 0; j < NQ; j += 4) {
-              const float4 qa = *reinterpret_cast<const float4 *>(&qr[h][QQ * NQ + j]);
-              d0 = fmaf(qa.x, y[j], d0);
-              d1 = fmaf(qa.y, y[j + 1], d1);
-              d0 = fmaf(qa.z, y[j + 2], d0);
-              d1 = fmaf(qa.w, y[j + 3], d1);
-            }
-            psk[QQ][h][tt] = live ? d0 + d1 : 0.0f;
-          }
-        }
-      }
-    };
-    switch (qq) {
-      case 0: decode_quarter(IntTag<0>{}); break;
-      case 1: decode_quarter(IntTag<1>{}); break;
-      case 2: decode_quarter(IntTag<2>{}); break;
-      default: decode_quarter(IntTag<3>{}); break;
+      // lane (token n16, group grp): heads 2 grp and 2 grp + 1, hi + lo rows
+      *reinterpret_cast<float2 *>(&dts[wv][16 * sb + n16][2 * grp]) =
+          make_float2((kacc[0] + kacc[1]) * qiv[2 * grp], (kacc[2] + kacc[3]) * qiv[2 * grp + 1]);
     }
-    // ---- the QJL sums of 32-token tile qq, by value waves 0 and 1: the sign bits as int8
-    // bytes (bit e of each nibble in place, as in the packed-cache decode) against the S q
-    // digit rows, one v_mfma_i32_32x32x32_i8 per 32 signs; lane = (token, half of the rows)
-    if (kv && qq < CH / 32) {
-      const int row = lane & 31, hf = lane >> 5, t2 = 32 * qq + row;
-      const uint32_t *sgw = &krs[t2 * KWP + 3 * D / 32 + hf * (D / 64)];
+
+    // ---- QJL sums: the sign bits as int8 bytes (bit e of each nibble in place) against
+    // the S q digit rows; lane = (token t32, half hf of the digit rows)
+    float sc[4];
+    {
+      const uint32_t *sgw = &krs[wv][t32 * KWP + 3 * D / 32 + hf * (D / 64)];
       const uint2 sw = make_uint2(sgw[0], D >= 128 ? sgw[1] : 0u);
       v16i s2 = {};
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c) {
+      for (int c = 0; c < NK; ++c) {
         const uint32_t w = (c >> 1) ? sw.y : sw.x;
         const uint32_t nb = (c & 1) ? w >> 4 : w;
         v4i bp;
 #pragma unroll
         for (int e = 0; e < 4; ++e) bp[e] = int(nb & (0x01010101u << e));
-        s2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(As[c], bp, s2, 0, 0, 0);
+        s2 = __builtin_amdgcn_mfma_i32_32x32x32_i8(qsa[c][lane], bp, s2, 0, 0, 0);
       }
-      const float rn16 = f16_bits_to_float(kns[t2] >> 16);   // 0 past the chunk's end
+      const uint32_t kn = kns[wv][t32];
+      const float n16f = f16_bits_to_float(kn & 0xFFFFu), rn16 = f16_bits_to_float(kn >> 16);
+      const float4 dt = *reinterpret_cast<const float4 *>(&dts[wv][t32][4 * hf]);
+      const float dv[4] = {dt.x, dt.y, dt.z, dt.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int h = 4 * hf + r;
         // digit sums: rows 8 digit + head are accumulator registers 4 digit + r
         const float S2 = fmaf(float(s2[r] + 256 * s2[4 + r]), 0x1p-16f, float(s2[8 + r] + 256 * s2[12 + r]));
-        qj[h][t2] = rn16 * fmaf(qjc[0][h], S2, -qjc[1][h]);
+        sc[r] = fmaf(n16f, dv[r], rn16 * fmaf(qjc[0][h], S2, -qjc[1][h]));
       }
+    }
+    const bool live = t32 < cn;
+    if (a.scores && live) {
+      // one head half at a time, so that every row address is uniform
+      float *srow = a.scores + (size_t(b) * a.q_heads + hq0) * a.score_stride + t0;
+      const size_t ss = size_t(a.score_stride);
+      if (hf == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (r < G) srow[ss * r + t32] = sc[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 + r < G) srow[ss * (4 + r) + t32] = sc[r];
+      }
+    }
+    // ---- online softmax with a lazy reference: the weights are 2^(v - mref), and mref
+    // moves only when a logit passes it by more than 8, so the weights stay below 2^8
+    float v[4];
+    bool up = false;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v[r] = live ? sc[r] * a.scale_log2 : -INFINITY;
+      up = up || v[r] > mref[r] + 8.0f;
+    }
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      float al[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // the maximum over each half's 32 tokens ends in lanes 31 and 63
+        const int mx = dpp_max32_tail(f2ord(v[r]));
+        const float m0 = ord2f(__builtin_amdgcn_readlane(mx, 31)), m1 = ord2f(__builtin_amdgcn_readlane(mx, 63));
+        const float mn = fmaxf(mref[r], hf ? m1 : m0);
+        al[r] = mref[r] == -INFINITY ? 0.0f : exp2f(mref[r] - mn);
+        mref[r] = mn;
+        lsum[r] *= al[r];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al[i]), 0));
+        const float a1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al[i]), 32));
+        const float ai = (grp & 1) ? a1 : a0;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) acc[j][i] *= ai;
+      }
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = exp2f(v[r] - mref[r]);   // 0 past the range
+      lsum[r] += p[r];
+    }
+    *reinterpret_cast<float4 *>(&pts[wv][t32][4 * hf]) = make_float4(p[0], p[1], p[2], p[3]);
+    wave_lds_sync();
+
+    // ---- values, 4 tokens at a time: lane = (subtree n16, token grp of the group);
+    // acc[j] (rows = heads, columns = subtrees) sums coordinate CPL n16 + j
+#pragma unroll 1
+    for (int qd = 0; qd < ST / 4; ++qd) {
+      if (4 * qd < cn) {
+        const int tk = 4 * qd + grp;
+        const float pa = pts[wv][tk][n16 & 7];   // rows 8..15 repeat the heads
+        const uint32_t *w = &vrs[wv][tk * VWP];
+        float r[CPL / 2];
+        polar_pair_radii<D, SV, 16>(w, n16, vns[wv][tk], csh, r);
+        const uint32_t nib = rec_bits<0, 2 * CPL, 16>(w, n16);
+#pragma unroll
+        for (int i = 0; i < CPL / 2; ++i) {
+          const float2 cs = cs1[(nib >> (4 * i)) & 15u];
+          acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, r[i] * cs.x, acc[2 * i], 0, 0, 0);
+          acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, r[i] * cs.y, acc[2 * i + 1], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // ---- the block's combination of its 8 wave states: sums per head over each half's
+  // lanes, the block maximum, then the waves' scaled value sums added in wave order
+  const int n16 = lane & 15, grp = lane >> 4, t32 = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float ls = lsum[r];
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) ls += __shfl_xor(ls, o, 64);
+    if (t32 == 0) {
+      wst[0][wv][4 * hf + r] = mref[r];
+      wst[1][wv][4 * hf + r] = ls;
+    }
+  }
+  __syncthreads();
+  float fac[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * (grp & 1) + i;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, wst[0][w][h]);
+    const float mw = wst[0][wv][h];
+    fac[i] = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+  }
+  for (int w = 0; w < NW; ++w) {
+    if (wv == w && grp < 2) {
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ys[4 * grp + i][CPL * n16 + j] += acc[j][i] * fac[i];
     }
     __syncthreads();
-    // ---- scores: wave = head, lane = token
-    if (wv < G) {
-      const int h = wv, t = lane;
-      const float n16 = f16_bits_to_float(kns[t] & 0xFFFFu);
-      const float s0 = psk[0][h][t], s1 = psk[1][h][t], s2 = psk[2][h][t], s3 = psk[3][h][t];
-      const float sc = fmaf(n16, (s0 + s1) + (s2 + s3), qj[h][t]);
-      if (a.scores && t < cn) a.scores[(size_t(b) * a.q_heads + hq0 + h) * a.score_stride + c0 + t] = sc;
-      // online softmax of this head over the chunk
-      const float v = t < cn ? sc * a.scale_log2 : -INFINITY;
-      const float mold = mstat[0][h], mnew = fmaxf(mold, wave_max_dpp(v));
-      const float al = mold == -INFINITY ? 0.0f : exp2f(mold - mnew);
-      const float p = t < cn ? exp2f(v - mnew) : 0.0f;
-      const float l = wave_sum_dpp(p);
-      const float ps_ = p * kPScale;
-      const _Float16 ph = _Float16(ps_);
-      pt[h][t] = ph;
-      pt[8 + h][t] = _Float16(ps_ - float(ph));
-      if (lane == 0) {
-        mstat[0][h] = mnew;
-        mstat[1][h] = mstat[1][h] * al + l;
-        mstat[2][h] = al;
-      }
-    }
-    __syncthreads();
-    // ---- values: acc[16 rows x 16 coordinates] += P[rows x tokens] V[tokens x coordinates]
-    // for coordinate block wv, with P and V each split into fp16 hi + lo (rows h and 8 + h
-    // carry P's parts, two MFMAs V's: every product above 2^-22 relative is kept)
-    if (wv < NCB) {
-      const float4 al4 = *reinterpret_cast<const float4 *>(&mstat[2][4 * (vq & 1)]);
-      acc[0] *= al4.x;
-      acc[1] *= al4.y;
-      acc[2] *= al4.z;
-      acc[3] *= al4.w;
-#pragma unroll
-      for (int tb = 0; tb < CH / 32; ++tb) {
-        const v8h A = *reinterpret_cast<const v8h *>(&pt[vn][32 * tb + 8 * vq]);
-        const v8h Bh = *reinterpret_cast<const v8h *>(&vth[16 * wv + vn][32 * tb + 8 * vq]);
-        const v8h Bl = *reinterpret_cast<const v8h *>(&vtl[16 * wv + vn][32 * tb + 8 * vq]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
-      }
-    }
   }
-  // partial (rotated basis): the hi and lo rows of each head summed, max (natural log), sum
-  __syncthreads();
-  float *ys = &psk[0][0][0];   // [GM][D]: the key score parts are no longer needed
-  if (wv < NCB && vq < 2) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ys[(4 * vq + j) * D + 16 * wv + vn] = acc[j];
-  }
-  __syncthreads();
-  if (wv < NCB && vq >= 2) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) ys[(4 * (vq - 2) + j) * D + 16 * wv + vn] += acc[j];
-  }
-  __syncthreads();
-  for (int i = tid; i < G * D; i += NT) {
+  for (int i = tid; i < G * D; i += 512) {
     const int h = i / D, j = i % D;
     float *o = a.part + ((size_t(b) * a.q_heads + hq0 + h) * a.splits + split) * (D + 2);
-    o[j] = ys[h * D + j] * (1.0f / kPScale);
+    o[j] = ys[h][j];
     if (j == 0) {
-      o[D] = mstat[0][h] == -INFINITY ? -INFINITY : mstat[0][h] * 0.69314718055994531f;
-      o[D + 1] = mstat[1][h];
+      float M = -INFINITY;
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, wst[0][w][h]);
+      float l = 0.0f;
+      for (int w = 0; w < NW; ++w)
+        if (wst[0][w][h] != -INFINITY) l += wst[1][w][h] * exp2f(wst[0][w][h] - M);
+      o[D] = M == -INFINITY ? -INFINITY : M * 0.69314718055994531f;   // natural-log units
+      o[D + 1] = l;
     }
   }
 }
