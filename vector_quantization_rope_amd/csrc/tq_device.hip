@@ -2726,10 +2726,10 @@ __device__ __forceinline__ float wave_sum_dpp(float x) {
 //         B operand; the A rows are the heads' rotated queries as fp16 hi + lo, so the
 //         four cross products of hi and lo parts all land in fp32.
 //   QJL:  the sign bits against the S q digit rows on v_mfma_i32_32x32x32_i8.
-//   values: lane = (subtree of d / 16 coordinates, token of a group of 4): the decoded
-//         coordinates, times the value norm, are the B operand of v_mfma_f32_16x16x4_f32
-//         with the softmax weights as A, so the value sums never leave fp32 and need no
-//         transposition through LDS.
+//   values: lane = (subtree of d / 16 coordinates, 4 consecutive tokens): the decoded
+//         coordinates, times the value norm, split into fp16 hi + lo, are already the B
+//         operand of v_mfma_f32_16x16x16_f16 (k = token) without any transposition; the
+//         A rows are the softmax weights as fp16 hi + lo.
 // The sums stay in the rotated basis: the partials are the merge's usual input.
 
 // a compile-time int carried by a value (selects a templated lambda body)
@@ -2764,12 +2764,10 @@ __device__ __forceinline__ uint32_t rec_bits(const uint32_t *w, int j) {
   }
 }
 
-// Radii of the level-1 pairs of subtree J (root at level S, 0 <= J < JN) of a record:
-// r0 times cos or sin of each ancestor's angle (the branch J takes), then each subtree
-// level splits every radius into its cos and sin parts.  r gets 2^(S-1) radii.
+// Radius of subtree J (root at level S, 0 <= J < JN) of a record, times r0: cos or sin
+// of each ancestor's angle, by the branch J takes.
 template <int D, int S, int JN>
-__device__ __forceinline__ void polar_pair_radii(const uint32_t *w, int J, float r0, const float2 (*csh)[4],
-                                                 float *r) {
+__device__ __forceinline__ float polar_path_radius(const uint32_t *w, int J, float r0, const float2 (*csh)[4]) {
   constexpr int L = D == 128 ? 7 : 6;
   static_for_down<L, S + 1>([&](auto t) {
     constexpr int lv = decltype(t)::value, up = lv - S;
@@ -2778,6 +2776,14 @@ __device__ __forceinline__ void polar_pair_radii(const uint32_t *w, int J, float
     const float2 cs = csh[lv - 2][code];
     r0 *= ((J >> (up - 1)) & 1) ? cs.y : cs.x;
   });
+  return r0;
+}
+
+// Radii of the level-1 pairs of subtree J (root at level S, radius r0): each subtree
+// level splits every radius into its cos and sin parts.  r gets 2^(S-1) radii.
+template <int D, int S, int JN>
+__device__ __forceinline__ void polar_sub_radii(const uint32_t *w, int J, float r0, const float2 (*csh)[4],
+                                                float *r) {
   r[0] = r0;
   static_for_down<S, 2>([&](auto t) {
     constexpr int lv = decltype(t)::value, n = 1 << (S - lv);
@@ -2790,6 +2796,12 @@ __device__ __forceinline__ void polar_pair_radii(const uint32_t *w, int J, float
       r[2 * i + 1] = rr * cs.y;
     }
   });
+}
+
+template <int D, int S, int JN>
+__device__ __forceinline__ void polar_pair_radii(const uint32_t *w, int J, float r0, const float2 (*csh)[4],
+                                                 float *r) {
+  polar_sub_radii<D, S, JN>(w, J, polar_path_radius<D, S, JN>(w, J, r0, csh), csh, r);
 }
 
 // Orders a wave's LDS writes before its later reads of other lanes' data (and the reads
@@ -2815,6 +2827,7 @@ struct PolarArgs {
 };
 
 typedef __fp16 h2v __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 template <int D>
@@ -2843,7 +2856,7 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
   __shared__ uint32_t kns[NW][ST];
   __shared__ float vns[NW][ST];
   __shared__ __align__(16) float dts[NW][ST][8];   // <q_rot, yhat> by token and head
-  __shared__ __align__(16) float pts[NW][ST][8];   // softmax weights by token and head
+  __shared__ __align__(16) float pts[NW][8][ST];   // softmax weights by head and token
   __shared__ float wst[2][NW][8];               // per wave: reference maximum and sum per head
   __shared__ float ys[8][D];                    // the block's value sums
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -3088,25 +3101,75 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
       p[r] = exp2f(v[r] - mref[r]);   // 0 past the range
       lsum[r] += p[r];
     }
-    *reinterpret_cast<float4 *>(&pts[wv][t32][4 * hf]) = make_float4(p[0], p[1], p[2], p[3]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pts[wv][4 * hf + r][t32] = p[r];
     wave_lds_sync();
 
-    // ---- values, 4 tokens at a time: lane = (subtree n16, token grp of the group);
-    // acc[j] (rows = heads, columns = subtrees) sums coordinate CPL n16 + j
+    // ---- values, 16 tokens at a time: lane = (subtree n16, tokens 4 grp .. 4 grp + 3),
+    // which is the B layout of v_mfma_f32_16x16x16_f16 (k = token); the A rows are the
+    // weights as fp16 hi (rows 0..7) and lo (rows 8..15), B the coordinates as fp16 hi
+    // and lo in two products, so every cross product of the parts lands in fp32.
+    // acc[j] (rows = head parts, columns = subtrees) sums coordinate CPL n16 + j.
 #pragma unroll 1
-    for (int qd = 0; qd < ST / 4; ++qd) {
-      if (4 * qd < cn) {
-        const int tk = 4 * qd + grp;
-        const float pa = pts[wv][tk][n16 & 7];   // rows 8..15 repeat the heads
-        const uint32_t *w = &vrs[wv][tk * VWP];
-        float r[CPL / 2];
-        polar_pair_radii<D, SV, 16>(w, n16, vns[wv][tk], csh, r);
-        const uint32_t nib = rec_bits<0, 2 * CPL, 16>(w, n16);
+    for (int vb = 0; vb < ST / 16; ++vb) {
+      if (16 * vb < cn) {
+        const float4 p4 = *reinterpret_cast<const float4 *>(&pts[wv][n16 & 7][16 * vb + 4 * grp]);
+        h2v pa0 = __builtin_amdgcn_cvt_pkrtz(p4.x, p4.y), pa1 = __builtin_amdgcn_cvt_pkrtz(p4.z, p4.w);
+        if (n16 & 8) {
+          pa0 = __builtin_amdgcn_cvt_pkrtz(p4.x - float(pa0.x), p4.y - float(pa0.y));
+          pa1 = __builtin_amdgcn_cvt_pkrtz(p4.z - float(pa1.x), p4.w - float(pa1.y));
+        }
+        const v4h A = __builtin_bit_cast(v4h, make_uint2(__builtin_bit_cast(uint32_t, pa0),
+                                                         __builtin_bit_cast(uint32_t, pa1)));
+        // the subtree in two halves (the children of its root), so that only half of
+        // the B operands are live at a time; the second half's radius is kept per token
+        constexpr int HC = CPL / 2;   // coordinates per half
+        float rho1[4];
 #pragma unroll
-        for (int i = 0; i < CPL / 2; ++i) {
-          const float2 cs = cs1[(nib >> (4 * i)) & 15u];
-          acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, r[i] * cs.x, acc[2 * i], 0, 0, 0);
-          acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, r[i] * cs.y, acc[2 * i + 1], 0, 0, 0);
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t bh[HC][2], bl[HC][2];   // coordinate j of tokens (0, 1) and (2, 3)
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2) {
+            float vc[2][HC];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+              const int tk = 16 * vb + 4 * grp + 2 * i2 + i;
+              const uint32_t *w = &vrs[wv][tk * VWP];
+              float rh;
+              if (hh == 0) {
+                const float rho = polar_path_radius<D, SV, 16>(w, n16, vns[wv][tk], csh);
+                const float2 cs = csh[SV - 2][rec_bits<polar_level_bit(D, SV), 2, 16>(w, n16) & 3u];
+                rh = rho * cs.x;
+                rho1[2 * i2 + i] = rho * cs.y;
+              } else {
+                rh = rho1[2 * i2 + i];
+              }
+              float r[HC / 2];
+              polar_sub_radii<D, SV - 1, 32>(w, 2 * n16 + hh, rh, csh, r);
+              const uint32_t nib = rec_bits<0, CPL, 32>(w, 2 * n16 + hh);
+#pragma unroll
+              for (int e = 0; e < HC / 2; ++e) {
+                const float2 cs = cs1[(nib >> (4 * e)) & 15u];
+                vc[i][2 * e] = r[e] * cs.x;
+                vc[i][2 * e + 1] = r[e] * cs.y;
+              }
+            }
+#pragma unroll
+            for (int j = 0; j < HC; ++j) {
+              const h2v hv = __builtin_amdgcn_cvt_pkrtz(vc[0][j], vc[1][j]);
+              const h2v lv = __builtin_amdgcn_cvt_pkrtz(vc[0][j] - float(hv.x), vc[1][j] - float(hv.y));
+              bh[j][i2] = __builtin_bit_cast(uint32_t, hv);
+              bl[j][i2] = __builtin_bit_cast(uint32_t, lv);
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < HC; ++j) {
+            v4f &c = acc[HC * hh + j];
+            c = __builtin_amdgcn_mfma_f32_16x16x16f16(A, __builtin_bit_cast(v4h, make_uint2(bh[j][0], bh[j][1])), c,
+                                                      0, 0, 0);
+            c = __builtin_amdgcn_mfma_f32_16x16x16f16(A, __builtin_bit_cast(v4h, make_uint2(bl[j][0], bl[j][1])), c,
+                                                      0, 0, 0);
+          }
         }
       }
     }
@@ -3136,6 +3199,11 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
     const float mw = wst[0][wv][h];
     fac[i] = mw == -INFINITY ? 0.0f : exp2f(mw - M);
   }
+  // the lo rows (lane groups 2, 3) onto the hi rows of the same heads
+#pragma unroll
+  for (int j = 0; j < CPL; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[j][i] += __shfl_xor(acc[j][i], 32, 64);
   for (int w = 0; w < NW; ++w) {
     if (wv == w && grp < 2) {
 #pragma unroll
