@@ -2769,13 +2769,19 @@ __device__ __forceinline__ uint32_t rec_bits(const uint32_t *w, int j) {
 template <int D, int S, int JN>
 __device__ __forceinline__ float polar_path_radius(const uint32_t *w, int J, float r0, const float2 (*csh)[4]) {
   constexpr int L = D == 128 ? 7 : 6;
+  // cos or sin of each ancestor's code, read as one float (the branch picks the
+  // component), every level's read in flight before the first product
+  const float *csf = reinterpret_cast<const float *>(&csh[0][0]);
+  float c[L - S];
   static_for_down<L, S + 1>([&](auto t) {
     constexpr int lv = decltype(t)::value, up = lv - S;
     constexpr int nodes = (JN + (1 << up) - 1) >> up;
     const uint32_t code = rec_bits<polar_level_bit(D, lv), 2, nodes>(w, J >> up) & 3u;
-    const float2 cs = csh[lv - 2][code];
-    r0 *= ((J >> (up - 1)) & 1) ? cs.y : cs.x;
+    c[lv - S - 1] = csf[(lv - 2) * 8 + 2 * code + ((J >> (up - 1)) & 1)];
   });
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = L - S - 1; i >= 0; --i) r0 *= c[i];
   return r0;
 }
 
@@ -2788,12 +2794,16 @@ __device__ __forceinline__ void polar_sub_radii(const uint32_t *w, int J, float 
   static_for_down<S, 2>([&](auto t) {
     constexpr int lv = decltype(t)::value, n = 1 << (S - lv);
     const uint32_t f = rec_bits<polar_level_bit(D, lv), 2 * n, JN>(w, J);
+    // the level's lookups are all issued before the first product waits on one
+    float2 cs[n];
+#pragma unroll
+    for (int i = 0; i < n; ++i) cs[i] = csh[lv - 2][(f >> (2 * i)) & 3u];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = n - 1; i >= 0; --i) {
-      const float2 cs = csh[lv - 2][(f >> (2 * i)) & 3u];
       const float rr = r[i];
-      r[2 * i] = rr * cs.x;
-      r[2 * i + 1] = rr * cs.y;
+      r[2 * i] = rr * cs[i].x;
+      r[2 * i + 1] = rr * cs[i].y;
     }
   });
 }
@@ -2830,10 +2840,14 @@ typedef __fp16 h2v __attribute__((ext_vector_type(2)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
+// PolarQuant decode blocks: 4 waves, 3 blocks per CU (3 waves per SIMD, up to 168
+// registers each: room for the table lookups of a decode level to be in flight together)
+constexpr int kPolarWaves = 4, kPolarBlocksPerCU = 3;
+
 template <int D>
-__global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
+__global__ __launch_bounds__(64 * kPolarWaves, kPolarBlocksPerCU * kPolarWaves / 4) void k_decode_polar(PolarArgs a) {
   // m = D QJL rows, at most 8 heads
-  constexpr int L = D == 128 ? 7 : 6, NW = 8, ST = 32;
+  constexpr int L = D == 128 ? 7 : 6, NW = kPolarWaves, NT = 64 * NW, ST = 32;
   constexpr int KW = D / 8, VW = 3 * D / 32;    // record dwords: key (angles, signs), value
   constexpr int KWP = KW + 1, VWP = VW + 1;     // odd LDS strides: one token per bank
   constexpr int NQ = D / 4, NK = D / 32;        // key quarter; f16 MFMAs per hi or lo part
@@ -2876,10 +2890,9 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
     qjc[0][tid] = coef[tid * kQpackCoef + 3];
     qjc[1][tid] = coef[tid * kQpackCoef + 4];
   }
-  for (int i = tid; i < 8 * D; i += 512) (&ys[0][0])[i] = 0.0f;
-  {
-    // wave h: the scale of head h's query
-    const int h = wv;
+  for (int i = tid; i < 8 * D; i += NT) (&ys[0][0])[i] = 0.0f;
+  for (int h = wv; h < 8; h += NW) {
+    // the scale of head h's query
     float mx = 0.0f;
     if (h < G)
       for (int j = lane; j < D; j += 64) mx = fmaxf(mx, fabsf(qrow[size_t(h) * a.qstride + j]));
@@ -2896,7 +2909,7 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
   // key A operand of MFMA k: lane (row m, group q) holds coordinates q NQ + 8 k .. + 7 of
   // row m; rows 4 i .. 4 i + 3 are head 2 i hi, lo and head 2 i + 1 hi, lo, so that the
   // lanes of result row group i hold both parts of two heads
-  for (int i = tid; i < NK * 64; i += 512) {
+  for (int i = tid; i < NK * 64; i += NT) {
     const int k = i / 64, l = i % 64, mrow = l & 15, qg = l >> 4;
     const int h = 2 * (mrow >> 2) + ((mrow >> 1) & 1), part = mrow & 1;
     v8h v;
@@ -2910,7 +2923,7 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
   }
   {
     const v4i *src = reinterpret_cast<const v4i *>(qpk);
-    for (int i = tid; i < NK * 64; i += 512) {
+    for (int i = tid; i < NK * 64; i += NT) {
       const int c = i / 64, l = i % 64;
       qsa[c][l] = src[((kSqVec * 32 + (l & 31)) * 2 + (l >> 5)) * NK + c];
     }
@@ -3003,10 +3016,14 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
       for (int k = 0; k < NK; ++k) {
         // coordinates 8 k .. 8 k + 7 of the quarter: level-1 pairs 4 k .. 4 k + 3
         const uint32_t nib = w[(2 * NQ * grp + 16 * k) >> 5] >> ((16 * k) & 31);
+        float2 cs4[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) cs4[p] = cs1[(nib >> (4 * p)) & 15u];
+        __builtin_amdgcn_sched_barrier(0);
         v4u hb, lb;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float2 cs = cs1[(nib >> (4 * p)) & 15u];
+          const float2 cs = cs4[p];
           const float y0 = r[4 * k + p] * cs.x, y1 = r[4 * k + p] * cs.y;
           const h2v hh = __builtin_amdgcn_cvt_pkrtz(y0, y1);
           const h2v hl = __builtin_amdgcn_cvt_pkrtz(y0 - float(hh.x), y1 - float(hh.y));
@@ -3147,11 +3164,14 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
               float r[HC / 2];
               polar_sub_radii<D, SV - 1, 32>(w, 2 * n16 + hh, rh, csh, r);
               const uint32_t nib = rec_bits<0, CPL, 32>(w, 2 * n16 + hh);
+              float2 cs2[HC / 2];
+#pragma unroll
+              for (int e = 0; e < HC / 2; ++e) cs2[e] = cs1[(nib >> (4 * e)) & 15u];
+              __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
               for (int e = 0; e < HC / 2; ++e) {
-                const float2 cs = cs1[(nib >> (4 * e)) & 15u];
-                vc[i][2 * e] = r[e] * cs.x;
-                vc[i][2 * e + 1] = r[e] * cs.y;
+                vc[i][2 * e] = r[e] * cs2[e].x;
+                vc[i][2 * e + 1] = r[e] * cs2[e].y;
               }
             }
 #pragma unroll
@@ -3213,7 +3233,7 @@ __global__ __launch_bounds__(512, 4) void k_decode_polar(PolarArgs a) {
     }
     __syncthreads();
   }
-  for (int i = tid; i < G * D; i += 512) {
+  for (int i = tid; i < G * D; i += NT) {
     const int h = i / D, j = i % D;
     float *o = a.part + ((size_t(b) * a.q_heads + hq0 + h) * a.splits + split) * (D + 2);
     o[j] = ys[h][j];
@@ -4026,8 +4046,8 @@ int default_splits(const tq_cache_desc &c, int length) {
   const int by_len = (length + kMfmaChunk - 1) / kMfmaChunk;
   // one round of blocks: the split kernel keeps kDecBlocksPerCU blocks resident per CU
   // and MI355X has 256 CUs, so all blocks start together and none waits for a second round
-  // (PolarQuant's decode kernel fits two blocks per CU: twice the blocks)
-  const int want = ((c.polar ? 2 : 1) * kDecodeBlocks + units - 1) / units;
+  // (PolarQuant's decode kernel keeps kPolarBlocksPerCU)
+  const int want = ((c.polar ? 256 * kPolarBlocksPerCU : kDecodeBlocks) + units - 1) / units;
   int s = by_len < want ? by_len : want;
   if (s < 1) s = 1;
   if (s > 4096) s = 4096;
@@ -4387,9 +4407,9 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
     const dim3 grid(units, used_splits);
     if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
     if (d == 64)
-      hipLaunchKernelGGL(k_decode_polar<64>, grid, dim3(512), 0, s, pa);
+      hipLaunchKernelGGL(k_decode_polar<64>, grid, dim3(64 * kPolarWaves), 0, s, pa);
     else
-      hipLaunchKernelGGL(k_decode_polar<128>, grid, dim3(512), 0, s, pa);
+      hipLaunchKernelGGL(k_decode_polar<128>, grid, dim3(64 * kPolarWaves), 0, s, pa);
     if (ev_stop && hipEventRecord(hipEvent_t(ev_stop), s) != hipSuccess) return TQ_EDEVICE;
   } else {
     DecodeArgs a;
