@@ -2764,6 +2764,17 @@ __device__ __forceinline__ uint32_t rec_bits(const uint32_t *w, int j) {
   }
 }
 
+// 2-bit code j (0 <= j < JN) of the level whose codes start at bit C
+template <int C, int JN>
+__device__ __forceinline__ uint32_t rec_code(const uint32_t *w, int j) {
+  if constexpr ((C & 31) + 2 * JN <= 32) {
+    return __builtin_amdgcn_ubfe(w[C >> 5], (C & 31) + 2 * j, 2);
+  } else {
+    const int p = C + 2 * j;
+    return __builtin_amdgcn_ubfe(w[p >> 5], p & 31, 2);
+  }
+}
+
 // Radius of subtree J (root at level S, 0 <= J < JN) of a record, times r0: cos or sin
 // of each ancestor's angle, by the branch J takes.
 template <int D, int S, int JN>
@@ -2771,13 +2782,13 @@ __device__ __forceinline__ float polar_path_radius(const uint32_t *w, int J, flo
   constexpr int L = D == 128 ? 7 : 6;
   // cos or sin of each ancestor's code, read as one float (the branch picks the
   // component), every level's read in flight before the first product
-  const float *csf = reinterpret_cast<const float *>(&csh[0][0]);
   float c[L - S];
   static_for_down<L, S + 1>([&](auto t) {
     constexpr int lv = decltype(t)::value, up = lv - S;
     constexpr int nodes = (JN + (1 << up) - 1) >> up;
-    const uint32_t code = rec_bits<polar_level_bit(D, lv), 2, nodes>(w, J >> up) & 3u;
-    c[lv - S - 1] = csf[(lv - 2) * 8 + 2 * code + ((J >> (up - 1)) & 1)];
+    const uint32_t code = rec_code<polar_level_bit(D, lv), nodes>(w, J >> up);
+    const uint32_t off = (code << 3) + uint32_t(((J >> (up - 1)) & 1) << 2);   // bytes into the level's table
+    c[lv - S - 1] = *reinterpret_cast<const float *>(reinterpret_cast<const char *>(&csh[lv - 2][0]) + off);
   });
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
