@@ -414,13 +414,14 @@ def nsn_bench(tq, w, K, V, q, dev, ev, stream, reps: int = 30):
 def polar_bench(tq, w, K, V, q, dev, ev, stream, reps: int = 20):
     """PolarQuant caches (recursive polar angles as stage 1, QJL on the key residual) on the
     long-context shape, outside the timed steps: the 4096-token append, decode and logits
-    only, medians of back-to-back calls.  The decode kernel decodes every token's angle
-    tree and runs fp32 dot products: it is bound by vector ALU work, not by its bytes."""
+    only, medians of back-to-back calls.  The decode kernel decodes every key and value
+    coordinate from its angle tree and splits it into fp16 hi + lo for the MFMA dot
+    products and value sums: it is bound by vector instruction issue, not by its bytes."""
     import torch
 
     T, A = w.context, w.append
     pre = T - A
-    units, G, d = w.batch * w.kv_heads, w.q_heads // w.kv_heads, w.d
+    units, d = w.batch * w.kv_heads, w.d
     E = [[ev.create() for _ in range(4)] for _ in range(reps)]
     codec = tq.Codec(d, 3, 3, d, seed=0, device=dev)
     cache = tq.PackedCache(w.batch, w.kv_heads, d, T, 3, 3, d, device=dev, polar=1)
@@ -438,8 +439,6 @@ def polar_bench(tq, w, K, V, q, dev, ev, stream, reps: int = 20):
                                                          w.rope_base, None, scores=sc, ws=ws, events=e), ev, stream, E)
     rec = 3 * d // 8 + d // 8 + 4 + 3 * d // 8 + 2          # angles + signs + norms, keys and values
     dbytes = units * T * rec
-    # vector work per token and head pair: decode ~3 d, scores and values 2 d G each, QJL d G / 4
-    flops = units * T * (3 * d + 4 * d * G + d * G // 4)
     return {"workload": ("long_context shape, PolarQuant keys (3 - 2/d bits of angles + QJL m = d) and values; "
                          "append of 4096 tokens, decode and logits at 131072; medians over %d calls" % reps),
             "record_bytes_per_token": rec,
@@ -448,8 +447,8 @@ def polar_bench(tq, w, K, V, q, dev, ev, stream, reps: int = 20):
             "decode_call_us": round(dec_call, 2), "split_kernel_us": round(dec_kern, 2),
             "split_kernel_gbs": round(dbytes / (dec_kern * 1e-6) / 1e9, 1),
             "split_kernel_hbm_frac": round(dbytes / (dec_kern * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-            "split_kernel_alu_tflops": round(flops / (dec_kern * 1e-6) / 1e12, 2),
-            "split_kernel_alu_frac_fp32": round(flops / (dec_kern * 1e-6) / 1e12 / 157.3, 4),
+            "split_kernel_limiter": ("VALU issue: the angle-tree decode of every coordinate and its fp16 hi + lo "
+                                     "split; dots and value sums on MFMA (profiles/decode_polar_long_context.md)"),
             "logits_call_us": round(lg_call, 2)}
 
 
