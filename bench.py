@@ -344,7 +344,10 @@ def configs_bench(tq, W, dev, ev, stream):
 def timed_calls(fn, ev, stream, E):
     """Median call and kernel times (us) of fn over len(E) back-to-back calls, after 80 ms of
     the same calls (the work before idles the GPU and its clock ramps up again); fn(events)
-    records its kernel between the given pair of events, fn(None) records nothing."""
+    records its kernel between the given pair of events, fn(None) records nothing.  Events
+    recorded between a call's kernels hold the stream for a few microseconds each, so the
+    calls alternate: the odd ones are timed whole with no event inside, the even ones give
+    the kernel time."""
     import torch
 
     med = lambda v: sorted(v)[len(v) // 2]
@@ -354,12 +357,16 @@ def timed_calls(fn, ev, stream, E):
         n += 1
         if n % 16 == 0:
             torch.cuda.synchronize()
-    for e in E:
-        ev.record(e[0], stream)
-        fn((e[1], e[2]))
-        ev.record(e[3], stream)
+    for i, e in enumerate(E):
+        if i % 2:
+            ev.record(e[0], stream)
+            fn(None)
+            ev.record(e[3], stream)
+        else:
+            fn((e[1], e[2]))
     torch.cuda.synchronize()
-    return med([ev.elapsed_ms(e[0], e[3]) * 1e3 for e in E]), med([ev.elapsed_ms(e[1], e[2]) * 1e3 for e in E])
+    return (med([ev.elapsed_ms(e[0], e[3]) * 1e3 for i, e in enumerate(E) if i % 2]),
+            med([ev.elapsed_ms(e[1], e[2]) * 1e3 for i, e in enumerate(E) if not i % 2]))
 
 
 def nsn_bench(tq, w, K, V, q, dev, ev, stream, reps: int = 30):
@@ -612,6 +619,10 @@ def main():
         print("bench.py measures one GPU: the packed-KV path runs on a single device and this "
               "build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 2:
+        # odd steps time the decode call, even steps its split kernel
+        print("bench.py needs --steps 2 or more", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
@@ -650,10 +661,16 @@ def main():
             return
         tq.quantize_kv(cache.desc, codec.dev, cache.buf, Ka, Va, pre, w.rope_base,
                        events=(E["a0"][i], E["a1"][i]))
-        ev.record(E["d0"][i], stream)
-        tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos, w.rope_base, out, ws=ws,
-                         events=(E["k0"][i], E["k1"][i]))
-        ev.record(E["d1"][i], stream)
+        # events recorded between the decode call's kernels hold the stream for a few
+        # microseconds each: odd steps time the whole call with no event inside it, even
+        # steps time its split kernel
+        if i % 2:
+            ev.record(E["d0"][i], stream)
+            tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos, w.rope_base, out, ws=ws)
+            ev.record(E["d1"][i], stream)
+        else:
+            tq.decode_attend(cache.desc, codec.dev, cache.buf, T, q, w.q_pos, w.rope_base, out, ws=ws,
+                             events=(E["k0"][i], E["k1"][i]))
 
     t_spin = time.perf_counter()
     spin = 0
@@ -674,8 +691,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     append_ms = [ev.elapsed_ms(E["a0"][i], E["a1"][i]) for i in range(args.steps)]
-    kern_ms = [ev.elapsed_ms(E["k0"][i], E["k1"][i]) for i in range(args.steps)]
-    dec_ms = [ev.elapsed_ms(E["d0"][i], E["d1"][i]) for i in range(args.steps)]
+    kern_ms = [ev.elapsed_ms(E["k0"][i], E["k1"][i]) for i in range(0, args.steps, 2)]
+    dec_ms = [ev.elapsed_ms(E["d0"][i], E["d1"][i]) for i in range(1, args.steps, 2)]
     mean = lambda v: sum(v) / len(v)
     units = w.batch * w.kv_heads
     dec_bytes = units * T * (KEY_RECORD + VALUE_RECORD)
