@@ -162,6 +162,12 @@ struct RopeFreq {
   double theta[64], c[64], s[64];
 };
 
+// cos and sin of the query position's rotary angles q_pos * theta_j (fp64 on the host,
+// rounded to fp32), j < d / 2; identity (1, 0) when the call has no RoPE
+struct QueryRope {
+  float c[64], s[64];
+};
+
 struct QuantArgs {
   CodecPtrs cp;
   CachePtrs ch;
@@ -1650,7 +1656,7 @@ __global__ __launch_bounds__(256) void k_qprep_pack(const void *q, int dtype, in
 // thread's slice of S^T, the query pair and its signs) is issued before the fp64 RoPE
 // angle is computed, the FWHT runs in one wave's registers, and one barrier less.
 template <int D>
-__global__ __launch_bounds__(256) void k_qprep_fast(const void *q, int dtype, int q_pos, float rope_base,
+__global__ __launch_bounds__(256) void k_qprep_fast(const void *q, int dtype, QueryRope qr,
                                                     CodecPtrs cp, float *qrows, int qstride,
                                                     int q_heads, int G, int bits_k, uint8_t *qpack,
                                                     const float *nsn) {
@@ -1671,16 +1677,9 @@ __global__ __launch_bounds__(256) void k_qprep_fast(const void *q, int dtype, in
     const int j = tid;
     const float x0 = load_elem(q, base + j, dtype), x1 = load_elem(q, base + j + H2, dtype);
     const float d0 = cp.D[j], d1 = cp.D[j + H2];
-    if (rope_base != 0.0f) {
-      const double theta = pow(double(rope_base), -2.0 * double(j) / double(D));
-      double sn, c;
-      sincos(double(q_pos) * theta, &sn, &c);
-      qs[j] = (x0 * float(c) - x1 * float(sn)) * d0;
-      qs[j + H2] = (x0 * float(sn) + x1 * float(c)) * d1;
-    } else {
-      qs[j] = x0 * d0;
-      qs[j + H2] = x1 * d1;
-    }
+    const float c = qr.c[j], sn = qr.s[j];
+    qs[j] = (x0 * c - x1 * sn) * d0;
+    qs[j + H2] = (x0 * sn + x1 * c) * d1;
   }
   __syncthreads();
   if (tid < 64) {
@@ -4326,12 +4325,23 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
   const CachePtrs ch = cache_ptrs(const_cast<void *>(cache_dev), *desc);
   if (length > 0) {
   if (d == m && (d == 64 || d == 128) && cp.block == d) {
+    QueryRope qr;
+    for (int j = 0; j < d / 2; ++j) {
+      if (rope_base != 0.0f) {
+        const double ang = double(q_pos) * std::pow(double(rope_base), -2.0 * double(j) / double(d));
+        qr.c[j] = float(std::cos(ang));
+        qr.s[j] = float(std::sin(ang));
+      } else {
+        qr.c[j] = 1.0f;
+        qr.s[j] = 0.0f;
+      }
+    }
     if (d == 64)
-      hipLaunchKernelGGL(k_qprep_fast<64>, dim3(rows), dim3(256), 0, s, q, int(dtype), q_pos, rope_base, cp, qp,
-                         qstride, q_heads, G, bk, with_qpack ? qpack : nullptr, ch.nsn);
+      hipLaunchKernelGGL(k_qprep_fast<64>, dim3(rows), dim3(256), 0, s, q, int(dtype), qr, cp, qp, qstride,
+                         q_heads, G, bk, with_qpack ? qpack : nullptr, ch.nsn);
     else
-      hipLaunchKernelGGL(k_qprep_fast<128>, dim3(rows), dim3(256), 0, s, q, int(dtype), q_pos, rope_base, cp, qp,
-                         qstride, q_heads, G, bk, with_qpack ? qpack : nullptr, ch.nsn);
+      hipLaunchKernelGGL(k_qprep_fast<128>, dim3(rows), dim3(256), 0, s, q, int(dtype), qr, cp, qp, qstride,
+                         q_heads, G, bk, with_qpack ? qpack : nullptr, ch.nsn);
   } else {
     hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s, q,
                        int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, bk,
