@@ -322,6 +322,9 @@ def test_nsn_means_input_dtypes(tq, P, d, dt, T):
     (128, 8, 700, [(0, 300), (300, 700)], "laplace"),   # two appends, a ragged tail
     (64, 4, 530, None, "student_t3"),
     (128, 2, 64, None, "normal"),
+    (128, 5, 33, None, "normal"),                       # odd head count, one step and a token
+    (64, 8, 97, [(0, 40), (40, 97)], "laplace"),        # d 64 with 8 heads, appends off the 32 grid
+    (128, 1, 1, None, "normal"),                        # a single token and head
 ])
 def test_polar_codes_and_decode(tq, P, d, G, T, chunks, dist):
     """PolarQuant caches ([TurboQuant] "PolarQuant" as stage 1, QJL on the key residual):

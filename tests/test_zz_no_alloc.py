@@ -24,25 +24,27 @@ def say(*a):
     sys.stdout.flush()
 
 
-def _case(tq, batch, kv_heads, G, T, bits_k, dtype, seed):
+def _case(tq, batch, kv_heads, G, T, bits_k, dtype, seed, polar=0):
     w = W.LONG_CONTEXT.scaled(batch=batch, kv_heads=kv_heads, q_heads=G * kv_heads, context=T, bits_k=bits_k,
-                              dtype=dtype)
+                              dtype=dtype, **({"bits_v": 3, "m": 128} if polar else {}))
     K, V = W.gen_kv(w, device="cuda")
     q = W.gen_q(w, device="cuda")
     codec = tq.Codec(w.d, bits_k, w.bits_v, w.m, seed=seed)
-    cache = tq.PackedCache(batch, kv_heads, w.d, T, bits_k, w.bits_v, w.m)
+    cache = tq.PackedCache(batch, kv_heads, w.d, T, bits_k, w.bits_v, w.m, polar=polar)
     tq.quantize_kv(cache.desc, codec.dev, cache.buf, K.contiguous(), V.contiguous(), 0, w.rope_base)
     return w, q, codec, cache
 
 
 @pytest.mark.gpu
 def test_noalloc_decode_equals_decode_attend(tq):
-    # (batch, kv_heads, G, context, key bits, dtype): the MFMA path at two shapes, the second
-    # smaller, then the fp32 path (16 q-heads per kv-head) smaller still
-    cases = [(2, 4, 8, 5000, 2, "bf16"), (1, 2, 4, 700, 2, "bf16"), (1, 1, 16, 300, 3, "f32")]
-    for i, (B, H, G, T, bk, dt) in enumerate(cases):
-        say(f"[noalloc] case {i}: batch {B} kv_heads {H} G {G} context {T} keys {bk}-bit {dt}")
-        w, q, codec, cache = _case(tq, B, H, G, T, bk, dt, seed=i)
+    # (batch, kv_heads, G, context, key bits, dtype, polar): the MFMA path at two shapes, the
+    # second smaller, then the fp32 path (16 q-heads per kv-head) smaller still, then a
+    # PolarQuant cache (its own decode kernel; logits on the same kernel)
+    cases = [(2, 4, 8, 5000, 2, "bf16", 0), (1, 2, 4, 700, 2, "bf16", 0), (1, 1, 16, 300, 3, "f32", 0),
+             (1, 2, 8, 260, 3, "bf16", 1)]
+    for i, (B, H, G, T, bk, dt, pol) in enumerate(cases):
+        say(f"[noalloc] case {i}: batch {B} kv_heads {H} G {G} context {T} keys {bk}-bit {dt} polar {pol}")
+        w, q, codec, cache = _case(tq, B, H, G, T, bk, dt, seed=i, polar=pol)
         Hq = G * H
         assert tq.decode_workspace_bytes(cache.desc, Hq, T) <= tq.NOALLOC_SCRATCH_BYTES
         out_ref = torch.empty((B, Hq, w.d), dtype=torch.float32, device="cuda")
