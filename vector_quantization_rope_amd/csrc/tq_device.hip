@@ -340,22 +340,37 @@ __device__ __forceinline__ void store_plane(uint32_t hA, uint32_t hB, int q, uin
 
 // ------------------------------------------------------------------ PolarQuant encode
 // Code of a level-1 angle psi = atan2(b, a) in [0, 2 pi) (signed zeros taken as +0): the
-// number of boundaries k pi / 8 (k = 1..15) at or below psi.
+// number of boundaries k pi / 8 (k = 1..15) at or below psi.  Without the angle itself:
+// exact half and quarter turns bring (a, b) into [0, pi / 2) (a > 0, b >= 0, or the zero
+// pair), and the three boundaries inside that quarter are the tests b >= a tan(t), with
+// tan(pi / 4) = 1 exact.  A test differs from the fp64 angle comparison only for angles
+// within a few ulps of a boundary.
 __device__ __forceinline__ int polar_code1(double a, double b) {
-  double psi = atan2(b + 0.0, a + 0.0);
-  if (psi < 0.0) psi += 2.0 * M_PI;
-  constexpr double w = 2.0 * M_PI / 16.0;
-  int c = min(int(psi / w), 15);
-  if (c < 15 && psi >= double(c + 1) * w) ++c;
-  if (c > 0 && psi < double(c) * w) --c;
+  a += 0.0;
+  b += 0.0;
+  int c = 0;
+  if (b < 0.0 || (b == 0.0 && a < 0.0)) {   // [pi, 2 pi): angle - pi
+    a = -a;
+    b = -b;
+    c = 8;
+  }
+  if (a <= 0.0 && b > 0.0) {   // [pi / 2, pi): angle - pi / 2
+    const double t = a;
+    a = b;
+    b = -t;
+    c += 4;
+  }
+  constexpr double kTan1 = 0.41421356237309503;   // tan(pi / 8) = sqrt(2) - 1
+  constexpr double kTan3 = 2.4142135623730949;    // tan(3 pi / 8) = sqrt(2) + 1
+  if (b > 0.0) c += int(b >= a * kTan1) + int(b >= a) + int(b >= a * kTan3);
   return c;
 }
 
-// Code of a higher-level angle psi = atan2(r1, r0) in [0, pi/2] against the level's three
-// fp64 boundaries.
-__device__ __forceinline__ int polar_codeh(double r0, double r1, const double *t) {
-  const double psi = atan2(r1, r0);
-  return int(psi >= t[0]) + int(psi >= t[1]) + int(psi >= t[2]);
+// Code of a higher-level angle psi = atan2(r1, r0) in [0, pi/2] (radii r0, r1 >= 0)
+// against the level's three boundaries, given as their tangents: psi >= t is r1 >= r0 tan t
+// for r1 > 0, and the angle of r1 = 0 is 0, below every boundary.
+__device__ __forceinline__ int polar_codeh(double r0, double r1, const double *tn) {
+  return r1 > 0.0 ? int(r1 >= r0 * tn[0]) + int(r1 >= r0 * tn[1]) + int(r1 >= r0 * tn[2]) : 0;
 }
 
 __device__ __forceinline__ double hyp(double a, double b) { return sqrt(fma(a, a, b * b)); }
@@ -364,7 +379,7 @@ __device__ __forceinline__ double hyp(double a, double b) { return sqrt(fma(a, a
 // by level, level 1 first (HC/2 codes), the chunk's top level last (one code at HC - 2);
 // returns the chunk's radius.
 template <int HC>
-__device__ __forceinline__ double polar_encode_chunk(const double *x, const double *pt, int *cc) {
+__device__ __forceinline__ double polar_encode_chunk(const double *x, const double *ptn, int *cc) {
   double r[HC / 2];
 #pragma unroll
   for (int i = 0; i < HC / 2; ++i) {
@@ -376,7 +391,7 @@ __device__ __forceinline__ double polar_encode_chunk(const double *x, const doub
     const int n = HC >> lv, base = HC - 2 * n;
 #pragma unroll
     for (int i = 0; i < n; ++i) {
-      cc[base + i] = polar_codeh(r[2 * i], r[2 * i + 1], pt + (lv - 1) * kPolarCodes);
+      cc[base + i] = polar_codeh(r[2 * i], r[2 * i + 1], ptn + 4 * lv);
       r[i] = hyp(r[2 * i], r[2 * i + 1]);
     }
   }
@@ -425,26 +440,25 @@ __device__ __forceinline__ void put_bits(uint32_t (&w)[NW], int bit, uint32_t va
 // lane ends with the whole record (3 D / 32 dwords); lane 0's *nh is the norm in H-units.
 // With recon, x becomes the reconstruction error x - yhat, yhat built from the fp16 norm.
 template <int D>
-__device__ __forceinline__ void polar_encode_group(double *x, int q, const CodecPtrs &cp, uint32_t (&w)[3 * D / 32],
-                                                   double *nh, bool recon, double sqrt_b, double inv_sqrt_b,
-                                                   uint16_t *n16b, bool *over) {
+__device__ __forceinline__ void polar_encode_group(double *x, int q, const CodecPtrs &cp, const double *ptn,
+                                                   uint32_t (&w)[3 * D / 32], double *nh, bool recon, double sqrt_b,
+                                                   double inv_sqrt_b, uint16_t *n16b, bool *over) {
   constexpr int HC = D / 8, L1 = (HC == 16 ? 4 : 3);   // in-chunk levels
   constexpr int LC1 = L1 + 1, LC2 = L1 + 2, LT = L1 + 3;
   static_assert(HC == 8 || HC == 16, "d = 64 or 128");
-  const double *pt = cp.pt;
   int ccA[HC - 1], ccB[HC - 1];
-  const double RA = polar_encode_chunk<HC>(x, pt, ccA), RB = polar_encode_chunk<HC>(x + HC, pt, ccB);
+  const double RA = polar_encode_chunk<HC>(x, ptn, ccA), RB = polar_encode_chunk<HC>(x + HC, ptn, ccB);
   // chunk pairs (q, q ^ 1): the even lane's chunk is the lower one
   const double RA1 = dpp_f64<kDppXor1>(RA), RB1 = dpp_f64<kDppXor1>(RB);
-  const int cA1 = polar_codeh(RA, RA1, pt + (LC1 - 1) * kPolarCodes);
-  const int cB1 = polar_codeh(RB, RB1, pt + (LC1 - 1) * kPolarCodes);
+  const int cA1 = polar_codeh(RA, RA1, ptn + 4 * LC1);
+  const int cB1 = polar_codeh(RB, RB1, ptn + 4 * LC1);
   const double RA2 = hyp(RA, RA1), RB2 = hyp(RB, RB1);
   // block pairs (lanes 0 and 2), then the halves (lane 0)
   const double RA2p = dpp_f64<kDppXor2>(RA2), RB2p = dpp_f64<kDppXor2>(RB2);
-  const int cA2 = polar_codeh(RA2, RA2p, pt + (LC2 - 1) * kPolarCodes);
-  const int cB2 = polar_codeh(RB2, RB2p, pt + (LC2 - 1) * kPolarCodes);
+  const int cA2 = polar_codeh(RA2, RA2p, ptn + 4 * LC2);
+  const int cB2 = polar_codeh(RB2, RB2p, ptn + 4 * LC2);
   const double RA3 = hyp(RA2, RA2p), RB3 = hyp(RB2, RB2p);
-  const int cT = polar_codeh(RA3, RB3, pt + (LT - 1) * kPolarCodes);
+  const int cT = polar_codeh(RA3, RB3, ptn + 4 * LT);
   *nh = hyp(RA3, RB3);
   bool ov = false;
   *n16b = f64_to_f16_sat(*nh * inv_sqrt_b, &ov);
@@ -558,6 +572,8 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   // which write the same columns, land on different banks
   __shared__ __align__(16) uint8_t vcode_s[64][D + 4];
   __shared__ float cb_s[4][kMaxCodes];
+  // PolarQuant: the tangents of each level's three angle boundaries, [4 level + k]
+  __shared__ double ptan_s[POLAR ? 32 : 1];
   double2 *rope_s = reinterpret_cast<double2 *>(u_s);   // [64][RH]
   _Float16 *r_s = reinterpret_cast<_Float16 *>(u_s);     // [2 parts][64][RS]
 
@@ -590,6 +606,13 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
     cb_s[1][tid] = a.cp.tk[tid];
     cb_s[2][tid] = a.cp.cv[tid];
     cb_s[3][tid] = a.cp.tv[tid];
+  }
+  if constexpr (POLAR) {
+    constexpr int L = D == 128 ? 7 : 6;
+    if (tid < 32) {
+      const int lv = tid >> 2, k = tid & 3;
+      ptan_s[tid] = lv >= 2 && lv <= L && k < 3 ? tan(a.cp.pt[(lv - 1) * kPolarCodes + k]) : 0.0;
+    }
   }
   const bool use_rope = a.rope_base != 0.0f;
   if (use_rope) {
@@ -647,7 +670,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
     uint32_t w[3 * D / 32];
     double nh;
     uint16_t n16b;
-    polar_encode_group<D>(x, q, a.cp, w, &nh, true, sqrt_b, inv_sqrt_b, &n16b, &over);
+    polar_encode_group<D>(x, q, a.cp, ptan_s, w, &nh, true, sqrt_b, inv_sqrt_b, &n16b, &over);
 #pragma unroll
     for (int i = 0; i < 3 * D / 32; ++i)
       if ((i & 3) == q && valid) rec[i] = w[i];
@@ -808,7 +831,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
       uint32_t w[3 * D / 32];
       double nh;
       uint16_t n16b;
-      polar_encode_group<D>(x, q, a.cp, w, &nh, false, sqrt_b, inv_sqrt_b, &n16b, &over);
+      polar_encode_group<D>(x, q, a.cp, ptan_s, w, &nh, false, sqrt_b, inv_sqrt_b, &n16b, &over);
       uint32_t *vrec = reinterpret_cast<uint32_t *>(reinterpret_cast<uint8_t *>(a.ch.vcodes) +
                                                     (size_t(unit) * a.capacity + (valid ? p : 0)) * (3 * D / 8));
 #pragma unroll
