@@ -366,36 +366,36 @@ __device__ __forceinline__ int polar_code1(double a, double b) {
   return c;
 }
 
-// Code of a higher-level angle psi = atan2(r1, r0) in [0, pi/2] (radii r0, r1 >= 0)
-// against the level's three boundaries, given as their tangents: psi >= t is r1 >= r0 tan t
-// for r1 > 0, and the angle of r1 = 0 is 0, below every boundary.
-__device__ __forceinline__ int polar_codeh(double r0, double r1, const double *tn) {
-  return r1 > 0.0 ? int(r1 >= r0 * tn[0]) + int(r1 >= r0 * tn[1]) + int(r1 >= r0 * tn[2]) : 0;
+// Code of a higher-level angle psi = atan2(r1, r0) in [0, pi/2] against the level's three
+// boundaries, from the squared radii s = r^2 and the boundaries' squared tangents: psi >= t
+// is s1 >= s0 tan(t)^2 for s1 > 0, and the angle of r1 = 0 is 0, below every boundary.  No
+// radius needs a square root until the norm.
+__device__ __forceinline__ int polar_codeh(double s0, double s1, const double *tn2) {
+  return s1 > 0.0 ? int(s1 >= s0 * tn2[0]) + int(s1 >= s0 * tn2[1]) + int(s1 >= s0 * tn2[2]) : 0;
 }
 
-__device__ __forceinline__ double hyp(double a, double b) { return sqrt(fma(a, a, b * b)); }
 
 // The in-chunk levels of HC consecutive coordinates (a power of two): codes stored level
 // by level, level 1 first (HC/2 codes), the chunk's top level last (one code at HC - 2);
 // returns the chunk's radius.
 template <int HC>
 __device__ __forceinline__ double polar_encode_chunk(const double *x, const double *ptn, int *cc) {
-  double r[HC / 2];
+  double s[HC / 2];   // squared radii
 #pragma unroll
   for (int i = 0; i < HC / 2; ++i) {
     cc[i] = polar_code1(x[2 * i], x[2 * i + 1]);
-    r[i] = hyp(x[2 * i], x[2 * i + 1]);
+    s[i] = fma(x[2 * i], x[2 * i], x[2 * i + 1] * x[2 * i + 1]);
   }
 #pragma unroll
   for (int lv = 2; (1 << lv) <= HC; ++lv) {
     const int n = HC >> lv, base = HC - 2 * n;
 #pragma unroll
     for (int i = 0; i < n; ++i) {
-      cc[base + i] = polar_codeh(r[2 * i], r[2 * i + 1], ptn + 4 * lv);
-      r[i] = hyp(r[2 * i], r[2 * i + 1]);
+      cc[base + i] = polar_codeh(s[2 * i], s[2 * i + 1], ptn + 4 * lv);
+      s[i] = s[2 * i] + s[2 * i + 1];
     }
   }
-  return r[0];
+  return s[0];
 }
 
 // Reconstruction of a chunk from its radius R and codes, top level down, each radius split
@@ -447,19 +447,20 @@ __device__ __forceinline__ void polar_encode_group(double *x, int q, const Codec
   constexpr int LC1 = L1 + 1, LC2 = L1 + 2, LT = L1 + 3;
   static_assert(HC == 8 || HC == 16, "d = 64 or 128");
   int ccA[HC - 1], ccB[HC - 1];
+  // squared radii of the chunks, then of the chunk pairs, blocks and halves
   const double RA = polar_encode_chunk<HC>(x, ptn, ccA), RB = polar_encode_chunk<HC>(x + HC, ptn, ccB);
   // chunk pairs (q, q ^ 1): the even lane's chunk is the lower one
   const double RA1 = dpp_f64<kDppXor1>(RA), RB1 = dpp_f64<kDppXor1>(RB);
   const int cA1 = polar_codeh(RA, RA1, ptn + 4 * LC1);
   const int cB1 = polar_codeh(RB, RB1, ptn + 4 * LC1);
-  const double RA2 = hyp(RA, RA1), RB2 = hyp(RB, RB1);
+  const double RA2 = RA + RA1, RB2 = RB + RB1;
   // block pairs (lanes 0 and 2), then the halves (lane 0)
   const double RA2p = dpp_f64<kDppXor2>(RA2), RB2p = dpp_f64<kDppXor2>(RB2);
   const int cA2 = polar_codeh(RA2, RA2p, ptn + 4 * LC2);
   const int cB2 = polar_codeh(RB2, RB2p, ptn + 4 * LC2);
-  const double RA3 = hyp(RA2, RA2p), RB3 = hyp(RB2, RB2p);
+  const double RA3 = RA2 + RA2p, RB3 = RB2 + RB2p;
   const int cT = polar_codeh(RA3, RB3, ptn + 4 * LT);
-  *nh = hyp(RA3, RB3);
+  *nh = sqrt(RA3 + RB3);
   bool ov = false;
   *n16b = f64_to_f16_sat(*nh * inv_sqrt_b, &ov);
   if (q == 0) *over |= ov;
@@ -572,7 +573,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   // which write the same columns, land on different banks
   __shared__ __align__(16) uint8_t vcode_s[64][D + 4];
   __shared__ float cb_s[4][kMaxCodes];
-  // PolarQuant: the tangents of each level's three angle boundaries, [4 level + k]
+  // PolarQuant: the squared tangents of each level's three angle boundaries, [4 level + k]
   __shared__ double ptan_s[POLAR ? 32 : 1];
   double2 *rope_s = reinterpret_cast<double2 *>(u_s);   // [64][RH]
   _Float16 *r_s = reinterpret_cast<_Float16 *>(u_s);     // [2 parts][64][RS]
@@ -611,7 +612,8 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
     constexpr int L = D == 128 ? 7 : 6;
     if (tid < 32) {
       const int lv = tid >> 2, k = tid & 3;
-      ptan_s[tid] = lv >= 2 && lv <= L && k < 3 ? tan(a.cp.pt[(lv - 1) * kPolarCodes + k]) : 0.0;
+      const double tn = lv >= 2 && lv <= L && k < 3 ? tan(a.cp.pt[(lv - 1) * kPolarCodes + k]) : 0.0;
+      ptan_s[tid] = tn * tn;
     }
   }
   const bool use_rope = a.rope_base != 0.0f;
