@@ -2716,8 +2716,8 @@ __global__ __launch_bounds__(256) void k_window(WindowArgs a) {
   }
 }
 
-// Max / sum over the 64 lanes, in every lane: DPP within rows of 16 (quad swaps, rotations
-// by 4 and 8), then the four row results read lane by lane.
+// Max over the 64 lanes, in every lane: DPP within rows of 16 (quad swaps, rotations by 4
+// and 8), then the four row results read lane by lane.
 __device__ __forceinline__ float row_dpp_f32(float x, bool mx) {
   const auto op = [mx](float u, float v) { return mx ? fmaxf(u, v) : u + v; };
   x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true)));
@@ -2732,10 +2732,6 @@ __device__ __forceinline__ float lane_f32(float x, int l) {
 __device__ __forceinline__ float wave_max_dpp(float x) {
   x = row_dpp_f32(x, true);
   return fmaxf(fmaxf(lane_f32(x, 0), lane_f32(x, 16)), fmaxf(lane_f32(x, 32), lane_f32(x, 48)));
-}
-__device__ __forceinline__ float wave_sum_dpp(float x) {
-  x = row_dpp_f32(x, false);
-  return (lane_f32(x, 0) + lane_f32(x, 16)) + (lane_f32(x, 32) + lane_f32(x, 48));
 }
 
 // ------------------------------------------------------------------ PolarQuant decode
