@@ -272,10 +272,18 @@ __device__ __forceinline__ void fwht_group4(double *x, int q) {
     x[HC + e] = a - b;
   }
   const double s1 = (q & 1) ? -1.0 : 1.0, s2 = (q & 2) ? -1.0 : 1.0;
+  // (eight coordinates at a time: two DPP results per double in flight for all of them
+  // would outgrow the registers of three waves per SIMD in the append)
 #pragma unroll
-  for (int e = 0; e < 2 * HC; ++e) x[e] = fma(s1, x[e], dpp_f64<kDppXor1>(x[e]));
+  for (int e = 0; e < 2 * HC; ++e) {
+    x[e] = fma(s1, x[e], dpp_f64<kDppXor1>(x[e]));
+    if ((e & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
-  for (int e = 0; e < 2 * HC; ++e) x[e] = fma(s2, x[e], dpp_f64<kDppXor2>(x[e]));
+  for (int e = 0; e < 2 * HC; ++e) {
+    x[e] = fma(s2, x[e], dpp_f64<kDppXor2>(x[e]));
+    if ((e & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // The 16-byte vectors of N consecutive input elements (off * sizeof(element) a multiple of
@@ -312,6 +320,27 @@ __device__ __forceinline__ void raw_to_f64(const RawRow<DT, N> &r, double *x) {
         x[8 * i + 2 * k + 1] = double(f16_bits_to_float(w[k] >> 16));
       }
     }
+  }
+}
+
+// Sign flip of a double by a mask word that holds the sign bit (bit 31) or nothing.
+__device__ __forceinline__ double xor_sign(double v, uint32_t m) {
+  return __builtin_bit_cast(double, __builtin_bit_cast(uint64_t, v) ^ (uint64_t(m) << 32));
+}
+
+// Sign flips of raw input elements before their conversion: m holds one mask word per
+// element for fp32 rows (bit 31) and one per element pair for 2-byte rows (bits 15 and
+// 31), 16-byte aligned, in the row's order.
+template <int DT, int N>
+__device__ __forceinline__ void xor_raw(RawRow<DT, N> &r, const uint32_t *m) {
+  const uint4 *mv = reinterpret_cast<const uint4 *>(m);
+#pragma unroll
+  for (int i = 0; i < RawRow<DT, N>::NV; ++i) {
+    const uint4 w = mv[i];
+    r.v[i].x ^= w.x;
+    r.v[i].y ^= w.y;
+    r.v[i].z ^= w.z;
+    r.v[i].w ^= w.w;
   }
 }
 
@@ -547,25 +576,30 @@ __device__ __forceinline__ void nsn_shift(double *x, int q, const float *po, dou
 }
 
 // One workgroup (4 waves) per 64-token window aligned to value tiles; 4 lanes per token.
-// Keys: RoPE (fp64 angles from an LDS table built by the fp64 rotation recurrence), the
-// seeded signs D, the unnormalised FWHT H_B, norm, codes and residual in fp64, with the
-// 1/sqrt(B) of Pi folded into the norms; the QJL projection z = S r runs on fp32 MFMA
-// (v_mfma_f32_32x32x2f32) over the window's 64 residuals.  Values: signs, FWHT, norm and
-// codes in fp64, then the window's codes are packed into value tiles.
+// Keys: RoPE (fp64 angles from two small LDS tables, the window's rows of 8 tokens and the
+// offsets inside a row), the seeded signs D, the unnormalised FWHT H_B, norm, codes and
+// residual in fp64, with the 1/sqrt(B) of Pi folded into the norms; the QJL projection
+// z = S r runs on fp16 MFMA (v_mfma_f32_32x32x16_f16, split operands) over the window's 64
+// residuals.  Values: signs, FWHT, norm and codes in fp64, then the window's codes are
+// packed into value tiles.  Three workgroups per CU (at most 168 VGPRs; the PolarQuant
+// encode needs more and runs two).
 // KK / KV: number of key / value codes when known at compile time (0: from the
 // descriptor, a slower loop).  Codes compare the unnormalised coordinate y_j with
 // ||y|| * t_k, which is u_j >= t_k up to one rounding.
 template <int D, int DT, int KK, int KV, bool POLAR = false>
-__global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
+__global__ __launch_bounds__(256, POLAR ? 2 : 3) void k_quantize_kv(QuantArgs a) {
   constexpr int H = D / 2;
   constexpr int HC = D / 8;     // coordinates per chunk
   constexpr int C = 2 * HC;     // coordinates per lane
   constexpr int W = D / 32;     // dwords per plane
   constexpr int RS = D + 8;     // padded residual row (fp16 elements)
-  // RoPE table rows padded by one entry: the 16 tokens of a wave read the same columns, and
-  // an unpadded row stride (a multiple of the bank width) sent them all to the same banks
-  constexpr int RH = H + 1;
-  constexpr int ROPE_BYTES = 64 * RH * 16;
+  // RoPE tables: rows of (cos, sin) of the window's angles (p0 + 8 a) theta_j and of the
+  // in-group offsets b theta_j (a, b < 8); token slot 8 a + b combines row a of the first
+  // with row b of the second.  Entry j = HC q + e sits at (HC + 1) q + e of its row (rows of
+  // 4 (HC + 1) entries): the 8 rows times 4 lane chunks a wave reads at once then fall on
+  // distinct 16-byte bank groups, two to a group.
+  constexpr int RW = 4 * (HC + 1);
+  constexpr int ROPE_BYTES = 2 * 8 * RW * 16;
   constexpr int R_BYTES = 2 * 64 * RS * 2;
   constexpr int U_BYTES = ROPE_BYTES > R_BYTES ? ROPE_BYTES : R_BYTES;
   __shared__ __align__(16) unsigned char u_s[U_BYTES];   // RoPE table, later residuals
@@ -575,7 +609,11 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   __shared__ float cb_s[4][kMaxCodes];
   // PolarQuant: the squared tangents of each level's three angle boundaries, [4 level + k]
   __shared__ double ptan_s[POLAR ? 32 : 1];
-  double2 *rope_s = reinterpret_cast<double2 *>(u_s);   // [64][RH]
+  // the seeded signs D as sign masks: one word per coordinate (bit 31 set where D_j = -1),
+  // then one word per coordinate pair (bits 15 and 31) for 2-byte value rows
+  __shared__ __align__(16) uint32_t dsg_s[D + D / 2];
+  double2 *ropeA_s = reinterpret_cast<double2 *>(u_s);   // [8][RW]
+  double2 *ropeB_s = ropeA_s + 8 * RW;                    // [8][RW]
   _Float16 *r_s = reinterpret_cast<_Float16 *>(u_s);     // [2 parts][64][RS]
 
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
@@ -589,17 +627,13 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   const size_t row = size_t(unit) * size_t(a.n_new) + size_t(valid ? p - a.start : 0);
   bool over = false;
 
-  // the token's key row, and for 2-byte inputs its value row, are requested before the
-  // RoPE table is built, so that their latency overlaps the table and the key work
-  constexpr bool kEarlyV = DT != TQ_F32;
+  // the token's key row is requested before the RoPE tables are built, so that its latency
+  // overlaps them (the value row is requested when the keys are done: holding it through
+  // the key work would cost the registers of the third wave per SIMD)
   RawRow<DT, HC> rk0, rk1, rv0, rv1;
   if (valid) {
     load_raw<DT, HC>(a.k, row * D + HC * q, rk0);
     load_raw<DT, HC>(a.k, row * D + H + HC * q, rk1);
-    if (kEarlyV && a.bits_v > 0) {
-      load_raw<DT, HC>(a.v, row * D + HC * q, rv0);
-      load_raw<DT, HC>(a.v, row * D + H + HC * q, rv1);
-    }
   }
 
   if (tid < kMaxCodes) {
@@ -617,26 +651,49 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
     }
   }
   const bool use_rope = a.rope_base != 0.0f;
-  if (use_rope) {
-    constexpr int nblk = 256 / H, per = 64 / nblk;
-    const int j = tid % H, i0 = (tid / H) * per;
-    // the angle of the thread's first row; the rows below it by the rotation recurrence
+  if (use_rope && tid < 2 * H) {
+    // threads j < H: row a of table A by the rotation recurrence from sincos(p0 theta_j) in
+    // steps of 8 theta_j (three doublings of theta_j); threads H + j: table B from (1, 0)
+    // in steps of theta_j.  Doublings, products and the recurrences involve no argument
+    // reduction; the angles match the fp64 ones to about 1e-14.
+    const int j = tid % H;
+    const int col = (j / HC) * (HC + 1) + j % HC;
     const double cd = a.rf.c[j], sd = a.rf.s[j];
-    double s, c;
-    sincos(double(p0 + i0) * a.rf.theta[j], &s, &c);
-    for (int i = 0; i < per; ++i) {
-      rope_s[(i0 + i) * RH + j] = make_double2(c, s);
-      const double cn = c * cd - s * sd;
-      s = s * cd + c * sd;
+    double c, s, cs, ss;
+    double2 *tab;
+    if (tid < H) {
+      sincos(double(p0) * a.rf.theta[j], &s, &c);
+      cs = cd;
+      ss = sd;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const double c2 = cs * cs - ss * ss;
+        ss = 2.0 * cs * ss;
+        cs = c2;
+      }
+      tab = ropeA_s;
+    } else {
+      c = 1.0;
+      s = 0.0;
+      cs = cd;
+      ss = sd;
+      tab = ropeB_s;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      tab[i * RW + col] = make_double2(c, s);
+      const double cn = c * cs - s * ss;
+      s = s * cs + c * ss;
       c = cn;
     }
   }
-  // seeded signs of this lane's coordinates: bit e set when D_j = -1
-  uint32_t dmask = 0u;
-#pragma unroll
-  for (int e = 0; e < HC; ++e) {
-    dmask |= uint32_t(a.cp.D[HC * q + e] < 0.0f) << e;
-    dmask |= uint32_t(a.cp.D[H + HC * q + e] < 0.0f) << (HC + e);
+  for (int i = tid; i < D + D / 2; i += 256) {
+    if (i < D) {
+      dsg_s[i] = a.cp.D[i] < 0.0f ? 0x80000000u : 0u;
+    } else {
+      const int k = 2 * (i - D);
+      dsg_s[i] = (a.cp.D[k] < 0.0f ? 0x8000u : 0u) | (a.cp.D[k + 1] < 0.0f ? 0x80000000u : 0u);
+    }
   }
   __syncthreads();
 
@@ -646,6 +703,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
 
   // ------------------------------------------------------------ keys
   double x[C];
+  float r32[C];   // the key residual rounded to fp32, for the QJL projection
   if (valid) {
     raw_to_f64<DT, HC>(rk0, x);
     raw_to_f64<DT, HC>(rk1, x + HC);
@@ -654,16 +712,34 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
     for (int e = 0; e < C; ++e) x[e] = 0.0;
   }
   if (use_rope) {
+    const double2 *ta = ropeA_s + (slot >> 3) * RW + (HC + 1) * q;
+    const double2 *tb = ropeB_s + (slot & 7) * RW + (HC + 1) * q;
 #pragma unroll
     for (int e = 0; e < HC; ++e) {
-      const double2 cs = rope_s[slot * RH + HC * q + e];
+      const double2 u = ta[e], w = tb[e];
+      const double c = u.x * w.x - u.y * w.y, sn = u.y * w.x + u.x * w.y;
       const double x0 = x[e], x1 = x[HC + e];
-      x[e] = x0 * cs.x - x1 * cs.y;
-      x[HC + e] = x0 * cs.y + x1 * cs.x;
+      x[e] = x0 * c - x1 * sn;
+      x[HC + e] = x0 * sn + x1 * c;
     }
   }
+  {
+    // the signs D after the rotary step (sign flips of the fp64 high words)
+    const uint4 *ma = reinterpret_cast<const uint4 *>(dsg_s + HC * q);
+    const uint4 *mb = reinterpret_cast<const uint4 *>(dsg_s + H + HC * q);
 #pragma unroll
-  for (int e = 0; e < C; ++e) x[e] = ((dmask >> e) & 1u) ? -x[e] : x[e];
+    for (int i = 0; i < HC / 4; ++i) {
+      const uint4 wa = ma[i], wb = mb[i];
+      x[4 * i] = xor_sign(x[4 * i], wa.x);
+      x[4 * i + 1] = xor_sign(x[4 * i + 1], wa.y);
+      x[4 * i + 2] = xor_sign(x[4 * i + 2], wa.z);
+      x[4 * i + 3] = xor_sign(x[4 * i + 3], wa.w);
+      x[HC + 4 * i] = xor_sign(x[HC + 4 * i], wb.x);
+      x[HC + 4 * i + 1] = xor_sign(x[HC + 4 * i + 1], wb.y);
+      x[HC + 4 * i + 2] = xor_sign(x[HC + 4 * i + 2], wb.z);
+      x[HC + 4 * i + 3] = xor_sign(x[HC + 4 * i + 3], wb.w);
+    }
+  }
   fwht_group4<D>(x, q);
   uint16_t ks1b = 0;
   if (a.ch.nsn) nsn_shift<D>(x, q, a.ch.nsn + size_t(unit) * 4 * D + 2 * D, sqrt_b, inv_sqrt_b, &ks1b, &over);
@@ -678,7 +754,10 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
       if ((i & 3) == q && valid) rec[i] = w[i];
     double rr = 0.0;
 #pragma unroll
-    for (int e = 0; e < C; ++e) rr = fma(x[e], x[e], rr);
+    for (int e = 0; e < C; ++e) {
+      rr = fma(x[e], x[e], rr);
+      r32[e] = float(x[e]);
+    }
     const uint16_t rn16b = f64_to_f16_sat(sqrt(group4_sum(rr)) * inv_sqrt_b, &over);
     if (valid && q == 0) a.ch.knorm[size_t(unit) * a.capacity + p] = uint32_t(n16b) | (uint32_t(rn16b) << 16);
   } else {
@@ -706,7 +785,8 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
       const uint64_t uo = uint64_t(__double_as_longlong(wo)), ui = uint64_t(__double_as_longlong(wi));
       const uint32_t olo = uint32_t(uo), ohi = uint32_t(uo >> 32), ilo = uint32_t(ui), ihi = uint32_t(ui >> 32);
       uint32_t sxA = 0u, sxB = 0u, sgA = 0u, sgB = 0u;   // sign bits of x; sign(x) xor sign(d)
-      auto code2 = [&](double &xe, uint32_t &sx, uint32_t &sg) {
+      auto code2 = [&](int i, uint32_t &sx, uint32_t &sg) {
+        double xe = x[i];
         const uint32_t xh = uint32_t(uint64_t(__double_as_longlong(xe)) >> 32);
         const uint32_t dh = uint32_t(uint64_t(__double_as_longlong(fabs(xe) - s1)) >> 32);
         sx = __builtin_amdgcn_alignbit(sx, xh, 31);        // sx << 1 | sign(x)
@@ -716,11 +796,17 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
         const uint32_t wh = (((ihi & m) | (ohi & ~m)) & 0x7FFFFFFFu) | (xh & 0x80000000u);
         xe -= __longlong_as_double(int64_t((uint64_t(wh) << 32) | wl));
         rr = fma(xe, xe, rr);
+        float rf = float(xe);
+        asm volatile("" : "+v"(rf));   // convert here: the fp64 residual dies at once
+        r32[i] = rf;
       };
 #pragma unroll
       for (int e = HC - 1; e >= 0; --e) {
-        code2(x[e], sxA, sgA);
-        code2(x[HC + e], sxB, sgB);
+        code2(e, sxA, sgA);
+        code2(HC + e, sxB, sgB);
+        // in order, four coordinates at a time: interleaving the whole loop holds more
+        // residuals than the registers of three waves per SIMD allow
+        if ((e & 1) == 0) __builtin_amdgcn_sched_barrier(0);
       }
       constexpr uint32_t hm = HC >= 32 ? 0xFFFFFFFFu : (1u << HC) - 1u;
       // a zero vector takes code 2 (the first positive centroid) everywhere
@@ -752,6 +838,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
         }
         x[e] -= w;
         rr = fma(x[e], x[e], rr);
+        r32[e] = float(x[e]);
       }
     } else {
       const int K = 1 << a.bits_k;
@@ -766,6 +853,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
         }
         x[e] -= nb16 * double(cb_s[0][code]);
         rr = fma(x[e], x[e], rr);
+        r32[e] = float(x[e]);
       }
     }
     const uint16_t rn16b = f64_to_f16_sat(sqrt(group4_sum(rr)) * inv_sqrt_b, &over);
@@ -787,7 +875,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
     // [2^13, 2^14) (the signs of S r do not change), and split into fp16 hi + lo parts
     float amax = 0.0f;
 #pragma unroll
-    for (int e = 0; e < C; ++e) amax = fmaxf(amax, fabsf(float(x[e])));
+    for (int e = 0; e < C; ++e) amax = fmaxf(amax, fabsf(r32[e]));
     amax = fmaxf(amax, __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(amax))));
     amax = fmaxf(amax, __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(amax))));
     const float rscale = amax > 0.0f ? __builtin_ldexpf(1.0f, 14 - __builtin_amdgcn_frexp_expf(amax)) : 1.0f;
@@ -796,7 +884,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
       v8h part[2][HC / 8];
 #pragma unroll
       for (int e = 0; e < HC; ++e) {
-        const float rr = float(x[c * HC + e]) * rscale;
+        const float rr = r32[c * HC + e] * rscale;
         const _Float16 hv = _Float16(rr);
         part[0][e / 8][e % 8] = hv;
         part[1][e / 8][e % 8] = _Float16(rr - float(hv));
@@ -813,18 +901,18 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
   // ------------------------------------------------------------ values
   if (a.bits_v > 0) {
     if (valid) {
-      if constexpr (!kEarlyV) {
-        load_raw<DT, HC>(a.v, row * D + HC * q, rv0);
-        load_raw<DT, HC>(a.v, row * D + H + HC * q, rv1);
-      }
+      load_raw<DT, HC>(a.v, row * D + HC * q, rv0);
+      load_raw<DT, HC>(a.v, row * D + H + HC * q, rv1);
+      // the signs D on the raw elements (no rotary step on values)
+      constexpr bool w32 = DT == TQ_F32;
+      xor_raw<DT, HC>(rv0, w32 ? dsg_s + HC * q : dsg_s + D + HC * q / 2);
+      xor_raw<DT, HC>(rv1, w32 ? dsg_s + H + HC * q : dsg_s + D + (H + HC * q) / 2);
       raw_to_f64<DT, HC>(rv0, x);
       raw_to_f64<DT, HC>(rv1, x + HC);
     } else {
 #pragma unroll
       for (int e = 0; e < C; ++e) x[e] = 0.0;
     }
-#pragma unroll
-    for (int e = 0; e < C; ++e) x[e] = ((dmask >> e) & 1u) ? -x[e] : x[e];
     fwht_group4<D>(x, q);
     uint16_t vs1b = 0;
     if (a.ch.nsn) nsn_shift<D>(x, q, a.ch.nsn + size_t(unit) * 4 * D + 3 * D, sqrt_b, inv_sqrt_b, &vs1b, &over);
@@ -865,7 +953,7 @@ __global__ __launch_bounds__(256, 2) void k_quantize_kv(QuantArgs a) {
         const double ax = fabs(x[e]);
         uint32_t nb = 0u;
 #pragma unroll
-        for (int i = 1; i < h; ++i) nb += uint32_t(uint64_t(__double_as_longlong(ax - sp[i - 1])) >> 63);
+        for (int i = 1; i < h; ++i) nb += ax < sp[i - 1] ? 1u : 0u;
         const uint32_t code = nb ^ ((2u * uint32_t(h) - 1u) & ~uint32_t(int32_t(xh) >> 31));
         cw[e / 4] |= code << (8 * (e % 4));
       }
