@@ -174,6 +174,7 @@ struct QuantArgs {
   const void *k, *v;
   int start, n_new, capacity, bits_k, bits_v, m, units;
   float rope_base;
+  double sqrt_b, inv_sqrt_b;   // sqrt(B) and 1 / sqrt(B) of the Hadamard block B (host fp64)
   RopeFreq rf;
 };
 
@@ -697,8 +698,7 @@ __global__ __launch_bounds__(256, POLAR ? 2 : 3) void k_quantize_kv(QuantArgs a)
   }
   __syncthreads();
 
-  const double sqrt_b = sqrt(double(a.cp.block));
-  const double inv_sqrt_b = 1.0 / sqrt_b;
+  const double sqrt_b = a.sqrt_b, inv_sqrt_b = a.inv_sqrt_b;
   uint32_t *rec = reinterpret_cast<uint32_t *>(a.ch.kbits + (size_t(unit) * a.capacity + (valid ? p : 0)) * a.ch.kbytes);
 
   // ------------------------------------------------------------ keys
@@ -4267,6 +4267,8 @@ tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_d
   a.m = desc->m;
   a.units = desc->batch * desc->kv_heads;
   a.rope_base = rope_base;
+  a.sqrt_b = std::sqrt(double(a.cp.block));
+  a.inv_sqrt_b = 1.0 / a.sqrt_b;
   if (rope_base != 0.0f && small) {
     for (int j = 0; j < d / 2; ++j) {
       const double th = std::pow(double(rope_base), -2.0 * double(j) / double(d));
