@@ -629,8 +629,8 @@ __global__ __launch_bounds__(256, POLAR ? 2 : 3) void k_quantize_kv(QuantArgs a)
   bool over = false;
 
   // the token's key row is requested before the RoPE tables are built, so that its latency
-  // overlaps them (the value row is requested when the keys are done: holding it through
-  // the key work would cost the registers of the third wave per SIMD)
+  // overlaps them (the value row is requested once the key codes are done: holding it
+  // through the key work would cost the registers of the third wave per SIMD)
   RawRow<DT, HC> rk0, rk1, rv0, rv1;
   if (valid) {
     load_raw<DT, HC>(a.k, row * D + HC * q, rk0);
@@ -868,6 +868,12 @@ __global__ __launch_bounds__(256, POLAR ? 2 : 3) void k_quantize_kv(QuantArgs a)
         a.ch.knorm[size_t(unit) * a.capacity + p] = nw;
     }
   }   // scalar codes
+  // the value row is requested now: the key doubles are dead, and its latency overlaps the
+  // barrier and the residual staging
+  if (valid && a.bits_v > 0) {
+    load_raw<DT, HC>(a.v, row * D + HC * q, rv0);
+    load_raw<DT, HC>(a.v, row * D + H + HC * q, rv1);
+  }
   __syncthreads();   // every wave is done with the RoPE table before residuals overwrite it
   {
     // residual r_H = H D x' - fp16(n) sqrt(B) c = sqrt(B) r (same signs of S r), rounded
@@ -901,8 +907,6 @@ __global__ __launch_bounds__(256, POLAR ? 2 : 3) void k_quantize_kv(QuantArgs a)
   // ------------------------------------------------------------ values
   if (a.bits_v > 0) {
     if (valid) {
-      load_raw<DT, HC>(a.v, row * D + HC * q, rv0);
-      load_raw<DT, HC>(a.v, row * D + H + HC * q, rv1);
       // the signs D on the raw elements (no rotary step on values)
       constexpr bool w32 = DT == TQ_F32;
       xor_raw<DT, HC>(rv0, w32 ? dsg_s + HC * q : dsg_s + D + HC * q / 2);
