@@ -1009,32 +1009,33 @@ __global__ __launch_bounds__(256, POLAR ? 2 : 3) void k_quantize_kv(QuantArgs a)
       const size_t srow = size_t(32 * mt + (lane & 31)) * D + 8 * half;
       const _Float16 *r0 = r_s + (lane & 31) * RS + 8 * half;
       const _Float16 *r1 = r0 + 32 * RS;
-      // the next step's S slices are requested one step ahead
+      // Every step's S slices are requested at once, so their L2 latency is paid once per
+      // block of rows (fetched one step ahead, the loop waited on them at every step).  The
+      // scheduling barrier keeps the loads here: hoisted into the value work their 96 VGPRs
+      // spill.  (Requested before the barrier above they would be waited for at it.)
       constexpr int NS = D / 16;
-      v8h sa[3];
+      v8h sv[NS][3];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < 3; ++k) sa[k] = *reinterpret_cast<const v8h *>(a.cp.Sh[k] + srow);
-#pragma unroll 2
+      for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int k = 0; k < 3; ++k) sv[i][k] = *reinterpret_cast<const v8h *>(a.cp.Sh[k] + srow + 16 * i);
+#pragma unroll
       for (int i = 0; i < NS; ++i) {
-        v8h ra[2], rb[2], sn[3];
-        const int inext = i + 1 < NS ? i + 1 : i;
-#pragma unroll
-        for (int k = 0; k < 3; ++k) sn[k] = *reinterpret_cast<const v8h *>(a.cp.Sh[k] + srow + 16 * inext);
+        v8h ra[2], rb[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
           ra[k] = *reinterpret_cast<const v8h *>(r0 + k * 64 * RS + 16 * i);
           rb[k] = *reinterpret_cast<const v8h *>(r1 + k * 64 * RS + 16 * i);
         }
 #define TQ_SR(A, B)                                                             \
-  acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[A], ra[B], acc0, 0, 0, 0); \
-  acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sa[A], rb[B], acc1, 0, 0, 0)
+  acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sv[i][A], ra[B], acc0, 0, 0, 0); \
+  acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sv[i][A], rb[B], acc1, 0, 0, 0)
         TQ_SR(2, 0);
         TQ_SR(0, 1);
         TQ_SR(1, 0);
         TQ_SR(0, 0);
 #undef TQ_SR
-#pragma unroll
-        for (int k = 0; k < 3; ++k) sa[k] = sn[k];
       }
       // lane holds rows 8 (r / 4) + 4 (lane / 32) + r % 4 of token column lane % 32
       uint32_t b0 = 0u, b1 = 0u;
