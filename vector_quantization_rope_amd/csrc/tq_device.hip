@@ -994,11 +994,12 @@ __global__ __launch_bounds__(256, POLAR ? 2 : 3) void k_quantize_kv(QuantArgs a)
 
   // ------------------------------------------------------------ QJL signs: z = S r
   // z^T[32 rows x 64 tokens] per 32-row block of S, both 32-token halves sharing the S
-  // operand, on fp16 MFMA (v_mfma_f32_32x32x16_f16): S in three fp16 parts (hi, mid, lo),
-  // the scaled residual in two (hi, lo).  The four products hi.hi, mid.hi, hi.lo and
-  // lo.hi leave out only mid.lo and lo.lo (2^-22 and 2^-33 of the leading term), and the
-  // residual's own split costs 2^-23: z to about 2^-22 relative, which moves a sign only
-  // for |z| a few 1e-7 of |r|, against the 2^-24 of fp32 MFMA at half the MFMA cycles.
+  // operand, on fp16 MFMA (v_mfma_f32_32x32x16_f16): S in fp16 parts hi + mid (the codec's
+  // third part, lo, is not needed here), the scaled residual in two (hi, lo).  The three
+  // products hi.hi, mid.hi and hi.lo leave out lo.hi and mid.lo (each at most 2^-22 of
+  // the leading term) and lo.lo (2^-33), and the residual's own split costs 2^-23: z to
+  // a few 2^-22 relative per term, a few 1e-7 of |r| over the d-term sum, so a sign can
+  // move only for |z| that close to zero (the parity rule's band is 1e-6 |r|).
   // Step i contracts k = 16 i + 8 (lane / 32) + 0..7 on both operands.
   {
     const int mt_n = a.m / 32;
@@ -1011,15 +1012,15 @@ __global__ __launch_bounds__(256, POLAR ? 2 : 3) void k_quantize_kv(QuantArgs a)
       const _Float16 *r1 = r0 + 32 * RS;
       // Every step's S slices are requested at once, so their L2 latency is paid once per
       // block of rows (fetched one step ahead, the loop waited on them at every step).  The
-      // scheduling barrier keeps the loads here: hoisted into the value work their 96 VGPRs
-      // spill.  (Requested before the barrier above they would be waited for at it.)
+      // scheduling barrier keeps the loads here: hoisted into the value work their 64 VGPRs
+      // spill.  (Requested before the barrier above they were slower.)
       constexpr int NS = D / 16;
-      v8h sv[NS][3];
+      v8h sv[NS][2];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NS; ++i)
 #pragma unroll
-        for (int k = 0; k < 3; ++k) sv[i][k] = *reinterpret_cast<const v8h *>(a.cp.Sh[k] + srow + 16 * i);
+        for (int k = 0; k < 2; ++k) sv[i][k] = *reinterpret_cast<const v8h *>(a.cp.Sh[k] + srow + 16 * i);
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         v8h ra[2], rb[2];
@@ -1031,7 +1032,6 @@ __global__ __launch_bounds__(256, POLAR ? 2 : 3) void k_quantize_kv(QuantArgs a)
 #define TQ_SR(A, B)                                                             \
   acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sv[i][A], ra[B], acc0, 0, 0, 0); \
   acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(sv[i][A], rb[B], acc1, 0, 0, 0)
-        TQ_SR(2, 0);
         TQ_SR(0, 1);
         TQ_SR(1, 0);
         TQ_SR(0, 0);
