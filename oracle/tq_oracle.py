@@ -30,7 +30,7 @@ Sources (titles of the pages; sections as they appear there):
               part plus a full-precision residual that is quantized and appended once
               full) -- attention over packed tokens and a full-precision window.
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent:
   * PRNG: SplitMix64 (Steele, Lea & Flood 2014) used as a counter-based generator;
     Gaussians by Box-Muller (cos branch) in fp64, rounded to fp32.
   * Rotation: Pi = blockdiag(H_B, ..., H_B) diag(D) / sqrt(B), H_B Sylvester, B the
