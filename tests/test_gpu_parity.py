@@ -420,7 +420,7 @@ def test_decode_step_loop(tq, P, bk, bv, d, G, L0, cap, steps, dt, nsn):
         f"worst {worst:.2e}, codes {rep}")
 
 
-@pytest.mark.parametrize("bk,bv,m", [(1, 2, 64), (3, 4, 128), (4, 1, 32), (2, 3, 0)])
+@pytest.mark.parametrize("bk,bv,m", [(1, 2, 64), (3, 4, 128), (4, 1, 32), (2, 3, 0), (2, 3, 96), (2, 3, 256)])
 def test_other_bit_widths(tq, P, bk, bv, m):
     w = W.LLAMA3_8B.scaled(batch=1, kv_heads=2, q_heads=4, context=300, bits_k=bk, bits_v=bv, m=m)
     K, V = W.gen_kv(w)
