@@ -131,6 +131,11 @@ def test_gqa_ragged_and_appends(tq, P, d, G, T, chunks):
     (1, 64, 4, 500, "laplace"),
     (3, 64, 2, 530, "laplace"),
     (3, 64, 1, 1024, "student_t3"),
+    # groups of at most 4 query heads at d = 128 take the 16-row key-score kernel
+    (1, 128, 4, 640, "laplace"),
+    (3, 128, 2, 650, "normal"),
+    (2, 128, 3, 515, "laplace"),
+    (3, 128, 1, 333, "normal"),
 ])
 def test_mfma_key_widths(tq, P, bk, d, G, T, dist):
     """1-bit and 3-bit keys (+ QJL) with 3-bit values on the MFMA decode path: for 3-bit

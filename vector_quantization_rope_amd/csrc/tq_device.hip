@@ -10,6 +10,8 @@
 //   k_decode_lds        split-K decode on MFMA with LDS-staged tiles: key scores (int8),
 //                       online softmax, values (fp16 hi/lo against LUT-dequantized
 //                       centroids), accumulated in the rotated basis
+//   k_decode_lds16      the same for groups of at most 4 query heads at d = 128, key
+//                       scores on the 16-row int8 MFMA form
 //   k_decode_split      the same on plain fp32 arithmetic for the other bit widths
 //   k_decode_merge      merge of the splits, normalisation, inverse rotation Pi^T (a
 //                       one-wave-per-row form, k_decode_merge_wave, for d = 64 and 128)
@@ -1530,7 +1532,8 @@ __device__ __forceinline__ float sum32(float v) {
 __device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, int d, int m,
                                            const CodecPtrs &cp, float *o, float (*red)[4], int tid,
                                            int lane, int wv, int b, int g, int h, int G,
-                                           int kv_heads, int bits_k, uint8_t *qpack, const float *nsn) {
+                                           int kv_heads, int bits_k, uint8_t *qpack, const float *nsn,
+                                           bool l16 = false) {
   // fp32 rows and sums; maxima for the fixed-point scaling (the two plane vectors
   // (c1 - c0) q and (c2 - c0) q share one exponent, set by the larger weight)
   // Key-plane weights of the odd codebook: c[code] = c0 + sum_p pw[p] bit_p(code).  For
@@ -1646,10 +1649,22 @@ __device__ __forceinline__ void qprep_tail(const float *qs, const float *sqs, in
       const int dg = digit == 0 ? d0 : (digit == 1 ? d1 : (digit == 2 ? d2 : d3));
       word |= uint32_t(dg & 255) << (8 * beta);
     }
+    // l16 (d = 128, G <= 4): the A operand of the 16-row key-score MFMA, rows 4 head + digit,
+    // the same 16-byte fragments at [slot][row][dword kg = 2 half + c / 2][nibble c % 2]
     const int row = digit * 8 + h;
-    o32[(((v * 32 + row) * 2 + half) * nch + c) * 4 + e] = word;
+    const int oi = l16 ? ((((v * 16 + 4 * h + digit) * 4 + 2 * half + (c >> 1)) * 2 + (c & 1)) * 4 + e)
+                       : ((((v * 32 + row) * 2 + half) * nch + c) * 4 + e);
+    o32[oi] = word;
   }
-  if (h == 0 && G < 8) {
+  if (h == 0 && l16 && G < 4) {
+    // rows 4 head + digit of the absent heads G <= head < 4, 32 words each
+    const int nrow = kDigits * (4 - G);
+    for (int i = tid; i < kQpackVecs * nrow * 32; i += 256) {
+      const int w = i & 31, ri = (i >> 5) % nrow, v = i / (32 * nrow);
+      o32[(v * 16 + 4 * (G + ri / kDigits) + ri % kDigits) * 32 + w] = 0u;
+    }
+  }
+  if (h == 0 && !l16 && G < 8) {
     // rows (digit, head) of the absent heads h >= G
     const int nrow = kDigits * (8 - G);
     for (int i = tid; i < kQpackVecs * nrow * 2 * nch * 4; i += 256) {
@@ -1777,7 +1792,7 @@ template <int D>
 __global__ __launch_bounds__(256) void k_qprep_fast(const void *q, int dtype, QueryRope qr,
                                                     CodecPtrs cp, float *qrows, int qstride,
                                                     int q_heads, int G, int bits_k, uint8_t *qpack,
-                                                    const float *nsn) {
+                                                    const float *nsn, int l16) {
   constexpr int H2 = D / 2, G4 = D / 4, SL = 256 / G4, JL = D / SL, E = D / 64;
   __shared__ float qs[D], sqs[D], part[SL * D];
   __shared__ float red[5][4];
@@ -1848,7 +1863,7 @@ __global__ __launch_bounds__(256) void k_qprep_fast(const void *q, int dtype, Qu
     sqs[tid] = z;
   }
   qprep_tail(qs, sqs, D, D, cp, qrows + size_t(rowi) * qstride, red, tid, lane, wv, b, g, h, G, kv_heads, bits_k, qpack,
-             nsn);
+             nsn, l16 != 0);
 }
 
 // LDS-staged split-K decode.  Each wave streams its tiles through a ring of kRing LDS
@@ -2345,6 +2360,341 @@ __global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds(
     }
     // NSN: the values' mean, sum_t p_t s1_t Pi o_V, joins the rotated accumulator
     if constexpr (NSN) v = fmaf(SO, a.nsn[size_t(unit) * 4 * D + 3 * D + j], v);
+    float *o = a.part + ((size_t(b * a.q_heads + hq0 + h) * a.splits) + split) * (D + 2);
+    o[j] = v;
+    if (j == 0) {
+      o[D] = mx == -INFINITY ? -INFINITY : mx * 0.69314718055994531f;
+      o[D + 1] = L;
+    }
+  }
+#else
+  (void)a;
+#endif
+}
+
+// Maxima of x over each row of 16 lanes, left in every lane of the row (quad swaps, then
+// half-row and row mirrors).
+__device__ __forceinline__ int dpp_max16(int x) {
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true));
+  x = max(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true));
+  return x;
+}
+
+// The split-K decode of k_decode_lds for groups of at most 4 query heads per kv-head
+// (G <= 4) at d = 128, plain caches.  Tiles, ring, value LUT and value MFMAs are the same;
+// the key scores run on v_mfma_i32_16x16x64_i8 with the 16 A rows 4 head + digit, where
+// the 32x32x32 form would leave half of its 32 rows (digit x head for 8 heads) idle: half
+// the matrix-core cycles per tile.  Lane l holds, for head l / 16, tokens l % 16 and
+// 16 + l % 16 of the tile: its B operands are dword l / 16 of those tokens' plane and sign
+// words (low nibbles for coordinates chunk 0, high nibbles for chunk 1, as the 32x32 form
+// splits a dword), and its four accumulator rows are the four digits of its head, so the
+// digit sums recombine in-lane as before.  The query prep writes the matching A operand
+// (the same 16-byte fragments, indexed [slot][4 head + digit][dword][nibble]).
+template <int KBITS, bool SCORES>
+__global__ __launch_bounds__(64 * kDecWaves, kDecBlocksPerCU) void k_decode_lds16(MfmaArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int D = 128;
+  using Gm = LdsGeom<D, KBITS, false>;
+  constexpr int NT = D / 16, NW = kDecWaves, NTH = 64 * NW, R = kRing;
+  constexpr int NP = KBITS == 3 ? 4 : KBITS;
+  static_assert(KBITS >= 1 && KBITS <= 3, "key planes");
+  __shared__ __align__(32768) uint2 lut[4096];
+  __shared__ __align__(16) uint8_t ring[R][NW][Gm::SLOT];
+  __shared__ __align__(16) _Float16 pt_s[NW][16][40];
+  __shared__ float red_s[NW][2][4];
+  static_assert(NW * 16 * D * 4 <= int(sizeof(ring)), "the waves' accumulators fit in the ring for the merge");
+
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int unit = blockIdx.x, split = blockIdx.y;
+  const int b = unit / a.kv_heads, kvh = unit % a.kv_heads;
+  const int hq0 = kvh * a.G;
+  for (int i = tid; i < 4096; i += NTH) {
+    const uint32_t h0 = f16bits(a.cv[i & 7]), h1 = f16bits(a.cv[(i >> 3) & 7]);
+    const uint32_t h2 = f16bits(a.cv[(i >> 6) & 7]), h3 = f16bits(a.cv[(i >> 9) & 7]);
+    lut[i] = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+  }
+  // P rows 4..7 and 12..15 (heads 4..7) are never written: zero once
+  {
+    uint32_t *pz = reinterpret_cast<uint32_t *>(&pt_s[0][0][0]);
+    for (int i = tid; i < NW * 16 * 40 / 2; i += NTH) pz[i] = 0u;
+  }
+  const int n = lane & 15, gh = lane >> 4;   // token of 16 (and its B/A lane group), head
+  const uint8_t *qpk = a.qpack + size_t(unit) * qpack_unit_bytes(D);
+  const float *coef = reinterpret_cast<const float *>(qpk + size_t(kQpackVecs) * 32 * 2 * (D / 32) * 16);
+  // this lane's head's score coefficients with the softmax scale (log2 domain)
+  const float K0 = coef[gh * kQpackCoef + 0] * a.scale_log2, K1 = coef[gh * kQpackCoef + 1] * a.scale_log2;
+  const float K3 = coef[gh * kQpackCoef + 3] * a.scale_log2, K4 = coef[gh * kQpackCoef + 4] * a.scale_log2;
+  // int8 digit rows: A lane (row n = 4 head + digit, K group gh), chunks 0 and 1
+  v4i Aq[NP][2], As[2];
+  {
+    const v4i *src = reinterpret_cast<const v4i *>(qpk);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int pp = 0; pp < NP; ++pp) Aq[pp][c] = src[((pp * 16 + n) * 4 + gh) * 2 + c];
+      As[c] = src[((kSqVec * 16 + n) * 4 + gh) * 2 + c];
+    }
+  }
+  __syncthreads();
+
+  const int t_begin = split * a.chunk;
+  const int t_end = min(a.length, t_begin + a.chunk);
+  const size_t ubase = size_t(unit) * a.capacity;
+  const int t_first = t_begin + 32 * wv;
+  constexpr int TS = 32 * NW;
+  const int nk = t_end > t_first ? (t_end - t_first + TS - 1) / TS : 0;
+  float M[4];   // running maxima per head (wave-uniform); absent heads: any finite value
+#pragma unroll
+  for (int h = 0; h < 4; ++h) M[h] = h < a.G ? -INFINITY : 0.0f;
+  const uint32_t gm0 = (gh & 1) ? 0xFFFFFFFFu : 0u, gm1 = (gh & 2) ? 0xFFFFFFFFu : 0u;
+  auto head_of = [&](const float *v) { return pick_bits(gm1, pick_bits(gm0, v[3], v[2]), pick_bits(gm0, v[1], v[0])); };
+  float Mh = head_of(M), lsum = 0.0f;
+  v4f acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int vq = lane >> 4, vn = lane & 15;
+  const int vidx = vq == 0 ? -1 : (24 * vq) >> 5;
+  const uint32_t vsh = vq == 0 ? 29u : uint32_t(((24 * vq) & 31) - 3);
+  const uint8_t *vbase = reinterpret_cast<const uint8_t *>(a.vcodes) + size_t(unit) * a.tiles * Gm::VT;
+  const uint8_t *vnbase = reinterpret_cast<const uint8_t *>(a.vnorm);
+  uint32_t koff[Gm::NK];
+#pragma unroll
+  for (int i = 0; i < Gm::NK; ++i) koff[i] = uint32_t(Gm::KCH * (64 * i + lane));
+  const uint8_t *kb0 = a.kbits + (ubase + t_first) * Gm::KB;
+  const uint8_t *vb0 = vbase + size_t(t_first / kValueTile) * Gm::VT;
+  const uint8_t *kn0 = reinterpret_cast<const uint8_t *>(a.knorm) + (ubase + t_first) * Gm::KNR;
+  const uint8_t *vn0 = vnbase + (ubase + t_first) * 2;
+  auto issue_dma = [&](int k, uint8_t *slot) {
+    const int kk = k < nk ? k : nk - 1;
+    const int t0 = t_first + TS * kk;
+    const int nv = t_end - t0;
+    const bool whole = nv >= 32;
+    const size_t tk0 = size_t(kk) * TS;
+    const uint8_t *ksrc = kb0 + tk0 * Gm::KB;
+    const int last = nv * Gm::KB / Gm::KCH - 1;
+    constexpr int kchunks = Gm::KT / Gm::KCH;
+#pragma unroll
+    for (int i = 0; i < Gm::NK; ++i) {
+      if (64 * i + 64 <= kchunks || lane < kchunks - 64 * i) {
+        const uint32_t o = whole ? koff[i] : uint32_t(Gm::KCH * min(64 * i + lane, last));
+        __builtin_amdgcn_global_load_lds(ksrc + o, slot + 64 * Gm::KCH * i, Gm::KCH, 0, 0);
+      }
+    }
+    const uint8_t *vsrc = vb0 + (tk0 / kValueTile) * Gm::VT;
+    constexpr int vchunks = Gm::VT / 16;
+#pragma unroll
+    for (int i = 0; i < Gm::NV; ++i) {
+      if (64 * i + 64 <= vchunks || lane < vchunks - 64 * i)
+        __builtin_amdgcn_global_load_lds(vsrc + 1024 * i + uint32_t(16 * lane), slot + Gm::KT + 1024 * i, 16, 0, 0);
+    }
+    if (lane < 32) {
+      const uint8_t *kn = kn0 + tk0 * 4;
+      __builtin_amdgcn_global_load_lds(kn + uint32_t(4 * (whole ? lane : min(lane, nv - 1))), slot + Gm::KN, 4, 0, 0);
+    }
+    if (lane < 17) {
+      const uint8_t *v2 = vn0 + tk0 * 2;
+      const uint32_t r = uint32_t(reinterpret_cast<uintptr_t>(vn0)) & 3u;
+      const uint32_t span = (r + 2u * uint32_t(nv - 1)) & ~3u;
+      __builtin_amdgcn_global_load_lds(v2 - r + min(uint32_t(4 * lane), span), slot + Gm::VN, 4, 0, 0);
+    }
+  };
+
+  auto step = [&](int k, const uint8_t *slot, uint8_t *nxt) {
+    issue_dma(k + R - 1, nxt);
+    if constexpr (SCORES)
+      __builtin_amdgcn_s_waitcnt(0);
+    else
+      wait_vmcnt_le<(R - 1) * Gm::NDMA>();
+    const int t0 = t_first + TS * k;
+    const int ta = t0 + n, tb = ta + 16;
+    const bool va = ta < t_end, vb = tb < t_end;
+    const uint32_t sbase = uint32_t(reinterpret_cast<uintptr_t>(slot));
+    // dword gh of the plane and sign words of tokens n and 16 + n (four words each: with
+    // fewer than three planes the extra reads fall on the next record or the value region
+    // of the slot and are not used), their norms and value norms, and the value-code words
+    uint32_t wa[4], wb[4], nra, nrb, vna, vnb2;
+    uint32_t vwr[NT][2];
+    {
+      const uint32_t kaddr = sbase + n * Gm::KB + 4 * gh;
+      const uint32_t naddr = sbase + Gm::KN + 4 * n;
+      const uint32_t vaddr = sbase + Gm::VN + uint32_t(((ubase + t0) * 2) & 3) + 2 * n;
+      const uint32_t caddr = sbase + Gm::KT + vn * 12 + 4 * vidx;
+      asm volatile(
+          "ds_read_b32 %0, %28\n"
+          "ds_read_b32 %1, %28 offset:16\n"
+          "ds_read_b32 %2, %28 offset:32\n"
+          "ds_read_b32 %3, %28 offset:48\n"
+          "ds_read_b32 %4, %32\n"
+          "ds_read_b32 %5, %32 offset:16\n"
+          "ds_read_b32 %6, %32 offset:32\n"
+          "ds_read_b32 %7, %32 offset:48\n"
+          "ds_read_b32 %8, %29\n"
+          "ds_read_b32 %9, %29 offset:64\n"
+          "ds_read_u16 %10, %30\n"
+          "ds_read_u16 %11, %30 offset:32\n"
+          "ds_read_b32 %12, %31\n"
+          "ds_read_b32 %13, %31 offset:4\n"
+          "ds_read_b32 %14, %31 offset:192\n"
+          "ds_read_b32 %15, %31 offset:196\n"
+          "ds_read_b32 %16, %31 offset:384\n"
+          "ds_read_b32 %17, %31 offset:388\n"
+          "ds_read_b32 %18, %31 offset:576\n"
+          "ds_read_b32 %19, %31 offset:580\n"
+          "ds_read_b32 %20, %31 offset:768\n"
+          "ds_read_b32 %21, %31 offset:772\n"
+          "ds_read_b32 %22, %31 offset:960\n"
+          "ds_read_b32 %23, %31 offset:964\n"
+          "ds_read_b32 %24, %31 offset:1152\n"
+          "ds_read_b32 %25, %31 offset:1156\n"
+          "ds_read_b32 %26, %31 offset:1344\n"
+          "ds_read_b32 %27, %31 offset:1348\n"
+          "s_waitcnt lgkmcnt(0)\n"
+          : "=&v"(wa[0]), "=&v"(wa[1]), "=&v"(wa[2]), "=&v"(wa[3]), "=&v"(wb[0]), "=&v"(wb[1]), "=&v"(wb[2]),
+            "=&v"(wb[3]), "=&v"(nra), "=&v"(nrb), "=&v"(vna), "=&v"(vnb2), "=&v"(vwr[0][0]), "=&v"(vwr[0][1]),
+            "=&v"(vwr[1][0]), "=&v"(vwr[1][1]), "=&v"(vwr[2][0]), "=&v"(vwr[2][1]), "=&v"(vwr[3][0]),
+            "=&v"(vwr[3][1]), "=&v"(vwr[4][0]), "=&v"(vwr[4][1]), "=&v"(vwr[5][0]), "=&v"(vwr[5][1]),
+            "=&v"(vwr[6][0]), "=&v"(vwr[6][1]), "=&v"(vwr[7][0]), "=&v"(vwr[7][1])
+          : "v"(kaddr), "v"(naddr), "v"(vaddr), "v"(caddr), "v"(kaddr + 16 * Gm::KB)
+          : "memory");
+    }
+    v8h Bv[NT];
+    const uint8_t *lutb = reinterpret_cast<const uint8_t *>(lut);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const uint32_t y = __builtin_amdgcn_alignbit(vwr[nt][1], vwr[nt][0], vsh);
+      const uint2 e0 = *reinterpret_cast<const uint2 *>(lutb + (y & 0x7FF8u));
+      const uint2 e1 = *reinterpret_cast<const uint2 *>(lutb + ((y >> 12) & 0x7FF8u));
+      v4i bw = {int(e0.x), int(e0.y), int(e1.x), int(e1.y)};
+      __builtin_memcpy(&Bv[nt], &bw, 16);
+    }
+    // ---- key scores: for each token half, chunk and plane, the B bytes are bit e of the
+    // low (chunk 0) or high (chunk 1) nibbles of the lane's plane word, masked in place
+    v4i s01[2] = {}, s2[2] = {};
+#pragma unroll
+    for (int tbk = 0; tbk < 2; ++tbk) {
+      const uint32_t *w = tbk ? wb : wa;
+      uint32_t pl[NP + 1];
+#pragma unroll
+      for (int pp = 0; pp < KBITS; ++pp) pl[pp] = w[pp];
+      if constexpr (KBITS == 3) pl[3] = w[0] ^ w[1] ^ w[2];
+      pl[NP] = w[KBITS];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        v4i bp[NP + 1];
+#pragma unroll
+        for (int pp = 0; pp <= NP; ++pp) {
+          const uint32_t nb = c ? pl[pp] >> 4 : pl[pp];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) bp[pp][e] = int(nb & (0x01010101u << e));
+        }
+#pragma unroll
+        for (int pp = 0; pp < NP; ++pp) s01[tbk] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Aq[pp][c], bp[pp], s01[tbk], 0, 0, 0);
+        s2[tbk] = __builtin_amdgcn_mfma_i32_16x16x64_i8(As[c], bp[NP], s2[tbk], 0, 0, 0);
+      }
+    }
+    float lam[2], rel[2], vnorm[2];
+#pragma unroll
+    for (int tbk = 0; tbk < 2; ++tbk) {
+      const uint32_t nr = tbk ? nrb : nra;
+      const float n16 = f16_bits_to_float(nr & 0xFFFFu), rn16 = f16_bits_to_float(nr >> 16);
+      vnorm[tbk] = f16_bits_to_float((tbk ? vnb2 : vna) & 0xFFFFu);
+      // the four accumulator rows are digits 0..3 of the lane's head
+      const float S01 = fmaf(float(s01[tbk][0] + 256 * s01[tbk][1]), 0x1p-16f, float(s01[tbk][2] + 256 * s01[tbk][3]));
+      const float S2 = fmaf(float(s2[tbk][0] + 256 * s2[tbk][1]), 0x1p-16f, float(s2[tbk][2] + 256 * s2[tbk][3]));
+      const float vbias = (tbk ? vb : va) ? 0.0f : -INFINITY;
+      lam[tbk] = fmaf(n16, fmaf(K1, S01, K0), fmaf(rn16, fmaf(K3, S2, -K4), vbias));
+      rel[tbk] = lam[tbk] - Mh;
+    }
+    if constexpr (SCORES) {
+      if (gh < a.G) {
+        float *srow = a.scores + (size_t(b) * a.q_heads + hq0 + gh) * a.score_stride;
+        if (va) srow[ta] = lam[0] * a.inv_scale_log2;
+        if (vb) srow[tb] = lam[1] * a.inv_scale_log2;
+      }
+    }
+    // ---- online softmax (log2 domain), maxima raised only past a slack of 8 (as in
+    // k_decode_lds); the tile maximum of a head is the maximum over its row of 16 lanes
+    const float sla = vnorm[0] < 255.0f ? 8.0f : 0.0f, slb = vnorm[1] < 255.0f ? 8.0f : 0.0f;
+    const uint64_t above = __builtin_amdgcn_ballot_w64(rel[0] > sla || rel[1] > slb);
+    if (above != 0) {
+      const int v = dpp_max16(max(f2ord(lam[0]), f2ord(lam[1])));
+      float alpha[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float tm = ord2f(__builtin_amdgcn_readlane(v, 16 * h + 15));
+        const float nm = fmaxf(M[h], tm);
+        alpha[h] = (nm == M[h]) ? 1.0f : __builtin_amdgcn_exp2f(M[h] - nm);
+        M[h] = nm;
+      }
+      // accumulator row 4 vq + r holds head r (hi for vq = 0, lo for vq = 2; the rows of
+      // vq = 1 and 3 are the zero P rows of heads 4..7)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][r] *= alpha[r];
+      lsum *= head_of(alpha);
+      Mh = head_of(M);
+      rel[0] = lam[0] - Mh;
+      rel[1] = lam[1] - Mh;
+    }
+#pragma unroll
+    for (int tbk = 0; tbk < 2; ++tbk) {
+      const float p = __builtin_amdgcn_exp2f(rel[tbk]);
+      lsum += p;
+      const float pv = p * vnorm[tbk];
+      const _Float16 hi = (_Float16)pv;
+      const _Float16 lo = (_Float16)(pv - float(hi));
+      pt_s[wv][gh][n + 16 * tbk] = hi;
+      pt_s[wv][8 + gh][n + 16 * tbk] = lo;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const v8h A = *reinterpret_cast<const v8h *>(&pt_s[wv][vn][8 * vq]);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bv[nt], acc[nt], 0, 0, 0);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  };
+
+  if (nk > 0) {
+#pragma unroll
+    for (int k = 0; k < R - 1; ++k) issue_dma(k, &ring[k][wv][0]);
+    for (int k = 0; k < nk; k += R) {
+#pragma unroll
+      for (int sl = 0; sl < R; ++sl)
+        if (k + sl < nk) step(k + sl, &ring[sl][wv][0], &ring[(sl + R - 1) % R][wv][0]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+  // ---- merge the block's waves: the head's sum over its row of 16 lanes
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+  __syncthreads();
+  float *acc_s = reinterpret_cast<float *>(&ring[0][0][0]);   // [NW waves][16 rows][D]
+  if (n == 0) red_s[wv][1][gh] = lsum;
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) red_s[wv][0][h] = M[h];
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc_s[(wv * 16 + 4 * vq + r) * D + 16 * nt + vn] = acc[nt][r];
+  __syncthreads();
+  for (int i = tid; i < a.G * D; i += NTH) {
+    const int h = i / D, j = i % D;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, red_s[w][0][h]);
+    float v = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float mw = red_s[w][0][h];
+      if (mw == -INFINITY) continue;
+      const float f = exp2f(mw - mx);
+      v += (acc_s[(w * 16 + h) * D + j] + acc_s[(w * 16 + 8 + h) * D + j]) * f;
+      L += red_s[w][1][h] * f;
+    }
     float *o = a.part + ((size_t(b * a.q_heads + hq0 + h) * a.splits) + split) * (D + 2);
     o[j] = v;
     if (j == 0) {
@@ -4222,6 +4572,20 @@ static void launch_mfma(int d, int bk, dim3 grid, dim3 blk, hipStream_t s, const
 #undef TQ_MFMA
 }
 
+static void launch_mfma16(int bk, dim3 grid, dim3 blk, hipStream_t s, const MfmaArgs &ma) {
+#define TQ_MFMA16(BK)                                                                   \
+  if (bk == BK) {                                                                       \
+    if (ma.scores)                                                                      \
+      hipLaunchKernelGGL((k_decode_lds16<BK, true>), grid, blk, 0, s, ma);              \
+    else                                                                                \
+      hipLaunchKernelGGL((k_decode_lds16<BK, false>), grid, blk, 0, s, ma);             \
+  }
+  TQ_MFMA16(1)
+  TQ_MFMA16(2)
+  TQ_MFMA16(3)
+#undef TQ_MFMA16
+}
+
 extern "C" {
 
 tq_status tq_cache_init(const tq_cache_desc *desc, void *cache_dev, tq_stream_t stream) {
@@ -4432,6 +4796,9 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
   const int G = q_heads / desc->kv_heads;
   const float sc = scale == 0.0f ? float(1.0 / std::sqrt(double(d))) : scale;
   const bool mfma = decode_mfma_path(*desc, q_heads);
+  // groups of at most 4 query heads at d = 128 (plain caches, with an output): key scores
+  // on the 16-row MFMA form (k_decode_lds16), whose digit rows the query prep lays out
+  const bool l16 = mfma && out && d == 128 && m == 128 && !desc->nsn && q_heads / desc->kv_heads <= 4;
   // the int8 digit rows: the MFMA path's key and QJL scores, PolarQuant's QJL sums
   const bool with_qpack = mfma || desc->polar;
   // odd key codebook on the MFMA path: c[code] = c0 + a weighted sum of bit planes
@@ -4454,10 +4821,10 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
     }
     if (d == 64)
       hipLaunchKernelGGL(k_qprep_fast<64>, dim3(rows), dim3(256), 0, s, q, int(dtype), qr, cp, qp, qstride,
-                         q_heads, G, bk, with_qpack ? qpack : nullptr, ch.nsn);
+                         q_heads, G, bk, with_qpack ? qpack : nullptr, ch.nsn, 0);
     else
       hipLaunchKernelGGL(k_qprep_fast<128>, dim3(rows), dim3(256), 0, s, q, int(dtype), qr, cp, qp, qstride,
-                         q_heads, G, bk, with_qpack ? qpack : nullptr, ch.nsn);
+                         q_heads, G, bk, with_qpack ? qpack : nullptr, ch.nsn, l16 ? 1 : 0);
   } else {
     hipLaunchKernelGGL(k_qprep_pack, dim3(rows), dim3(256), size_t(d + m + (m > 1024 ? m : 1024)) * 4, s, q,
                        int(dtype), d, m, q_pos, rope_base, cp, qp, qstride, q_heads, G, bk,
@@ -4510,7 +4877,9 @@ static tq_status decode_impl(const tq_cache_desc *desc, const void *codec_dev,
     dim3 grid(units, used_splits);
     if (ev_start && hipEventRecord(hipEvent_t(ev_start), s) != hipSuccess) return TQ_EDEVICE;
     const dim3 blk(64 * kDecWaves);
-    if (desc->nsn)
+    if (l16)
+      launch_mfma16(bk, grid, blk, s, ma);
+    else if (desc->nsn)
       launch_mfma<false, true>(d, bk, grid, blk, s, ma);
     else
       launch_mfma<false, false>(d, bk, grid, blk, s, ma);
