@@ -548,6 +548,28 @@ def test_search_small(tq, P):
     check_topk(idx.cpu().numpy(), val.cpu().numpy(), s_o, idx_o, val_o)
 
 
+@pytest.mark.parametrize("d,bits,m", [(256, 3, 256), (512, 2, 512), (1024, 3, 512), (2048, 1, 2048)])
+def test_db_codes_widths(tq, P, d, bits, m):
+    """Database vectors at the other widths the wide-vector encoder serves (one wave per
+    vector, S r on fp32 MFMA): every code, norm, QJL bit and residual norm against the
+    oracle's encode under the boundary rule; 40 vectors, so the last group of 16 is
+    ragged."""
+    w = W.VECTOR_SEARCH.scaled(n_db=40, nq=1, d=d, bits=bits, m=m)
+    db, _ = W.gen_search(w)
+    codec = tq.Codec(d, bits, 0, m, seed=3)
+    cache = tq.PackedCache(1, 1, d, w.n_db, bits, 0, m)
+    tq.quantize_kv(cache.desc, codec.dev, cache.buf, db.cuda()[None, None], None, 0, 0.0)
+    torch.cuda.synchronize()
+    codec_o = O.make_codec(d, bits, 0, m, 3)
+    enc = O.encode(db.double().numpy(), codec_o, kind="db")
+    g = O.unpack_cache(cache.buf.cpu().numpy(), cache.desc.as_dict(), w.n_db)
+    orc = {"kcodes": enc["codes"][None, None], "n16": enc["n16"][None, None], "rn16": enc["rn16"][None, None],
+           "bits": enc["bits"][None, None], "ku": enc["u"][None, None], "kn": enc["n"][None, None],
+           "krn": enc["rn"][None, None], "kz": enc["z"][None, None]}
+    rep = P.compare_codes(g, orc, codec_o)
+    say(f"[db d={d} bits={bits} m={m}] {rep}")
+
+
 def check_topk(idx, val, s_o, idx_o, val_o, tie=1e-6, stol=1e-4):
     """Top-k identical except swaps among entries whose oracle scores differ by <= tie."""
     nq, k = idx.shape

@@ -1125,7 +1125,9 @@ __global__ __launch_bounds__(256) void k_quantize_db(QuantArgs a) {
   constexpr int RS = Dm + 4;
   extern __shared__ float r_s[];   // [16][RS]
   __shared__ float cb_s[2][kMaxCodes];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  // (the wave index is wave-uniform: what derives from it, the S rows' buffer resource
+  // included, lives in scalar registers)
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = blockIdx.y;
   const int g0 = a.start + int(blockIdx.x) * kLargeGroup;
   const int end = a.start + a.n_new;
@@ -1219,15 +1221,53 @@ __global__ __launch_bounds__(256) void k_quantize_db(QuantArgs a) {
     }
   }
   __syncthreads();
-  // z^T[m x 16] = S[m x Dm] . R^T[Dm x 16], 16-row output tiles spread over the waves
+  // z^T[m x 16] = S[m x Dm] . R^T[Dm x 16], 16-row output tiles spread over the waves.
+  // The contraction runs in chunks of 16 coordinates; in chunk c, MFMA i takes from lane
+  // group g = lane / 16 the coordinate 16 c + 4 g + i (any order of k serves, A and B
+  // using the same), so a lane reads S and R as one 16-byte vector per chunk.  The S
+  // vectors of the next kDbPf chunks are in flight while a chunk is multiplied: S comes
+  // from L2 / the last-level cache, and one wave per SIMD has nothing else to hide the
+  // latency behind.
+  constexpr int kDbPf = 8;
+  constexpr int NCK = Dm / 16;
+  static_assert(NCK % kDbPf == 0, "whole prefetch rounds");
   const int mt_n = a.m / 16;
   for (int mt = wv; mt < mt_n; mt += 4) {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    const float *srow = a.cp.S + size_t(16 * mt + (lane & 15)) * Dm + (lane >> 4);
-    const float *rrow = r_s + (lane & 15) * RS + (lane >> 4);
-#pragma unroll 8
-    for (int j0 = 0; j0 < Dm; j0 += 4)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(srow[j0], rrow[j0], acc, 0, 0, 0);
+    // (buffer loads: S is read-only, and from plain loads the compiler would load each
+    // vector again where it is used instead of keeping the early load's result)
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(a.cp.S + size_t(16 * mt) * Dm), 0, 16 * Dm * 4, 0x00020000);
+    const int soff = ((lane & 15) * Dm + 4 * (lane >> 4)) * 4;   // bytes: the lane's row, group
+    auto sload = [&](int c) {
+      return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(srs, soff + 64 * c, 0, 0));
+    };
+    const float4 *rrow = reinterpret_cast<const float4 *>(r_s + (lane & 15) * RS) + (lane >> 4);
+    v4f sb[kDbPf];
+#pragma unroll
+    for (int f = 0; f < kDbPf; ++f) sb[f] = sload(f);
+    for (int c0 = 0; c0 < NCK; c0 += kDbPf) {
+      // this round's vectors, then the next round's requested in one block (the scheduling
+      // barriers keep the compiler from sinking each load to its use)
+      v4f cur[kDbPf];
+#pragma unroll
+      for (int f = 0; f < kDbPf; ++f) cur[f] = sb[f];
+      __builtin_amdgcn_sched_barrier(0);
+      if (c0 + kDbPf < NCK) {
+#pragma unroll
+        for (int f = 0; f < kDbPf; ++f) sb[f] = sload(c0 + kDbPf + f);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < kDbPf; ++f) {
+        const float4 rv = rrow[4 * (c0 + f)];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][0], rv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][1], rv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][2], rv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][3], rv.w, acc, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // lane holds outputs 16 mt + 4 (lane / 16) + r of vector lane % 16
     uint32_t bits = 0u;
 #pragma unroll
