@@ -1139,18 +1139,36 @@ __global__ __launch_bounds__(256) void k_quantize_db(QuantArgs a) {
   const double inv_sqrt_b = 1.0 / sqrt(double(B));
   const int K = 1 << a.bits_k;
   const int dbytes = Dm / 8;
-  for (int vi = wv; vi < kLargeGroup; vi += 4) {
-    const int p = g0 + vi;
-    const bool valid = p < end;
-    const size_t row = size_t(unit) * size_t(a.n_new) + size_t(valid ? p - a.start : 0);
-    double x[C];
+  // the rows of all of this wave's vectors (and the signs D) are requested up front, so
+  // that one memory latency, not one per vector, precedes the encodes (one wave per SIMD
+  // has nothing else to hide it behind); elements as fp32, exact for every input type
+  // (at d = 2048 one row ahead: more would not fit beside the encode's registers)
+  constexpr int NVW = kLargeGroup / 4, NPRE = C >= 32 ? 1 : NVW;
+  float xr[NPRE][C], dj[C];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int e = 0; e < E; ++e) dj[b * E + e] = a.cp.D[b * B + E * lane + e];
+  auto load_row = [&](int v, float *dst) {
+    const int p = g0 + wv + 4 * v;
+    const size_t row = size_t(unit) * size_t(a.n_new) + size_t(p < end ? p - a.start : 0);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int j = b * B + E * lane + e;
-        x[b * E + e] = valid ? load_d<DT>(a.k, row * Dm + j) * double(a.cp.D[j]) : 0.0;
-      }
+      for (int e = 0; e < E; ++e)
+        dst[b * E + e] = p < end ? float(load_d<DT>(a.k, row * Dm + b * B + E * lane + e)) : 0.0f;
+  };
+#pragma unroll
+  for (int v = 0; v < NPRE; ++v) load_row(v, xr[v]);
+#pragma unroll
+  for (int v = 0; v < NVW; ++v) {
+    const int vi = wv + 4 * v;
+    const int p = g0 + vi;
+    const bool valid = p < end;
+    double x[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) x[c] = double(xr[v % NPRE][c]) * double(dj[c]);
+    if (v + NPRE < NVW) load_row(v + NPRE, xr[v % NPRE]);   // the slot just read: the next row it serves
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       fwht_regs<E>(x + b * E);
