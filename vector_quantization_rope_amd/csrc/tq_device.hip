@@ -1114,11 +1114,13 @@ __global__ __launch_bounds__(256, POLAR ? 2 : 3) void k_quantize_kv(QuantArgs a)
 // Database vectors of large d (keys only, no RoPE): one wave per vector for the fp64
 // rotation, norm, codes and residual (lane l holds, in each Hadamard block b, the E
 // consecutive coordinates b*B + E*l + e); the workgroup's 16 residuals then go through
-// z = S r on fp32 MFMA (v_mfma_f32_16x16x4f32), S streamed from L2.
+// z = S r on fp32 MFMA (v_mfma_f32_16x16x4f32), S streamed from L2.  Eight waves, two
+// per SIMD, so that one wave's S loads are in flight while the other multiplies.
 constexpr int kLargeGroup = 16;
+constexpr int kDbWaves = 8;
 
 template <int C, int E, int DT>
-__global__ __launch_bounds__(256) void k_quantize_db(QuantArgs a) {
+__global__ __launch_bounds__(64 * kDbWaves) void k_quantize_db(QuantArgs a) {
   constexpr int NB = C / E;
   constexpr int B = 64 * E;
   constexpr int Dm = C * 64;
@@ -1139,18 +1141,18 @@ __global__ __launch_bounds__(256) void k_quantize_db(QuantArgs a) {
   const double inv_sqrt_b = 1.0 / sqrt(double(B));
   const int K = 1 << a.bits_k;
   const int dbytes = Dm / 8;
-  // the rows of all of this wave's vectors (and the signs D) are requested up front, so
-  // that one memory latency, not one per vector, precedes the encodes (one wave per SIMD
-  // has nothing else to hide it behind); elements as fp32, exact for every input type
-  // (at d = 2048 one row ahead: more would not fit beside the encode's registers)
-  constexpr int NVW = kLargeGroup / 4, NPRE = C >= 32 ? 1 : NVW;
+  // the rows of both of this wave's vectors (and the signs D) are requested up front, so
+  // that one memory latency, not one per vector, precedes the encodes; elements as fp32,
+  // exact for every input type (at d >= 1536 one row ahead: more would not fit beside the
+  // encode's registers)
+  constexpr int NVW = kLargeGroup / kDbWaves, NPRE = C >= 24 ? 1 : NVW;
   float xr[NPRE][C], dj[C];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
 #pragma unroll
     for (int e = 0; e < E; ++e) dj[b * E + e] = a.cp.D[b * B + E * lane + e];
   auto load_row = [&](int v, float *dst) {
-    const int p = g0 + wv + 4 * v;
+    const int p = g0 + wv + kDbWaves * v;
     const size_t row = size_t(unit) * size_t(a.n_new) + size_t(p < end ? p - a.start : 0);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -1162,7 +1164,7 @@ __global__ __launch_bounds__(256) void k_quantize_db(QuantArgs a) {
   for (int v = 0; v < NPRE; ++v) load_row(v, xr[v]);
 #pragma unroll
   for (int v = 0; v < NVW; ++v) {
-    const int vi = wv + 4 * v;
+    const int vi = wv + kDbWaves * v;
     const int p = g0 + vi;
     const bool valid = p < end;
     double x[C];
@@ -1244,13 +1246,13 @@ __global__ __launch_bounds__(256) void k_quantize_db(QuantArgs a) {
   // group g = lane / 16 the coordinate 16 c + 4 g + i (any order of k serves, A and B
   // using the same), so a lane reads S and R as one 16-byte vector per chunk.  The S
   // vectors of the next kDbPf chunks are in flight while a chunk is multiplied: S comes
-  // from L2 / the last-level cache, and one wave per SIMD has nothing else to hide the
-  // latency behind.
+  // from L2 / the last-level cache, and two waves per SIMD cannot hide that latency by
+  // themselves.
   constexpr int kDbPf = 8;
   constexpr int NCK = Dm / 16;
   static_assert(NCK % kDbPf == 0, "whole prefetch rounds");
   const int mt_n = a.m / 16;
-  for (int mt = wv; mt < mt_n; mt += 4) {
+  for (int mt = wv; mt < mt_n; mt += kDbWaves) {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
     // (buffer loads: S is read-only, and from plain loads the compiler would load each
     // vector again where it is used instead of keeping the early load's result)
@@ -4734,7 +4736,7 @@ tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_d
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_quantize_db<CC, EE, TT>),         \
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess) \
       return TQ_EDEVICE;                                                                       \
-    hipLaunchKernelGGL((k_quantize_db<CC, EE, TT>), grid, dim3(256), shm, s, a);               \
+    hipLaunchKernelGGL((k_quantize_db<CC, EE, TT>), grid, dim3(64 * kDbWaves), shm, s, a);               \
   } while (0)
 #define TQ_QDB_T(CC, EE) \
   do { if (dtype == TQ_F32) TQ_QDB(CC, EE, TQ_F32); else if (dtype == TQ_BF16) TQ_QDB(CC, EE, TQ_BF16); else TQ_QDB(CC, EE, TQ_F16); } while (0)
