@@ -4736,7 +4736,7 @@ tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_d
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_quantize_db<CC, EE, TT>),         \
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess) \
       return TQ_EDEVICE;                                                                       \
-    hipLaunchKernelGGL((k_quantize_db<CC, EE, TT>), grid, dim3(64 * kDbWaves), shm, s, a);      \
+    hipLaunchKernelGGL((k_quantize_db<CC, EE, TT>), grid, dim3(64 * kDbWaves), shm, s, a);     \
   } while (0)
 #define TQ_QDB_T(CC, EE) \
   do { if (dtype == TQ_F32) TQ_QDB(CC, EE, TQ_F32); else if (dtype == TQ_BF16) TQ_QDB(CC, EE, TQ_BF16); else TQ_QDB(CC, EE, TQ_F16); } while (0)
