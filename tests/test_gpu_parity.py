@@ -548,12 +548,12 @@ def test_search_small(tq, P):
     check_topk(idx.cpu().numpy(), val.cpu().numpy(), s_o, idx_o, val_o)
 
 
-@pytest.mark.parametrize("d,bits,m", [(256, 3, 256), (512, 2, 512), (1024, 3, 512), (2048, 1, 2048)])
+@pytest.mark.parametrize("d,bits,m", [(256, 3, 256), (512, 2, 512), (1024, 3, 512), (1536, 3, 1536), (2048, 1, 2048)])
 def test_db_codes_widths(tq, P, d, bits, m):
-    """Database vectors at the other widths the wide-vector encoder serves (one wave per
-    vector, S r on fp32 MFMA): every code, norm, QJL bit and residual norm against the
-    oracle's encode under the boundary rule; 40 vectors, so the last group of 16 is
-    ragged."""
+    """Database vectors at every width the wide-vector encoder serves (one wave per vector;
+    S r on fp16 MFMA in groups of 24 up to d = 1536, on fp32 MFMA in groups of 16 at
+    2048): every code, norm, QJL bit and residual norm against the oracle's encode under
+    the boundary rule; 40 vectors, so the last group is ragged."""
     w = W.VECTOR_SEARCH.scaled(n_db=40, nq=1, d=d, bits=bits, m=m)
     db, _ = W.gen_search(w)
     codec = tq.Codec(d, bits, 0, m, seed=3)

@@ -1114,24 +1114,35 @@ __global__ __launch_bounds__(256, POLAR ? 2 : 3) void k_quantize_kv(QuantArgs a)
 // Database vectors of large d (keys only, no RoPE): one wave per vector for the fp64
 // rotation, norm, codes and residual (lane l holds, in each Hadamard block b, the E
 // consecutive coordinates b*B + E*l + e); the workgroup's 16 residuals then go through
-// z = S r on fp32 MFMA (v_mfma_f32_16x16x4f32), S streamed from L2.  Eight waves, two
-// per SIMD, so that one wave's S loads are in flight while the other multiplies.
-constexpr int kLargeGroup = 16;
+// z = S r on MFMA with S streamed from L2.  Eight waves, two per SIMD, so that one wave's
+// S loads are in flight while the other multiplies.  For d <= 1536 a workgroup takes 24
+// vectors, whose residuals fit in LDS as fp16 hi + lo parts, and the products run on fp16
+// MFMA (v_mfma_f32_32x32x16_f16: S hi.r hi + S mid.r hi + S hi.r lo, as in the append);
+// at d = 2048 it takes 16 vectors with fp32 residuals on v_mfma_f32_16x16x4f32.
 constexpr int kDbWaves = 8;
+__host__ __device__ constexpr int db_group(int c) { return c <= 24 ? 24 : 16; }
+__host__ __device__ constexpr size_t db_lds_bytes(int c) {
+  return c <= 24 ? size_t(2) * db_group(c) * (64 * c + 8) * 2 : size_t(db_group(c)) * (64 * c + 4) * 4;
+}
 
 template <int C, int E, int DT>
 __global__ __launch_bounds__(64 * kDbWaves) void k_quantize_db(QuantArgs a) {
   constexpr int NB = C / E;
   constexpr int B = 64 * E;
   constexpr int Dm = C * 64;
-  constexpr int RS = Dm + 4;
-  extern __shared__ float r_s[];   // [16][RS]
+  constexpr bool F16 = C <= 24;
+  constexpr int GV = db_group(C);
+  constexpr int RS = Dm + 4;        // fp32 residual row
+  constexpr int RS16 = Dm + 8;      // fp16 residual row
+  static_assert(GV % kDbWaves == 0, "whole vectors per wave");
+  extern __shared__ float r_s[];   // fp32: [GV][RS]; fp16: [2 parts][GV][RS16]
+  _Float16 *r16 = reinterpret_cast<_Float16 *>(r_s);
   __shared__ float cb_s[2][kMaxCodes];
   // (the wave index is wave-uniform: what derives from it, the S rows' buffer resource
   // included, lives in scalar registers)
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = blockIdx.y;
-  const int g0 = a.start + int(blockIdx.x) * kLargeGroup;
+  const int g0 = a.start + int(blockIdx.x) * GV;
   const int end = a.start + a.n_new;
   if (tid < kMaxCodes) {
     cb_s[0][tid] = a.cp.ck[tid];
@@ -1145,7 +1156,7 @@ __global__ __launch_bounds__(64 * kDbWaves) void k_quantize_db(QuantArgs a) {
   // that one memory latency, not one per vector, precedes the encodes; elements as fp32,
   // exact for every input type (at d >= 1536 one row ahead: more would not fit beside the
   // encode's registers)
-  constexpr int NVW = kLargeGroup / kDbWaves, NPRE = C >= 24 ? 1 : NVW;
+  constexpr int NVW = GV / kDbWaves, NPRE = C >= 24 ? 1 : NVW;
   float xr[NPRE][C], dj[C];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -1231,74 +1242,162 @@ __global__ __launch_bounds__(64 * kDbWaves) void k_quantize_db(QuantArgs a) {
         }
       }
     }
+    if constexpr (F16) {
+      // the residual rounded to fp32, scaled by a power of two that brings its largest
+      // |r_j| into [2^13, 2^14) (the signs of S r do not change), split into fp16 hi + lo
+      float amax = 0.0f;
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+      for (int c = 0; c < C; ++c) amax = fmaxf(amax, fabsf(float(x[c])));
+      amax = wave_max(amax);
+      const float rscale = amax > 0.0f ? __builtin_ldexpf(1.0f, 14 - __builtin_amdgcn_frexp_expf(amax)) : 1.0f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) r_s[vi * RS + b * B + E * lane + e] = float(x[b * E + e]);
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float rv = float(x[b * E + e]) * rscale;
+          const _Float16 hv = _Float16(rv);
+          r16[size_t(vi) * RS16 + b * B + E * lane + e] = hv;
+          r16[size_t(GV + vi) * RS16 + b * B + E * lane + e] = _Float16(rv - float(hv));
+        }
+    } else {
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < E; ++e) r_s[vi * RS + b * B + E * lane + e] = float(x[b * E + e]);
+    }
     if (valid && lane == 0) {
       a.ch.knorm[size_t(unit) * a.capacity + p] = uint32_t(n16b) | (uint32_t(rn16b) << 16);
       if (over) atomicOr(a.ch.flags, 1u);
     }
   }
   __syncthreads();
-  // z^T[m x 16] = S[m x Dm] . R^T[Dm x 16], 16-row output tiles spread over the waves.
-  // The contraction runs in chunks of 16 coordinates; in chunk c, MFMA i takes from lane
-  // group g = lane / 16 the coordinate 16 c + 4 g + i (any order of k serves, A and B
-  // using the same), so a lane reads S and R as one 16-byte vector per chunk.  The S
-  // vectors of the next kDbPf chunks are in flight while a chunk is multiplied: S comes
-  // from L2 / the last-level cache, and two waves per SIMD cannot hide that latency by
-  // themselves.
-  constexpr int kDbPf = 8;
-  constexpr int NCK = Dm / 16;
-  static_assert(NCK % kDbPf == 0, "whole prefetch rounds");
-  const int mt_n = a.m / 16;
-  for (int mt = wv; mt < mt_n; mt += kDbWaves) {
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    // (buffer loads: S is read-only, and from plain loads the compiler would load each
-    // vector again where it is used instead of keeping the early load's result)
-    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(a.cp.S + size_t(16 * mt) * Dm), 0, 16 * Dm * 4, 0x00020000);
-    const int soff = ((lane & 15) * Dm + 4 * (lane >> 4)) * 4;   // bytes: the lane's row, group
-    auto sload = [&](int c) {
-      return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(srs, soff + 64 * c, 0, 0));
-    };
-    const float4 *rrow = reinterpret_cast<const float4 *>(r_s + (lane & 15) * RS) + (lane >> 4);
-    v4f sb[kDbPf];
+  if constexpr (F16) {
+    // z^T[32 rows x 32 columns] per 32-row tile of S, the group's GV vectors in columns
+    // 0..GV-1 (the other columns read vector GV-1 again and are not stored), on
+    // v_mfma_f32_32x32x16_f16: S in its fp16 parts hi + mid, the scaled residual in hi + lo,
+    // and the products hi.hi, mid.hi and hi.lo (each term left out is at most 2^-22 of the
+    // leading one).  Step i contracts k = 16 i + 8 (lane / 32) + 0..7 on both operands.
+    // The S parts of the next kDbPf16 steps are in flight while a step is multiplied
+    // (buffer loads, for the same reason as in the fp32 form below).
+    constexpr int kDbPf16 = 4;
+    constexpr int NS = Dm / 16;
+    static_assert(NS % kDbPf16 == 0, "whole prefetch rounds");
+    const int mt_n = a.m / 32;
+    const int half = lane >> 5, col = lane & 31;
+    const _Float16 *rh = r16 + size_t(col < GV ? col : GV - 1) * RS16 + 8 * half;
+    const _Float16 *rl = rh + size_t(GV) * RS16;
+    const int soff = (col * Dm + 8 * half) * 2;   // bytes: the lane's row and k half
+    for (int mt = wv; mt < mt_n; mt += kDbWaves) {
+      v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      const __amdgpu_buffer_rsrc_t sr0 = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<_Float16 *>(a.cp.Sh[0] + size_t(32 * mt) * Dm), 0, 32 * Dm * 2, 0x00020000);
+      const __amdgpu_buffer_rsrc_t sr1 = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<_Float16 *>(a.cp.Sh[1] + size_t(32 * mt) * Dm), 0, 32 * Dm * 2, 0x00020000);
+      v8h sb[kDbPf16][2];
 #pragma unroll
-    for (int f = 0; f < kDbPf; ++f) sb[f] = sload(f);
-    for (int c0 = 0; c0 < NCK; c0 += kDbPf) {
-      // this round's vectors, then the next round's requested in one block (the scheduling
-      // barriers keep the compiler from sinking each load to its use)
-      v4f cur[kDbPf];
-#pragma unroll
-      for (int f = 0; f < kDbPf; ++f) cur[f] = sb[f];
-      __builtin_amdgcn_sched_barrier(0);
-      if (c0 + kDbPf < NCK) {
-#pragma unroll
-        for (int f = 0; f < kDbPf; ++f) sb[f] = sload(c0 + kDbPf + f);
+      for (int f = 0; f < kDbPf16; ++f) {
+        sb[f][0] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(sr0, soff + 32 * f, 0, 0));
+        sb[f][1] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(sr1, soff + 32 * f, 0, 0));
       }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i0 = 0; i0 < NS; i0 += kDbPf16) {
+        v8h cur[kDbPf16][2];
 #pragma unroll
-      for (int f = 0; f < kDbPf; ++f) {
-        const float4 rv = rrow[4 * (c0 + f)];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][0], rv.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][1], rv.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][2], rv.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][3], rv.w, acc, 0, 0, 0);
+        for (int f = 0; f < kDbPf16; ++f) {
+          cur[f][0] = sb[f][0];
+          cur[f][1] = sb[f][1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (i0 + kDbPf16 < NS) {
+#pragma unroll
+          for (int f = 0; f < kDbPf16; ++f) {
+            const int o = soff + 32 * (i0 + kDbPf16 + f);
+            sb[f][0] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(sr0, o, 0, 0));
+            sb[f][1] = __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(sr1, o, 0, 0));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int f = 0; f < kDbPf16; ++f) {
+          const int i = i0 + f;
+          const v8h ra = *reinterpret_cast<const v8h *>(rh + 16 * i);
+          const v8h rb = *reinterpret_cast<const v8h *>(rl + 16 * i);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[f][0], rb, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[f][1], ra, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur[f][0], ra, acc, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      // lane holds rows 8 (r / 4) + 4 (lane / 32) + r % 4 of the tile, column lane % 32
+      uint32_t bits = 0u;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bits |= uint32_t(acc[r] >= 0.0f) << (8 * (r >> 2) + 4 * half + (r & 3));
+      bits |= __shfl_xor(bits, 32, 64);
+      const int p = g0 + col;
+      if (half == 0 && col < GV && p < end) {
+        uint8_t *rec = a.ch.kbits + (size_t(unit) * a.capacity + p) * a.ch.kbytes;
+        *reinterpret_cast<uint32_t *>(rec + a.bits_k * dbytes + 4 * mt) = bits;
+      }
     }
-    // lane holds outputs 16 mt + 4 (lane / 16) + r of vector lane % 16
-    uint32_t bits = 0u;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) bits |= uint32_t(acc[r] >= 0.0f) << (4 * (lane >> 4) + r);
-    bits |= __shfl_xor(bits, 16, 64);
-    bits |= __shfl_xor(bits, 32, 64);
-    const int p = g0 + (lane & 15);
-    if (lane < 16 && p < end) {
-      uint8_t *rec = a.ch.kbits + (size_t(unit) * a.capacity + p) * a.ch.kbytes;
-      uint16_t *sb = reinterpret_cast<uint16_t *>(rec + a.bits_k * dbytes + 2 * mt);
-      *sb = uint16_t(bits);
+  } else {
+    // z^T[m x 16] = S[m x Dm] . R^T[Dm x 16], 16-row output tiles spread over the waves.
+    // The contraction runs in chunks of 16 coordinates; in chunk c, MFMA i takes from lane
+    // group g = lane / 16 the coordinate 16 c + 4 g + i (any order of k serves, A and B
+    // using the same), so a lane reads S and R as one 16-byte vector per chunk.  The S
+    // vectors of the next kDbPf chunks are in flight while a chunk is multiplied: S comes
+    // from L2 / the last-level cache, and two waves per SIMD cannot hide that latency by
+    // themselves.
+    constexpr int kDbPf = 8;
+    constexpr int NCK = Dm / 16;
+    static_assert(NCK % kDbPf == 0, "whole prefetch rounds");
+    const int mt_n = a.m / 16;
+    for (int mt = wv; mt < mt_n; mt += kDbWaves) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      // (buffer loads: S is read-only, and from plain loads the compiler would load each
+      // vector again where it is used instead of keeping the early load's result)
+      const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float *>(a.cp.S + size_t(16 * mt) * Dm), 0, 16 * Dm * 4, 0x00020000);
+      const int soff = ((lane & 15) * Dm + 4 * (lane >> 4)) * 4;   // bytes: the lane's row, group
+      auto sload = [&](int c) {
+        return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(srs, soff + 64 * c, 0, 0));
+      };
+      const float4 *rrow = reinterpret_cast<const float4 *>(r_s + (lane & 15) * RS) + (lane >> 4);
+      v4f sb[kDbPf];
+  #pragma unroll
+      for (int f = 0; f < kDbPf; ++f) sb[f] = sload(f);
+      for (int c0 = 0; c0 < NCK; c0 += kDbPf) {
+        // this round's vectors, then the next round's requested in one block (the scheduling
+        // barriers keep the compiler from sinking each load to its use)
+        v4f cur[kDbPf];
+  #pragma unroll
+        for (int f = 0; f < kDbPf; ++f) cur[f] = sb[f];
+        __builtin_amdgcn_sched_barrier(0);
+        if (c0 + kDbPf < NCK) {
+  #pragma unroll
+          for (int f = 0; f < kDbPf; ++f) sb[f] = sload(c0 + kDbPf + f);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+        for (int f = 0; f < kDbPf; ++f) {
+          const float4 rv = rrow[4 * (c0 + f)];
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][0], rv.x, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][1], rv.y, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][2], rv.z, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(cur[f][3], rv.w, acc, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // lane holds outputs 16 mt + 4 (lane / 16) + r of vector lane % 16
+      uint32_t bits = 0u;
+  #pragma unroll
+      for (int r = 0; r < 4; ++r) bits |= uint32_t(acc[r] >= 0.0f) << (4 * (lane >> 4) + r);
+      bits |= __shfl_xor(bits, 16, 64);
+      bits |= __shfl_xor(bits, 32, 64);
+      const int p = g0 + (lane & 15);
+      if (lane < 16 && p < end) {
+        uint8_t *rec = a.ch.kbits + (size_t(unit) * a.capacity + p) * a.ch.kbytes;
+        uint16_t *sb = reinterpret_cast<uint16_t *>(rec + a.bits_k * dbytes + 2 * mt);
+        *sb = uint16_t(bits);
+      }
     }
   }
 }
@@ -4729,10 +4828,10 @@ tq_status tq_quantize_kv_profiled(const tq_cache_desc *desc, const void *codec_d
     }
 #undef TQ_QKV
   } else {
-    dim3 grid((n_new + kLargeGroup - 1) / kLargeGroup, a.units);
-    const size_t shm = size_t(kLargeGroup) * (d + 4) * 4;
 #define TQ_QDB(CC, EE, TT)                                                                     \
   do {                                                                                         \
+    const dim3 grid((n_new + db_group(CC) - 1) / db_group(CC), a.units);                       \
+    const size_t shm = db_lds_bytes(CC);                                                       \
     if (hipFuncSetAttribute(reinterpret_cast<const void *>(k_quantize_db<CC, EE, TT>),         \
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(shm)) != hipSuccess) \
       return TQ_EDEVICE;                                                                       \
